@@ -1,0 +1,162 @@
+"""CPU oracle: ctypes wrapper over ``igc_oracle.cpp``.
+
+TEST INFRASTRUCTURE ONLY. It may be imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the library. It shares no code with the HIP path.
+
+Each function cites the passage it follows (see ``igc_oracle.cpp`` for the definitions
+and the readings taken where the pages are silent). All functions here are pinned by the
+``-m "not gpu"`` tests in ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "igc_oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+__all__ = ["build_library", "OracleGrid", "kernel_map", "conv", "standard_offsets", "num_threads"]
+
+
+def build_library(force: bool = True) -> str:
+    """Compiles the oracle with g++ (-O2, OpenMP). Returns the library path."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["g++", "-O2", "-std=c++17", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp],
+                       check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build_library(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        i32 = ctypes.c_int32
+        lib.orc_build.restype = P
+        lib.orc_build.argtypes = [P, i64]
+        lib.orc_free.argtypes = [P]
+        lib.orc_counts.argtypes = [P, P]
+        lib.orc_export.argtypes = [P] * 12
+        lib.orc_active_ijk.argtypes = [P, P]
+        lib.orc_ijk_to_index.argtypes = [P, P, i64, P]
+        lib.orc_kernel_map.argtypes = [P, P, i32, P, P]
+        lib.orc_conv.argtypes = [P, i64, i32, P, i32, P, i32, P, i64, P]
+        lib.orc_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def standard_offsets() -> np.ndarray:
+    """The 27 offsets of a 3x3x3 kernel, o = (di+1)*9 + (dj+1)*3 + (dk+1)."""
+    d = np.array([-1, 0, 1], dtype=np.int32)
+    di, dj, dk = np.meshgrid(d, d, d, indexing="ij")
+    return np.ascontiguousarray(np.stack([di.ravel(), dj.ravel(), dk.ravel()], axis=1))
+
+
+def num_threads() -> int:
+    return int(_load().orc_num_threads())
+
+
+class OracleGrid:
+    """IndexGrid built on the CPU from int32[n,3] coordinates (fVDB notes: "IndexGrid" and
+    "GPU-accelerated IndexGrid build" sections; the order and encoding are defined in
+    igc_oracle.cpp)."""
+
+    def __init__(self, coords: np.ndarray):
+        lib = _load()
+        c = np.ascontiguousarray(coords, dtype=np.int32).reshape(-1, 3)
+        self._keep = c
+        h = lib.orc_build(_ptr(c), c.shape[0])
+        if not h:
+            raise ValueError("oracle build failed")
+        self._h = h
+        cnt = np.zeros(4, dtype=np.int64)
+        lib.orc_counts(h, _ptr(cnt))
+        self.n, self.n_leaf, self.n_lower, self.n_upper = (int(x) for x in cnt)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.orc_free(h)
+            self._h = None
+
+    def topology(self) -> dict:
+        """Canonical topology arrays, keyed like the HIP library's export."""
+        U, L, F = self.n_upper, self.n_lower, self.n_leaf
+        t = {
+            "root_key": np.zeros(U, np.uint64),
+            "upper_origin": np.zeros((U, 3), np.int32),
+            "upper_mask": np.zeros((U, 512), np.uint64),
+            "upper_first": np.zeros(U, np.uint32),
+            "lower_origin": np.zeros((L, 3), np.int32),
+            "lower_mask": np.zeros((L, 64), np.uint64),
+            "lower_first": np.zeros(L, np.uint32),
+            "leaf_origin": np.zeros((F, 3), np.int32),
+            "leaf_mask": np.zeros((F, 8), np.uint64),
+            "leaf_offset": np.zeros(F, np.uint64),
+            "leaf_prefix": np.zeros(F, np.uint64),
+        }
+        _load().orc_export(self._h, *[_ptr(t[k]) for k in (
+            "root_key", "upper_origin", "upper_mask", "upper_first", "lower_origin", "lower_mask",
+            "lower_first", "leaf_origin", "leaf_mask", "leaf_offset", "leaf_prefix")])
+        return t
+
+    def active_ijk(self) -> np.ndarray:
+        out = np.zeros((self.n, 3), np.int32)
+        _load().orc_active_ijk(self._h, _ptr(out))
+        return out
+
+    def ijk_to_index(self, q: np.ndarray) -> np.ndarray:
+        q = np.ascontiguousarray(q, dtype=np.int32).reshape(-1, 3)
+        out = np.zeros(q.shape[0], np.int32)
+        _load().orc_ijk_to_index(self._h, _ptr(q), q.shape[0], _ptr(out))
+        return out
+
+    def kernel_map(self, offsets: np.ndarray | None = None, with_mask: bool = False):
+        """Neighbour map int32[K, N] (DriveRT page, "Shared neighbour maps")."""
+        off = standard_offsets() if offsets is None else np.ascontiguousarray(offsets, dtype=np.int32)
+        K = off.shape[0]
+        m = np.zeros((K, self.n), np.int32)
+        nb = np.zeros(self.n, np.uint32) if with_mask else None
+        _load().orc_kernel_map(self._h, _ptr(off), K, _ptr(m), _ptr(nb))
+        return (m, nb) if with_mask else m
+
+
+def kernel_map(grid: OracleGrid, offsets: np.ndarray | None = None):
+    return grid.kernel_map(offsets)
+
+
+def conv(kmap: np.ndarray, feats: np.ndarray, w: np.ndarray, rows: np.ndarray | None = None) -> np.ndarray:
+    """Submanifold convolution in float64 over a neighbour map (fVDB notes, sparse-conv
+    operators): out[r] = sum_o W[o]^T feats[map[o, r]] over map[o, r] >= 0.
+
+    feats float32[N, cin] (bf16 inputs are passed as their exact float32 values),
+    w float32[K, cin, cout]; returns float64[len(rows) or N, cout].
+    """
+    kmap = np.ascontiguousarray(kmap, dtype=np.int32)
+    K, N = kmap.shape
+    f = np.ascontiguousarray(feats, dtype=np.float32)
+    ww = np.ascontiguousarray(w, dtype=np.float32)
+    cin, cout = ww.shape[1], ww.shape[2]
+    assert f.shape == (N, cin) and ww.shape[0] == K
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    R = N if r is None else r.shape[0]
+    out = np.zeros((R, cout), np.float64)
+    _load().orc_conv(_ptr(kmap), N, K, _ptr(f), cin, _ptr(ww), cout, _ptr(r), R, _ptr(out))
+    return out
