@@ -1,0 +1,181 @@
+/*
+ * igconv.h - C ABI of libigconv: a VDB-style IndexGrid built on the GPU from voxel
+ * coordinates, its neighbour (kernel) map, and the 3x3x3 submanifold sparse convolution
+ * over it, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of what each call computes:
+ *  - "fVDB: A Deep-Learning Framework for Sparse, Large Scale, and High Performance Spatial
+ *    Intelligence", reading notes (woaixuexisr.github.io), sections "core method"
+ *    (VDB tree: hashed root, dense child nodes of fanout 32/16/8 per axis), "IndexGrid:
+ *    separating topology from values" (the tree returns an index into an external linear
+ *    "sidecar" array; only active voxels are indexed; bitmask prefix sums + popcount),
+ *    "GPU-accelerated IndexGrid build" (64-bit root keys, radix sort, run-length encoding,
+ *    per-tile keys, local radix sort, node counts, top-down registration), and
+ *    "accelerated operators for sparse convolution" (leaf-local densification of 8^3 leaves
+ *    plus a one-voxel halo; gather-GEMM-scatter over tiles of consecutive outputs for very
+ *    sparse inputs with high channel counts; automatic backend choice).
+ *  - DriveRT (lucabrembilla.dev/projects/drivert): "Shared neighbour maps" (a map is
+ *    defined by coordinate domain, kernel geometry and row order), "Compilation and
+ *    deployment" (runtime behind a C ABI; dynamic sizes: buffers start from an estimate
+ *    and the invocation repeats with a larger buffer, never a truncated result), "Inspection
+ *    and debugging" (errors name the operation; precision is never changed implicitly).
+ *
+ * Conventions for every call:
+ *  - Pointers prefixed d_ are device memory (hipMalloc / torch CUDA tensors) on the current
+ *    device; h_ pointers are host memory. The caller owns every buffer it passes in.
+ *  - `stream` is a hipStream_t (NULL = the null stream). All device work is enqueued on it;
+ *    calls return when the work is enqueued, except where a host synchronisation is stated.
+ *  - Layouts are row-major and densely packed. Coordinates are int32 triples (i, j, k).
+ *  - Every call returns IGC_OK (0) or an igc_status code; igc_last_error() then returns a
+ *    message naming the call and the argument or step that failed (per host thread).
+ *    Arguments are validated on the host before anything is launched. On error no grid is
+ *    created and output buffers hold unspecified values.
+ *  - Linear index: the row of an active voxel in every feature array over the grid; rows are
+ *    0-based, -1 means "not an active voxel". The row order is the depth-first tree order:
+ *    root tiles by their packed 64-bit key (i field most significant, each field the 32-bit
+ *    pattern shifted right logically by 12), then children x-major inside each node (upper
+ *    32^3, lower 16^3, leaf 8^3).
+ */
+#ifndef IGCONV_H
+#define IGCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct igc_grid igc_grid; /* opaque, immutable once built */
+typedef void* igc_stream;         /* hipStream_t */
+
+typedef enum {
+  IGC_OK = 0,
+  IGC_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad enum value, bad offset list */
+  IGC_ERR_UNSUPPORTED = 2, /* dtype / channel count / path combination not implemented */
+  IGC_ERR_OOM = 3,         /* device or pinned host allocation failed */
+  IGC_ERR_HIP = 4,         /* a HIP runtime call failed; the message holds hipGetErrorString */
+  IGC_ERR_RANGE = 5,       /* a size beyond the int32 row range (more than 2^31-1 rows) */
+  IGC_ERR_CAPACITY = 6,    /* an internal capacity retry was exhausted */
+  IGC_ERR_INTERNAL = 7     /* a device-side consistency check failed */
+} igc_status;
+
+typedef enum { IGC_F32 = 0, IGC_BF16 = 1 } igc_dtype;
+
+typedef enum {
+  IGC_PATH_AUTO = 0, /* choose from measured leaf occupancy, neighbour count and channels */
+  IGC_PATH_LEAF = 1, /* leaf-local dense convolution over an LDS window of 10^3 voxels */
+  IGC_PATH_GGS = 2   /* gather-GEMM-scatter over tiles of consecutive output rows */
+} igc_path;
+
+typedef struct {
+  int64_t n_input;        /* coordinates passed to igc_grid_build (duplicates included) */
+  int64_t n_voxels;       /* N: distinct active voxels = rows of every feature array */
+  int64_t n_leaf;         /* F: 8^3 leaf nodes */
+  int64_t n_lower;        /* Lw: 128^3 lower internal nodes */
+  int64_t n_upper;        /* U: 4096^3 upper internal nodes = root tiles */
+  int64_t topology_bytes; /* device bytes held by the grid */
+  int32_t sort_passes;    /* 8-bit digit passes the build's radix sort ran */
+  int32_t root_capacity;  /* slots of the root hash table */
+} igc_grid_info;
+
+/* Host buffers for igc_grid_export, sized from igc_grid_info (U, Lw, F). A null pointer
+ * skips that array. Layouts:
+ *   root_key     uint64[U]      packed tile key of each upper node, ascending
+ *   upper_origin int32[U,3]     coordinate of the node's first voxel (low 12 bits clear)
+ *   upper_mask   uint64[U,512]  child mask, bit c = (x*32+y)*32+z in word c/64
+ *   upper_first  uint32[U]      row of the node's first lower node
+ *   lower_origin int32[Lw,3]    (low 7 bits clear)
+ *   lower_mask   uint64[Lw,64]  child mask, bit c = (x*16+y)*16+z
+ *   lower_first  uint32[Lw]     row of the node's first leaf
+ *   leaf_origin  int32[F,3]     (low 3 bits clear)
+ *   leaf_mask    uint64[F,8]    active mask, word = x, bit = y*8+z
+ *   leaf_offset  uint64[F]      linear index of the leaf's first active voxel
+ *   leaf_prefix  uint64[F]      for w = 1..7, active voxels in words 0..w-1, 9 bits each at
+ *                               bit 9*(w-1)
+ * The per-leaf index record (8 mask words, offset, prefix) is 80 bytes, as in the fVDB
+ * notes' "IndexGrid" section. */
+typedef struct {
+  uint64_t* root_key;
+  int32_t* upper_origin;
+  uint64_t* upper_mask;
+  uint32_t* upper_first;
+  int32_t* lower_origin;
+  uint64_t* lower_mask;
+  uint32_t* lower_first;
+  int32_t* leaf_origin;
+  uint64_t* leaf_mask;
+  uint64_t* leaf_offset;
+  uint64_t* leaf_prefix;
+} igc_topology_host;
+
+/* Builds an IndexGrid from d_ijk int32[n_in,3] (device; any order; duplicates allowed;
+ * n_in == 0 gives an empty grid) - fVDB notes, "GPU-accelerated IndexGrid build": root
+ * tile keys, radix sort of per-tile 64-bit keys, run-length encoding, upper / lower / leaf
+ * counts, allocation, top-down registration of nodes and leaf bit masks.
+ * Host synchronisations: two (tile count, then node counts, to size allocations). If the
+ * root hash table overflows its first capacity the step repeats with a larger one
+ * (DriveRT, dynamic sizes). Errors: IGC_ERR_INVALID_ARG (out null, d_ijk null with
+ * n_in > 0, n_in < 0), IGC_ERR_RANGE (n_in > 2^31-1), IGC_ERR_OOM, IGC_ERR_HIP,
+ * IGC_ERR_CAPACITY, IGC_ERR_INTERNAL. On success *out owns device memory until
+ * igc_grid_destroy. d_ijk may be freed once the stream reaches the end of the call. */
+int igc_grid_build(const int32_t* d_ijk, int64_t n_in, igc_stream stream, igc_grid** out);
+
+/* Frees the grid (waits for its stream first). NULL is accepted. */
+int igc_grid_destroy(igc_grid* grid);
+
+/* Counts and sizes of the grid (host only, no device work). */
+int igc_grid_get_info(const igc_grid* grid, igc_grid_info* out);
+
+/* d_out int32[N,3] (device): the active voxels in linear-index order. This is the row order
+ * every feature array over the grid uses. */
+int igc_grid_active_ijk(const igc_grid* grid, int32_t* d_out, igc_stream stream);
+
+/* d_idx[r] = linear index of d_q[r] (int32[m,3], device), -1 if inactive - fVDB notes,
+ * "IndexGrid": root hash, fixed-fanout descent, mask test and popcount of the masked word
+ * plus the leaf's prefix count. */
+int igc_grid_ijk_to_index(const igc_grid* grid, const int32_t* d_q, int64_t m, int32_t* d_idx,
+                          igc_stream stream);
+
+/* Synchronous copy of the topology into caller-owned host buffers (see igc_topology_host). */
+int igc_grid_export(const igc_grid* grid, const igc_topology_host* out);
+
+/* Neighbour map (DriveRT, "Shared neighbour maps"): d_map int32[K,N] (device, caller-owned),
+ * d_map[o*N + r] = linear index of active voxel r shifted by h_offsets[o] (host int32[K,3]),
+ * or -1. Neighbours outside the int32 coordinate range are absent. d_nbmask (uint32[N],
+ * device, may be NULL) gets bit o set when d_map[o*N+r] >= 0; it requires K <= 32.
+ * Limits: 1 <= K <= 256 and |offset component| <= 8 (IGC_ERR_INVALID_ARG otherwise).
+ * The 3x3x3 convolution uses K = 27 in the order o = (di+1)*9 + (dj+1)*3 + (dk+1). */
+int igc_kernel_map(const igc_grid* grid, const int32_t* h_offsets, int32_t K, int32_t* d_map,
+                   uint32_t* d_nbmask, igc_stream stream);
+
+/* Submanifold 3x3x3 convolution (fVDB notes, "accelerated operators for sparse
+ * convolution"): for every active voxel r,
+ *     d_out[r, co] = sum_{o, ci : map[o, r] >= 0} d_feats[map[o, r], ci] * d_w[o, ci, co]
+ * with the 27 offsets ordered as in igc_kernel_map. d_feats [N,cin], d_w [27,cin,cout] and
+ * d_out [N,cout] all have type `dtype`; accumulation is fp32; bf16 outputs are rounded to
+ * nearest even. Precision is never changed implicitly: an fp32 call computes in fp32.
+ * d_map (int32[27,N] from igc_kernel_map with the standard 27 offsets) is required by
+ * IGC_PATH_GGS and ignored by IGC_PATH_LEAF; with IGC_PATH_AUTO it is required whenever the
+ * choice (see igc_select_path) is GGS. Supported combinations:
+ *     LEAF: dtype F32, cin in {4, 8, 12, 16}, cout a multiple of 16 up to 64
+ *     GGS : dtype BF16, cin a multiple of 32 up to 256, cout a multiple of 64 up to 512
+ * Anything else returns IGC_ERR_UNSUPPORTED. d_out must not alias d_feats. */
+int igc_sparse_conv(const igc_grid* grid, const int32_t* d_map, const void* d_feats, int32_t dtype,
+                    int32_t cin, const void* d_w, int32_t cout, void* d_out, int32_t path,
+                    igc_stream stream);
+
+/* The path IGC_PATH_AUTO takes for this grid and layer shape (host only). Leaf when the
+ * dtype is F32 and the shape is supported by LEAF, GGS otherwise; IGC_ERR_UNSUPPORTED when
+ * neither path supports the shape. The IGC_PATH environment variable ("leaf" / "ggs")
+ * overrides the automatic choice. */
+int igc_select_path(const igc_grid* grid, int32_t dtype, int32_t cin, int32_t cout, int32_t* path);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char* igc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IGCONV_H */

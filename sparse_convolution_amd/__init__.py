@@ -1,0 +1,171 @@
+"""MI355X-native IndexGrid build, neighbour map and submanifold sparse convolution.
+
+Thin Python binding over libigconv (include/igconv.h): it checks tensor shapes, dtypes and
+devices, and passes raw device pointers and the current HIP stream to the C ABI. All device
+work runs in the library's HIP kernels; torch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import IgcError
+
+__all__ = [
+    "Grid", "grid_build", "kernel_map", "sparse_conv", "standard_offsets", "IgcError",
+    "PATH_AUTO", "PATH_LEAF", "PATH_GGS",
+]
+
+F32, BF16 = 0, 1
+PATH_AUTO, PATH_LEAF, PATH_GGS = 0, 1, 2
+_PATHS = {"auto": PATH_AUTO, "leaf": PATH_LEAF, "ggs": PATH_GGS}
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p | None:
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _device_tensor(t: torch.Tensor, name: str, dtype: torch.dtype, cols: int | None = None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if cols is not None and (t.dim() != 2 or t.shape[1] != cols):
+        raise ValueError(f"{name} must have shape [n, {cols}], got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def standard_offsets() -> np.ndarray:
+    """The 27 offsets of a 3x3x3 kernel in the order o = (di+1)*9 + (dj+1)*3 + (dk+1)."""
+    d = np.array([-1, 0, 1], dtype=np.int32)
+    di, dj, dk = np.meshgrid(d, d, d, indexing="ij")
+    return np.ascontiguousarray(np.stack([di.ravel(), dj.ravel(), dk.ravel()], axis=1))
+
+
+class Grid:
+    """An immutable IndexGrid on one GPU (igc_grid_build)."""
+
+    def __init__(self, handle: ctypes.c_void_p, device: torch.device):
+        self._h = handle
+        self.device = device
+        info = _lib.GridInfo()
+        _lib.check(_lib.load().igc_grid_get_info(self._h, ctypes.byref(info)))
+        self.n_input = info.n_input
+        self.n_voxels = info.n_voxels
+        self.n_leaf = info.n_leaf
+        self.n_lower = info.n_lower
+        self.n_upper = info.n_upper
+        self.topology_bytes = info.topology_bytes
+        self.sort_passes = info.sort_passes
+        self.root_capacity = info.root_capacity
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            try:
+                _lib.load().igc_grid_destroy(h)
+            except Exception:
+                pass
+            self._h = None
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    @property
+    def leaf_occupancy(self) -> float:
+        return self.n_voxels / (512.0 * self.n_leaf) if self.n_leaf else 0.0
+
+    def active_ijk(self) -> torch.Tensor:
+        out = torch.empty((self.n_voxels, 3), dtype=torch.int32, device=self.device)
+        _lib.check(_lib.load().igc_grid_active_ijk(self._h, _ptr(out), _stream(self.device)))
+        return out
+
+    def ijk_to_index(self, q: torch.Tensor) -> torch.Tensor:
+        q = _device_tensor(q, "q", torch.int32, 3)
+        out = torch.empty(q.shape[0], dtype=torch.int32, device=self.device)
+        _lib.check(_lib.load().igc_grid_ijk_to_index(self._h, _ptr(q), q.shape[0], _ptr(out),
+                                                      _stream(self.device)))
+        return out
+
+    def export(self) -> dict:
+        """Topology copied to host numpy arrays (igc_grid_export)."""
+        U, L, F = self.n_upper, self.n_lower, self.n_leaf
+        t = {
+            "root_key": np.zeros(U, np.uint64), "upper_origin": np.zeros((U, 3), np.int32),
+            "upper_mask": np.zeros((U, 512), np.uint64), "upper_first": np.zeros(U, np.uint32),
+            "lower_origin": np.zeros((L, 3), np.int32), "lower_mask": np.zeros((L, 64), np.uint64),
+            "lower_first": np.zeros(L, np.uint32), "leaf_origin": np.zeros((F, 3), np.int32),
+            "leaf_mask": np.zeros((F, 8), np.uint64), "leaf_offset": np.zeros(F, np.uint64),
+            "leaf_prefix": np.zeros(F, np.uint64),
+        }
+        th = _lib.TopologyHost(**{k: v.ctypes.data_as(ctypes.c_void_p) for k, v in t.items()})
+        _lib.check(_lib.load().igc_grid_export(self._h, ctypes.byref(th)))
+        return t
+
+    def select_path(self, dtype: torch.dtype, cin: int, cout: int) -> str:
+        p = ctypes.c_int32(0)
+        _lib.check(_lib.load().igc_select_path(self._h, _dtype_code(dtype), cin, cout, ctypes.byref(p)))
+        return {PATH_LEAF: "leaf", PATH_GGS: "ggs"}[p.value]
+
+
+def _dtype_code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return F32
+    if dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def grid_build(ijk: torch.Tensor) -> Grid:
+    """IndexGrid from int32[n, 3] device coordinates (any order, duplicates allowed)."""
+    ijk = _device_tensor(ijk, "ijk", torch.int32, 3)
+    h = ctypes.c_void_p()
+    _lib.check(_lib.load().igc_grid_build(_ptr(ijk), ijk.shape[0], _stream(ijk.device), ctypes.byref(h)))
+    return Grid(h, ijk.device)
+
+
+def kernel_map(grid: Grid, offsets: np.ndarray | None = None, with_mask: bool = False):
+    """Neighbour map int32[K, N] (and optionally the uint32[N] neighbour bit masks, stored
+    in an int32 tensor)."""
+    off = standard_offsets() if offsets is None else np.ascontiguousarray(offsets, dtype=np.int32).reshape(-1, 3)
+    K = off.shape[0]
+    m = torch.empty((K, grid.n_voxels), dtype=torch.int32, device=grid.device)
+    nb = torch.empty(grid.n_voxels, dtype=torch.int32, device=grid.device) if with_mask else None
+    _lib.check(_lib.load().igc_kernel_map(grid.handle, off.ctypes.data_as(ctypes.c_void_p), K, _ptr(m),
+                                          _ptr(nb), _stream(grid.device)))
+    return (m, nb) if with_mask else m
+
+
+def sparse_conv(grid: Grid, feats: torch.Tensor, weights: torch.Tensor, kmap: torch.Tensor | None = None,
+                path: str = "auto", out: torch.Tensor | None = None) -> torch.Tensor:
+    """3x3x3 submanifold convolution: feats [N, cin], weights [27, cin, cout] -> [N, cout]."""
+    dt = feats.dtype
+    cin = feats.shape[1] if feats.dim() == 2 else -1
+    feats = _device_tensor(feats, "feats", dt, cin)
+    if feats.shape[0] != grid.n_voxels:
+        raise ValueError(f"feats has {feats.shape[0]} rows, grid has {grid.n_voxels} voxels")
+    if weights.dim() != 3 or weights.shape[0] != 27 or weights.shape[1] != cin:
+        raise ValueError(f"weights must have shape [27, {cin}, cout], got {tuple(weights.shape)}")
+    weights = _device_tensor(weights, "weights", dt)
+    cout = weights.shape[2]
+    if kmap is not None:
+        kmap = _device_tensor(kmap, "kmap", torch.int32)
+        if tuple(kmap.shape) != (27, grid.n_voxels):
+            raise ValueError(f"kmap must have shape [27, {grid.n_voxels}]")
+    if out is None:
+        out = torch.empty((grid.n_voxels, cout), dtype=dt, device=grid.device)
+    else:
+        out = _device_tensor(out, "out", dt, cout)
+    _lib.check(_lib.load().igc_sparse_conv(grid.handle, _ptr(kmap), _ptr(feats), _dtype_code(dt), cin,
+                                           _ptr(weights), cout, _ptr(out), _PATHS[path], _stream(grid.device)))
+    return out

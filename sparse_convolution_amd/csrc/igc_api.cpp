@@ -1,0 +1,273 @@
+// extern "C" entry points of libigconv: host-side validation, error reporting, allocation
+// and dispatch to the HIP kernels. Every check runs on the host before any launch.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "igc_host.h"
+
+namespace igc {
+
+namespace {
+thread_local std::string g_last_error;
+std::mutex g_pool_mutex;
+std::vector<int> g_pool_ready;
+thread_local void* g_staging = nullptr;
+thread_local size_t g_staging_bytes = 0;
+}  // namespace
+
+int set_error(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+int hip_status(hipError_t e, const char* what) {
+  std::string m = std::string(what) + ": " + hipGetErrorString(e);
+  return set_error(e == hipErrorOutOfMemory ? IGC_ERR_OOM : IGC_ERR_HIP, m);
+}
+
+// Keeps freed blocks in the device's default pool so repeated builds do not return memory
+// to the driver between calls.
+static void prepare_pool(int dev) {
+  std::lock_guard<std::mutex> lock(g_pool_mutex);
+  if ((int)g_pool_ready.size() <= dev) g_pool_ready.resize(dev + 1, 0);
+  if (g_pool_ready[dev]) return;
+  hipMemPool_t pool;
+  if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+    uint64_t threshold = ~0ull;
+    (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+  }
+  g_pool_ready[dev] = 1;
+}
+
+int dev_alloc(void** p, size_t bytes, hipStream_t s, const char* what) {
+  *p = nullptr;
+  int dev = 0;
+  IGC_HIP(hipGetDevice(&dev), what);
+  prepare_pool(dev);
+  if (bytes == 0) bytes = 256;
+  hipError_t e = hipMallocAsync(p, bytes, s);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    return set_error(e == hipErrorOutOfMemory ? IGC_ERR_OOM : IGC_ERR_HIP,
+                     std::string(what) + ": device allocation of " + std::to_string(bytes) +
+                         " bytes failed: " + hipGetErrorString(e));
+  }
+  return IGC_OK;
+}
+
+void dev_free(void* p, hipStream_t s) {
+  if (p) (void)hipFreeAsync(p, s);
+}
+
+void* host_staging(size_t bytes) {
+  if (g_staging_bytes < bytes) {
+    if (g_staging) (void)hipHostFree(g_staging);
+    g_staging = nullptr;
+    g_staging_bytes = 0;
+    if (hipHostMalloc(&g_staging, bytes, hipHostMallocDefault) != hipSuccess) return nullptr;
+    g_staging_bytes = bytes;
+  }
+  return g_staging;
+}
+
+static void free_grid(igc_grid* g) {
+  if (!g) return;
+  dev_free(g->block, g->stream);
+  dev_free(g->root_keys, g->stream);
+  dev_free(g->root_vals, g->stream);
+  delete g;
+}
+
+static bool leaf_occupancy_ok(const igc_grid* g) {
+  // Leaf path pays for 512 positions per leaf; the fVDB notes put its break-even against a
+  // general backend at a leaf occupancy of about 20%.
+  return g->n_leaf > 0 && (double)g->n_voxels >= 0.2 * 512.0 * (double)g->n_leaf;
+}
+
+static int choose_path(const igc_grid* g, int32_t dtype, int32_t cin, int32_t cout, int32_t* path) {
+  const bool leaf_ok = leaf_conv_supported(dtype, cin, cout);
+  const bool ggs_ok = ggs_conv_supported(dtype, cin, cout);
+  if (const char* e = std::getenv("IGC_PATH")) {
+    if (!std::strcmp(e, "leaf") && leaf_ok) return *path = IGC_PATH_LEAF, IGC_OK;
+    if (!std::strcmp(e, "ggs") && ggs_ok) return *path = IGC_PATH_GGS, IGC_OK;
+  }
+  if (leaf_ok && (leaf_occupancy_ok(g) || !ggs_ok)) return *path = IGC_PATH_LEAF, IGC_OK;
+  if (ggs_ok) return *path = IGC_PATH_GGS, IGC_OK;
+  return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: no path supports dtype " + std::to_string(dtype) +
+                                            " with cin " + std::to_string(cin) + " and cout " + std::to_string(cout));
+}
+
+}  // namespace igc
+
+using namespace igc;
+
+extern "C" {
+
+int igc_grid_build(const int32_t* d_ijk, int64_t n_in, igc_stream stream, igc_grid** out) {
+  clear_error();
+  if (!out) return set_error(IGC_ERR_INVALID_ARG, "igc_grid_build: out is null");
+  *out = nullptr;
+  if (n_in < 0) return set_error(IGC_ERR_INVALID_ARG, "igc_grid_build: n_in is negative");
+  if (n_in > 0 && !d_ijk) return set_error(IGC_ERR_INVALID_ARG, "igc_grid_build: d_ijk is null");
+  if (n_in > INT32_MAX) return set_error(IGC_ERR_RANGE, "igc_grid_build: n_in exceeds 2^31-1");
+  igc_grid* g = new (std::nothrow) igc_grid();
+  if (!g) return set_error(IGC_ERR_OOM, "igc_grid_build: host allocation");
+  g->stream = (hipStream_t)stream;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    delete g;
+    return hip_status(e, "igc_grid_build: hipGetDevice");
+  }
+  g->device = dev;
+  const int rc = build_grid(d_ijk, n_in, (hipStream_t)stream, g);
+  if (rc != IGC_OK) {
+    free_grid(g);
+    return rc;
+  }
+  *out = g;
+  return IGC_OK;
+}
+
+int igc_grid_destroy(igc_grid* grid) {
+  clear_error();
+  if (!grid) return IGC_OK;
+  hipError_t e = hipStreamSynchronize(grid->stream);
+  free_grid(grid);
+  if (e != hipSuccess) return hip_status(e, "igc_grid_destroy: stream synchronize");
+  return IGC_OK;
+}
+
+int igc_grid_get_info(const igc_grid* g, igc_grid_info* out) {
+  clear_error();
+  if (!g || !out) return set_error(IGC_ERR_INVALID_ARG, "igc_grid_get_info: null argument");
+  out->n_input = g->n_input;
+  out->n_voxels = g->n_voxels;
+  out->n_leaf = g->n_leaf;
+  out->n_lower = g->n_lower;
+  out->n_upper = g->n_upper;
+  out->topology_bytes = (int64_t)g->bytes;
+  out->sort_passes = g->sort_passes;
+  out->root_capacity = (int32_t)g->root_cap;
+  return IGC_OK;
+}
+
+int igc_grid_active_ijk(const igc_grid* g, int32_t* d_out, igc_stream stream) {
+  clear_error();
+  if (!g) return set_error(IGC_ERR_INVALID_ARG, "igc_grid_active_ijk: grid is null");
+  if (!d_out && g->n_voxels > 0) return set_error(IGC_ERR_INVALID_ARG, "igc_grid_active_ijk: d_out is null");
+  return launch_active_ijk(g, d_out, (hipStream_t)stream);
+}
+
+int igc_grid_ijk_to_index(const igc_grid* g, const int32_t* d_q, int64_t m, int32_t* d_idx, igc_stream stream) {
+  clear_error();
+  if (!g) return set_error(IGC_ERR_INVALID_ARG, "igc_grid_ijk_to_index: grid is null");
+  if (m < 0) return set_error(IGC_ERR_INVALID_ARG, "igc_grid_ijk_to_index: m is negative");
+  if (m > 0 && (!d_q || !d_idx)) return set_error(IGC_ERR_INVALID_ARG, "igc_grid_ijk_to_index: null buffer");
+  return launch_ijk_to_index(g, d_q, m, d_idx, (hipStream_t)stream);
+}
+
+int igc_grid_export(const igc_grid* g, const igc_topology_host* out) {
+  clear_error();
+  if (!g || !out) return set_error(IGC_ERR_INVALID_ARG, "igc_grid_export: null argument");
+  hipStream_t s = g->stream;
+  IGC_HIP(hipStreamSynchronize(s), "igc_grid_export: stream synchronize");
+  const int64_t U = g->n_upper, L = g->n_lower, F = g->n_leaf;
+  auto copy = [&](void* dst, const void* src, size_t bytes, const char* what) -> int {
+    if (!dst || bytes == 0) return IGC_OK;
+    IGC_HIP(hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost), what);
+    return IGC_OK;
+  };
+  auto origins = [&](int32_t* dst, const int4* src, int64_t n, const char* what) -> int {
+    if (!dst || n == 0) return IGC_OK;
+    std::vector<int4> tmp((size_t)n);
+    IGC_HIP(hipMemcpy(tmp.data(), src, (size_t)n * sizeof(int4), hipMemcpyDeviceToHost), what);
+    for (int64_t r = 0; r < n; ++r) {
+      dst[3 * r] = tmp[r].x;
+      dst[3 * r + 1] = tmp[r].y;
+      dst[3 * r + 2] = tmp[r].z;
+    }
+    return IGC_OK;
+  };
+  int rc;
+  if ((rc = copy(out->root_key, g->root_list, U * 8, "igc_grid_export: root keys"))) return rc;
+  if ((rc = origins(out->upper_origin, g->upper_origin, U, "igc_grid_export: upper origins"))) return rc;
+  if ((rc = copy(out->upper_mask, g->upper_mask, U * 512 * 8, "igc_grid_export: upper masks"))) return rc;
+  if ((rc = copy(out->upper_first, g->upper_first, U * 4, "igc_grid_export: upper links"))) return rc;
+  if ((rc = origins(out->lower_origin, g->lower_origin, L, "igc_grid_export: lower origins"))) return rc;
+  if ((rc = copy(out->lower_mask, g->lower_mask, L * 64 * 8, "igc_grid_export: lower masks"))) return rc;
+  if ((rc = copy(out->lower_first, g->lower_first, L * 4, "igc_grid_export: lower links"))) return rc;
+  if ((rc = origins(out->leaf_origin, g->leaf_origin, F, "igc_grid_export: leaf origins"))) return rc;
+  if (F > 0 && (out->leaf_mask || out->leaf_offset || out->leaf_prefix)) {
+    std::vector<LeafRec> tmp((size_t)F);
+    IGC_HIP(hipMemcpy(tmp.data(), g->leaf, (size_t)F * sizeof(LeafRec), hipMemcpyDeviceToHost),
+            "igc_grid_export: leaves");
+    for (int64_t f = 0; f < F; ++f) {
+      if (out->leaf_mask) std::memcpy(out->leaf_mask + 8 * f, tmp[f].mask, 64);
+      if (out->leaf_offset) out->leaf_offset[f] = tmp[f].offset;
+      if (out->leaf_prefix) out->leaf_prefix[f] = tmp[f].prefix;
+    }
+  }
+  return IGC_OK;
+}
+
+int igc_kernel_map(const igc_grid* g, const int32_t* h_offsets, int32_t K, int32_t* d_map, uint32_t* d_nbmask,
+                   igc_stream stream) {
+  clear_error();
+  if (!g) return set_error(IGC_ERR_INVALID_ARG, "igc_kernel_map: grid is null");
+  if (!h_offsets) return set_error(IGC_ERR_INVALID_ARG, "igc_kernel_map: h_offsets is null");
+  if (K < 1 || K > 256) return set_error(IGC_ERR_INVALID_ARG, "igc_kernel_map: K must be in [1, 256]");
+  for (int32_t a = 0; a < 3 * K; ++a)
+    if (h_offsets[a] < -8 || h_offsets[a] > 8)
+      return set_error(IGC_ERR_INVALID_ARG, "igc_kernel_map: offset component outside [-8, 8]");
+  if (d_nbmask && K > 32) return set_error(IGC_ERR_INVALID_ARG, "igc_kernel_map: d_nbmask needs K <= 32");
+  if (!d_map && g->n_voxels > 0) return set_error(IGC_ERR_INVALID_ARG, "igc_kernel_map: d_map is null");
+  return launch_kernel_map(g, h_offsets, K, d_map, d_nbmask, (hipStream_t)stream);
+}
+
+int igc_select_path(const igc_grid* g, int32_t dtype, int32_t cin, int32_t cout, int32_t* path) {
+  clear_error();
+  if (!g || !path) return set_error(IGC_ERR_INVALID_ARG, "igc_select_path: null argument");
+  if (dtype != IGC_F32 && dtype != IGC_BF16) return set_error(IGC_ERR_INVALID_ARG, "igc_select_path: bad dtype");
+  return choose_path(g, dtype, cin, cout, path);
+}
+
+int igc_sparse_conv(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype, int32_t cin,
+                    const void* d_w, int32_t cout, void* d_out, int32_t path, igc_stream stream) {
+  clear_error();
+  if (!g) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: grid is null");
+  if (dtype != IGC_F32 && dtype != IGC_BF16) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: bad dtype");
+  if (cin < 1 || cout < 1) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: cin and cout must be positive");
+  if (path != IGC_PATH_AUTO && path != IGC_PATH_LEAF && path != IGC_PATH_GGS)
+    return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: bad path");
+  if (!d_w) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: d_w is null");
+  if (g->n_voxels > 0 && (!d_feats || !d_out))
+    return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: d_feats or d_out is null");
+  if (d_feats && d_feats == d_out) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: d_out aliases d_feats");
+  int32_t p = path;
+  if (p == IGC_PATH_AUTO) {
+    const int rc = choose_path(g, dtype, cin, cout, &p);
+    if (rc) return rc;
+  }
+  if (p == IGC_PATH_LEAF && !leaf_conv_supported(dtype, cin, cout))
+    return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: leaf path does not support this dtype / cin / cout");
+  if (p == IGC_PATH_GGS && !ggs_conv_supported(dtype, cin, cout))
+    return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: gather-GEMM-scatter path does not support this dtype / cin / cout");
+  if (p == IGC_PATH_GGS && !d_map && g->n_voxels > 0)
+    return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: the gather-GEMM-scatter path needs d_map");
+  if (g->n_voxels == 0) return IGC_OK;
+  if (p == IGC_PATH_LEAF) return launch_conv_leaf(g, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream);
+  return launch_conv_ggs(g, d_map, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream);
+}
+
+const char* igc_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,813 @@
+// GPU IndexGrid build (fVDB notes, "GPU-accelerated IndexGrid build").
+//
+// The pages' build: 64-bit root keys (i, j, k each >> 12, packed 21+21+21 bits), a full radix
+// sort and run-length encoding of them, a 64-bit in-tile key per coordinate, a local radix
+// sort, upper / lower / leaf counts from the runs and unique keys, allocation from the
+// counts, and top-down registration of nodes and voxel bit masks.
+//
+// What this implementation keeps and changes on gfx950:
+//  1. Root tiles are deduplicated in an open-addressing hash table instead of by a full
+//     sort + RLE of N keys: a wave first collapses equal tile keys with ballots, the leader
+//     reads the slot and only then tries a compare-and-swap, so the few tiles of a scene
+//     cost a cached read per wave. The U distinct tiles are then sorted (U is small) and
+//     their rank in key order is stored back in the table. This gives the same tile order
+//     as the sort + RLE of the pages at a fraction of the traffic. The table is the root of
+//     the finished tree.
+//  2. Per coordinate, key2 = tile rank << 36 | upper child (15 bits) << 21 | lower child
+//     (12 bits) << 9 | leaf voxel (9 bits). The pass that writes key2 also builds the digit
+//     histograms of every radix pass, and only the bit span where keys differ is sorted
+//     (the OR and AND of all keys, taken in the tile pass, give that span).
+//  3. The sort is an LSD radix sort with 8-bit digits in the onesweep form: one read and one
+//     write of the keys per pass, ranks from 64-lane ballots (stable multisplit), a tile of
+//     4096 keys staged in LDS so that the scattered writes leave the CU as runs per digit,
+//     and digit offsets of earlier tiles found by decoupled look-back. Tiles take their
+//     index from an atomic counter, so every tile waits only on tiles already running.
+//  4. Unique voxels, leaves, lower and upper nodes are counted in one pass over the sorted
+//     keys (a key starts a voxel / leaf / lower / upper when key, key>>9, key>>21, key>>36
+//     differ from its predecessor); after the one read-back of the counts, a second pass
+//     gives every key its voxel / leaf / node rows from the scanned block counts and
+//     registers the nodes top-down. Leaf mask bits are OR-ed in (duplicates set the same
+//     bit), so no separate unique-compaction pass is needed.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "igc_host.h"
+#include "igc_internal.h"
+#include "igc_wave.h"
+
+namespace igc {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kKeysPerThread = 16;
+constexpr int kTileKeys = kThreads * kKeysPerThread;  // 4096 keys per onesweep tile
+constexpr int kMaxPasses = 8;
+constexpr uint64_t kLbAggregate = 1ull << 62;
+constexpr uint64_t kLbInclusive = 2ull << 62;
+constexpr uint64_t kLbValue = (1ull << 62) - 1ull;
+constexpr uint32_t kSpinLimit = 1u << 22;  // look-back waits end (and flag an error) after this
+constexpr int kSmallSort = 4096;             // tile-key sorts up to this size run in one workgroup
+
+struct BuildState {
+  uint32_t overflow;          // root table ran out of probes
+  uint32_t n_tiles;           // distinct root tiles inserted
+  uint32_t lookback_timeout;  // a look-back wait hit its spin limit
+  uint32_t tile_list_count;   // compaction cursor
+  uint32_t guard;             // a device-side bounds check failed (the build is rejected)
+  uint32_t pad;
+  uint64_t off_or, off_and;   // OR / AND over all in-tile offsets
+  uint64_t key_or, key_and;   // OR / AND over all tile keys
+  uint64_t counts[4];         // N, F, Lw, U from the sorted keys
+  uint32_t tile_counter[2 * kMaxPasses];
+};
+
+// ------------------------------------------------------------------------------ utilities
+
+__global__ void k_fill_u64(uint64_t* __restrict__ p, int64_t n, uint64_t v) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x)
+    p[e] = v;
+}
+
+__global__ void k_init_state(BuildState* st) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    st->overflow = 0;
+    st->n_tiles = 0;
+    st->lookback_timeout = 0;
+    st->tile_list_count = 0;
+    st->guard = 0;
+    st->off_or = 0;
+    st->off_and = ~0ull;
+    st->key_or = 0;
+    st->key_and = ~0ull;
+    for (int c = 0; c < 4; ++c) st->counts[c] = 0;
+    for (int p = 0; p < 2 * kMaxPasses; ++p) st->tile_counter[p] = 0;
+  }
+}
+
+int grid_for(int64_t n, int threads, int cap) {
+  int64_t b = (n + threads - 1) / threads;
+  if (b < 1) b = 1;
+  if (b > cap) b = cap;
+  return (int)b;
+}
+
+int fill_u64(uint64_t* p, int64_t n, uint64_t v, hipStream_t s) {
+  if (n <= 0) return IGC_OK;
+  k_fill_u64<<<grid_for(n, 256, 4096), 256, 0, s>>>(p, n, v);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: fill kernel launch");
+  return IGC_OK;
+}
+
+// ------------------------------------------------------------------------------ root tiles
+
+__device__ void insert_tile(uint64_t* keys, uint32_t mask, uint32_t limit, uint64_t key, BuildState* st) {
+  uint32_t s = hash_tile(key) & mask;
+  for (uint32_t p = 0; p < limit; ++p) {
+    const uint64_t cur = __hip_atomic_load(&keys[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (cur == key) return;
+    if (cur == kEmptyKey) {
+      const unsigned long long prev = atomicCAS((unsigned long long*)&keys[s], (unsigned long long)kEmptyKey,
+                                                (unsigned long long)key);
+      if (prev == kEmptyKey) {
+        atomicAdd(&st->n_tiles, 1u);
+        return;
+      }
+      if (prev == key) return;
+    }
+    s = (s + 1) & mask;
+  }
+  atomicOr(&st->overflow, 1u);
+}
+
+__global__ __launch_bounds__(256) void k_tile_insert(const int32_t* __restrict__ ijk, int64_t n,
+                                                     uint64_t* __restrict__ keys, uint32_t mask, uint32_t limit,
+                                                     BuildState* st) {
+  __shared__ uint64_t s_red[4][4];
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  uint64_t off_or = 0, off_and = ~0ull, key_or = 0, key_and = ~0ull;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t base = (int64_t)blockIdx.x * blockDim.x; base < n; base += stride) {
+    const int64_t e = base + threadIdx.x;
+    const bool valid = e < n;
+    uint64_t key = kEmptyKey;
+    if (valid) {
+      const int32_t i = ijk[3 * e], j = ijk[3 * e + 1], k = ijk[3 * e + 2];
+      key = tile_key(i, j, k);
+      const uint64_t off = tile_offset(i, j, k);
+      off_or |= off;
+      off_and &= off;
+      key_or |= key;
+      key_and &= key;
+    }
+    uint64_t pending = __ballot(valid);
+    while (pending) {
+      const int leader = __ffsll((unsigned long long)pending) - 1;
+      const uint64_t lk = shfl64(key, leader);
+      const uint64_t same = __ballot(valid && key == lk);
+      if (lane == leader) insert_tile(keys, mask, limit, lk, st);
+      pending &= ~same;
+    }
+  }
+  off_or = wave_or64(off_or);
+  off_and = wave_and64(off_and);
+  key_or = wave_or64(key_or);
+  key_and = wave_and64(key_and);
+  if (lane == 0) {
+    s_red[wave][0] = off_or;
+    s_red[wave][1] = off_and;
+    s_red[wave][2] = key_or;
+    s_red[wave][3] = key_and;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) {
+      off_or |= s_red[w][0];
+      off_and &= s_red[w][1];
+      key_or |= s_red[w][2];
+      key_and &= s_red[w][3];
+    }
+    atomicOr((unsigned long long*)&st->off_or, (unsigned long long)off_or);
+    atomicAnd((unsigned long long*)&st->off_and, (unsigned long long)off_and);
+    atomicOr((unsigned long long*)&st->key_or, (unsigned long long)key_or);
+    atomicAnd((unsigned long long*)&st->key_and, (unsigned long long)key_and);
+  }
+}
+
+__global__ void k_tile_compact(const uint64_t* __restrict__ keys, uint32_t cap, uint64_t* __restrict__ list,
+                               uint32_t U, BuildState* st) {
+  for (uint32_t s = blockIdx.x * blockDim.x + threadIdx.x; s < cap; s += gridDim.x * blockDim.x) {
+    const uint64_t k = keys[s];
+    if (k != kEmptyKey) {
+      const uint32_t pos = atomicAdd(&st->tile_list_count, 1u);
+      if (pos < U) list[pos] = k; else atomicOr(&st->guard, 1u);
+    }
+  }
+}
+
+// Bitonic sort of up to kSmallSort keys in one workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void k_sort_small(const uint64_t* __restrict__ in, uint64_t* __restrict__ out,
+                                                     int n) {
+  __shared__ uint64_t s[kSmallSort];
+  int p2 = 2;
+  while (p2 < n) p2 <<= 1;
+  for (int t = threadIdx.x; t < p2; t += blockDim.x) s[t] = t < n ? in[t] : kEmptyKey;
+  __syncthreads();
+  for (int size = 2; size <= p2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = threadIdx.x; t < p2 / 2; t += blockDim.x) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint64_t a = s[lo], b = s[hi];
+        if ((a > b) == up) {
+          s[lo] = b;
+          s[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int t = threadIdx.x; t < n; t += blockDim.x) out[t] = s[t];
+}
+
+// Slot of tile key k (present by construction); flags the guard if it is missing.
+__device__ __forceinline__ int64_t probe_slot(const uint64_t* __restrict__ keys, uint32_t mask, uint64_t k,
+                                              BuildState* st) {
+  uint32_t s = hash_tile(k) & mask;
+  for (uint32_t p = 0; p <= mask; ++p) {
+    if (keys[s] == k) return s;
+    s = (s + 1) & mask;
+  }
+  atomicOr(&st->guard, 1u);
+  return -1;
+}
+
+__global__ void k_tile_rank(const uint64_t* __restrict__ sorted, int64_t U, const uint64_t* __restrict__ keys,
+                            int32_t* __restrict__ vals, uint32_t mask, BuildState* st) {
+  for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < U; r += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t s = probe_slot(keys, mask, sorted[r], st);
+    if (s >= 0) vals[s] = (int32_t)r;
+  }
+}
+
+// ------------------------------------------------------------------------------ radix sort
+
+struct PassSpec {
+  int lo_bit;  // bit of digit 0
+  int passes;  // digits of 8 bits
+};
+
+// Per-wave LDS histograms of every pass digit, merged into the global histograms.
+__device__ __forceinline__ void hist_add(uint32_t* s_hist, uint64_t key, PassSpec ps) {
+  for (int p = 0; p < ps.passes; ++p) {
+    const uint32_t d = (uint32_t)(key >> (ps.lo_bit + 8 * p)) & 255u;
+    atomicAdd(&s_hist[p * 256 + d], 1u);
+  }
+}
+
+__device__ __forceinline__ void hist_flush(uint32_t (*s_hist)[kMaxPasses * 256], uint32_t* g_hist, PassSpec ps) {
+  __syncthreads();
+  for (int x = threadIdx.x; x < ps.passes * 256; x += blockDim.x) {
+    const uint32_t v = s_hist[0][x] + s_hist[1][x] + s_hist[2][x] + s_hist[3][x];
+    if (v) atomicAdd(&g_hist[x], v);
+  }
+}
+
+// key2 for every coordinate, plus the digit histograms of every sort pass.
+__global__ __launch_bounds__(256) void k_key2(const int32_t* __restrict__ ijk, int64_t n,
+                                              const uint64_t* __restrict__ root_keys,
+                                              const int32_t* __restrict__ root_vals, uint32_t mask,
+                                              uint64_t* __restrict__ out, PassSpec ps, uint32_t* __restrict__ hist,
+                                              BuildState* st) {
+  __shared__ uint32_t s_hist[4][kMaxPasses * 256];
+  for (int x = threadIdx.x; x < 4 * kMaxPasses * 256; x += blockDim.x) (&s_hist[0][0])[x] = 0;
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) {
+    const int32_t i = ijk[3 * e], j = ijk[3 * e + 1], k = ijk[3 * e + 2];
+    const uint64_t tk = tile_key(i, j, k);
+    const int64_t s = probe_slot(root_keys, mask, tk, st);
+    const uint64_t rank = s >= 0 ? (uint64_t)(uint32_t)root_vals[s] : 0ull;
+    const uint64_t key = (rank << 36) | tile_offset(i, j, k);
+    out[e] = key;
+    hist_add(s_hist[wave], key, ps);
+  }
+  hist_flush(s_hist, hist, ps);
+}
+
+// Digit histograms of an existing key array (used for the tile-key sort when U is large).
+__global__ __launch_bounds__(256) void k_hist(const uint64_t* __restrict__ keys, int64_t n, PassSpec ps,
+                                              uint32_t* __restrict__ hist) {
+  __shared__ uint32_t s_hist[4][kMaxPasses * 256];
+  for (int x = threadIdx.x; x < 4 * kMaxPasses * 256; x += blockDim.x) (&s_hist[0][0])[x] = 0;
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x)
+    hist_add(s_hist[wave], keys[e], ps);
+  hist_flush(s_hist, hist, ps);
+}
+
+// One LSD pass over the 8-bit digit at `shift`: stable, tile of 4096 keys per workgroup.
+__global__ __launch_bounds__(256) void k_onesweep(const uint64_t* __restrict__ src, uint64_t* __restrict__ dst,
+                                                  int64_t n, int shift, const uint32_t* __restrict__ hist,
+                                                  uint64_t* __restrict__ lookback, uint32_t* tile_counter,
+                                                  uint32_t* timeout, uint32_t* guard) {
+  __shared__ uint64_t s_keys[kTileKeys];
+  __shared__ uint32_t s_cnt[4][256];
+  __shared__ uint32_t s_tile_start[256];
+  __shared__ int64_t s_base[256];
+  __shared__ uint64_t s_tmp[4];
+  __shared__ uint32_t s_tile;
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  if (tid == 0) s_tile = atomicAdd(tile_counter, 1u);
+  for (int x = tid; x < 4 * 256; x += kThreads) (&s_cnt[0][0])[x] = 0;
+  __syncthreads();
+  const int64_t tile = s_tile;
+  const int64_t tile_base = tile * kTileKeys;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+
+  // Stable rank of every key among equal digits of its wave (blocked: wave w owns the
+  // tile's keys [w*1024, (w+1)*1024), 64 consecutive keys per round).
+  uint64_t key[kKeysPerThread];
+  uint32_t rank[kKeysPerThread];
+#pragma unroll
+  for (int r = 0; r < kKeysPerThread; ++r) {
+    const int64_t pos = tile_base + wave * 1024 + r * 64 + lane;
+    const bool valid = pos < n;
+    const uint64_t k = valid ? src[pos] : 0ull;
+    key[r] = k;
+    const uint32_t d = (uint32_t)(k >> shift) & 255u;
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool set = (d >> b) & 1u;
+      const uint64_t bb = __ballot(set);
+      m &= set ? bb : ~bb;
+    }
+    const uint32_t before = (uint32_t)__popcll(m & lt_mask);
+    uint32_t old = 0;
+    if (valid) old = s_cnt[wave][d];
+    if (valid && before == 0) s_cnt[wave][d] = old + (uint32_t)__popcll(m);
+    rank[r] = old + before;
+  }
+  __syncthreads();
+
+  // Thread tid owns digit tid: tile count, per-wave exclusive offsets, tile and bucket scans.
+  const uint32_t d = (uint32_t)tid;
+  const uint32_t c0 = s_cnt[0][d], c1 = s_cnt[1][d], c2 = s_cnt[2][d], c3 = s_cnt[3][d];
+  const uint32_t tcount = c0 + c1 + c2 + c3;
+  uint64_t* lb = lookback + tile * 256 + d;
+  __hip_atomic_store(lb, (tile == 0 ? kLbInclusive : kLbAggregate) | (uint64_t)tcount, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t tstart = (uint32_t)block_excl_scan64<kThreads>(tcount, s_tmp, nullptr);
+  const uint64_t bstart = block_excl_scan64<kThreads>(hist[d], s_tmp, nullptr);
+  s_cnt[0][d] = 0;
+  s_cnt[1][d] = c0;
+  s_cnt[2][d] = c0 + c1;
+  s_cnt[3][d] = c0 + c1 + c2;
+  s_tile_start[d] = tstart;
+
+  uint64_t excl = 0;
+  if (tile > 0) {
+    int64_t t = tile - 1;
+    while (true) {
+      uint64_t v;
+      uint32_t spins = 0;
+      while (true) {
+        v = __hip_atomic_load(lookback + t * 256 + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (v >> 62) break;
+        __builtin_amdgcn_s_sleep(1);
+        ++spins;
+        // Bounded wait: after the limit, or once any other wait has given up, stop waiting
+        // and flag the error so the host rejects the build.
+        if (spins >= kSpinLimit ||
+            ((spins & 1023u) == 0 && __hip_atomic_load(timeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+          atomicOr(timeout, 1u);
+          v = kLbInclusive;
+          break;
+        }
+      }
+      excl += v & kLbValue;
+      if ((v >> 62) == 2ull || t == 0) break;
+      --t;
+    }
+    __hip_atomic_store(lb, kLbInclusive | (excl + tcount), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  s_base[d] = (int64_t)bstart + (int64_t)excl - (int64_t)tstart;
+  __syncthreads();
+
+  // Digit-sorted order inside the tile, staged in LDS.
+#pragma unroll
+  for (int r = 0; r < kKeysPerThread; ++r) {
+    const int64_t pos = tile_base + wave * 1024 + r * 64 + lane;
+    if (pos < n) {
+      const uint32_t dd = (uint32_t)(key[r] >> shift) & 255u;
+      s_keys[s_tile_start[dd] + s_cnt[wave][dd] + rank[r]] = key[r];
+    }
+  }
+  __syncthreads();
+  const int64_t valid_count = n - tile_base < kTileKeys ? n - tile_base : kTileKeys;
+#pragma unroll
+  for (int q = 0; q < kKeysPerThread; ++q) {
+    const int p = q * kThreads + tid;
+    if (p < valid_count) {
+      const uint64_t k = s_keys[p];
+      const int64_t gp = s_base[(uint32_t)(k >> shift) & 255u] + p;
+      if (gp >= 0 && gp < n) dst[gp] = k; else atomicOr(guard, 1u);
+    }
+  }
+}
+
+// Sorts keys[0..n) (in a, scratch b) over the digits of ps; returns the buffer holding the
+// result. The histograms must already be in `hist` ([passes][256]).
+int onesweep_sort(uint64_t* a, uint64_t* b, int64_t n, PassSpec ps, const uint32_t* hist, uint32_t* tile_counters,
+                  uint32_t* timeout, uint32_t* guard, hipStream_t s, uint64_t** result) {
+  *result = a;
+  if (n <= 0 || ps.passes == 0) return IGC_OK;
+  const int64_t tiles = (n + kTileKeys - 1) / kTileKeys;
+  uint64_t* lb = nullptr;
+  int st = dev_alloc((void**)&lb, (size_t)ps.passes * tiles * 256 * sizeof(uint64_t), s, "igc_grid_build: look-back");
+  if (st) return st;
+  st = fill_u64(lb, (int64_t)ps.passes * tiles * 256, 0, s);
+  if (st) {
+    dev_free(lb, s);
+    return st;
+  }
+  uint64_t* src = a;
+  uint64_t* dst = b;
+  for (int p = 0; p < ps.passes; ++p) {
+    k_onesweep<<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, ps.lo_bit + 8 * p, hist + 256 * p,
+                                                    lb + (size_t)p * tiles * 256, tile_counters + p, timeout, guard);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      dev_free(lb, s);
+      return hip_status(e, "igc_grid_build: radix pass launch");
+    }
+    std::swap(src, dst);
+  }
+  dev_free(lb, s);
+  *result = src;
+  return IGC_OK;
+}
+
+PassSpec pass_spec(uint64_t varying) {
+  PassSpec ps{0, 0};
+  if (!varying) return ps;
+  const int lo = __builtin_ctzll(varying);
+  const int hi = 63 - __builtin_clzll(varying);
+  ps.lo_bit = lo;
+  ps.passes = (hi - lo + 8) / 8;
+  return ps;
+}
+
+// ------------------------------------------------------------------------------ counting
+
+// Block b counts, among keys [b*4096, (b+1)*4096), those that start a new voxel, leaf, lower
+// node and upper node. Counts are packed in 16-bit fields of one 64-bit word.
+__device__ __forceinline__ uint64_t start_flags(uint64_t key, uint64_t prev, bool first) {
+  if (first) return 0x0001000100010001ull;
+  return (uint64_t)(key != prev) | ((uint64_t)((key >> 9) != (prev >> 9)) << 16) |
+         ((uint64_t)((key >> 21) != (prev >> 21)) << 32) | ((uint64_t)((key >> 36) != (prev >> 36)) << 48);
+}
+
+__device__ __forceinline__ void stage_block(const uint64_t* __restrict__ keys, int64_t n, int64_t base,
+                                            uint64_t* s_keys, uint64_t* s_prev) {
+  for (int q = 0; q < kKeysPerThread; ++q) {
+    const int p = q * kThreads + threadIdx.x;
+    if (base + p < n) s_keys[p] = keys[base + p];
+  }
+  if (threadIdx.x == 0) *s_prev = base > 0 ? keys[base - 1] : 0ull;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void k_count(const uint64_t* __restrict__ keys, int64_t n,
+                                               uint64_t* __restrict__ block_counts) {
+  __shared__ uint64_t s_keys[kTileKeys];
+  __shared__ uint64_t s_prev;
+  __shared__ uint64_t s_tmp[4];
+  const int64_t base = (int64_t)blockIdx.x * kTileKeys;
+  stage_block(keys, n, base, s_keys, &s_prev);
+  uint64_t c = 0;
+  for (int q = 0; q < kKeysPerThread; ++q) {
+    const int p = threadIdx.x * kKeysPerThread + q;
+    const int64_t e = base + p;
+    if (e < n) c += start_flags(s_keys[p], p ? s_keys[p - 1] : s_prev, e == 0);
+  }
+  uint64_t total;
+  block_excl_scan64<kThreads>(c, s_tmp, &total);
+  if (threadIdx.x == 0) block_counts[blockIdx.x] = total;
+}
+
+// Exclusive scan of the per-block packed counts into four 64-bit prefixes per block, and the
+// totals N, F, Lw, U. One workgroup.
+__global__ __launch_bounds__(1024) void k_scan_blocks(const uint64_t* __restrict__ block_counts, int64_t nb,
+                                                      uint64_t* __restrict__ prefix, BuildState* st) {
+  __shared__ uint64_t s_tmp[16];
+  const int64_t per = (nb + 1023) / 1024;
+  const int64_t b0 = threadIdx.x * per;
+  uint64_t run[4] = {0, 0, 0, 0};
+  for (int64_t b = b0; b < b0 + per && b < nb; ++b)
+    for (int c = 0; c < 4; ++c) run[c] += (block_counts[b] >> (16 * c)) & 0xFFFFull;
+  uint64_t excl[4], tot[4];
+  for (int c = 0; c < 4; ++c) excl[c] = block_excl_scan64<1024>(run[c], s_tmp, &tot[c]);
+  for (int64_t b = b0; b < b0 + per && b < nb; ++b)
+    for (int c = 0; c < 4; ++c) {
+      prefix[b * 4 + c] = excl[c];
+      excl[c] += (block_counts[b] >> (16 * c)) & 0xFFFFull;
+    }
+  if (threadIdx.x == 0)
+    for (int c = 0; c < 4; ++c) st->counts[c] = tot[c];
+}
+
+// ------------------------------------------------------------------------------ registration
+
+struct Topo {
+  int64_t n_voxels, n_leaf, n_lower, n_upper;  // allocation sizes (bounds checks)
+  uint32_t* guard;
+  const uint64_t* tiles;  // [U] tile keys in rank order
+  uint64_t* root_list;
+  int4* upper_origin;
+  uint64_t* upper_mask;
+  uint32_t* upper_first;
+  int4* lower_origin;
+  uint64_t* lower_mask;
+  uint32_t* lower_first;
+  LeafRec* leaf;
+  int4* leaf_origin;
+};
+
+__device__ __forceinline__ int4 key_origin(uint64_t key, uint64_t tile, uint32_t clear_bits) {
+  const uint32_t up = (uint32_t)(key >> 21) & 0x7FFFu;
+  const uint32_t lo = (uint32_t)(key >> 9) & 0xFFFu;
+  const uint32_t lf = (uint32_t)key & 511u;
+  const uint32_t i = ((uint32_t)(tile >> 42) << 12) | ((up >> 10) << 7) | ((lo >> 8) << 3) | (lf >> 6);
+  const uint32_t j = ((uint32_t)((tile >> 21) & 0xFFFFFu) << 12) | (((up >> 5) & 31u) << 7) | (((lo >> 4) & 15u) << 3) |
+                     ((lf >> 3) & 7u);
+  const uint32_t k = ((uint32_t)(tile & 0xFFFFFu) << 12) | ((up & 31u) << 7) | ((lo & 15u) << 3) | (lf & 7u);
+  const uint32_t m = ~((1u << clear_bits) - 1u);
+  return make_int4((int32_t)(i & m), (int32_t)(j & m), (int32_t)(k & m), 0);
+}
+
+__global__ __launch_bounds__(256) void k_register(const uint64_t* __restrict__ keys, int64_t n,
+                                                  const uint64_t* __restrict__ prefix, Topo t) {
+  __shared__ uint64_t s_keys[kTileKeys];
+  __shared__ uint64_t s_prev;
+  __shared__ uint64_t s_tmp[4];
+  const int64_t base = (int64_t)blockIdx.x * kTileKeys;
+  stage_block(keys, n, base, s_keys, &s_prev);
+  const int p0 = threadIdx.x * kKeysPerThread;
+  uint64_t c = 0;
+  for (int q = 0; q < kKeysPerThread; ++q) {
+    const int64_t e = base + p0 + q;
+    if (e < n) c += start_flags(s_keys[p0 + q], (p0 + q) ? s_keys[p0 + q - 1] : s_prev, e == 0);
+  }
+  const uint64_t excl = block_excl_scan64<kThreads>(c, s_tmp, nullptr);
+  // Running inclusive counts; ids are count - 1.
+  int64_t nv = (int64_t)prefix[blockIdx.x * 4 + 0] + (int64_t)(excl & 0xFFFF);
+  int64_t nf = (int64_t)prefix[blockIdx.x * 4 + 1] + (int64_t)((excl >> 16) & 0xFFFF);
+  int64_t nl = (int64_t)prefix[blockIdx.x * 4 + 2] + (int64_t)((excl >> 32) & 0xFFFF);
+  int64_t nu = (int64_t)prefix[blockIdx.x * 4 + 3] + (int64_t)((excl >> 48) & 0xFFFF);
+
+  int64_t run_word = -1;  // leaf * 8 + word of the pending mask bits
+  uint64_t run_bits = 0;
+  for (int q = 0; q < kKeysPerThread; ++q) {
+    const int64_t e = base + p0 + q;
+    if (e >= n) break;
+    const uint64_t key = s_keys[p0 + q];
+    const uint64_t f = start_flags(key, (p0 + q) ? s_keys[p0 + q - 1] : s_prev, e == 0);
+    nv += (int64_t)(f & 1);
+    nf += (int64_t)((f >> 16) & 1);
+    nl += (int64_t)((f >> 32) & 1);
+    nu += (int64_t)((f >> 48) & 1);
+    const int64_t v = nv - 1, lf = nf - 1, lw = nl - 1, u = nu - 1;
+    if (v >= t.n_voxels || lf >= t.n_leaf || lw >= t.n_lower || u >= t.n_upper || (int64_t)(key >> 36) >= t.n_upper) {
+      atomicOr(t.guard, 1u);
+      break;
+    }
+    const uint64_t tile = t.tiles[key >> 36];
+    if ((f >> 48) & 1) {
+      t.root_list[u] = tile;
+      t.upper_origin[u] = key_origin(key, tile, 12);
+      t.upper_first[u] = (uint32_t)lw;
+    }
+    if ((f >> 32) & 1) {
+      const uint32_t cu = (uint32_t)(key >> 21) & 0x7FFFu;
+      atomicOr((unsigned long long*)&t.upper_mask[u * 512 + (cu >> 6)], 1ull << (cu & 63u));
+      t.lower_origin[lw] = key_origin(key, tile, 7);
+      t.lower_first[lw] = (uint32_t)lf;
+    }
+    if ((f >> 16) & 1) {
+      const uint32_t cl = (uint32_t)(key >> 9) & 0xFFFu;
+      atomicOr((unsigned long long*)&t.lower_mask[lw * 64 + (cl >> 6)], 1ull << (cl & 63u));
+      t.leaf[lf].offset = (uint64_t)v;
+      t.leaf_origin[lf] = key_origin(key, tile, 3);
+    }
+    const uint32_t vox = (uint32_t)key & 511u;
+    const int64_t word = lf * 8 + (vox >> 6);
+    if (word != run_word) {
+      if (run_word >= 0) atomicOr((unsigned long long*)&t.leaf[run_word >> 3].mask[run_word & 7], run_bits);
+      run_word = word;
+      run_bits = 0;
+    }
+    run_bits |= 1ull << (vox & 63u);
+  }
+  if (run_word >= 0) atomicOr((unsigned long long*)&t.leaf[run_word >> 3].mask[run_word & 7], run_bits);
+}
+
+// Packed 9-bit prefix counts of every leaf.
+__global__ void k_leaf_prefix(LeafRec* __restrict__ leaf, int64_t F) {
+  for (int64_t f = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; f < F; f += (int64_t)gridDim.x * blockDim.x) {
+    uint64_t packed = 0, run = 0;
+    for (int w = 1; w < 8; ++w) {
+      run += (uint64_t)__popcll(leaf[f].mask[w - 1]);
+      packed |= run << (9 * (w - 1));
+    }
+    leaf[f].prefix = packed;
+  }
+}
+
+// Per-word prefix counts of internal-node child masks: one wave per node.
+__global__ __launch_bounds__(256) void k_node_prefix(const uint64_t* __restrict__ mask, uint16_t* __restrict__ pre,
+                                                     int64_t nodes, int words) {
+  const int lane = lane_id();
+  const int64_t node = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (node >= nodes) return;
+  uint32_t base = 0;
+  for (int w0 = 0; w0 < words; w0 += 64) {
+    const uint32_t c = (uint32_t)__popcll(mask[node * words + w0 + lane]);
+    const uint32_t inc = wave_incl_scan(c);
+    pre[node * words + w0 + lane] = (uint16_t)(base + inc - c);
+    base += (uint32_t)__shfl((int)inc, 63, 64);
+  }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------ host side
+
+// Temporary device buffers of one build, released (stream-ordered) on every exit path.
+struct Temps {
+  hipStream_t s;
+  std::vector<void*> p;
+  explicit Temps(hipStream_t st) : s(st) {}
+  ~Temps() {
+    for (auto it = p.rbegin(); it != p.rend(); ++it) dev_free(*it, s);
+  }
+  template <class T>
+  int get(T** out, size_t bytes, const char* what) {
+    const int rc = dev_alloc((void**)out, bytes, s, what);
+    if (rc == IGC_OK) p.push_back(*out);
+    return rc;
+  }
+};
+
+int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
+  g->n_input = n_in;
+  if (n_in == 0) return IGC_OK;
+  Temps tmp(s);
+
+  BuildState* st = nullptr;
+  int rc = tmp.get(&st, sizeof(BuildState), "igc_grid_build: state");
+  if (rc) return rc;
+  BuildState* h = (BuildState*)host_staging(sizeof(BuildState));
+  if (!h) return set_error(IGC_ERR_OOM, "igc_grid_build: pinned staging buffer");
+
+  // Root table: first capacity from an estimate, then the size that always suffices.
+  uint64_t full_cap = 16;
+  while (full_cap < 2ull * (uint64_t)n_in) full_cap <<= 1;
+  uint64_t cap = std::min<uint64_t>(full_cap, 1ull << 16);
+  if (const char* e = std::getenv("IGC_TEST_INITIAL_CAPACITY")) {
+    uint64_t want = std::strtoull(e, nullptr, 10);
+    cap = 1;
+    while (cap < want) cap <<= 1;
+  }
+  uint64_t* root_keys = nullptr;
+  for (int attempt = 0;; ++attempt) {
+    k_init_state<<<1, 1, 0, s>>>(st);
+    IGC_HIP(hipGetLastError(), "igc_grid_build: init launch");
+    rc = dev_alloc((void**)&root_keys, cap * sizeof(uint64_t), s, "igc_grid_build: root table");
+    if (rc) return rc;
+    g->root_keys = root_keys;
+    if ((rc = fill_u64(root_keys, (int64_t)cap, kEmptyKey, s))) return rc;
+    const uint32_t limit = (uint32_t)std::min<uint64_t>(cap, 4096);
+    k_tile_insert<<<grid_for(n_in, 256, 2048), 256, 0, s>>>(d_ijk, n_in, root_keys, (uint32_t)(cap - 1), limit, st);
+    IGC_HIP(hipGetLastError(), "igc_grid_build: tile insert launch");
+    IGC_HIP(hipMemcpyAsync(h, st, sizeof(BuildState), hipMemcpyDeviceToHost, s), "igc_grid_build: read tile count");
+    IGC_HIP(hipStreamSynchronize(s), "igc_grid_build: tile pass");
+    if (!h->overflow) break;
+    dev_free(root_keys, s);
+    root_keys = nullptr;
+    g->root_keys = nullptr;
+    if (cap >= full_cap || attempt >= 2)
+      return set_error(IGC_ERR_CAPACITY, "igc_grid_build: root table overflow after retries");
+    cap = full_cap;
+  }
+  const int64_t U = h->n_tiles;
+  const uint64_t off_var = h->off_or ^ h->off_and;
+  const uint64_t key_var = h->key_or ^ h->key_and;
+  if (U < 1 || (uint64_t)U > (1ull << 27))
+    return set_error(U < 1 ? IGC_ERR_INTERNAL : IGC_ERR_RANGE, "igc_grid_build: root tile count out of range");
+
+  int32_t* root_vals = nullptr;
+  uint64_t *tile_list = nullptr, *tile_tmp = nullptr;
+  if ((rc = dev_alloc((void**)&root_vals, cap * sizeof(int32_t), s, "igc_grid_build: root values"))) return rc;
+  g->root_vals = root_vals;
+  if ((rc = tmp.get(&tile_list, U * sizeof(uint64_t), "igc_grid_build: tile list"))) return rc;
+  if ((rc = tmp.get(&tile_tmp, U * sizeof(uint64_t), "igc_grid_build: tile list"))) return rc;
+  k_tile_compact<<<grid_for((int64_t)cap, 256, 1024), 256, 0, s>>>(root_keys, (uint32_t)cap, tile_list, (uint32_t)U,
+                                                                   st);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: tile compaction launch");
+  uint64_t* tiles_sorted = tile_tmp;
+  uint32_t* hist = nullptr;
+  if ((rc = tmp.get(&hist, 2 * kMaxPasses * 256 * sizeof(uint32_t), "igc_grid_build: histograms")))
+    return rc;
+  if ((rc = fill_u64((uint64_t*)hist, kMaxPasses * 256, 0, s))) return rc;
+  if (U <= kSmallSort) {
+    k_sort_small<<<1, 1024, 0, s>>>(tile_list, tile_tmp, (int)U);
+    IGC_HIP(hipGetLastError(), "igc_grid_build: tile sort launch");
+  } else {
+    const PassSpec tps = pass_spec(key_var);
+    k_hist<<<grid_for(U, 256, 1024), 256, 0, s>>>(tile_list, U, tps, hist + kMaxPasses * 256);
+    IGC_HIP(hipGetLastError(), "igc_grid_build: tile histogram launch");
+    if ((rc = onesweep_sort(tile_list, tile_tmp, U, tps, hist + kMaxPasses * 256, st->tile_counter + kMaxPasses,
+                            &st->lookback_timeout, &st->guard, s, &tiles_sorted)))
+      return rc;
+  }
+  k_tile_rank<<<grid_for(U, 256, 1024), 256, 0, s>>>(tiles_sorted, U, root_keys, root_vals, (uint32_t)(cap - 1), st);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: tile rank launch");
+
+  // key2 and its sort.
+  int rank_bits = 0;
+  while ((1ll << rank_bits) < U) ++rank_bits;
+  const uint64_t varying = off_var | (rank_bits ? (((1ull << rank_bits) - 1ull) << 36) : 0ull);
+  const PassSpec ps = pass_spec(varying);
+  uint64_t *ka = nullptr, *kb = nullptr;
+  if ((rc = tmp.get(&ka, n_in * sizeof(uint64_t), "igc_grid_build: keys"))) return rc;
+  if ((rc = tmp.get(&kb, n_in * sizeof(uint64_t), "igc_grid_build: keys"))) return rc;
+  k_key2<<<grid_for(n_in, 256, 2048), 256, 0, s>>>(d_ijk, n_in, root_keys, root_vals, (uint32_t)(cap - 1), ka, ps,
+                                                   hist, st);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: key pass launch");
+  uint64_t* sorted = ka;
+  if ((rc = onesweep_sort(ka, kb, n_in, ps, hist, st->tile_counter, &st->lookback_timeout, &st->guard, s, &sorted)))
+    return rc;
+
+  // Counts, then the one read-back that sizes the topology.
+  const int64_t nb = (n_in + kTileKeys - 1) / kTileKeys;
+  uint64_t *bcounts = nullptr, *bprefix = nullptr;
+  if ((rc = tmp.get(&bcounts, nb * sizeof(uint64_t), "igc_grid_build: block counts"))) return rc;
+  if ((rc = tmp.get(&bprefix, nb * 4 * sizeof(uint64_t), "igc_grid_build: block prefixes"))) return rc;
+  k_count<<<(unsigned)nb, kThreads, 0, s>>>(sorted, n_in, bcounts);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: count launch");
+  k_scan_blocks<<<1, 1024, 0, s>>>(bcounts, nb, bprefix, st);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: block scan launch");
+  IGC_HIP(hipMemcpyAsync(h, st, sizeof(BuildState), hipMemcpyDeviceToHost, s), "igc_grid_build: read counts");
+  IGC_HIP(hipStreamSynchronize(s), "igc_grid_build: sort and count");
+  if (h->lookback_timeout) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: radix sort look-back timed out");
+  if (h->guard) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: device bounds check failed before registration");
+  const int64_t N = (int64_t)h->counts[0], F = (int64_t)h->counts[1], Lw = (int64_t)h->counts[2];
+  if ((int64_t)h->counts[3] != U || N < 1 || N > n_in || F > N || Lw > F)
+    return set_error(IGC_ERR_INTERNAL, "igc_grid_build: inconsistent node counts");
+
+  // Topology block.
+  size_t off = 0;
+  auto carve = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t o_root_list = carve(U * 8), o_upo = carve(U * 16), o_upm = carve(U * 512 * 8),
+               o_upp = carve(U * 512 * 2), o_upf = carve(U * 4), o_loo = carve(Lw * 16), o_lom = carve(Lw * 64 * 8),
+               o_lop = carve(Lw * 64 * 2), o_lof = carve(Lw * 4), o_leaf = carve(F * sizeof(LeafRec)),
+               o_lfo = carve(F * 16);
+  char* blk = nullptr;
+  if ((rc = dev_alloc((void**)&blk, off, s, "igc_grid_build: topology"))) return rc;
+  g->block = blk;
+  g->bytes = off + cap * 12;
+  g->root_keys = root_keys;
+  g->root_vals = root_vals;
+  g->root_cap = (uint32_t)cap;
+  g->root_list = (uint64_t*)(blk + o_root_list);
+  g->upper_origin = (int4*)(blk + o_upo);
+  g->upper_mask = (uint64_t*)(blk + o_upm);
+  g->upper_pre = (uint16_t*)(blk + o_upp);
+  g->upper_first = (uint32_t*)(blk + o_upf);
+  g->lower_origin = (int4*)(blk + o_loo);
+  g->lower_mask = (uint64_t*)(blk + o_lom);
+  g->lower_pre = (uint16_t*)(blk + o_lop);
+  g->lower_first = (uint32_t*)(blk + o_lof);
+  g->leaf = (LeafRec*)(blk + o_leaf);
+  g->leaf_origin = (int4*)(blk + o_lfo);
+  g->n_voxels = N;
+  g->n_leaf = F;
+  g->n_lower = Lw;
+  g->n_upper = U;
+  g->sort_passes = ps.passes;
+  if ((rc = fill_u64(g->upper_mask, U * 512, 0, s))) return rc;
+  if ((rc = fill_u64(g->lower_mask, Lw * 64, 0, s))) return rc;
+  if ((rc = fill_u64((uint64_t*)g->leaf, F * (int64_t)(sizeof(LeafRec) / 8), 0, s))) return rc;
+
+  Topo t{N,           F,           Lw,           U,          &st->guard,     tiles_sorted,
+         g->root_list, g->upper_origin, g->upper_mask, g->upper_first, g->lower_origin, g->lower_mask,
+         g->lower_first, g->leaf,     g->leaf_origin};
+  k_register<<<(unsigned)nb, kThreads, 0, s>>>(sorted, n_in, bprefix, t);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: register launch");
+  k_leaf_prefix<<<grid_for(F, 256, 4096), 256, 0, s>>>(g->leaf, F);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: leaf prefix launch");
+  k_node_prefix<<<(unsigned)((Lw + 3) / 4), 256, 0, s>>>(g->lower_mask, g->lower_pre, Lw, 64);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: lower prefix launch");
+  k_node_prefix<<<(unsigned)((U + 3) / 4), 256, 0, s>>>(g->upper_mask, g->upper_pre, U, 512);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: upper prefix launch");
+
+  return IGC_OK;
+}
+
+}  // namespace igc

@@ -1,0 +1,91 @@
+// Host-side internals of libigconv: the grid object, error reporting and allocation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/igconv.h"
+#include "igc_internal.h"
+
+struct igc_grid {
+  int device = 0;
+  hipStream_t stream = nullptr;  // stream the grid was built on (destroy waits for it)
+  int64_t n_input = 0, n_voxels = 0, n_leaf = 0, n_lower = 0, n_upper = 0;
+  int32_t sort_passes = 0;
+  uint32_t root_cap = 0;
+  size_t bytes = 0;
+  void* block = nullptr;  // one device allocation holding every array below
+
+  uint64_t* root_keys = nullptr;   // [root_cap]
+  int32_t* root_vals = nullptr;    // [root_cap]
+  uint64_t* root_list = nullptr;   // [U] tile keys in upper-node order
+  int4* upper_origin = nullptr;    // [U]
+  uint64_t* upper_mask = nullptr;  // [U*512]
+  uint16_t* upper_pre = nullptr;   // [U*512]
+  uint32_t* upper_first = nullptr; // [U]
+  int4* lower_origin = nullptr;    // [Lw]
+  uint64_t* lower_mask = nullptr;  // [Lw*64]
+  uint16_t* lower_pre = nullptr;   // [Lw*64]
+  uint32_t* lower_first = nullptr; // [Lw]
+  igc::LeafRec* leaf = nullptr;    // [F]
+  int4* leaf_origin = nullptr;     // [F]
+
+  igc::GridView view() const {
+    igc::GridView v;
+    v.root_keys = root_keys;
+    v.root_vals = root_vals;
+    v.root_mask = root_cap ? root_cap - 1u : 0u;
+    v.upper_mask = upper_mask;
+    v.upper_pre = upper_pre;
+    v.upper_first = upper_first;
+    v.lower_mask = lower_mask;
+    v.lower_pre = lower_pre;
+    v.lower_first = lower_first;
+    v.leaf = leaf;
+    v.leaf_origin = leaf_origin;
+    v.n_voxels = n_voxels;
+    v.n_leaf = n_leaf;
+    return v;
+  }
+};
+
+namespace igc {
+
+// Records the message for igc_last_error and returns the status.
+int set_error(int status, const std::string& msg);
+void clear_error();
+
+// Status from a HIP call, with the call site named in the message.
+int hip_status(hipError_t e, const char* what);
+
+#define IGC_HIP(call, what)                                   \
+  do {                                                        \
+    hipError_t e_ = (call);                                   \
+    if (e_ != hipSuccess) return ::igc::hip_status(e_, what); \
+  } while (0)
+
+// Stream-ordered device allocation from the device's memory pool (kept across calls).
+int dev_alloc(void** p, size_t bytes, hipStream_t s, const char* what);
+void dev_free(void* p, hipStream_t s);
+
+// Pinned host staging buffer of at least `bytes` for small device -> host reads.
+void* host_staging(size_t bytes);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Launchers (defined in the .hip files).
+int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g);
+int launch_active_ijk(const igc_grid* g, int32_t* d_out, hipStream_t s);
+int launch_ijk_to_index(const igc_grid* g, const int32_t* d_q, int64_t m, int32_t* d_idx, hipStream_t s);
+int launch_kernel_map(const igc_grid* g, const int32_t* h_offsets, int32_t K, int32_t* d_map, uint32_t* d_nbmask,
+                      hipStream_t s);
+bool leaf_conv_supported(int32_t dtype, int32_t cin, int32_t cout);
+bool ggs_conv_supported(int32_t dtype, int32_t cin, int32_t cout);
+int launch_conv_leaf(const igc_grid* g, const void* d_feats, int32_t dtype, int32_t cin, const void* d_w, int32_t cout,
+                     void* d_out, hipStream_t s);
+int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype, int32_t cin,
+                    const void* d_w, int32_t cout, void* d_out, hipStream_t s);
+
+}  // namespace igc

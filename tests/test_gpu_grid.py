@@ -1,0 +1,167 @@
+"""GPU parity of the IndexGrid build, the index query and the kernel map against the CPU
+oracle: bit-exact topology, row order, indices and maps."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._gpu import assert_topology_equal, require_gpu, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _igc():
+    import sparse_convolution_amd as igc
+    return igc
+
+
+def check_grid(coords: np.ndarray, name: str, offsets=None, queries: np.ndarray | None = None):
+    igc = _igc()
+    say(f"build {name} n_in={coords.shape[0]}")
+    g = igc.grid_build(to_dev(coords))
+    torch.cuda.synchronize()
+    ref = oracle.OracleGrid(coords)
+    assert (g.n_voxels, g.n_leaf, g.n_lower, g.n_upper) == (ref.n, ref.n_leaf, ref.n_lower, ref.n_upper)
+    assert_topology_equal(g.export(), ref.topology())
+    say(f"active_ijk / ijk_to_index {name}")
+    act = g.active_ijk().cpu().numpy()
+    assert np.array_equal(act, ref.active_ijk())
+    q = coords if queries is None else np.concatenate([coords, queries])
+    got = g.ijk_to_index(to_dev(q)).cpu().numpy()
+    assert np.array_equal(got, ref.ijk_to_index(q))
+    say(f"kernel_map {name}")
+    m, nb = igc.kernel_map(g, offsets, with_mask=True) if (offsets is None or len(offsets) <= 32) else (
+        igc.kernel_map(g, offsets), None)
+    mr, nbr = ref.kernel_map(offsets, with_mask=True)
+    assert np.array_equal(m.cpu().numpy(), mr)
+    if nb is not None:
+        assert np.array_equal(nb.cpu().numpy().view(np.uint32), nbr)
+    return g, ref
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_random_signed_with_duplicates(seed):
+    rng = np.random.default_rng(seed)
+    # clusters straddling tile / node boundaries and the sign change, plus scattered points
+    centres = np.array([[0, 0, 0], [4096, -4096, 128], [-1, 2047, -2049], [123457, -98765, 5]])
+    parts = [c + rng.integers(-40, 41, size=(20000, 3)) for c in centres]
+    parts.append(rng.integers(-2**20, 2**20, size=(3001, 3)))
+    c = np.concatenate(parts).astype(np.int32)
+    c = np.concatenate([c, c[rng.integers(0, c.shape[0], 7777)]])
+    c = c[rng.permutation(c.shape[0])]
+    q = rng.integers(-50, 50, size=(5000, 3)).astype(np.int32)
+    check_grid(c, f"random seed {seed}", queries=q)
+
+
+def test_tiny_workload():
+    check_grid(workloads.make_coords("tiny"), "tiny")
+
+
+def test_leaf_workload():
+    check_grid(workloads.make_coords("leaf"), "leaf")
+
+
+def test_lidar_workload():
+    check_grid(workloads.make_coords("lidar"), "lidar")
+
+
+def test_band_workload():
+    check_grid(workloads.make_coords("band"), "band")
+
+
+def test_all_identical():
+    check_grid(np.tile(np.array([[-7, 3, 100000]], np.int32), (10000, 1)), "identical")
+
+
+def test_sorted_and_reverse_sorted_inputs():
+    g3 = np.stack(np.meshgrid(np.arange(40), np.arange(40), np.arange(40), indexing="ij"), -1).reshape(-1, 3)
+    c = (g3 - 20).astype(np.int32)
+    check_grid(c, "sorted")
+    check_grid(c[::-1].copy(), "reverse")
+
+
+def test_one_voxel_per_leaf_and_full_leaves():
+    rng = np.random.default_rng(5)
+    origins = np.unique(rng.integers(-300, 300, size=(3000, 3)) * 8, axis=0)
+    one = (origins + rng.integers(0, 8, size=origins.shape)).astype(np.int32)
+    check_grid(one, "one per leaf")
+    g3 = np.stack(np.meshgrid(np.arange(8), np.arange(8), np.arange(8), indexing="ij"), -1).reshape(-1, 3)
+    full = (origins[:200, None, :] + g3[None]).reshape(-1, 3).astype(np.int32)
+    check_grid(full[rng.permutation(full.shape[0])], "full leaves")
+
+
+def test_int32_extremes():
+    M, m = 2**31 - 1, -2**31
+    c = np.array([[M, M, M], [m, m, m], [M, 0, m], [m, M, 0], [M - 1, M, M], [m + 1, m, m], [0, 0, 0], [-1, -1, -1],
+                  [M, M - 8, M], [m, m + 8, m]], np.int32)
+    check_grid(c, "int32 extremes")
+
+
+def test_general_offsets():
+    rng = np.random.default_rng(9)
+    c = (rng.integers(-30, 30, size=(20000, 3))).astype(np.int32)
+    d = np.arange(-2, 3)
+    off = np.stack(np.meshgrid(d, d, d, indexing="ij"), -1).reshape(-1, 3).astype(np.int32)  # 5x5x5
+    check_grid(c, "5x5x5 offsets", offsets=off)
+    off8 = np.array([[8, 0, 0], [-8, 8, -8], [7, -7, 1], [0, 0, 0]], np.int32)
+    check_grid(c, "offsets up to 8", offsets=off8)
+
+
+def test_capacity_retry(monkeypatch):
+    monkeypatch.setenv("IGC_TEST_INITIAL_CAPACITY", "1")
+    rng = np.random.default_rng(13)
+    c = rng.integers(-2**24, 2**24, size=(5000, 3)).astype(np.int32)  # ~5000 root tiles
+    g, _ = check_grid(c, "root table retry")
+    assert g.root_capacity >= 2 * g.n_upper
+
+
+def test_many_tiles_radix_tile_sort():
+    # more than 4096 distinct root tiles: the tile keys go through the radix sort too
+    rng = np.random.default_rng(17)
+    c = rng.integers(-2**30, 2**30, size=(60000, 3)).astype(np.int32)
+    check_grid(c, "many tiles")
+
+
+def test_empty_grid():
+    igc = _igc()
+    say("empty grid")
+    g = igc.grid_build(torch.zeros((0, 3), dtype=torch.int32, device="cuda"))
+    assert (g.n_voxels, g.n_leaf, g.n_lower, g.n_upper) == (0, 0, 0, 0)
+    assert igc.kernel_map(g).shape == (27, 0)
+    idx = g.ijk_to_index(torch.tensor([[0, 0, 0]], dtype=torch.int32, device="cuda"))
+    assert idx.cpu().tolist() == [-1]
+
+
+def test_deterministic():
+    igc = _igc()
+    c = workloads.make_coords("lidar")
+    say("determinism lidar")
+    a = igc.grid_build(to_dev(c))
+    b = igc.grid_build(to_dev(c))
+    ta, tb = a.export(), b.export()
+    for k in ta:
+        assert np.array_equal(ta[k], tb[k])
+    assert torch.equal(igc.kernel_map(a), igc.kernel_map(b))
+
+
+def test_errors():
+    igc = _igc()
+    from sparse_convolution_amd import _lib
+    lib = _lib.load()
+    import ctypes
+    h = ctypes.c_void_p()
+    assert lib.igc_grid_build(None, 5, None, ctypes.byref(h)) == 1
+    assert b"d_ijk" in lib.igc_last_error()
+    assert lib.igc_grid_build(None, -1, None, ctypes.byref(h)) == 1
+    g = igc.grid_build(to_dev(np.array([[1, 2, 3]], np.int32)))
+    off = np.array([[9, 0, 0]], np.int32)
+    with pytest.raises(igc.IgcError):
+        igc.kernel_map(g, off)
