@@ -1,0 +1,152 @@
+"""GPU parity of the submanifold convolution (leaf path, fp32; gather-GEMM-scatter path,
+bf16 with fp32 accumulation) against the float64 CPU oracle.
+
+Tolerances (normwise, max|y - r| / max|r| over the output): 1e-5 for fp32 and 2e-2 for bf16,
+where the oracle reads exactly the bf16 values the GPU reads. Both paths must run: the
+path is forced explicitly in every case.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._gpu import normwise_error, require_gpu, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _igc():
+    import sparse_convolution_amd as igc
+    return igc
+
+
+def _inputs(n, cin, cout, dtype, seed, std=None):
+    f = workloads.make_features(n, cin, 3000 + seed)
+    w = workloads.make_weights(cin, cout, 4000 + seed, std)
+    ft = torch.from_numpy(f).to(dtype)
+    wt = torch.from_numpy(w).to(dtype)
+    return ft, wt
+
+
+def run_conv(coords, cin, cout, dtype, path, name, seed=0, std=None, sample_rows=None):
+    igc = _igc()
+    say(f"conv {name} path={path} {dtype} {cin}->{cout} n_in={coords.shape[0]}")
+    g = igc.grid_build(to_dev(coords))
+    m = igc.kernel_map(g)
+    ft, wt = _inputs(g.n_voxels, cin, cout, dtype, seed, std)
+    y = igc.sparse_conv(g, ft.cuda(), wt.cuda(), kmap=m, path=path)
+    torch.cuda.synchronize()
+    ref_grid = oracle.OracleGrid(coords)
+    mr = ref_grid.kernel_map()
+    rows = None
+    if sample_rows is not None and sample_rows < g.n_voxels:
+        rows = np.sort(np.random.default_rng(seed + 77).choice(g.n_voxels, sample_rows, replace=False))
+        rows = np.concatenate([rows, [0, g.n_voxels - 1]])
+    r = oracle.conv(mr, ft.float().numpy(), wt.float().numpy(), rows=rows)
+    yy = y.float().cpu().numpy()
+    if rows is not None:
+        yy = yy[rows]
+    err = normwise_error(yy, r)
+    say(f"  normwise error {err:.3e}")
+    assert np.all(np.isfinite(yy))
+    assert err <= TOL[dtype], f"normwise error {err} > {TOL[dtype]}"
+    return g, y
+
+
+def _cluster_coords(n_clusters, size, spread, seed, fill=0.35):
+    rng = np.random.default_rng(seed)
+    parts = []
+    for _ in range(n_clusters):
+        c = rng.integers(-spread, spread, size=3)
+        cube = np.stack(np.meshgrid(*[np.arange(size)] * 3, indexing="ij"), -1).reshape(-1, 3)
+        keep = rng.random(cube.shape[0]) < fill
+        parts.append(cube[keep] + c)
+    return np.concatenate(parts).astype(np.int32)
+
+
+@pytest.mark.parametrize("cin,cout", [(4, 8), (8, 8), (8, 16), (8, 32), (16, 16), (4, 32)])
+def test_leaf_path_shapes(cin, cout):
+    c = _cluster_coords(6, 20, 200, seed=cin * 100 + cout)
+    run_conv(c, cin, cout, torch.float32, "leaf", "clusters", seed=cin + cout)
+
+
+@pytest.mark.parametrize("cin,cout", [(32, 64), (64, 64), (64, 128), (128, 128), (128, 256), (96, 192)])
+def test_ggs_path_shapes(cin, cout):
+    c = _cluster_coords(5, 24, 300, seed=cin + cout, fill=0.2)
+    run_conv(c, cin, cout, torch.bfloat16, "ggs", "clusters", seed=cin * 3 + cout, std=1.0 / np.sqrt(27 * cin))
+
+
+def test_tiny_workload_leaf():
+    w = workloads.WORKLOADS["tiny"]
+    run_conv(workloads.make_coords("tiny"), w.cin, w.cout, torch.float32, "leaf", "tiny", seed=w.index)
+
+
+def test_leaf_workload_leaf():
+    w = workloads.WORKLOADS["leaf"]
+    run_conv(workloads.make_coords("leaf"), w.cin, w.cout, torch.float32, "leaf", "leaf", seed=w.index,
+             std=w.weight_std)
+
+
+def test_lidar_workload_ggs():
+    w = workloads.WORKLOADS["lidar"]
+    run_conv(workloads.make_coords("lidar"), w.cin, w.cout, torch.bfloat16, "ggs", "lidar", seed=w.index,
+             std=w.weight_std)
+
+
+def test_band_workload_ggs_sampled():
+    w = workloads.WORKLOADS["band"]
+    run_conv(workloads.make_coords("band"), w.cin, w.cout, torch.bfloat16, "ggs", "band", seed=w.index,
+             std=w.weight_std, sample_rows=1 << 16)
+
+
+def test_identity_kernel_both_paths():
+    igc = _igc()
+    c = _cluster_coords(3, 16, 100, seed=3)
+    g = igc.grid_build(to_dev(c))
+    m = igc.kernel_map(g)
+    say("identity kernels")
+    f32 = torch.randn(g.n_voxels, 8, device="cuda")
+    w32 = torch.zeros(27, 8, 8, device="cuda")
+    w32[13] = torch.eye(8, device="cuda")
+    assert torch.equal(igc.sparse_conv(g, f32, w32, path="leaf"), f32)
+    f16 = torch.randn(g.n_voxels, 64, device="cuda").bfloat16()
+    w16 = torch.zeros(27, 64, 64, device="cuda", dtype=torch.bfloat16)
+    w16[13] = torch.eye(64, device="cuda", dtype=torch.bfloat16)
+    assert torch.equal(igc.sparse_conv(g, f16, w16, kmap=m, path="ggs"), f16)
+
+
+def test_path_selection_and_errors():
+    igc = _igc()
+    g = igc.grid_build(to_dev(workloads.make_coords("tiny")))
+    assert g.select_path(torch.float32, 8, 8) == "leaf"
+    assert g.select_path(torch.bfloat16, 64, 64) == "ggs"
+    f = torch.randn(g.n_voxels, 8, device="cuda")
+    w = torch.randn(27, 8, 8, device="cuda")
+    with pytest.raises(igc.IgcError):
+        igc.sparse_conv(g, f, w, path="ggs")  # fp32 is not a gather-GEMM-scatter dtype
+    fb = torch.randn(g.n_voxels, 64, device="cuda").bfloat16()
+    wb = torch.randn(27, 64, 64, device="cuda").bfloat16()
+    with pytest.raises(igc.IgcError):
+        igc.sparse_conv(g, fb, wb, path="ggs")  # no map
+    with pytest.raises(igc.IgcError):
+        igc.sparse_conv(g, torch.randn(g.n_voxels, 5, device="cuda"), torch.randn(27, 5, 8, device="cuda"))
+
+
+def test_conv_deterministic():
+    igc = _igc()
+    c = workloads.make_coords("lidar")
+    g = igc.grid_build(to_dev(c))
+    m = igc.kernel_map(g)
+    ft, wt = _inputs(g.n_voxels, 128, 128, torch.bfloat16, 4, 0.03)
+    say("determinism ggs")
+    a = igc.sparse_conv(g, ft.cuda(), wt.cuda(), kmap=m, path="ggs")
+    b = igc.sparse_conv(g, ft.cuda(), wt.cuda(), kmap=m, path="ggs")
+    assert torch.equal(a, b)
