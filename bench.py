@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Throughput of the IndexGrid hot path on one MI355X.
+
+One step = the whole path over one synthetic scene already resident in HBM: build the
+IndexGrid from the shuffled coordinates (tile hash, radix sort, node registration), the
+27-offset kernel map, and the 3x3x3 submanifold convolution on the automatically chosen
+path. Prints one JSON line.
+
+    python bench.py [--workload leaf] [--steps K] [--warmup W] [--gpus 1]
+
+value = effective conv FLOPs (2 * pairs * cin * cout, empty MACs excluded, as the fVDB notes
+define effective TFLOPS in their micro-benchmarks) per second of the whole step. The line also
+carries per-phase times, the build rate in Mvox/s, the roofline of the dominant kernel (the
+convolution) timed with HIP events on its launch stream, and the CPU oracle timed on the host
+cores as a reference point.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-conv effective TFLOP/s (2·pairs·Cin·Cout/s) + IndexGrid build Mvox/s"
+HBM_PEAK_GBS = 8000.0
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}  # dense MFMA peaks of MI355X
+CONV_SRC = {"leaf": "sparse_convolution_amd/csrc/igc_conv_leaf.hip",
+            "ggs": "sparse_convolution_amd/csrc/igc_conv_ggs.hip"}
+CONV_KERNEL = {"leaf": "k_conv_leaf_f32", "ggs": "k_conv_ggs_bf16"}
+DEFAULT_STEPS = {"tiny": (50, 5), "leaf": (20, 3), "band": (10, 2), "lidar": (20, 3), "large": (3, 1)}
+
+
+def _sha(path: str) -> str:
+    with open(os.path.join(ROOT, path), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def _traffic(path_name: str, workload: str):
+    """Measured HBM bytes per launch of the conv kernel, if the committed counter summary was
+    taken on the current kernel source; None otherwise."""
+    f = os.path.join(ROOT, "profiles", f"traffic_{CONV_KERNEL[path_name]}_{workload}.json")
+    if not os.path.exists(f):
+        return None
+    with open(f) as fh:
+        d = json.load(fh)
+    if d.get("source_sha") != _sha(CONV_SRC[path_name]):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def _pct(a, q):
+    return float(np.percentile(np.asarray(a), q)) if len(a) else None
+
+
+def copy_calibration(gib: float = 2.0, reps: int = 5) -> None:
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": 4 * n, "reps": reps}))
+
+
+def cpu_baseline(coords, wl, cin, cout, dtype_name, min_seconds=10.0):
+    """The CPU oracle (as written, untuned) on a bounded sample of the same workload."""
+    import oracle
+    import workloads
+    max_coords = 4_000_000
+    sample = coords[:max_coords]
+    t0 = time.perf_counter()
+    g = oracle.OracleGrid(sample)
+    t_build = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    m = g.kernel_map()
+    t_kmap = time.perf_counter() - t0
+    pairs = int((m >= 0).sum())
+    mean_pairs = pairs / max(g.n, 1)
+    rows_max = max(1024, int(2e10 / max(mean_pairs * cin * cout, 1)))
+    f = workloads.make_features(g.n, cin, 3000 + wl.index)
+    w = workloads.make_weights(cin, cout, 4000 + wl.index, wl.weight_std)
+    if dtype_name == "bf16":
+        import torch
+        f = torch.from_numpy(f).bfloat16().float().numpy()
+        w = torch.from_numpy(w).bfloat16().float().numpy()
+    rows = None
+    if g.n > rows_max:
+        rows = np.sort(np.random.default_rng(7).choice(g.n, rows_max, replace=False))
+    t0 = time.perf_counter()
+    oracle.conv(m, f, w, rows=rows)
+    t_conv = time.perf_counter() - t0
+    n_rows = g.n if rows is None else rows.shape[0]
+    t_conv_all = t_conv * g.n / n_rows
+    total = t_build + t_kmap + t_conv_all
+    flops = 2.0 * pairs * cin * cout
+    desc = (f"oracle build + kernel map on the first {sample.shape[0]} of {coords.shape[0]} input coordinates "
+            f"({g.n} voxels), conv on {n_rows} of those rows")
+    if rows is not None:
+        desc += " (conv time scaled to all rows)"
+    desc += f"; build {t_build:.2f} s, kernel map {t_kmap:.2f} s, conv {t_conv_all:.2f} s"
+    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": desc, "build_mvox_s": sample.shape[0] / t_build / 1e6}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="leaf", choices=["tiny", "leaf", "band", "lidar", "large"])
+    ap.add_argument("--path", default="auto", choices=["auto", "leaf", "ggs"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding of this "
+              "path is a design note, not an implemented mode.", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    import torch
+    import sparse_convolution_amd as igc
+    import workloads
+
+    wl = workloads.WORKLOADS[args.workload]
+    steps, warmup = DEFAULT_STEPS[args.workload]
+    steps = args.steps if args.steps is not None else steps
+    warmup = args.warmup if args.warmup is not None else warmup
+    tdtype = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+
+    coords = workloads.make_coords(args.workload)
+    dev = torch.device("cuda", 0)
+    coords_d = torch.from_numpy(coords).to(dev)
+    g0 = igc.grid_build(coords_d)
+    N = g0.n_voxels
+    feats = torch.from_numpy(workloads.make_features(N, wl.cin, 3000 + wl.index)).to(dev, tdtype)
+    weights = torch.from_numpy(workloads.make_weights(wl.cin, wl.cout, 4000 + wl.index, wl.weight_std)).to(dev, tdtype)
+    m0 = igc.kernel_map(g0)
+    pairs = int((m0 >= 0).sum().item())
+    path = g0.select_path(tdtype, wl.cin, wl.cout) if args.path == "auto" else args.path
+    info = dict(n_input=g0.n_input, n_voxels=N, n_leaf=g0.n_leaf, n_lower=g0.n_lower, n_upper=g0.n_upper,
+                sort_passes=g0.sort_passes, leaf_occupancy=round(g0.leaf_occupancy, 4))
+    out = torch.empty((N, wl.cout), dtype=tdtype, device=dev)
+    del m0, g0
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev):
+        ev[0].record(stream)
+        g = igc.grid_build(coords_d)
+        ev[1].record(stream)
+        m = igc.kernel_map(g)
+        ev[2].record(stream)
+        igc.sparse_conv(g, feats, weights, kmap=m, path=path, out=out)
+        ev[3].record(stream)
+        return g, m
+
+    for _ in range(warmup):
+        step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    keep = None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        keep = step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del keep
+
+    t_build = [e[0].elapsed_time(e[1]) for e in events]
+    t_kmap = [e[1].elapsed_time(e[2]) for e in events]
+    t_conv = [e[2].elapsed_time(e[3]) for e in events]
+    ms_step = wall * 1e3 / steps
+    flops = 2.0 * pairs * wl.cin * wl.cout
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    conv_ms = float(np.mean(t_conv))
+    conv_tflops = flops / (conv_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+    roofline = {"bound": "mfma", "achieved": round(conv_tflops, 3), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(conv_tflops / peak, 4), "traffic": _traffic(path, args.workload),
+                "kernel": CONV_KERNEL[path], "flops_per_launch": flops,
+                "avg_launch_ms": round(conv_ms, 4)}
+
+    # Phase-level HBM view (algorithmic bytes; see the design notes for the per-unit figures).
+    esize = 4 if wl.dtype == "f32" else 2
+    kmap_bytes = 108.0 * N
+    p = info["sort_passes"]
+    build_bytes = (48.0 + 16.0 * p) * info["n_input"]
+    conv_bytes = N * (wl.cin + wl.cout) * esize + 27 * wl.cin * wl.cout * esize + (108.0 * N if path == "ggs" else 0)
+    phases = {
+        "build_ms": {"mean": round(float(np.mean(t_build)), 4), "p50": _pct(t_build, 50), "p95": _pct(t_build, 95),
+                     "p99": _pct(t_build, 99)},
+        "kernel_map_ms": {"mean": round(float(np.mean(t_kmap)), 4), "p50": _pct(t_kmap, 50),
+                          "p95": _pct(t_kmap, 95), "p99": _pct(t_kmap, 99)},
+        "conv_ms": {"mean": round(conv_ms, 4), "p50": _pct(t_conv, 50), "p95": _pct(t_conv, 95),
+                    "p99": _pct(t_conv, 99)},
+        "build_hbm_frac": round(build_bytes / (np.mean(t_build) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernel_map_gbs": round(kmap_bytes / (np.mean(t_kmap) * 1e-3) / 1e9, 1),
+        "kernel_map_hbm_frac": round(kmap_bytes / (np.mean(t_kmap) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "conv_hbm_frac": round(conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "host_syncs_per_step": 2,
+    }
+
+    line = {
+        "metric": METRIC, "value": round(value, 4), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "description": wl.description, "cin": wl.cin, "cout": wl.cout,
+                   "path": path, "pairs": pairs, "pairs_per_voxel": round(pairs / N, 3), **info},
+        "build_mvox_s": round(info["n_input"] / (np.mean(t_build) * 1e-3) / 1e6, 1),
+        "conv_tflops": round(conv_tflops, 3),
+        "phases": phases,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(coords, wl, wl.cin, wl.cout, wl.dtype)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
