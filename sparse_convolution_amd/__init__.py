@@ -134,15 +134,22 @@ def grid_build(ijk: torch.Tensor) -> Grid:
     return Grid(h, ijk.device)
 
 
+_STD_OFFSETS = standard_offsets()
+_STD_OFFSETS_PTR = _STD_OFFSETS.ctypes.data_as(ctypes.c_void_p)
+
+
 def kernel_map(grid: Grid, offsets: np.ndarray | None = None, with_mask: bool = False):
     """Neighbour map int32[K, N] (and optionally the uint32[N] neighbour bit masks, stored
     in an int32 tensor)."""
-    off = standard_offsets() if offsets is None else np.ascontiguousarray(offsets, dtype=np.int32).reshape(-1, 3)
+    if offsets is None:
+        off, off_ptr = _STD_OFFSETS, _STD_OFFSETS_PTR
+    else:
+        off = np.ascontiguousarray(offsets, dtype=np.int32).reshape(-1, 3)
+        off_ptr = off.ctypes.data_as(ctypes.c_void_p)
     K = off.shape[0]
     m = torch.empty((K, grid.n_voxels), dtype=torch.int32, device=grid.device)
     nb = torch.empty(grid.n_voxels, dtype=torch.int32, device=grid.device) if with_mask else None
-    _lib.check(_lib.load().igc_kernel_map(grid.handle, off.ctypes.data_as(ctypes.c_void_p), K, _ptr(m),
-                                          _ptr(nb), _stream(grid.device)))
+    _lib.check(_lib.load().igc_kernel_map(grid.handle, off_ptr, K, _ptr(m), _ptr(nb), _stream(grid.device)))
     return (m, nb) if with_mask else m
 
 

@@ -81,8 +81,7 @@ void* host_staging(size_t bytes) {
 static void free_grid(igc_grid* g) {
   if (!g) return;
   dev_free(g->block, g->stream);
-  dev_free(g->root_keys, g->stream);
-  dev_free(g->root_vals, g->stream);
+  dev_free(g->root_keys, g->stream);  // root values live in the same allocation
   delete g;
 }
 
@@ -140,9 +139,7 @@ int igc_grid_build(const int32_t* d_ijk, int64_t n_in, igc_stream stream, igc_gr
 int igc_grid_destroy(igc_grid* grid) {
   clear_error();
   if (!grid) return IGC_OK;
-  hipError_t e = hipStreamSynchronize(grid->stream);
-  free_grid(grid);
-  if (e != hipSuccess) return hip_status(e, "igc_grid_destroy: stream synchronize");
+  free_grid(grid);  // stream-ordered: the memory is released once the build stream reaches this point
   return IGC_OK;
 }
 

@@ -51,6 +51,9 @@ constexpr uint64_t kLbInclusive = 2ull << 62;
 constexpr uint64_t kLbValue = (1ull << 62) - 1ull;
 constexpr uint32_t kSpinLimit = 1u << 22;  // look-back waits end (and flag an error) after this
 constexpr int kSmallSort = 4096;             // tile-key sorts up to this size run in one workgroup
+constexpr int kTileCache = 64;               // per-workgroup LDS cache of tiles already in the table
+constexpr int kLookBatch = 16;               // predecessors read per look-back step
+constexpr int kRootInLds = 512;              // root tables up to this capacity are copied to LDS
 
 struct BuildState {
   uint32_t overflow;          // root table ran out of probes
@@ -107,7 +110,8 @@ int fill_u64(uint64_t* p, int64_t n, uint64_t v, hipStream_t s) {
 __device__ void insert_tile(uint64_t* keys, uint32_t mask, uint32_t limit, uint64_t key, BuildState* st) {
   uint32_t s = hash_tile(key) & mask;
   for (uint32_t p = 0; p < limit; ++p) {
-    const uint64_t cur = __hip_atomic_load(&keys[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t cur = keys[s];  // cached read first; a stale empty slot is settled by the CAS
+    if (cur != key && cur == kEmptyKey) cur = __hip_atomic_load(&keys[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (cur == key) return;
     if (cur == kEmptyKey) {
       const unsigned long long prev = atomicCAS((unsigned long long*)&keys[s], (unsigned long long)kEmptyKey,
@@ -123,36 +127,69 @@ __device__ void insert_tile(uint64_t* keys, uint32_t mask, uint32_t limit, uint6
   atomicOr(&st->overflow, 1u);
 }
 
+// Tile pass: every workgroup collects the distinct tile keys of its coordinates in an LDS set
+// (a wave first collapses equal keys with ballots) and inserts each of them into the global
+// table once, at the end. The global table's slots therefore see one access per workgroup and
+// distinct tile, not one per wave (same-address device atomics serialise). Keys that do not
+// fit the LDS set go to the table directly. Also records OR / AND of keys and in-tile offsets.
 __global__ __launch_bounds__(256) void k_tile_insert(const int32_t* __restrict__ ijk, int64_t n,
                                                      uint64_t* __restrict__ keys, uint32_t mask, uint32_t limit,
-                                                     BuildState* st) {
+                                                     uint64_t* __restrict__ partial, BuildState* st) {
   __shared__ uint64_t s_red[4][4];
+  __shared__ uint64_t s_set[kTileCache];
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
+  if (threadIdx.x < kTileCache) s_set[threadIdx.x] = kEmptyKey;
+  __syncthreads();
   uint64_t off_or = 0, off_and = ~0ull, key_or = 0, key_and = ~0ull;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t base = (int64_t)blockIdx.x * blockDim.x; base < n; base += stride) {
-    const int64_t e = base + threadIdx.x;
-    const bool valid = e < n;
-    uint64_t key = kEmptyKey;
-    if (valid) {
-      const int32_t i = ijk[3 * e], j = ijk[3 * e + 1], k = ijk[3 * e + 2];
-      key = tile_key(i, j, k);
-      const uint64_t off = tile_offset(i, j, k);
-      off_or |= off;
-      off_and &= off;
-      key_or |= key;
-      key_and &= key;
+  constexpr int U4 = 4;  // coordinates in flight per thread
+  for (int64_t base = (int64_t)blockIdx.x * blockDim.x; base < n; base += U4 * stride) {
+    int32_t ci[U4], cj[U4], ck[U4];
+#pragma unroll
+    for (int u = 0; u < U4; ++u) {
+      const int64_t e = base + u * stride + threadIdx.x;
+      ci[u] = e < n ? ijk[3 * e] : 0;
+      cj[u] = e < n ? ijk[3 * e + 1] : 0;
+      ck[u] = e < n ? ijk[3 * e + 2] : 0;
     }
-    uint64_t pending = __ballot(valid);
-    while (pending) {
-      const int leader = __ffsll((unsigned long long)pending) - 1;
-      const uint64_t lk = shfl64(key, leader);
-      const uint64_t same = __ballot(valid && key == lk);
-      if (lane == leader) insert_tile(keys, mask, limit, lk, st);
-      pending &= ~same;
+#pragma unroll
+    for (int u = 0; u < U4; ++u) {
+      const int64_t e = base + u * stride + threadIdx.x;
+      const bool valid = e < n;
+      uint64_t key = kEmptyKey;
+      if (valid) {
+        key = tile_key(ci[u], cj[u], ck[u]);
+        const uint64_t off = tile_offset(ci[u], cj[u], ck[u]);
+        off_or |= off;
+        off_and &= off;
+        key_or |= key;
+        key_and &= key;
+      }
+      uint64_t pending = __ballot(valid);
+      while (pending) {
+        const int leader = __ffsll((unsigned long long)pending) - 1;
+        const uint64_t lk = shfl64(key, leader);
+        const uint64_t same = __ballot(valid && key == lk);
+        if (lane == leader) {
+          const uint32_t h = hash_tile(lk) & (kTileCache - 1);
+          bool placed = false;
+          for (int p = 0; p < 8; ++p) {
+            const unsigned long long prev = atomicCAS((unsigned long long*)&s_set[(h + p) & (kTileCache - 1)],
+                                                      (unsigned long long)kEmptyKey, (unsigned long long)lk);
+            if (prev == kEmptyKey || prev == lk) {
+              placed = true;
+              break;
+            }
+          }
+          if (!placed) insert_tile(keys, mask, limit, lk, st);
+        }
+        pending &= ~same;
+      }
     }
   }
+  __syncthreads();
+  if (threadIdx.x < kTileCache && s_set[threadIdx.x] != kEmptyKey) insert_tile(keys, mask, limit, s_set[threadIdx.x], st);
   off_or = wave_or64(off_or);
   off_and = wave_and64(off_and);
   key_or = wave_or64(key_or);
@@ -171,10 +208,47 @@ __global__ __launch_bounds__(256) void k_tile_insert(const int32_t* __restrict__
       key_or |= s_red[w][2];
       key_and &= s_red[w][3];
     }
-    atomicOr((unsigned long long*)&st->off_or, (unsigned long long)off_or);
-    atomicAnd((unsigned long long*)&st->off_and, (unsigned long long)off_and);
-    atomicOr((unsigned long long*)&st->key_or, (unsigned long long)key_or);
-    atomicAnd((unsigned long long*)&st->key_and, (unsigned long long)key_and);
+    // Per-workgroup partials (same-address atomics from every workgroup would serialise).
+    partial[4 * blockIdx.x + 0] = off_or;
+    partial[4 * blockIdx.x + 1] = off_and;
+    partial[4 * blockIdx.x + 2] = key_or;
+    partial[4 * blockIdx.x + 3] = key_and;
+  }
+}
+
+// OR / AND of the tile pass's per-workgroup partials into the state. One workgroup.
+__global__ __launch_bounds__(256) void k_reduce_bits(const uint64_t* __restrict__ partial, int nb, BuildState* st) {
+  __shared__ uint64_t s_red[4][4];
+  uint64_t off_or = 0, off_and = ~0ull, key_or = 0, key_and = ~0ull;
+  for (int b = threadIdx.x; b < nb; b += 256) {
+    off_or |= partial[4 * b];
+    off_and &= partial[4 * b + 1];
+    key_or |= partial[4 * b + 2];
+    key_and &= partial[4 * b + 3];
+  }
+  off_or = wave_or64(off_or);
+  off_and = wave_and64(off_and);
+  key_or = wave_or64(key_or);
+  key_and = wave_and64(key_and);
+  const int wave = threadIdx.x >> 6;
+  if (lane_id() == 0) {
+    s_red[wave][0] = off_or;
+    s_red[wave][1] = off_and;
+    s_red[wave][2] = key_or;
+    s_red[wave][3] = key_and;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) {
+      off_or |= s_red[w][0];
+      off_and &= s_red[w][1];
+      key_or |= s_red[w][2];
+      key_and &= s_red[w][3];
+    }
+    st->off_or = off_or;
+    st->off_and = off_and;
+    st->key_or = key_or;
+    st->key_and = key_and;
   }
 }
 
@@ -250,33 +324,85 @@ __device__ __forceinline__ void hist_add(uint32_t* s_hist, uint64_t key, PassSpe
   }
 }
 
-__device__ __forceinline__ void hist_flush(uint32_t (*s_hist)[kMaxPasses * 256], uint32_t* g_hist, PassSpec ps) {
+// Writes this workgroup's histograms to its row of `part` ([blocks][passes*256]).
+__device__ __forceinline__ void hist_flush(uint32_t (*s_hist)[kMaxPasses * 256], uint32_t* part, PassSpec ps) {
   __syncthreads();
-  for (int x = threadIdx.x; x < ps.passes * 256; x += blockDim.x) {
-    const uint32_t v = s_hist[0][x] + s_hist[1][x] + s_hist[2][x] + s_hist[3][x];
-    if (v) atomicAdd(&g_hist[x], v);
-  }
+  uint32_t* row = part + (size_t)blockIdx.x * ps.passes * 256;
+  for (int x = threadIdx.x; x < ps.passes * 256; x += blockDim.x)
+    row[x] = s_hist[0][x] + s_hist[1][x] + s_hist[2][x] + s_hist[3][x];
 }
 
-// key2 for every coordinate, plus the digit histograms of every sort pass.
+// hist[x] = sum over workgroups b of part[b][x]. A workgroup owns 64 columns; its four waves
+// sum interleaved row slices with four loads in flight each, then combine in LDS.
+__global__ __launch_bounds__(256) void k_hist_reduce(const uint32_t* __restrict__ part, int nb, int width,
+                                                     uint32_t* __restrict__ hist) {
+  __shared__ uint32_t s_sum[4][64];
+  const int col = blockIdx.x * 64 + lane_id();
+  const int slice = threadIdx.x >> 6;
+  uint32_t acc[4] = {0, 0, 0, 0};
+  if (col < width) {
+    int b = slice;
+    for (; b + 12 < nb; b += 16) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] += part[(size_t)(b + 4 * u) * width + col];
+    }
+    for (; b < nb; b += 4) acc[0] += part[(size_t)b * width + col];
+  }
+  s_sum[slice][lane_id()] = acc[0] + acc[1] + acc[2] + acc[3];
+  __syncthreads();
+  if (slice == 0 && col < width) hist[col] = s_sum[0][lane_id()] + s_sum[1][lane_id()] + s_sum[2][lane_id()] + s_sum[3][lane_id()];
+}
+
+// key2 for every coordinate, plus the digit histograms of every sort pass. When there are at
+// most kRootInLds tiles, ranks come from a binary search of the sorted tile list in LDS;
+// otherwise from the global root table.
 __global__ __launch_bounds__(256) void k_key2(const int32_t* __restrict__ ijk, int64_t n,
                                               const uint64_t* __restrict__ root_keys,
                                               const int32_t* __restrict__ root_vals, uint32_t mask,
+                                              const uint64_t* __restrict__ tiles, int64_t U,
                                               uint64_t* __restrict__ out, PassSpec ps, uint32_t* __restrict__ hist,
                                               BuildState* st) {
   __shared__ uint32_t s_hist[4][kMaxPasses * 256];
+  __shared__ uint64_t s_tiles[kRootInLds];
   for (int x = threadIdx.x; x < 4 * kMaxPasses * 256; x += blockDim.x) (&s_hist[0][0])[x] = 0;
+  const bool local = U <= kRootInLds;
+  if (local)
+    for (int x = threadIdx.x; x < U; x += blockDim.x) s_tiles[x] = tiles[x];
   __syncthreads();
   const int wave = threadIdx.x >> 6;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) {
-    const int32_t i = ijk[3 * e], j = ijk[3 * e + 1], k = ijk[3 * e + 2];
+  constexpr int U4 = 4;  // coordinates in flight per thread
+  for (int64_t e0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e0 < n; e0 += U4 * stride) {
+   int32_t ci[U4], cj[U4], ck[U4];
+#pragma unroll
+   for (int u = 0; u < U4; ++u) {
+     const int64_t e = e0 + u * stride;
+     ci[u] = e < n ? ijk[3 * e] : 0;
+     cj[u] = e < n ? ijk[3 * e + 1] : 0;
+     ck[u] = e < n ? ijk[3 * e + 2] : 0;
+   }
+#pragma unroll
+   for (int u = 0; u < U4; ++u) {
+    const int64_t e = e0 + u * stride;
+    if (e >= n) break;
+    const int32_t i = ci[u], j = cj[u], k = ck[u];
     const uint64_t tk = tile_key(i, j, k);
-    const int64_t s = probe_slot(root_keys, mask, tk, st);
-    const uint64_t rank = s >= 0 ? (uint64_t)(uint32_t)root_vals[s] : 0ull;
+    uint64_t rank = 0;
+    if (local) {
+      int lo = 0, hi = (int)U - 1;  // s_tiles is ascending and holds tk
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_tiles[mid] < tk) lo = mid + 1; else hi = mid;
+      }
+      rank = (uint64_t)lo;
+    } else {
+      const int64_t s = probe_slot(root_keys, mask, tk, st);
+      rank = s >= 0 ? (uint64_t)(uint32_t)root_vals[s] : 0ull;
+    }
     const uint64_t key = (rank << 36) | tile_offset(i, j, k);
     out[e] = key;
     hist_add(s_hist[wave], key, ps);
+   }
   }
   hist_flush(s_hist, hist, ps);
 }
@@ -316,16 +442,17 @@ __global__ __launch_bounds__(256) void k_onesweep(const uint64_t* __restrict__ s
   const uint64_t lt_mask = (1ull << lane) - 1ull;
 
   // Stable rank of every key among equal digits of its wave (blocked: wave w owns the
-  // tile's keys [w*1024, (w+1)*1024), 64 consecutive keys per round).
+  // tile's keys [w*1024, (w+1)*1024), 64 consecutive keys per round). All loads are issued
+  // before the first ballot so that their latency overlaps.
   uint64_t key[kKeysPerThread];
   uint32_t rank[kKeysPerThread];
+  const int64_t wbase = tile_base + wave * 1024 + lane;
+#pragma unroll
+  for (int r = 0; r < kKeysPerThread; ++r) key[r] = wbase + r * 64 < n ? src[wbase + r * 64] : 0ull;
 #pragma unroll
   for (int r = 0; r < kKeysPerThread; ++r) {
-    const int64_t pos = tile_base + wave * 1024 + r * 64 + lane;
-    const bool valid = pos < n;
-    const uint64_t k = valid ? src[pos] : 0ull;
-    key[r] = k;
-    const uint32_t d = (uint32_t)(k >> shift) & 255u;
+    const bool valid = wbase + r * 64 < n;
+    const uint32_t d = (uint32_t)(key[r] >> shift) & 255u;
     uint64_t m = __ballot(valid);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -341,13 +468,21 @@ __global__ __launch_bounds__(256) void k_onesweep(const uint64_t* __restrict__ s
   }
   __syncthreads();
 
-  // Thread tid owns digit tid: tile count, per-wave exclusive offsets, tile and bucket scans.
+  // Thread tid owns digit tid: tile count (published at once), per-wave exclusive offsets,
+  // tile and bucket scans, and the look-back of the digit.
   const uint32_t d = (uint32_t)tid;
   const uint32_t c0 = s_cnt[0][d], c1 = s_cnt[1][d], c2 = s_cnt[2][d], c3 = s_cnt[3][d];
   const uint32_t tcount = c0 + c1 + c2 + c3;
   uint64_t* lb = lookback + tile * 256 + d;
   __hip_atomic_store(lb, (tile == 0 ? kLbInclusive : kLbAggregate) | (uint64_t)tcount, __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
+  // First look-back batch in flight while the scans run.
+  uint64_t v[kLookBatch];
+  int64_t t = tile - 1;  // next predecessor not yet added
+#pragma unroll
+  for (int b = 0; b < kLookBatch; ++b)
+    v[b] = t - b >= 0 ? __hip_atomic_load(lookback + (t - b) * 256 + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                      : kLbInclusive;
   const uint32_t tstart = (uint32_t)block_excl_scan64<kThreads>(tcount, s_tmp, nullptr);
   const uint64_t bstart = block_excl_scan64<kThreads>(hist[d], s_tmp, nullptr);
   s_cnt[0][d] = 0;
@@ -356,29 +491,41 @@ __global__ __launch_bounds__(256) void k_onesweep(const uint64_t* __restrict__ s
   s_cnt[3][d] = c0 + c1 + c2;
   s_tile_start[d] = tstart;
 
+  // Decoupled look-back, kLookBatch predecessors per step with independent loads (all tiles
+  // of a pass are often resident together, so the first inclusive prefix can be far back).
   uint64_t excl = 0;
   if (tile > 0) {
-    int64_t t = tile - 1;
+    uint32_t spins = 0;
     while (true) {
-      uint64_t v;
-      uint32_t spins = 0;
-      while (true) {
-        v = __hip_atomic_load(lookback + t * 256 + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (v >> 62) break;
-        __builtin_amdgcn_s_sleep(1);
-        ++spins;
-        // Bounded wait: after the limit, or once any other wait has given up, stop waiting
-        // and flag the error so the host rejects the build.
-        if (spins >= kSpinLimit ||
-            ((spins & 1023u) == 0 && __hip_atomic_load(timeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
-          atomicOr(timeout, 1u);
-          v = kLbInclusive;
+      int b = 0;
+      bool done = false;
+      for (; b < kLookBatch; ++b) {
+        const uint64_t st = v[b] >> 62;
+        if (st == 0) break;  // not published yet: wait for it below
+        excl += v[b] & kLbValue;
+        if (st == 2) {
+          done = true;
           break;
         }
       }
-      excl += v & kLbValue;
-      if ((v >> 62) == 2ull || t == 0) break;
-      --t;
+      if (done) break;
+      t -= b;
+      if (b < kLookBatch) {
+        // Bounded wait: after the limit, or once any other wait has given up, stop waiting
+        // and flag the error so the host rejects the build.
+        __builtin_amdgcn_s_sleep(1);
+        ++spins;
+        if (spins >= kSpinLimit ||
+            ((spins & 1023u) == 0 && __hip_atomic_load(timeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+          atomicOr(timeout, 1u);
+          break;
+        }
+      }
+#pragma unroll
+      for (int bb = 0; bb < kLookBatch; ++bb)
+        v[bb] = t - bb >= 0
+                    ? __hip_atomic_load(lookback + (t - bb) * 256 + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                    : kLbInclusive;
     }
     __hip_atomic_store(lb, kLbInclusive | (excl + tcount), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -388,8 +535,7 @@ __global__ __launch_bounds__(256) void k_onesweep(const uint64_t* __restrict__ s
   // Digit-sorted order inside the tile, staged in LDS.
 #pragma unroll
   for (int r = 0; r < kKeysPerThread; ++r) {
-    const int64_t pos = tile_base + wave * 1024 + r * 64 + lane;
-    if (pos < n) {
+    if (wbase + r * 64 < n) {
       const uint32_t dd = (uint32_t)(key[r] >> shift) & 255u;
       s_keys[s_tile_start[dd] + s_cnt[wave][dd] + rank[r]] = key[r];
     }
@@ -409,32 +555,21 @@ __global__ __launch_bounds__(256) void k_onesweep(const uint64_t* __restrict__ s
 
 // Sorts keys[0..n) (in a, scratch b) over the digits of ps; returns the buffer holding the
 // result. The histograms must already be in `hist` ([passes][256]).
-int onesweep_sort(uint64_t* a, uint64_t* b, int64_t n, PassSpec ps, const uint32_t* hist, uint32_t* tile_counters,
-                  uint32_t* timeout, uint32_t* guard, hipStream_t s, uint64_t** result) {
+int onesweep_sort(uint64_t* a, uint64_t* b, int64_t n, PassSpec ps, const uint32_t* hist, uint64_t* lb,
+                  uint32_t* tile_counters, uint32_t* timeout, uint32_t* guard, hipStream_t s, uint64_t** result) {
   *result = a;
   if (n <= 0 || ps.passes == 0) return IGC_OK;
   const int64_t tiles = (n + kTileKeys - 1) / kTileKeys;
-  uint64_t* lb = nullptr;
-  int st = dev_alloc((void**)&lb, (size_t)ps.passes * tiles * 256 * sizeof(uint64_t), s, "igc_grid_build: look-back");
+  int st = fill_u64(lb, (int64_t)ps.passes * tiles * 256, 0, s);
   if (st) return st;
-  st = fill_u64(lb, (int64_t)ps.passes * tiles * 256, 0, s);
-  if (st) {
-    dev_free(lb, s);
-    return st;
-  }
   uint64_t* src = a;
   uint64_t* dst = b;
   for (int p = 0; p < ps.passes; ++p) {
     k_onesweep<<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, ps.lo_bit + 8 * p, hist + 256 * p,
                                                     lb + (size_t)p * tiles * 256, tile_counters + p, timeout, guard);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) {
-      dev_free(lb, s);
-      return hip_status(e, "igc_grid_build: radix pass launch");
-    }
+    IGC_HIP(hipGetLastError(), "igc_grid_build: radix pass launch");
     std::swap(src, dst);
   }
-  dev_free(lb, s);
   *result = src;
   return IGC_OK;
 }
@@ -634,39 +769,73 @@ __global__ __launch_bounds__(256) void k_node_prefix(const uint64_t* __restrict_
 
 // ------------------------------------------------------------------------------ host side
 
-// Temporary device buffers of one build, released (stream-ordered) on every exit path.
-struct Temps {
+// One stream-ordered allocation holds every temporary of a build (the host pays for each
+// allocator call while the device waits on it after a read-back); released on every exit path.
+struct Arena {
   hipStream_t s;
-  std::vector<void*> p;
-  explicit Temps(hipStream_t st) : s(st) {}
-  ~Temps() {
-    for (auto it = p.rbegin(); it != p.rend(); ++it) dev_free(*it, s);
+  char* base = nullptr;
+  size_t used = 0, cap = 0;
+  std::vector<void*> extra;  // rare oversized pieces
+  explicit Arena(hipStream_t st) : s(st) {}
+  ~Arena() {
+    for (void* p : extra) dev_free(p, s);
+    dev_free(base, s);
+  }
+  int reserve(size_t bytes) { return dev_alloc((void**)&base, cap = bytes, s, "igc_grid_build: workspace"); }
+  template <class T>
+  T* take(size_t bytes) {
+    T* p = (T*)(base + used);
+    used = align_up(used + bytes, 256);
+    return used <= cap ? p : nullptr;
   }
   template <class T>
-  int get(T** out, size_t bytes, const char* what) {
+  int get_extra(T** out, size_t bytes, const char* what) {
     const int rc = dev_alloc((void**)out, bytes, s, what);
-    if (rc == IGC_OK) p.push_back(*out);
+    if (rc == IGC_OK) extra.push_back(*out);
     return rc;
   }
 };
 
+constexpr int kHistBlocks = 512;  // workgroups of the key / histogram passes
+constexpr int kTileBlocks = 512;  // workgroups of the tile pass
+
 int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   g->n_input = n_in;
   if (n_in == 0) return IGC_OK;
-  Temps tmp(s);
 
-  BuildState* st = nullptr;
-  int rc = tmp.get(&st, sizeof(BuildState), "igc_grid_build: state");
+  // Workspace sizes depend on n_in only (the tile lists of more than kSmallSort tiles are
+  // allocated on their own once U is known).
+  const int64_t tiles = (n_in + kTileKeys - 1) / kTileKeys;
+  const size_t ws = align_up(sizeof(BuildState), 256) + align_up((size_t)kTileBlocks * 32, 256) +
+                    align_up(2 * kMaxPasses * 256 * 4, 256) + align_up((size_t)kHistBlocks * kMaxPasses * 256 * 4, 256) +
+                    2 * align_up((size_t)n_in * 8, 256) + align_up((size_t)kMaxPasses * tiles * 256 * 8, 256) +
+                    align_up((size_t)tiles * 8, 256) + align_up((size_t)tiles * 32, 256) +
+                    2 * align_up((size_t)kSmallSort * 8, 256);
+  Arena ar(s);
+  int rc = ar.reserve(ws);
   if (rc) return rc;
+  BuildState* st = ar.take<BuildState>(sizeof(BuildState));
+  uint64_t* partial = ar.take<uint64_t>((size_t)kTileBlocks * 32);
+  uint32_t* hist = ar.take<uint32_t>(2 * kMaxPasses * 256 * 4);
+  uint32_t* hpart = ar.take<uint32_t>((size_t)kHistBlocks * kMaxPasses * 256 * 4);
+  uint64_t* ka = ar.take<uint64_t>((size_t)n_in * 8);
+  uint64_t* kb = ar.take<uint64_t>((size_t)n_in * 8);
+  uint64_t* lookback = ar.take<uint64_t>((size_t)kMaxPasses * tiles * 256 * 8);
+  uint64_t* bcounts = ar.take<uint64_t>((size_t)tiles * 8);
+  uint64_t* bprefix = ar.take<uint64_t>((size_t)tiles * 32);
+  uint64_t* tile_list = ar.take<uint64_t>((size_t)kSmallSort * 8);
+  uint64_t* tile_tmp = ar.take<uint64_t>((size_t)kSmallSort * 8);
+  if (!tile_tmp) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: workspace layout");
   BuildState* h = (BuildState*)host_staging(sizeof(BuildState));
   if (!h) return set_error(IGC_ERR_OOM, "igc_grid_build: pinned staging buffer");
 
-  // Root table: first capacity from an estimate, then the size that always suffices.
+  // Root table (keys, then upper-node rows): first capacity from an estimate, then the size
+  // that always suffices (U <= n_in) - the capacity retry.
   uint64_t full_cap = 16;
   while (full_cap < 2ull * (uint64_t)n_in) full_cap <<= 1;
   uint64_t cap = std::min<uint64_t>(full_cap, 1ull << 16);
   if (const char* e = std::getenv("IGC_TEST_INITIAL_CAPACITY")) {
-    uint64_t want = std::strtoull(e, nullptr, 10);
+    const uint64_t want = std::strtoull(e, nullptr, 10);
     cap = 1;
     while (cap < want) cap <<= 1;
   }
@@ -674,13 +843,16 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   for (int attempt = 0;; ++attempt) {
     k_init_state<<<1, 1, 0, s>>>(st);
     IGC_HIP(hipGetLastError(), "igc_grid_build: init launch");
-    rc = dev_alloc((void**)&root_keys, cap * sizeof(uint64_t), s, "igc_grid_build: root table");
+    rc = dev_alloc((void**)&root_keys, cap * 12, s, "igc_grid_build: root table");
     if (rc) return rc;
     g->root_keys = root_keys;
     if ((rc = fill_u64(root_keys, (int64_t)cap, kEmptyKey, s))) return rc;
     const uint32_t limit = (uint32_t)std::min<uint64_t>(cap, 4096);
-    k_tile_insert<<<grid_for(n_in, 256, 2048), 256, 0, s>>>(d_ijk, n_in, root_keys, (uint32_t)(cap - 1), limit, st);
+    const int nbt = grid_for((n_in + 3) / 4, 256, kTileBlocks);
+    k_tile_insert<<<nbt, 256, 0, s>>>(d_ijk, n_in, root_keys, (uint32_t)(cap - 1), limit, partial, st);
     IGC_HIP(hipGetLastError(), "igc_grid_build: tile insert launch");
+    k_reduce_bits<<<1, 256, 0, s>>>(partial, nbt, st);
+    IGC_HIP(hipGetLastError(), "igc_grid_build: tile bits launch");
     IGC_HIP(hipMemcpyAsync(h, st, sizeof(BuildState), hipMemcpyDeviceToHost, s), "igc_grid_build: read tile count");
     IGC_HIP(hipStreamSynchronize(s), "igc_grid_build: tile pass");
     if (!h->overflow) break;
@@ -691,60 +863,63 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
       return set_error(IGC_ERR_CAPACITY, "igc_grid_build: root table overflow after retries");
     cap = full_cap;
   }
+  int32_t* root_vals = (int32_t*)(root_keys + cap);
+  g->root_vals = root_vals;
+  g->root_cap = (uint32_t)cap;
   const int64_t U = h->n_tiles;
   const uint64_t off_var = h->off_or ^ h->off_and;
   const uint64_t key_var = h->key_or ^ h->key_and;
   if (U < 1 || (uint64_t)U > (1ull << 27))
     return set_error(U < 1 ? IGC_ERR_INTERNAL : IGC_ERR_RANGE, "igc_grid_build: root tile count out of range");
 
-  int32_t* root_vals = nullptr;
-  uint64_t *tile_list = nullptr, *tile_tmp = nullptr;
-  if ((rc = dev_alloc((void**)&root_vals, cap * sizeof(int32_t), s, "igc_grid_build: root values"))) return rc;
-  g->root_vals = root_vals;
-  if ((rc = tmp.get(&tile_list, U * sizeof(uint64_t), "igc_grid_build: tile list"))) return rc;
-  if ((rc = tmp.get(&tile_tmp, U * sizeof(uint64_t), "igc_grid_build: tile list"))) return rc;
+  if (U > kSmallSort) {
+    if ((rc = ar.get_extra(&tile_list, U * sizeof(uint64_t), "igc_grid_build: tile list"))) return rc;
+    if ((rc = ar.get_extra(&tile_tmp, U * sizeof(uint64_t), "igc_grid_build: tile list"))) return rc;
+  }
   k_tile_compact<<<grid_for((int64_t)cap, 256, 1024), 256, 0, s>>>(root_keys, (uint32_t)cap, tile_list, (uint32_t)U,
                                                                    st);
   IGC_HIP(hipGetLastError(), "igc_grid_build: tile compaction launch");
   uint64_t* tiles_sorted = tile_tmp;
-  uint32_t* hist = nullptr;
-  if ((rc = tmp.get(&hist, 2 * kMaxPasses * 256 * sizeof(uint32_t), "igc_grid_build: histograms")))
-    return rc;
-  if ((rc = fill_u64((uint64_t*)hist, kMaxPasses * 256, 0, s))) return rc;
   if (U <= kSmallSort) {
     k_sort_small<<<1, 1024, 0, s>>>(tile_list, tile_tmp, (int)U);
     IGC_HIP(hipGetLastError(), "igc_grid_build: tile sort launch");
   } else {
     const PassSpec tps = pass_spec(key_var);
-    k_hist<<<grid_for(U, 256, 1024), 256, 0, s>>>(tile_list, U, tps, hist + kMaxPasses * 256);
+    const int nbh = grid_for(U, 256, kHistBlocks);
+    k_hist<<<nbh, 256, 0, s>>>(tile_list, U, tps, hpart);
     IGC_HIP(hipGetLastError(), "igc_grid_build: tile histogram launch");
-    if ((rc = onesweep_sort(tile_list, tile_tmp, U, tps, hist + kMaxPasses * 256, st->tile_counter + kMaxPasses,
+    k_hist_reduce<<<tps.passes * 4, 256, 0, s>>>(hpart, nbh, tps.passes * 256, hist + kMaxPasses * 256);
+    IGC_HIP(hipGetLastError(), "igc_grid_build: tile histogram reduce launch");
+    uint64_t* tlb = nullptr;
+    const int64_t ttiles = (U + kTileKeys - 1) / kTileKeys;
+    if ((rc = ar.get_extra(&tlb, (size_t)kMaxPasses * ttiles * 256 * 8, "igc_grid_build: tile look-back"))) return rc;
+    if ((rc = onesweep_sort(tile_list, tile_tmp, U, tps, hist + kMaxPasses * 256, tlb, st->tile_counter + kMaxPasses,
                             &st->lookback_timeout, &st->guard, s, &tiles_sorted)))
       return rc;
   }
   k_tile_rank<<<grid_for(U, 256, 1024), 256, 0, s>>>(tiles_sorted, U, root_keys, root_vals, (uint32_t)(cap - 1), st);
   IGC_HIP(hipGetLastError(), "igc_grid_build: tile rank launch");
 
-  // key2 and its sort.
+  // key2, its histograms and its sort over the varying bit span.
   int rank_bits = 0;
   while ((1ll << rank_bits) < U) ++rank_bits;
   const uint64_t varying = off_var | (rank_bits ? (((1ull << rank_bits) - 1ull) << 36) : 0ull);
   const PassSpec ps = pass_spec(varying);
-  uint64_t *ka = nullptr, *kb = nullptr;
-  if ((rc = tmp.get(&ka, n_in * sizeof(uint64_t), "igc_grid_build: keys"))) return rc;
-  if ((rc = tmp.get(&kb, n_in * sizeof(uint64_t), "igc_grid_build: keys"))) return rc;
-  k_key2<<<grid_for(n_in, 256, 2048), 256, 0, s>>>(d_ijk, n_in, root_keys, root_vals, (uint32_t)(cap - 1), ka, ps,
-                                                   hist, st);
+  const int nbk = grid_for((n_in + 3) / 4, 256, kHistBlocks);
+  k_key2<<<nbk, 256, 0, s>>>(d_ijk, n_in, root_keys, root_vals, (uint32_t)(cap - 1), tiles_sorted, U, ka, ps, hpart,
+                             st);
   IGC_HIP(hipGetLastError(), "igc_grid_build: key pass launch");
+  if (ps.passes > 0) {
+    k_hist_reduce<<<ps.passes * 4, 256, 0, s>>>(hpart, nbk, ps.passes * 256, hist);
+    IGC_HIP(hipGetLastError(), "igc_grid_build: histogram reduce launch");
+  }
   uint64_t* sorted = ka;
-  if ((rc = onesweep_sort(ka, kb, n_in, ps, hist, st->tile_counter, &st->lookback_timeout, &st->guard, s, &sorted)))
+  if ((rc = onesweep_sort(ka, kb, n_in, ps, hist, lookback, st->tile_counter, &st->lookback_timeout, &st->guard, s,
+                          &sorted)))
     return rc;
 
-  // Counts, then the one read-back that sizes the topology.
-  const int64_t nb = (n_in + kTileKeys - 1) / kTileKeys;
-  uint64_t *bcounts = nullptr, *bprefix = nullptr;
-  if ((rc = tmp.get(&bcounts, nb * sizeof(uint64_t), "igc_grid_build: block counts"))) return rc;
-  if ((rc = tmp.get(&bprefix, nb * 4 * sizeof(uint64_t), "igc_grid_build: block prefixes"))) return rc;
+  // Counts, then the read-back that sizes the topology.
+  const int64_t nb = tiles;
   k_count<<<(unsigned)nb, kThreads, 0, s>>>(sorted, n_in, bcounts);
   IGC_HIP(hipGetLastError(), "igc_grid_build: count launch");
   k_scan_blocks<<<1, 1024, 0, s>>>(bcounts, nb, bprefix, st);
@@ -757,24 +932,21 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   if ((int64_t)h->counts[3] != U || N < 1 || N > n_in || F > N || Lw > F)
     return set_error(IGC_ERR_INTERNAL, "igc_grid_build: inconsistent node counts");
 
-  // Topology block.
+  // Topology block (zeroed with one fill: masks start empty).
   size_t off = 0;
   auto carve = [&](size_t bytes) {
     const size_t o = off;
     off = align_up(off + bytes, 256);
     return o;
   };
-  const size_t o_root_list = carve(U * 8), o_upo = carve(U * 16), o_upm = carve(U * 512 * 8),
-               o_upp = carve(U * 512 * 2), o_upf = carve(U * 4), o_loo = carve(Lw * 16), o_lom = carve(Lw * 64 * 8),
-               o_lop = carve(Lw * 64 * 2), o_lof = carve(Lw * 4), o_leaf = carve(F * sizeof(LeafRec)),
+  const size_t o_upm = carve(U * 512 * 8), o_lom = carve(Lw * 64 * 8), o_leaf = carve(F * sizeof(LeafRec)),
+               zero_end = off, o_root_list = carve(U * 8), o_upo = carve(U * 16), o_upp = carve(U * 512 * 2),
+               o_upf = carve(U * 4), o_loo = carve(Lw * 16), o_lop = carve(Lw * 64 * 2), o_lof = carve(Lw * 4),
                o_lfo = carve(F * 16);
   char* blk = nullptr;
   if ((rc = dev_alloc((void**)&blk, off, s, "igc_grid_build: topology"))) return rc;
   g->block = blk;
   g->bytes = off + cap * 12;
-  g->root_keys = root_keys;
-  g->root_vals = root_vals;
-  g->root_cap = (uint32_t)cap;
   g->root_list = (uint64_t*)(blk + o_root_list);
   g->upper_origin = (int4*)(blk + o_upo);
   g->upper_mask = (uint64_t*)(blk + o_upm);
@@ -791,9 +963,7 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   g->n_lower = Lw;
   g->n_upper = U;
   g->sort_passes = ps.passes;
-  if ((rc = fill_u64(g->upper_mask, U * 512, 0, s))) return rc;
-  if ((rc = fill_u64(g->lower_mask, Lw * 64, 0, s))) return rc;
-  if ((rc = fill_u64((uint64_t*)g->leaf, F * (int64_t)(sizeof(LeafRec) / 8), 0, s))) return rc;
+  if ((rc = fill_u64((uint64_t*)blk, (int64_t)(zero_end / 8), 0, s))) return rc;
 
   Topo t{N,           F,           Lw,           U,          &st->guard,     tiles_sorted,
          g->root_list, g->upper_origin, g->upper_mask, g->upper_first, g->lower_origin, g->lower_mask,
@@ -806,7 +976,6 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   IGC_HIP(hipGetLastError(), "igc_grid_build: lower prefix launch");
   k_node_prefix<<<(unsigned)((U + 3) / 4), 256, 0, s>>>(g->upper_mask, g->upper_pre, U, 512);
   IGC_HIP(hipGetLastError(), "igc_grid_build: upper prefix launch");
-
   return IGC_OK;
 }
 
