@@ -765,6 +765,27 @@ __global__ __launch_bounds__(256) void k_node_prefix(const uint64_t* __restrict_
   }
 }
 
+// The 3x3x3 block of leaves around every leaf, resolved once through the tree (root hash and
+// fixed-fanout descent) for the kernel map and the leaf-local convolution.
+__global__ __launch_bounds__(256) void k_leaf_neighbors(GridView g, int32_t* __restrict__ nbr) {
+  const int64_t total = g.n_leaf * 27;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t f = e / 27;
+    const int slot = (int)(e - f * 27);
+    int32_t nl = (int32_t)f;
+    if (slot != 13) {
+      const int4 o = g.leaf_origin[f];
+      const int64_t ni = (int64_t)o.x + 8 * (slot / 9 - 1), nj = (int64_t)o.y + 8 * ((slot / 3) % 3 - 1),
+                    nk = (int64_t)o.z + 8 * (slot % 3 - 1);
+      nl = -1;
+      if (ni >= INT32_MIN && ni <= INT32_MAX && nj >= INT32_MIN && nj <= INT32_MAX && nk >= INT32_MIN &&
+          nk <= INT32_MAX)
+        nl = find_leaf(g, (int32_t)ni, (int32_t)nj, (int32_t)nk);
+    }
+    nbr[e] = nl;
+  }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------------ host side
@@ -942,7 +963,7 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   const size_t o_upm = carve(U * 512 * 8), o_lom = carve(Lw * 64 * 8), o_leaf = carve(F * sizeof(LeafRec)),
                zero_end = off, o_root_list = carve(U * 8), o_upo = carve(U * 16), o_upp = carve(U * 512 * 2),
                o_upf = carve(U * 4), o_loo = carve(Lw * 16), o_lop = carve(Lw * 64 * 2), o_lof = carve(Lw * 4),
-               o_lfo = carve(F * 16);
+               o_lfo = carve(F * 16), o_nbr = carve(F * 27 * 4);
   char* blk = nullptr;
   if ((rc = dev_alloc((void**)&blk, off, s, "igc_grid_build: topology"))) return rc;
   g->block = blk;
@@ -958,6 +979,7 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   g->lower_first = (uint32_t*)(blk + o_lof);
   g->leaf = (LeafRec*)(blk + o_leaf);
   g->leaf_origin = (int4*)(blk + o_lfo);
+  g->leaf_nbr = (int32_t*)(blk + o_nbr);
   g->n_voxels = N;
   g->n_leaf = F;
   g->n_lower = Lw;
@@ -976,6 +998,8 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   IGC_HIP(hipGetLastError(), "igc_grid_build: lower prefix launch");
   k_node_prefix<<<(unsigned)((U + 3) / 4), 256, 0, s>>>(g->upper_mask, g->upper_pre, U, 512);
   IGC_HIP(hipGetLastError(), "igc_grid_build: upper prefix launch");
+  k_leaf_neighbors<<<grid_for(F * 27, 256, 8192), 256, 0, s>>>(g->view(), g->leaf_nbr);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: leaf neighbour launch");
   return IGC_OK;
 }
 

@@ -5,10 +5,11 @@
 // plus a one-voxel halo (a 10^3 window) is densified in on-chip memory and a regular local
 // dense convolution runs on the matrix units, with no auxiliary index structure.
 //
-// gfx950 form: one workgroup per leaf. It resolves the 26 neighbour leaves through the tree,
-// fills a 10 x 10 x 10 x cin window in LDS from the leaf records (inactive or absent cells are
-// zero), and stages W in LDS. Every neighbour read is then an LDS address computed from the
-// voxel's position - the kernel map is not used. Output rows are produced only for the leaf's
+// gfx950 form: one workgroup per leaf. It takes the 3x3x3 block of leaves from the grid's
+// neighbour table, fills a 10 x 10 x 10 x cin window in LDS from the leaf records (inactive or
+// absent cells are zero), and keeps W in registers (or LDS when it does not fit). Every
+// neighbour read is then an LDS address computed from the voxel's position - the kernel map
+// is not used. Output rows are produced only for the leaf's
 // active voxels: they are compacted in row order, taken 16 at a time as the M dimension of a
 // 16x16x4 fp32 MFMA whose A operand is read straight from the window at the shifted cell of
 // each offset, K = 27 offsets x cin and N = cout (padded to 16). The result rows of one leaf
@@ -36,8 +37,10 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
   constexpr int COUTP = (COUT + 15) / 16 * 16;
   constexpr int NS = COUTP / 16;  // 16-column MFMA slabs
   constexpr int KS = CIN / 4;     // 4-channel MFMA steps per offset
+  // W fragments stay in registers when they fit (54 per lane at 8 -> 16); otherwise in LDS.
+  constexpr bool kWRegs = NS * 27 * KS <= 64;
   __shared__ __attribute__((aligned(16))) float s_win[1000 * CIN];
-  __shared__ float s_w[27 * CIN * COUTP];
+  __shared__ float s_w[kWRegs ? 1 : 27 * CIN * COUTP];
   __shared__ uint64_t s_mask[27][8];
   __shared__ uint64_t s_off[27];
   __shared__ uint64_t s_pre[27];
@@ -47,20 +50,13 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
+  const int rl = lane & 15;  // A row / B column / D column
+  const int kq = lane >> 4;  // A column / B row / D row group
   const int64_t f = xcd_block(blockIdx.x, gridDim.x);
 
-  // Neighbour leaf records (slot 13 = this leaf) and the weights, zero-padded to COUTP columns.
+  // Leaf records of the 3x3x3 block (slot 13 = this leaf) from the grid's neighbour table.
   if (tid < 27) {
-    const int4 o = g.leaf_origin[f];
-    const int di = tid / 9 - 1, dj = (tid / 3) % 3 - 1, dk = tid % 3 - 1;
-    const int64_t ni = (int64_t)o.x + 8 * di, nj = (int64_t)o.y + 8 * dj, nk = (int64_t)o.z + 8 * dk;
-    int32_t nl = -1;
-    if (tid == 13) {
-      nl = (int32_t)f;
-    } else if (ni >= INT32_MIN && ni <= INT32_MAX && nj >= INT32_MIN && nj <= INT32_MAX && nk >= INT32_MIN &&
-               nk <= INT32_MAX) {
-      nl = find_leaf(g, (int32_t)ni, (int32_t)nj, (int32_t)nk);
-    }
+    const int32_t nl = g.leaf_nbr[f * 27 + tid];
     if (nl >= 0) {
       const LeafRec& L = g.leaf[nl];
       for (int q = 0; q < 8; ++q) s_mask[tid][q] = L.mask[q];
@@ -72,10 +68,22 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
       s_pre[tid] = 0;
     }
   }
-  for (int e = tid; e < 27 * CIN * COUTP; e += 256) {
-    const int col = e % COUTP;
-    const int ok = e / COUTP;  // o * CIN + k
-    s_w[e] = col < COUT ? w[ok * COUT + col] : 0.f;
+  float wreg[kWRegs ? 27 * KS * NS : 1];
+  if constexpr (kWRegs) {
+#pragma unroll
+    for (int o = 0; o < 27; ++o)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+          const int col = ns * 16 + rl;
+          wreg[(o * KS + ks) * NS + ns] = col < COUT ? w[(o * CIN + ks * 4 + kq) * COUT + col] : 0.f;
+        }
+  } else {
+    for (int e = tid; e < 27 * CIN * COUTP; e += 256) {
+      const int col = e % COUTP;
+      s_w[e] = col < COUT ? w[(e / COUTP) * COUT + col] : 0.f;
+    }
   }
   __syncthreads();
 
@@ -112,24 +120,25 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
 
   const uint32_t count = s_count;
   const uint64_t base = s_off[13];
-  const int rl = lane & 15;  // A row / B column / D column
-  const int kq = lane >> 4;  // A column / B row / D row group
   for (uint32_t g0 = (uint32_t)wave * 16; g0 < count; g0 += 64) {
     const uint32_t t = g0 + rl;
     const uint32_t p = s_pos[t < count ? t : 0];
     const int px = (int)(p >> 6), py = (int)((p >> 3) & 7u), pz = (int)(p & 7u);
+    const int cell0 = (px * 10 + py) * 10 + pz;  // window cell of offset (-1,-1,-1)
     f32x4 acc[NS];
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) acc[ns] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int o = 0; o < 27; ++o) {
-      const int cell = ((px + o / 9) * 10 + (py + (o / 3) % 3)) * 10 + (pz + o % 3);
+      const int cell = cell0 + (o / 9) * 100 + ((o / 3) % 3) * 10 + o % 3;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const float a = s_win[cell * CIN + ks * 4 + kq];
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
-          const float b = s_w[(o * CIN + ks * 4 + kq) * COUTP + ns * 16 + rl];
+          float b;
+          if constexpr (kWRegs) b = wreg[(o * KS + ks) * NS + ns];
+          else b = s_w[(o * CIN + ks * 4 + kq) * COUTP + ns * 16 + rl];
           acc[ns] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[ns], 0, 0, 0);
         }
       }

@@ -31,6 +31,7 @@ struct igc_grid {
   uint32_t* lower_first = nullptr; // [Lw]
   igc::LeafRec* leaf = nullptr;    // [F]
   int4* leaf_origin = nullptr;     // [F]
+  int32_t* leaf_nbr = nullptr;     // [F*27] neighbour leaves (the 3x3x3 block around each leaf)
 
   igc::GridView view() const {
     igc::GridView v;
@@ -45,6 +46,7 @@ struct igc_grid {
     v.lower_first = lower_first;
     v.leaf = leaf;
     v.leaf_origin = leaf_origin;
+    v.leaf_nbr = leaf_nbr;
     v.n_voxels = n_voxels;
     v.n_leaf = n_leaf;
     return v;

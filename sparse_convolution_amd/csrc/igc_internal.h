@@ -41,6 +41,7 @@ struct GridView {
   const uint32_t* lower_first;  // [Lw]
   const LeafRec* leaf;          // [F]
   const int4* leaf_origin;      // [F] (i, j, k, 0)
+  const int32_t* leaf_nbr;      // [F*27] leaf at origin + 8*(di,dj,dk), slot (di+1)*9+(dj+1)*3+(dk+1), -1 absent
   int64_t n_voxels;
   int64_t n_leaf;
 };

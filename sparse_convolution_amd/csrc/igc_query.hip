@@ -3,8 +3,8 @@
 //
 // Kernel map (DriveRT, "Shared neighbour maps"; fVDB notes, sparse-conv operators): for each
 // active voxel and each kernel offset, the row of the voxel at coordinate + offset, or -1.
-// One wave handles one leaf. It resolves the leaf's 26 neighbour leaves once (root hash and
-// fixed-fanout descent), keeps the 27 leaf index records (80 B each) in LDS, compacts the
+// One wave handles one leaf. It reads the leaf's 3x3x3 block of neighbour leaves from the
+// grid's neighbour table, keeps the 27 leaf index records (80 B each) in LDS, compacts the
 // leaf's active voxels, and then answers every (voxel, offset) pair with an LDS mask test,
 // the prefix count and a popcount - no tree walk per pair. Offsets up to 8 voxels per axis
 // stay inside the 3x3x3 block of leaves. For a fixed offset the wave's 64 voxels have
@@ -74,18 +74,9 @@ __global__ __launch_bounds__(256) void k_kernel_map(GridView g, OffsetList off, 
   const int64_t f = (int64_t)blockIdx.x * 4 + wave;
   const bool has_leaf = f < g.n_leaf;
 
-  // The 27 leaves around this one (slot 13 is the leaf itself).
+  // The 27 leaf records around this one (slot 13 is the leaf itself), from the neighbour table.
   if (has_leaf && lane < 27) {
-    const int4 o = g.leaf_origin[f];
-    const int di = lane / 9 - 1, dj = (lane / 3) % 3 - 1, dk = lane % 3 - 1;
-    const int64_t ni = (int64_t)o.x + 8 * di, nj = (int64_t)o.y + 8 * dj, nk = (int64_t)o.z + 8 * dk;
-    int32_t nl = -1;
-    if (lane == 13) {
-      nl = (int32_t)f;
-    } else if (ni >= INT32_MIN && ni <= INT32_MAX && nj >= INT32_MIN && nj <= INT32_MAX && nk >= INT32_MIN &&
-               nk <= INT32_MAX) {
-      nl = find_leaf(g, (int32_t)ni, (int32_t)nj, (int32_t)nk);
-    }
+    const int32_t nl = g.leaf_nbr[f * 27 + lane];
     if (nl >= 0) {
       const LeafRec& L = g.leaf[nl];
       for (int w = 0; w < 8; ++w) s_mask[wave][lane][w] = L.mask[w];
@@ -139,6 +130,80 @@ __global__ __launch_bounds__(256) void k_kernel_map(GridView g, OffsetList off, 
   }
 }
 
+// Kernel map for offsets inside the 3x3x3 block (|component| <= 1): one wave per leaf builds
+// the 10 x 10 x 10 window of row indices around its leaf in LDS (one mask test + prefix +
+// popcount per cell), after which each (voxel, offset) pair is a single LDS read at a constant
+// cell offset, stored contiguously per offset.
+__global__ __launch_bounds__(256) void k_kernel_map_window(GridView g, OffsetList off, int32_t* __restrict__ map,
+                                                           uint32_t* __restrict__ nbmask) {
+  __shared__ uint64_t s_mask[4][27][8];
+  __shared__ uint64_t s_off[4][27];
+  __shared__ uint64_t s_pre[4][27];
+  __shared__ int32_t s_idx[4][1000];
+  __shared__ uint16_t s_pos[4][512];
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int64_t f = (int64_t)blockIdx.x * 4 + wave;
+  const bool has_leaf = f < g.n_leaf;
+
+  if (has_leaf && lane < 27) {
+    const int32_t nl = g.leaf_nbr[f * 27 + lane];
+    if (nl >= 0) {
+      const LeafRec& L = g.leaf[nl];
+      for (int w = 0; w < 8; ++w) s_mask[wave][lane][w] = L.mask[w];
+      s_off[wave][lane] = L.offset;
+      s_pre[wave][lane] = L.prefix;
+    } else {
+      for (int w = 0; w < 8; ++w) s_mask[wave][lane][w] = 0;
+      s_off[wave][lane] = 0;
+      s_pre[wave][lane] = 0;
+    }
+  }
+  __syncthreads();
+
+  uint32_t count = 0;
+  if (has_leaf) {
+    const uint64_t lt = (1ull << lane) - 1ull;
+    for (int w = 0; w < 8; ++w) {
+      const uint64_t word = s_mask[wave][13][w];
+      if ((word >> lane) & 1ull) s_pos[wave][count + (uint32_t)__popcll(word & lt)] = (uint16_t)(w * 64 + lane);
+      count += (uint32_t)__popcll(word);
+    }
+    for (int c = lane; c < 1000; c += 64) {
+      const int x = c / 100 - 1, y = (c / 10) % 10 - 1, z = c % 10 - 1;
+      const int slot = ((x >> 3) + 1) * 9 + ((y >> 3) + 1) * 3 + ((z >> 3) + 1);
+      const uint32_t q = (uint32_t)(x & 7);
+      const uint64_t word = s_mask[wave][slot][q];
+      const uint64_t bit = 1ull << ((uint32_t)((y & 7) << 3) | (uint32_t)(z & 7));
+      int32_t idx = -1;
+      if (word & bit) {
+        const uint32_t pre = q ? (uint32_t)(s_pre[wave][slot] >> (9u * (q - 1u))) & 511u : 0u;
+        idx = (int32_t)(s_off[wave][slot] + pre + (uint32_t)__popcll(word & (bit - 1ull)));
+      }
+      s_idx[wave][c] = idx;
+    }
+  }
+  __syncthreads();
+  if (!has_leaf) return;
+
+  const int64_t N = g.n_voxels;
+  const uint64_t base = s_off[wave][13];
+  for (uint32_t q = 0; q < count; q += 64) {
+    const uint32_t t = q + lane;
+    const bool act = t < count && base + t < (uint64_t)N;
+    const uint32_t n = act ? s_pos[wave][t] : 0u;
+    const int cell0 = (int)((n >> 6) * 100 + ((n >> 3) & 7u) * 10 + (n & 7u)) + 111;  // cell of offset 0
+    int32_t* dst = map + base + t;
+    uint32_t bits = 0;
+    for (int o = 0; o < off.K; ++o) {
+      const int idx = s_idx[wave][cell0 + off.d[o][0] * 100 + off.d[o][1] * 10 + off.d[o][2]];
+      if (idx >= 0 && o < 32) bits |= 1u << o;
+      if (act) dst[(size_t)o * (size_t)N] = idx;
+    }
+    if (nbmask && act) nbmask[base + t] = bits;
+  }
+}
+
 }  // namespace
 
 int launch_active_ijk(const igc_grid* g, int32_t* d_out, hipStream_t s) {
@@ -168,7 +233,12 @@ int launch_kernel_map(const igc_grid* g, const int32_t* h_offsets, int32_t K, in
   off.K = K;
   for (int o = 0; o < K; ++o)
     for (int a = 0; a < 3; ++a) off.d[o][a] = (int8_t)h_offsets[3 * o + a];
-  k_kernel_map<<<(unsigned)((g->n_leaf + 3) / 4), 256, 0, s>>>(g->view(), off, d_map, d_nbmask);
+  bool unit = true;
+  for (int a = 0; a < 3 * K; ++a) unit = unit && h_offsets[a] >= -1 && h_offsets[a] <= 1;
+  if (unit)
+    k_kernel_map_window<<<(unsigned)((g->n_leaf + 3) / 4), 256, 0, s>>>(g->view(), off, d_map, d_nbmask);
+  else
+    k_kernel_map<<<(unsigned)((g->n_leaf + 3) / 4), 256, 0, s>>>(g->view(), off, d_map, d_nbmask);
   IGC_HIP(hipGetLastError(), "igc_kernel_map: launch");
   return IGC_OK;
 }
