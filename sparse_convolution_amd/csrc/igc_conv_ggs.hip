@@ -1,25 +1,39 @@
 // Gather-GEMM-scatter submanifold convolution, bf16 inputs / weights / outputs with fp32
-// accumulation on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
+// accumulation on the gfx950 matrix cores (v_mfma_f32_16x16x32_bf16).
 //
 // fVDB notes, "accelerated operators for sparse convolution", third case: work is tiled over
 // consecutive output rows, a workgroup-local buffer replaces global scatter, and for each of
-// the 27 stencil offsets the tile's (input, output) pairs feed a tensor-core GEMM.
+// the 27 stencil offsets the tile's (input, output) pairs feed a tensor-core GEMM, with the
+// pairs of each offset padded to a multiple of 16 rows.
 //
-// The gfx950 form used here is output-stationary: a workgroup owns BM = 128 consecutive
-// output rows and BN output channels and keeps their fp32 accumulators in registers for the
-// whole reduction, so the "scatter" of every offset's product lands in registers and the
-// output is written once (no atomics, deterministic). For each offset that at least one row
-// of the tile uses, and each 32-channel slice of the input, the tile gathers its 128 input
-// rows by the kernel map (absent neighbours read as zeros) into LDS next to the matching
-// 32 x BN slice of W[o], and four waves run 32x32x16 MFMAs on 64 x BN/2 sub-tiles. The next
-// slice is fetched into registers while the current one is multiplied (two LDS buffers, one
-// barrier per slice). Offsets that no row of the tile uses are skipped entirely, which is the
-// pages' per-offset pair packing at tile granularity.
+// gfx950 form, in two kernels:
 //
-// Rows are padded to 80 bytes in LDS so that eight lanes reading 16 bytes of eight
-// consecutive rows hit distinct banks. Workgroups are numbered so that each of the eight
-// XCDs (each with its own L2) walks a contiguous range of row tiles: neighbouring output
-// rows gather neighbouring input rows, and those stay in one L2.
+// k_ggs_plan, one workgroup per tile of 256 consecutive output rows: each row's 27-bit
+// neighbour mask (bit o set when the kernel map has a neighbour at offset o) is read from the
+// map, the tile's rows are sorted by that mask, and for every offset a 16-bit mask records
+// which 16-row blocks of the sorted tile hold at least one pair. Sorting groups rows with the
+// same neighbour set (DriveRT, "Kernels selected per GPU": rows sorted by their 27-bit
+// neighbour mask give threads uniform work), so the pages' per-offset pair lists padded to 16
+// become "the blocks whose bit is set".
+//
+// k_conv_ggs_bf16, one workgroup (4 waves) per tile x BN output channels, output-stationary:
+// the fp32 accumulators of the 256 x BN tile stay in registers for the whole reduction, so
+// every offset's product is "scattered" into registers and each output row is written once,
+// with no atomics and a fixed summation order (deterministic). The reduction runs over chunks
+// (used offset, KC input channels): the tile's input rows of that offset are gathered by the
+// kernel map (absent neighbours read a zero row) into LDS next to the matching BN x KC slice
+// of W[o]^T, and each wave multiplies its (256/WM) x (BN/WN) sub-tile with 16x16x32 MFMAs,
+// skipping the 16-row blocks that have no pair at that offset. Both operands go from global
+// memory straight into LDS (global_load_lds_dwordx4: no staging registers, which the 256 x 256
+// accumulators leave none of); the next chunk's loads are in flight while the current chunk is
+// multiplied (two LDS stages, one barrier per chunk), and the map entries of the offset after
+// next are fetched one chunk ahead so the gather never waits on the map. The output tile is
+// staged through LDS and leaves as whole rows.
+//
+// Staged rows are unpadded and their 16-byte granules XOR-swizzled by row, so the rows read
+// together by one fragment load fall on distinct banks. Workgroups are numbered so that each
+// of the eight XCDs (each with its own L2) walks a contiguous range of row tiles: neighbouring
+// output rows gather neighbouring input rows, and those stay in one L2.
 #include <hip/hip_runtime.h>
 
 #include "igc_host.h"
@@ -30,11 +44,10 @@ namespace igc {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128;    // output rows per workgroup
-constexpr int kBK = 32;     // input channels per slice
-constexpr int kLD = kBK + 8;  // LDS row stride in bf16 (80 bytes)
+constexpr int kBM = 256;  // output rows per tile (= threads per workgroup)
+constexpr int kNOff = 27;
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -60,130 +73,261 @@ __global__ void k_transpose_w(const uint16_t* __restrict__ w, uint16_t* __restri
   }
 }
 
-template <int BN>
+// Per tile: perm[tile*256 + p] = output row at sorted position p (-1 past N), and
+// blk[tile*27 + o] bit b = some row at sorted positions [16b, 16b+16) has a neighbour at o.
+__global__ __launch_bounds__(kBM) void k_ggs_plan(const int32_t* __restrict__ map, int64_t N,
+                                                  int32_t* __restrict__ perm, uint16_t* __restrict__ blk) {
+  __shared__ uint64_t s_key[kBM];
+  __shared__ uint32_t s_part[kBM / 64][kNOff];
+  const int t = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * kBM;
+  const int64_t row = r0 + t;
+  uint32_t mask = 0;
+  if (row < N) {
+#pragma unroll
+    for (int o = 0; o < kNOff; ++o) mask |= (map[(size_t)o * (size_t)N + row] >= 0 ? 1u : 0u) << o;
+  }
+  // Ascending on the complemented mask: equal masks adjacent, padding rows (mask 0) last.
+  s_key[t] = ((uint64_t)(~mask & 0x7FFFFFFu) << 8) | (uint64_t)t;
+  __syncthreads();
+  for (int k = 2; k <= kBM; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int p = t ^ j;
+      if (p > t) {
+        const uint64_t a = s_key[t], b = s_key[p];
+        if ((a > b) == ((t & k) == 0)) {
+          s_key[t] = b;
+          s_key[p] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const uint64_t key = s_key[t];
+  const int64_t src = r0 + (int64_t)(key & 255u);
+  const uint32_t m = ~(uint32_t)(key >> 8) & 0x7FFFFFFu;
+  perm[row] = src < N ? (int32_t)src : -1;
+  const int lane = lane_id(), wave = t >> 6;
+  for (int o = 0; o < kNOff; ++o) {
+    const uint64_t b = __ballot((m >> o) & 1u);
+    if (lane == 0) {
+      uint32_t bits = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bits |= ((b >> (16 * q)) & 0xFFFFull) ? (1u << q) : 0u;
+      s_part[wave][o] = bits;
+    }
+  }
+  __syncthreads();
+  if (t < kNOff) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int w = 0; w < kBM / 64; ++w) v |= s_part[w][t] << (4 * w);
+    blk[(size_t)blockIdx.x * kNOff + t] = (uint16_t)v;
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// Gathered in place of an absent neighbour's row (any channel slice of up to 1024 channels).
+__device__ __attribute__((aligned(16))) uint16_t g_zero_row[1024];
+
+// 16-byte granule g of staged row r sits at granule g ^ swz(r): with 8 granules per row (64
+// channels) the eight rows read together by one fragment load land on eight distinct 4-bank
+// groups; with 4 granules per row (32 channels) pairs of rows share a bank half, so rows are
+// swizzled in pairs.
+template <int SEG>
+__device__ __forceinline__ int stage_swz(int r) {
+  return SEG == 8 ? (r & 7) : ((r >> 1) & 3);
+}
+
+// BN output channels per workgroup, KC input channels per chunk, WM waves along the rows
+// (4 / WM along the channels).
+template <int BN, int KC, int WM>
 __global__ __launch_bounds__(256) void k_conv_ggs_bf16(const int32_t* __restrict__ map, int64_t N,
+                                                       const int32_t* __restrict__ perm,
+                                                       const uint16_t* __restrict__ blk,
                                                        const uint16_t* __restrict__ feats,
                                                        const uint16_t* __restrict__ wt, int cin, int cout,
                                                        uint16_t* __restrict__ out, int64_t col_tiles) {
-  constexpr int NB = BN / 64;  // 32-column MFMA blocks per wave
-  __shared__ int32_t s_map[27][kBM];
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][kBM * kLD];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b[2][BN * kLD];
-  __shared__ uint32_t s_used;
-  __shared__ uint8_t s_olist[27];
+  constexpr int WN = 4 / WM;
+  constexpr int MW = kBM / WM;  // rows per wave
+  constexpr int NW = BN / WN;   // channels per wave
+  constexpr int MI = MW / 16, NI = NW / 16;
+  constexpr int SEG = KC / 8;                 // 16-byte granules per staged row
+  constexpr int ROWB = KC * 2;                // bytes per staged row
+  constexpr int RPI = 64 / SEG;               // rows filled by one wave-wide LDS load
+  constexpr int AI = kBM / RPI / 4;           // A loads per wave and chunk
+  constexpr int BI = BN / RPI / 4;            // B loads per wave and chunk
+  constexpr int A_BYTES = kBM * ROWB, B_BYTES = BN * ROWB;
+  constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  constexpr int OUT_ROWS = 128 * BN * 2 <= STAGE_BYTES ? 128 : (64 * BN * 2 <= STAGE_BYTES ? 64 : 32);
+  constexpr int NPASS = kBM / OUT_ROWS;
+  constexpr int OG = BN / 8;                  // 16-byte granules per output row
+  static_assert(MI >= 1 && NI >= 1 && AI >= 1 && BI >= 1, "tile shape");
+  static_assert(OUT_ROWS * BN * 2 <= STAGE_BYTES && OG >= 8, "output pass fits one stage");
+  // Two stages as two objects: the compiler then sees that the loads into one stage never
+  // feed the fragment reads of the other and does not wait for them.
+  __shared__ uint4 s_st0[STAGE_BYTES / 16];
+  __shared__ uint4 s_st1[STAGE_BYTES / 16];
+  __shared__ int32_t s_perm[kBM];
+  __shared__ int32_t s_map[kNOff][kBM];
+  __shared__ uint16_t s_blk[kNOff];
+  __shared__ uint8_t s_olist[kNOff];
   __shared__ int s_nused;
+  __shared__ uint32_t s_used;
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
   const int64_t t_lin = xcd_tile(blockIdx.x, gridDim.x);
-  const int64_t r0 = (t_lin / col_tiles) * kBM;
-  const int64_t n0 = (t_lin % col_tiles) * BN;
+  const int64_t tile = t_lin / col_tiles;
+  const int n0 = (int)(t_lin % col_tiles) * BN;
 
-  if (tid == 0) s_used = 0;
-  __syncthreads();
-  uint32_t used = 0;
-  for (int idx = tid; idx < 27 * kBM; idx += 256) {
-    const int o = idx / kBM, r = idx - o * kBM;
-    const int32_t v = r0 + r < N ? map[(size_t)o * (size_t)N + r0 + r] : -1;
-    s_map[o][r] = v;
-    if (v >= 0) used |= 1u << o;
-  }
-  if (used) atomicOr(&s_used, used);
+  s_perm[tid] = perm[tile * kBM + tid];
+  if (tid < kNOff) s_blk[tid] = blk[tile * kNOff + tid];
   __syncthreads();
   if (tid == 0) {
     int n = 0;
-    for (int o = 0; o < 27; ++o)
-      if ((s_used >> o) & 1u) s_olist[n++] = (uint8_t)o;
+    uint32_t u = 0;
+    for (int o = 0; o < kNOff; ++o)
+      if (s_blk[o]) {
+        s_olist[n++] = (uint8_t)o;
+        u |= 1u << o;
+      }
     s_nused = n;
+    s_used = u;
   }
   __syncthreads();
 
-  const int kslices = cin / kBK;
-  const int nchunks = s_nused * kslices;
-
-  // Loader: A has 128 rows x 4 segments of 16 B (2 per thread); B has BN rows x 4 (NB per thread).
-  uint4 ra[2], rb[NB];
-  auto load = [&](int c) {
-    const int o = s_olist[c / kslices];
-    const int kc = (c % kslices) * kBK;
+  // The tile's kernel-map entries of every used offset, in sorted-row order, go to LDS once:
+  // all loads are issued before the first wait, so the map's latency is paid once per tile.
+  {
+    const int32_t myrow = s_perm[tid];
+    const uint32_t used = myrow >= 0 ? s_used : 0u;
+    int32_t v[kNOff];
+    // Branch-free: unused entries load element 0 and are replaced by -1.
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int slot = tid + 256 * i;
-      const int row = slot >> 2, seg = slot & 3;
-      const int32_t src = s_map[o][row];
-      ra[i] = src >= 0 ? *(const uint4*)(feats + (size_t)src * cin + kc + seg * 8) : make_uint4(0, 0, 0, 0);
-    }
+    for (int o = 0; o < kNOff; ++o) v[o] = map[(used >> o) & 1u ? (size_t)o * (size_t)N + myrow : 0];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int slot = tid + 256 * i;
-      const int n = slot >> 2, seg = slot & 3;
-      rb[i] = *(const uint4*)(wt + ((size_t)o * cout + n0 + n) * cin + kc + seg * 8);
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int slot = tid + 256 * i;
-      *(uint4*)&s_a[buf][(slot >> 2) * kLD + (slot & 3) * 8] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int slot = tid + 256 * i;
-      *(uint4*)&s_b[buf][(slot >> 2) * kLD + (slot & 3) * 8] = rb[i];
-    }
-  };
-
-  const int wm = wave >> 1, wn = wave & 1;
-  f32x16 acc[2][NB];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NB; ++ni)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
-
-  if (nchunks > 0) {
-    load(0);
-    store(0);
+    for (int o = 0; o < kNOff; ++o) s_map[o][tid] = (used >> o) & 1u ? v[o] : -1;
   }
   __syncthreads();
-  const int arow = lane & 31, akg = (lane >> 5) * 8;
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < nchunks) load(c + 1);
+
+  const int ksl = cin / KC;  // chunks per offset
+  const int nchunks = s_nused * ksl;
+
+  // This lane's staged rows: row (wave*AI + q)*RPI + lane/SEG, granule slot lane%SEG, which
+  // holds the row's granule (lane%SEG) ^ swz (the swizzle is the same for every q).
+  const int gran = (lane % SEG) ^ ((lane >> 3) & (SEG - 1));
+  const uint16_t* bptr = wt + (size_t)(n0 + wave * BI * RPI + lane / SEG) * cin + gran * 8;
+  auto issue = [&](int c, uint4* st) {
+    const int o = s_olist[c / ksl];
+    const int kc = (c % ksl) * KC;
 #pragma unroll
-    for (int ks = 0; ks < kBK; ks += 16) {
-      bf16x8 a[2], b[NB];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        a[mi] = *(const bf16x8*)&s_a[buf][(wm * 64 + mi * 32 + arow) * kLD + ks + akg];
-#pragma unroll
-      for (int ni = 0; ni < NB; ++ni)
-        b[ni] = *(const bf16x8*)&s_b[buf][(wn * (BN / 2) + ni * 32 + arow) * kLD + ks + akg];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NB; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    for (int q = 0; q < AI; ++q) {
+      const int32_t src = s_map[o][(wave * AI + q) * RPI + lane / SEG];
+      const uint16_t* ap = src >= 0 ? feats + (size_t)src * cin + kc + gran * 8 : g_zero_row + kc + gran * 8;
+      __builtin_amdgcn_global_load_lds((const glb_void*)ap, (lds_void*)(st + (wave * AI + q) * 64), 16, 0, 0);
     }
-    if (c + 1 < nchunks) store(buf ^ 1);
+    const uint16_t* bsrc = bptr + (size_t)o * cout * cin + kc;
+#pragma unroll
+    for (int q = 0; q < BI; ++q)
+      __builtin_amdgcn_global_load_lds((const glb_void*)(bsrc + (size_t)q * RPI * cin),
+                                       (lds_void*)(st + A_BYTES / 16 + (wave * BI + q) * 64), 16, 0, 0);
+  };
+
+  f32x4 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int frow = lane & 15;
+  const int fsw = stage_swz<SEG>(frow);  // row bases are multiples of 16
+  auto compute = [&](int c, const uint4* st) {
+    const uint32_t vm = __builtin_amdgcn_readfirstlane(((uint32_t)s_blk[s_olist[c / ksl]] >> (wm * MI)) &
+                                                       ((1u << MI) - 1u));
+    const char* A = (const char*)st;
+    const char* B = A + A_BYTES;
+    // All fragments of the chunk are read before the first MFMA (skipped blocks included), so
+    // the LDS latency is paid once per chunk rather than once per 16-row block.
+    constexpr int KST = KC / 32;
+    bf16x8 a[KST][MI], b[KST][NI];
+#pragma unroll
+    for (int t = 0; t < KST; ++t) {
+      const int slot = (((t * 4) + (lane >> 4)) ^ fsw) * 16;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) b[t][ni] = *(const bf16x8*)(B + (wn * NW + ni * 16 + frow) * ROWB + slot);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) a[t][mi] = *(const bf16x8*)(A + (wm * MW + mi * 16 + frow) * ROWB + slot);
+    }
+#pragma unroll
+    for (int t = 0; t < KST; ++t) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        if ((vm >> mi) & 1u) {
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t][mi], b[t][ni], acc[mi][ni], 0, 0, 0);
+        }
+      }
+    }
+  };
+  // One chunk: start filling the other stage with chunk c+1, multiply chunk c, then wait for
+  // this wave's loads and meet the other waves.
+  auto step = [&](int c, const uint4* cur, uint4* nxt) {
+    if (c + 1 < nchunks) issue(c + 1, nxt);
+    compute(c, cur);
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+    __syncthreads();
+  };
+
+  if (nchunks > 0) issue(0, s_st0);
+  __builtin_amdgcn_s_waitcnt(0xF70);
+  __syncthreads();
+  for (int c = 0; c < nchunks; c += 2) {
+    step(c, s_st0, s_st1);
+    if (c + 1 < nchunks) step(c + 1, s_st1, s_st0);
+  }
+
+  // Output: rows in passes of OUT_ROWS through stage 0, granules swizzled by row; D layout of
+  // a 16x16 block: lane holds column lane%16 of rows 4*(lane/16) + j.
+  uint16_t* O = (uint16_t*)s_st0;
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int rb = wm * MW + mi * 16;
+      if (rb / OUT_ROWS == p) {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = rb - p * OUT_ROWS + (lane >> 4) * 4 + j;
+            const int col = wn * NW + ni * 16 + frow;
+            O[row * BN + (((col >> 3) ^ (row & 7)) << 3) + (col & 7)] = f32_to_bf16_rne(acc[mi][ni][j]);
+          }
+      }
+    }
+    __syncthreads();
+    for (int s = tid; s < OUT_ROWS * OG; s += 256) {
+      const int row = s / OG, g = s % OG;
+      const int32_t r = s_perm[p * OUT_ROWS + row];
+      if (r >= 0)
+        *(uint4*)(out + (size_t)r * cout + n0 + g * 8) = *(const uint4*)&O[row * BN + ((g ^ (row & 7)) << 3)];
+    }
     __syncthreads();
   }
+}
 
-  // D layout of the 32x32 block: lane holds column lane%32, rows 8i + 4(lane/32) + j.
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NB; ++ni)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t row = r0 + wm * 64 + mi * 32 + 8 * i + (lane >> 5) * 4 + j;
-          const int64_t col = n0 + wn * (BN / 2) + ni * 32 + (lane & 31);
-          if (row < N) out[row * cout + col] = f32_to_bf16_rne(acc[mi][ni][4 * i + j]);
-        }
+template <int BN, int KC, int WM>
+void launch_main(int64_t n_tiles, int64_t col_tiles, const int32_t* map, int64_t N, const int32_t* perm,
+                 const uint16_t* blk, const void* feats, const uint16_t* wt, int cin, int cout, void* out,
+                 hipStream_t s) {
+  k_conv_ggs_bf16<BN, KC, WM><<<(unsigned)(n_tiles * col_tiles), 256, 0, s>>>(
+      map, N, perm, blk, (const uint16_t*)feats, wt, cin, cout, (uint16_t*)out, col_tiles);
 }
 
 }  // namespace
@@ -197,25 +341,38 @@ int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats
                     const void* d_w, int32_t cout, void* d_out, hipStream_t s) {
   (void)dtype;
   const int64_t N = g->n_voxels;
-  uint16_t* wt = nullptr;
-  int rc = dev_alloc((void**)&wt, (size_t)27 * cin * cout * 2, s, "igc_sparse_conv: transposed weights");
+  const int64_t n_tiles = (N + kBM - 1) / kBM;
+  const size_t wt_bytes = align_up((size_t)27 * cin * cout * 2, 256);
+  const size_t perm_bytes = align_up((size_t)n_tiles * kBM * 4, 256);
+  const size_t blk_bytes = align_up((size_t)n_tiles * kNOff * 2, 256);
+  char* ws = nullptr;
+  int rc = dev_alloc((void**)&ws, wt_bytes + perm_bytes + blk_bytes, s, "igc_sparse_conv: gather-GEMM-scatter workspace");
   if (rc) return rc;
+  uint16_t* wt = (uint16_t*)ws;
+  int32_t* perm = (int32_t*)(ws + wt_bytes);
+  uint16_t* blk = (uint16_t*)(ws + wt_bytes + perm_bytes);
   k_transpose_w<<<256, 256, 0, s>>>((const uint16_t*)d_w, wt, cin, cout);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) {
-    const int64_t row_tiles = (N + kBM - 1) / kBM;
-    if (cout % 128 == 0) {
-      const int64_t col_tiles = cout / 128;
-      k_conv_ggs_bf16<128><<<(unsigned)(row_tiles * col_tiles), 256, 0, s>>>(
-          d_map, N, (const uint16_t*)d_feats, wt, cin, cout, (uint16_t*)d_out, col_tiles);
+    k_ggs_plan<<<(unsigned)n_tiles, kBM, 0, s>>>(d_map, N, perm, blk);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) {
+    const bool k64 = cin % 64 == 0;
+    // 256-channel tiles only with 64-channel chunks: the 256 x 256 accumulators take all 256
+    // AGPRs, and the 32-channel form needs more registers than remain.
+    if (cout % 256 == 0 && k64) {
+      launch_main<256, 64, 2>(n_tiles, cout / 256, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
+    } else if (cout % 128 == 0) {
+      if (k64) launch_main<128, 64, 2>(n_tiles, cout / 128, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      else launch_main<128, 32, 2>(n_tiles, cout / 128, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
     } else {
-      const int64_t col_tiles = cout / 64;
-      k_conv_ggs_bf16<64><<<(unsigned)(row_tiles * col_tiles), 256, 0, s>>>(
-          d_map, N, (const uint16_t*)d_feats, wt, cin, cout, (uint16_t*)d_out, col_tiles);
+      if (k64) launch_main<64, 64, 4>(n_tiles, cout / 64, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      else launch_main<64, 32, 4>(n_tiles, cout / 64, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
     }
     e = hipGetLastError();
   }
-  dev_free(wt, s);
+  dev_free(ws, s);
   if (e != hipSuccess) return hip_status(e, "igc_sparse_conv: gather-GEMM-scatter launch");
   return IGC_OK;
 }
