@@ -16,7 +16,7 @@
 // neighbour mask give threads uniform work), so the pages' per-offset pair lists padded to 16
 // become "the blocks whose bit is set".
 //
-// k_conv_ggs_bf16, one workgroup (4 waves) per tile x BN output channels, output-stationary:
+// k_conv_ggs_bf16, one workgroup per tile x BN output channels, output-stationary:
 // the fp32 accumulators of the 256 x BN tile stay in registers for the whole reduction, so
 // every offset's product is "scattered" into registers and each output row is written once,
 // with no atomics and a fixed summation order (deterministic). The reduction runs over chunks
@@ -141,24 +141,32 @@ __device__ __forceinline__ int stage_swz(int r) {
   return SEG == 8 ? (r & 7) : ((r >> 1) & 3);
 }
 
+// vmcnt(n): wait until at most n vector-memory operations of this wave are outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+}
+
 // BN output channels per workgroup, KC input channels per chunk, WM waves along the rows
-// (4 / WM along the channels).
-template <int BN, int KC, int WM>
-__global__ __launch_bounds__(256) void k_conv_ggs_bf16(const int32_t* __restrict__ map, int64_t N,
+// (NWV / WM along the channels), NST LDS stages (NST - 1 chunks of loads in flight), NWV waves.
+template <int BN, int KC, int WM, int NST, int NWV>
+__global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __restrict__ map, int64_t N,
                                                        const int32_t* __restrict__ perm,
                                                        const uint16_t* __restrict__ blk,
                                                        const uint16_t* __restrict__ feats,
                                                        const uint16_t* __restrict__ wt, int cin, int cout,
                                                        uint16_t* __restrict__ out, int64_t col_tiles) {
-  constexpr int WN = 4 / WM;
+  constexpr int NT = 64 * NWV;  // threads
+  constexpr int WN = NWV / WM;
   constexpr int MW = kBM / WM;  // rows per wave
   constexpr int NW = BN / WN;   // channels per wave
   constexpr int MI = MW / 16, NI = NW / 16;
   constexpr int SEG = KC / 8;                 // 16-byte granules per staged row
   constexpr int ROWB = KC * 2;                // bytes per staged row
   constexpr int RPI = 64 / SEG;               // rows filled by one wave-wide LDS load
-  constexpr int AI = kBM / RPI / 4;           // A loads per wave and chunk
-  constexpr int BI = BN / RPI / 4;            // B loads per wave and chunk
+  constexpr int AI = kBM / RPI / NWV;         // A loads per wave and chunk
+  constexpr int BI = BN / RPI / NWV;          // B loads per wave and chunk
   constexpr int A_BYTES = kBM * ROWB, B_BYTES = BN * ROWB;
   constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   constexpr int OUT_ROWS = 128 * BN * 2 <= STAGE_BYTES ? 128 : (64 * BN * 2 <= STAGE_BYTES ? 64 : 32);
@@ -166,10 +174,15 @@ __global__ __launch_bounds__(256) void k_conv_ggs_bf16(const int32_t* __restrict
   constexpr int OG = BN / 8;                  // 16-byte granules per output row
   static_assert(MI >= 1 && NI >= 1 && AI >= 1 && BI >= 1, "tile shape");
   static_assert(OUT_ROWS * BN * 2 <= STAGE_BYTES && OG >= 8, "output pass fits one stage");
-  // Two stages as two objects: the compiler then sees that the loads into one stage never
-  // feed the fragment reads of the other and does not wait for them.
+  static_assert(NST == 2 || NST == 4, "stages");
+  constexpr int LPC = AI + BI;  // loads per wave and chunk
+  static_assert((NST - 2) * LPC < 64, "vmcnt range");
+  // Stages as separate objects: the compiler then sees that the loads into one stage never
+  // feed the fragment reads of another and does not wait for them.
   __shared__ uint4 s_st0[STAGE_BYTES / 16];
   __shared__ uint4 s_st1[STAGE_BYTES / 16];
+  __shared__ uint4 s_st2[NST > 2 ? STAGE_BYTES / 16 : 1];
+  __shared__ uint4 s_st3[NST > 2 ? STAGE_BYTES / 16 : 1];
   __shared__ int32_t s_perm[kBM];
   __shared__ int32_t s_map[kNOff][kBM];
   __shared__ uint16_t s_blk[kNOff];
@@ -185,7 +198,7 @@ __global__ __launch_bounds__(256) void k_conv_ggs_bf16(const int32_t* __restrict
   const int64_t tile = t_lin / col_tiles;
   const int n0 = (int)(t_lin % col_tiles) * BN;
 
-  s_perm[tid] = perm[tile * kBM + tid];
+  for (int r = tid; r < kBM; r += NT) s_perm[r] = perm[tile * kBM + r];
   if (tid < kNOff) s_blk[tid] = blk[tile * kNOff + tid];
   __syncthreads();
   if (tid == 0) {
@@ -204,14 +217,25 @@ __global__ __launch_bounds__(256) void k_conv_ggs_bf16(const int32_t* __restrict
   // The tile's kernel-map entries of every used offset, in sorted-row order, go to LDS once:
   // all loads are issued before the first wait, so the map's latency is paid once per tile.
   {
-    const int32_t myrow = s_perm[tid];
+    // kBM rows x 27 offsets over NT threads: thread t takes row t % kBM and every
+    // (NT / kBM)-th offset starting at t / kBM.
+    constexpr int OSTEP = NT / kBM;
+    constexpr int OPT = (kNOff + OSTEP - 1) / OSTEP;
+    const int row = tid % kBM, o0 = tid / kBM;
+    const int32_t myrow = s_perm[row];
     const uint32_t used = myrow >= 0 ? s_used : 0u;
-    int32_t v[kNOff];
+    int32_t v[OPT];
     // Branch-free: unused entries load element 0 and are replaced by -1.
 #pragma unroll
-    for (int o = 0; o < kNOff; ++o) v[o] = map[(used >> o) & 1u ? (size_t)o * (size_t)N + myrow : 0];
+    for (int i = 0; i < OPT; ++i) {
+      const int o = o0 + OSTEP * i;
+      v[i] = (o < kNOff && ((used >> o) & 1u)) ? map[(size_t)o * (size_t)N + myrow] : map[0];
+    }
 #pragma unroll
-    for (int o = 0; o < kNOff; ++o) s_map[o][tid] = (used >> o) & 1u ? v[o] : -1;
+    for (int i = 0; i < OPT; ++i) {
+      const int o = o0 + OSTEP * i;
+      if (o < kNOff) s_map[o][row] = (used >> o) & 1u ? v[i] : -1;
+    }
   }
   __syncthreads();
 
@@ -251,45 +275,65 @@ __global__ __launch_bounds__(256) void k_conv_ggs_bf16(const int32_t* __restrict
                                                        ((1u << MI) - 1u));
     const char* A = (const char*)st;
     const char* B = A + A_BYTES;
-    // All fragments of the chunk are read before the first MFMA (skipped blocks included), so
-    // the LDS latency is paid once per chunk rather than once per 16-row block.
     constexpr int KST = KC / 32;
-    bf16x8 a[KST][MI], b[KST][NI];
-#pragma unroll
-    for (int t = 0; t < KST; ++t) {
+    // Fragments of k-step t+1 are read while the MFMAs of k-step t run; blocks without pairs
+    // at this offset skip their MFMAs (their fragments are read anyway).
+    bf16x8 a[2][MI], b[2][NI];
+    auto frags = [&](int t, int d) {
       const int slot = (((t * 4) + (lane >> 4)) ^ fsw) * 16;
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) b[t][ni] = *(const bf16x8*)(B + (wn * NW + ni * 16 + frow) * ROWB + slot);
+      for (int ni = 0; ni < NI; ++ni) b[d][ni] = *(const bf16x8*)(B + (wn * NW + ni * 16 + frow) * ROWB + slot);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) a[t][mi] = *(const bf16x8*)(A + (wm * MW + mi * 16 + frow) * ROWB + slot);
-    }
+      for (int mi = 0; mi < MI; ++mi) a[d][mi] = *(const bf16x8*)(A + (wm * MW + mi * 16 + frow) * ROWB + slot);
+    };
+    frags(0, 0);
 #pragma unroll
     for (int t = 0; t < KST; ++t) {
+      if (t + 1 < KST) frags(t + 1, (t + 1) & 1);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         if ((vm >> mi) & 1u) {
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t][mi], b[t][ni], acc[mi][ni], 0, 0, 0);
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t & 1][mi], b[t & 1][ni], acc[mi][ni], 0, 0, 0);
         }
       }
     }
   };
-  // One chunk: start filling the other stage with chunk c+1, multiply chunk c, then wait for
-  // this wave's loads and meet the other waves.
-  auto step = [&](int c, const uint4* cur, uint4* nxt) {
-    if (c + 1 < nchunks) issue(c + 1, nxt);
+  // Waits until chunk c+1 has landed while the chunks after it, up to `last`, stay in flight
+  // (every chunk issues exactly LPC loads per wave, and vmcnt retires them in order).
+  auto wait_next = [&](int ahead) {
+    if (NST > 2 && ahead >= 2) wait_vmcnt<(NST > 2 ? 2 * LPC : 0)>();
+    else if (NST > 2 && ahead == 1) wait_vmcnt<(NST > 2 ? LPC : 0)>();
+    else wait_vmcnt<0>();
+  };
+  // One chunk: start filling the stage freed by the previous chunk with chunk c+NST-1,
+  // multiply chunk c, wait for chunk c+1 and meet the other waves.
+  auto step = [&](int c, const uint4* cur, uint4* fill) {
+    if (c + NST - 1 < nchunks) issue(c + NST - 1, fill);
     compute(c, cur);
-    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+    const int last = (c + NST - 1 < nchunks ? c + NST - 1 : nchunks - 1);
+    wait_next(last - (c + 1));
     __syncthreads();
   };
 
   if (nchunks > 0) issue(0, s_st0);
-  __builtin_amdgcn_s_waitcnt(0xF70);
+  if (NST > 2) {
+    if (nchunks > 1) issue(1, s_st1);
+    if (nchunks > 2) issue(2, s_st2);
+  }
+  wait_next((NST > 2 ? (nchunks < NST - 1 ? nchunks : NST - 1) : 1) - 1);
   __syncthreads();
-  for (int c = 0; c < nchunks; c += 2) {
-    step(c, s_st0, s_st1);
-    if (c + 1 < nchunks) step(c + 1, s_st1, s_st0);
+  for (int c = 0; c < nchunks; c += NST) {
+    if (NST == 2) {
+      step(c, s_st0, s_st1);
+      if (c + 1 < nchunks) step(c + 1, s_st1, s_st0);
+    } else {
+      step(c, s_st0, s_st3);
+      if (c + 1 < nchunks) step(c + 1, s_st1, s_st0);
+      if (c + 2 < nchunks) step(c + 2, s_st2, s_st1);
+      if (c + 3 < nchunks) step(c + 3, s_st3, s_st2);
+    }
   }
 
   // Output: rows in passes of OUT_ROWS through stage 0, granules swizzled by row; D layout of
@@ -312,7 +356,7 @@ __global__ __launch_bounds__(256) void k_conv_ggs_bf16(const int32_t* __restrict
       }
     }
     __syncthreads();
-    for (int s = tid; s < OUT_ROWS * OG; s += 256) {
+    for (int s = tid; s < OUT_ROWS * OG; s += NT) {
       const int row = s / OG, g = s % OG;
       const int32_t r = s_perm[p * OUT_ROWS + row];
       if (r >= 0)
@@ -322,11 +366,11 @@ __global__ __launch_bounds__(256) void k_conv_ggs_bf16(const int32_t* __restrict
   }
 }
 
-template <int BN, int KC, int WM>
+template <int BN, int KC, int WM, int NST, int NWV>
 void launch_main(int64_t n_tiles, int64_t col_tiles, const int32_t* map, int64_t N, const int32_t* perm,
                  const uint16_t* blk, const void* feats, const uint16_t* wt, int cin, int cout, void* out,
                  hipStream_t s) {
-  k_conv_ggs_bf16<BN, KC, WM><<<(unsigned)(n_tiles * col_tiles), 256, 0, s>>>(
+  k_conv_ggs_bf16<BN, KC, WM, NST, NWV><<<(unsigned)(n_tiles * col_tiles), 64 * NWV, 0, s>>>(
       map, N, perm, blk, (const uint16_t*)feats, wt, cin, cout, (uint16_t*)out, col_tiles);
 }
 
@@ -359,16 +403,19 @@ int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats
   }
   if (e == hipSuccess) {
     const bool k64 = cin % 64 == 0;
-    // 256-channel tiles only with 64-channel chunks: the 256 x 256 accumulators take all 256
-    // AGPRs, and the 32-channel form needs more registers than remain.
+    // Tile shapes measured on MI355X: 256 x 256 with eight waves (two per SIMD), 256 x 128
+    // with sixteen, 256 x 64 with eight; 32-channel chunks when cin is not a multiple of 64.
+    const int64_t n256 = cout / 256, n128 = cout / 128, n64 = cout / 64;
     if (cout % 256 == 0 && k64) {
-      launch_main<256, 64, 2>(n_tiles, cout / 256, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      launch_main<256, 64, 2, 2, 8>(n_tiles, n256, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
+    } else if (cout % 128 == 0 && k64) {
+      launch_main<128, 64, 4, 2, 16>(n_tiles, n128, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
     } else if (cout % 128 == 0) {
-      if (k64) launch_main<128, 64, 2>(n_tiles, cout / 128, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
-      else launch_main<128, 32, 2>(n_tiles, cout / 128, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      launch_main<128, 32, 2, 2, 8>(n_tiles, n128, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
+    } else if (k64) {
+      launch_main<64, 64, 4, 2, 8>(n_tiles, n64, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
     } else {
-      if (k64) launch_main<64, 64, 4>(n_tiles, cout / 64, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
-      else launch_main<64, 32, 4>(n_tiles, cout / 64, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      launch_main<64, 32, 4, 2, 4>(n_tiles, n64, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
     }
     e = hipGetLastError();
   }
