@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "igc_oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-__all__ = ["build_library", "OracleGrid", "kernel_map", "conv", "standard_offsets", "num_threads"]
+__all__ = ["build_library", "OracleGrid", "kernel_map", "conv", "conv_rows", "standard_offsets", "num_threads"]
 
 
 def build_library(force: bool = True) -> str:
@@ -159,4 +159,22 @@ def conv(kmap: np.ndarray, feats: np.ndarray, w: np.ndarray, rows: np.ndarray | 
     R = N if r is None else r.shape[0]
     out = np.zeros((R, cout), np.float64)
     _load().orc_conv(_ptr(kmap), N, K, _ptr(f), cin, _ptr(ww), cout, _ptr(r), R, _ptr(out))
+    return out
+
+
+def conv_rows(nbrs: np.ndarray, feats_of: dict, w: np.ndarray) -> np.ndarray:
+    """The same submanifold convolution as ``conv`` for output rows given by their neighbour
+    lists: out[i] = sum over o with nbrs[i, o] >= 0 of W[o]^T feats[nbrs[i, o]], in float64.
+
+    nbrs int[R, K] (row i's entries of the kernel map), feats_of maps an input row to its
+    float32[cin] features (only the rows nbrs refers to are needed), w float32[K, cin, cout].
+    """
+    nbrs = np.asarray(nbrs)
+    ww = np.asarray(w, dtype=np.float64)
+    out = np.zeros((nbrs.shape[0], ww.shape[2]), np.float64)
+    for i in range(nbrs.shape[0]):
+        for o in range(nbrs.shape[1]):
+            s = int(nbrs[i, o])
+            if s >= 0:
+                out[i] += np.asarray(feats_of[s], dtype=np.float64) @ ww[o]
     return out

@@ -337,3 +337,18 @@ def test_conv_sampled_rows_equal_full():
     full = oracle.conv(m, f, w)
     rows = rng.choice(g.n, size=100, replace=False)
     assert np.array_equal(oracle.conv(m, f, w, rows=rows), full[rows])
+
+
+def test_conv_rows_equals_conv():
+    """conv_rows (neighbour lists of chosen rows) is the same definition as conv."""
+    c = workloads.random_coords(3000, -12, 12, seed=21)
+    g = oracle.OracleGrid(c)
+    m = g.kernel_map()
+    rng = np.random.default_rng(22)
+    f = rng.standard_normal((g.n, 5)).astype(np.float32)
+    w = rng.standard_normal((27, 5, 7)).astype(np.float32)
+    rows = np.sort(rng.choice(g.n, 64, replace=False))
+    nbrs = m[:, rows].T
+    ref = oracle.conv(m, f, w, rows=rows)
+    got = oracle.conv_rows(nbrs, {int(s): f[s] for s in np.unique(nbrs[nbrs >= 0])}, w)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)

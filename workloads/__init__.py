@@ -37,6 +37,7 @@ __all__ = [
     "lidar_coords",
     "large_band_coords",
     "random_coords",
+    "make_features_device",
 ]
 
 
@@ -359,3 +360,13 @@ def make_weights(cin: int, cout: int, seed: int, std: float | None) -> np.ndarra
     if std is not None:
         w *= np.float32(std)
     return w
+
+
+def make_features_device(n: int, cin: int, seed: int, device, dtype=None):
+    """float32[n, cin] ~ N(0, 1) drawn on `device` by torch's seeded generator (Philox on the
+    GPU), cast to `dtype` if given. For feature arrays too large to draw on the host."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    f = torch.randn((n, cin), generator=g, dtype=torch.float32, device=device)
+    return f if dtype is None else f.to(dtype)
