@@ -26,8 +26,8 @@
 // skipping the 16-row blocks that have no pair at that offset. Both operands go from global
 // memory straight into LDS (global_load_lds_dwordx4: no staging registers, which the 256 x 256
 // accumulators leave none of); the next chunk's loads are in flight while the current chunk is
-// multiplied (two LDS stages, one barrier per chunk), and the map entries of the offset after
-// next are fetched one chunk ahead so the gather never waits on the map. The output tile is
+// multiplied (two LDS stages, one barrier per chunk). The tile's map entries of every used
+// offset are staged in LDS once, so the gather never waits on the map. The output tile is
 // staged through LDS and leaves as whole rows.
 //
 // Staged rows are unpadded and their 16-byte granules XOR-swizzled by row, so the rows read

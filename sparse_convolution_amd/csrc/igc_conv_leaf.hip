@@ -32,7 +32,7 @@ __device__ __forceinline__ int64_t xcd_block(int64_t bid, int64_t nblk) {
 }
 
 template <int CIN, int COUT>
-__global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* __restrict__ feats,
+__global__ __launch_bounds__(256) void k_conv_leaf_f32_wide(GridView g, const float* __restrict__ feats,
                                                        const float* __restrict__ w, float* __restrict__ out) {
   constexpr int COUTP = (COUT + 15) / 16 * 16;
   constexpr int NS = COUTP / 16;  // 16-column MFMA slabs
@@ -155,10 +155,214 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
   }
 }
 
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Round to nearest even (finite inputs), as a 16-bit pattern.
+__device__ __forceinline__ uint16_t bf16_bits_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_value(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// v = hi + mid + lo exactly (three bf16 values of 8 significant bits each): each residual is
+// exact in fp32, and the last one has at most 8 significant bits left.
+__device__ __forceinline__ void split3(float v, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  hi = bf16_bits_rne(v);
+  const float r1 = v - bf16_value(hi);
+  mid = bf16_bits_rne(r1);
+  const float r2 = r1 - bf16_value(mid);
+  lo = bf16_bits_rne(r2);
+}
+
+// Window cell offset of stencil offset o relative to the cell of offset (-1,-1,-1).
+__device__ __forceinline__ int cell_delta(int o) { return (o / 9) * 100 + ((o / 3) % 3) * 10 + o % 3; }
+
+// fp32 leaf conv on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16). Same structure as the
+// fp32-MFMA form above: one workgroup per leaf, the 10^3 window in LDS, active voxels taken 16
+// at a time as the M dimension. Every fp32 operand is split into three bf16 parts whose sum is
+// exact (split3), and the product a*b is summed as the six partial products with index sum <= 2
+// (a2 b0, a1 b1, a0 b2, a1 b0, a0 b1, a0 b0), each exact in fp32 and accumulated in fp32; the
+// three dropped terms are below 2^-24 of |a b|, the size of fp32 rounding (the split-bf16
+// scheme of Henry, Tang & Heinecke, "Leveraging the bfloat16 artificial intelligence datatype
+// for higher-precision computations", 2019). The window holds the three splits of every cell,
+// made once when the window is filled, and W's splits stay in registers. K = 27 offsets x CIN
+// runs in chunks of 32: lane group g = lane/16 holds k = 8g..8g+7 of a chunk, i.e. one offset's
+// 8 channels (CIN 8) or two offsets' 4 channels (CIN 4); offsets past 26 are zero.
+template <int CIN, int COUT>
+__global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* __restrict__ feats,
+                                                       const float* __restrict__ w, float* __restrict__ out) {
+  static_assert(CIN == 4 || CIN == 8, "channel layout of the split form");
+  constexpr int COUTP = (COUT + 15) / 16 * 16;
+  constexpr int NS = COUTP / 16;
+  constexpr int OPG = 8 / CIN;                   // offsets per lane group and chunk
+  constexpr int NCH = (27 * CIN + 31) / 32;      // chunks of 32 k values
+  constexpr int CS = 3 * CIN;                    // bf16 elements per window cell (three splits)
+  __shared__ __attribute__((aligned(16))) uint16_t s_win[1000 * CS];
+  __shared__ uint64_t s_mask[27][8];
+  __shared__ uint64_t s_off[27];
+  __shared__ uint64_t s_pre[27];
+  __shared__ uint16_t s_pos[512];
+  __shared__ uint32_t s_count;
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const int rl = lane & 15;  // A row / B column / D column
+  const int kg = lane >> 4;  // k group of A and B, row group of D
+  const int64_t f = xcd_block(blockIdx.x, gridDim.x);
+
+  if (tid < 27) {
+    const int32_t nl = g.leaf_nbr[f * 27 + tid];
+    if (nl >= 0) {
+      const LeafRec& L = g.leaf[nl];
+      for (int q = 0; q < 8; ++q) s_mask[tid][q] = L.mask[q];
+      s_off[tid] = L.offset;
+      s_pre[tid] = L.prefix;
+    } else {
+      for (int q = 0; q < 8; ++q) s_mask[tid][q] = 0;
+      s_off[tid] = 0;
+      s_pre[tid] = 0;
+    }
+  }
+
+  // W splits for this lane: chunk q, split s, column slab ns -> 8 bf16 (k = 8 kg .. 8 kg + 7).
+  bf16x8 wb[NCH][3][NS];
+  int dcell[NCH][OPG];
+  bool dvalid[NCH][OPG];
+#pragma unroll
+  for (int q = 0; q < NCH; ++q) {
+#pragma unroll
+    for (int h = 0; h < OPG; ++h) {
+      const int o = (q * 32 + kg * 8) / CIN + h;
+      dvalid[q][h] = o < 27;
+      dcell[q][h] = cell_delta(o < 27 ? o : 0);
+    }
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      const int col = ns * 16 + rl;
+      uint16_t hs[8], ms[8], ls[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = q * 32 + kg * 8 + e;  // k = o * CIN + ci
+        const float v = (k < 27 * CIN && col < COUT) ? w[(size_t)k * COUT + col] : 0.f;
+        split3(v, hs[e], ms[e], ls[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        wb[q][0][ns][e] = __builtin_bit_cast(__bf16, hs[e]);
+        wb[q][1][ns][e] = __builtin_bit_cast(__bf16, ms[e]);
+        wb[q][2][ns][e] = __builtin_bit_cast(__bf16, ls[e]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // Compacted active positions of this leaf (wave 0), and the split window (all threads).
+  if (wave == 0) {
+    const uint64_t lt = (1ull << lane) - 1ull;
+    uint32_t count = 0;
+    for (int q = 0; q < 8; ++q) {
+      const uint64_t word = s_mask[13][q];
+      if ((word >> lane) & 1ull) s_pos[count + (uint32_t)__popcll(word & lt)] = (uint16_t)(q * 64 + lane);
+      count += (uint32_t)__popcll(word);
+    }
+    if (lane == 0) s_count = count;
+  }
+  for (int c = tid; c < 1000; c += 256) {
+    const int x = c / 100 - 1, y = (c / 10) % 10 - 1, z = c % 10 - 1;  // leaf-local, in [-1, 8]
+    const int slot = ((x >> 3) + 1) * 9 + ((y >> 3) + 1) * 3 + ((z >> 3) + 1);
+    const uint32_t q = (uint32_t)(x & 7);
+    const uint64_t bit = 1ull << ((uint32_t)((y & 7) << 3) | (uint32_t)(z & 7));
+    const uint64_t word = s_mask[slot][q];
+    float v[CIN];
+    if (word & bit) {
+      const uint32_t pre = q ? (uint32_t)(s_pre[slot] >> (9u * (q - 1u))) & 511u : 0u;
+      const uint64_t row = s_off[slot] + pre + (uint32_t)__popcll(word & (bit - 1ull));
+      const float4* src = (const float4*)(feats + row * CIN);
+#pragma unroll
+      for (int i = 0; i < CIN / 4; ++i) {
+        const float4 t = src[i];
+        v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CIN; ++i) v[i] = 0.f;
+    }
+    uint16_t hs[CIN], ms[CIN], ls[CIN];
+#pragma unroll
+    for (int i = 0; i < CIN; ++i) split3(v[i], hs[i], ms[i], ls[i]);
+    uint16_t* dst = &s_win[c * CS];
+#pragma unroll
+    for (int i = 0; i < CIN; ++i) {
+      dst[i] = hs[i];
+      dst[CIN + i] = ms[i];
+      dst[2 * CIN + i] = ls[i];
+    }
+  }
+  __syncthreads();
+
+  const uint32_t count = s_count;
+  const uint64_t base = s_off[13];
+  for (uint32_t g0 = (uint32_t)wave * 16; g0 < count; g0 += 64) {
+    const uint32_t t = g0 + rl;
+    const uint32_t p = s_pos[t < count ? t : 0];
+    const int cell0 = (int)((p >> 6) * 100 + ((p >> 3) & 7u) * 10 + (p & 7u));  // cell of offset (-1,-1,-1)
+    f32x4 acc[NS];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) acc[ns] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      bf16x8 a[3];
+#pragma unroll
+      for (int sp = 0; sp < 3; ++sp) {
+        if constexpr (CIN == 8) {
+          const bf16x8 v = *(const bf16x8*)&s_win[(cell0 + dcell[q][0]) * CS + sp * CIN];
+          a[sp] = dvalid[q][0] ? v : bf16x8{};
+        } else {
+          const uint2 v0 = *(const uint2*)&s_win[(cell0 + dcell[q][0]) * CS + sp * CIN];
+          const uint2 v1 = *(const uint2*)&s_win[(cell0 + dcell[q][1]) * CS + sp * CIN];
+          const uint4 u = make_uint4(dvalid[q][0] ? v0.x : 0u, dvalid[q][0] ? v0.y : 0u, dvalid[q][1] ? v1.x : 0u,
+                                     dvalid[q][1] ? v1.y : 0u);
+          a[sp] = __builtin_bit_cast(bf16x8, u);
+        }
+      }
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) {
+        f32x4 c = acc[ns];
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], wb[q][0][ns], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], wb[q][1][ns], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], wb[q][2][ns], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], wb[q][0][ns], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], wb[q][1][ns], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], wb[q][0][ns], c, 0, 0, 0);
+        acc[ns] = c;
+      }
+    }
+    // D: lane holds column lane%16 of rows 4*(lane/16) + j.
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t r = g0 + (uint32_t)kg * 4 + j;
+        const int col = ns * 16 + rl;
+        if (r < count && col < COUT) out[(base + r) * COUT + col] = acc[ns][j];
+      }
+  }
+}
+
 template <int CIN, int COUT>
 int launch_leaf(const igc_grid* g, const void* d_feats, const void* d_w, void* d_out, hipStream_t s) {
-  k_conv_leaf_f32<CIN, COUT><<<(unsigned)g->n_leaf, 256, 0, s>>>(g->view(), (const float*)d_feats, (const float*)d_w,
-                                                                 (float*)d_out);
+  // Split-bf16 form for 4 or 8 input channels and up to 32 (CIN 4) / 16 (CIN 8) outputs, whose
+  // W splits fit in registers; the fp32-MFMA form for the wider shapes.
+  constexpr bool split = (CIN == 4 && COUT <= 32) || (CIN == 8 && COUT <= 16);
+  if constexpr (split)
+    k_conv_leaf_f32<CIN, COUT><<<(unsigned)g->n_leaf, 256, 0, s>>>(g->view(), (const float*)d_feats,
+                                                                  (const float*)d_w, (float*)d_out);
+  else
+    k_conv_leaf_f32_wide<CIN, COUT><<<(unsigned)g->n_leaf, 256, 0, s>>>(g->view(), (const float*)d_feats,
+                                                                       (const float*)d_w, (float*)d_out);
   IGC_HIP(hipGetLastError(), "igc_sparse_conv: leaf launch");
   return IGC_OK;
 }
