@@ -187,12 +187,38 @@ __device__ __forceinline__ int cell_delta(int o) { return (o / 9) * 100 + ((o / 
 // three dropped terms are below 2^-24 of |a b|, the size of fp32 rounding (the split-bf16
 // scheme of Henry, Tang & Heinecke, "Leveraging the bfloat16 artificial intelligence datatype
 // for higher-precision computations", 2019). The window holds the three splits of every cell,
-// made once when the window is filled, and W's splits stay in registers. K = 27 offsets x CIN
-// runs in chunks of 32: lane group g = lane/16 holds k = 8g..8g+7 of a chunk, i.e. one offset's
-// 8 channels (CIN 8) or two offsets' 4 channels (CIN 4); offsets past 26 are zero.
+// made once when the window is filled; W's splits are made once per call (k_leaf_wsplit) and
+// stay in registers. K = 27 offsets x CIN runs in chunks of 32: lane group g = lane/16 holds
+// k = 8g..8g+7 of a chunk, i.e. one offset's 8 channels (CIN 8) or two offsets' 4 channels
+// (CIN 4); offsets past 26 are zero.
+template <int CIN, int COUT>
+__global__ __launch_bounds__(64) void k_leaf_wsplit(const float* __restrict__ w, bf16x8* __restrict__ wsplit) {
+  constexpr int COUTP = (COUT + 15) / 16 * 16;
+  constexpr int NS = COUTP / 16;
+  constexpr int NCH = (27 * CIN + 31) / 32;
+  const int lane = threadIdx.x, rl = lane & 15, kg = lane >> 4;
+  for (int q = 0; q < NCH; ++q)
+    for (int ns = 0; ns < NS; ++ns) {
+      const int col = ns * 16 + rl;
+      bf16x8 h, m, l;
+      for (int e = 0; e < 8; ++e) {
+        const int k = q * 32 + kg * 8 + e;  // k = o * CIN + ci
+        const float v = (k < 27 * CIN && col < COUT) ? w[(size_t)k * COUT + col] : 0.f;
+        uint16_t hs, ms, ls;
+        split3(v, hs, ms, ls);
+        h[e] = __builtin_bit_cast(__bf16, hs);
+        m[e] = __builtin_bit_cast(__bf16, ms);
+        l[e] = __builtin_bit_cast(__bf16, ls);
+      }
+      wsplit[((q * 3 + 0) * NS + ns) * 64 + lane] = h;
+      wsplit[((q * 3 + 1) * NS + ns) * 64 + lane] = m;
+      wsplit[((q * 3 + 2) * NS + ns) * 64 + lane] = l;
+    }
+}
+
 template <int CIN, int COUT>
 __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* __restrict__ feats,
-                                                       const float* __restrict__ w, float* __restrict__ out) {
+                                                       const bf16x8* __restrict__ wsplit, float* __restrict__ out) {
   static_assert(CIN == 4 || CIN == 8, "channel layout of the split form");
   constexpr int COUTP = (COUT + 15) / 16 * 16;
   constexpr int NS = COUTP / 16;
@@ -227,7 +253,8 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
     }
   }
 
-  // W splits for this lane: chunk q, split s, column slab ns -> 8 bf16 (k = 8 kg .. 8 kg + 7).
+  // W splits for this lane (made once per call by k_leaf_wsplit): chunk q, split s, column
+  // slab ns -> 8 bf16 (k = 8 kg .. 8 kg + 7).
   bf16x8 wb[NCH][3][NS];
   int dcell[NCH][OPG];
   bool dvalid[NCH][OPG];
@@ -240,22 +267,9 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
       dcell[q][h] = cell_delta(o < 27 ? o : 0);
     }
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) {
-      const int col = ns * 16 + rl;
-      uint16_t hs[8], ms[8], ls[8];
+    for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int k = q * 32 + kg * 8 + e;  // k = o * CIN + ci
-        const float v = (k < 27 * CIN && col < COUT) ? w[(size_t)k * COUT + col] : 0.f;
-        split3(v, hs[e], ms[e], ls[e]);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        wb[q][0][ns][e] = __builtin_bit_cast(__bf16, hs[e]);
-        wb[q][1][ns][e] = __builtin_bit_cast(__bf16, ms[e]);
-        wb[q][2][ns][e] = __builtin_bit_cast(__bf16, ls[e]);
-      }
-    }
+      for (int ns = 0; ns < NS; ++ns) wb[q][sp][ns] = wsplit[((q * 3 + sp) * NS + ns) * 64 + lane];
   }
   __syncthreads();
 
@@ -270,35 +284,55 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
     }
     if (lane == 0) s_count = count;
   }
-  for (int c = tid; c < 1000; c += 256) {
+  // Window: up to four cells per thread; all their feature loads are issued before the first
+  // split so that their latencies overlap.
+  constexpr int CPT = (1000 + 255) / 256;
+  float v[CPT][CIN];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + 256 * i;
     const int x = c / 100 - 1, y = (c / 10) % 10 - 1, z = c % 10 - 1;  // leaf-local, in [-1, 8]
     const int slot = ((x >> 3) + 1) * 9 + ((y >> 3) + 1) * 3 + ((z >> 3) + 1);
     const uint32_t q = (uint32_t)(x & 7);
     const uint64_t bit = 1ull << ((uint32_t)((y & 7) << 3) | (uint32_t)(z & 7));
-    const uint64_t word = s_mask[slot][q];
-    float v[CIN];
+    const uint64_t word = c < 1000 ? s_mask[slot][q] : 0ull;
     if (word & bit) {
       const uint32_t pre = q ? (uint32_t)(s_pre[slot] >> (9u * (q - 1u))) & 511u : 0u;
       const uint64_t row = s_off[slot] + pre + (uint32_t)__popcll(word & (bit - 1ull));
       const float4* src = (const float4*)(feats + row * CIN);
 #pragma unroll
-      for (int i = 0; i < CIN / 4; ++i) {
-        const float4 t = src[i];
-        v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+      for (int j = 0; j < CIN / 4; ++j) {
+        const float4 t = src[j];
+        v[i][4 * j] = t.x; v[i][4 * j + 1] = t.y; v[i][4 * j + 2] = t.z; v[i][4 * j + 3] = t.w;
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < CIN; ++i) v[i] = 0.f;
+      for (int j = 0; j < CIN; ++j) v[i][j] = 0.f;
     }
-    uint16_t hs[CIN], ms[CIN], ls[CIN];
+  }
 #pragma unroll
-    for (int i = 0; i < CIN; ++i) split3(v[i], hs[i], ms[i], ls[i]);
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + 256 * i;
+    if (c >= 1000) break;
+    uint32_t hw[CIN / 2], mw[CIN / 2], lw[CIN / 2];
+#pragma unroll
+    for (int j = 0; j < CIN / 2; ++j) {
+      uint16_t h0, m0, l0, h1, m1, l1;
+      split3(v[i][2 * j], h0, m0, l0);
+      split3(v[i][2 * j + 1], h1, m1, l1);
+      hw[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      mw[j] = (uint32_t)m0 | ((uint32_t)m1 << 16);
+      lw[j] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
     uint16_t* dst = &s_win[c * CS];
-#pragma unroll
-    for (int i = 0; i < CIN; ++i) {
-      dst[i] = hs[i];
-      dst[CIN + i] = ms[i];
-      dst[2 * CIN + i] = ls[i];
+    if constexpr (CIN == 8) {
+      *(uint4*)&dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *(uint4*)&dst[8] = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+      *(uint4*)&dst[16] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    } else {
+      *(uint2*)&dst[0] = make_uint2(hw[0], hw[1]);
+      *(uint2*)&dst[4] = make_uint2(mw[0], mw[1]);
+      *(uint2*)&dst[8] = make_uint2(lw[0], lw[1]);
     }
   }
   __syncthreads();
@@ -357,13 +391,26 @@ int launch_leaf(const igc_grid* g, const void* d_feats, const void* d_w, void* d
   // Split-bf16 form for 4 or 8 input channels and up to 32 (CIN 4) / 16 (CIN 8) outputs, whose
   // W splits fit in registers; the fp32-MFMA form for the wider shapes.
   constexpr bool split = (CIN == 4 && COUT <= 32) || (CIN == 8 && COUT <= 16);
-  if constexpr (split)
-    k_conv_leaf_f32<CIN, COUT><<<(unsigned)g->n_leaf, 256, 0, s>>>(g->view(), (const float*)d_feats,
-                                                                  (const float*)d_w, (float*)d_out);
-  else
+  if constexpr (split) {
+    constexpr int NS = (COUT + 15) / 16;
+    constexpr int NCH = (27 * CIN + 31) / 32;
+    bf16x8* ws = nullptr;
+    int rc = dev_alloc((void**)&ws, (size_t)NCH * 3 * NS * 64 * sizeof(bf16x8), s, "igc_sparse_conv: W splits");
+    if (rc) return rc;
+    k_leaf_wsplit<CIN, COUT><<<1, 64, 0, s>>>((const float*)d_w, ws);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) {
+      k_conv_leaf_f32<CIN, COUT><<<(unsigned)g->n_leaf, 256, 0, s>>>(g->view(), (const float*)d_feats, ws,
+                                                                    (float*)d_out);
+      e = hipGetLastError();
+    }
+    dev_free(ws, s);
+    if (e != hipSuccess) return hip_status(e, "igc_sparse_conv: leaf launch");
+  } else {
     k_conv_leaf_f32_wide<CIN, COUT><<<(unsigned)g->n_leaf, 256, 0, s>>>(g->view(), (const float*)d_feats,
                                                                        (const float*)d_w, (float*)d_out);
-  IGC_HIP(hipGetLastError(), "igc_sparse_conv: leaf launch");
+    IGC_HIP(hipGetLastError(), "igc_sparse_conv: leaf launch");
+  }
   return IGC_OK;
 }
 
