@@ -44,7 +44,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kKeysPerThread = 16;
-constexpr int kTileKeys = kThreads * kKeysPerThread;  // 4096 keys per onesweep tile
+constexpr int kTileKeys = kThreads * kKeysPerThread;  // 4096 keys per counting / registration block
+constexpr int kSortKPT = 16;                           // keys per thread of a radix pass
+constexpr int kSortTile = kThreads * kSortKPT;         // keys per onesweep tile
 constexpr int kMaxPasses = 8;
 constexpr uint64_t kLbAggregate = 1ull << 62;
 constexpr uint64_t kLbInclusive = 2ull << 62;
@@ -419,12 +421,12 @@ __global__ __launch_bounds__(256) void k_hist(const uint64_t* __restrict__ keys,
   hist_flush(s_hist, hist, ps);
 }
 
-// One LSD pass over the 8-bit digit at `shift`: stable, tile of 4096 keys per workgroup.
+// One LSD pass over the 8-bit digit at `shift`: stable, tile of kSortTile keys per workgroup.
 __global__ __launch_bounds__(256) void k_onesweep(const uint64_t* __restrict__ src, uint64_t* __restrict__ dst,
                                                   int64_t n, int shift, const uint32_t* __restrict__ hist,
                                                   uint64_t* __restrict__ lookback, uint32_t* tile_counter,
                                                   uint32_t* timeout, uint32_t* guard) {
-  __shared__ uint64_t s_keys[kTileKeys];
+  __shared__ uint64_t s_keys[kSortTile];
   __shared__ uint32_t s_cnt[4][256];
   __shared__ uint32_t s_tile_start[256];
   __shared__ int64_t s_base[256];
@@ -438,19 +440,19 @@ __global__ __launch_bounds__(256) void k_onesweep(const uint64_t* __restrict__ s
   for (int x = tid; x < 4 * 256; x += kThreads) (&s_cnt[0][0])[x] = 0;
   __syncthreads();
   const int64_t tile = s_tile;
-  const int64_t tile_base = tile * kTileKeys;
+  const int64_t tile_base = tile * kSortTile;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
 
   // Stable rank of every key among equal digits of its wave (blocked: wave w owns the
-  // tile's keys [w*1024, (w+1)*1024), 64 consecutive keys per round). All loads are issued
+  // tile's keys [w*64*kSortKPT, (w+1)*64*kSortKPT), 64 consecutive keys per round). All loads are issued
   // before the first ballot so that their latency overlaps.
-  uint64_t key[kKeysPerThread];
-  uint32_t rank[kKeysPerThread];
-  const int64_t wbase = tile_base + wave * 1024 + lane;
+  uint64_t key[kSortKPT];
+  uint32_t rank[kSortKPT];
+  const int64_t wbase = tile_base + wave * (64 * kSortKPT) + lane;
 #pragma unroll
-  for (int r = 0; r < kKeysPerThread; ++r) key[r] = wbase + r * 64 < n ? src[wbase + r * 64] : 0ull;
+  for (int r = 0; r < kSortKPT; ++r) key[r] = wbase + r * 64 < n ? src[wbase + r * 64] : 0ull;
 #pragma unroll
-  for (int r = 0; r < kKeysPerThread; ++r) {
+  for (int r = 0; r < kSortKPT; ++r) {
     const bool valid = wbase + r * 64 < n;
     const uint32_t d = (uint32_t)(key[r] >> shift) & 255u;
     uint64_t m = __ballot(valid);
@@ -534,16 +536,16 @@ __global__ __launch_bounds__(256) void k_onesweep(const uint64_t* __restrict__ s
 
   // Digit-sorted order inside the tile, staged in LDS.
 #pragma unroll
-  for (int r = 0; r < kKeysPerThread; ++r) {
+  for (int r = 0; r < kSortKPT; ++r) {
     if (wbase + r * 64 < n) {
       const uint32_t dd = (uint32_t)(key[r] >> shift) & 255u;
       s_keys[s_tile_start[dd] + s_cnt[wave][dd] + rank[r]] = key[r];
     }
   }
   __syncthreads();
-  const int64_t valid_count = n - tile_base < kTileKeys ? n - tile_base : kTileKeys;
+  const int64_t valid_count = n - tile_base < kSortTile ? n - tile_base : kSortTile;
 #pragma unroll
-  for (int q = 0; q < kKeysPerThread; ++q) {
+  for (int q = 0; q < kSortKPT; ++q) {
     const int p = q * kThreads + tid;
     if (p < valid_count) {
       const uint64_t k = s_keys[p];
@@ -556,10 +558,13 @@ __global__ __launch_bounds__(256) void k_onesweep(const uint64_t* __restrict__ s
 // Sorts keys[0..n) (in a, scratch b) over the digits of ps; returns the buffer holding the
 // result. The histograms must already be in `hist` ([passes][256]).
 int onesweep_sort(uint64_t* a, uint64_t* b, int64_t n, PassSpec ps, const uint32_t* hist, uint64_t* lb,
-                  uint32_t* tile_counters, uint32_t* timeout, uint32_t* guard, hipStream_t s, uint64_t** result) {
+                  int64_t lb_tiles, uint32_t* tile_counters, uint32_t* timeout, uint32_t* guard, hipStream_t s,
+                  uint64_t** result) {
   *result = a;
   if (n <= 0 || ps.passes == 0) return IGC_OK;
-  const int64_t tiles = (n + kTileKeys - 1) / kTileKeys;
+  const int64_t tiles = (n + kSortTile - 1) / kSortTile;
+  if (tiles > lb_tiles || ps.passes > kMaxPasses)
+    return set_error(IGC_ERR_INTERNAL, "igc_grid_build: radix look-back buffer too small");
   int st = fill_u64(lb, (int64_t)ps.passes * tiles * 256, 0, s);
   if (st) return st;
   uint64_t* src = a;
@@ -827,9 +832,10 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   // Workspace sizes depend on n_in only (the tile lists of more than kSmallSort tiles are
   // allocated on their own once U is known).
   const int64_t tiles = (n_in + kTileKeys - 1) / kTileKeys;
+  const int64_t sort_tiles = (n_in + kSortTile - 1) / kSortTile;
   const size_t ws = align_up(sizeof(BuildState), 256) + align_up((size_t)kTileBlocks * 32, 256) +
                     align_up(2 * kMaxPasses * 256 * 4, 256) + align_up((size_t)kHistBlocks * kMaxPasses * 256 * 4, 256) +
-                    2 * align_up((size_t)n_in * 8, 256) + align_up((size_t)kMaxPasses * tiles * 256 * 8, 256) +
+                    2 * align_up((size_t)n_in * 8, 256) + align_up((size_t)kMaxPasses * sort_tiles * 256 * 8, 256) +
                     align_up((size_t)tiles * 8, 256) + align_up((size_t)tiles * 32, 256) +
                     2 * align_up((size_t)kSmallSort * 8, 256);
   Arena ar(s);
@@ -841,7 +847,7 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   uint32_t* hpart = ar.take<uint32_t>((size_t)kHistBlocks * kMaxPasses * 256 * 4);
   uint64_t* ka = ar.take<uint64_t>((size_t)n_in * 8);
   uint64_t* kb = ar.take<uint64_t>((size_t)n_in * 8);
-  uint64_t* lookback = ar.take<uint64_t>((size_t)kMaxPasses * tiles * 256 * 8);
+  uint64_t* lookback = ar.take<uint64_t>((size_t)kMaxPasses * sort_tiles * 256 * 8);
   uint64_t* bcounts = ar.take<uint64_t>((size_t)tiles * 8);
   uint64_t* bprefix = ar.take<uint64_t>((size_t)tiles * 32);
   uint64_t* tile_list = ar.take<uint64_t>((size_t)kSmallSort * 8);
@@ -912,9 +918,9 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
     k_hist_reduce<<<tps.passes * 4, 256, 0, s>>>(hpart, nbh, tps.passes * 256, hist + kMaxPasses * 256);
     IGC_HIP(hipGetLastError(), "igc_grid_build: tile histogram reduce launch");
     uint64_t* tlb = nullptr;
-    const int64_t ttiles = (U + kTileKeys - 1) / kTileKeys;
+    const int64_t ttiles = (U + kSortTile - 1) / kSortTile;
     if ((rc = ar.get_extra(&tlb, (size_t)kMaxPasses * ttiles * 256 * 8, "igc_grid_build: tile look-back"))) return rc;
-    if ((rc = onesweep_sort(tile_list, tile_tmp, U, tps, hist + kMaxPasses * 256, tlb, st->tile_counter + kMaxPasses,
+    if ((rc = onesweep_sort(tile_list, tile_tmp, U, tps, hist + kMaxPasses * 256, tlb, ttiles, st->tile_counter + kMaxPasses,
                             &st->lookback_timeout, &st->guard, s, &tiles_sorted)))
       return rc;
   }
@@ -935,7 +941,7 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
     IGC_HIP(hipGetLastError(), "igc_grid_build: histogram reduce launch");
   }
   uint64_t* sorted = ka;
-  if ((rc = onesweep_sort(ka, kb, n_in, ps, hist, lookback, st->tile_counter, &st->lookback_timeout, &st->guard, s,
+  if ((rc = onesweep_sort(ka, kb, n_in, ps, hist, lookback, sort_tiles, st->tile_counter, &st->lookback_timeout, &st->guard, s,
                           &sorted)))
     return rc;
 
