@@ -17,11 +17,12 @@
 //     (12 bits) << 9 | leaf voxel (9 bits). The pass that writes key2 also builds the digit
 //     histograms of every radix pass, and only the bit span where keys differ is sorted
 //     (the OR and AND of all keys, taken in the tile pass, give that span).
-//  3. The sort is an LSD radix sort with 8-bit digits in the onesweep form: one read and one
-//     write of the keys per pass, ranks from 64-lane ballots (stable multisplit), a tile of
-//     4096 keys staged in LDS so that the scattered writes leave the CU as runs per digit,
-//     and digit offsets of earlier tiles found by decoupled look-back. Tiles take their
-//     index from an atomic counter, so every tile waits only on tiles already running.
+//  3. The sort is an LSD radix sort with 8-bit digits over tiles of 4096 keys. Each pass is
+//     reduce-then-scan: per-tile digit counts, a scan of every digit's counts over the tiles,
+//     and a scatter that ranks the tile's keys with 64-lane ballots (stable multisplit), sorts
+//     them in LDS and writes them out as runs per digit. A single-pass form with decoupled
+//     look-back was measured slower here: with all tiles resident at once, late tiles walk
+//     back over hundreds of predecessors that have published only their own counts.
 //  4. Unique voxels, leaves, lower and upper nodes are counted in one pass over the sorted
 //     keys (a key starts a voxel / leaf / lower / upper when key, key>>9, key>>21, key>>36
 //     differ from its predecessor); after the one read-back of the counts, a second pass
@@ -48,26 +49,19 @@ constexpr int kTileKeys = kThreads * kKeysPerThread;  // 4096 keys per counting 
 constexpr int kSortKPT = 16;                           // keys per thread of a radix pass
 constexpr int kSortTile = kThreads * kSortKPT;         // keys per onesweep tile
 constexpr int kMaxPasses = 8;
-constexpr uint64_t kLbAggregate = 1ull << 62;
-constexpr uint64_t kLbInclusive = 2ull << 62;
-constexpr uint64_t kLbValue = (1ull << 62) - 1ull;
-constexpr uint32_t kSpinLimit = 1u << 22;  // look-back waits end (and flag an error) after this
 constexpr int kSmallSort = 4096;             // tile-key sorts up to this size run in one workgroup
 constexpr int kTileCache = 64;               // per-workgroup LDS cache of tiles already in the table
-constexpr int kLookBatch = 16;               // predecessors read per look-back step
 constexpr int kRootInLds = 512;              // root tables up to this capacity are copied to LDS
 
 struct BuildState {
   uint32_t overflow;          // root table ran out of probes
   uint32_t n_tiles;           // distinct root tiles inserted
-  uint32_t lookback_timeout;  // a look-back wait hit its spin limit
   uint32_t tile_list_count;   // compaction cursor
   uint32_t guard;             // a device-side bounds check failed (the build is rejected)
   uint32_t pad;
   uint64_t off_or, off_and;   // OR / AND over all in-tile offsets
   uint64_t key_or, key_and;   // OR / AND over all tile keys
   uint64_t counts[4];         // N, F, Lw, U from the sorted keys
-  uint32_t tile_counter[2 * kMaxPasses];
 };
 
 // ------------------------------------------------------------------------------ utilities
@@ -81,7 +75,6 @@ __global__ void k_init_state(BuildState* st) {
   if (threadIdx.x == 0 && blockIdx.x == 0) {
     st->overflow = 0;
     st->n_tiles = 0;
-    st->lookback_timeout = 0;
     st->tile_list_count = 0;
     st->guard = 0;
     st->off_or = 0;
@@ -89,7 +82,6 @@ __global__ void k_init_state(BuildState* st) {
     st->key_or = 0;
     st->key_and = ~0ull;
     for (int c = 0; c < 4; ++c) st->counts[c] = 0;
-    for (int p = 0; p < 2 * kMaxPasses; ++p) st->tile_counter[p] = 0;
   }
 }
 
@@ -421,34 +413,19 @@ __global__ __launch_bounds__(256) void k_hist(const uint64_t* __restrict__ keys,
   hist_flush(s_hist, hist, ps);
 }
 
-// One LSD pass over the 8-bit digit at `shift`: stable, tile of kSortTile keys per workgroup.
-__global__ __launch_bounds__(256) void k_onesweep(const uint64_t* __restrict__ src, uint64_t* __restrict__ dst,
-                                                  int64_t n, int shift, const uint32_t* __restrict__ hist,
-                                                  uint64_t* __restrict__ lookback, uint32_t* tile_counter,
-                                                  uint32_t* timeout, uint32_t* guard) {
-  __shared__ uint64_t s_keys[kSortTile];
-  __shared__ uint32_t s_cnt[4][256];
-  __shared__ uint32_t s_tile_start[256];
-  __shared__ int64_t s_base[256];
-  __shared__ uint64_t s_tmp[4];
-  __shared__ uint32_t s_tile;
+// One LSD pass over the 8-bit digit at `shift` runs as three kernels over tiles of kSortTile
+// keys (reduce-then-scan): per-tile digit counts, a scan of every digit's counts over the
+// tiles, and a stable scatter that ranks the tile's keys with 64-lane ballots, sorts them in
+// LDS and writes them out in per-digit runs.
 
-  const int tid = threadIdx.x;
+// Stable rank of every key among the equal digits of its wave (wave w owns the tile's keys
+// [w*64*kSortKPT, (w+1)*64*kSortKPT), 64 consecutive keys per round): the lanes holding the
+// same digit are found with 8 ballots, and the first of them adds their number to the
+// wave's count of that digit, so no two lanes update one counter in the same round.
+__device__ __forceinline__ void rank_keys(const uint64_t* __restrict__ src, int64_t n, int64_t wbase, int shift,
+                                          uint64_t* key, uint32_t* rank, uint32_t* cnt) {
   const int lane = lane_id();
-  const int wave = tid >> 6;
-  if (tid == 0) s_tile = atomicAdd(tile_counter, 1u);
-  for (int x = tid; x < 4 * 256; x += kThreads) (&s_cnt[0][0])[x] = 0;
-  __syncthreads();
-  const int64_t tile = s_tile;
-  const int64_t tile_base = tile * kSortTile;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
-
-  // Stable rank of every key among equal digits of its wave (blocked: wave w owns the
-  // tile's keys [w*64*kSortKPT, (w+1)*64*kSortKPT), 64 consecutive keys per round). All loads are issued
-  // before the first ballot so that their latency overlaps.
-  uint64_t key[kSortKPT];
-  uint32_t rank[kSortKPT];
-  const int64_t wbase = tile_base + wave * (64 * kSortKPT) + lane;
 #pragma unroll
   for (int r = 0; r < kSortKPT; ++r) key[r] = wbase + r * 64 < n ? src[wbase + r * 64] : 0ull;
 #pragma unroll
@@ -464,77 +441,82 @@ __global__ __launch_bounds__(256) void k_onesweep(const uint64_t* __restrict__ s
     }
     const uint32_t before = (uint32_t)__popcll(m & lt_mask);
     uint32_t old = 0;
-    if (valid) old = s_cnt[wave][d];
-    if (valid && before == 0) s_cnt[wave][d] = old + (uint32_t)__popcll(m);
+    if (valid) old = cnt[d];
+    if (valid && before == 0) cnt[d] = old + (uint32_t)__popcll(m);
     rank[r] = old + before;
   }
+}
+
+// Step 1: cnt[d * T + tile] = keys of the tile with digit d.
+__global__ __launch_bounds__(kThreads) void k_radix_hist(const uint64_t* __restrict__ src, int64_t n, int shift,
+                                                         uint32_t* __restrict__ cnt, int64_t T) {
+  __shared__ uint32_t s_cnt[4][256];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  for (int x = tid; x < 4 * 256; x += kThreads) (&s_cnt[0][0])[x] = 0;
+  __syncthreads();
+  const int64_t tile = blockIdx.x;
+  uint64_t key[kSortKPT];
+  uint32_t rank[kSortKPT];
+  rank_keys(src, n, tile * kSortTile + wave * (64 * kSortKPT) + lane_id(), shift, key, rank, s_cnt[wave]);
+  __syncthreads();
+  cnt[(int64_t)tid * T + tile] = s_cnt[0][tid] + s_cnt[1][tid] + s_cnt[2][tid] + s_cnt[3][tid];
+}
+
+// Step 2, one workgroup per digit d: off[d * T + t] = (keys whose digit is below d) +
+// (keys with digit d in tiles before t). hist holds the pass's digit counts over all keys.
+__global__ __launch_bounds__(kThreads) void k_radix_scan(const uint32_t* __restrict__ cnt, int64_t T,
+                                                         const uint32_t* __restrict__ hist, uint32_t* __restrict__ off) {
+  __shared__ uint64_t s_tmp[kThreads / 64];
+  const int d = blockIdx.x, tid = threadIdx.x;
+  uint64_t carry = 0;
+  block_excl_scan64<kThreads>(tid < d ? (uint64_t)hist[tid] : 0ull, s_tmp, &carry);
+  for (int64_t b = 0; b < T; b += kThreads) {
+    const int64_t t = b + tid;
+    const uint64_t c = t < T ? (uint64_t)cnt[(int64_t)d * T + t] : 0ull;
+    uint64_t sum = 0;
+    const uint64_t ex = block_excl_scan64<kThreads>(c, s_tmp, &sum);
+    if (t < T) off[(int64_t)d * T + t] = (uint32_t)(carry + ex);
+    carry += sum;
+  }
+}
+
+// Step 3: stable scatter of one tile to its digits' runs.
+__global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint64_t* __restrict__ src,
+                                                            uint64_t* __restrict__ dst, int64_t n, int shift,
+                                                            const uint32_t* __restrict__ off, int64_t T,
+                                                            uint32_t* guard) {
+  __shared__ uint64_t s_keys[kSortTile];
+  __shared__ uint32_t s_cnt[4][256];
+  __shared__ uint32_t s_tile_start[256];
+  __shared__ int64_t s_base[256];
+  __shared__ uint64_t s_tmp[kThreads / 64];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int64_t tile = blockIdx.x;
+  const int64_t tile_base = tile * kSortTile;
+  const uint32_t goff = off[(int64_t)tid * T + tile];  // in flight during the ranking
+  for (int x = tid; x < 4 * 256; x += kThreads) (&s_cnt[0][0])[x] = 0;
+  __syncthreads();
+  uint64_t key[kSortKPT];
+  uint32_t rank[kSortKPT];
+  const int64_t wbase = tile_base + wave * (64 * kSortKPT) + lane_id();
+  rank_keys(src, n, wbase, shift, key, rank, s_cnt[wave]);
   __syncthreads();
 
-  // Thread tid owns digit tid: tile count (published at once), per-wave exclusive offsets,
-  // tile and bucket scans, and the look-back of the digit.
+  // Thread tid owns digit tid: tile count, per-wave exclusive offsets and the tile scan.
   const uint32_t d = (uint32_t)tid;
   const uint32_t c0 = s_cnt[0][d], c1 = s_cnt[1][d], c2 = s_cnt[2][d], c3 = s_cnt[3][d];
-  const uint32_t tcount = c0 + c1 + c2 + c3;
-  uint64_t* lb = lookback + tile * 256 + d;
-  __hip_atomic_store(lb, (tile == 0 ? kLbInclusive : kLbAggregate) | (uint64_t)tcount, __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-  // First look-back batch in flight while the scans run.
-  uint64_t v[kLookBatch];
-  int64_t t = tile - 1;  // next predecessor not yet added
-#pragma unroll
-  for (int b = 0; b < kLookBatch; ++b)
-    v[b] = t - b >= 0 ? __hip_atomic_load(lookback + (t - b) * 256 + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                      : kLbInclusive;
-  const uint32_t tstart = (uint32_t)block_excl_scan64<kThreads>(tcount, s_tmp, nullptr);
-  const uint64_t bstart = block_excl_scan64<kThreads>(hist[d], s_tmp, nullptr);
+  const uint32_t tstart = (uint32_t)block_excl_scan64<kThreads>(c0 + c1 + c2 + c3, s_tmp, nullptr);
   s_cnt[0][d] = 0;
   s_cnt[1][d] = c0;
   s_cnt[2][d] = c0 + c1;
   s_cnt[3][d] = c0 + c1 + c2;
   s_tile_start[d] = tstart;
-
-  // Decoupled look-back, kLookBatch predecessors per step with independent loads (all tiles
-  // of a pass are often resident together, so the first inclusive prefix can be far back).
-  uint64_t excl = 0;
-  if (tile > 0) {
-    uint32_t spins = 0;
-    while (true) {
-      int b = 0;
-      bool done = false;
-      for (; b < kLookBatch; ++b) {
-        const uint64_t st = v[b] >> 62;
-        if (st == 0) break;  // not published yet: wait for it below
-        excl += v[b] & kLbValue;
-        if (st == 2) {
-          done = true;
-          break;
-        }
-      }
-      if (done) break;
-      t -= b;
-      if (b < kLookBatch) {
-        // Bounded wait: after the limit, or once any other wait has given up, stop waiting
-        // and flag the error so the host rejects the build.
-        __builtin_amdgcn_s_sleep(1);
-        ++spins;
-        if (spins >= kSpinLimit ||
-            ((spins & 1023u) == 0 && __hip_atomic_load(timeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
-          atomicOr(timeout, 1u);
-          break;
-        }
-      }
-#pragma unroll
-      for (int bb = 0; bb < kLookBatch; ++bb)
-        v[bb] = t - bb >= 0
-                    ? __hip_atomic_load(lookback + (t - bb) * 256 + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                    : kLbInclusive;
-    }
-    __hip_atomic_store(lb, kLbInclusive | (excl + tcount), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  s_base[d] = (int64_t)bstart + (int64_t)excl - (int64_t)tstart;
+  s_base[d] = (int64_t)goff - (int64_t)tstart;
   __syncthreads();
 
-  // Digit-sorted order inside the tile, staged in LDS.
+  // Digit-sorted order inside the tile, staged in LDS, then written out in per-digit runs.
 #pragma unroll
   for (int r = 0; r < kSortKPT; ++r) {
     if (wbase + r * 64 < n) {
@@ -556,22 +538,22 @@ __global__ __launch_bounds__(256) void k_onesweep(const uint64_t* __restrict__ s
 }
 
 // Sorts keys[0..n) (in a, scratch b) over the digits of ps; returns the buffer holding the
-// result. The histograms must already be in `hist` ([passes][256]).
-int onesweep_sort(uint64_t* a, uint64_t* b, int64_t n, PassSpec ps, const uint32_t* hist, uint64_t* lb,
-                  int64_t lb_tiles, uint32_t* tile_counters, uint32_t* timeout, uint32_t* guard, hipStream_t s,
-                  uint64_t** result) {
+// result. hist holds the digit counts of every pass ([passes][256]); cnt and off hold
+// 256 * cap_tiles words each.
+int radix_sort(uint64_t* a, uint64_t* b, int64_t n, PassSpec ps, const uint32_t* hist, uint32_t* cnt, uint32_t* off,
+               int64_t cap_tiles, uint32_t* guard, hipStream_t s, uint64_t** result) {
   *result = a;
   if (n <= 0 || ps.passes == 0) return IGC_OK;
   const int64_t tiles = (n + kSortTile - 1) / kSortTile;
-  if (tiles > lb_tiles || ps.passes > kMaxPasses)
-    return set_error(IGC_ERR_INTERNAL, "igc_grid_build: radix look-back buffer too small");
-  int st = fill_u64(lb, (int64_t)ps.passes * tiles * 256, 0, s);
-  if (st) return st;
+  if (tiles > cap_tiles || ps.passes > kMaxPasses)
+    return set_error(IGC_ERR_INTERNAL, "igc_grid_build: radix sort workspace too small");
   uint64_t* src = a;
   uint64_t* dst = b;
   for (int p = 0; p < ps.passes; ++p) {
-    k_onesweep<<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, ps.lo_bit + 8 * p, hist + 256 * p,
-                                                    lb + (size_t)p * tiles * 256, tile_counters + p, timeout, guard);
+    const int shift = ps.lo_bit + 8 * p;
+    k_radix_hist<<<(unsigned)tiles, kThreads, 0, s>>>(src, n, shift, cnt, tiles);
+    k_radix_scan<<<256, kThreads, 0, s>>>(cnt, tiles, hist + 256 * p, off);
+    k_radix_scatter<<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, shift, off, tiles, guard);
     IGC_HIP(hipGetLastError(), "igc_grid_build: radix pass launch");
     std::swap(src, dst);
   }
@@ -835,7 +817,7 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   const int64_t sort_tiles = (n_in + kSortTile - 1) / kSortTile;
   const size_t ws = align_up(sizeof(BuildState), 256) + align_up((size_t)kTileBlocks * 32, 256) +
                     align_up(2 * kMaxPasses * 256 * 4, 256) + align_up((size_t)kHistBlocks * kMaxPasses * 256 * 4, 256) +
-                    2 * align_up((size_t)n_in * 8, 256) + align_up((size_t)kMaxPasses * sort_tiles * 256 * 8, 256) +
+                    2 * align_up((size_t)n_in * 8, 256) + 2 * align_up((size_t)sort_tiles * 256 * 4, 256) +
                     align_up((size_t)tiles * 8, 256) + align_up((size_t)tiles * 32, 256) +
                     2 * align_up((size_t)kSmallSort * 8, 256);
   Arena ar(s);
@@ -847,7 +829,8 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   uint32_t* hpart = ar.take<uint32_t>((size_t)kHistBlocks * kMaxPasses * 256 * 4);
   uint64_t* ka = ar.take<uint64_t>((size_t)n_in * 8);
   uint64_t* kb = ar.take<uint64_t>((size_t)n_in * 8);
-  uint64_t* lookback = ar.take<uint64_t>((size_t)kMaxPasses * sort_tiles * 256 * 8);
+  uint32_t* rcnt = ar.take<uint32_t>((size_t)sort_tiles * 256 * 4);
+  uint32_t* roff = ar.take<uint32_t>((size_t)sort_tiles * 256 * 4);
   uint64_t* bcounts = ar.take<uint64_t>((size_t)tiles * 8);
   uint64_t* bprefix = ar.take<uint64_t>((size_t)tiles * 32);
   uint64_t* tile_list = ar.take<uint64_t>((size_t)kSmallSort * 8);
@@ -917,11 +900,11 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
     IGC_HIP(hipGetLastError(), "igc_grid_build: tile histogram launch");
     k_hist_reduce<<<tps.passes * 4, 256, 0, s>>>(hpart, nbh, tps.passes * 256, hist + kMaxPasses * 256);
     IGC_HIP(hipGetLastError(), "igc_grid_build: tile histogram reduce launch");
-    uint64_t* tlb = nullptr;
+    uint32_t* tcnt = nullptr;
     const int64_t ttiles = (U + kSortTile - 1) / kSortTile;
-    if ((rc = ar.get_extra(&tlb, (size_t)kMaxPasses * ttiles * 256 * 8, "igc_grid_build: tile look-back"))) return rc;
-    if ((rc = onesweep_sort(tile_list, tile_tmp, U, tps, hist + kMaxPasses * 256, tlb, ttiles, st->tile_counter + kMaxPasses,
-                            &st->lookback_timeout, &st->guard, s, &tiles_sorted)))
+    if ((rc = ar.get_extra(&tcnt, (size_t)2 * ttiles * 256 * 4, "igc_grid_build: tile radix counts"))) return rc;
+    if ((rc = radix_sort(tile_list, tile_tmp, U, tps, hist + kMaxPasses * 256, tcnt, tcnt + ttiles * 256, ttiles,
+                         &st->guard, s, &tiles_sorted)))
       return rc;
   }
   k_tile_rank<<<grid_for(U, 256, 1024), 256, 0, s>>>(tiles_sorted, U, root_keys, root_vals, (uint32_t)(cap - 1), st);
@@ -941,9 +924,7 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
     IGC_HIP(hipGetLastError(), "igc_grid_build: histogram reduce launch");
   }
   uint64_t* sorted = ka;
-  if ((rc = onesweep_sort(ka, kb, n_in, ps, hist, lookback, sort_tiles, st->tile_counter, &st->lookback_timeout, &st->guard, s,
-                          &sorted)))
-    return rc;
+  if ((rc = radix_sort(ka, kb, n_in, ps, hist, rcnt, roff, sort_tiles, &st->guard, s, &sorted))) return rc;
 
   // Counts, then the read-back that sizes the topology.
   const int64_t nb = tiles;
@@ -953,7 +934,6 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   IGC_HIP(hipGetLastError(), "igc_grid_build: block scan launch");
   IGC_HIP(hipMemcpyAsync(h, st, sizeof(BuildState), hipMemcpyDeviceToHost, s), "igc_grid_build: read counts");
   IGC_HIP(hipStreamSynchronize(s), "igc_grid_build: sort and count");
-  if (h->lookback_timeout) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: radix sort look-back timed out");
   if (h->guard) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: device bounds check failed before registration");
   const int64_t N = (int64_t)h->counts[0], F = (int64_t)h->counts[1], Lw = (int64_t)h->counts[2];
   if ((int64_t)h->counts[3] != U || N < 1 || N > n_in || F > N || Lw > F)
