@@ -187,45 +187,20 @@ __device__ __forceinline__ int cell_delta(int o) { return (o / 9) * 100 + ((o / 
 // three dropped terms are below 2^-24 of |a b|, the size of fp32 rounding (the split-bf16
 // scheme of Henry, Tang & Heinecke, "Leveraging the bfloat16 artificial intelligence datatype
 // for higher-precision computations", 2019). The window holds the three splits of every cell,
-// made once when the window is filled; W's splits are made once per call (k_leaf_wsplit) and
-// stay in registers. K = 27 offsets x CIN runs in chunks of 32: lane group g = lane/16 holds
+// made once when the window is filled, and W's splits stay in registers. K = 27 offsets x CIN runs in chunks of 32: lane group g = lane/16 holds
 // k = 8g..8g+7 of a chunk, i.e. one offset's 8 channels (CIN 8) or two offsets' 4 channels
 // (CIN 4); offsets past 26 are zero.
 template <int CIN, int COUT>
-__global__ __launch_bounds__(64) void k_leaf_wsplit(const float* __restrict__ w, bf16x8* __restrict__ wsplit) {
-  constexpr int COUTP = (COUT + 15) / 16 * 16;
-  constexpr int NS = COUTP / 16;
-  constexpr int NCH = (27 * CIN + 31) / 32;
-  const int lane = threadIdx.x, rl = lane & 15, kg = lane >> 4;
-  for (int q = 0; q < NCH; ++q)
-    for (int ns = 0; ns < NS; ++ns) {
-      const int col = ns * 16 + rl;
-      bf16x8 h, m, l;
-      for (int e = 0; e < 8; ++e) {
-        const int k = q * 32 + kg * 8 + e;  // k = o * CIN + ci
-        const float v = (k < 27 * CIN && col < COUT) ? w[(size_t)k * COUT + col] : 0.f;
-        uint16_t hs, ms, ls;
-        split3(v, hs, ms, ls);
-        h[e] = __builtin_bit_cast(__bf16, hs);
-        m[e] = __builtin_bit_cast(__bf16, ms);
-        l[e] = __builtin_bit_cast(__bf16, ls);
-      }
-      wsplit[((q * 3 + 0) * NS + ns) * 64 + lane] = h;
-      wsplit[((q * 3 + 1) * NS + ns) * 64 + lane] = m;
-      wsplit[((q * 3 + 2) * NS + ns) * 64 + lane] = l;
-    }
-}
-
-template <int CIN, int COUT>
 __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* __restrict__ feats,
-                                                       const bf16x8* __restrict__ wsplit, float* __restrict__ out) {
+                                                       const float* __restrict__ w, float* __restrict__ out) {
   static_assert(CIN == 4 || CIN == 8, "channel layout of the split form");
   constexpr int COUTP = (COUT + 15) / 16 * 16;
   constexpr int NS = COUTP / 16;
   constexpr int OPG = 8 / CIN;                   // offsets per lane group and chunk
   constexpr int NCH = (27 * CIN + 31) / 32;      // chunks of 32 k values
   constexpr int CS = 3 * CIN;                    // bf16 elements per window cell (three splits)
-  __shared__ __attribute__((aligned(16))) uint16_t s_win[1000 * CS];
+  constexpr int WSP = NCH * 3 * NS * 64 * 8;     // bf16 elements of W's splits (staged before the window)
+  __shared__ __attribute__((aligned(16))) uint16_t s_win[1000 * CS > WSP ? 1000 * CS : WSP];
   __shared__ uint64_t s_mask[27][8];
   __shared__ uint64_t s_off[27];
   __shared__ uint64_t s_pre[27];
@@ -253,24 +228,50 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
     }
   }
 
-  // W splits for this lane (made once per call by k_leaf_wsplit): chunk q, split s, column
-  // slab ns -> 8 bf16 (k = 8 kg .. 8 kg + 7).
-  bf16x8 wb[NCH][3][NS];
+  // W splits for this lane: chunk q, split s, column slab ns -> 8 bf16 (k = 8 kg .. 8 kg + 7).
+  // Every wave needs the same fragments: wave w splits the (q, ns) pairs with (q*NS+ns) % 4 ==
+  // w into LDS (the window's space, filled afterwards), and all waves then load all of them.
   int dcell[NCH][OPG];
   bool dvalid[NCH][OPG];
 #pragma unroll
-  for (int q = 0; q < NCH; ++q) {
+  for (int q = 0; q < NCH; ++q)
 #pragma unroll
     for (int h = 0; h < OPG; ++h) {
       const int o = (q * 32 + kg * 8) / CIN + h;
       dvalid[q][h] = o < 27;
       dcell[q][h] = cell_delta(o < 27 ? o : 0);
     }
+  bf16x8* s_wsp = (bf16x8*)s_win;
+  for (int pr = wave; pr < NCH * NS; pr += 4) {
+    const int q = pr / NS, ns = pr % NS;
+    const int col = ns * 16 + rl;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = q * 32 + kg * 8 + e;  // k = o * CIN + ci
+      v[e] = (k < 27 * CIN && col < COUT) ? w[(size_t)k * COUT + col] : 0.f;
+    }
+    bf16x8 h, m, l;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint16_t hs, ms, ls;
+      split3(v[e], hs, ms, ls);
+      h[e] = __builtin_bit_cast(__bf16, hs);
+      m[e] = __builtin_bit_cast(__bf16, ms);
+      l[e] = __builtin_bit_cast(__bf16, ls);
+    }
+    s_wsp[((q * 3 + 0) * NS + ns) * 64 + lane] = h;
+    s_wsp[((q * 3 + 1) * NS + ns) * 64 + lane] = m;
+    s_wsp[((q * 3 + 2) * NS + ns) * 64 + lane] = l;
+  }
+  __syncthreads();
+  bf16x8 wb[NCH][3][NS];
+#pragma unroll
+  for (int q = 0; q < NCH; ++q)
 #pragma unroll
     for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns) wb[q][sp][ns] = wsplit[((q * 3 + sp) * NS + ns) * 64 + lane];
-  }
+      for (int ns = 0; ns < NS; ++ns) wb[q][sp][ns] = s_wsp[((q * 3 + sp) * NS + ns) * 64 + lane];
   __syncthreads();
 
   // Compacted active positions of this leaf (wave 0), and the split window (all threads).
@@ -392,20 +393,9 @@ int launch_leaf(const igc_grid* g, const void* d_feats, const void* d_w, void* d
   // W splits fit in registers; the fp32-MFMA form for the wider shapes.
   constexpr bool split = (CIN == 4 && COUT <= 32) || (CIN == 8 && COUT <= 16);
   if constexpr (split) {
-    constexpr int NS = (COUT + 15) / 16;
-    constexpr int NCH = (27 * CIN + 31) / 32;
-    bf16x8* ws = nullptr;
-    int rc = dev_alloc((void**)&ws, (size_t)NCH * 3 * NS * 64 * sizeof(bf16x8), s, "igc_sparse_conv: W splits");
-    if (rc) return rc;
-    k_leaf_wsplit<CIN, COUT><<<1, 64, 0, s>>>((const float*)d_w, ws);
-    hipError_t e = hipGetLastError();
-    if (e == hipSuccess) {
-      k_conv_leaf_f32<CIN, COUT><<<(unsigned)g->n_leaf, 256, 0, s>>>(g->view(), (const float*)d_feats, ws,
-                                                                    (float*)d_out);
-      e = hipGetLastError();
-    }
-    dev_free(ws, s);
-    if (e != hipSuccess) return hip_status(e, "igc_sparse_conv: leaf launch");
+    k_conv_leaf_f32<CIN, COUT><<<(unsigned)g->n_leaf, 256, 0, s>>>(g->view(), (const float*)d_feats,
+                                                                  (const float*)d_w, (float*)d_out);
+    IGC_HIP(hipGetLastError(), "igc_sparse_conv: leaf launch");
   } else {
     k_conv_leaf_f32_wide<CIN, COUT><<<(unsigned)g->n_leaf, 256, 0, s>>>(g->view(), (const float*)d_feats,
                                                                        (const float*)d_w, (float*)d_out);
