@@ -19,7 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "igc_oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-__all__ = ["build_library", "OracleGrid", "kernel_map", "conv", "conv_rows", "standard_offsets", "num_threads"]
+__all__ = ["build_library", "OracleGrid", "kernel_map", "conv", "conv_rows", "conv_dgrad", "conv_wgrad",
+           "standard_offsets", "num_threads"]
 
 
 def build_library(force: bool = True) -> str:
@@ -178,3 +179,35 @@ def conv_rows(nbrs: np.ndarray, feats_of: dict, w: np.ndarray) -> np.ndarray:
             if s >= 0:
                 out[i] += np.asarray(feats_of[s], dtype=np.float64) @ ww[o]
     return out
+
+
+def conv_dgrad(kmap: np.ndarray, dout: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Gradient of the submanifold convolution with respect to its input features, in float64:
+    dX[s, ci] = sum over the pairs (o, r) with map[o, r] = s of sum_co dY[r, co] W[o, ci, co]
+    (the convolution of the fVDB notes' sparse-conv operators differentiated term by term).
+
+    kmap int32[K, N], dout float32[N, cout] (exact bf16 values for bf16 data),
+    w float32[K, cin, cout]; returns float64[N, cin]."""
+    kmap = np.asarray(kmap)
+    dy = np.asarray(dout, dtype=np.float64)
+    ww = np.asarray(w, dtype=np.float64)
+    dx = np.zeros((kmap.shape[1], ww.shape[1]), np.float64)
+    for o in range(kmap.shape[0]):
+        valid = kmap[o] >= 0
+        np.add.at(dx, kmap[o][valid], dy[valid] @ ww[o].T)
+    return dx
+
+
+def conv_wgrad(kmap: np.ndarray, feats: np.ndarray, dout: np.ndarray) -> np.ndarray:
+    """Gradient of the submanifold convolution with respect to its weights, in float64:
+    dW[o, ci, co] = sum over r with map[o, r] >= 0 of feats[map[o, r], ci] dY[r, co].
+
+    kmap int32[K, N], feats float32[N, cin], dout float32[N, cout]; returns float64[K, cin, cout]."""
+    kmap = np.asarray(kmap)
+    f = np.asarray(feats, dtype=np.float64)
+    dy = np.asarray(dout, dtype=np.float64)
+    dw = np.zeros((kmap.shape[0], f.shape[1], dy.shape[1]), np.float64)
+    for o in range(kmap.shape[0]):
+        valid = kmap[o] >= 0
+        dw[o] = f[kmap[o][valid]].T @ dy[valid]
+    return dw

@@ -352,3 +352,50 @@ def test_conv_rows_equals_conv():
     ref = oracle.conv(m, f, w, rows=rows)
     got = oracle.conv_rows(nbrs, {int(s): f[s] for s in np.unique(nbrs[nbrs >= 0])}, w)
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- backward pass
+
+def test_conv_gradients_match_autograd_of_masked_dense_conv3d():
+    """dgrad and wgrad equal torch autograd (float64) of conv3d on the zero-filled dense volume,
+    read at the active voxels: the loss sum(out * dY) over active outputs."""
+    c = workloads.random_coords(900, -5, 7, seed=51)
+    g = OracleGrid(c)
+    act = g.active_ijk().astype(np.int64)
+    rng = np.random.default_rng(52)
+    cin, cout = 3, 4
+    f = rng.standard_normal((g.n, cin)).astype(np.float32)
+    w = rng.standard_normal((27, cin, cout)).astype(np.float32)
+    dy = rng.standard_normal((g.n, cout)).astype(np.float32)
+    lo = act.min(axis=0) - 1
+    ext = act.max(axis=0) - lo + 2
+    loc = torch.from_numpy(act - lo)
+    x = torch.from_numpy(f.astype(np.float64)).requires_grad_(True)
+    wt = torch.from_numpy(w.astype(np.float64)).requires_grad_(True)
+    vol = torch.zeros((cin, *ext.tolist()), dtype=torch.float64)
+    vol = vol.index_put((torch.arange(cin)[:, None], loc[:, 0][None], loc[:, 1][None], loc[:, 2][None]), x.T)
+    k = wt.reshape(3, 3, 3, cin, cout).permute(4, 3, 0, 1, 2)
+    out = torch.nn.functional.conv3d(vol[None], k, padding=1)[0]
+    loss = (out[:, loc[:, 0], loc[:, 1], loc[:, 2]].T * torch.from_numpy(dy.astype(np.float64))).sum()
+    loss.backward()
+    m = g.kernel_map()
+    dx = oracle.conv_dgrad(m, dy, w)
+    dw = oracle.conv_wgrad(m, f, dy)
+    assert np.max(np.abs(dx - x.grad.numpy())) <= 1e-12 * np.max(np.abs(dx))
+    assert np.max(np.abs(dw - wt.grad.numpy())) <= 1e-12 * np.max(np.abs(dw))
+
+
+def test_conv_gradients_are_adjoints_of_the_forward():
+    """<conv(x, W), dY> = <x, dgrad(dY, W)> = <W, wgrad(x, dY)>."""
+    c = workloads.random_coords(4000, -15, 15, seed=61)
+    g = OracleGrid(c)
+    m = g.kernel_map()
+    rng = np.random.default_rng(62)
+    f = rng.standard_normal((g.n, 5)).astype(np.float32)
+    w = rng.standard_normal((27, 5, 6)).astype(np.float32)
+    dy = rng.standard_normal((g.n, 6)).astype(np.float32)
+    lhs = float(np.sum(oracle.conv(m, f, w) * dy.astype(np.float64)))
+    via_x = float(np.sum(f.astype(np.float64) * oracle.conv_dgrad(m, dy, w)))
+    via_w = float(np.sum(w.astype(np.float64) * oracle.conv_wgrad(m, f, dy)))
+    assert abs(lhs - via_x) <= 1e-10 * abs(lhs)
+    assert abs(lhs - via_w) <= 1e-10 * abs(lhs)
