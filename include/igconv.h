@@ -165,6 +165,25 @@ int igc_sparse_conv(const igc_grid* grid, const int32_t* d_map, const void* d_fe
                     int32_t cin, const void* d_w, int32_t cout, void* d_out, int32_t path,
                     igc_stream stream);
 
+/* Backward pass of igc_sparse_conv (the same operator differentiated; fVDB notes, "accelerated
+ * operators for sparse convolution", which list training support for these backends as future
+ * work). Given d_dout = dL/dY [N, cout] (type `dtype`):
+ *     d_dfeats[s, ci] = sum over (o, r) with map[o, r] = s of sum_co d_dout[r, co] * W[o, ci, co]
+ *                       ([N, cin], type `dtype`; NULL skips it)
+ *     d_dw[o, ci, co] = sum over r with map[o, r] >= 0 of feats[map[o, r], ci] * d_dout[r, co]
+ *                       ([27, cin, cout] float32, summed in fp32 per chunk of rows and over the
+ *                       chunks in fp64, in a fixed order; NULL skips it)
+ * d_map (int32[27, N], standard offsets) is required. The input gradient is the forward
+ * convolution of d_dout with W~[o] = W[26 - o]^T (the map is symmetric under offset negation),
+ * so it runs on the path igc_select_path picks for (dtype, cout, cin) unless `path` forces one;
+ * that shape must be supported (see igc_sparse_conv; the leaf path also takes 8 -> 4, 16 -> 4,
+ * 16 -> 8). The weight gradient supports BF16 with cin a multiple of 32 and cout a multiple of
+ * 64 (up to 1024), and F32 with cin, cout <= 64 and cin * cout <= 1024. Anything else returns
+ * IGC_ERR_UNSUPPORTED. Outputs must not alias inputs. */
+int igc_sparse_conv_backward(const igc_grid* grid, const int32_t* d_map, const void* d_feats, int32_t dtype,
+                             int32_t cin, const void* d_w, int32_t cout, const void* d_dout, void* d_dfeats,
+                             float* d_dw, int32_t path, igc_stream stream);
+
 /* The path IGC_PATH_AUTO takes for this grid and layer shape (host only). Leaf when the
  * dtype is F32 and the shape is supported by LEAF, GGS otherwise; IGC_ERR_UNSUPPORTED when
  * neither path supports the shape. The IGC_PATH environment variable ("leaf" / "ggs")

@@ -15,7 +15,7 @@ from . import _lib
 from ._lib import IgcError
 
 __all__ = [
-    "Grid", "grid_build", "kernel_map", "sparse_conv", "standard_offsets", "IgcError",
+    "Grid", "grid_build", "kernel_map", "sparse_conv", "sparse_conv_backward", "standard_offsets", "IgcError",
     "PATH_AUTO", "PATH_LEAF", "PATH_GGS",
 ]
 
@@ -176,3 +176,27 @@ def sparse_conv(grid: Grid, feats: torch.Tensor, weights: torch.Tensor, kmap: to
     _lib.check(_lib.load().igc_sparse_conv(grid.handle, _ptr(kmap), _ptr(feats), _dtype_code(dt), cin,
                                            _ptr(weights), cout, _ptr(out), _PATHS[path], _stream(grid.device)))
     return out
+
+
+def sparse_conv_backward(grid: Grid, feats: torch.Tensor, weights: torch.Tensor, dout: torch.Tensor,
+                         kmap: torch.Tensor, path: str = "auto", need_dfeats: bool = True,
+                         need_dweights: bool = True):
+    """Gradients of sparse_conv: (dfeats [N, cin] of feats' dtype or None, dweights [27, cin, cout]
+    float32 or None) for the output gradient dout [N, cout]."""
+    dt = feats.dtype
+    cin = feats.shape[1] if feats.dim() == 2 else -1
+    feats = _device_tensor(feats, "feats", dt, cin)
+    if weights.dim() != 3 or weights.shape[0] != 27 or weights.shape[1] != cin:
+        raise ValueError(f"weights must have shape [27, {cin}, cout], got {tuple(weights.shape)}")
+    weights = _device_tensor(weights, "weights", dt)
+    cout = weights.shape[2]
+    dout = _device_tensor(dout, "dout", dt, cout)
+    kmap = _device_tensor(kmap, "kmap", torch.int32)
+    if tuple(kmap.shape) != (27, grid.n_voxels) or feats.shape[0] != grid.n_voxels or dout.shape[0] != grid.n_voxels:
+        raise ValueError("feats, dout and kmap must cover the grid's voxels")
+    dx = torch.empty((grid.n_voxels, cin), dtype=dt, device=grid.device) if need_dfeats else None
+    dw = torch.empty((27, cin, cout), dtype=torch.float32, device=grid.device) if need_dweights else None
+    _lib.check(_lib.load().igc_sparse_conv_backward(grid.handle, _ptr(kmap), _ptr(feats), _dtype_code(dt), cin,
+                                                    _ptr(weights), cout, _ptr(dout), _ptr(dx), _ptr(dw),
+                                                    _PATHS[path], _stream(grid.device)))
+    return dx, dw

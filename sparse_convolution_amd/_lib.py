@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libigconv.s
 EXPORTS = (
     "igc_grid_build", "igc_grid_destroy", "igc_grid_get_info", "igc_grid_active_ijk",
     "igc_grid_ijk_to_index", "igc_grid_export", "igc_kernel_map", "igc_sparse_conv",
-    "igc_select_path", "igc_last_error",
+    "igc_sparse_conv_backward", "igc_select_path", "igc_last_error",
 )
 
 STATUS = {
@@ -61,6 +61,7 @@ def load() -> ctypes.CDLL:
         "igc_grid_export": [P, ctypes.POINTER(TopologyHost)],
         "igc_kernel_map": [P, P, i32, P, P, P],
         "igc_sparse_conv": [P, P, P, i32, i32, P, i32, P, i32, P],
+        "igc_sparse_conv_backward": [P, P, P, i32, i32, P, i32, P, P, P, i32, P],
         "igc_select_path": [P, i32, i32, i32, ctypes.POINTER(i32)],
         "igc_last_error": [],
     }

@@ -265,6 +265,44 @@ int igc_sparse_conv(const igc_grid* g, const int32_t* d_map, const void* d_feats
   return launch_conv_ggs(g, d_map, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream);
 }
 
+int igc_sparse_conv_backward(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype,
+                             int32_t cin, const void* d_w, int32_t cout, const void* d_dout, void* d_dfeats,
+                             float* d_dw, int32_t path, igc_stream stream) {
+  clear_error();
+  if (!g) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_backward: grid is null");
+  if (dtype != IGC_F32 && dtype != IGC_BF16)
+    return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_backward: bad dtype");
+  if (cin < 1 || cout < 1)
+    return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_backward: cin and cout must be positive");
+  if (path != IGC_PATH_AUTO && path != IGC_PATH_LEAF && path != IGC_PATH_GGS)
+    return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_backward: bad path");
+  if (!d_w) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_backward: d_w is null");
+  if (g->n_voxels > 0 && (!d_map || !d_dout || (d_dw && !d_feats)))
+    return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_backward: d_map, d_dout or d_feats is null");
+  if (d_dfeats && (d_dfeats == d_dout || d_dfeats == d_feats))
+    return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_backward: d_dfeats aliases an input");
+  int32_t p = path;
+  if (d_dfeats) {
+    if (p == IGC_PATH_AUTO) {
+      const int rc = choose_path(g, dtype, cout, cin, &p);
+      if (rc) return rc;
+    }
+    if (p == IGC_PATH_LEAF && !leaf_conv_supported(dtype, cout, cin))
+      return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv_backward: leaf path does not support the input-gradient shape");
+    if (p == IGC_PATH_GGS && !ggs_conv_supported(dtype, cout, cin))
+      return set_error(IGC_ERR_UNSUPPORTED,
+                       "igc_sparse_conv_backward: gather-GEMM-scatter path does not support the input-gradient shape");
+  }
+  if (d_dw && !wgrad_supported(dtype, cin, cout))
+    return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv_backward: weight gradient does not support this dtype / cin / cout");
+  if (g->n_voxels == 0) {
+    if (d_dw) IGC_HIP(hipMemsetAsync(d_dw, 0, (size_t)27 * cin * cout * 4, (hipStream_t)stream),
+                      "igc_sparse_conv_backward: clear weight gradient");
+    return IGC_OK;
+  }
+  return launch_conv_backward(g, d_map, d_feats, dtype, cin, d_w, cout, d_dout, d_dfeats, d_dw, p, (hipStream_t)stream);
+}
+
 const char* igc_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

@@ -1,0 +1,329 @@
+// Backward pass of the submanifold convolution (the operator of the fVDB notes' "accelerated
+// operators for sparse convolution", differentiated; the notes list training support for these
+// backends as future work).
+//
+// Forward: Y[r] = sum over o with map[o, r] >= 0 of W[o]^T X[map[o, r]].
+//
+// dgrad: dX[s] = sum over the pairs (o, r) with map[o, r] = s of W[o] dY[r]. For the 27 offsets
+// of a 3x3x3 kernel the map is symmetric under negation (map[o, r] = s <=> map[26 - o, s] = r),
+// so dX is the forward convolution of dY with W~[o] = W[26 - o]^T (k_flip_w) over the same map
+// and grid: both forward paths serve as they are.
+//
+// wgrad: dW[o] = sum over r with map[o, r] >= 0 of X[map[o, r]] dY[r]^T, a reduction over all
+// rows. Work is split over (offset, chunk of row tiles, channel block); each workgroup writes
+// its partial block and k_wgrad_reduce adds the partials of all chunks in a fixed order, in
+// fp64, so the result does not depend on scheduling.
+//  - bf16: on the matrix cores (v_mfma_f32_16x16x32_bf16) with K = rows. Rows are taken in the
+//    mask-sorted order of the gather-GEMM-scatter plan, 64 at a time; a 64-row stage that has
+//    no pair at the workgroup's offset is skipped. The stage's gathered input rows and output
+//    gradients are written to LDS transposed (channel-major, rows contiguous), so both MFMA
+//    operands are 16-byte reads of 8 consecutive rows.
+//  - fp32 (the leaf path's narrow shapes): plain fp32 FMAs over 64-row stages in LDS.
+#include <hip/hip_runtime.h>
+
+#include "igc_host.h"
+#include "igc_internal.h"
+#include "igc_wave.h"
+
+namespace igc {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kNOff = 27;
+constexpr int kTileRows = 256;  // rows of a plan tile
+constexpr int kStage = 64;      // rows staged at a time
+constexpr int kLdT = kStage + 8;  // LDS row stride of the transposed stages (bf16): 144 bytes
+
+// wf[o][co][ci] = w[26 - o][ci][co].
+template <typename T>
+__global__ void k_flip_w(const T* __restrict__ w, T* __restrict__ wf, int cin, int cout) {
+  const int64_t total = (int64_t)kNOff * cin * cout;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t o = e / ((int64_t)cin * cout);
+    const int64_t rem = e - o * cin * cout;
+    const int64_t co = rem / cin, ci = rem - co * cin;
+    wf[e] = w[((kNOff - 1 - o) * cin + ci) * cout + co];
+  }
+}
+
+// Workgroup index -> (offset, chunk, m block, n block); the 27 offsets of one (chunk, block)
+// are neighbours, so the chunk's output-gradient rows are re-read from L2.
+struct WgradSplit {
+  int64_t chunks, mblocks, nblocks;
+  __device__ void decode(int64_t id, int& o, int64_t& chunk, int& mb, int& nb) const {
+    o = (int)(id % kNOff);
+    int64_t rest = id / kNOff;
+    nb = (int)(rest % nblocks);
+    rest /= nblocks;
+    mb = (int)(rest % mblocks);
+    chunk = rest / mblocks;
+  }
+};
+
+// Partial dW blocks of MB input x NB output channels per (offset, chunk of tiles), bf16 data.
+// Four waves in 2 x 2, each (MB/2) x (NB/2) with 16x16x32 MFMAs.
+template <int MB, int NB>
+__global__ __launch_bounds__(256) void k_wgrad_bf16(const int32_t* __restrict__ map, int64_t N,
+                                                    const int32_t* __restrict__ perm,
+                                                    const uint16_t* __restrict__ blk,
+                                                    const uint16_t* __restrict__ feats,
+                                                    const uint16_t* __restrict__ dout, int cin, int cout,
+                                                    int64_t n_tiles, int64_t tiles_per_chunk, WgradSplit sp,
+                                                    float* __restrict__ part) {
+  constexpr int MI = MB / 32, NI = NB / 32;  // 16-blocks per wave
+  static_assert(MI >= 1 && NI >= 1, "block shape");
+  __shared__ __attribute__((aligned(16))) uint16_t s_xt[MB * kLdT];  // [channel][row]
+  __shared__ __attribute__((aligned(16))) uint16_t s_dt[NB * kLdT];
+  __shared__ int32_t s_row[kStage], s_src[kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int o, mb, nb;
+  int64_t chunk;
+  sp.decode(blockIdx.x, o, chunk, mb, nb);
+  const int c0 = mb * MB, n0 = nb * NB;
+  const int64_t t0 = chunk * tiles_per_chunk;
+  const int64_t t1 = t0 + tiles_per_chunk < n_tiles ? t0 + tiles_per_chunk : n_tiles;
+
+  f32x4 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int frow = lane & 15, fk = (lane >> 4) * 8;
+  for (int64_t t = t0; t < t1; ++t) {
+    const uint32_t bits = blk[t * kNOff + o];
+    for (int st = 0; st < kTileRows / kStage; ++st) {
+      if (((bits >> (st * 4)) & 0xFu) == 0u) continue;  // no pair at this offset in these 64 rows
+      __syncthreads();  // the previous stage's reads are done
+      if (tid < kStage) {
+        const int32_t r = perm[t * kTileRows + st * kStage + tid];
+        s_row[tid] = r;
+        s_src[tid] = r >= 0 ? map[(size_t)o * (size_t)N + r] : -1;
+      }
+      __syncthreads();
+      // Transposed staging: item = (row pair, 8-channel granule); two 16-byte loads, eight
+      // 4-byte LDS writes of (row 2p, row 2p+1) per channel.
+      for (int it = tid; it < (kStage / 2) * (MB / 8); it += 256) {
+        const int pr = it % (kStage / 2), g = it / (kStage / 2);
+        const int32_t s0 = s_src[2 * pr], s1 = s_src[2 * pr + 1];
+        const uint4 a = s0 >= 0 ? *(const uint4*)(feats + (size_t)s0 * cin + c0 + g * 8) : make_uint4(0, 0, 0, 0);
+        const uint4 b = s1 >= 0 ? *(const uint4*)(feats + (size_t)s1 * cin + c0 + g * 8) : make_uint4(0, 0, 0, 0);
+        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint32_t lo = (av[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu, hi = (bv[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu;
+          *(uint32_t*)&s_xt[(g * 8 + c) * kLdT + 2 * pr] = lo | (hi << 16);
+        }
+      }
+      for (int it = tid; it < (kStage / 2) * (NB / 8); it += 256) {
+        const int pr = it % (kStage / 2), g = it / (kStage / 2);
+        const int32_t r0 = s_src[2 * pr] >= 0 ? s_row[2 * pr] : -1, r1 = s_src[2 * pr + 1] >= 0 ? s_row[2 * pr + 1] : -1;
+        const uint4 a = r0 >= 0 ? *(const uint4*)(dout + (size_t)r0 * cout + n0 + g * 8) : make_uint4(0, 0, 0, 0);
+        const uint4 b = r1 >= 0 ? *(const uint4*)(dout + (size_t)r1 * cout + n0 + g * 8) : make_uint4(0, 0, 0, 0);
+        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint32_t lo = (av[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu, hi = (bv[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu;
+          *(uint32_t*)&s_dt[(g * 8 + c) * kLdT + 2 * pr] = lo | (hi << 16);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < kStage; ks += 32) {
+        bf16x8 a[MI], b[NI];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+          a[mi] = *(const bf16x8*)&s_xt[(wm * (MB / 2) + mi * 16 + frow) * kLdT + ks + fk];
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          b[ni] = *(const bf16x8*)&s_dt[(wn * (NB / 2) + ni * 16 + frow) * kLdT + ks + fk];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+      }
+    }
+  }
+  // D layout: lane holds column lane%16 of rows 4*(lane/16) + j.
+  float* dst = part + ((size_t)chunk * kNOff + o) * (size_t)cin * cout;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = c0 + wm * (MB / 2) + mi * 16 + (lane >> 4) * 4 + j;
+        const int n = n0 + wn * (NB / 2) + ni * 16 + frow;
+        dst[(size_t)m * cout + n] = acc[mi][ni][j];
+      }
+}
+
+// Partial dW per (offset, chunk of rows), fp32 data with cin, cout <= 64 and cin * cout <= 1024.
+__global__ __launch_bounds__(256) void k_wgrad_f32(const int32_t* __restrict__ map, int64_t N,
+                                                   const float* __restrict__ feats, const float* __restrict__ dout,
+                                                   int cin, int cout, int64_t rows_per_chunk,
+                                                   float* __restrict__ part) {
+  __shared__ float s_x[kStage * 64];
+  __shared__ float s_d[kStage * 64];
+  const int tid = threadIdx.x;
+  const int o = (int)(blockIdx.x % kNOff);
+  const int64_t chunk = blockIdx.x / kNOff;
+  const int64_t r0 = chunk * rows_per_chunk;
+  const int64_t r1 = r0 + rows_per_chunk < N ? r0 + rows_per_chunk : N;
+  const int E = cin * cout;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t base = r0; base < r1; base += kStage) {
+    __syncthreads();
+    for (int i = tid; i < kStage * cin; i += 256) {
+      const int k = i / cin, c = i - k * cin;
+      const int64_t r = base + k;
+      const int32_t src = r < r1 ? map[(size_t)o * (size_t)N + r] : -1;
+      s_x[i] = src >= 0 ? feats[(size_t)src * cin + c] : 0.f;
+    }
+    for (int i = tid; i < kStage * cout; i += 256) {
+      const int k = i / cout, c = i - k * cout;
+      const int64_t r = base + k;
+      s_d[i] = r < r1 ? dout[(size_t)r * cout + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = tid + 256 * j;
+      if (e < E) {
+        const int ci = e / cout, co = e - ci * cout;
+        float sum = 0.f;
+        for (int k = 0; k < kStage; ++k) sum = fmaf(s_x[k * cin + ci], s_d[k * cout + co], sum);
+        acc[j] += sum;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid + 256 * j;
+    if (e < E) part[((size_t)chunk * kNOff + o) * E + e] = acc[j];
+  }
+}
+
+// dw[e] = sum over chunks c (in order) of part[c * E + e], accumulated in fp64.
+__global__ void k_wgrad_reduce(const float* __restrict__ part, int64_t chunks, int64_t E, float* __restrict__ dw) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < E; e += (int64_t)gridDim.x * blockDim.x) {
+    double s = 0.0;
+    for (int64_t c = 0; c < chunks; ++c) s += (double)part[c * E + e];
+    dw[e] = (float)s;
+  }
+}
+
+template <int MB, int NB>
+int launch_wgrad_bf16(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t cin,
+                      const void* d_dout, int32_t cout, float* d_dw, hipStream_t s) {
+  const int64_t N = g->n_voxels;
+  const int64_t n_tiles = (N + kTileRows - 1) / kTileRows;
+  WgradSplit sp;
+  sp.mblocks = cin / MB;
+  sp.nblocks = cout / NB;
+  // About 2048 workgroups: enough to fill 256 CUs, few enough partial blocks to reduce.
+  int64_t chunks = 2048 / (kNOff * sp.mblocks * sp.nblocks);
+  if (chunks < 1) chunks = 1;
+  if (chunks > n_tiles) chunks = n_tiles;
+  const int64_t tpc = (n_tiles + chunks - 1) / chunks;
+  chunks = (n_tiles + tpc - 1) / tpc;
+  sp.chunks = chunks;
+  const int64_t E = (int64_t)kNOff * cin * cout;
+  const size_t perm_bytes = align_up((size_t)n_tiles * kTileRows * 4, 256);
+  const size_t blk_bytes = align_up((size_t)n_tiles * kNOff * 2, 256);
+  const size_t part_bytes = align_up((size_t)chunks * E * 4, 256);
+  char* ws = nullptr;
+  int rc = dev_alloc((void**)&ws, perm_bytes + blk_bytes + part_bytes, s, "igc_sparse_conv_backward: wgrad workspace");
+  if (rc) return rc;
+  int32_t* perm = (int32_t*)ws;
+  uint16_t* blk = (uint16_t*)(ws + perm_bytes);
+  float* part = (float*)(ws + perm_bytes + blk_bytes);
+  rc = launch_ggs_plan(d_map, N, perm, blk, s);
+  hipError_t e = hipSuccess;
+  if (rc == IGC_OK) {
+    k_wgrad_bf16<MB, NB><<<(unsigned)(kNOff * chunks * sp.mblocks * sp.nblocks), 256, 0, s>>>(
+        d_map, N, perm, blk, (const uint16_t*)d_feats, (const uint16_t*)d_dout, cin, cout, n_tiles, tpc, sp, part);
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+      k_wgrad_reduce<<<(unsigned)((E + 255) / 256 < 4096 ? (E + 255) / 256 : 4096), 256, 0, s>>>(part, chunks, E, d_dw);
+      e = hipGetLastError();
+    }
+  }
+  dev_free(ws, s);
+  if (rc) return rc;
+  if (e != hipSuccess) return hip_status(e, "igc_sparse_conv_backward: wgrad launch");
+  return IGC_OK;
+}
+
+int launch_wgrad_f32(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t cin, const void* d_dout,
+                     int32_t cout, float* d_dw, hipStream_t s) {
+  const int64_t N = g->n_voxels;
+  int64_t chunks = 2048 / kNOff;
+  int64_t rpc = (N + chunks - 1) / chunks;
+  rpc = (rpc + kStage - 1) / kStage * kStage;
+  chunks = (N + rpc - 1) / rpc;
+  const int64_t E = (int64_t)kNOff * cin * cout;
+  float* part = nullptr;
+  int rc = dev_alloc((void**)&part, (size_t)chunks * E * 4, s, "igc_sparse_conv_backward: wgrad partials");
+  if (rc) return rc;
+  k_wgrad_f32<<<(unsigned)(kNOff * chunks), 256, 0, s>>>(d_map, N, (const float*)d_feats, (const float*)d_dout, cin,
+                                                        cout, rpc, part);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) {
+    k_wgrad_reduce<<<(unsigned)((E + 255) / 256 < 4096 ? (E + 255) / 256 : 4096), 256, 0, s>>>(part, chunks, E, d_dw);
+    e = hipGetLastError();
+  }
+  dev_free(part, s);
+  if (e != hipSuccess) return hip_status(e, "igc_sparse_conv_backward: wgrad launch");
+  return IGC_OK;
+}
+
+}  // namespace
+
+bool wgrad_supported(int32_t dtype, int32_t cin, int32_t cout) {
+  if (dtype == IGC_BF16) return cin >= 32 && cin % 32 == 0 && cin <= 1024 && cout >= 64 && cout % 64 == 0 && cout <= 1024;
+  return dtype == IGC_F32 && cin >= 1 && cout >= 1 && cin <= 64 && cout <= 64 && cin * cout <= 1024;
+}
+
+int launch_conv_backward(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype, int32_t cin,
+                         const void* d_w, int32_t cout, const void* d_dout, void* d_dfeats, float* d_dw,
+                         int32_t dgrad_path, hipStream_t s) {
+  const size_t esize = dtype == IGC_BF16 ? 2 : 4;
+  if (d_dfeats) {
+    void* wf = nullptr;
+    int rc = dev_alloc(&wf, (size_t)kNOff * cin * cout * esize, s, "igc_sparse_conv_backward: flipped weights");
+    if (rc) return rc;
+    if (dtype == IGC_BF16)
+      k_flip_w<uint16_t><<<256, 256, 0, s>>>((const uint16_t*)d_w, (uint16_t*)wf, cin, cout);
+    else
+      k_flip_w<float><<<256, 256, 0, s>>>((const float*)d_w, (float*)wf, cin, cout);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      dev_free(wf, s);
+      return hip_status(e, "igc_sparse_conv_backward: weight flip launch");
+    }
+    // dX = forward conv of dY (cout channels) with W~ (cout -> cin).
+    rc = dgrad_path == IGC_PATH_LEAF ? launch_conv_leaf(g, d_dout, dtype, cout, wf, cin, d_dfeats, s)
+                                     : launch_conv_ggs(g, d_map, d_dout, dtype, cout, wf, cin, d_dfeats, s);
+    dev_free(wf, s);
+    if (rc) return rc;
+  }
+  if (d_dw) {
+    if (dtype == IGC_BF16) {
+      if (cin % 128 == 0 && cout % 128 == 0) return launch_wgrad_bf16<128, 128>(g, d_map, d_feats, cin, d_dout, cout, d_dw, s);
+      if (cin % 64 == 0) return launch_wgrad_bf16<64, 64>(g, d_map, d_feats, cin, d_dout, cout, d_dw, s);
+      return launch_wgrad_bf16<32, 64>(g, d_map, d_feats, cin, d_dout, cout, d_dw, s);
+    }
+    return launch_wgrad_f32(g, d_map, d_feats, cin, d_dout, cout, d_dw, s);
+  }
+  return IGC_OK;
+}
+
+}  // namespace igc

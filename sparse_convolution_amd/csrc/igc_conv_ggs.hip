@@ -376,6 +376,14 @@ void launch_main(int64_t n_tiles, int64_t col_tiles, const int32_t* map, int64_t
 
 }  // namespace
 
+int launch_ggs_plan(const int32_t* d_map, int64_t N, int32_t* perm, uint16_t* blk, hipStream_t s) {
+  const int64_t n_tiles = (N + kBM - 1) / kBM;
+  if (n_tiles == 0) return IGC_OK;
+  k_ggs_plan<<<(unsigned)n_tiles, kBM, 0, s>>>(d_map, N, perm, blk);
+  IGC_HIP(hipGetLastError(), "igc_sparse_conv: plan launch");
+  return IGC_OK;
+}
+
 bool ggs_conv_supported(int32_t dtype, int32_t cin, int32_t cout) {
   return dtype == IGC_BF16 && cin >= 32 && cin <= 1024 && cin % 32 == 0 && cout >= 64 && cout <= 1024 &&
          cout % 64 == 0;

@@ -410,6 +410,7 @@ bool leaf_conv_supported(int32_t dtype, int32_t cin, int32_t cout) {
   if (dtype != IGC_F32) return false;
   switch (cin * 1000 + cout) {
     case 4008: case 4016: case 4032: case 8008: case 8016: case 8032: case 16016:
+    case 8004: case 16004: case 16008:  // the input-gradient shapes of 4 -> 8, 4 -> 16, 8 -> 16
       return true;
     default:
       return false;
@@ -427,6 +428,9 @@ int launch_conv_leaf(const igc_grid* g, const void* d_feats, int32_t dtype, int3
     case 8016: return launch_leaf<8, 16>(g, d_feats, d_w, d_out, s);
     case 8032: return launch_leaf<8, 32>(g, d_feats, d_w, d_out, s);
     case 16016: return launch_leaf<16, 16>(g, d_feats, d_w, d_out, s);
+    case 8004: return launch_leaf<8, 4>(g, d_feats, d_w, d_out, s);
+    case 16004: return launch_leaf<16, 4>(g, d_feats, d_w, d_out, s);
+    case 16008: return launch_leaf<16, 8>(g, d_feats, d_w, d_out, s);
     default: return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: leaf path shape");
   }
 }
