@@ -6,13 +6,18 @@ IndexGrid from the shuffled coordinates (tile hash, radix sort, node registratio
 27-offset kernel map, and the 3x3x3 submanifold convolution on the automatically chosen
 path. Prints one JSON line.
 
-    python bench.py [--workload leaf] [--steps K] [--warmup W] [--gpus 1]
+    python bench.py [--workload leaf] [--steps K] [--warmup W] [--gpus 1] [--backward]
 
 value = effective conv FLOPs (2 * pairs * cin * cout, empty MACs excluded, as the fVDB notes
 define effective TFLOPS in their micro-benchmarks) per second of the whole step. The line also
 carries per-phase times, the build rate in Mvox/s, the roofline of the dominant kernel (the
 convolution) timed with HIP events on its launch stream, and the CPU oracle timed on the host
 cores as a reference point.
+
+With --backward a step also runs the two gradients of the convolution (input gradient, then
+weight gradient, as two calls of igc_sparse_conv_backward) for a synthetic output gradient;
+value is then 3 * 2 * pairs * cin * cout per second of the whole step, and the line carries
+both gradients' phase times and rooflines. The default line is unchanged.
 """
 from __future__ import annotations
 
@@ -120,6 +125,7 @@ def main() -> int:
     ap.add_argument("--path", default="auto", choices=["auto", "leaf", "ggs"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--backward", action="store_true", help="add the input and weight gradients to the step")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -153,7 +159,10 @@ def main() -> int:
     info = dict(n_input=g0.n_input, n_voxels=N, n_leaf=g0.n_leaf, n_lower=g0.n_lower, n_upper=g0.n_upper,
                 sort_passes=g0.sort_passes, leaf_occupancy=round(g0.leaf_occupancy, 4))
     out = torch.empty((N, wl.cout), dtype=tdtype, device=dev)
+    dout = (torch.from_numpy(workloads.make_features(N, wl.cout, 7000 + wl.index)).to(dev, tdtype)
+            if args.backward else None)
     del m0, g0
+    n_ev = 6 if args.backward else 4
 
     stream = torch.cuda.current_stream(dev)
 
@@ -165,13 +174,19 @@ def main() -> int:
         ev[2].record(stream)
         igc.sparse_conv(g, feats, weights, kmap=m, path=path, out=out)
         ev[3].record(stream)
+        if args.backward:
+            dx, _ = igc.sparse_conv_backward(g, feats, weights, dout, m, path=path, need_dweights=False)
+            ev[4].record(stream)
+            _, dw = igc.sparse_conv_backward(g, feats, weights, dout, m, path=path, need_dfeats=False)
+            ev[5].record(stream)
+            return g, m, dx, dw
         return g, m
 
     for _ in range(warmup):
-        step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+        step([torch.cuda.Event(enable_timing=True) for _ in range(n_ev)])
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
     keep = None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -186,7 +201,7 @@ def main() -> int:
     t_conv = [e[2].elapsed_time(e[3]) for e in events]
     ms_step = wall * 1e3 / steps
     flops = 2.0 * pairs * wl.cin * wl.cout
-    value = flops / (ms_step * 1e-3) / 1e12
+    value = (3.0 if args.backward else 1.0) * flops / (ms_step * 1e-3) / 1e12
 
     conv_ms = float(np.mean(t_conv))
     conv_tflops = flops / (conv_ms * 1e-3) / 1e12
@@ -216,8 +231,25 @@ def main() -> int:
         "host_syncs_per_step": 2,
     }
 
+    if args.backward:
+        t_dgrad = [e[3].elapsed_time(e[4]) for e in events]
+        t_wgrad = [e[4].elapsed_time(e[5]) for e in events]
+        for name, t in (("dgrad_ms", t_dgrad), ("wgrad_ms", t_wgrad)):
+            phases[name] = {"mean": round(float(np.mean(t)), 4), "p50": _pct(t, 50), "p95": _pct(t, 95),
+                            "p99": _pct(t, 99)}
+        backward = {}
+        for name, t in (("dgrad", t_dgrad), ("wgrad", t_wgrad)):
+            tf = flops / (float(np.mean(t)) * 1e-3) / 1e12
+            # The weight gradient's operands are the layer's dtype; its fp32 form runs on fp32 MFMA.
+            backward[name] = {"tflops": round(tf, 3), "peak": peak, "frac": round(tf / peak, 4),
+                              "avg_call_ms": round(float(np.mean(t)), 4)}
+        backward["wgrad"]["kernel"] = "k_wgrad_bf16" if wl.dtype == "bf16" else "k_wgrad_leaf_f32"
+
     line = {
-        "metric": METRIC, "value": round(value, 4), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "metric": (METRIC if not args.backward else
+                   "sparse-conv training-step effective TFLOP/s (3·2·pairs·Cin·Cout/s: forward, input and weight "
+                   "gradients) incl. IndexGrid build and kernel map"),
+        "value": round(value, 4), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": args.workload, "description": wl.description, "cin": wl.cin, "cout": wl.cout,
@@ -227,6 +259,8 @@ def main() -> int:
         "phases": phases,
         "roofline": roofline,
     }
+    if args.backward:
+        line["backward"] = backward
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(coords, wl, wl.cin, wl.cout, wl.dtype)
     print(json.dumps(line), flush=True)

@@ -18,7 +18,8 @@
 //    no pair at the workgroup's offset is skipped. The stage's gathered input rows and output
 //    gradients are written to LDS transposed (channel-major, rows contiguous), so both MFMA
 //    operands are 16-byte reads of 8 consecutive rows.
-//  - fp32 (the leaf path's narrow shapes): plain fp32 FMAs over 64-row stages in LDS.
+//  - fp32: the leaf-local kernel (k_wgrad_leaf_f32, fp32 MFMA over each leaf's window) for the
+//    leaf path's shapes, otherwise plain fp32 FMAs over 64-row stages in LDS.
 #include <hip/hip_runtime.h>
 
 #include "igc_host.h"
@@ -63,7 +64,12 @@ struct WgradSplit {
 };
 
 // Partial dW blocks of MB input x NB output channels per (offset, chunk of tiles), bf16 data.
-// Four waves in 2 x 2, each (MB/2) x (NB/2) with 16x16x32 MFMAs.
+// Four waves in 2 x 2, each (MB/2) x (NB/2) with 16x16x32 MFMAs. The stages (64 rows of a
+// tile that hold at least one pair at the offset) are software-pipelined through registers:
+// while the MFMAs consume stage i from LDS, the thread's loads for the next stages are in
+// flight - the input and output-gradient rows of stage i+1, the source rows (kernel map) of
+// stage i+2 and the row order of stage i+3. Thread tid stages rows 2 (tid % 32) and
+// 2 (tid % 32) + 1 of a stage, for the 8-channel granules tid / 32 + 8 j.
 template <int MB, int NB>
 __global__ __launch_bounds__(256) void k_wgrad_bf16(const int32_t* __restrict__ map, int64_t N,
                                                     const int32_t* __restrict__ perm,
@@ -73,21 +79,79 @@ __global__ __launch_bounds__(256) void k_wgrad_bf16(const int32_t* __restrict__ 
                                                     int64_t n_tiles, int64_t tiles_per_chunk, WgradSplit sp,
                                                     float* __restrict__ part) {
   constexpr int MI = MB / 32, NI = NB / 32;  // 16-blocks per wave
+  constexpr int XG = MB / 8, DG = NB / 8;    // 8-channel granules of a row
+  constexpr int XI = (32 * XG + 255) / 256, DI = (32 * DG + 255) / 256;  // staging items per thread
   static_assert(MI >= 1 && NI >= 1, "block shape");
   __shared__ __attribute__((aligned(16))) uint16_t s_xt[MB * kLdT];  // [channel][row]
   __shared__ __attribute__((aligned(16))) uint16_t s_dt[NB * kLdT];
-  __shared__ int32_t s_row[kStage], s_src[kStage];
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const int pr = tid & 31;
   int o, mb, nb;
   int64_t chunk;
   sp.decode(blockIdx.x, o, chunk, mb, nb);
   const int c0 = mb * MB, n0 = nb * NB;
   const int64_t t0 = chunk * tiles_per_chunk;
   const int64_t t1 = t0 + tiles_per_chunk < n_tiles ? t0 + tiles_per_chunk : n_tiles;
+  const int32_t* map_o = map + (size_t)o * (size_t)N;
+
+  // Stage cursor over the chunk: code t * 4 + st of the next stage with a pair, -1 past the end.
+  int64_t ct = t0;
+  int cst = -1;
+  uint32_t cbits = t0 < t1 ? blk[t0 * kNOff + o] : 0u;
+  uint32_t nbits = t0 + 1 < t1 ? blk[(t0 + 1) * kNOff + o] : 0u;
+  auto next_stage = [&]() -> int64_t {
+    while (ct < t1) {
+      if (++cst == 4) {
+        cst = 0;
+        ++ct;
+        cbits = nbits;
+        nbits = ct + 1 < t1 ? blk[(ct + 1) * kNOff + o] : 0u;
+        if (ct >= t1) break;
+      }
+      if ((cbits >> (cst * 4)) & 0xFu) return ct * 4 + cst;
+    }
+    return -1;
+  };
+  auto load_perm = [&](int64_t sc, int32_t& r0, int32_t& r1) {
+    if (sc >= 0) {
+      const int2 v = *(const int2*)&perm[(sc >> 2) * kTileRows + (sc & 3) * kStage + 2 * pr];
+      r0 = v.x;
+      r1 = v.y;
+    } else {
+      r0 = r1 = -1;
+    }
+  };
+  auto load_src = [&](int32_t r, int32_t& src) { src = r >= 0 ? map_o[r] : -1; };
+  uint4 xa[XI], xb[XI], da[DI], db[DI];  // stage data: rows 2 pr (a) and 2 pr + 1 (b)
+  auto load_data = [&](int32_t r0, int32_t r1, int32_t s0, int32_t s1) {
+#pragma unroll
+    for (int j = 0; j < XI; ++j) {
+      const int g = (tid >> 5) + 8 * j;
+      const bool ok = 32 * XG >= 256 || g < XG;
+      xa[j] = ok && s0 >= 0 ? *(const uint4*)(feats + (size_t)s0 * cin + c0 + g * 8) : make_uint4(0, 0, 0, 0);
+      xb[j] = ok && s1 >= 0 ? *(const uint4*)(feats + (size_t)s1 * cin + c0 + g * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < DI; ++j) {
+      const int g = (tid >> 5) + 8 * j;
+      const bool ok = 32 * DG >= 256 || g < DG;
+      da[j] = ok && s0 >= 0 ? *(const uint4*)(dout + (size_t)r0 * cout + n0 + g * 8) : make_uint4(0, 0, 0, 0);
+      db[j] = ok && s1 >= 0 ? *(const uint4*)(dout + (size_t)r1 * cout + n0 + g * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // Transposed store: channel c of granule g gets the pair (row 2 pr, row 2 pr + 1) as one word.
+  auto store_pair = [&](uint16_t* dst, int g, const uint4& a, const uint4& b) {
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t lo = (av[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu, hi = (bv[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu;
+      *(uint32_t*)&dst[(g * 8 + c) * kLdT + 2 * pr] = lo | (hi << 16);
+    }
+  };
 
   f32x4 acc[MI][NI];
 #pragma unroll
@@ -95,61 +159,62 @@ __global__ __launch_bounds__(256) void k_wgrad_bf16(const int32_t* __restrict__ 
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Prologue: data of the first stage, source rows of the second, row order of the third.
+  int64_t cur = next_stage();
+  int64_t nx1 = next_stage();
+  int64_t nx2 = next_stage();
+  int32_t r0, r1, s0, s1;
+  load_perm(cur, r0, r1);
+  load_src(r0, s0);
+  load_src(r1, s1);
+  load_data(r0, r1, s0, s1);
+  int32_t m_r0, m_r1, m_s0, m_s1;  // stage nx1
+  load_perm(nx1, m_r0, m_r1);
+  load_src(m_r0, m_s0);
+  load_src(m_r1, m_s1);
+  int32_t p_r0, p_r1;  // stage nx2
+  load_perm(nx2, p_r0, p_r1);
+
   const int frow = lane & 15, fk = (lane >> 4) * 8;
-  for (int64_t t = t0; t < t1; ++t) {
-    const uint32_t bits = blk[t * kNOff + o];
-    for (int st = 0; st < kTileRows / kStage; ++st) {
-      if (((bits >> (st * 4)) & 0xFu) == 0u) continue;  // no pair at this offset in these 64 rows
-      __syncthreads();  // the previous stage's reads are done
-      if (tid < kStage) {
-        const int32_t r = perm[t * kTileRows + st * kStage + tid];
-        s_row[tid] = r;
-        s_src[tid] = r >= 0 ? map[(size_t)o * (size_t)N + r] : -1;
-      }
-      __syncthreads();
-      // Transposed staging: item = (row pair, 8-channel granule); two 16-byte loads, eight
-      // 4-byte LDS writes of (row 2p, row 2p+1) per channel.
-      for (int it = tid; it < (kStage / 2) * (MB / 8); it += 256) {
-        const int pr = it % (kStage / 2), g = it / (kStage / 2);
-        const int32_t s0 = s_src[2 * pr], s1 = s_src[2 * pr + 1];
-        const uint4 a = s0 >= 0 ? *(const uint4*)(feats + (size_t)s0 * cin + c0 + g * 8) : make_uint4(0, 0, 0, 0);
-        const uint4 b = s1 >= 0 ? *(const uint4*)(feats + (size_t)s1 * cin + c0 + g * 8) : make_uint4(0, 0, 0, 0);
-        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+  while (cur >= 0) {
+    __syncthreads();  // the previous stage's LDS reads are done
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint32_t lo = (av[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu, hi = (bv[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu;
-          *(uint32_t*)&s_xt[(g * 8 + c) * kLdT + 2 * pr] = lo | (hi << 16);
-        }
-      }
-      for (int it = tid; it < (kStage / 2) * (NB / 8); it += 256) {
-        const int pr = it % (kStage / 2), g = it / (kStage / 2);
-        const int32_t r0 = s_src[2 * pr] >= 0 ? s_row[2 * pr] : -1, r1 = s_src[2 * pr + 1] >= 0 ? s_row[2 * pr + 1] : -1;
-        const uint4 a = r0 >= 0 ? *(const uint4*)(dout + (size_t)r0 * cout + n0 + g * 8) : make_uint4(0, 0, 0, 0);
-        const uint4 b = r1 >= 0 ? *(const uint4*)(dout + (size_t)r1 * cout + n0 + g * 8) : make_uint4(0, 0, 0, 0);
-        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+    for (int j = 0; j < XI; ++j) {
+      const int g = (tid >> 5) + 8 * j;
+      if (32 * XG >= 256 || g < XG) store_pair(s_xt, g, xa[j], xb[j]);
+    }
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint32_t lo = (av[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu, hi = (bv[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu;
-          *(uint32_t*)&s_dt[(g * 8 + c) * kLdT + 2 * pr] = lo | (hi << 16);
-        }
-      }
-      __syncthreads();
+    for (int j = 0; j < DI; ++j) {
+      const int g = (tid >> 5) + 8 * j;
+      if (32 * DG >= 256 || g < DG) store_pair(s_dt, g, da[j], db[j]);
+    }
+    // Loads for the next stages.
+    load_data(m_r0, m_r1, m_s0, m_s1);
+    m_r0 = p_r0;
+    m_r1 = p_r1;
+    load_src(m_r0, m_s0);
+    load_src(m_r1, m_s1);
+    const int64_t nx3 = next_stage();
+    load_perm(nx3, p_r0, p_r1);
+    __syncthreads();
 #pragma unroll
-      for (int ks = 0; ks < kStage; ks += 32) {
-        bf16x8 a[MI], b[NI];
+    for (int ks = 0; ks < kStage; ks += 32) {
+      bf16x8 a[MI], b[NI];
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-          a[mi] = *(const bf16x8*)&s_xt[(wm * (MB / 2) + mi * 16 + frow) * kLdT + ks + fk];
+      for (int mi = 0; mi < MI; ++mi)
+        a[mi] = *(const bf16x8*)&s_xt[(wm * (MB / 2) + mi * 16 + frow) * kLdT + ks + fk];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        b[ni] = *(const bf16x8*)&s_dt[(wn * (NB / 2) + ni * 16 + frow) * kLdT + ks + fk];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
-          b[ni] = *(const bf16x8*)&s_dt[(wn * (NB / 2) + ni * 16 + frow) * kLdT + ks + fk];
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
-      }
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
     }
+    cur = nx1;
+    nx1 = nx2;
+    nx2 = nx3;
   }
   // D layout: lane holds column lane%16 of rows 4*(lane/16) + j.
   float* dst = part + ((size_t)chunk * kNOff + o) * (size_t)cin * cout;
@@ -211,13 +276,39 @@ __global__ __launch_bounds__(256) void k_wgrad_f32(const int32_t* __restrict__ m
   }
 }
 
-// dw[e] = sum over chunks c (in order) of part[c * E + e], accumulated in fp64.
-__global__ void k_wgrad_reduce(const float* __restrict__ part, int64_t chunks, int64_t E, float* __restrict__ dw) {
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < E; e += (int64_t)gridDim.x * blockDim.x) {
-    double s = 0.0;
-    for (int64_t c = 0; c < chunks; ++c) s += (double)part[c * E + e];
-    dw[e] = (float)s;
+// dw[e] = sum over chunks c of part[c * E + e], in fp64 and in a fixed order: thread group q
+// of NG adds the chunks c = q, q + NG, ... in increasing order, then the NG group sums are added
+// in order of q. A workgroup covers 256 / NG consecutive elements.
+template <int NG>
+__global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ part, int64_t chunks, int64_t E,
+                                                      float* __restrict__ dw) {
+  constexpr int EL = 256 / NG;
+  __shared__ double s_sum[NG][EL];
+  const int el = threadIdx.x % EL, q = threadIdx.x / EL;
+  const int64_t e = (int64_t)blockIdx.x * EL + el;
+  double acc = 0.0;
+  if (e < E) {
+#pragma unroll 8
+    for (int64_t c = q; c < chunks; c += NG) acc += (double)part[c * E + e];
   }
+  s_sum[q][el] = acc;
+  __syncthreads();
+  if (q == 0 && e < E) {
+    double t = 0.0;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) t += s_sum[k][el];
+    dw[e] = (float)t;
+  }
+}
+
+int launch_wgrad_reduce(const float* part, int64_t chunks, int64_t E, float* dw, hipStream_t s) {
+  // Few elements and many chunks: more threads per element.
+  if (E >= 65536 || chunks <= 64)
+    k_wgrad_reduce<8><<<(unsigned)((E + 31) / 32), 256, 0, s>>>(part, chunks, E, dw);
+  else
+    k_wgrad_reduce<32><<<(unsigned)((E + 7) / 8), 256, 0, s>>>(part, chunks, E, dw);
+  IGC_HIP(hipGetLastError(), "igc_sparse_conv_backward: weight-gradient reduction launch");
+  return IGC_OK;
 }
 
 template <int MB, int NB>
@@ -251,38 +342,40 @@ int launch_wgrad_bf16(const igc_grid* g, const int32_t* d_map, const void* d_fea
     k_wgrad_bf16<MB, NB><<<(unsigned)(kNOff * chunks * sp.mblocks * sp.nblocks), 256, 0, s>>>(
         d_map, N, perm, blk, (const uint16_t*)d_feats, (const uint16_t*)d_dout, cin, cout, n_tiles, tpc, sp, part);
     e = hipGetLastError();
-    if (e == hipSuccess) {
-      k_wgrad_reduce<<<(unsigned)((E + 255) / 256 < 4096 ? (E + 255) / 256 : 4096), 256, 0, s>>>(part, chunks, E, d_dw);
-      e = hipGetLastError();
-    }
+    if (e != hipSuccess) rc = hip_status(e, "igc_sparse_conv_backward: wgrad launch");
+    else rc = launch_wgrad_reduce(part, chunks, E, d_dw, s);
   }
   dev_free(ws, s);
-  if (rc) return rc;
-  if (e != hipSuccess) return hip_status(e, "igc_sparse_conv_backward: wgrad launch");
-  return IGC_OK;
+  return rc;
 }
 
 int launch_wgrad_f32(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t cin, const void* d_dout,
                      int32_t cout, float* d_dw, hipStream_t s) {
+  const int64_t E = (int64_t)kNOff * cin * cout;
+  if (wgrad_leaf_supported(cin, cout)) {
+    const int64_t groups = wgrad_leaf_groups(g);
+    float* part = nullptr;
+    int rc = dev_alloc((void**)&part, (size_t)groups * E * 4, s, "igc_sparse_conv_backward: wgrad partials");
+    if (rc) return rc;
+    rc = launch_wgrad_leaf(g, d_feats, cin, d_dout, cout, part, groups, s);
+    if (rc == IGC_OK) rc = launch_wgrad_reduce(part, groups, E, d_dw, s);
+    dev_free(part, s);
+    return rc;
+  }
   const int64_t N = g->n_voxels;
   int64_t chunks = 2048 / kNOff;
   int64_t rpc = (N + chunks - 1) / chunks;
   rpc = (rpc + kStage - 1) / kStage * kStage;
   chunks = (N + rpc - 1) / rpc;
-  const int64_t E = (int64_t)kNOff * cin * cout;
   float* part = nullptr;
   int rc = dev_alloc((void**)&part, (size_t)chunks * E * 4, s, "igc_sparse_conv_backward: wgrad partials");
   if (rc) return rc;
   k_wgrad_f32<<<(unsigned)(kNOff * chunks), 256, 0, s>>>(d_map, N, (const float*)d_feats, (const float*)d_dout, cin,
                                                         cout, rpc, part);
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess) {
-    k_wgrad_reduce<<<(unsigned)((E + 255) / 256 < 4096 ? (E + 255) / 256 : 4096), 256, 0, s>>>(part, chunks, E, d_dw);
-    e = hipGetLastError();
-  }
+  rc = e != hipSuccess ? hip_status(e, "igc_sparse_conv_backward: wgrad launch") : launch_wgrad_reduce(part, chunks, E, d_dw, s);
   dev_free(part, s);
-  if (e != hipSuccess) return hip_status(e, "igc_sparse_conv_backward: wgrad launch");
-  return IGC_OK;
+  return rc;
 }
 
 }  // namespace

@@ -31,14 +31,83 @@ __device__ __forceinline__ int64_t xcd_block(int64_t bid, int64_t nblk) {
   return x * q + (x < rem ? x : rem) + (bid >> 3);
 }
 
+// Leaf records of the 3x3x3 block of leaves around leaf f (slot 13 = f) from the grid's
+// neighbour table into LDS (threads 0..26); an absent leaf is an empty record.
+__device__ __forceinline__ void load_leaf_block(const GridView& g, int64_t f, int tid, uint64_t (*s_mask)[8],
+                                                uint64_t* s_off, uint64_t* s_pre) {
+  if (tid < 27) {
+    const int32_t nl = g.leaf_nbr[f * 27 + tid];
+    if (nl >= 0) {
+      const LeafRec& L = g.leaf[nl];
+      for (int q = 0; q < 8; ++q) s_mask[tid][q] = L.mask[q];
+      s_off[tid] = L.offset;
+      s_pre[tid] = L.prefix;
+    } else {
+      for (int q = 0; q < 8; ++q) s_mask[tid][q] = 0;
+      s_off[tid] = 0;
+      s_pre[tid] = 0;
+    }
+  }
+}
+
+// Positions of slot 13's active voxels in row order, and their count (one wave).
+__device__ __forceinline__ void compact_leaf(int lane, const uint64_t (*s_mask)[8], uint16_t* s_pos,
+                                             uint32_t* s_count) {
+  const uint64_t lt = (1ull << lane) - 1ull;
+  uint32_t count = 0;
+  for (int q = 0; q < 8; ++q) {
+    const uint64_t word = s_mask[13][q];
+    if ((word >> lane) & 1ull) s_pos[count + (uint32_t)__popcll(word & lt)] = (uint16_t)(q * 64 + lane);
+    count += (uint32_t)__popcll(word);
+  }
+  if (lane == 0) *s_count = count;
+}
+
+// Rotation of the 4-channel granules of window cell c: granule j of a cell is stored at granule
+// (j + win_rot<CIN>(c)) mod CIN/4. Cells 64/CIN apart start on the same LDS bank, so without it
+// the 16 rows of an MFMA operand read (16 cells, one granule each) meet on a few banks; with it
+// consecutive groups of 64/CIN cells use different granules.
+template <int CIN>
+__device__ __forceinline__ int win_rot(int c) {
+  return CIN >= 8 ? (c / (64 / CIN)) & (CIN / 4 - 1) : 0;
+}
+
+// fp32 window [1000 cells][CIN]: cell (x+1, y+1, z+1) for leaf-local x, y, z in [-1, 8] holds
+// the features of that voxel (granules rotated by win_rot), zero where it is inactive or its
+// leaf is absent.
+template <int CIN>
+__device__ __forceinline__ void fill_window_f32(float* s_win, const uint64_t (*s_mask)[8], const uint64_t* s_off,
+                                                const uint64_t* s_pre, const float* __restrict__ feats, int tid) {
+  for (int c = tid; c < 1000; c += 256) {
+    const int x = c / 100 - 1, y = (c / 10) % 10 - 1, z = c % 10 - 1;  // leaf-local, in [-1, 8]
+    const int slot = ((x >> 3) + 1) * 9 + ((y >> 3) + 1) * 3 + ((z >> 3) + 1);
+    const uint32_t q = (uint32_t)(x & 7);
+    const uint64_t bit = 1ull << ((uint32_t)((y & 7) << 3) | (uint32_t)(z & 7));
+    const uint64_t word = s_mask[slot][q];
+    float4* dst = (float4*)&s_win[c * CIN];
+    if (word & bit) {
+      const uint32_t pre = q ? (uint32_t)(s_pre[slot] >> (9u * (q - 1u))) & 511u : 0u;
+      const uint64_t row = s_off[slot] + pre + (uint32_t)__popcll(word & (bit - 1ull));
+      const float4* src = (const float4*)(feats + row * CIN);
+      const int rot = win_rot<CIN>(c);
+#pragma unroll
+      for (int v = 0; v < CIN / 4; ++v) dst[(v + rot) & (CIN / 4 - 1)] = src[v];
+    } else {
+#pragma unroll
+      for (int v = 0; v < CIN / 4; ++v) dst[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+}
+
 template <int CIN, int COUT>
 __global__ __launch_bounds__(256) void k_conv_leaf_f32_wide(GridView g, const float* __restrict__ feats,
                                                        const float* __restrict__ w, float* __restrict__ out) {
   constexpr int COUTP = (COUT + 15) / 16 * 16;
   constexpr int NS = COUTP / 16;  // 16-column MFMA slabs
   constexpr int KS = CIN / 4;     // 4-channel MFMA steps per offset
-  // W fragments stay in registers when they fit (54 per lane at 8 -> 16); otherwise in LDS.
-  constexpr bool kWRegs = NS * 27 * KS <= 64;
+  // W fragments stay in registers when they fit (108 per lane at 16 -> 16 or 16 -> 8);
+  // otherwise in LDS.
+  constexpr bool kWRegs = NS * 27 * KS <= 112;
   __shared__ __attribute__((aligned(16))) float s_win[1000 * CIN];
   __shared__ float s_w[kWRegs ? 1 : 27 * CIN * COUTP];
   __shared__ uint64_t s_mask[27][8];
@@ -54,20 +123,7 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32_wide(GridView g, const fl
   const int kq = lane >> 4;  // A column / B row / D row group
   const int64_t f = xcd_block(blockIdx.x, gridDim.x);
 
-  // Leaf records of the 3x3x3 block (slot 13 = this leaf) from the grid's neighbour table.
-  if (tid < 27) {
-    const int32_t nl = g.leaf_nbr[f * 27 + tid];
-    if (nl >= 0) {
-      const LeafRec& L = g.leaf[nl];
-      for (int q = 0; q < 8; ++q) s_mask[tid][q] = L.mask[q];
-      s_off[tid] = L.offset;
-      s_pre[tid] = L.prefix;
-    } else {
-      for (int q = 0; q < 8; ++q) s_mask[tid][q] = 0;
-      s_off[tid] = 0;
-      s_pre[tid] = 0;
-    }
-  }
+  load_leaf_block(g, f, tid, s_mask, s_off, s_pre);
   float wreg[kWRegs ? 27 * KS * NS : 1];
   if constexpr (kWRegs) {
 #pragma unroll
@@ -88,34 +144,8 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32_wide(GridView g, const fl
   __syncthreads();
 
   // Compacted active positions of this leaf (wave 0), and the window (all threads).
-  if (wave == 0) {
-    const uint64_t lt = (1ull << lane) - 1ull;
-    uint32_t count = 0;
-    for (int q = 0; q < 8; ++q) {
-      const uint64_t word = s_mask[13][q];
-      if ((word >> lane) & 1ull) s_pos[count + (uint32_t)__popcll(word & lt)] = (uint16_t)(q * 64 + lane);
-      count += (uint32_t)__popcll(word);
-    }
-    if (lane == 0) s_count = count;
-  }
-  for (int c = tid; c < 1000; c += 256) {
-    const int x = c / 100 - 1, y = (c / 10) % 10 - 1, z = c % 10 - 1;  // leaf-local, in [-1, 8]
-    const int slot = ((x >> 3) + 1) * 9 + ((y >> 3) + 1) * 3 + ((z >> 3) + 1);
-    const uint32_t q = (uint32_t)(x & 7);
-    const uint64_t bit = 1ull << ((uint32_t)((y & 7) << 3) | (uint32_t)(z & 7));
-    const uint64_t word = s_mask[slot][q];
-    float4* dst = (float4*)&s_win[c * CIN];
-    if (word & bit) {
-      const uint32_t pre = q ? (uint32_t)(s_pre[slot] >> (9u * (q - 1u))) & 511u : 0u;
-      const uint64_t row = s_off[slot] + pre + (uint32_t)__popcll(word & (bit - 1ull));
-      const float4* src = (const float4*)(feats + row * CIN);
-#pragma unroll
-      for (int v = 0; v < CIN / 4; ++v) dst[v] = src[v];
-    } else {
-#pragma unroll
-      for (int v = 0; v < CIN / 4; ++v) dst[v] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
+  if (wave == 0) compact_leaf(lane, s_mask, s_pos, &s_count);
+  fill_window_f32<CIN>(s_win, s_mask, s_off, s_pre, feats, tid);
   __syncthreads();
 
   const uint32_t count = s_count;
@@ -131,9 +161,10 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32_wide(GridView g, const fl
 #pragma unroll
     for (int o = 0; o < 27; ++o) {
       const int cell = cell0 + (o / 9) * 100 + ((o / 3) % 3) * 10 + o % 3;
+      const int rot = win_rot<CIN>(cell);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const float a = s_win[cell * CIN + ks * 4 + kq];
+        const float a = s_win[cell * CIN + (((ks + rot) & (KS - 1)) << 2) + kq];
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
           float b;
@@ -214,19 +245,7 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
   const int kg = lane >> 4;  // k group of A and B, row group of D
   const int64_t f = xcd_block(blockIdx.x, gridDim.x);
 
-  if (tid < 27) {
-    const int32_t nl = g.leaf_nbr[f * 27 + tid];
-    if (nl >= 0) {
-      const LeafRec& L = g.leaf[nl];
-      for (int q = 0; q < 8; ++q) s_mask[tid][q] = L.mask[q];
-      s_off[tid] = L.offset;
-      s_pre[tid] = L.prefix;
-    } else {
-      for (int q = 0; q < 8; ++q) s_mask[tid][q] = 0;
-      s_off[tid] = 0;
-      s_pre[tid] = 0;
-    }
-  }
+  load_leaf_block(g, f, tid, s_mask, s_off, s_pre);
 
   // W splits for this lane: chunk q, split s, column slab ns -> 8 bf16 (k = 8 kg .. 8 kg + 7).
   // Every wave needs the same fragments: wave w splits the (q, ns) pairs with (q*NS+ns) % 4 ==
@@ -275,16 +294,7 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
   __syncthreads();
 
   // Compacted active positions of this leaf (wave 0), and the split window (all threads).
-  if (wave == 0) {
-    const uint64_t lt = (1ull << lane) - 1ull;
-    uint32_t count = 0;
-    for (int q = 0; q < 8; ++q) {
-      const uint64_t word = s_mask[13][q];
-      if ((word >> lane) & 1ull) s_pos[count + (uint32_t)__popcll(word & lt)] = (uint16_t)(q * 64 + lane);
-      count += (uint32_t)__popcll(word);
-    }
-    if (lane == 0) s_count = count;
-  }
+  if (wave == 0) compact_leaf(lane, s_mask, s_pos, &s_count);
   // Window: up to four cells per thread; all their feature loads are issued before the first
   // split so that their latencies overlap.
   constexpr int CPT = (1000 + 255) / 256;
@@ -387,6 +397,165 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
   }
 }
 
+// Weight gradient of the leaf-local convolution, fp32 data (v_mfma_f32_16x16x4_f32):
+// dW[o][ci][co] = sum over active voxels v of X[v + offset o][ci] dY[v][co], X zero where
+// inactive. A workgroup walks a contiguous run of leaves; for each it fills the fp32 10^3 window
+// of X as the forward does and stages the leaf's dY rows (consecutive output rows) in LDS. The
+// MFMA's M dimension is the flattened pair m = o * CIN + ci (27 CIN, padded to 16), N the output
+// channels (padded to 16) and K the leaf's active voxels, four per step: the A operand is one
+// window read at the voxel's shifted cell, the B operand one dY read. Wave w takes the K steps
+// w, w + 4, ... of every leaf with all M blocks, so one step issues MB x NS independent MFMAs,
+// and keeps its sums in registers across the run. At the end the four waves' sums are added in
+// LDS in wave order and the workgroup writes its partial dW; the partials of all workgroups are
+// added in a fixed order afterwards.
+template <int CIN, int COUT>
+__global__ __launch_bounds__(256) void k_wgrad_leaf_f32(GridView g, int64_t n_leaf, int64_t leaves_per_group,
+                                                        const float* __restrict__ feats,
+                                                        const float* __restrict__ dout, float* __restrict__ part) {
+  constexpr int MB = (27 * CIN + 15) / 16;  // 16-row M blocks
+  constexpr int NS = (COUT + 15) / 16;      // 16-column N slabs
+  constexpr int CPT = (1000 + 255) / 256;   // window cells per thread
+  constexpr int DPT = (512 * COUT / 4 + 255) / 256;  // dY float4s per thread
+  static_assert(MB * NS * 256 <= 1000 * CIN, "the cross-wave sum fits in the window");
+  __shared__ __attribute__((aligned(16))) float s_win[1000 * CIN];
+  __shared__ __attribute__((aligned(16))) float s_dy[512 * COUT];
+  __shared__ uint64_t s_mask[27][8];
+  __shared__ uint64_t s_off[27];
+  __shared__ uint64_t s_pre[27];
+  __shared__ uint16_t s_cell[512];
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const int rl = lane & 15;  // A row (m) / B column (n) / D column
+  const int kq = lane >> 4;  // A column / B row (k) / D row group
+  const int64_t grp = xcd_block(blockIdx.x, gridDim.x);
+
+  // Window offset (cells * CIN + channel) of this lane's A row in each M block, -1 for padding
+  // rows (o > 26).
+  int aoff[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = mb * 16 + rl;
+    aoff[mb] = m < 27 * CIN ? cell_delta(m / CIN) * CIN + m % CIN : -1;
+  }
+  f32x4 acc[MB][NS];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) acc[mb][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t f0 = grp * leaves_per_group;
+  const int64_t f1 = f0 + leaves_per_group < n_leaf ? f0 + leaves_per_group : n_leaf;
+  for (int64_t f = f0; f < f1; ++f) {
+    __syncthreads();  // the previous leaf's window, dY and cell reads are done
+    load_leaf_block(g, f, tid, s_mask, s_off, s_pre);
+    __syncthreads();
+    uint32_t count = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) count += (uint32_t)__popcll(s_mask[13][q]);
+    const uint32_t cnt4 = (count + 3u) & ~3u;
+    // All window and dY loads are issued before the first LDS store.
+    float4 v[CPT][CIN / 4];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      const int x = c / 100 - 1, y = (c / 10) % 10 - 1, z = c % 10 - 1;  // leaf-local, in [-1, 8]
+      const int slot = ((x >> 3) + 1) * 9 + ((y >> 3) + 1) * 3 + ((z >> 3) + 1);
+      const uint32_t q = (uint32_t)(x & 7);
+      const uint64_t bit = 1ull << ((uint32_t)((y & 7) << 3) | (uint32_t)(z & 7));
+      const uint64_t word = c < 1000 ? s_mask[slot][q] : 0ull;
+      if (word & bit) {
+        const uint32_t pre = q ? (uint32_t)(s_pre[slot] >> (9u * (q - 1u))) & 511u : 0u;
+        const uint64_t row = s_off[slot] + pre + (uint32_t)__popcll(word & (bit - 1ull));
+        const float4* src = (const float4*)(feats + row * CIN);
+#pragma unroll
+        for (int j = 0; j < CIN / 4; ++j) v[i][j] = src[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < CIN / 4; ++j) v[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    // The leaf's dY rows are rows s_off[13] .. + count - 1; rows count .. cnt4 - 1 are zero.
+    const float4* dsrc = (const float4*)(dout + s_off[13] * COUT);
+    float4 d[DPT];
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) {
+      const uint32_t e = (uint32_t)tid + 256u * i;
+      d[i] = e < count * (COUT / 4) ? dsrc[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (wave == 0) {
+      // Window cell of offset (-1,-1,-1) for each active voxel, in row order.
+      const uint64_t lt = (1ull << lane) - 1ull;
+      uint32_t n = 0;
+      for (int q = 0; q < 8; ++q) {
+        const uint64_t word = s_mask[13][q];
+        if ((word >> lane) & 1ull)
+          s_cell[n + (uint32_t)__popcll(word & lt)] = (uint16_t)(q * 100 + (lane >> 3) * 10 + (lane & 7));
+        n += (uint32_t)__popcll(word);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      if (c < 1000) {
+#pragma unroll
+        for (int j = 0; j < CIN / 4; ++j) ((float4*)&s_win[c * CIN])[j] = v[i][j];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) {
+      const uint32_t e = (uint32_t)tid + 256u * i;
+      if (e < cnt4 * (COUT / 4)) ((float4*)s_dy)[e] = d[i];
+    }
+    __syncthreads();
+    for (uint32_t t0 = (uint32_t)wave * 4; t0 < count; t0 += 16) {
+      const uint32_t t = t0 + (uint32_t)kq;
+      const int cell0 = s_cell[t < count ? t : 0u];
+      float b[NS];
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) {
+        const int col = ns * 16 + rl;
+        b[ns] = col < COUT ? s_dy[t * COUT + col] : 0.f;
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const float a = aoff[mb] >= 0 ? s_win[cell0 * CIN + aoff[mb]] : 0.f;
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) acc[mb][ns] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b[ns], acc[mb][ns], 0, 0, 0);
+      }
+    }
+  }
+  // Cross-wave sum in the window's space, fragment-major: wave 0 stores, waves 1..3 add in turn.
+  __syncthreads();
+  f32x4* s_sum = (f32x4*)s_win;
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+          f32x4* p = &s_sum[(mb * NS + ns) * 64 + lane];
+          *p = w == 0 ? acc[mb][ns] : *p + acc[mb][ns];
+        }
+    }
+    __syncthreads();
+  }
+  // D: lane holds column lane%16 of rows 4*(lane/16) + j. Wave w writes M blocks w, w + 4, ...
+  float* dst = part + grp * (int64_t)(27 * CIN * COUT);
+  for (int mb = wave; mb < MB; mb += 4)
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      const f32x4 r = s_sum[(mb * NS + ns) * 64 + lane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = mb * 16 + kq * 4 + j;
+        const int col = ns * 16 + rl;
+        if (m < 27 * CIN && col < COUT) dst[m * COUT + col] = r[j];
+      }
+    }
+}
+
 template <int CIN, int COUT>
 int launch_leaf(const igc_grid* g, const void* d_feats, const void* d_w, void* d_out, hipStream_t s) {
   // Split-bf16 form for 4 or 8 input channels and up to 32 (CIN 4) / 16 (CIN 8) outputs, whose
@@ -401,6 +570,16 @@ int launch_leaf(const igc_grid* g, const void* d_feats, const void* d_w, void* d
                                                                        (const float*)d_w, (float*)d_out);
     IGC_HIP(hipGetLastError(), "igc_sparse_conv: leaf launch");
   }
+  return IGC_OK;
+}
+
+template <int CIN, int COUT>
+int launch_wgrad_leaf_t(const igc_grid* g, const void* d_feats, const void* d_dout, float* part, int64_t groups,
+                        hipStream_t s) {
+  const int64_t lpg = (g->n_leaf + groups - 1) / groups;
+  k_wgrad_leaf_f32<CIN, COUT><<<(unsigned)groups, 256, 0, s>>>(g->view(), g->n_leaf, lpg, (const float*)d_feats,
+                                                               (const float*)d_dout, part);
+  IGC_HIP(hipGetLastError(), "igc_sparse_conv_backward: leaf weight-gradient launch");
   return IGC_OK;
 }
 
@@ -432,6 +611,43 @@ int launch_conv_leaf(const igc_grid* g, const void* d_feats, int32_t dtype, int3
     case 16004: return launch_leaf<16, 4>(g, d_feats, d_w, d_out, s);
     case 16008: return launch_leaf<16, 8>(g, d_feats, d_w, d_out, s);
     default: return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: leaf path shape");
+  }
+}
+
+bool wgrad_leaf_supported(int32_t cin, int32_t cout) {
+  switch (cin * 1000 + cout) {
+    case 4004: case 4008: case 4016: case 4032: case 8004: case 8008: case 8016: case 8032:
+    case 16004: case 16008: case 16016:
+      return true;
+    default:
+      return false;
+  }
+}
+
+int64_t wgrad_leaf_groups(const igc_grid* g) {
+  // About four workgroups per CU, each over a run of consecutive leaves; every group has at least
+  // one leaf.
+  const int64_t want = 1024;
+  if (g->n_leaf <= want) return g->n_leaf;
+  const int64_t lpg = (g->n_leaf + want - 1) / want;
+  return (g->n_leaf + lpg - 1) / lpg;
+}
+
+int launch_wgrad_leaf(const igc_grid* g, const void* d_feats, int32_t cin, const void* d_dout, int32_t cout,
+                      float* part, int64_t groups, hipStream_t s) {
+  switch (cin * 1000 + cout) {
+    case 4004: return launch_wgrad_leaf_t<4, 4>(g, d_feats, d_dout, part, groups, s);
+    case 4008: return launch_wgrad_leaf_t<4, 8>(g, d_feats, d_dout, part, groups, s);
+    case 4016: return launch_wgrad_leaf_t<4, 16>(g, d_feats, d_dout, part, groups, s);
+    case 4032: return launch_wgrad_leaf_t<4, 32>(g, d_feats, d_dout, part, groups, s);
+    case 8004: return launch_wgrad_leaf_t<8, 4>(g, d_feats, d_dout, part, groups, s);
+    case 8008: return launch_wgrad_leaf_t<8, 8>(g, d_feats, d_dout, part, groups, s);
+    case 8016: return launch_wgrad_leaf_t<8, 16>(g, d_feats, d_dout, part, groups, s);
+    case 8032: return launch_wgrad_leaf_t<8, 32>(g, d_feats, d_dout, part, groups, s);
+    case 16004: return launch_wgrad_leaf_t<16, 4>(g, d_feats, d_dout, part, groups, s);
+    case 16008: return launch_wgrad_leaf_t<16, 8>(g, d_feats, d_dout, part, groups, s);
+    case 16016: return launch_wgrad_leaf_t<16, 16>(g, d_feats, d_dout, part, groups, s);
+    default: return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv_backward: leaf weight-gradient shape");
   }
 }
 

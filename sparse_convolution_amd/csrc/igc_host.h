@@ -91,6 +91,11 @@ int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats
                     const void* d_w, int32_t cout, void* d_out, hipStream_t s);
 // Mask-sorted tiles of 256 output rows (row order perm, 16-row blocks with pairs per offset blk).
 int launch_ggs_plan(const int32_t* d_map, int64_t N, int32_t* perm, uint16_t* blk, hipStream_t s);
+// Leaf-local fp32 weight gradient: `groups` partial dW blocks [groups][27][cin][cout] in `part`.
+bool wgrad_leaf_supported(int32_t cin, int32_t cout);
+int64_t wgrad_leaf_groups(const igc_grid* g);
+int launch_wgrad_leaf(const igc_grid* g, const void* d_feats, int32_t cin, const void* d_dout, int32_t cout,
+                      float* part, int64_t groups, hipStream_t s);
 bool wgrad_supported(int32_t dtype, int32_t cin, int32_t cout);
 int launch_conv_backward(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype, int32_t cin,
                          const void* d_w, int32_t cout, const void* d_dout, void* d_dfeats, float* d_dw,

@@ -93,10 +93,17 @@ def test_bf16_weight_gradient_shapes(cin, cout):
                  need_dfeats=cin % 64 == 0)
 
 
-@pytest.mark.parametrize("cin,cout", [(4, 8), (4, 16), (8, 16), (8, 8), (16, 16)])
+@pytest.mark.parametrize("cin,cout", [(4, 8), (4, 16), (8, 16), (8, 8), (16, 16), (16, 8), (16, 4)])
 def test_fp32_leaf_shapes(cin, cout):
     c = _cluster_coords(6, 20, 200, seed=cin * 31 + cout)
     run_backward(c, cin, cout, torch.float32, "leaf", "clusters", seed=cin * 5 + cout)
+
+
+@pytest.mark.parametrize("cin,cout", [(4, 32), (8, 32), (4, 4), (8, 4)])
+def test_fp32_leaf_weight_gradient_only_shapes(cin, cout):
+    # The input gradient of these runs cout -> cin, not a leaf-path shape.
+    c = _cluster_coords(6, 20, 200, seed=cin * 37 + cout)
+    run_backward(c, cin, cout, torch.float32, "leaf", "clusters", seed=cin * 7 + cout, need_dfeats=False)
 
 
 def test_fp32_weight_gradient_odd_channels():
