@@ -17,18 +17,23 @@
 //     (12 bits) << 9 | leaf voxel (9 bits). The pass that writes key2 also builds the digit
 //     histograms of every radix pass, and only the bit span where keys differ is sorted
 //     (the OR and AND of all keys, taken in the tile pass, give that span).
-//  3. The sort is an LSD radix sort with 8-bit digits over tiles of 4096 keys. Each pass is
+//  3. Keys are sorted by their leaf part (key2 >> 9) only: the voxel bits inside a leaf are
+//     OR-ed into the leaf's mask, so their order never matters, and the sort needs
+//     ceil(varying leaf-key bits / 8) passes instead of ceil(varying key bits / 8). The sort
+//     is an LSD radix sort with 8-bit digits over tiles of 4096 keys. Each pass is
 //     reduce-then-scan: per-tile digit counts, a scan of every digit's counts over the tiles,
 //     and a scatter that ranks the tile's keys with 64-lane ballots (stable multisplit), sorts
 //     them in LDS and writes them out as runs per digit. A single-pass form with decoupled
 //     look-back was measured slower here: with all tiles resident at once, late tiles walk
 //     back over hundreds of predecessors that have published only their own counts.
-//  4. Unique voxels, leaves, lower and upper nodes are counted in one pass over the sorted
-//     keys (a key starts a voxel / leaf / lower / upper when key, key>>9, key>>21, key>>36
-//     differ from its predecessor); after the one read-back of the counts, a second pass
-//     gives every key its voxel / leaf / node rows from the scanned block counts and
-//     registers the nodes top-down. Leaf mask bits are OR-ed in (duplicates set the same
-//     bit), so no separate unique-compaction pass is needed.
+//  4. Leaves, lower and upper nodes are counted in one pass over the sorted keys (a key
+//     starts a leaf / lower / upper when key>>9, key>>21, key>>36 differ from its
+//     predecessor); after the read-back of the counts, a second pass gives every key its
+//     leaf / node rows from the scanned block counts and registers the nodes top-down. Leaf
+//     mask bits are OR-ed in (duplicates set the same bit), first in LDS per block of keys:
+//     leaves that lie inside the block are stored whole, the block's first and last leaf
+//     are OR-ed into memory. Unique voxels are then the masks' popcounts: a scan over the
+//     leaves gives every leaf its first row and the voxel count N (read back last).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -561,8 +566,10 @@ int radix_sort(uint64_t* a, uint64_t* b, int64_t n, PassSpec ps, const uint32_t*
   return IGC_OK;
 }
 
-PassSpec pass_spec(uint64_t varying) {
+// Digits over the varying bits at or above min_bit.
+PassSpec pass_spec(uint64_t varying, int min_bit = 0) {
   PassSpec ps{0, 0};
+  if (min_bit > 0) varying &= ~((1ull << min_bit) - 1ull);
   if (!varying) return ps;
   const int lo = __builtin_ctzll(varying);
   const int hi = 63 - __builtin_clzll(varying);
@@ -573,11 +580,12 @@ PassSpec pass_spec(uint64_t varying) {
 
 // ------------------------------------------------------------------------------ counting
 
-// Block b counts, among keys [b*4096, (b+1)*4096), those that start a new voxel, leaf, lower
-// node and upper node. Counts are packed in 16-bit fields of one 64-bit word.
+// Block b counts, among keys [b*4096, (b+1)*4096), those that start a new leaf, lower node
+// and upper node. Counts are packed in 16-bit fields 1..3 of one 64-bit word (field 0, the
+// voxels, is counted from the leaf masks after registration).
 __device__ __forceinline__ uint64_t start_flags(uint64_t key, uint64_t prev, bool first) {
-  if (first) return 0x0001000100010001ull;
-  return (uint64_t)(key != prev) | ((uint64_t)((key >> 9) != (prev >> 9)) << 16) |
+  if (first) return 0x0001000100010000ull;
+  return ((uint64_t)((key >> 9) != (prev >> 9)) << 16) |
          ((uint64_t)((key >> 21) != (prev >> 21)) << 32) | ((uint64_t)((key >> 36) != (prev >> 36)) << 48);
 }
 
@@ -609,8 +617,8 @@ __global__ __launch_bounds__(256) void k_count(const uint64_t* __restrict__ keys
   if (threadIdx.x == 0) block_counts[blockIdx.x] = total;
 }
 
-// Exclusive scan of the per-block packed counts into four 64-bit prefixes per block, and the
-// totals N, F, Lw, U. One workgroup.
+// Exclusive scan of the per-block packed counts into 64-bit prefixes per block (fields 1..3
+// of four), and the totals F, Lw, U. One workgroup.
 __global__ __launch_bounds__(1024) void k_scan_blocks(const uint64_t* __restrict__ block_counts, int64_t nb,
                                                       uint64_t* __restrict__ prefix, BuildState* st) {
   __shared__ uint64_t s_tmp[16];
@@ -618,22 +626,22 @@ __global__ __launch_bounds__(1024) void k_scan_blocks(const uint64_t* __restrict
   const int64_t b0 = threadIdx.x * per;
   uint64_t run[4] = {0, 0, 0, 0};
   for (int64_t b = b0; b < b0 + per && b < nb; ++b)
-    for (int c = 0; c < 4; ++c) run[c] += (block_counts[b] >> (16 * c)) & 0xFFFFull;
-  uint64_t excl[4], tot[4];
-  for (int c = 0; c < 4; ++c) excl[c] = block_excl_scan64<1024>(run[c], s_tmp, &tot[c]);
+    for (int c = 1; c < 4; ++c) run[c] += (block_counts[b] >> (16 * c)) & 0xFFFFull;
+  uint64_t excl[4] = {0, 0, 0, 0}, tot[4] = {0, 0, 0, 0};
+  for (int c = 1; c < 4; ++c) excl[c] = block_excl_scan64<1024>(run[c], s_tmp, &tot[c]);
   for (int64_t b = b0; b < b0 + per && b < nb; ++b)
     for (int c = 0; c < 4; ++c) {
       prefix[b * 4 + c] = excl[c];
       excl[c] += (block_counts[b] >> (16 * c)) & 0xFFFFull;
     }
   if (threadIdx.x == 0)
-    for (int c = 0; c < 4; ++c) st->counts[c] = tot[c];
+    for (int c = 1; c < 4; ++c) st->counts[c] = tot[c];
 }
 
 // ------------------------------------------------------------------------------ registration
 
 struct Topo {
-  int64_t n_voxels, n_leaf, n_lower, n_upper;  // allocation sizes (bounds checks)
+  int64_t n_leaf, n_lower, n_upper;  // allocation sizes (bounds checks)
   uint32_t* guard;
   const uint64_t* tiles;  // [U] tile keys in rank order
   uint64_t* root_list;
@@ -659,11 +667,15 @@ __device__ __forceinline__ int4 key_origin(uint64_t key, uint64_t tile, uint32_t
   return make_int4((int32_t)(i & m), (int32_t)(j & m), (int32_t)(k & m), 0);
 }
 
+constexpr int kLeafCache = 64;  // leaves of a block whose masks are merged in LDS
+
 __global__ __launch_bounds__(256) void k_register(const uint64_t* __restrict__ keys, int64_t n,
                                                   const uint64_t* __restrict__ prefix, Topo t) {
   __shared__ uint64_t s_keys[kTileKeys];
   __shared__ uint64_t s_prev;
   __shared__ uint64_t s_tmp[4];
+  __shared__ uint64_t s_lmask[kLeafCache][8];
+  for (int x = threadIdx.x; x < kLeafCache * 8; x += kThreads) (&s_lmask[0][0])[x] = 0;
   const int64_t base = (int64_t)blockIdx.x * kTileKeys;
   stage_block(keys, n, base, s_keys, &s_prev);
   const int p0 = threadIdx.x * kKeysPerThread;
@@ -672,26 +684,30 @@ __global__ __launch_bounds__(256) void k_register(const uint64_t* __restrict__ k
     const int64_t e = base + p0 + q;
     if (e < n) c += start_flags(s_keys[p0 + q], (p0 + q) ? s_keys[p0 + q - 1] : s_prev, e == 0);
   }
-  const uint64_t excl = block_excl_scan64<kThreads>(c, s_tmp, nullptr);
+  uint64_t total;
+  const uint64_t excl = block_excl_scan64<kThreads>(c, s_tmp, &total);
   // Running inclusive counts; ids are count - 1.
-  int64_t nv = (int64_t)prefix[blockIdx.x * 4 + 0] + (int64_t)(excl & 0xFFFF);
-  int64_t nf = (int64_t)prefix[blockIdx.x * 4 + 1] + (int64_t)((excl >> 16) & 0xFFFF);
+  const int64_t pf = (int64_t)prefix[blockIdx.x * 4 + 1];
+  int64_t nf = pf + (int64_t)((excl >> 16) & 0xFFFF);
   int64_t nl = (int64_t)prefix[blockIdx.x * 4 + 2] + (int64_t)((excl >> 32) & 0xFFFF);
   int64_t nu = (int64_t)prefix[blockIdx.x * 4 + 3] + (int64_t)((excl >> 48) & 0xFFFF);
+  // Leaves of the block's first and last key; the leaves between them lie inside the block.
+  const bool first_starts = base == 0 || (s_keys[0] >> 9) != (s_prev >> 9);
+  const int64_t lf0 = pf + (first_starts ? 1 : 0) - 1;
+  const int64_t lf1 = pf + (int64_t)((total >> 16) & 0xFFFF) - 1;
 
-  int64_t run_word = -1;  // leaf * 8 + word of the pending mask bits
+  int64_t run_word = -1;  // leaf * 8 + word of the pending mask bits (leaves past the LDS cache)
   uint64_t run_bits = 0;
   for (int q = 0; q < kKeysPerThread; ++q) {
     const int64_t e = base + p0 + q;
     if (e >= n) break;
     const uint64_t key = s_keys[p0 + q];
     const uint64_t f = start_flags(key, (p0 + q) ? s_keys[p0 + q - 1] : s_prev, e == 0);
-    nv += (int64_t)(f & 1);
     nf += (int64_t)((f >> 16) & 1);
     nl += (int64_t)((f >> 32) & 1);
     nu += (int64_t)((f >> 48) & 1);
-    const int64_t v = nv - 1, lf = nf - 1, lw = nl - 1, u = nu - 1;
-    if (v >= t.n_voxels || lf >= t.n_leaf || lw >= t.n_lower || u >= t.n_upper || (int64_t)(key >> 36) >= t.n_upper) {
+    const int64_t lf = nf - 1, lw = nl - 1, u = nu - 1;
+    if (lf < lf0 || lf >= t.n_leaf || lw >= t.n_lower || u >= t.n_upper || (int64_t)(key >> 36) >= t.n_upper) {
       atomicOr(t.guard, 1u);
       break;
     }
@@ -710,10 +726,13 @@ __global__ __launch_bounds__(256) void k_register(const uint64_t* __restrict__ k
     if ((f >> 16) & 1) {
       const uint32_t cl = (uint32_t)(key >> 9) & 0xFFFu;
       atomicOr((unsigned long long*)&t.lower_mask[lw * 64 + (cl >> 6)], 1ull << (cl & 63u));
-      t.leaf[lf].offset = (uint64_t)v;
       t.leaf_origin[lf] = key_origin(key, tile, 3);
     }
     const uint32_t vox = (uint32_t)key & 511u;
+    if (lf - lf0 < kLeafCache) {
+      atomicOr((unsigned long long*)&s_lmask[lf - lf0][vox >> 6], 1ull << (vox & 63u));
+      continue;
+    }
     const int64_t word = lf * 8 + (vox >> 6);
     if (word != run_word) {
       if (run_word >= 0) atomicOr((unsigned long long*)&t.leaf[run_word >> 3].mask[run_word & 7], run_bits);
@@ -723,18 +742,86 @@ __global__ __launch_bounds__(256) void k_register(const uint64_t* __restrict__ k
     run_bits |= 1ull << (vox & 63u);
   }
   if (run_word >= 0) atomicOr((unsigned long long*)&t.leaf[run_word >> 3].mask[run_word & 7], run_bits);
+  __syncthreads();
+  // The block owns the masks of its inner leaves whole; its first and last leaf may have keys
+  // in the neighbouring blocks.
+  const int64_t nloc = lf1 - lf0 + 1 < kLeafCache ? lf1 - lf0 + 1 : kLeafCache;
+  for (int x = threadIdx.x; x < nloc * 8; x += kThreads) {
+    const int slot = x >> 3, w = x & 7;
+    const int64_t lf = lf0 + slot;
+    if (lf < 0 || lf >= t.n_leaf) {
+      atomicOr(t.guard, 1u);
+      continue;
+    }
+    const uint64_t v = s_lmask[slot][w];
+    if (slot == 0 || lf == lf1) {
+      if (v) atomicOr((unsigned long long*)&t.leaf[lf].mask[w], v);
+    } else {
+      t.leaf[lf].mask[w] = v;
+    }
+  }
 }
 
-// Packed 9-bit prefix counts of every leaf.
-__global__ void k_leaf_prefix(LeafRec* __restrict__ leaf, int64_t F) {
-  for (int64_t f = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; f < F; f += (int64_t)gridDim.x * blockDim.x) {
-    uint64_t packed = 0, run = 0;
-    for (int w = 1; w < 8; ++w) {
-      run += (uint64_t)__popcll(leaf[f].mask[w - 1]);
-      packed |= run << (9 * (w - 1));
+// Voxel rows of the leaves: per leaf the packed 9-bit prefix counts of its mask words and its
+// popcount; the exclusive voxel count of the leaf within its group of kLeafGroup leaves goes
+// to offset, the group's total to group_sum (a scan over the groups and k_leaf_offset finish
+// the rows).
+constexpr int kLeafPer = 4;                       // leaves per thread
+constexpr int kLeafGroup = 256 * kLeafPer;        // leaves per workgroup
+__global__ __launch_bounds__(256) void k_leaf_count(LeafRec* __restrict__ leaf, int64_t F,
+                                                    uint64_t* __restrict__ group_sum) {
+  __shared__ uint64_t s_tmp[4];
+  const int64_t f0 = (int64_t)blockIdx.x * kLeafGroup + (int64_t)threadIdx.x * kLeafPer;
+  uint32_t cnt[kLeafPer];
+  uint64_t tsum = 0;
+#pragma unroll
+  for (int q = 0; q < kLeafPer; ++q) {
+    const int64_t f = f0 + q;
+    cnt[q] = 0;
+    if (f < F) {
+      uint64_t packed = 0, run = 0;
+      for (int w = 0; w < 8; ++w) {
+        if (w) packed |= run << (9 * (w - 1));
+        run += (uint64_t)__popcll(leaf[f].mask[w]);
+      }
+      leaf[f].prefix = packed;
+      cnt[q] = (uint32_t)run;
     }
-    leaf[f].prefix = packed;
+    tsum += cnt[q];
   }
+  uint64_t total;
+  uint64_t run = block_excl_scan64<256>(tsum, s_tmp, &total);
+#pragma unroll
+  for (int q = 0; q < kLeafPer; ++q) {
+    const int64_t f = f0 + q;
+    if (f < F) leaf[f].offset = run;
+    run += cnt[q];
+  }
+  if (threadIdx.x == 0) group_sum[blockIdx.x] = total;
+}
+
+// In-place exclusive scan of v[0..nb); the total is the voxel count N. One workgroup.
+__global__ __launch_bounds__(1024) void k_scan_groups(uint64_t* __restrict__ v, int64_t nb, BuildState* st) {
+  __shared__ uint64_t s_tmp[16];
+  uint64_t carry = 0;
+  for (int64_t b0 = 0; b0 < nb; b0 += 1024) {
+    const int64_t b = b0 + threadIdx.x;
+    const uint64_t x = b < nb ? v[b] : 0ull;
+    uint64_t tot;
+    const uint64_t ex = block_excl_scan64<1024>(x, s_tmp, &tot);
+    if (b < nb) v[b] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) st->counts[0] = carry;
+}
+
+__global__ __launch_bounds__(256) void k_leaf_offset(LeafRec* __restrict__ leaf, int64_t F,
+                                                     const uint64_t* __restrict__ group_pre) {
+  const uint64_t add = group_pre[blockIdx.x];
+  const int64_t f0 = (int64_t)blockIdx.x * kLeafGroup + (int64_t)threadIdx.x * kLeafPer;
+#pragma unroll
+  for (int q = 0; q < kLeafPer; ++q)
+    if (f0 + q < F) leaf[f0 + q].offset += add;
 }
 
 // Per-word prefix counts of internal-node child masks: one wave per node.
@@ -914,7 +1001,7 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   int rank_bits = 0;
   while ((1ll << rank_bits) < U) ++rank_bits;
   const uint64_t varying = off_var | (rank_bits ? (((1ull << rank_bits) - 1ull) << 36) : 0ull);
-  const PassSpec ps = pass_spec(varying);
+  const PassSpec ps = pass_spec(varying, 9);  // leaf part of key2 only
   const int nbk = grid_for((n_in + 3) / 4, 256, kHistBlocks);
   k_key2<<<nbk, 256, 0, s>>>(d_ijk, n_in, root_keys, root_vals, (uint32_t)(cap - 1), tiles_sorted, U, ka, ps, hpart,
                              st);
@@ -935,8 +1022,8 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   IGC_HIP(hipMemcpyAsync(h, st, sizeof(BuildState), hipMemcpyDeviceToHost, s), "igc_grid_build: read counts");
   IGC_HIP(hipStreamSynchronize(s), "igc_grid_build: sort and count");
   if (h->guard) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: device bounds check failed before registration");
-  const int64_t N = (int64_t)h->counts[0], F = (int64_t)h->counts[1], Lw = (int64_t)h->counts[2];
-  if ((int64_t)h->counts[3] != U || N < 1 || N > n_in || F > N || Lw > F)
+  const int64_t F = (int64_t)h->counts[1], Lw = (int64_t)h->counts[2];
+  if ((int64_t)h->counts[3] != U || F < 1 || F > n_in || Lw > F)
     return set_error(IGC_ERR_INTERNAL, "igc_grid_build: inconsistent node counts");
 
   // Topology block (zeroed with one fill: masks start empty).
@@ -966,26 +1053,41 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   g->leaf = (LeafRec*)(blk + o_leaf);
   g->leaf_origin = (int4*)(blk + o_lfo);
   g->leaf_nbr = (int32_t*)(blk + o_nbr);
-  g->n_voxels = N;
   g->n_leaf = F;
   g->n_lower = Lw;
   g->n_upper = U;
   g->sort_passes = ps.passes;
   if ((rc = fill_u64((uint64_t*)blk, (int64_t)(zero_end / 8), 0, s))) return rc;
 
-  Topo t{N,           F,           Lw,           U,          &st->guard,     tiles_sorted,
+  Topo t{F,           Lw,           U,          &st->guard,     tiles_sorted,
          g->root_list, g->upper_origin, g->upper_mask, g->upper_first, g->lower_origin, g->lower_mask,
          g->lower_first, g->leaf,     g->leaf_origin};
   k_register<<<(unsigned)nb, kThreads, 0, s>>>(sorted, n_in, bprefix, t);
   IGC_HIP(hipGetLastError(), "igc_grid_build: register launch");
-  k_leaf_prefix<<<grid_for(F, 256, 4096), 256, 0, s>>>(g->leaf, F);
-  IGC_HIP(hipGetLastError(), "igc_grid_build: leaf prefix launch");
+  const int64_t groups = (F + kLeafGroup - 1) / kLeafGroup;
+  uint64_t* gsum = bprefix;  // the block prefixes are consumed by the register pass
+  if ((size_t)groups * 8 > (size_t)tiles * 32) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: leaf scan workspace");
+  k_leaf_count<<<(unsigned)groups, 256, 0, s>>>(g->leaf, F, gsum);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: leaf count launch");
+  k_scan_groups<<<1, 1024, 0, s>>>(gsum, groups, st);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: leaf scan launch");
+  if (groups > 1) {
+    k_leaf_offset<<<(unsigned)groups, 256, 0, s>>>(g->leaf, F, gsum);
+    IGC_HIP(hipGetLastError(), "igc_grid_build: leaf offset launch");
+  }
   k_node_prefix<<<(unsigned)((Lw + 3) / 4), 256, 0, s>>>(g->lower_mask, g->lower_pre, Lw, 64);
   IGC_HIP(hipGetLastError(), "igc_grid_build: lower prefix launch");
   k_node_prefix<<<(unsigned)((U + 3) / 4), 256, 0, s>>>(g->upper_mask, g->upper_pre, U, 512);
   IGC_HIP(hipGetLastError(), "igc_grid_build: upper prefix launch");
   k_leaf_neighbors<<<grid_for(F * 27, 256, 8192), 256, 0, s>>>(g->view(), g->leaf_nbr);
   IGC_HIP(hipGetLastError(), "igc_grid_build: leaf neighbour launch");
+  // Last read-back: the voxel count.
+  IGC_HIP(hipMemcpyAsync(h, st, sizeof(BuildState), hipMemcpyDeviceToHost, s), "igc_grid_build: read voxel count");
+  IGC_HIP(hipStreamSynchronize(s), "igc_grid_build: registration");
+  if (h->guard) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: device bounds check failed in registration");
+  const int64_t N = (int64_t)h->counts[0];
+  if (N < F || N > n_in) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: inconsistent voxel count");
+  g->n_voxels = N;
   return IGC_OK;
 }
 
