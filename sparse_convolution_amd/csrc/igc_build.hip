@@ -165,11 +165,25 @@ __global__ __launch_bounds__(256) void k_tile_insert(const int32_t* __restrict__
         key_or |= key;
         key_and &= key;
       }
-      uint64_t pending = __ballot(valid);
+      // Keys already in the workgroup's cache need nothing more: each lane looks its own up
+      // with plain LDS reads, and only the rest go through the per-key leader rounds.
+      bool need = valid;
+      if (valid) {
+        const uint32_t h = hash_tile(key) & (kTileCache - 1);
+        for (int p = 0; p < 8; ++p) {
+          const uint64_t v = s_set[(h + p) & (kTileCache - 1)];
+          if (v == key) {
+            need = false;
+            break;
+          }
+          if (v == kEmptyKey) break;
+        }
+      }
+      uint64_t pending = __ballot(need);
       while (pending) {
         const int leader = __ffsll((unsigned long long)pending) - 1;
         const uint64_t lk = shfl64(key, leader);
-        const uint64_t same = __ballot(valid && key == lk);
+        const uint64_t same = __ballot(need && key == lk);
         if (lane == leader) {
           const uint32_t h = hash_tile(lk) & (kTileCache - 1);
           bool placed = false;
