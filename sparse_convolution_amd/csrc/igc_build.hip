@@ -54,6 +54,9 @@ constexpr int kTileKeys = kThreads * kKeysPerThread;  // 4096 keys per counting 
 constexpr int kSortKPT = 16;                           // keys per thread of a radix pass
 constexpr int kSortTile = kThreads * kSortKPT;         // keys per onesweep tile
 constexpr int kMaxPasses = 8;
+constexpr int kMaxDigitBits = 9;                       // digits of 8 or 9 bits (wider ones measured slower)
+constexpr int kMaxBins = 1 << kMaxDigitBits;
+constexpr int kHistWidth = 4096;                       // passes * bins of the LDS histograms
 constexpr int kSmallSort = 4096;             // tile-key sorts up to this size run in one workgroup
 constexpr int kTileCache = 64;               // per-workgroup LDS cache of tiles already in the table
 constexpr int kRootInLds = 512;              // root tables up to this capacity are copied to LDS
@@ -326,44 +329,74 @@ __global__ void k_tile_rank(const uint64_t* __restrict__ sorted, int64_t U, cons
 
 struct PassSpec {
   int lo_bit;  // bit of digit 0
-  int passes;  // digits of 8 bits
+  int passes;  // number of digits
+  int bits;    // bits per digit, 8..10 (digit p is bits [lo_bit + bits p, lo_bit + bits (p + 1)))
 };
 
-// Per-wave LDS histograms of every pass digit, merged into the global histograms.
+// The varying bits of the keys' leaf part (key2 >> 9) as runs of consecutive bits: the sort
+// orders keys compacted to those bits ((leaf part gathered to the low bits) << 9 | voxel bits),
+// which keeps their order and takes fewer digits; the last pass writes them expanded again.
+struct BitRuns {
+  int n;                             // 0: keys are sorted as they are
+  uint8_t lo[16], len[16], pos[16];  // run i: bits [lo, lo + len) of the leaf part -> [pos, pos + len)
+  uint64_t cbits;                    // bits of the leaf part that are the same in every key
+};
+
+__device__ __forceinline__ uint64_t runs_compress(uint64_t key, const BitRuns& r) {
+  const uint64_t x = key >> 9;
+  uint64_t c = 0;
+  for (int i = 0; i < r.n; ++i) c |= ((x >> r.lo[i]) & ((1ull << r.len[i]) - 1ull)) << r.pos[i];
+  return (c << 9) | (key & 511u);
+}
+
+__device__ __forceinline__ uint64_t runs_expand(uint64_t sk, const BitRuns& r) {
+  const uint64_t c = sk >> 9;
+  uint64_t x = r.cbits;
+  for (int i = 0; i < r.n; ++i) x |= ((c >> r.pos[i]) & ((1ull << r.len[i]) - 1ull)) << r.lo[i];
+  return (x << 9) | (sk & 511u);
+}
+
+// LDS histograms of every pass digit (one copy per workgroup), merged into the global ones.
 __device__ __forceinline__ void hist_add(uint32_t* s_hist, uint64_t key, PassSpec ps) {
+  const uint32_t bins = 1u << ps.bits;
   for (int p = 0; p < ps.passes; ++p) {
-    const uint32_t d = (uint32_t)(key >> (ps.lo_bit + 8 * p)) & 255u;
-    atomicAdd(&s_hist[p * 256 + d], 1u);
+    const uint32_t d = (uint32_t)(key >> (ps.lo_bit + ps.bits * p)) & (bins - 1u);
+    atomicAdd(&s_hist[p * bins + d], 1u);
   }
 }
 
-// Writes this workgroup's histograms to its row of `part` ([blocks][passes*256]).
-__device__ __forceinline__ void hist_flush(uint32_t (*s_hist)[kMaxPasses * 256], uint32_t* part, PassSpec ps) {
+// Writes this workgroup's histograms to its row of `part` ([blocks][passes * bins]).
+__device__ __forceinline__ void hist_flush(const uint32_t* s_hist, uint32_t* part, PassSpec ps) {
   __syncthreads();
-  uint32_t* row = part + (size_t)blockIdx.x * ps.passes * 256;
-  for (int x = threadIdx.x; x < ps.passes * 256; x += blockDim.x)
-    row[x] = s_hist[0][x] + s_hist[1][x] + s_hist[2][x] + s_hist[3][x];
+  const int width = ps.passes << ps.bits;
+  uint32_t* row = part + (size_t)blockIdx.x * width;
+  for (int x = threadIdx.x; x < width; x += blockDim.x) row[x] = s_hist[x];
 }
 
-// hist[x] = sum over workgroups b of part[b][x]. A workgroup owns 64 columns; its four waves
-// sum interleaved row slices with four loads in flight each, then combine in LDS.
+// hist[x] = sum over workgroups b of part[b][x]. A workgroup owns 16 columns; its 16 row
+// slices of 16 threads sum interleaved rows, then combine in LDS.
 __global__ __launch_bounds__(256) void k_hist_reduce(const uint32_t* __restrict__ part, int nb, int width,
                                                      uint32_t* __restrict__ hist) {
-  __shared__ uint32_t s_sum[4][64];
-  const int col = blockIdx.x * 64 + lane_id();
-  const int slice = threadIdx.x >> 6;
+  __shared__ uint32_t s_sum[16][16];
+  const int cl = threadIdx.x & 15, slice = threadIdx.x >> 4;
+  const int col = blockIdx.x * 16 + cl;
   uint32_t acc[4] = {0, 0, 0, 0};
   if (col < width) {
     int b = slice;
-    for (; b + 12 < nb; b += 16) {
+    for (; b + 48 < nb; b += 64) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] += part[(size_t)(b + 4 * u) * width + col];
+      for (int u = 0; u < 4; ++u) acc[u] += part[(size_t)(b + 16 * u) * width + col];
     }
-    for (; b < nb; b += 4) acc[0] += part[(size_t)b * width + col];
+    for (; b < nb; b += 16) acc[0] += part[(size_t)b * width + col];
   }
-  s_sum[slice][lane_id()] = acc[0] + acc[1] + acc[2] + acc[3];
+  s_sum[slice][cl] = acc[0] + acc[1] + acc[2] + acc[3];
   __syncthreads();
-  if (slice == 0 && col < width) hist[col] = s_sum[0][lane_id()] + s_sum[1][lane_id()] + s_sum[2][lane_id()] + s_sum[3][lane_id()];
+  if (slice == 0 && col < width) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t += s_sum[k][cl];
+    hist[col] = t;
+  }
 }
 
 // key2 for every coordinate, plus the digit histograms of every sort pass. When there are at
@@ -373,11 +406,11 @@ __global__ __launch_bounds__(256) void k_key2(const int32_t* __restrict__ ijk, i
                                               const uint64_t* __restrict__ root_keys,
                                               const int32_t* __restrict__ root_vals, uint32_t mask,
                                               const uint64_t* __restrict__ tiles, int64_t U,
-                                              uint64_t* __restrict__ out, PassSpec ps, uint32_t* __restrict__ hist,
-                                              BuildState* st) {
-  __shared__ uint32_t s_hist[4][kMaxPasses * 256];
+                                              uint64_t* __restrict__ out, PassSpec ps, BitRuns runs,
+                                              uint32_t* __restrict__ hist, BuildState* st) {
+  __shared__ uint32_t s_hist[kHistWidth];
   __shared__ uint64_t s_tiles[kRootInLds];
-  for (int x = threadIdx.x; x < 4 * kMaxPasses * 256; x += blockDim.x) (&s_hist[0][0])[x] = 0;
+  for (int x = threadIdx.x; x < (ps.passes << ps.bits); x += blockDim.x) s_hist[x] = 0;
   const bool local = U <= kRootInLds;
   if (local)
     for (int x = threadIdx.x; x < U; x += blockDim.x) s_tiles[x] = tiles[x];
@@ -412,9 +445,10 @@ __global__ __launch_bounds__(256) void k_key2(const int32_t* __restrict__ ijk, i
       const int64_t s = probe_slot(root_keys, mask, tk, st);
       rank = s >= 0 ? (uint64_t)(uint32_t)root_vals[s] : 0ull;
     }
-    const uint64_t key = (rank << 36) | tile_offset(i, j, k);
+    uint64_t key = (rank << 36) | tile_offset(i, j, k);
+    if (runs.n) key = runs_compress(key, runs);
     out[e] = key;
-    hist_add(s_hist[wave], key, ps);
+    hist_add(s_hist, key, ps);
    }
   }
   hist_flush(s_hist, hist, ps);
@@ -423,24 +457,24 @@ __global__ __launch_bounds__(256) void k_key2(const int32_t* __restrict__ ijk, i
 // Digit histograms of an existing key array (used for the tile-key sort when U is large).
 __global__ __launch_bounds__(256) void k_hist(const uint64_t* __restrict__ keys, int64_t n, PassSpec ps,
                                               uint32_t* __restrict__ hist) {
-  __shared__ uint32_t s_hist[4][kMaxPasses * 256];
-  for (int x = threadIdx.x; x < 4 * kMaxPasses * 256; x += blockDim.x) (&s_hist[0][0])[x] = 0;
+  __shared__ uint32_t s_hist[kHistWidth];
+  for (int x = threadIdx.x; x < (ps.passes << ps.bits); x += blockDim.x) s_hist[x] = 0;
   __syncthreads();
-  const int wave = threadIdx.x >> 6;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x)
-    hist_add(s_hist[wave], keys[e], ps);
+    hist_add(s_hist, keys[e], ps);
   hist_flush(s_hist, hist, ps);
 }
 
-// One LSD pass over the 8-bit digit at `shift` runs as three kernels over tiles of kSortTile
-// keys (reduce-then-scan): per-tile digit counts, a scan of every digit's counts over the
-// tiles, and a stable scatter that ranks the tile's keys with 64-lane ballots, sorts them in
-// LDS and writes them out in per-digit runs.
+// One LSD pass over the BITS-bit digit at `shift` runs as three kernels over tiles of
+// kSortTile keys (reduce-then-scan): per-tile digit counts, a scan of every digit's counts
+// over the tiles, and a stable scatter that ranks the tile's keys with 64-lane ballots, sorts
+// them in LDS and writes them out in per-digit runs.
 
 // Stable rank of every key among the equal digits of its wave (wave w owns the tile's keys
 // [w*64*kSortKPT, (w+1)*64*kSortKPT), 64 consecutive keys per round): the lanes holding the
-// same digit are found with 8 ballots, and the first of them adds their number to the
+// same digit are found with BITS ballots, and the first of them adds their number to the
 // wave's count of that digit, so no two lanes update one counter in the same round.
+template <int BITS>
 __device__ __forceinline__ void rank_keys(const uint64_t* __restrict__ src, int64_t n, int64_t wbase, int shift,
                                           uint64_t* key, uint32_t* rank, uint32_t* cnt) {
   const int lane = lane_id();
@@ -450,10 +484,10 @@ __device__ __forceinline__ void rank_keys(const uint64_t* __restrict__ src, int6
 #pragma unroll
   for (int r = 0; r < kSortKPT; ++r) {
     const bool valid = wbase + r * 64 < n;
-    const uint32_t d = (uint32_t)(key[r] >> shift) & 255u;
+    const uint32_t d = (uint32_t)(key[r] >> shift) & ((1u << BITS) - 1u);
     uint64_t m = __ballot(valid);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
+    for (int b = 0; b < BITS; ++b) {
       const bool set = (d >> b) & 1u;
       const uint64_t bb = __ballot(set);
       m &= set ? bb : ~bb;
@@ -467,18 +501,20 @@ __device__ __forceinline__ void rank_keys(const uint64_t* __restrict__ src, int6
 }
 
 // Step 1: cnt[d * T + tile] = keys of the tile with digit d.
+template <int BITS>
 __global__ __launch_bounds__(kThreads) void k_radix_hist(const uint64_t* __restrict__ src, int64_t n, int shift,
                                                          uint32_t* __restrict__ cnt, int64_t T) {
-  __shared__ uint32_t s_cnt[4][256];
+  constexpr int D = 1 << BITS;
+  __shared__ uint32_t s_cnt[4][D];
   const int tid = threadIdx.x, wave = tid >> 6;
-  for (int x = tid; x < 4 * 256; x += kThreads) (&s_cnt[0][0])[x] = 0;
+  for (int x = tid; x < 4 * D; x += kThreads) (&s_cnt[0][0])[x] = 0;
   __syncthreads();
   const int64_t tile = blockIdx.x;
   uint64_t key[kSortKPT];
   uint32_t rank[kSortKPT];
-  rank_keys(src, n, tile * kSortTile + wave * (64 * kSortKPT) + lane_id(), shift, key, rank, s_cnt[wave]);
+  rank_keys<BITS>(src, n, tile * kSortTile + wave * (64 * kSortKPT) + lane_id(), shift, key, rank, s_cnt[wave]);
   __syncthreads();
-  cnt[(int64_t)tid * T + tile] = s_cnt[0][tid] + s_cnt[1][tid] + s_cnt[2][tid] + s_cnt[3][tid];
+  for (int d = tid; d < D; d += kThreads) cnt[(int64_t)d * T + tile] = s_cnt[0][d] + s_cnt[1][d] + s_cnt[2][d] + s_cnt[3][d];
 }
 
 // Step 2, one workgroup per digit d: off[d * T + t] = (keys whose digit is below d) +
@@ -487,8 +523,10 @@ __global__ __launch_bounds__(kThreads) void k_radix_scan(const uint32_t* __restr
                                                          const uint32_t* __restrict__ hist, uint32_t* __restrict__ off) {
   __shared__ uint64_t s_tmp[kThreads / 64];
   const int d = blockIdx.x, tid = threadIdx.x;
+  uint64_t below = 0;
+  for (int x = tid; x < d; x += kThreads) below += hist[x];
   uint64_t carry = 0;
-  block_excl_scan64<kThreads>(tid < d ? (uint64_t)hist[tid] : 0ull, s_tmp, &carry);
+  block_excl_scan64<kThreads>(below, s_tmp, &carry);
   for (int64_t b = 0; b < T; b += kThreads) {
     const int64_t t = b + tid;
     const uint64_t c = t < T ? (uint64_t)cnt[(int64_t)d * T + t] : 0ull;
@@ -499,47 +537,64 @@ __global__ __launch_bounds__(kThreads) void k_radix_scan(const uint32_t* __restr
   }
 }
 
-// Step 3: stable scatter of one tile to its digits' runs.
+// Step 3: stable scatter of one tile to its digits' runs. Thread tid owns the J consecutive
+// digits [tid J, tid J + J).
+template <int BITS>
 __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint64_t* __restrict__ src,
                                                             uint64_t* __restrict__ dst, int64_t n, int shift,
                                                             const uint32_t* __restrict__ off, int64_t T,
-                                                            uint32_t* guard) {
+                                                            uint32_t* guard, const BitRuns runs) {
+  constexpr int D = 1 << BITS, J = D / kThreads;
   __shared__ uint64_t s_keys[kSortTile];
-  __shared__ uint32_t s_cnt[4][256];
-  __shared__ uint32_t s_tile_start[256];
-  __shared__ int64_t s_base[256];
+  __shared__ uint32_t s_cnt[4][D];
+  __shared__ uint32_t s_tile_start[D];
+  __shared__ int64_t s_base[D];
   __shared__ uint64_t s_tmp[kThreads / 64];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int64_t tile = blockIdx.x;
   const int64_t tile_base = tile * kSortTile;
-  const uint32_t goff = off[(int64_t)tid * T + tile];  // in flight during the ranking
-  for (int x = tid; x < 4 * 256; x += kThreads) (&s_cnt[0][0])[x] = 0;
+  uint32_t goff[J];  // in flight during the ranking
+#pragma unroll
+  for (int j = 0; j < J; ++j) goff[j] = off[(int64_t)(tid * J + j) * T + tile];
+  for (int x = tid; x < 4 * D; x += kThreads) (&s_cnt[0][0])[x] = 0;
   __syncthreads();
   uint64_t key[kSortKPT];
   uint32_t rank[kSortKPT];
   const int64_t wbase = tile_base + wave * (64 * kSortKPT) + lane_id();
-  rank_keys(src, n, wbase, shift, key, rank, s_cnt[wave]);
+  rank_keys<BITS>(src, n, wbase, shift, key, rank, s_cnt[wave]);
   __syncthreads();
 
-  // Thread tid owns digit tid: tile count, per-wave exclusive offsets and the tile scan.
-  const uint32_t d = (uint32_t)tid;
-  const uint32_t c0 = s_cnt[0][d], c1 = s_cnt[1][d], c2 = s_cnt[2][d], c3 = s_cnt[3][d];
-  const uint32_t tstart = (uint32_t)block_excl_scan64<kThreads>(c0 + c1 + c2 + c3, s_tmp, nullptr);
-  s_cnt[0][d] = 0;
-  s_cnt[1][d] = c0;
-  s_cnt[2][d] = c0 + c1;
-  s_cnt[3][d] = c0 + c1 + c2;
-  s_tile_start[d] = tstart;
-  s_base[d] = (int64_t)goff - (int64_t)tstart;
+  // Tile counts of the owned digits, per-wave exclusive offsets and the tile scan.
+  uint32_t c[J][4], tot[J], mine = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int d = tid * J + j;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) c[j][w] = s_cnt[w][d];
+    tot[j] = c[j][0] + c[j][1] + c[j][2] + c[j][3];
+    mine += tot[j];
+  }
+  uint32_t tstart = (uint32_t)block_excl_scan64<kThreads>(mine, s_tmp, nullptr);
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int d = tid * J + j;
+    s_cnt[0][d] = 0;
+    s_cnt[1][d] = c[j][0];
+    s_cnt[2][d] = c[j][0] + c[j][1];
+    s_cnt[3][d] = c[j][0] + c[j][1] + c[j][2];
+    s_tile_start[d] = tstart;
+    s_base[d] = (int64_t)goff[j] - (int64_t)tstart;
+    tstart += tot[j];
+  }
   __syncthreads();
 
   // Digit-sorted order inside the tile, staged in LDS, then written out in per-digit runs.
 #pragma unroll
   for (int r = 0; r < kSortKPT; ++r) {
     if (wbase + r * 64 < n) {
-      const uint32_t dd = (uint32_t)(key[r] >> shift) & 255u;
+      const uint32_t dd = (uint32_t)(key[r] >> shift) & (D - 1u);
       s_keys[s_tile_start[dd] + s_cnt[wave][dd] + rank[r]] = key[r];
     }
   }
@@ -550,29 +605,40 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint64_t* __re
     const int p = q * kThreads + tid;
     if (p < valid_count) {
       const uint64_t k = s_keys[p];
-      const int64_t gp = s_base[(uint32_t)(k >> shift) & 255u] + p;
-      if (gp >= 0 && gp < n) dst[gp] = k; else atomicOr(guard, 1u);
+      const int64_t gp = s_base[(uint32_t)(k >> shift) & (D - 1u)] + p;
+      if (gp >= 0 && gp < n) dst[gp] = runs.n ? runs_expand(k, runs) : k; else atomicOr(guard, 1u);
     }
   }
 }
 
+template <int BITS>
+void radix_pass(const uint64_t* src, uint64_t* dst, int64_t n, int shift, const uint32_t* hist, uint32_t* cnt,
+                uint32_t* off, int64_t tiles, uint32_t* guard, const BitRuns& runs, hipStream_t s) {
+  k_radix_hist<BITS><<<(unsigned)tiles, kThreads, 0, s>>>(src, n, shift, cnt, tiles);
+  k_radix_scan<<<1u << BITS, kThreads, 0, s>>>(cnt, tiles, hist, off);
+  k_radix_scatter<BITS><<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, shift, off, tiles, guard, runs);
+}
+
 // Sorts keys[0..n) (in a, scratch b) over the digits of ps; returns the buffer holding the
-// result. hist holds the digit counts of every pass ([passes][256]); cnt and off hold
-// 256 * cap_tiles words each.
+// result. hist holds the digit counts of every pass ([passes][bins]); cnt and off hold
+// kMaxBins * cap_tiles words each. With compacted keys (runs.n > 0) the last pass writes them
+// expanded.
 int radix_sort(uint64_t* a, uint64_t* b, int64_t n, PassSpec ps, const uint32_t* hist, uint32_t* cnt, uint32_t* off,
-               int64_t cap_tiles, uint32_t* guard, hipStream_t s, uint64_t** result) {
+               int64_t cap_tiles, uint32_t* guard, hipStream_t s, uint64_t** result, const BitRuns* runs = nullptr) {
   *result = a;
   if (n <= 0 || ps.passes == 0) return IGC_OK;
   const int64_t tiles = (n + kSortTile - 1) / kSortTile;
-  if (tiles > cap_tiles || ps.passes > kMaxPasses)
+  if (tiles > cap_tiles || ps.passes > kMaxPasses || ps.bits < 8 || ps.bits > kMaxDigitBits || (runs && runs->n && ps.passes == 0))
     return set_error(IGC_ERR_INTERNAL, "igc_grid_build: radix sort workspace too small");
   uint64_t* src = a;
   uint64_t* dst = b;
   for (int p = 0; p < ps.passes; ++p) {
-    const int shift = ps.lo_bit + 8 * p;
-    k_radix_hist<<<(unsigned)tiles, kThreads, 0, s>>>(src, n, shift, cnt, tiles);
-    k_radix_scan<<<256, kThreads, 0, s>>>(cnt, tiles, hist + 256 * p, off);
-    k_radix_scatter<<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, shift, off, tiles, guard);
+    const int shift = ps.lo_bit + ps.bits * p;
+    const uint32_t* hp = hist + ((size_t)p << ps.bits);
+    BitRuns r{};
+    if (runs && p == ps.passes - 1) r = *runs;
+    if (ps.bits == 8) radix_pass<8>(src, dst, n, shift, hp, cnt, off, tiles, guard, r, s);
+    else radix_pass<9>(src, dst, n, shift, hp, cnt, off, tiles, guard, r, s);
     IGC_HIP(hipGetLastError(), "igc_grid_build: radix pass launch");
     std::swap(src, dst);
   }
@@ -580,15 +646,25 @@ int radix_sort(uint64_t* a, uint64_t* b, int64_t n, PassSpec ps, const uint32_t*
   return IGC_OK;
 }
 
-// Digits over the varying bits at or above min_bit.
+// Digits over the varying bits at or above min_bit: as few passes as digits of up to
+// kMaxDigitBits allow, each digit as narrow as that pass count allows (at least 8 bits).
 PassSpec pass_spec(uint64_t varying, int min_bit = 0) {
-  PassSpec ps{0, 0};
+  PassSpec ps{0, 0, 8};
   if (min_bit > 0) varying &= ~((1ull << min_bit) - 1ull);
   if (!varying) return ps;
   const int lo = __builtin_ctzll(varying);
   const int hi = 63 - __builtin_clzll(varying);
+  const int span = hi - lo + 1;
   ps.lo_bit = lo;
-  ps.passes = (hi - lo + 8) / 8;
+  ps.passes = (span + kMaxDigitBits - 1) / kMaxDigitBits;
+  ps.bits = (span + ps.passes - 1) / ps.passes;
+  if (ps.bits < 8) ps.bits = 8;
+  // The key pass keeps passes * bins counters in LDS (at most kHistWidth).
+  while ((ps.passes << ps.bits) > kHistWidth) {
+    ++ps.passes;
+    ps.bits = (span + ps.passes - 1) / ps.passes;
+    if (ps.bits < 8) ps.bits = 8;
+  }
   return ps;
 }
 
@@ -917,8 +993,8 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   const int64_t tiles = (n_in + kTileKeys - 1) / kTileKeys;
   const int64_t sort_tiles = (n_in + kSortTile - 1) / kSortTile;
   const size_t ws = align_up(sizeof(BuildState), 256) + align_up((size_t)kTileBlocks * 32, 256) +
-                    align_up(2 * kMaxPasses * 256 * 4, 256) + align_up((size_t)kHistBlocks * kMaxPasses * 256 * 4, 256) +
-                    2 * align_up((size_t)n_in * 8, 256) + 2 * align_up((size_t)sort_tiles * 256 * 4, 256) +
+                    align_up(2 * kMaxPasses * kMaxBins * 4, 256) + align_up((size_t)kHistBlocks * kHistWidth * 4, 256) +
+                    2 * align_up((size_t)n_in * 8, 256) + 2 * align_up((size_t)sort_tiles * kMaxBins * 4, 256) +
                     align_up((size_t)tiles * 8, 256) + align_up((size_t)tiles * 32, 256) +
                     2 * align_up((size_t)kSmallSort * 8, 256);
   Arena ar(s);
@@ -926,12 +1002,12 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   if (rc) return rc;
   BuildState* st = ar.take<BuildState>(sizeof(BuildState));
   uint64_t* partial = ar.take<uint64_t>((size_t)kTileBlocks * 32);
-  uint32_t* hist = ar.take<uint32_t>(2 * kMaxPasses * 256 * 4);
-  uint32_t* hpart = ar.take<uint32_t>((size_t)kHistBlocks * kMaxPasses * 256 * 4);
+  uint32_t* hist = ar.take<uint32_t>(2 * kMaxPasses * kMaxBins * 4);
+  uint32_t* hpart = ar.take<uint32_t>((size_t)kHistBlocks * kHistWidth * 4);
   uint64_t* ka = ar.take<uint64_t>((size_t)n_in * 8);
   uint64_t* kb = ar.take<uint64_t>((size_t)n_in * 8);
-  uint32_t* rcnt = ar.take<uint32_t>((size_t)sort_tiles * 256 * 4);
-  uint32_t* roff = ar.take<uint32_t>((size_t)sort_tiles * 256 * 4);
+  uint32_t* rcnt = ar.take<uint32_t>((size_t)sort_tiles * kMaxBins * 4);
+  uint32_t* roff = ar.take<uint32_t>((size_t)sort_tiles * kMaxBins * 4);
   uint64_t* bcounts = ar.take<uint64_t>((size_t)tiles * 8);
   uint64_t* bprefix = ar.take<uint64_t>((size_t)tiles * 32);
   uint64_t* tile_list = ar.take<uint64_t>((size_t)kSmallSort * 8);
@@ -999,12 +1075,13 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
     const int nbh = grid_for(U, 256, kHistBlocks);
     k_hist<<<nbh, 256, 0, s>>>(tile_list, U, tps, hpart);
     IGC_HIP(hipGetLastError(), "igc_grid_build: tile histogram launch");
-    k_hist_reduce<<<tps.passes * 4, 256, 0, s>>>(hpart, nbh, tps.passes * 256, hist + kMaxPasses * 256);
+    const int twidth = tps.passes << tps.bits;
+    k_hist_reduce<<<(twidth + 15) / 16, 256, 0, s>>>(hpart, nbh, twidth, hist + kMaxPasses * kMaxBins);
     IGC_HIP(hipGetLastError(), "igc_grid_build: tile histogram reduce launch");
     uint32_t* tcnt = nullptr;
     const int64_t ttiles = (U + kSortTile - 1) / kSortTile;
-    if ((rc = ar.get_extra(&tcnt, (size_t)2 * ttiles * 256 * 4, "igc_grid_build: tile radix counts"))) return rc;
-    if ((rc = radix_sort(tile_list, tile_tmp, U, tps, hist + kMaxPasses * 256, tcnt, tcnt + ttiles * 256, ttiles,
+    if ((rc = ar.get_extra(&tcnt, (size_t)2 * ttiles * kMaxBins * 4, "igc_grid_build: tile radix counts"))) return rc;
+    if ((rc = radix_sort(tile_list, tile_tmp, U, tps, hist + kMaxPasses * kMaxBins, tcnt, tcnt + ttiles * kMaxBins, ttiles,
                          &st->guard, s, &tiles_sorted)))
       return rc;
   }
@@ -1015,17 +1092,43 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   int rank_bits = 0;
   while ((1ll << rank_bits) < U) ++rank_bits;
   const uint64_t varying = off_var | (rank_bits ? (((1ull << rank_bits) - 1ull) << 36) : 0ull);
-  const PassSpec ps = pass_spec(varying, 9);  // leaf part of key2 only
+  // Sort on the leaf part of key2 only, compacted to its varying bits.
+  BitRuns runs{};
+  const uint64_t leaf_var = varying >> 9;
+  if (leaf_var) {
+    int pos = 0;
+    for (int b = 0; b < 55 && runs.n <= 16;) {
+      if (!((leaf_var >> b) & 1ull)) { ++b; continue; }
+      int e = b;
+      while (e < 55 && ((leaf_var >> e) & 1ull)) ++e;
+      if (runs.n == 16) { runs.n = 17; break; }
+      runs.lo[runs.n] = (uint8_t)b;
+      runs.len[runs.n] = (uint8_t)(e - b);
+      runs.pos[runs.n] = (uint8_t)pos;
+      ++runs.n;
+      pos += e - b;
+      b = e;
+    }
+    if (runs.n > 16 || (runs.n == 1 && runs.lo[0] == 0)) {
+      runs.n = 0;  // too fragmented, or already compact
+    } else {
+      runs.cbits = (h->off_and >> 9) & ~leaf_var;
+    }
+  }
+  const uint64_t sort_var = runs.n ? (((1ull << __builtin_popcountll(leaf_var)) - 1ull) << 9) : varying;
+  const PassSpec ps = pass_spec(sort_var, 9);
   const int nbk = grid_for((n_in + 3) / 4, 256, kHistBlocks);
-  k_key2<<<nbk, 256, 0, s>>>(d_ijk, n_in, root_keys, root_vals, (uint32_t)(cap - 1), tiles_sorted, U, ka, ps, hpart,
-                             st);
+  if (ps.passes == 0) runs.n = 0;
+  k_key2<<<nbk, 256, 0, s>>>(d_ijk, n_in, root_keys, root_vals, (uint32_t)(cap - 1), tiles_sorted, U, ka, ps, runs,
+                             hpart, st);
   IGC_HIP(hipGetLastError(), "igc_grid_build: key pass launch");
   if (ps.passes > 0) {
-    k_hist_reduce<<<ps.passes * 4, 256, 0, s>>>(hpart, nbk, ps.passes * 256, hist);
+    const int width = ps.passes << ps.bits;
+    k_hist_reduce<<<(width + 15) / 16, 256, 0, s>>>(hpart, nbk, width, hist);
     IGC_HIP(hipGetLastError(), "igc_grid_build: histogram reduce launch");
   }
   uint64_t* sorted = ka;
-  if ((rc = radix_sort(ka, kb, n_in, ps, hist, rcnt, roff, sort_tiles, &st->guard, s, &sorted))) return rc;
+  if ((rc = radix_sort(ka, kb, n_in, ps, hist, rcnt, roff, sort_tiles, &st->guard, s, &sorted, &runs))) return rc;
 
   // Counts, then the read-back that sizes the topology.
   const int64_t nb = tiles;
