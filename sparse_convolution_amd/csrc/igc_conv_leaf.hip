@@ -207,6 +207,19 @@ __device__ __forceinline__ void split3(float v, uint16_t& hi, uint16_t& mid, uin
   lo = bf16_bits_rne(r2);
 }
 
+// split3 of two values at once with the hardware's round-to-nearest-even conversion
+// (v_cvt_pk_bf16_f32); value a in the low halves of the three words, b in the high halves.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split3x2(float a, float b, uint32_t& hw, uint32_t& mw, uint32_t& lw) {
+  const f32x2 v = {a, b};
+  hw = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  const f32x2 r1 = v - f32x2{__uint_as_float(hw << 16), __uint_as_float(hw & 0xFFFF0000u)};
+  mw = __builtin_bit_cast(uint32_t, __builtin_convertvector(r1, bf16x2));
+  const f32x2 r2 = r1 - f32x2{__uint_as_float(mw << 16), __uint_as_float(mw & 0xFFFF0000u)};
+  lw = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2));
+}
+
 // Window cell offset of stencil offset o relative to the cell of offset (-1,-1,-1).
 __device__ __forceinline__ int cell_delta(int o) { return (o / 9) * 100 + ((o / 3) % 3) * 10 + o % 3; }
 
@@ -251,13 +264,11 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
   // Every wave needs the same fragments: wave w splits the (q, ns) pairs with (q*NS+ns) % 4 ==
   // w into LDS (the window's space, filled afterwards), and all waves then load all of them.
   int dcell[NCH][OPG];
-  bool dvalid[NCH][OPG];
 #pragma unroll
   for (int q = 0; q < NCH; ++q)
 #pragma unroll
     for (int h = 0; h < OPG; ++h) {
       const int o = (q * 32 + kg * 8) / CIN + h;
-      dvalid[q][h] = o < 27;
       dcell[q][h] = cell_delta(o < 27 ? o : 0);
     }
   bf16x8* s_wsp = (bf16x8*)s_win;
@@ -327,14 +338,7 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
     if (c >= 1000) break;
     uint32_t hw[CIN / 2], mw[CIN / 2], lw[CIN / 2];
 #pragma unroll
-    for (int j = 0; j < CIN / 2; ++j) {
-      uint16_t h0, m0, l0, h1, m1, l1;
-      split3(v[i][2 * j], h0, m0, l0);
-      split3(v[i][2 * j + 1], h1, m1, l1);
-      hw[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-      mw[j] = (uint32_t)m0 | ((uint32_t)m1 << 16);
-      lw[j] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-    }
+    for (int j = 0; j < CIN / 2; ++j) split3x2(v[i][2 * j], v[i][2 * j + 1], hw[j], mw[j], lw[j]);
     uint16_t* dst = &s_win[c * CS];
     if constexpr (CIN == 8) {
       *(uint4*)&dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
@@ -362,15 +366,13 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
       bf16x8 a[3];
 #pragma unroll
       for (int sp = 0; sp < 3; ++sp) {
+        // k past 27 CIN reads the cell of offset 0, a real neighbour, against zero W splits.
         if constexpr (CIN == 8) {
-          const bf16x8 v = *(const bf16x8*)&s_win[(cell0 + dcell[q][0]) * CS + sp * CIN];
-          a[sp] = dvalid[q][0] ? v : bf16x8{};
+          a[sp] = *(const bf16x8*)&s_win[(cell0 + dcell[q][0]) * CS + sp * CIN];
         } else {
           const uint2 v0 = *(const uint2*)&s_win[(cell0 + dcell[q][0]) * CS + sp * CIN];
           const uint2 v1 = *(const uint2*)&s_win[(cell0 + dcell[q][1]) * CS + sp * CIN];
-          const uint4 u = make_uint4(dvalid[q][0] ? v0.x : 0u, dvalid[q][0] ? v0.y : 0u, dvalid[q][1] ? v1.x : 0u,
-                                     dvalid[q][1] ? v1.y : 0u);
-          a[sp] = __builtin_bit_cast(bf16x8, u);
+          a[sp] = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
         }
       }
 #pragma unroll
