@@ -20,7 +20,7 @@ _SRC = os.path.join(_HERE, "igc_oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 __all__ = ["build_library", "OracleGrid", "kernel_map", "conv", "conv_rows", "conv_dgrad", "conv_wgrad",
-           "standard_offsets", "num_threads"]
+           "conv_grid_coords", "conv_map_between", "standard_offsets", "num_threads"]
 
 
 def build_library(force: bool = True) -> str:
@@ -147,7 +147,8 @@ def conv(kmap: np.ndarray, feats: np.ndarray, w: np.ndarray, rows: np.ndarray | 
     """Submanifold convolution in float64 over a neighbour map (fVDB notes, sparse-conv
     operators): out[r] = sum_o W[o]^T feats[map[o, r]] over map[o, r] >= 0.
 
-    feats float32[N, cin] (bf16 inputs are passed as their exact float32 values),
+    feats float32[N_in, cin] (bf16 inputs are passed as their exact float32 values; N_in = N
+    for a map over one grid, the input grid's size for a map between two grids),
     w float32[K, cin, cout]; returns float64[len(rows) or N, cout].
     """
     kmap = np.ascontiguousarray(kmap, dtype=np.int32)
@@ -155,7 +156,8 @@ def conv(kmap: np.ndarray, feats: np.ndarray, w: np.ndarray, rows: np.ndarray | 
     f = np.ascontiguousarray(feats, dtype=np.float32)
     ww = np.ascontiguousarray(w, dtype=np.float32)
     cin, cout = ww.shape[1], ww.shape[2]
-    assert f.shape == (N, cin) and ww.shape[0] == K
+    assert f.ndim == 2 and f.shape[1] == cin and ww.shape[0] == K
+    assert kmap.size == 0 or int(kmap.max()) < f.shape[0]
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     R = N if r is None else r.shape[0]
     out = np.zeros((R, cout), np.float64)
@@ -211,3 +213,55 @@ def conv_wgrad(kmap: np.ndarray, feats: np.ndarray, dout: np.ndarray) -> np.ndar
         valid = kmap[o] >= 0
         dw[o] = f[kmap[o][valid]].T @ dy[valid]
     return dw
+
+
+def _stride3(stride) -> np.ndarray:
+    s = np.broadcast_to(np.asarray(stride, dtype=np.int64), (3,)).copy()
+    assert np.all(s >= 1)
+    return s
+
+
+def conv_grid_coords(coords: np.ndarray, stride, transposed: bool = False) -> np.ndarray:
+    """Output coordinates of a 3x3x3 sparse convolution with the given stride (fVDB notes'
+    grid-to-grid ops ConvGrid / ConvTransposeGrid; the pages name them without a formula, so
+    the plain reading is used). Offsets d run over {-1, 0, 1}^3.
+
+    strided:    y is an output iff some input x has x = s * y + d (its receptive field holds
+                an input voxel);
+    transposed: y is an output iff y = s * x + d for some input x.
+    Returns the unique coordinates, int32[M, 3], in lexicographic order."""
+    c = np.asarray(coords, dtype=np.int64).reshape(-1, 3)
+    s = _stride3(stride)
+    parts = []
+    for d in standard_offsets().astype(np.int64):
+        if transposed:
+            parts.append(s * c + d)
+        else:
+            z = c - d
+            ok = np.all(z % s == 0, axis=1)
+            parts.append(z[ok] // s)
+    out = np.unique(np.concatenate(parts, axis=0), axis=0) if parts else np.zeros((0, 3), np.int64)
+    return out.astype(np.int32)
+
+
+def conv_map_between(out_grid: OracleGrid, in_grid: OracleGrid, stride, transposed: bool = False) -> np.ndarray:
+    """Neighbour map int32[27, N_out] from the output grid's rows to the input grid's rows
+    (DriveRT page, "Shared neighbour maps", for two coordinate domains):
+    strided:    map[o, r] = in.index(s * y_r + d_o);
+    transposed: map[o, r] = in.index((y_r - d_o) / s) where s divides y_r - d_o, else -1.
+    o = (dx+1)*9 + (dy+1)*3 + (dz+1); -1 where the input voxel is absent."""
+    y = out_grid.active_ijk().astype(np.int64)
+    s = _stride3(stride)
+    offs = standard_offsets().astype(np.int64)
+    m = np.full((27, y.shape[0]), -1, np.int32)
+    for o, d in enumerate(offs):
+        if transposed:
+            z = y - d
+            ok = np.all(z % s == 0, axis=1)
+            q = z // s
+        else:
+            q = s * y + d
+            ok = np.ones(y.shape[0], bool)
+        if np.any(ok):
+            m[o, ok] = in_grid.ijk_to_index(q[ok].astype(np.int32))
+    return m

@@ -399,3 +399,137 @@ def test_conv_gradients_are_adjoints_of_the_forward():
     via_w = float(np.sum(w.astype(np.float64) * oracle.conv_wgrad(m, f, dy)))
     assert abs(lhs - via_x) <= 1e-10 * abs(lhs)
     assert abs(lhs - via_w) <= 1e-10 * abs(lhs)
+
+
+# ----------------------------------------------------------------------------- strided / transposed grids
+
+def _occupancy(act: np.ndarray, lo: np.ndarray, ext: np.ndarray) -> torch.Tensor:
+    vol = torch.zeros((1, 1, *ext.tolist()), dtype=torch.float64)
+    loc = torch.from_numpy((act - lo).astype(np.int64))
+    vol[0, 0, loc[:, 0], loc[:, 1], loc[:, 2]] = 1.0
+    return vol
+
+
+def _coords_of(vol: torch.Tensor, shift: np.ndarray) -> set:
+    nz = torch.nonzero(vol[0, 0] > 0).numpy()
+    return {tuple(int(v) for v in (r + shift)) for r in nz}
+
+
+@pytest.mark.parametrize("stride", [1, 2, 3])
+def test_conv_grid_equals_dense_max_pool(stride):
+    # Output y is active iff the 3x3x3 window centred on s*y holds an input: max_pool3d with
+    # kernel 3, stride s and padding 1 over the occupancy, on coordinates >= 0.
+    act = workloads.random_coords(900, 1, 17, seed=31 + stride)  # every output index is >= 0
+    got = {tuple(r) for r in oracle.conv_grid_coords(act, stride).tolist()}
+    ext = act.max(axis=0) + 2  # the pooled volume reaches every output
+    occ = _occupancy(act, np.zeros(3, np.int64), ext)
+    pooled = torch.nn.functional.max_pool3d(occ, kernel_size=3, stride=stride, padding=1)
+    assert got == _coords_of(pooled, np.zeros(3, np.int64))
+
+
+def test_conv_grid_brute_force_signed_and_anisotropic():
+    act = workloads.random_coords(60, -9, 9, seed=35)
+    s = np.array([2, 1, 3])
+    got = {tuple(r) for r in oracle.conv_grid_coords(act, s).tolist()}
+    inputs = {tuple(r) for r in act.tolist()}
+    want = set()
+    for y0 in range(-6, 7):
+        for y1 in range(-11, 12):
+            for y2 in range(-5, 6):
+                if any((s[0] * y0 + a, s[1] * y1 + b, s[2] * y2 + c) in inputs
+                       for a in (-1, 0, 1) for b in (-1, 0, 1) for c in (-1, 0, 1)):
+                    want.add((y0, y1, y2))
+    assert got == want
+
+
+def test_conv_transpose_grid_equals_dense_transposed_conv():
+    # y = 2x + d: conv_transpose3d of the occupancy with a 3^3 box of ones, stride 2, padding 1.
+    act = workloads.random_coords(700, 1, 15, seed=37)
+    got = {tuple(r) for r in oracle.conv_grid_coords(act, 2, transposed=True).tolist()}
+    ext = act.max(axis=0) + 1
+    occ = _occupancy(act, np.zeros(3, np.int64), ext)
+    ones = torch.ones((1, 1, 3, 3, 3), dtype=torch.float64)
+    up = torch.nn.functional.conv_transpose3d(occ, ones, stride=2, padding=1, output_padding=1)
+    assert got == _coords_of(up, np.zeros(3, np.int64))
+
+
+def _strided_case(seed, transposed):
+    act = workloads.random_coords(800, 1, 15, seed=seed)
+    gi = OracleGrid(act)
+    go = OracleGrid(oracle.conv_grid_coords(gi.active_ijk(), 2, transposed=transposed))
+    m = oracle.conv_map_between(go, gi, 2, transposed=transposed)
+    return gi, go, m
+
+
+def test_conv_map_between_brute_force():
+    for transposed in (False, True):
+        gi, go, m = _strided_case(41, transposed)
+        xin = {tuple(r): i for i, r in enumerate(gi.active_ijk().tolist())}
+        y = go.active_ijk().astype(np.int64)
+        offs = standard_offsets().astype(np.int64)
+        for r in range(0, y.shape[0], 7):
+            for o, d in enumerate(offs):
+                if transposed:
+                    z = y[r] - d
+                    q = tuple((z // 2).tolist()) if np.all(z % 2 == 0) else None
+                else:
+                    q = tuple((2 * y[r] + d).tolist())
+                assert m[o, r] == (xin.get(q, -1) if q is not None else -1)
+
+
+def test_strided_conv_matches_dense_conv3d():
+    gi, go, m = _strided_case(43, False)
+    cin, cout = 4, 6
+    rng = np.random.default_rng(44)
+    f = rng.standard_normal((gi.n, cin)).astype(np.float32)
+    w = rng.standard_normal((27, cin, cout)).astype(np.float32)
+    got = oracle.conv(m, f, w)
+    xi = gi.active_ijk().astype(np.int64)
+    ext = xi.max(axis=0) + 2
+    vol = torch.zeros((1, cin, *ext.tolist()), dtype=torch.float64)
+    vol[0, :, xi[:, 0], xi[:, 1], xi[:, 2]] = torch.from_numpy(f.astype(np.float64)).T
+    wt = torch.from_numpy(w.astype(np.float64)).reshape(3, 3, 3, cin, cout).permute(4, 3, 0, 1, 2).contiguous()
+    dense = torch.nn.functional.conv3d(vol, wt, stride=2, padding=1)
+    y = go.active_ijk().astype(np.int64)
+    want = dense[0, :, y[:, 0], y[:, 1], y[:, 2]].T.numpy()
+    assert np.max(np.abs(got - want)) < 1e-9 * max(1.0, np.max(np.abs(want)))
+
+
+def test_transposed_conv_matches_dense_conv_transpose3d():
+    gi, go, m = _strided_case(45, True)
+    cin, cout = 5, 3
+    rng = np.random.default_rng(46)
+    f = rng.standard_normal((gi.n, cin)).astype(np.float32)
+    w = rng.standard_normal((27, cin, cout)).astype(np.float32)
+    got = oracle.conv(m, f, w)
+    xi = gi.active_ijk().astype(np.int64)
+    ext = xi.max(axis=0) + 1
+    vol = torch.zeros((1, cin, *ext.tolist()), dtype=torch.float64)
+    vol[0, :, xi[:, 0], xi[:, 1], xi[:, 2]] = torch.from_numpy(f.astype(np.float64)).T
+    # conv_transpose3d: out[y] += in[x] w[ci, co, k] for y = 2x - 1 + k, i.e. d = k - 1.
+    wt = torch.from_numpy(w.astype(np.float64)).reshape(3, 3, 3, cin, cout).permute(3, 4, 0, 1, 2).contiguous()
+    dense = torch.nn.functional.conv_transpose3d(vol, wt, stride=2, padding=1, output_padding=1)
+    y = go.active_ijk().astype(np.int64)
+    want = dense[0, :, y[:, 0], y[:, 1], y[:, 2]].T.numpy()
+    assert np.max(np.abs(got - want)) < 1e-9 * max(1.0, np.max(np.abs(want)))
+
+
+def test_transposed_conv_is_adjoint_of_strided_conv():
+    # <Y, S X> = <T Y, X> where S is the stride-2 conv with W and T the transposed conv of the
+    # output grid with W[o]^T, read at the input grid's voxels (T's grid contains them).
+    act = workloads.random_coords(600, -8, 8, seed=47)
+    gx = OracleGrid(act)
+    gy = OracleGrid(oracle.conv_grid_coords(gx.active_ijk(), 2))
+    gt = OracleGrid(oracle.conv_grid_coords(gy.active_ijk(), 2, transposed=True))
+    cin, cout = 3, 4
+    rng = np.random.default_rng(48)
+    X = rng.standard_normal((gx.n, cin)).astype(np.float32)
+    Y = rng.standard_normal((gy.n, cout)).astype(np.float32)
+    w = rng.standard_normal((27, cin, cout)).astype(np.float32)
+    SX = oracle.conv(oracle.conv_map_between(gy, gx, 2), X, w)
+    TY = oracle.conv(oracle.conv_map_between(gt, gy, 2, transposed=True), Y, np.ascontiguousarray(w.transpose(0, 2, 1)))
+    rows = gt.ijk_to_index(gx.active_ijk())
+    assert np.all(rows >= 0)
+    lhs = float(np.sum(Y.astype(np.float64) * SX))
+    rhs = float(np.sum(TY[rows] * X.astype(np.float64)))
+    assert abs(lhs - rhs) < 1e-9 * max(1.0, abs(lhs))
