@@ -6,7 +6,7 @@ IndexGrid from the shuffled coordinates (tile hash, radix sort, node registratio
 27-offset kernel map, and the 3x3x3 submanifold convolution on the automatically chosen
 path. Prints one JSON line.
 
-    python bench.py [--workload leaf] [--steps K] [--warmup W] [--gpus 1] [--backward]
+    python bench.py [--workload leaf] [--steps K] [--warmup W] [--gpus 1] [--backward | --strided S]
 
 value = effective conv FLOPs (2 * pairs * cin * cout, empty MACs excluded, as the fVDB notes
 define effective TFLOPS in their micro-benchmarks) per second of the whole step. The line also
@@ -17,7 +17,11 @@ cores as a reference point.
 With --backward a step also runs the two gradients of the convolution (input gradient, then
 weight gradient, as two calls of igc_sparse_conv_backward) for a synthetic output gradient;
 value is then 3 * 2 * pairs * cin * cout per second of the whole step, and the line carries
-both gradients' phase times and rooflines. The default line is unchanged.
+both gradients' phase times and rooflines. With --strided S a step is one strided layer on
+the gather-GEMM-scatter path (bf16 workloads): build the input grid, its stride-S output grid
+(igc_conv_grid), the map between them (igc_conv_map) and the convolution (igc_sparse_conv_between);
+value is 2 * pairs * cin * cout of that convolution per second of the step. The default line is
+unchanged.
 """
 from __future__ import annotations
 
@@ -126,6 +130,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--backward", action="store_true", help="add the input and weight gradients to the step")
+    ap.add_argument("--strided", type=int, default=0, help="time one strided layer with this stride instead")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -139,6 +144,9 @@ def main() -> int:
     import torch
     import sparse_convolution_amd as igc
     import workloads
+
+    if args.strided:
+        return strided_main(args, torch, igc, workloads)
 
     wl = workloads.WORKLOADS[args.workload]
     steps, warmup = DEFAULT_STEPS[args.workload]
@@ -263,6 +271,79 @@ def main() -> int:
         line["backward"] = backward
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(coords, wl, wl.cin, wl.cout, wl.dtype)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def strided_main(args, torch, igc, workloads) -> int:
+    wl = workloads.WORKLOADS[args.workload]
+    if wl.dtype != "bf16":
+        print("--strided runs on the gather-GEMM-scatter path: pick a bf16 workload (band, lidar, large)",
+              file=sys.stderr)
+        return 2
+    steps, warmup = DEFAULT_STEPS[args.workload]
+    steps = args.steps if args.steps is not None else steps
+    warmup = args.warmup if args.warmup is not None else warmup
+    S = args.strided
+    dev = torch.device("cuda", 0)
+    coords_d = torch.from_numpy(workloads.make_coords(args.workload)).to(dev)
+    g0 = igc.grid_build(coords_d)
+    go0 = igc.conv_grid(g0, S)
+    m0 = igc.conv_map(g0, go0, S)
+    pairs = int((m0 >= 0).sum().item())
+    n_in, n_out = g0.n_voxels, go0.n_voxels
+    feats = workloads.make_features_device(n_in, wl.cin, 3000 + wl.index, dev, torch.bfloat16)
+    weights = torch.from_numpy(workloads.make_weights(wl.cin, wl.cout, 4000 + wl.index, wl.weight_std)).to(
+        dev, torch.bfloat16)
+    out = torch.empty((n_out, wl.cout), dtype=torch.bfloat16, device=dev)
+    del m0, go0, g0
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev):
+        ev[0].record(stream)
+        g = igc.grid_build(coords_d)
+        ev[1].record(stream)
+        go = igc.conv_grid(g, S)
+        ev[2].record(stream)
+        m = igc.conv_map(g, go, S)
+        ev[3].record(stream)
+        igc.sparse_conv_between(go, feats, weights, m, out=out)
+        ev[4].record(stream)
+        return g, go, m
+
+    for _ in range(warmup):
+        step([torch.cuda.Event(enable_timing=True) for _ in range(5)])
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for st in range(steps):
+        keep = step(events[st])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del keep
+    ms_step = wall * 1e3 / steps
+    flops = 2.0 * pairs * wl.cin * wl.cout
+    names = ["build_ms", "conv_grid_ms", "conv_map_ms", "conv_ms"]
+    phases = {}
+    for i, name in enumerate(names):
+        t = [e[i].elapsed_time(e[i + 1]) for e in events]
+        phases[name] = {"mean": round(float(np.mean(t)), 4), "p50": _pct(t, 50), "p95": _pct(t, 95), "p99": _pct(t, 99)}
+    conv_ms = phases["conv_ms"]["mean"]
+    conv_tflops = flops / (conv_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["bf16"]
+    line = {
+        "metric": f"strided (stride {S}) sparse-conv layer effective TFLOP/s incl. IndexGrid builds and map",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 4), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "stride": S, "cin": wl.cin, "cout": wl.cout, "n_in": n_in,
+                   "n_out": n_out, "pairs": pairs, "pairs_per_output": round(pairs / max(n_out, 1), 3)},
+        "phases": phases,
+        "conv_map_gbs": round(108.0 * n_out / (phases["conv_map_ms"]["mean"] * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(conv_tflops, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(conv_tflops / peak, 4), "traffic": None, "kernel": "k_conv_ggs_bf16",
+                     "flops_per_launch": flops, "avg_launch_ms": round(conv_ms, 4)},
+    }
     print(json.dumps(line), flush=True)
     return 0
 

@@ -158,8 +158,9 @@ int igc_kernel_map(const igc_grid* grid, const int32_t* h_offsets, int32_t K, in
  * d_map (int32[27,N] from igc_kernel_map with the standard 27 offsets) is required by
  * IGC_PATH_GGS and ignored by IGC_PATH_LEAF; with IGC_PATH_AUTO it is required whenever the
  * choice (see igc_select_path) is GGS. Supported combinations:
- *     LEAF: dtype F32, cin in {4, 8, 12, 16}, cout a multiple of 16 up to 64
- *     GGS : dtype BF16, cin a multiple of 32 up to 256, cout a multiple of 64 up to 512
+ *     LEAF: dtype F32, (cin, cout) in {(4,8), (4,16), (4,32), (8,8), (8,16), (8,32),
+ *           (16,16), (8,4), (16,4), (16,8)}
+ *     GGS : dtype BF16, cin a multiple of 32 up to 1024, cout a multiple of 64 up to 1024
  * Anything else returns IGC_ERR_UNSUPPORTED. d_out must not alias d_feats. */
 int igc_sparse_conv(const igc_grid* grid, const int32_t* d_map, const void* d_feats, int32_t dtype,
                     int32_t cin, const void* d_w, int32_t cout, void* d_out, int32_t path,
@@ -183,6 +184,42 @@ int igc_sparse_conv(const igc_grid* grid, const int32_t* d_map, const void* d_fe
 int igc_sparse_conv_backward(const igc_grid* grid, const int32_t* d_map, const void* d_feats, int32_t dtype,
                              int32_t cin, const void* d_w, int32_t cout, const void* d_dout, void* d_dfeats,
                              float* d_dw, int32_t path, igc_stream stream);
+
+/* Output grid of a 3x3x3 convolution with per-axis stride h_stride[0..2] (host, each 1, 2 or 3)
+ * over `in` (fVDB notes, grid-to-grid ops ConvGrid and ConvTransposeGrid; the pages name the
+ * ops without a formula, so the plain reading is taken), offsets d in {-1, 0, 1}^3:
+ *     transposed == 0: y is active iff some active x of `in` has x = stride * y + d
+ *                      (stride 1 gives the dilation of `in` by one voxel);
+ *     transposed != 0: y is active iff y = stride * x + d for some active x of `in`.
+ * The result is a new immutable grid (*out, library-owned, freed with igc_grid_destroy) in the
+ * canonical order of igc_grid_build. Errors: IGC_ERR_UNSUPPORTED for strides outside 1..3,
+ * IGC_ERR_RANGE when an output coordinate leaves the int32 range; *out is then NULL. One host
+ * synchronization more than igc_grid_build. */
+int igc_conv_grid(const igc_grid* in, const int32_t* h_stride, int32_t transposed, igc_stream stream,
+                  igc_grid** out);
+
+/* Neighbour map between two grids for that convolution (DriveRT, "Shared neighbour maps", for
+ * two coordinate domains): d_map int32[27, N_out] (device, caller-owned, N_out = voxels of
+ * `out`), offsets ordered as in igc_kernel_map:
+ *     transposed == 0: d_map[o*N_out + r] = row of `in` at stride * y_r + d_o, or -1;
+ *     transposed != 0: d_map[o*N_out + r] = row of `in` at (y_r - d_o) / stride where the
+ *                      stride divides y_r - d_o on every axis, else -1.
+ * y_r are the coordinates of `out` in row order. Any two grids are accepted (`out` need not come
+ * from igc_conv_grid). Strides must be 1, 2 or 3 (IGC_ERR_UNSUPPORTED otherwise). */
+int igc_conv_map(const igc_grid* in, const igc_grid* out, const int32_t* h_stride, int32_t transposed,
+                 int32_t* d_map, igc_stream stream);
+
+/* Convolution between two grids (strided and transposed sparse convolution): for every active
+ * voxel r of `out`,
+ *     d_out[r, co] = sum_{o, ci : map[o, r] >= 0} d_feats[map[o, r], ci] * d_w[o, ci, co]
+ * with d_map from igc_conv_map (int32[27, N_out], values < n_in), d_feats [n_in, cin] the input
+ * grid's features, d_w [27, cin, cout] and d_out [N_out, cout]. Runs on the gather-GEMM-scatter
+ * path: dtype BF16 with the shapes igc_sparse_conv supports there (fp32 accumulation, outputs
+ * rounded to nearest even); anything else returns IGC_ERR_UNSUPPORTED. d_out must not alias
+ * d_feats. */
+int igc_sparse_conv_between(const igc_grid* out, const int32_t* d_map, int64_t n_in, const void* d_feats,
+                            int32_t dtype, int32_t cin, const void* d_w, int32_t cout, void* d_out,
+                            igc_stream stream);
 
 /* The path IGC_PATH_AUTO takes for this grid and layer shape (host only). Leaf when the
  * dtype is F32 and the shape is supported by LEAF, GGS otherwise; IGC_ERR_UNSUPPORTED when

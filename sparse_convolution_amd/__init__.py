@@ -15,7 +15,8 @@ from . import _lib
 from ._lib import IgcError
 
 __all__ = [
-    "Grid", "grid_build", "kernel_map", "sparse_conv", "sparse_conv_backward", "standard_offsets", "IgcError",
+    "Grid", "grid_build", "kernel_map", "sparse_conv", "sparse_conv_backward", "conv_grid", "conv_map",
+    "sparse_conv_between", "standard_offsets", "IgcError",
     "PATH_AUTO", "PATH_LEAF", "PATH_GGS",
 ]
 
@@ -200,3 +201,49 @@ def sparse_conv_backward(grid: Grid, feats: torch.Tensor, weights: torch.Tensor,
                                                     _ptr(weights), cout, _ptr(dout), _ptr(dx), _ptr(dw),
                                                     _PATHS[path], _stream(grid.device)))
     return dx, dw
+
+
+def _stride_array(stride) -> np.ndarray:
+    s = np.broadcast_to(np.asarray(stride, dtype=np.int32), (3,))
+    return np.ascontiguousarray(s)
+
+
+def conv_grid(grid: Grid, stride=2, transposed: bool = False) -> Grid:
+    """Output grid of a 3x3x3 convolution with the given stride (int or 3 ints, each 1..3) over
+    `grid`, or of the transposed convolution (igc_conv_grid)."""
+    s = _stride_array(stride)
+    h = ctypes.c_void_p()
+    _lib.check(_lib.load().igc_conv_grid(grid.handle, s.ctypes.data_as(ctypes.c_void_p), int(bool(transposed)),
+                                         _stream(grid.device), ctypes.byref(h)))
+    return Grid(h, grid.device)
+
+
+def conv_map(in_grid: Grid, out_grid: Grid, stride=2, transposed: bool = False) -> torch.Tensor:
+    """Neighbour map int32[27, N_out] from out_grid's rows to in_grid's rows (igc_conv_map)."""
+    s = _stride_array(stride)
+    m = torch.empty((27, out_grid.n_voxels), dtype=torch.int32, device=out_grid.device)
+    _lib.check(_lib.load().igc_conv_map(in_grid.handle, out_grid.handle, s.ctypes.data_as(ctypes.c_void_p),
+                                        int(bool(transposed)), _ptr(m), _stream(out_grid.device)))
+    return m
+
+
+def sparse_conv_between(out_grid: Grid, feats: torch.Tensor, weights: torch.Tensor, kmap: torch.Tensor,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """Convolution from an input grid's features [N_in, cin] to out_grid's rows through kmap
+    (from conv_map); weights [27, cin, cout] (igc_sparse_conv_between)."""
+    dt = feats.dtype
+    cin = feats.shape[1] if feats.dim() == 2 else -1
+    feats = _device_tensor(feats, "feats", dt, cin)
+    if weights.dim() != 3 or weights.shape[0] != 27 or weights.shape[1] != cin:
+        raise ValueError(f"weights must have shape [27, {cin}, cout], got {tuple(weights.shape)}")
+    weights = _device_tensor(weights, "weights", dt)
+    cout = weights.shape[2]
+    kmap = _device_tensor(kmap, "kmap", torch.int32)
+    if tuple(kmap.shape) != (27, out_grid.n_voxels):
+        raise ValueError(f"kmap must have shape [27, {out_grid.n_voxels}]")
+    if out is None:
+        out = torch.empty((out_grid.n_voxels, cout), dtype=dt, device=out_grid.device)
+    _lib.check(_lib.load().igc_sparse_conv_between(out_grid.handle, _ptr(kmap), feats.shape[0], _ptr(feats),
+                                                   _dtype_code(dt), cin, _ptr(weights), cout, _ptr(out),
+                                                   _stream(out_grid.device)))
+    return out

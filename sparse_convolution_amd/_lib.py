@@ -10,7 +10,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libigconv.s
 EXPORTS = (
     "igc_grid_build", "igc_grid_destroy", "igc_grid_get_info", "igc_grid_active_ijk",
     "igc_grid_ijk_to_index", "igc_grid_export", "igc_kernel_map", "igc_sparse_conv",
-    "igc_sparse_conv_backward", "igc_select_path", "igc_last_error",
+    "igc_sparse_conv_backward", "igc_conv_grid", "igc_conv_map", "igc_sparse_conv_between", "igc_select_path",
+    "igc_last_error",
 )
 
 STATUS = {
@@ -62,6 +63,9 @@ def load() -> ctypes.CDLL:
         "igc_kernel_map": [P, P, i32, P, P, P],
         "igc_sparse_conv": [P, P, P, i32, i32, P, i32, P, i32, P],
         "igc_sparse_conv_backward": [P, P, P, i32, i32, P, i32, P, P, P, i32, P],
+        "igc_conv_grid": [P, P, i32, P, ctypes.POINTER(P)],
+        "igc_conv_map": [P, P, P, i32, P, P],
+        "igc_sparse_conv_between": [P, P, i64, P, i32, i32, P, i32, P, P],
         "igc_select_path": [P, i32, i32, i32, ctypes.POINTER(i32)],
         "igc_last_error": [],
     }

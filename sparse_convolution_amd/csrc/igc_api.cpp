@@ -303,6 +303,57 @@ int igc_sparse_conv_backward(const igc_grid* g, const int32_t* d_map, const void
   return launch_conv_backward(g, d_map, d_feats, dtype, cin, d_w, cout, d_dout, d_dfeats, d_dw, p, (hipStream_t)stream);
 }
 
+int igc_conv_grid(const igc_grid* in, const int32_t* h_stride, int32_t transposed, igc_stream stream,
+                  igc_grid** out) {
+  clear_error();
+  if (!out) return set_error(IGC_ERR_INVALID_ARG, "igc_conv_grid: out is null");
+  *out = nullptr;
+  if (!in || !h_stride) return set_error(IGC_ERR_INVALID_ARG, "igc_conv_grid: in or h_stride is null");
+  int n[3];
+  if (!conv_grid_slots(h_stride, transposed, n))
+    return set_error(IGC_ERR_UNSUPPORTED, "igc_conv_grid: strides must be 1, 2 or 3");
+  igc_grid* g = new (std::nothrow) igc_grid();
+  if (!g) return set_error(IGC_ERR_OOM, "igc_conv_grid: host allocation");
+  g->stream = (hipStream_t)stream;
+  g->device = in->device;
+  const int rc = build_conv_grid(in, h_stride, transposed, (hipStream_t)stream, g);
+  if (rc != IGC_OK) {
+    free_grid(g);
+    return rc;
+  }
+  *out = g;
+  return IGC_OK;
+}
+
+int igc_conv_map(const igc_grid* in, const igc_grid* out, const int32_t* h_stride, int32_t transposed,
+                 int32_t* d_map, igc_stream stream) {
+  clear_error();
+  if (!in || !out || !h_stride) return set_error(IGC_ERR_INVALID_ARG, "igc_conv_map: null argument");
+  int n[3];
+  if (!conv_grid_slots(h_stride, transposed, n))
+    return set_error(IGC_ERR_UNSUPPORTED, "igc_conv_map: strides must be 1, 2 or 3");
+  if (out->n_voxels > 0 && !d_map) return set_error(IGC_ERR_INVALID_ARG, "igc_conv_map: d_map is null");
+  return launch_conv_map(in, out, h_stride, transposed, d_map, (hipStream_t)stream);
+}
+
+int igc_sparse_conv_between(const igc_grid* out, const int32_t* d_map, int64_t n_in, const void* d_feats,
+                            int32_t dtype, int32_t cin, const void* d_w, int32_t cout, void* d_out,
+                            igc_stream stream) {
+  clear_error();
+  if (!out) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_between: grid is null");
+  if (dtype != IGC_F32 && dtype != IGC_BF16) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_between: bad dtype");
+  if (cin < 1 || cout < 1 || n_in < 0)
+    return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_between: cin, cout must be positive and n_in >= 0");
+  if (!d_w) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_between: d_w is null");
+  if (!ggs_conv_supported(dtype, cin, cout))
+    return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv_between: gather-GEMM-scatter path does not support this dtype / cin / cout");
+  if (out->n_voxels > 0 && (!d_map || !d_out || (n_in > 0 && !d_feats)))
+    return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_between: d_map, d_feats or d_out is null");
+  if (d_feats && d_feats == d_out) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_between: d_out aliases d_feats");
+  if (out->n_voxels == 0) return IGC_OK;
+  return launch_conv_ggs(out, d_map, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream);
+}
+
 const char* igc_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

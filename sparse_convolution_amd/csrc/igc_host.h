@@ -96,6 +96,11 @@ bool wgrad_leaf_supported(int32_t cin, int32_t cout);
 int64_t wgrad_leaf_groups(const igc_grid* g);
 int launch_wgrad_leaf(const igc_grid* g, const void* d_feats, int32_t cin, const void* d_dout, int32_t cout,
                       float* part, int64_t groups, hipStream_t s);
+// Output grids of strided / transposed 3x3x3 convolutions and the map between two grids.
+int conv_grid_slots(const int32_t* stride, int32_t transposed, int* n);
+int build_conv_grid(const igc_grid* in, const int32_t* stride, int32_t transposed, hipStream_t s, igc_grid* out);
+int launch_conv_map(const igc_grid* in, const igc_grid* out, const int32_t* stride, int32_t transposed,
+                    int32_t* d_map, hipStream_t s);
 bool wgrad_supported(int32_t dtype, int32_t cin, int32_t cout);
 int launch_conv_backward(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype, int32_t cin,
                          const void* d_w, int32_t cout, const void* d_dout, void* d_dfeats, float* d_dw,
