@@ -79,7 +79,10 @@ __global__ void k_fill_u64(uint64_t* __restrict__ p, int64_t n, uint64_t v) {
     p[e] = v;
 }
 
-__global__ void k_init_state(BuildState* st) {
+// Build state reset and root table fill (every slot empty).
+__global__ void k_init_root(BuildState* st, uint64_t* __restrict__ keys, int64_t cap) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < cap; e += (int64_t)gridDim.x * blockDim.x)
+    keys[e] = kEmptyKey;
   if (threadIdx.x == 0 && blockIdx.x == 0) {
     st->overflow = 0;
     st->n_tiles = 0;
@@ -914,12 +917,18 @@ __global__ __launch_bounds__(256) void k_leaf_offset(LeafRec* __restrict__ leaf,
     if (f0 + q < F) leaf[f0 + q].offset += add;
 }
 
-// Per-word prefix counts of internal-node child masks: one wave per node.
-__global__ __launch_bounds__(256) void k_node_prefix(const uint64_t* __restrict__ mask, uint16_t* __restrict__ pre,
-                                                     int64_t nodes, int words) {
+// Per-word prefix counts of internal-node child masks: one wave per node, lower nodes (64
+// words) in the first nbl workgroups and upper nodes (512 words) after them.
+__global__ __launch_bounds__(256) void k_node_prefix(const uint64_t* __restrict__ lmask, uint16_t* __restrict__ lpre,
+                                                     int64_t nl, int64_t nbl, const uint64_t* __restrict__ umask,
+                                                     uint16_t* __restrict__ upre, int64_t nu) {
   const int lane = lane_id();
-  const int64_t node = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (node >= nodes) return;
+  const bool lower = (int64_t)blockIdx.x < nbl;
+  const int64_t node = (lower ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - nbl) * 4 + (threadIdx.x >> 6);
+  const int words = lower ? 64 : 512;
+  if (node >= (lower ? nl : nu)) return;
+  const uint64_t* mask = lower ? lmask : umask;
+  uint16_t* pre = lower ? lpre : upre;
   uint32_t base = 0;
   for (int w0 = 0; w0 < words; w0 += 64) {
     const uint32_t c = (uint32_t)__popcll(mask[node * words + w0 + lane]);
@@ -1028,12 +1037,11 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   }
   uint64_t* root_keys = nullptr;
   for (int attempt = 0;; ++attempt) {
-    k_init_state<<<1, 1, 0, s>>>(st);
-    IGC_HIP(hipGetLastError(), "igc_grid_build: init launch");
     rc = dev_alloc((void**)&root_keys, cap * 12, s, "igc_grid_build: root table");
     if (rc) return rc;
     g->root_keys = root_keys;
-    if ((rc = fill_u64(root_keys, (int64_t)cap, kEmptyKey, s))) return rc;
+    k_init_root<<<grid_for((int64_t)cap, 256, 4096), 256, 0, s>>>(st, root_keys, (int64_t)cap);
+    IGC_HIP(hipGetLastError(), "igc_grid_build: init launch");
     const uint32_t limit = (uint32_t)std::min<uint64_t>(cap, 4096);
     const int nbt = grid_for((n_in + 3) / 4, 256, kTileBlocks);
     k_tile_insert<<<nbt, 256, 0, s>>>(d_ijk, n_in, root_keys, (uint32_t)(cap - 1), limit, partial, st);
@@ -1192,10 +1200,10 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
     k_leaf_offset<<<(unsigned)groups, 256, 0, s>>>(g->leaf, F, gsum);
     IGC_HIP(hipGetLastError(), "igc_grid_build: leaf offset launch");
   }
-  k_node_prefix<<<(unsigned)((Lw + 3) / 4), 256, 0, s>>>(g->lower_mask, g->lower_pre, Lw, 64);
-  IGC_HIP(hipGetLastError(), "igc_grid_build: lower prefix launch");
-  k_node_prefix<<<(unsigned)((U + 3) / 4), 256, 0, s>>>(g->upper_mask, g->upper_pre, U, 512);
-  IGC_HIP(hipGetLastError(), "igc_grid_build: upper prefix launch");
+  const int64_t nbl = (Lw + 3) / 4;
+  k_node_prefix<<<(unsigned)(nbl + (U + 3) / 4), 256, 0, s>>>(g->lower_mask, g->lower_pre, Lw, nbl, g->upper_mask,
+                                                             g->upper_pre, U);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: node prefix launch");
   k_leaf_neighbors<<<grid_for(F * 27, 256, 8192), 256, 0, s>>>(g->view(), g->leaf_nbr);
   IGC_HIP(hipGetLastError(), "igc_grid_build: leaf neighbour launch");
   // Last read-back: the voxel count.
