@@ -236,7 +236,7 @@ def main() -> int:
         "kernel_map_gbs": round(kmap_bytes / (np.mean(t_kmap) * 1e-3) / 1e9, 1),
         "kernel_map_hbm_frac": round(kmap_bytes / (np.mean(t_kmap) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "conv_hbm_frac": round(conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "host_syncs_per_step": 2,
+        "host_syncs_per_step": 3,
     }
 
     if args.backward:
