@@ -296,8 +296,7 @@ int igc_sparse_conv_backward(const igc_grid* g, const int32_t* d_map, const void
   if (d_dw && !wgrad_supported(dtype, cin, cout))
     return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv_backward: weight gradient does not support this dtype / cin / cout");
   if (g->n_voxels == 0) {
-    if (d_dw) IGC_HIP(hipMemsetAsync(d_dw, 0, (size_t)27 * cin * cout * 4, (hipStream_t)stream),
-                      "igc_sparse_conv_backward: clear weight gradient");
+    if (d_dw) return fill_u32((uint32_t*)d_dw, (int64_t)27 * cin * cout, 0u, (hipStream_t)stream);
     return IGC_OK;
   }
   return launch_conv_backward(g, d_map, d_feats, dtype, cin, d_w, cout, d_dout, d_dfeats, d_dw, p, (hipStream_t)stream);

@@ -378,7 +378,19 @@ int launch_wgrad_f32(const igc_grid* g, const int32_t* d_map, const void* d_feat
   return rc;
 }
 
+__global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) p[e] = v;
+}
+
 }  // namespace
+
+int fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
+  if (n <= 0) return IGC_OK;
+  const int64_t b = (n + 255) / 256;
+  k_fill_u32<<<(unsigned)(b < 2048 ? b : 2048), 256, 0, s>>>(p, n, v);
+  IGC_HIP(hipGetLastError(), "fill kernel launch");
+  return IGC_OK;
+}
 
 bool wgrad_supported(int32_t dtype, int32_t cin, int32_t cout) {
   if (dtype == IGC_BF16) return cin >= 32 && cin % 32 == 0 && cin <= 1024 && cout >= 64 && cout % 64 == 0 && cout <= 1024;

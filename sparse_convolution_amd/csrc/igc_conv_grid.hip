@@ -200,7 +200,12 @@ int build_conv_grid(const igc_grid* in, const int32_t* stride, int32_t transpose
   int32_t* ijk = (int32_t*)ws;
   int32_t* cand = (int32_t*)(ws + ijk_bytes);
   uint32_t* flag = (uint32_t*)(ws + ijk_bytes + cand_bytes);
-  hipError_t e = hipMemsetAsync(flag, 0, 4, s);
+  rc = fill_u32(flag, 1, 0u, s);
+  hipError_t e = hipSuccess;
+  if (rc) {
+    dev_free(ws, s);
+    return rc;
+  }
   Stride3 st{{stride[0], stride[1], stride[2]}};
   if (e == hipSuccess && transposed) {
     rc = launch_active_ijk(in, ijk, s);

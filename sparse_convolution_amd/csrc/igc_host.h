@@ -101,6 +101,8 @@ int conv_grid_slots(const int32_t* stride, int32_t transposed, int* n);
 int build_conv_grid(const igc_grid* in, const int32_t* stride, int32_t transposed, hipStream_t s, igc_grid* out);
 int launch_conv_map(const igc_grid* in, const igc_grid* out, const int32_t* stride, int32_t transposed,
                     int32_t* d_map, hipStream_t s);
+// Fills n 32-bit words with v on stream s (a kernel, so it can sit in captured work).
+int fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 bool wgrad_supported(int32_t dtype, int32_t cin, int32_t cout);
 int launch_conv_backward(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype, int32_t cin,
                          const void* d_w, int32_t cout, const void* d_dout, void* d_dfeats, float* d_dw,
