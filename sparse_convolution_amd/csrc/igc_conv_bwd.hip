@@ -64,23 +64,26 @@ struct WgradSplit {
 };
 
 // Partial dW blocks of MB input x NB output channels per (offset, chunk of tiles), bf16 data.
-// Four waves in 2 x 2, each (MB/2) x (NB/2) with 16x16x32 MFMAs. The stages (64 rows of a
+// NWV waves in 2 x (NWV/2), each (MB/2) x (NB/(NWV/2)) with 16x16x32 MFMAs. The stages (64 rows of a
 // tile that hold at least one pair at the offset) are software-pipelined through registers:
 // while the MFMAs consume stage i from LDS, the thread's loads for the next stages are in
 // flight - the input and output-gradient rows of stage i+1, the source rows (kernel map) of
 // stage i+2 and the row order of stage i+3. Thread tid stages rows 2 (tid % 32) and
-// 2 (tid % 32) + 1 of a stage, for the 8-channel granules tid / 32 + 8 j.
-template <int MB, int NB>
-__global__ __launch_bounds__(256) void k_wgrad_bf16(const int32_t* __restrict__ map, int64_t N,
+// 2 (tid % 32) + 1 of a stage, for the 8-channel granules tid / 32 + (NT / 32) j.
+template <int MB, int NB, int NWV>
+__global__ __launch_bounds__(64 * NWV) void k_wgrad_bf16(const int32_t* __restrict__ map, int64_t N,
                                                     const int32_t* __restrict__ perm,
                                                     const uint16_t* __restrict__ blk,
                                                     const uint16_t* __restrict__ feats,
                                                     const uint16_t* __restrict__ dout, int cin, int cout,
                                                     int64_t n_tiles, int64_t tiles_per_chunk, WgradSplit sp,
                                                     float* __restrict__ part) {
-  constexpr int MI = MB / 32, NI = NB / 32;  // 16-blocks per wave
+  constexpr int NT = 64 * NWV;               // threads
+  constexpr int WNW = NWV / 2;               // waves along the output channels
+  constexpr int MI = MB / 32, NI = NB / WNW / 16;  // 16-blocks per wave
+  constexpr int GS = NT / 32;                // granule step of a thread's staging items
   constexpr int XG = MB / 8, DG = NB / 8;    // 8-channel granules of a row
-  constexpr int XI = (32 * XG + 255) / 256, DI = (32 * DG + 255) / 256;  // staging items per thread
+  constexpr int XI = (32 * XG + NT - 1) / NT, DI = (32 * DG + NT - 1) / NT;  // staging items per thread
   static_assert(MI >= 1 && NI >= 1, "block shape");
   __shared__ __attribute__((aligned(16))) uint16_t s_xt[MB * kLdT];  // [channel][row]
   __shared__ __attribute__((aligned(16))) uint16_t s_dt[NB * kLdT];
@@ -88,7 +91,7 @@ __global__ __launch_bounds__(256) void k_wgrad_bf16(const int32_t* __restrict__ 
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNW, wn = wave % WNW;
   const int pr = tid & 31;
   int o, mb, nb;
   int64_t chunk;
@@ -130,15 +133,15 @@ __global__ __launch_bounds__(256) void k_wgrad_bf16(const int32_t* __restrict__ 
   auto load_data = [&](int32_t r0, int32_t r1, int32_t s0, int32_t s1) {
 #pragma unroll
     for (int j = 0; j < XI; ++j) {
-      const int g = (tid >> 5) + 8 * j;
-      const bool ok = 32 * XG >= 256 || g < XG;
+      const int g = (tid >> 5) + GS * j;
+      const bool ok = 32 * XG >= NT || g < XG;
       xa[j] = ok && s0 >= 0 ? *(const uint4*)(feats + (size_t)s0 * cin + c0 + g * 8) : make_uint4(0, 0, 0, 0);
       xb[j] = ok && s1 >= 0 ? *(const uint4*)(feats + (size_t)s1 * cin + c0 + g * 8) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < DI; ++j) {
-      const int g = (tid >> 5) + 8 * j;
-      const bool ok = 32 * DG >= 256 || g < DG;
+      const int g = (tid >> 5) + GS * j;
+      const bool ok = 32 * DG >= NT || g < DG;
       da[j] = ok && s0 >= 0 ? *(const uint4*)(dout + (size_t)r0 * cout + n0 + g * 8) : make_uint4(0, 0, 0, 0);
       db[j] = ok && s1 >= 0 ? *(const uint4*)(dout + (size_t)r1 * cout + n0 + g * 8) : make_uint4(0, 0, 0, 0);
     }
@@ -180,13 +183,13 @@ __global__ __launch_bounds__(256) void k_wgrad_bf16(const int32_t* __restrict__ 
     __syncthreads();  // the previous stage's LDS reads are done
 #pragma unroll
     for (int j = 0; j < XI; ++j) {
-      const int g = (tid >> 5) + 8 * j;
-      if (32 * XG >= 256 || g < XG) store_pair(s_xt, g, xa[j], xb[j]);
+      const int g = (tid >> 5) + GS * j;
+      if (32 * XG >= NT || g < XG) store_pair(s_xt, g, xa[j], xb[j]);
     }
 #pragma unroll
     for (int j = 0; j < DI; ++j) {
-      const int g = (tid >> 5) + 8 * j;
-      if (32 * DG >= 256 || g < DG) store_pair(s_dt, g, da[j], db[j]);
+      const int g = (tid >> 5) + GS * j;
+      if (32 * DG >= NT || g < DG) store_pair(s_dt, g, da[j], db[j]);
     }
     // Loads for the next stages.
     load_data(m_r0, m_r1, m_s0, m_s1);
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(256) void k_wgrad_bf16(const int32_t* __restrict__ 
         a[mi] = *(const bf16x8*)&s_xt[(wm * (MB / 2) + mi * 16 + frow) * kLdT + ks + fk];
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        b[ni] = *(const bf16x8*)&s_dt[(wn * (NB / 2) + ni * 16 + frow) * kLdT + ks + fk];
+        b[ni] = *(const bf16x8*)&s_dt[(wn * (NB / WNW) + ni * 16 + frow) * kLdT + ks + fk];
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(256) void k_wgrad_bf16(const int32_t* __restrict__ 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int m = c0 + wm * (MB / 2) + mi * 16 + (lane >> 4) * 4 + j;
-        const int n = n0 + wn * (NB / 2) + ni * 16 + frow;
+        const int n = n0 + wn * (NB / WNW) + ni * 16 + frow;
         dst[(size_t)m * cout + n] = acc[mi][ni][j];
       }
 }
@@ -311,7 +314,7 @@ int launch_wgrad_reduce(const float* part, int64_t chunks, int64_t E, float* dw,
   return IGC_OK;
 }
 
-template <int MB, int NB>
+template <int MB, int NB, int NWV>
 int launch_wgrad_bf16(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t cin,
                       const void* d_dout, int32_t cout, float* d_dw, hipStream_t s) {
   const int64_t N = g->n_voxels;
@@ -339,7 +342,7 @@ int launch_wgrad_bf16(const igc_grid* g, const int32_t* d_map, const void* d_fea
   rc = launch_ggs_plan(d_map, N, perm, blk, s);
   hipError_t e = hipSuccess;
   if (rc == IGC_OK) {
-    k_wgrad_bf16<MB, NB><<<(unsigned)(kNOff * chunks * sp.mblocks * sp.nblocks), 256, 0, s>>>(
+    k_wgrad_bf16<MB, NB, NWV><<<(unsigned)(kNOff * chunks * sp.mblocks * sp.nblocks), 64 * NWV, 0, s>>>(
         d_map, N, perm, blk, (const uint16_t*)d_feats, (const uint16_t*)d_dout, cin, cout, n_tiles, tpc, sp, part);
     e = hipGetLastError();
     if (e != hipSuccess) rc = hip_status(e, "igc_sparse_conv_backward: wgrad launch");
@@ -422,9 +425,12 @@ int launch_conv_backward(const igc_grid* g, const int32_t* d_map, const void* d_
   }
   if (d_dw) {
     if (dtype == IGC_BF16) {
-      if (cin % 128 == 0 && cout % 128 == 0) return launch_wgrad_bf16<128, 128>(g, d_map, d_feats, cin, d_dout, cout, d_dw, s);
-      if (cin % 64 == 0) return launch_wgrad_bf16<64, 64>(g, d_map, d_feats, cin, d_dout, cout, d_dw, s);
-      return launch_wgrad_bf16<32, 64>(g, d_map, d_feats, cin, d_dout, cout, d_dw, s);
+      // 128 x 256 blocks on 8 waves (85 FLOP per staged byte instead of 64) measured slower on
+      // the large workload (222 ms against 214): staging is not bound by the L2 feed.
+      if (cin % 128 == 0 && cout % 128 == 0)
+        return launch_wgrad_bf16<128, 128, 4>(g, d_map, d_feats, cin, d_dout, cout, d_dw, s);
+      if (cin % 64 == 0) return launch_wgrad_bf16<64, 64, 4>(g, d_map, d_feats, cin, d_dout, cout, d_dw, s);
+      return launch_wgrad_bf16<32, 64, 4>(g, d_map, d_feats, cin, d_dout, cout, d_dw, s);
     }
     return launch_wgrad_f32(g, d_map, d_feats, cin, d_dout, cout, d_dw, s);
   }
