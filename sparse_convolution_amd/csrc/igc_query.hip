@@ -22,6 +22,7 @@ namespace {
 
 constexpr int kMaxOffsets = 256;
 constexpr int64_t kMapGroups = 1280;  // workgroups of the persistent kernel-map form (5 per CU)
+constexpr uint32_t kVoxelMajor = 128;  // leaves with at most this many voxels take the voxel-major stores
 
 struct OffsetList {
   int8_t d[kMaxOffsets][3];
@@ -220,6 +221,23 @@ __global__ __launch_bounds__(256) void k_kernel_map_window(GridView g, OffsetLis
 
     const uint64_t base = s_off[wave][13];
     if (base + count > (uint64_t)N) count = base < (uint64_t)N ? (uint32_t)(N - base) : 0u;
+    if (count <= kVoxelMajor) {
+      // Sparse leaf: lane t takes voxel t (and t + 64) for every offset, 4-byte stores that are
+      // contiguous over the lanes - fewer instructions than the quads for a short leaf.
+      for (uint32_t t = lane; t < count; t += 64) {
+        const int cell = s_cell[wave][t];
+        int32_t* dst = map + base + t;
+        uint32_t bits = 0;
+        for (int o = 0; o < off.K; ++o) {
+          const int idx = s_idx[wave][cell + s_delta[o]];
+          if (idx >= 0 && o < 32) bits |= 1u << o;
+          dst[(size_t)o * (size_t)N] = idx;
+        }
+        if (nbmask) nbmask[base + t] = bits;
+      }
+      wave_sync();
+      continue;
+    }
     // A row of the leaf spans at most (count + 6) / 4 quads; rows shorter than the wave share
     // it: lanes [G r, G r + G) take row ob + r, with G the smallest power of two that holds
     // the row's quads.
