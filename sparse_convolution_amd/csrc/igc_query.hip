@@ -134,151 +134,196 @@ __global__ __launch_bounds__(256) void k_kernel_map(GridView g, OffsetList off, 
   }
 }
 
-// Unit-stencil form (every offset within one voxel per axis). Waves are persistent: wave w
-// of the grid walks leaves w, w + W, ... (W waves in all), and while it answers one leaf, the
-// neighbour-table entries and leaf records of the next one are already on their way into
-// registers of lanes 0..26. Each wave owns its LDS slice (no workgroup barriers). Per leaf
-// the wave fills a 10^3 window of row indices (cell (x+1, y+1, z+1) for leaf-local x, y, z in
-// [-1, 8], -1 where there is no voxel) once from the 27 records, so a pair is one LDS read.
-// Offset o's rows of the leaf, map[o, base .. base + count), are written in 16-byte quads
-// aligned in memory (the quad grid of a row is shifted by (o N + base) mod 4); only the two
-// edge quads of a row, which the neighbouring leaves share, are written element by element.
-__global__ __launch_bounds__(256) void k_kernel_map_window(GridView g, OffsetList off, int32_t* __restrict__ map,
-                                                           uint32_t* __restrict__ nbmask) {
-  __shared__ uint64_t s_mask[4][27][8];
-  __shared__ uint64_t s_off[4][27];
-  __shared__ uint64_t s_pre[4][27];
+// Standard-stencil form (the 27 offsets in the order o = (dx+1)*9 + (dy+1)*3 + (dz+1)). Waves
+// are persistent: wave w of an XCD walks leaves b + w, b + w + W, ... of the XCD's range (W
+// waves on the XCD), and while it answers one leaf, the neighbour-table entries and leaf
+// records of the next one are already on their way into registers of lanes 0..26. Each wave
+// owns its LDS slice (no workgroup barriers). Per leaf the wave fills a 10^3 window of row
+// indices (cell (x+1)*100 + (y+1)*10 + (z+1) for leaf-local x, y, z in [-1, 8], -1 where there
+// is no voxel) once from the 27 records, so a pair is one LDS read at a constant offset from the
+// voxel's cell. The reads of a phase are all issued before their results are used, which keeps
+// the per-leaf chain of LDS round trips short, and the per-leaf vector work is kept small
+// (32-bit mask arithmetic, offsets folded into the LDS instructions, store addresses as a
+// uniform row pointer plus a 32-bit lane offset). Leaves of at most kVoxelMajor voxels are
+// written voxel-major (lane = voxel, 4-byte stores contiguous over the lanes). Fuller leaves
+// write offset o's row, map[o, base .. base + count), as 16-byte quads aligned in memory
+// (lane = quad; the quad grid of a row is shifted by (o N + base) mod 4), and the at most
+// three elements before the first and after the last whole quad of each row, shared with the
+// neighbouring leaves' rows, 64 (row, element) pairs to a 4-byte store.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRecWords = 20;  // a leaf record in LDS as 32-bit words: masks 0..15, offset 16-17, prefix 18-19
+
+// Window-cell distance of offset o of the standard stencil from cell (0, 0, 0) of the voxel's
+// 3x3x3 neighbourhood: the neighbour of the voxel in cell c is cell c - 111 + win_off(o).
+__host__ __device__ constexpr int win_off(int o) { return 100 * (o / 9) + 10 * ((o / 3) % 3) + o % 3; }
+
+// Window column (y, z) = (p / 10 - 1, p % 10 - 1) for the ten x = -1 .. 8: row index or -1.
+// rec holds the 27 records of the leaf's 3x3x3 block (zero records where a leaf is absent).
+// Rows fit in 32 bits, so the records' offsets are used by their low words.
+__device__ __forceinline__ void window_column(const uint32_t (*rec)[kRecWords], int p, int32_t* __restrict__ col) {
+  const int y = p / 10 - 1, z = p % 10 - 1;
+  const int syz = ((y >> 3) + 1) * 3 + ((z >> 3) + 1);
+  const uint32_t b = ((uint32_t)(y & 7) << 3) | (uint32_t)(z & 7);  // bit of (y, z) in a mask word
+  const uint32_t bit = 1u << (b & 31u), below = bit - 1u;
+  const bool high = b >= 32u;
+  const uint32_t tlo = high ? 0u : bit, thi = high ? bit : 0u;       // the bit, by half word
+  const uint32_t mlo = high ? ~0u : below, mhi = high ? below : 0u;  // the bits below it
+  const uint32_t* A = rec[syz];       // x = -1: mask word 7 of the leaf below in x
+  const uint32_t* B = rec[9 + syz];   // x = 0 .. 7
+  const uint32_t* C = rec[18 + syz];  // x = 8: mask word 0 of the leaf above in x
+  const uint32_t a_lo = A[14], a_hi = A[15], a_off = A[16], a_pre = A[19];
+  const uint32_t c_lo = C[0], c_hi = C[1], c_off = C[16];
+  const uint32_t b_off = B[16], p_lo = B[18], p_hi = B[19];
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = B[i];
+  auto cell = [&](uint32_t lo, uint32_t hi, uint32_t first) -> int32_t {
+    const bool on = ((lo & tlo) | (hi & thi)) != 0u;
+    return on ? (int32_t)(first + (uint32_t)__popc(lo & mlo) + (uint32_t)__popc(hi & mhi)) : -1;
+  };
+  // Prefix of mask word q (q >= 1): 9-bit field q - 1 of the 64-bit prefix word.
+  auto pre = [&](int q) -> uint32_t {
+    const int sh = 9 * (q - 1);
+    if (sh + 9 <= 32) return (p_lo >> sh) & 511u;
+    if (sh >= 32) return (p_hi >> (sh - 32)) & 511u;
+    return ((p_lo >> sh) | (p_hi << (32 - sh))) & 511u;
+  };
+  col[0] = cell(a_lo, a_hi, a_off + ((a_pre >> 22) & 511u));  // field 6 = bits 54..62
+  col[100] = cell(w[0], w[1], b_off);
+#pragma unroll
+  for (int q = 1; q < 8; ++q) col[100 * (1 + q)] = cell(w[2 * q], w[2 * q + 1], b_off + pre(q));
+  col[900] = cell(c_lo, c_hi, c_off);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_kernel_map_window(
+    GridView g, int32_t* __restrict__ map, uint32_t* __restrict__ nbmask) {
+  __shared__ __align__(16) uint32_t s_rec[4][27][kRecWords];
   __shared__ int32_t s_idx[4][1000];
   __shared__ uint16_t s_cell[4][512];
-  __shared__ int16_t s_delta[kMaxOffsets];  // window-cell offset of each stencil offset
-  for (int o = threadIdx.x; o < off.K; o += blockDim.x)
-    s_delta[o] = (int16_t)(off.d[o][0] * 100 + off.d[o][1] * 10 + off.d[o][2]);
-  __syncthreads();
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  const int64_t W = (int64_t)gridDim.x * 4;
   const int64_t F = g.n_leaf, N = g.n_voxels;
-  int64_t f = (int64_t)blockIdx.x * 4 + wave;
+  // Workgroups go to the eight XCDs in turn (workgroup b to XCD b mod 8); each XCD takes one
+  // contiguous range of leaves, in proportion to its waves, so the map rows of neighbouring
+  // leaves - which share their edge cache lines - are written through the same L2.
+  const int64_t G = gridDim.x, x = blockIdx.x & 7, q = G >> 3, rem = G & 7;
+  const int64_t before = x * q + (x < rem ? x : rem), mine = q + (x < rem ? 1 : 0);
+  const int64_t f_end = F * (before + mine) / G;
+  const int64_t W = 4 * mine;  // waves of this XCD
+  int64_t f = F * before / G + (int64_t)(blockIdx.x >> 3) * 4 + wave;
 
-  // Lanes 0..26: the records of the leaf to answer next (m, ro, rp) and the neighbour-table
-  // entry of the one after it (nb).
-  uint64_t m0 = 0, m1 = 0, m2 = 0, m3 = 0, m4 = 0, m5 = 0, m6 = 0, m7 = 0, ro = 0, rp = 0;
-#define IGC_LOAD_REC(nl_)                                                                   \
-  {                                                                                         \
-    const int32_t nl__ = (nl_);                                                             \
-    const bool ok__ = lane < 27 && nl__ >= 0;                                               \
-    const LeafRec* L__ = g.leaf + (ok__ ? nl__ : 0);                                        \
-    m0 = ok__ ? L__->mask[0] : 0ull; m1 = ok__ ? L__->mask[1] : 0ull;                       \
-    m2 = ok__ ? L__->mask[2] : 0ull; m3 = ok__ ? L__->mask[3] : 0ull;                       \
-    m4 = ok__ ? L__->mask[4] : 0ull; m5 = ok__ ? L__->mask[5] : 0ull;                       \
-    m6 = ok__ ? L__->mask[6] : 0ull; m7 = ok__ ? L__->mask[7] : 0ull;                       \
-    ro = ok__ ? L__->offset : 0ull; rp = ok__ ? L__->prefix : 0ull;                         \
+  // Lanes 0..26: the record of neighbour slot `lane` of the leaf to answer next, as five
+  // 16-byte parts (r0..r4; stored as zeros when the slot has no leaf), and the neighbour-table
+  // entry of the leaf after it (nb).
+  u32x4 r0 = {0, 0, 0, 0}, r1 = r0, r2 = r0, r3 = r0, r4 = r0;
+  bool rok = false;
+#define IGC_LOAD_REC(nl_)                                                 \
+  {                                                                       \
+    const int32_t nl__ = (nl_);                                           \
+    rok = nl__ >= 0;                                                      \
+    if (lane < 27) {                                                      \
+      const u32x4* p__ = (const u32x4*)(g.leaf + (nl__ >= 0 ? nl__ : 0)); \
+      r0 = p__[0]; r1 = p__[1]; r2 = p__[2]; r3 = p__[3]; r4 = p__[4];    \
+    }                                                                     \
   }
-  auto load_nb = [&](int64_t leaf) -> int32_t { return lane < 27 && leaf < F ? g.leaf_nbr[leaf * 27 + lane] : -1; };
+  auto load_nb = [&](int64_t leaf) -> int32_t { return lane < 27 && leaf < f_end ? g.leaf_nbr[leaf * 27 + lane] : -1; };
   IGC_LOAD_REC(load_nb(f));
   int32_t nb = load_nb(f + W);
 
-  for (; f < F; f += W) {
-    if (lane < 27) {
-      uint64_t* sm = s_mask[wave][lane];
-      sm[0] = m0; sm[1] = m1; sm[2] = m2; sm[3] = m3; sm[4] = m4; sm[5] = m5; sm[6] = m6; sm[7] = m7;
-      s_off[wave][lane] = ro;
-      s_pre[wave][lane] = rp;
+  for (; f < f_end; f += W) {
+    // The lane number through an opaque copy: values derived from it are recomputed per leaf
+    // instead of being kept live (or spilled) across the loop.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    if (ln < 27) {
+      u32x4* d = (u32x4*)s_rec[wave][ln];
+      const u32x4 z = {0, 0, 0, 0};
+      d[0] = rok ? r0 : z; d[1] = rok ? r1 : z; d[2] = rok ? r2 : z; d[3] = rok ? r3 : z; d[4] = rok ? r4 : z;
     }
     IGC_LOAD_REC(nb);  // the next leaf's records, in flight while this one is answered
     nb = load_nb(f + 2 * W);
     wave_sync();
 
-    // Window cells of the active voxels in row order, and the window of row indices.
+    // Window cells of the active voxels in row order (mbcnt: set bits of the word below the lane).
+    const uint32_t* own = s_rec[wave][13];
+    uint32_t mw[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mw[i] = own[i];
+    const uint32_t base = own[16];
     uint32_t count = 0;
-    const uint64_t lt = (1ull << lane) - 1ull;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-      const uint64_t word = s_mask[wave][13][w];
-      if ((word >> lane) & 1ull)
-        s_cell[wave][count + (uint32_t)__popcll(word & lt)] = (uint16_t)(w * 100 + (lane >> 3) * 10 + (lane & 7) + 111);
-      count += (uint32_t)__popcll(word);
+      const uint32_t lo = mw[2 * w], hi = mw[2 * w + 1];
+      const uint32_t rank = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, count));
+      if ((((uint64_t)hi << 32 | lo) >> ln) & 1ull)
+        s_cell[wave][rank] = (uint16_t)(w * 100 + (ln >> 3) * 10 + (ln & 7) + 111);
+      count += (uint32_t)__popc(lo) + (uint32_t)__popc(hi);
     }
-    // Lane p < 100 takes the window column (y, z) = (p / 10 - 1, p % 10 - 1) for all ten x.
-    for (int p = lane; p < 100; p += 64) {
-      const int y = p / 10 - 1, z = p % 10 - 1;
-      const int syz = ((y >> 3) + 1) * 3 + ((z >> 3) + 1);
-      const uint64_t bit = 1ull << ((uint32_t)((y & 7) << 3) | (uint32_t)(z & 7));
-#pragma unroll
-      for (int xi = 0; xi < 10; ++xi) {
-        const int slot = (xi == 0 ? 0 : xi == 9 ? 18 : 9) + syz;
-        const uint32_t q = (uint32_t)((xi + 7) & 7);  // x & 7 for x = xi - 1
-        const uint64_t word = s_mask[wave][slot][q];
-        int32_t idx = -1;
-        if (word & bit) {
-          const uint32_t pre = q ? (uint32_t)(s_pre[wave][slot] >> (9u * (q - 1u))) & 511u : 0u;
-          idx = (int32_t)(s_off[wave][slot] + pre + (uint32_t)__popcll(word & (bit - 1ull)));
-        }
-        s_idx[wave][xi * 100 + p] = idx;
-      }
-    }
+    // The window, one column (ten cells along x) per lane and pass.
+#pragma unroll 1
+    for (int p = ln; p < 100; p += 64) window_column(s_rec[wave], p, &s_idx[wave][p]);
     wave_sync();
 
-    const uint64_t base = s_off[wave][13];
-    if (base + count > (uint64_t)N) count = base < (uint64_t)N ? (uint32_t)(N - base) : 0u;
+    if ((uint64_t)base + count > (uint64_t)N) count = (uint64_t)base < (uint64_t)N ? (uint32_t)(N - base) : 0u;
     if (count <= kVoxelMajor) {
-      // Sparse leaf: lane t takes voxel t (and t + 64) for every offset, 4-byte stores that are
-      // contiguous over the lanes - fewer instructions than the quads for a short leaf.
-      for (uint32_t t = lane; t < count; t += 64) {
-        const int cell = s_cell[wave][t];
-        int32_t* dst = map + base + t;
-        uint32_t bits = 0;
-        for (int o = 0; o < off.K; ++o) {
-          const int idx = s_idx[wave][cell + s_delta[o]];
-          if (idx >= 0 && o < 32) bits |= 1u << o;
-          dst[(size_t)o * (size_t)N] = idx;
+      // Lane t takes voxel t (and t + 64) for every offset: 27 LDS reads in flight, then 27
+      // stores that are contiguous over the lanes.
+      for (uint32_t t = ln; t < count; t += 64) {
+        const int32_t* nbh = &s_idx[wave][s_cell[wave][t] - 111];
+        int32_t v[27];
+#pragma unroll
+        for (int o = 0; o < 27; ++o) v[o] = nbh[win_off(o)];
+#pragma unroll
+        for (int o = 0; o < 27; ++o) (map + (size_t)o * (size_t)N + base)[t] = v[o];
+        if (nbmask) {
+          uint32_t bits = 0;
+#pragma unroll
+          for (int o = 0; o < 27; ++o) bits |= (v[o] >= 0 ? 1u : 0u) << o;
+          nbmask[base + t] = bits;
         }
-        if (nbmask) nbmask[base + t] = bits;
       }
       wave_sync();
       continue;
     }
-    // A row of the leaf spans at most (count + 6) / 4 quads; rows shorter than the wave share
-    // it: lanes [G r, G r + G) take row ob + r, with G the smallest power of two that holds
-    // the row's quads.
-    const uint32_t nqm = (count + 6u) >> 2;
-    uint32_t G = 1;
-    while (G < nqm && G < 64u) G <<= 1;
-    const int R = 64 / (int)G;
-    const int sub = lane / (int)G;
-    const uint32_t k0 = (uint32_t)lane & (G - 1u);
-    for (int ob = 0; ob < off.K; ob += R) {
-      const int o = ob + sub;
-      if (o >= off.K) break;
-      const int delta = s_delta[o];
-      const uint64_t g0 = (uint64_t)o * (uint64_t)N + base;  // element of (o, base)
-      const uint64_t q0 = g0 & ~3ull;                         // first 16-byte aligned quad
-      const uint32_t nq = (uint32_t)((g0 + count + 3 - q0) >> 2);
-      for (uint32_t k = k0; k < nq; k += G) {
-        const uint64_t e0 = q0 + 4ull * k;
-        int v[4];
-        bool in[4];
+    // Rows: map[o, base .. base + count) starts at element g0 = o N + base, s = g0 mod 4; its
+    // first hd = (4 - s) mod 4 elements precede a 16-byte boundary, then fq whole quads.
+    const uint32_t n4 = (uint32_t)N & 3u, s0 = base & 3u;
+#pragma unroll 1
+    for (int ox = 0; ox < 3; ++ox) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t t = (int64_t)(e0 + e) - (int64_t)g0;  // voxel of this element
-          in[e] = t >= 0 && t < (int64_t)count;
-          v[e] = in[e] ? s_idx[wave][s_cell[wave][t] + delta] : 0;
-        }
-        if (in[0] && in[3]) {
-          *(int4*)(map + e0) = make_int4(v[0], v[1], v[2], v[3]);
-        } else {
+      for (int r = 0; r < 9; ++r) {
+        const int o = 9 * ox + r;
+        const uint32_t s = (s0 + (uint32_t)o * n4) & 3u;
+        const uint32_t hd = (4u - s) & 3u;
+        const uint32_t fq = ((s + count) >> 2) - (s ? 1u : 0u);
+        int32_t* rowp = map + (size_t)o * (size_t)N + base + hd;  // 16-byte aligned
+        for (uint32_t k = ln; k < fq; k += 64) {
+          const uint32_t t0 = hd + 4u * k;
+          int32_t v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (in[e]) map[e0 + e] = v[e];
+          for (int e = 0; e < 4; ++e) v[e] = s_idx[wave][(int)s_cell[wave][t0 + e] - 111 + 100 * ox + win_off(r)];
+          *(i32x4*)(rowp + 4u * k) = i32x4{v[0], v[1], v[2], v[3]};
         }
       }
     }
+    // The elements outside the whole quads: voxel c (c < 3) of the row's head, voxel
+    // count - 6 + c (c >= 3) of its tail; pair p = 6 o + c.
+    for (uint32_t p = ln; p < 162u; p += 64) {
+      const uint32_t o = p / 6u, c = p - 6u * o;
+      const uint32_t s = (s0 + o * n4) & 3u;
+      const uint32_t hd = (4u - s) & 3u;
+      const uint32_t fq = ((s + count) >> 2) - (s ? 1u : 0u);
+      const uint32_t t = c < 3u ? c : count - 6u + c;
+      if (c < 3u ? t < hd : t >= hd + 4u * fq)
+        (map + (size_t)o * (size_t)N + base)[t] = s_idx[wave][(int)s_cell[wave][t] - 111 + win_off((int)o)];
+    }
     if (nbmask) {
-      for (uint32_t t = lane; t < count; t += 64) {
-        const int cell = s_cell[wave][t];
+      for (uint32_t t = ln; t < count; t += 64) {
+        const int32_t* nbh = &s_idx[wave][s_cell[wave][t] - 111];
         uint32_t bits = 0;
-        for (int o = 0; o < off.K && o < 32; ++o)
-          if (s_idx[wave][cell + s_delta[o]] >= 0) bits |= 1u << o;
+#pragma unroll
+        for (int o = 0; o < 27; ++o) bits |= (nbh[win_off(o)] >= 0 ? 1u : 0u) << o;
         nbmask[base + t] = bits;
       }
     }
@@ -316,12 +361,13 @@ int launch_kernel_map(const igc_grid* g, const int32_t* h_offsets, int32_t K, in
   off.K = K;
   for (int o = 0; o < K; ++o)
     for (int a = 0; a < 3; ++a) off.d[o][a] = (int8_t)h_offsets[3 * o + a];
-  bool unit = true;
-  for (int a = 0; a < 3 * K; ++a) unit = unit && h_offsets[a] >= -1 && h_offsets[a] <= 1;
+  bool standard = K == 27;
+  for (int o = 0; o < K && standard; ++o)
+    standard = h_offsets[3 * o] == o / 9 - 1 && h_offsets[3 * o + 1] == (o / 3) % 3 - 1 && h_offsets[3 * o + 2] == o % 3 - 1;
   // The window form stores 16-byte quads: it needs a 16-byte aligned map.
-  if (unit && ((uintptr_t)d_map & 15u) == 0)
-    k_kernel_map_window<<<(unsigned)std::min<int64_t>((g->n_leaf + 3) / 4, kMapGroups), 256, 0, s>>>(g->view(), off,
-                                                                                                   d_map, d_nbmask);
+  if (standard && ((uintptr_t)d_map & 15u) == 0)
+    k_kernel_map_window<<<(unsigned)std::min<int64_t>((g->n_leaf + 3) / 4, kMapGroups), 256, 0, s>>>(g->view(), d_map,
+                                                                                                   d_nbmask);
   else
     k_kernel_map<<<(unsigned)((g->n_leaf + 3) / 4), 256, 0, s>>>(g->view(), off, d_map, d_nbmask);
   IGC_HIP(hipGetLastError(), "igc_kernel_map: launch");

@@ -115,6 +115,29 @@ def test_general_offsets():
     check_grid(c, "offsets up to 8", offsets=off8)
 
 
+def test_unit_stencil_forms():
+    """The standard 27-offset order takes the window kernel; a permuted or partial unit stencil
+    and an output buffer that is not 16-byte aligned take the per-pair kernel. All must agree
+    with the oracle."""
+    igc = _igc()
+    from sparse_convolution_amd import _lib, _ptr, _stream, _STD_OFFSETS_PTR
+    c = workloads.make_coords("lidar")
+    std = oracle.standard_offsets()
+    rng = np.random.default_rng(21)
+    perm = np.ascontiguousarray(std[rng.permutation(27)])
+    seven = np.array([[0, 0, 0], [1, 0, 0], [-1, 0, 0], [0, 1, 0], [0, -1, 0], [0, 0, 1], [0, 0, -1]], np.int32)
+    g, ref = check_grid(c, "lidar permuted stencil", offsets=perm)
+    check_grid(c, "lidar 7-point stencil", offsets=seven)
+    say("kernel map into a buffer offset by one element")
+    N = g.n_voxels
+    buf = torch.full((27 * N + 8,), 7, dtype=torch.int32, device="cuda")
+    out = buf[1:1 + 27 * N].view(27, N)
+    _lib.check(_lib.load().igc_kernel_map(g.handle, _STD_OFFSETS_PTR, 27, _ptr(out), None, _stream(g.device)))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), ref.kernel_map(None))
+    assert int(buf[0]) == 7 and bool((buf[1 + 27 * N:] == 7).all())
+
+
 def test_capacity_retry(monkeypatch):
     monkeypatch.setenv("IGC_TEST_INITIAL_CAPACITY", "1")
     rng = np.random.default_rng(13)
