@@ -113,10 +113,11 @@ typedef struct {
  * n_in == 0 gives an empty grid) - fVDB notes, "GPU-accelerated IndexGrid build": root
  * tile keys, radix sort of per-tile 64-bit keys, run-length encoding, upper / lower / leaf
  * counts, allocation, top-down registration of nodes and leaf bit masks.
- * Host synchronisations: two (tile count, then node counts, to size allocations). If the
- * root hash table overflows its first capacity the step repeats with a larger one
- * (DriveRT, dynamic sizes). Errors: IGC_ERR_INVALID_ARG (out null, d_ijk null with
- * n_in > 0, n_in < 0), IGC_ERR_RANGE (n_in > 2^31-1), IGC_ERR_OOM, IGC_ERR_HIP,
+ * Host synchronisations: three - the root tile count and varying key bits (to plan the
+ * sort), the node counts (to size the topology), and the voxel count N (reported by
+ * igc_grid_info). If the root hash table overflows its first capacity the first step
+ * repeats with a larger one (DriveRT, dynamic sizes). Errors: IGC_ERR_INVALID_ARG (out
+ * null, d_ijk null with n_in > 0, n_in < 0), IGC_ERR_RANGE (n_in > 2^31-1), IGC_ERR_OOM, IGC_ERR_HIP,
  * IGC_ERR_CAPACITY, IGC_ERR_INTERNAL. On success *out owns device memory until
  * igc_grid_destroy. d_ijk may be freed once the stream reaches the end of the call. */
 int igc_grid_build(const int32_t* d_ijk, int64_t n_in, igc_stream stream, igc_grid** out);
