@@ -42,8 +42,10 @@ HBM_PEAK_GBS = 8000.0
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}  # dense MFMA peaks of MI355X
 CONV_SRC = {"leaf": "sparse_convolution_amd/csrc/igc_conv_leaf.hip",
             "ggs": "sparse_convolution_amd/csrc/igc_conv_ggs.hip"}
-CONV_KERNEL = {"leaf": "k_conv_leaf_f32", "ggs": "k_conv_ggs_bf16"}
-DEFAULT_STEPS = {"tiny": (50, 5), "leaf": (20, 3), "band": (10, 2), "lidar": (20, 3), "large": (3, 1)}
+CONV_KERNEL = {("leaf", "f32"): "k_conv_leaf_f32", ("leaf", "bf16"): "k_conv_leaf_bf16",
+               ("ggs", "bf16"): "k_conv_ggs_bf16"}
+DEFAULT_STEPS = {"tiny": (50, 5), "leaf": (20, 3), "band": (10, 2), "lidar": (20, 3), "large": (3, 1),
+                 "band32": (10, 2)}
 
 
 def _sha(path: str) -> str:
@@ -51,10 +53,10 @@ def _sha(path: str) -> str:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
-def _traffic(path_name: str, workload: str):
+def _traffic(path_name: str, dtype: str, workload: str):
     """Measured HBM bytes per launch of the conv kernel, if the committed counter summary was
     taken on the current kernel source; None otherwise."""
-    f = os.path.join(ROOT, "profiles", f"traffic_{CONV_KERNEL[path_name]}_{workload}.json")
+    f = os.path.join(ROOT, "profiles", f"traffic_{CONV_KERNEL[(path_name, dtype)]}_{workload}.json")
     if not os.path.exists(f):
         return None
     with open(f) as fh:
@@ -125,7 +127,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="leaf", choices=["tiny", "leaf", "band", "lidar", "large"])
+    ap.add_argument("--workload", default="leaf", choices=["tiny", "leaf", "band", "lidar", "large", "band32"])
     ap.add_argument("--path", default="auto", choices=["auto", "leaf", "ggs"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -215,8 +217,8 @@ def main() -> int:
     conv_tflops = flops / (conv_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
     roofline = {"bound": "mfma", "achieved": round(conv_tflops, 3), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(conv_tflops / peak, 4), "traffic": _traffic(path, args.workload),
-                "kernel": CONV_KERNEL[path], "flops_per_launch": flops,
+                "frac": round(conv_tflops / peak, 4), "traffic": _traffic(path, wl.dtype, args.workload),
+                "kernel": CONV_KERNEL[(path, wl.dtype)], "flops_per_launch": flops,
                 "avg_launch_ms": round(conv_ms, 4)}
 
     # Phase-level HBM view (algorithmic bytes; see the design notes for the per-unit figures).

@@ -160,7 +160,9 @@ int igc_kernel_map(const igc_grid* grid, const int32_t* h_offsets, int32_t K, in
  * IGC_PATH_GGS and ignored by IGC_PATH_LEAF; with IGC_PATH_AUTO it is required whenever the
  * choice (see igc_select_path) is GGS. Supported combinations:
  *     LEAF: dtype F32, (cin, cout) in {(4,8), (4,16), (4,32), (8,8), (8,16), (8,32),
- *           (16,16), (8,4), (16,4), (16,8)}
+ *           (16,16), (8,4), (16,4), (16,8)};
+ *           dtype BF16 (the leaf window of the pages' brick backend: a dense bf16 10^3 halo
+ *           per leaf), cin in {16, 32}, cout in {16, 32, 64}
  *     GGS : dtype BF16, cin a multiple of 32 up to 1024, cout a multiple of 64 up to 1024
  * Anything else returns IGC_ERR_UNSUPPORTED. d_out must not alias d_feats. */
 int igc_sparse_conv(const igc_grid* grid, const int32_t* d_map, const void* d_feats, int32_t dtype,
@@ -178,8 +180,8 @@ int igc_sparse_conv(const igc_grid* grid, const int32_t* d_map, const void* d_fe
  * d_map (int32[27, N], standard offsets) is required. The input gradient is the forward
  * convolution of d_dout with W~[o] = W[26 - o]^T (the map is symmetric under offset negation),
  * so it runs on the path igc_select_path picks for (dtype, cout, cin) unless `path` forces one;
- * that shape must be supported (see igc_sparse_conv; the leaf path also takes 8 -> 4, 16 -> 4,
- * 16 -> 8). The weight gradient supports BF16 with cin a multiple of 32 and cout a multiple of
+ * that shape must be supported (see igc_sparse_conv; the fp32 leaf path also takes 8 -> 4,
+ * 16 -> 4, 16 -> 8). The weight gradient supports BF16 with cin a multiple of 32 and cout a multiple of
  * 64 (up to 1024), and F32 with cin, cout <= 64 and cin * cout <= 1024. Anything else returns
  * IGC_ERR_UNSUPPORTED. Outputs must not alias inputs. */
 int igc_sparse_conv_backward(const igc_grid* grid, const int32_t* d_map, const void* d_feats, int32_t dtype,

@@ -575,6 +575,164 @@ int launch_leaf(const igc_grid* g, const void* d_feats, const void* d_w, void* d
   return IGC_OK;
 }
 
+// ---------------------------------------------------------------- bf16 leaf window ("brick")
+//
+// fVDB notes, "accelerated operators for sparse convolution": the brick backend densifies small
+// output windows with their halo and runs a dense convolution on the tensor cores, for feature
+// depths of 32 to 64 at high neighbour occupancy. gfx950 form: the window is a whole leaf's
+// 10^3 halo in LDS as bf16 (2 KB per channel: 32 KB for 16 channels, 64 KB for 32), zeros where
+// inactive; the M dimension of v_mfma_f32_16x16x32_bf16 is the leaf's active voxels 16 at a
+// time (inactive outputs of the window are not computed), K = 27 offsets x CIN, N = COUT in
+// 16-column blocks, fp32 accumulation, bf16 output (round to nearest even).
+
+__device__ __forceinline__ uint16_t bf16_out_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));  // inf / nan
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// wt[n][k] = W[k][n] for k = o CIN + ci < 27 CIN, zero up to the padded K (a multiple of 32): a
+// lane's B fragment (8 consecutive k of one column) is one 16-byte load.
+template <int CIN, int COUT>
+__global__ void k_leaf_wt_bf16(const uint16_t* __restrict__ w, uint16_t* __restrict__ wt) {
+  constexpr int KP = (27 * CIN + 31) / 32 * 32;
+  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < COUT * KP; e += gridDim.x * blockDim.x) {
+    const int n = e / KP, k = e % KP;
+    wt[e] = k < 27 * CIN ? w[(size_t)k * COUT + n] : (uint16_t)0;
+  }
+}
+
+// 16-byte granule g of window cell c sits at granule g ^ bf16_swz<GPC>(c): eight consecutive
+// cells (one 128-byte LDS row's worth of fragment reads) then fall on distinct banks.
+template <int GPC>
+__device__ __forceinline__ int bf16_swz(int c) {
+  return (c / (8 / GPC)) & (GPC - 1);
+}
+
+// One workgroup per leaf. Wave w takes column block w % NS and the row blocks w / NS, w / NS +
+// 4 / NS, ...; its B fragments (W^T, one per k-step) stay in registers, and each k-step is one
+// 16-byte window read and one MFMA. K runs in steps of 32: lane group kg = lane / 16 holds k =
+// 32 q + 8 kg .. + 7, i.e. one offset's 8 channels; k past 27 CIN (CIN 16: the second half of
+// the last step) reads offset 0's cell against zero W.
+template <int CIN, int COUT>
+__global__ __launch_bounds__(256) void k_conv_leaf_bf16(GridView g, const uint16_t* __restrict__ feats,
+                                                        const uint16_t* __restrict__ wt, uint16_t* __restrict__ out) {
+  static_assert(CIN == 16 || CIN == 32, "window cells of two or four 16-byte granules");
+  static_assert(COUT == 16 || COUT == 32 || COUT == 64, "column blocks per wave");
+  constexpr int NS = COUT / 16;
+  constexpr int KP = (27 * CIN + 31) / 32 * 32;
+  constexpr int NCH = KP / 32;
+  constexpr int GPC = CIN / 8;
+  constexpr int RSTEP = 4 / NS;
+  __shared__ uint4 s_win[1000 * GPC];
+  __shared__ uint64_t s_mask[27][8];
+  __shared__ uint64_t s_off[27];
+  __shared__ uint64_t s_pre[27];
+  __shared__ uint16_t s_pos[512];
+  __shared__ uint32_t s_count;
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const int rl = lane & 15;  // A row / B column / D column
+  const int kg = lane >> 4;  // k group of A and B, row group of D
+  const int ns = wave % NS;
+  const int64_t f = xcd_block(blockIdx.x, gridDim.x);
+
+  // B fragments of this wave's column block (in flight while the leaf records arrive).
+  bf16x8 wb[NCH];
+  const uint16_t* wrow = wt + (size_t)(ns * 16 + rl) * KP + kg * 8;
+#pragma unroll
+  for (int q = 0; q < NCH; ++q) wb[q] = *(const bf16x8*)(wrow + q * 32);
+  // k-step q, lane group kg: offset q and granule kg (CIN 32), or offset 2 q + kg / 2 and
+  // granule kg % 2 (CIN 16).
+  const int gran = CIN == 32 ? kg : (kg & 1);
+  const int ohalf = CIN == 32 ? 0 : (kg >> 1);
+  load_leaf_block(g, f, tid, s_mask, s_off, s_pre);
+  __syncthreads();
+
+  // Compacted active positions (wave 0) and the window (all threads; every feature load of a
+  // thread is issued before the first LDS store).
+  if (wave == 0) compact_leaf(lane, s_mask, s_pos, &s_count);
+  constexpr int CPT = (1000 + 255) / 256;
+  uint4 v[CPT][GPC];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + 256 * i;
+    const int x = c / 100 - 1, y = (c / 10) % 10 - 1, z = c % 10 - 1;  // leaf-local, in [-1, 8]
+    const int slot = ((x >> 3) + 1) * 9 + ((y >> 3) + 1) * 3 + ((z >> 3) + 1);
+    const uint32_t q = (uint32_t)(x & 7);
+    const uint64_t bit = 1ull << ((uint32_t)((y & 7) << 3) | (uint32_t)(z & 7));
+    const uint64_t word = c < 1000 ? s_mask[slot][q] : 0ull;
+    if (word & bit) {
+      const uint32_t pre = q ? (uint32_t)(s_pre[slot] >> (9u * (q - 1u))) & 511u : 0u;
+      const uint64_t row = s_off[slot] + pre + (uint32_t)__popcll(word & (bit - 1ull));
+      const uint4* src = (const uint4*)(feats + row * CIN);
+#pragma unroll
+      for (int j = 0; j < GPC; ++j) v[i][j] = src[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < GPC; ++j) v[i][j] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + 256 * i;
+    if (c < 1000) {
+#pragma unroll
+      for (int j = 0; j < GPC; ++j) s_win[c * GPC + (j ^ bf16_swz<GPC>(c))] = v[i][j];
+    }
+  }
+  __syncthreads();
+
+  const uint32_t count = s_count;
+  const uint64_t base = s_off[13];
+  for (uint32_t rb = (uint32_t)(wave / NS); rb * 16 < count; rb += RSTEP) {
+    const uint32_t t = rb * 16 + rl;
+    const uint32_t p = s_pos[t < count ? t : 0];
+    const int cell0 = (int)((p >> 6) * 100 + ((p >> 3) & 7u) * 10 + (p & 7u));  // cell of offset (-1,-1,-1)
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      int dc;
+      if constexpr (CIN == 32) {
+        dc = cell_delta(q);
+      } else {
+        const int o0 = 2 * q, o1 = 2 * q + 1 < 27 ? 2 * q + 1 : 0;
+        dc = ohalf ? cell_delta(o1) : cell_delta(o0);
+      }
+      const int c = cell0 + dc;
+      const bf16x8 a = __builtin_bit_cast(bf16x8, s_win[c * GPC + (gran ^ bf16_swz<GPC>(c))]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wb[q], acc, 0, 0, 0);
+    }
+    // D: lane holds column lane%16 of rows 4*(lane/16) + j.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t r = rb * 16 + (uint32_t)kg * 4 + j;
+      if (r < count) out[(base + r) * COUT + ns * 16 + rl] = bf16_out_rne(acc[j]);
+    }
+  }
+}
+
+template <int CIN, int COUT>
+int launch_leaf_bf16(const igc_grid* g, const void* d_feats, const void* d_w, void* d_out, hipStream_t s) {
+  constexpr int KP = (27 * CIN + 31) / 32 * 32;
+  uint16_t* wt = nullptr;
+  int rc = dev_alloc((void**)&wt, (size_t)COUT * KP * 2, s, "igc_sparse_conv: leaf W transpose");
+  if (rc) return rc;
+  k_leaf_wt_bf16<CIN, COUT><<<(COUT * KP + 255) / 256, 256, 0, s>>>((const uint16_t*)d_w, wt);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) {
+    k_conv_leaf_bf16<CIN, COUT><<<(unsigned)g->n_leaf, 256, 0, s>>>(g->view(), (const uint16_t*)d_feats, wt,
+                                                                   (uint16_t*)d_out);
+    e = hipGetLastError();
+  }
+  dev_free(wt, s);
+  if (e != hipSuccess) return hip_status(e, "igc_sparse_conv: bf16 leaf launch");
+  return IGC_OK;
+}
+
 template <int CIN, int COUT>
 int launch_wgrad_leaf_t(const igc_grid* g, const void* d_feats, const void* d_dout, float* part, int64_t groups,
                         hipStream_t s) {
@@ -588,6 +746,14 @@ int launch_wgrad_leaf_t(const igc_grid* g, const void* d_feats, const void* d_do
 }  // namespace
 
 bool leaf_conv_supported(int32_t dtype, int32_t cin, int32_t cout) {
+  if (dtype == IGC_BF16) {
+    switch (cin * 1000 + cout) {
+      case 16016: case 16032: case 16064: case 32016: case 32032: case 32064:
+        return true;
+      default:
+        return false;
+    }
+  }
   if (dtype != IGC_F32) return false;
   switch (cin * 1000 + cout) {
     case 4008: case 4016: case 4032: case 8008: case 8016: case 8032: case 16016:
@@ -600,7 +766,17 @@ bool leaf_conv_supported(int32_t dtype, int32_t cin, int32_t cout) {
 
 int launch_conv_leaf(const igc_grid* g, const void* d_feats, int32_t dtype, int32_t cin, const void* d_w,
                      int32_t cout, void* d_out, hipStream_t s) {
-  (void)dtype;
+  if (dtype == IGC_BF16) {
+    switch (cin * 1000 + cout) {
+      case 16016: return launch_leaf_bf16<16, 16>(g, d_feats, d_w, d_out, s);
+      case 16032: return launch_leaf_bf16<16, 32>(g, d_feats, d_w, d_out, s);
+      case 16064: return launch_leaf_bf16<16, 64>(g, d_feats, d_w, d_out, s);
+      case 32016: return launch_leaf_bf16<32, 16>(g, d_feats, d_w, d_out, s);
+      case 32032: return launch_leaf_bf16<32, 32>(g, d_feats, d_w, d_out, s);
+      case 32064: return launch_leaf_bf16<32, 64>(g, d_feats, d_w, d_out, s);
+      default: return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: bf16 leaf path shape");
+    }
+  }
   switch (cin * 1000 + cout) {
     case 4008: return launch_leaf<4, 8>(g, d_feats, d_w, d_out, s);
     case 4016: return launch_leaf<4, 16>(g, d_feats, d_w, d_out, s);

@@ -99,6 +99,14 @@ def test_fp32_leaf_shapes(cin, cout):
     run_backward(c, cin, cout, torch.float32, "leaf", "clusters", seed=cin * 5 + cout)
 
 
+@pytest.mark.parametrize("cin,cout", [(16, 16), (16, 32), (32, 16), (32, 32)])
+def test_bf16_leaf_input_gradient_shapes(cin, cout):
+    # dgrad runs cout -> cin on the bf16 leaf window; the bf16 weight gradient needs cout >= 64.
+    c = _cluster_coords(4, 20, 200, seed=cin * 41 + cout)
+    run_backward(c, cin, cout, torch.bfloat16, "leaf", "clusters", seed=cin * 3 + cout, std=1.0 / np.sqrt(27 * cin),
+                 need_dweights=False)
+
+
 @pytest.mark.parametrize("cin,cout", [(4, 32), (8, 32), (4, 4), (8, 4)])
 def test_fp32_leaf_weight_gradient_only_shapes(cin, cout):
     # The input gradient of these runs cout -> cin, not a leaf-path shape.

@@ -1,5 +1,5 @@
-"""GPU parity of the submanifold convolution (leaf path, fp32; gather-GEMM-scatter path,
-bf16 with fp32 accumulation) against the float64 CPU oracle.
+"""GPU parity of the submanifold convolution (leaf path: fp32 and bf16 windows;
+gather-GEMM-scatter path: bf16; both with fp32 accumulation) against the float64 CPU oracle.
 
 Tolerances (normwise, max|y - r| / max|r| over the output): 1e-5 for fp32 and 2e-2 for bf16,
 where the oracle reads exactly the bf16 values the GPU reads. Both paths must run: the
@@ -84,6 +84,21 @@ def test_ggs_path_shapes(cin, cout):
     run_conv(c, cin, cout, torch.bfloat16, "ggs", "clusters", seed=cin * 3 + cout, std=1.0 / np.sqrt(27 * cin))
 
 
+@pytest.mark.parametrize("cin,cout", [(16, 16), (16, 32), (16, 64), (32, 16), (32, 32), (32, 64)])
+def test_leaf_path_bf16_shapes(cin, cout):
+    # The bf16 leaf window (brick) path: dense clusters and a sparse shell in one grid.
+    c = np.concatenate([_cluster_coords(4, 20, 200, seed=cin * 11 + cout, fill=0.6),
+                        workloads.make_coords("tiny") + 700])
+    run_conv(c, cin, cout, torch.bfloat16, "leaf", "clusters+shell", seed=cin * 13 + cout,
+             std=1.0 / np.sqrt(27 * cin))
+
+
+def test_leaf_workload_bf16_sampled():
+    w = workloads.WORKLOADS["leaf"]
+    run_conv(workloads.make_coords("leaf"), 32, 32, torch.bfloat16, "leaf", "leaf bf16 32->32", seed=w.index,
+             std=1.0 / np.sqrt(27 * 32), sample_rows=1 << 16)
+
+
 def test_tiny_workload_leaf():
     w = workloads.WORKLOADS["tiny"]
     run_conv(workloads.make_coords("tiny"), w.cin, w.cout, torch.float32, "leaf", "tiny", seed=w.index)
@@ -121,6 +136,10 @@ def test_identity_kernel_both_paths():
     w16 = torch.zeros(27, 64, 64, device="cuda", dtype=torch.bfloat16)
     w16[13] = torch.eye(64, device="cuda", dtype=torch.bfloat16)
     assert torch.equal(igc.sparse_conv(g, f16, w16, kmap=m, path="ggs"), f16)
+    fb = torch.randn(g.n_voxels, 32, device="cuda").bfloat16()
+    wb = torch.zeros(27, 32, 32, device="cuda", dtype=torch.bfloat16)
+    wb[13] = torch.eye(32, device="cuda", dtype=torch.bfloat16)
+    assert torch.equal(igc.sparse_conv(g, fb, wb, path="leaf"), fb)
 
 
 def test_path_selection_and_errors():
@@ -128,6 +147,7 @@ def test_path_selection_and_errors():
     g = igc.grid_build(to_dev(workloads.make_coords("tiny")))
     assert g.select_path(torch.float32, 8, 8) == "leaf"
     assert g.select_path(torch.bfloat16, 64, 64) == "ggs"
+    assert g.select_path(torch.bfloat16, 32, 32) == "leaf"  # the only bf16 path below 64 outputs
     f = torch.randn(g.n_voxels, 8, device="cuda")
     w = torch.randn(27, 8, 8, device="cuda")
     with pytest.raises(igc.IgcError):

@@ -69,6 +69,10 @@ WORKLOADS = {
                       "64-beam x 2048-azimuth scan of ground + 150 boxes at 0.1 m, 5 frames, bf16 128->128"),
     "large": Workload(5, "large", 128, 256, "bf16", _std(128),
                       "50M signed coords (~10% duplicates) from a band generator over [-2048,2048)^3, bf16 128->256"),
+    # The band geometry at feature depth 32, the regime of the pages' brick backend (depths 32-64,
+    # narrow bands); coordinates are those of "band", features and weights its own.
+    "band32": Workload(6, "band32", 32, 32, "bf16", _std(32),
+                       "the band geometry (workload 3) at bf16 32->32, the brick-backend regime"),
 }
 
 
@@ -336,6 +340,8 @@ def make_coords(name: str) -> np.ndarray:
         c = boxes_coords(w.index)
     elif name == "band":
         c = band_coords(w.index)
+    elif name == "band32":
+        return make_coords("band")
     elif name == "lidar":
         c = lidar_coords(w.index)
     elif name == "large":
