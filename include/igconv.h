@@ -118,8 +118,10 @@ typedef struct {
  * igc_grid_info). If the root hash table overflows its first capacity the first step
  * repeats with a larger one (DriveRT, dynamic sizes). Errors: IGC_ERR_INVALID_ARG (out
  * null, d_ijk null with n_in > 0, n_in < 0), IGC_ERR_RANGE (n_in > 2^31-1), IGC_ERR_OOM, IGC_ERR_HIP,
- * IGC_ERR_CAPACITY, IGC_ERR_INTERNAL. On success *out owns device memory until
- * igc_grid_destroy. d_ijk may be freed once the stream reaches the end of the call. */
+ * IGC_ERR_CAPACITY, IGC_ERR_INTERNAL. On success *out owns one device allocation until
+ * igc_grid_destroy. Temporaries come from a workspace block that the library keeps per device
+ * and reuses across calls (grown to the largest request; a call that finds it in use allocates
+ * its own). d_ijk may be freed once the stream reaches the end of the call. */
 int igc_grid_build(const int32_t* d_ijk, int64_t n_in, igc_stream stream, igc_grid** out);
 
 /* Frees the grid (waits for its stream first). NULL is accepted. */

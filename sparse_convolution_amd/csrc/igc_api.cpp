@@ -2,6 +2,7 @@
 // and dispatch to the HIP kernels. Every check runs on the host before any launch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -19,6 +20,16 @@ std::mutex g_pool_mutex;
 std::vector<int> g_pool_ready;
 thread_local void* g_staging = nullptr;
 thread_local size_t g_staging_bytes = 0;
+
+// The per-device cached workspace block (see Workspace).
+struct WsSlot {
+  void* p = nullptr;
+  size_t bytes = 0;
+  bool busy = false;
+  hipEvent_t released = nullptr;  // recorded on the last user's stream at release
+};
+std::mutex g_ws_mutex;
+std::vector<WsSlot> g_ws;
 }  // namespace
 
 int set_error(int status, const std::string& msg) {
@@ -67,6 +78,59 @@ void dev_free(void* p, hipStream_t s) {
   if (p) (void)hipFreeAsync(p, s);
 }
 
+int ws_acquire(Workspace* w, size_t bytes, hipStream_t s, const char* what) {
+  *w = Workspace{};
+  int dev = 0;
+  IGC_HIP(hipGetDevice(&dev), what);
+  prepare_pool(dev);
+  if (bytes == 0) bytes = 256;
+  {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+    WsSlot& sl = g_ws[dev];
+    if (!sl.busy) {
+      if (sl.released) IGC_HIP(hipStreamWaitEvent(s, sl.released, 0), what);
+      if (sl.bytes < bytes) {
+        if (sl.p) (void)hipFreeAsync(sl.p, s);
+        sl.p = nullptr;
+        sl.bytes = 0;
+        const size_t want = std::max(bytes, align_up(bytes + bytes / 4, 1 << 20));
+        if (hipMallocAsync(&sl.p, want, s) == hipSuccess) {
+          sl.bytes = want;
+        } else {
+          sl.p = nullptr;
+          (void)hipGetLastError();
+        }
+      }
+      if (sl.p) {
+        sl.busy = true;
+        w->p = sl.p;
+        w->bytes = sl.bytes;
+        w->dev = dev;
+        w->cached = true;
+        return IGC_OK;
+      }
+    }
+  }
+  w->dev = dev;
+  w->bytes = bytes;
+  return dev_alloc(&w->p, bytes, s, what);
+}
+
+void ws_release(Workspace* w, hipStream_t s) {
+  if (!w->p) return;
+  if (!w->cached) {
+    dev_free(w->p, s);
+  } else {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    WsSlot& sl = g_ws[w->dev];
+    if (!sl.released) (void)hipEventCreateWithFlags(&sl.released, hipEventDisableTiming);
+    if (sl.released) (void)hipEventRecord(sl.released, s);
+    sl.busy = false;
+  }
+  *w = Workspace{};
+}
+
 void* host_staging(size_t bytes) {
   if (g_staging_bytes < bytes) {
     if (g_staging) (void)hipHostFree(g_staging);
@@ -80,8 +144,7 @@ void* host_staging(size_t bytes) {
 
 static void free_grid(igc_grid* g) {
   if (!g) return;
-  dev_free(g->block, g->stream);
-  dev_free(g->root_keys, g->stream);  // root values live in the same allocation
+  dev_free(g->block, g->stream);  // the root table lives in the same allocation
   delete g;
 }
 

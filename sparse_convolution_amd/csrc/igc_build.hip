@@ -74,6 +74,16 @@ struct BuildState {
 
 // ------------------------------------------------------------------------------ utilities
 
+// Zeroes fill[0 .. nfill) and copies src[0 .. ncopy) to dst (one launch for both).
+__global__ void k_fill_copy_u64(uint64_t* __restrict__ fill, int64_t nfill, uint64_t* __restrict__ dst,
+                                const uint64_t* __restrict__ src, int64_t ncopy) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nfill + ncopy;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    if (e < nfill) fill[e] = 0ull;
+    else dst[e - nfill] = src[e - nfill];
+  }
+}
+
 __global__ void k_fill_u64(uint64_t* __restrict__ p, int64_t n, uint64_t v) {
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x)
     p[e] = v;
@@ -963,19 +973,26 @@ __global__ __launch_bounds__(256) void k_leaf_neighbors(GridView g, int32_t* __r
 
 // ------------------------------------------------------------------------------ host side
 
-// One stream-ordered allocation holds every temporary of a build (the host pays for each
-// allocator call while the device waits on it after a read-back); released on every exit path.
+// One workspace block holds every temporary of a build (the host pays for each allocator
+// call while the device waits on it after a read-back; the block is reused across builds);
+// released on every exit path.
 struct Arena {
   hipStream_t s;
+  Workspace ws;
   char* base = nullptr;
   size_t used = 0, cap = 0;
   std::vector<void*> extra;  // rare oversized pieces
   explicit Arena(hipStream_t st) : s(st) {}
   ~Arena() {
     for (void* p : extra) dev_free(p, s);
-    dev_free(base, s);
+    ws_release(&ws, s);
   }
-  int reserve(size_t bytes) { return dev_alloc((void**)&base, cap = bytes, s, "igc_grid_build: workspace"); }
+  int reserve(size_t bytes) {
+    const int rc = ws_acquire(&ws, bytes, s, "igc_grid_build: workspace");
+    base = (char*)ws.p;
+    cap = bytes;
+    return rc;
+  }
   template <class T>
   T* take(size_t bytes) {
     T* p = (T*)(base + used);
@@ -997,15 +1014,27 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   g->n_input = n_in;
   if (n_in == 0) return IGC_OK;
 
-  // Workspace sizes depend on n_in only (the tile lists of more than kSmallSort tiles are
-  // allocated on their own once U is known).
+  // Root table (keys, then upper-node rows): first capacity from an estimate, then the size
+  // that always suffices (U <= n_in) - the capacity retry. It is built in the workspace and
+  // copied into the grid's block once the block is allocated.
+  uint64_t full_cap = 16;
+  while (full_cap < 2ull * (uint64_t)n_in) full_cap <<= 1;
+  uint64_t cap = std::min<uint64_t>(full_cap, 1ull << 16);
+  if (const char* e = std::getenv("IGC_TEST_INITIAL_CAPACITY")) {
+    const uint64_t want = std::strtoull(e, nullptr, 10);
+    cap = 1;
+    while (cap < want) cap <<= 1;
+  }
+
+  // Workspace sizes depend on n_in only (the tile lists of more than kSmallSort tiles, and a
+  // root table grown by the retry, are allocated on their own).
   const int64_t tiles = (n_in + kTileKeys - 1) / kTileKeys;
   const int64_t sort_tiles = (n_in + kSortTile - 1) / kSortTile;
   const size_t ws = align_up(sizeof(BuildState), 256) + align_up((size_t)kTileBlocks * 32, 256) +
                     align_up(2 * kMaxPasses * kMaxBins * 4, 256) + align_up((size_t)kHistBlocks * kHistWidth * 4, 256) +
                     2 * align_up((size_t)n_in * 8, 256) + 2 * align_up((size_t)sort_tiles * kMaxBins * 4, 256) +
                     align_up((size_t)tiles * 8, 256) + align_up((size_t)tiles * 32, 256) +
-                    2 * align_up((size_t)kSmallSort * 8, 256);
+                    2 * align_up((size_t)kSmallSort * 8, 256) + align_up((size_t)cap * 12, 256);
   Arena ar(s);
   int rc = ar.reserve(ws);
   if (rc) return rc;
@@ -1021,25 +1050,12 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   uint64_t* bprefix = ar.take<uint64_t>((size_t)tiles * 32);
   uint64_t* tile_list = ar.take<uint64_t>((size_t)kSmallSort * 8);
   uint64_t* tile_tmp = ar.take<uint64_t>((size_t)kSmallSort * 8);
-  if (!tile_tmp) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: workspace layout");
+  uint64_t* root_keys = ar.take<uint64_t>((size_t)cap * 12);
+  if (!root_keys) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: workspace layout");
   BuildState* h = (BuildState*)host_staging(sizeof(BuildState));
   if (!h) return set_error(IGC_ERR_OOM, "igc_grid_build: pinned staging buffer");
 
-  // Root table (keys, then upper-node rows): first capacity from an estimate, then the size
-  // that always suffices (U <= n_in) - the capacity retry.
-  uint64_t full_cap = 16;
-  while (full_cap < 2ull * (uint64_t)n_in) full_cap <<= 1;
-  uint64_t cap = std::min<uint64_t>(full_cap, 1ull << 16);
-  if (const char* e = std::getenv("IGC_TEST_INITIAL_CAPACITY")) {
-    const uint64_t want = std::strtoull(e, nullptr, 10);
-    cap = 1;
-    while (cap < want) cap <<= 1;
-  }
-  uint64_t* root_keys = nullptr;
   for (int attempt = 0;; ++attempt) {
-    rc = dev_alloc((void**)&root_keys, cap * 12, s, "igc_grid_build: root table");
-    if (rc) return rc;
-    g->root_keys = root_keys;
     k_init_root<<<grid_for((int64_t)cap, 256, 4096), 256, 0, s>>>(st, root_keys, (int64_t)cap);
     IGC_HIP(hipGetLastError(), "igc_grid_build: init launch");
     const uint32_t limit = (uint32_t)std::min<uint64_t>(cap, 4096);
@@ -1051,16 +1067,12 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
     IGC_HIP(hipMemcpyAsync(h, st, sizeof(BuildState), hipMemcpyDeviceToHost, s), "igc_grid_build: read tile count");
     IGC_HIP(hipStreamSynchronize(s), "igc_grid_build: tile pass");
     if (!h->overflow) break;
-    dev_free(root_keys, s);
-    root_keys = nullptr;
-    g->root_keys = nullptr;
     if (cap >= full_cap || attempt >= 2)
       return set_error(IGC_ERR_CAPACITY, "igc_grid_build: root table overflow after retries");
     cap = full_cap;
+    if ((rc = ar.get_extra(&root_keys, cap * 12, "igc_grid_build: root table"))) return rc;
   }
   int32_t* root_vals = (int32_t*)(root_keys + cap);
-  g->root_vals = root_vals;
-  g->root_cap = (uint32_t)cap;
   const int64_t U = h->n_tiles;
   const uint64_t off_var = h->off_or ^ h->off_and;
   const uint64_t key_var = h->key_or ^ h->key_and;
@@ -1161,11 +1173,14 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   const size_t o_upm = carve(U * 512 * 8), o_lom = carve(Lw * 64 * 8), o_leaf = carve(F * sizeof(LeafRec)),
                zero_end = off, o_root_list = carve(U * 8), o_upo = carve(U * 16), o_upp = carve(U * 512 * 2),
                o_upf = carve(U * 4), o_loo = carve(Lw * 16), o_lop = carve(Lw * 64 * 2), o_lof = carve(Lw * 4),
-               o_lfo = carve(F * 16), o_nbr = carve(F * 27 * 4);
+               o_lfo = carve(F * 16), o_nbr = carve(F * 27 * 4), o_root = carve(cap * 12);
   char* blk = nullptr;
   if ((rc = dev_alloc((void**)&blk, off, s, "igc_grid_build: topology"))) return rc;
   g->block = blk;
-  g->bytes = off + cap * 12;
+  g->bytes = off;
+  g->root_keys = (uint64_t*)(blk + o_root);
+  g->root_vals = (int32_t*)(g->root_keys + cap);
+  g->root_cap = (uint32_t)cap;
   g->root_list = (uint64_t*)(blk + o_root_list);
   g->upper_origin = (int4*)(blk + o_upo);
   g->upper_mask = (uint64_t*)(blk + o_upm);
@@ -1182,7 +1197,11 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   g->n_lower = Lw;
   g->n_upper = U;
   g->sort_passes = ps.passes;
-  if ((rc = fill_u64((uint64_t*)blk, (int64_t)(zero_end / 8), 0, s))) return rc;
+  // cap * 12 bytes rounded up to whole words: both root-table regions are padded to 256 bytes.
+  const int64_t root_words = (int64_t)((cap * 12 + 7) / 8);
+  k_fill_copy_u64<<<grid_for((int64_t)(zero_end / 8) + root_words, 256, 4096), 256, 0, s>>>(
+      (uint64_t*)blk, (int64_t)(zero_end / 8), g->root_keys, root_keys, root_words);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: topology initialisation launch");
 
   Topo t{F,           Lw,           U,          &st->guard,     tiles_sorted,
          g->root_list, g->upper_origin, g->upper_mask, g->upper_first, g->lower_origin, g->lower_mask,

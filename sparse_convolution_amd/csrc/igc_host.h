@@ -75,6 +75,21 @@ void dev_free(void* p, hipStream_t s);
 // Pinned host staging buffer of at least `bytes` for small device -> host reads.
 void* host_staging(size_t bytes);
 
+// Temporary device workspace of one call. Each device keeps one block that is handed to one
+// call at a time and grows to the largest request (a call that finds it taken allocates its
+// own). A stream-ordered allocation and free cost tens of microseconds of host time per
+// call; the block makes the common case free of both. On release an event is recorded on the
+// caller's stream, and the next user's stream waits for it, so work still reading the block
+// finishes first.
+struct Workspace {
+  void* p = nullptr;
+  size_t bytes = 0;
+  int dev = -1;
+  bool cached = false;
+};
+int ws_acquire(Workspace* w, size_t bytes, hipStream_t s, const char* what);
+void ws_release(Workspace* w, hipStream_t s);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Launchers (defined in the .hip files).
