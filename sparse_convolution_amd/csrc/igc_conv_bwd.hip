@@ -333,9 +333,10 @@ int launch_wgrad_bf16(const igc_grid* g, const int32_t* d_map, const void* d_fea
   const size_t perm_bytes = align_up((size_t)n_tiles * kTileRows * 4, 256);
   const size_t blk_bytes = align_up((size_t)n_tiles * kNOff * 2, 256);
   const size_t part_bytes = align_up((size_t)chunks * E * 4, 256);
-  char* ws = nullptr;
-  int rc = dev_alloc((void**)&ws, perm_bytes + blk_bytes + part_bytes, s, "igc_sparse_conv_backward: wgrad workspace");
+  Workspace wsb;
+  int rc = ws_acquire(&wsb, perm_bytes + blk_bytes + part_bytes, s, "igc_sparse_conv_backward: wgrad workspace");
   if (rc) return rc;
+  char* ws = (char*)wsb.p;
   int32_t* perm = (int32_t*)ws;
   uint16_t* blk = (uint16_t*)(ws + perm_bytes);
   float* part = (float*)(ws + perm_bytes + blk_bytes);
@@ -348,7 +349,7 @@ int launch_wgrad_bf16(const igc_grid* g, const int32_t* d_map, const void* d_fea
     if (e != hipSuccess) rc = hip_status(e, "igc_sparse_conv_backward: wgrad launch");
     else rc = launch_wgrad_reduce(part, chunks, E, d_dw, s);
   }
-  dev_free(ws, s);
+  ws_release(&wsb, s);
   return rc;
 }
 
@@ -357,12 +358,13 @@ int launch_wgrad_f32(const igc_grid* g, const int32_t* d_map, const void* d_feat
   const int64_t E = (int64_t)kNOff * cin * cout;
   if (wgrad_leaf_supported(cin, cout)) {
     const int64_t groups = wgrad_leaf_groups(g);
-    float* part = nullptr;
-    int rc = dev_alloc((void**)&part, (size_t)groups * E * 4, s, "igc_sparse_conv_backward: wgrad partials");
+    Workspace wsb;
+    int rc = ws_acquire(&wsb, (size_t)groups * E * 4, s, "igc_sparse_conv_backward: wgrad partials");
     if (rc) return rc;
+    float* part = (float*)wsb.p;
     rc = launch_wgrad_leaf(g, d_feats, cin, d_dout, cout, part, groups, s);
     if (rc == IGC_OK) rc = launch_wgrad_reduce(part, groups, E, d_dw, s);
-    dev_free(part, s);
+    ws_release(&wsb, s);
     return rc;
   }
   const int64_t N = g->n_voxels;
@@ -370,14 +372,15 @@ int launch_wgrad_f32(const igc_grid* g, const int32_t* d_map, const void* d_feat
   int64_t rpc = (N + chunks - 1) / chunks;
   rpc = (rpc + kStage - 1) / kStage * kStage;
   chunks = (N + rpc - 1) / rpc;
-  float* part = nullptr;
-  int rc = dev_alloc((void**)&part, (size_t)chunks * E * 4, s, "igc_sparse_conv_backward: wgrad partials");
+  Workspace wsb;
+  int rc = ws_acquire(&wsb, (size_t)chunks * E * 4, s, "igc_sparse_conv_backward: wgrad partials");
   if (rc) return rc;
+  float* part = (float*)wsb.p;
   k_wgrad_f32<<<(unsigned)(kNOff * chunks), 256, 0, s>>>(d_map, N, (const float*)d_feats, (const float*)d_dout, cin,
                                                         cout, rpc, part);
   hipError_t e = hipGetLastError();
   rc = e != hipSuccess ? hip_status(e, "igc_sparse_conv_backward: wgrad launch") : launch_wgrad_reduce(part, chunks, E, d_dw, s);
-  dev_free(part, s);
+  ws_release(&wsb, s);
   return rc;
 }
 

@@ -397,9 +397,10 @@ int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats
   const size_t wt_bytes = align_up((size_t)27 * cin * cout * 2, 256);
   const size_t perm_bytes = align_up((size_t)n_tiles * kBM * 4, 256);
   const size_t blk_bytes = align_up((size_t)n_tiles * kNOff * 2, 256);
-  char* ws = nullptr;
-  int rc = dev_alloc((void**)&ws, wt_bytes + perm_bytes + blk_bytes, s, "igc_sparse_conv: gather-GEMM-scatter workspace");
+  Workspace wsb;
+  int rc = ws_acquire(&wsb, wt_bytes + perm_bytes + blk_bytes, s, "igc_sparse_conv: gather-GEMM-scatter workspace");
   if (rc) return rc;
+  char* ws = (char*)wsb.p;
   uint16_t* wt = (uint16_t*)ws;
   int32_t* perm = (int32_t*)(ws + wt_bytes);
   uint16_t* blk = (uint16_t*)(ws + wt_bytes + perm_bytes);
@@ -427,7 +428,7 @@ int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats
     }
     e = hipGetLastError();
   }
-  dev_free(ws, s);
+  ws_release(&wsb, s);
   if (e != hipSuccess) return hip_status(e, "igc_sparse_conv: gather-GEMM-scatter launch");
   return IGC_OK;
 }

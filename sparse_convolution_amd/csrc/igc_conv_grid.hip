@@ -234,9 +234,10 @@ int launch_conv_map(const igc_grid* in, const igc_grid* out, const int32_t* stri
                     int32_t* d_map, hipStream_t s) {
   const int64_t n_out = out->n_voxels;
   if (n_out == 0) return IGC_OK;
-  int32_t* ijk = nullptr;
-  int rc = dev_alloc((void**)&ijk, (size_t)n_out * 12, s, "igc_conv_map: output coordinates");
+  Workspace wsb;
+  int rc = ws_acquire(&wsb, (size_t)n_out * 12, s, "igc_conv_map: output coordinates");
   if (rc) return rc;
+  int32_t* ijk = (int32_t*)wsb.p;
   rc = launch_active_ijk(out, ijk, s);
   hipError_t e = hipSuccess;
   if (rc == IGC_OK) {
@@ -244,7 +245,7 @@ int launch_conv_map(const igc_grid* in, const igc_grid* out, const int32_t* stri
     k_conv_map<<<grid_blocks(n_out, 16384), 256, 0, s>>>(in->view(), ijk, n_out, st, transposed, d_map);
     e = hipGetLastError();
   }
-  dev_free(ijk, s);
+  ws_release(&wsb, s);
   if (rc) return rc;
   if (e != hipSuccess) return hip_status(e, "igc_conv_map: launch");
   return IGC_OK;

@@ -718,9 +718,10 @@ __global__ __launch_bounds__(256) void k_conv_leaf_bf16(GridView g, const uint16
 template <int CIN, int COUT>
 int launch_leaf_bf16(const igc_grid* g, const void* d_feats, const void* d_w, void* d_out, hipStream_t s) {
   constexpr int KP = (27 * CIN + 31) / 32 * 32;
-  uint16_t* wt = nullptr;
-  int rc = dev_alloc((void**)&wt, (size_t)COUT * KP * 2, s, "igc_sparse_conv: leaf W transpose");
+  Workspace wsb;
+  int rc = ws_acquire(&wsb, (size_t)COUT * KP * 2, s, "igc_sparse_conv: leaf W transpose");
   if (rc) return rc;
+  uint16_t* wt = (uint16_t*)wsb.p;
   k_leaf_wt_bf16<CIN, COUT><<<(COUT * KP + 255) / 256, 256, 0, s>>>((const uint16_t*)d_w, wt);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) {
@@ -728,7 +729,7 @@ int launch_leaf_bf16(const igc_grid* g, const void* d_feats, const void* d_w, vo
                                                                    (uint16_t*)d_out);
     e = hipGetLastError();
   }
-  dev_free(wt, s);
+  ws_release(&wsb, s);
   if (e != hipSuccess) return hip_status(e, "igc_sparse_conv: bf16 leaf launch");
   return IGC_OK;
 }
