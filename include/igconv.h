@@ -124,7 +124,10 @@ typedef struct {
  * its own). d_ijk may be freed once the stream reaches the end of the call. */
 int igc_grid_build(const int32_t* d_ijk, int64_t n_in, igc_stream stream, igc_grid** out);
 
-/* Frees the grid (waits for its stream first). NULL is accepted. */
+/* Frees the grid's device memory in order on the stream the grid was built on (no host
+ * synchronisation): work already queued on that stream finishes reading the grid first. Work
+ * that reads the grid on other streams must be complete, or ordered before that stream's
+ * current point, when this is called. NULL is accepted. */
 int igc_grid_destroy(igc_grid* grid);
 
 /* Counts and sizes of the grid (host only, no device work). */
