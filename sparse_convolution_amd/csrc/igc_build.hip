@@ -513,7 +513,8 @@ __device__ __forceinline__ void rank_keys(const uint64_t* __restrict__ src, int6
   }
 }
 
-// Step 1: cnt[d * T + tile] = keys of the tile with digit d.
+// Step 1: cnt[d * T + tile] = keys of the tile with digit d, counted with LDS atomics into
+// one histogram per wave (only the counts are needed here, not the ranks).
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void k_radix_hist(const uint64_t* __restrict__ src, int64_t n, int shift,
                                                          uint32_t* __restrict__ cnt, int64_t T) {
@@ -523,9 +524,13 @@ __global__ __launch_bounds__(kThreads) void k_radix_hist(const uint64_t* __restr
   for (int x = tid; x < 4 * D; x += kThreads) (&s_cnt[0][0])[x] = 0;
   __syncthreads();
   const int64_t tile = blockIdx.x;
+  const int64_t wbase = tile * kSortTile + wave * (64 * kSortKPT) + lane_id();
   uint64_t key[kSortKPT];
-  uint32_t rank[kSortKPT];
-  rank_keys<BITS>(src, n, tile * kSortTile + wave * (64 * kSortKPT) + lane_id(), shift, key, rank, s_cnt[wave]);
+#pragma unroll
+  for (int r = 0; r < kSortKPT; ++r) key[r] = wbase + r * 64 < n ? src[wbase + r * 64] : 0ull;
+#pragma unroll
+  for (int r = 0; r < kSortKPT; ++r)
+    if (wbase + r * 64 < n) atomicAdd(&s_cnt[wave][(uint32_t)(key[r] >> shift) & (D - 1u)], 1u);
   __syncthreads();
   for (int d = tid; d < D; d += kThreads) cnt[(int64_t)d * T + tile] = s_cnt[0][d] + s_cnt[1][d] + s_cnt[2][d] + s_cnt[3][d];
 }
