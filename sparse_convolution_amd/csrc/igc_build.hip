@@ -162,11 +162,11 @@ __global__ __launch_bounds__(256) void k_tile_insert(const int32_t* __restrict__
   for (int64_t base = (int64_t)blockIdx.x * blockDim.x; base < n; base += U4 * stride) {
     int32_t ci[U4], cj[U4], ck[U4];
 #pragma unroll
-    for (int u = 0; u < U4; ++u) {
-      const int64_t e = base + u * stride + threadIdx.x;
-      ci[u] = e < n ? ijk[3 * e] : 0;
-      cj[u] = e < n ? ijk[3 * e + 1] : 0;
-      ck[u] = e < n ? ijk[3 * e + 2] : 0;
+    for (int u = 0; u < U4; ++u) {  // clamped, unconditional: all loads in flight before the first use
+      const int64_t e = min(base + u * stride + threadIdx.x, n - 1);
+      ci[u] = ijk[3 * e];
+      cj[u] = ijk[3 * e + 1];
+      ck[u] = ijk[3 * e + 2];
     }
 #pragma unroll
     for (int u = 0; u < U4; ++u) {
@@ -355,17 +355,38 @@ struct BitRuns {
   uint64_t cbits;                    // bits of the leaf part that are the same in every key
 };
 
+// Runs are applied by a recursion over the fixed slot indices with a uniform exit: every
+// run's fields sit at constant offsets of the kernel argument and are read as scalars once
+// per wave (a loop over r.n leaves a remainder loop that reads them per key).
+template <int I>
+__device__ __forceinline__ void compress_from(uint64_t x, uint64_t& c, const BitRuns& r) {
+  if constexpr (I < 16) {
+    if (I < r.n) {
+      c |= ((x >> r.lo[I]) & ((1ull << r.len[I]) - 1ull)) << r.pos[I];
+      compress_from<I + 1>(x, c, r);
+    }
+  }
+}
+
+template <int I>
+__device__ __forceinline__ void expand_from(uint64_t c, uint64_t& x, const BitRuns& r) {
+  if constexpr (I < 16) {
+    if (I < r.n) {
+      x |= ((c >> r.pos[I]) & ((1ull << r.len[I]) - 1ull)) << r.lo[I];
+      expand_from<I + 1>(c, x, r);
+    }
+  }
+}
+
 __device__ __forceinline__ uint64_t runs_compress(uint64_t key, const BitRuns& r) {
-  const uint64_t x = key >> 9;
   uint64_t c = 0;
-  for (int i = 0; i < r.n; ++i) c |= ((x >> r.lo[i]) & ((1ull << r.len[i]) - 1ull)) << r.pos[i];
+  compress_from<0>(key >> 9, c, r);
   return (c << 9) | (key & 511u);
 }
 
 __device__ __forceinline__ uint64_t runs_expand(uint64_t sk, const BitRuns& r) {
-  const uint64_t c = sk >> 9;
   uint64_t x = r.cbits;
-  for (int i = 0; i < r.n; ++i) x |= ((c >> r.pos[i]) & ((1ull << r.len[i]) - 1ull)) << r.lo[i];
+  expand_from<0>(sk >> 9, x, r);
   return (x << 9) | (sk & 511u);
 }
 
@@ -434,11 +455,11 @@ __global__ __launch_bounds__(256) void k_key2(const int32_t* __restrict__ ijk, i
   for (int64_t e0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e0 < n; e0 += U4 * stride) {
    int32_t ci[U4], cj[U4], ck[U4];
 #pragma unroll
-   for (int u = 0; u < U4; ++u) {
-     const int64_t e = e0 + u * stride;
-     ci[u] = e < n ? ijk[3 * e] : 0;
-     cj[u] = e < n ? ijk[3 * e + 1] : 0;
-     ck[u] = e < n ? ijk[3 * e + 2] : 0;
+   for (int u = 0; u < U4; ++u) {  // clamped, unconditional: all loads in flight before the first use
+     const int64_t e = min(e0 + u * stride, n - 1);
+     ci[u] = ijk[3 * e];
+     cj[u] = ijk[3 * e + 1];
+     ck[u] = ijk[3 * e + 2];
    }
 #pragma unroll
    for (int u = 0; u < U4; ++u) {
@@ -699,9 +720,13 @@ __device__ __forceinline__ uint64_t start_flags(uint64_t key, uint64_t prev, boo
 
 __device__ __forceinline__ void stage_block(const uint64_t* __restrict__ keys, int64_t n, int64_t base,
                                             uint64_t* s_keys, uint64_t* s_prev) {
+  uint64_t v[kKeysPerThread];  // every load issued before the first LDS store waits on one
+#pragma unroll
+  for (int q = 0; q < kKeysPerThread; ++q) v[q] = keys[min(base + q * kThreads + threadIdx.x, n - 1)];
+#pragma unroll
   for (int q = 0; q < kKeysPerThread; ++q) {
     const int p = q * kThreads + threadIdx.x;
-    if (base + p < n) s_keys[p] = keys[base + p];
+    if (base + p < n) s_keys[p] = v[q];
   }
   if (threadIdx.x == 0) *s_prev = base > 0 ? keys[base - 1] : 0ull;
   __syncthreads();
