@@ -249,11 +249,22 @@ __global__ __launch_bounds__(256) void k_tile_insert(const int32_t* __restrict__
 __global__ __launch_bounds__(256) void k_reduce_bits(const uint64_t* __restrict__ partial, int nb, BuildState* st) {
   __shared__ uint64_t s_red[4][4];
   uint64_t off_or = 0, off_and = ~0ull, key_or = 0, key_and = ~0ull;
-  for (int b = threadIdx.x; b < nb; b += 256) {
-    off_or |= partial[4 * b];
-    off_and &= partial[4 * b + 1];
-    key_or |= partial[4 * b + 2];
-    key_and &= partial[4 * b + 3];
+  constexpr int R = 8;  // partials per thread and round, loaded before any is combined
+  for (int b0 = threadIdx.x; b0 < nb; b0 += R * 256) {
+    ulonglong2 v[R][2];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int b = min(b0 + r * 256, nb - 1);  // a repeated partial changes no OR / AND
+      v[r][0] = reinterpret_cast<const ulonglong2*>(partial)[2 * b];
+      v[r][1] = reinterpret_cast<const ulonglong2*>(partial)[2 * b + 1];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      off_or |= v[r][0].x;
+      off_and &= v[r][0].y;
+      key_or |= v[r][1].x;
+      key_and &= v[r][1].y;
+    }
   }
   off_or = wave_or64(off_or);
   off_and = wave_and64(off_and);
@@ -414,16 +425,20 @@ __global__ __launch_bounds__(256) void k_hist_reduce(const uint32_t* __restrict_
   __shared__ uint32_t s_sum[16][16];
   const int cl = threadIdx.x & 15, slice = threadIdx.x >> 4;
   const int col = blockIdx.x * 16 + cl;
-  uint32_t acc[4] = {0, 0, 0, 0};
+  constexpr int R = 16;  // rows per thread and round, all loaded before any is added
+  uint32_t acc = 0;
   if (col < width) {
     int b = slice;
-    for (; b + 48 < nb; b += 64) {
+    for (; b + 16 * (R - 1) < nb; b += 16 * R) {
+      uint32_t v[R];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] += part[(size_t)(b + 16 * u) * width + col];
+      for (int u = 0; u < R; ++u) v[u] = part[(size_t)(b + 16 * u) * width + col];
+#pragma unroll
+      for (int u = 0; u < R; ++u) acc += v[u];
     }
-    for (; b < nb; b += 16) acc[0] += part[(size_t)b * width + col];
+    for (; b < nb; b += 16) acc += part[(size_t)b * width + col];
   }
-  s_sum[slice][cl] = acc[0] + acc[1] + acc[2] + acc[3];
+  s_sum[slice][cl] = acc;
   __syncthreads();
   if (slice == 0 && col < width) {
     uint32_t t = 0;
@@ -718,6 +733,12 @@ __device__ __forceinline__ uint64_t start_flags(uint64_t key, uint64_t prev, boo
          ((uint64_t)((key >> 21) != (prev >> 21)) << 32) | ((uint64_t)((key >> 36) != (prev >> 36)) << 48);
 }
 
+// A block's keys sit in LDS with one pad entry after every 16: each thread then reads its 16
+// consecutive keys at a lane stride of 17 entries, which spreads a wave over the banks (a
+// stride of 16 entries, 128 bytes, puts every lane on the same bank).
+constexpr int kPaddedKeys = kTileKeys + kTileKeys / 16;
+__device__ __forceinline__ int kpad(int p) { return p + (p >> 4); }
+
 __device__ __forceinline__ void stage_block(const uint64_t* __restrict__ keys, int64_t n, int64_t base,
                                             uint64_t* s_keys, uint64_t* s_prev) {
   uint64_t v[kKeysPerThread];  // every load issued before the first LDS store waits on one
@@ -726,7 +747,7 @@ __device__ __forceinline__ void stage_block(const uint64_t* __restrict__ keys, i
 #pragma unroll
   for (int q = 0; q < kKeysPerThread; ++q) {
     const int p = q * kThreads + threadIdx.x;
-    if (base + p < n) s_keys[p] = v[q];
+    if (base + p < n) s_keys[kpad(p)] = v[q];
   }
   if (threadIdx.x == 0) *s_prev = base > 0 ? keys[base - 1] : 0ull;
   __syncthreads();
@@ -734,7 +755,7 @@ __device__ __forceinline__ void stage_block(const uint64_t* __restrict__ keys, i
 
 __global__ __launch_bounds__(256) void k_count(const uint64_t* __restrict__ keys, int64_t n,
                                                uint64_t* __restrict__ block_counts) {
-  __shared__ uint64_t s_keys[kTileKeys];
+  __shared__ uint64_t s_keys[kPaddedKeys];
   __shared__ uint64_t s_prev;
   __shared__ uint64_t s_tmp[4];
   const int64_t base = (int64_t)blockIdx.x * kTileKeys;
@@ -743,7 +764,7 @@ __global__ __launch_bounds__(256) void k_count(const uint64_t* __restrict__ keys
   for (int q = 0; q < kKeysPerThread; ++q) {
     const int p = threadIdx.x * kKeysPerThread + q;
     const int64_t e = base + p;
-    if (e < n) c += start_flags(s_keys[p], p ? s_keys[p - 1] : s_prev, e == 0);
+    if (e < n) c += start_flags(s_keys[kpad(p)], p ? s_keys[kpad(p - 1)] : s_prev, e == 0);
   }
   uint64_t total;
   block_excl_scan64<kThreads>(c, s_tmp, &total);
@@ -804,7 +825,7 @@ constexpr int kLeafCache = 64;  // leaves of a block whose masks are merged in L
 
 __global__ __launch_bounds__(256) void k_register(const uint64_t* __restrict__ keys, int64_t n,
                                                   const uint64_t* __restrict__ prefix, Topo t) {
-  __shared__ uint64_t s_keys[kTileKeys];
+  __shared__ uint64_t s_keys[kPaddedKeys];
   __shared__ uint64_t s_prev;
   __shared__ uint64_t s_tmp[4];
   __shared__ uint64_t s_lmask[kLeafCache][8];
@@ -815,7 +836,7 @@ __global__ __launch_bounds__(256) void k_register(const uint64_t* __restrict__ k
   uint64_t c = 0;
   for (int q = 0; q < kKeysPerThread; ++q) {
     const int64_t e = base + p0 + q;
-    if (e < n) c += start_flags(s_keys[p0 + q], (p0 + q) ? s_keys[p0 + q - 1] : s_prev, e == 0);
+    if (e < n) c += start_flags(s_keys[kpad(p0 + q)], (p0 + q) ? s_keys[kpad(p0 + q - 1)] : s_prev, e == 0);
   }
   uint64_t total;
   const uint64_t excl = block_excl_scan64<kThreads>(c, s_tmp, &total);
@@ -834,8 +855,8 @@ __global__ __launch_bounds__(256) void k_register(const uint64_t* __restrict__ k
   for (int q = 0; q < kKeysPerThread; ++q) {
     const int64_t e = base + p0 + q;
     if (e >= n) break;
-    const uint64_t key = s_keys[p0 + q];
-    const uint64_t f = start_flags(key, (p0 + q) ? s_keys[p0 + q - 1] : s_prev, e == 0);
+    const uint64_t key = s_keys[kpad(p0 + q)];
+    const uint64_t f = start_flags(key, (p0 + q) ? s_keys[kpad(p0 + q - 1)] : s_prev, e == 0);
     nf += (int64_t)((f >> 16) & 1);
     nl += (int64_t)((f >> 32) & 1);
     nu += (int64_t)((f >> 48) & 1);
