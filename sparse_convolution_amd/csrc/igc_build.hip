@@ -359,7 +359,8 @@ struct PassSpec {
 
 // The varying bits of the keys' leaf part (key2 >> 9) as runs of consecutive bits: the sort
 // orders keys compacted to those bits ((leaf part gathered to the low bits) << 9 | voxel bits),
-// which keeps their order and takes fewer digits; the last pass writes them expanded again.
+// which keeps their order and takes fewer digits. The sorted keys stay compacted; a key is
+// expanded only where it starts a leaf.
 struct BitRuns {
   int n;                             // 0: keys are sorted as they are
   uint8_t lo[16], len[16], pos[16];  // run i: bits [lo, lo + len) of the leaf part -> [pos, pos + len)
@@ -597,7 +598,7 @@ template <int BITS>
 __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint64_t* __restrict__ src,
                                                             uint64_t* __restrict__ dst, int64_t n, int shift,
                                                             const uint32_t* __restrict__ off, int64_t T,
-                                                            uint32_t* guard, const BitRuns runs) {
+                                                            uint32_t* guard) {
   constexpr int D = 1 << BITS, J = D / kThreads;
   __shared__ uint64_t s_keys[kSortTile];
   __shared__ uint32_t s_cnt[4][D];
@@ -660,39 +661,36 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint64_t* __re
     if (p < valid_count) {
       const uint64_t k = s_keys[p];
       const int64_t gp = s_base[(uint32_t)(k >> shift) & (D - 1u)] + p;
-      if (gp >= 0 && gp < n) dst[gp] = runs.n ? runs_expand(k, runs) : k; else atomicOr(guard, 1u);
+      if (gp >= 0 && gp < n) dst[gp] = k; else atomicOr(guard, 1u);
     }
   }
 }
 
 template <int BITS>
 void radix_pass(const uint64_t* src, uint64_t* dst, int64_t n, int shift, const uint32_t* hist, uint32_t* cnt,
-                uint32_t* off, int64_t tiles, uint32_t* guard, const BitRuns& runs, hipStream_t s) {
+                uint32_t* off, int64_t tiles, uint32_t* guard, hipStream_t s) {
   k_radix_hist<BITS><<<(unsigned)tiles, kThreads, 0, s>>>(src, n, shift, cnt, tiles);
   k_radix_scan<<<1u << BITS, kThreads, 0, s>>>(cnt, tiles, hist, off);
-  k_radix_scatter<BITS><<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, shift, off, tiles, guard, runs);
+  k_radix_scatter<BITS><<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, shift, off, tiles, guard);
 }
 
 // Sorts keys[0..n) (in a, scratch b) over the digits of ps; returns the buffer holding the
 // result. hist holds the digit counts of every pass ([passes][bins]); cnt and off hold
-// kMaxBins * cap_tiles words each. With compacted keys (runs.n > 0) the last pass writes them
-// expanded.
+// kMaxBins * cap_tiles words each. Compacted keys stay compacted.
 int radix_sort(uint64_t* a, uint64_t* b, int64_t n, PassSpec ps, const uint32_t* hist, uint32_t* cnt, uint32_t* off,
-               int64_t cap_tiles, uint32_t* guard, hipStream_t s, uint64_t** result, const BitRuns* runs = nullptr) {
+               int64_t cap_tiles, uint32_t* guard, hipStream_t s, uint64_t** result) {
   *result = a;
   if (n <= 0 || ps.passes == 0) return IGC_OK;
   const int64_t tiles = (n + kSortTile - 1) / kSortTile;
-  if (tiles > cap_tiles || ps.passes > kMaxPasses || ps.bits < 8 || ps.bits > kMaxDigitBits || (runs && runs->n && ps.passes == 0))
+  if (tiles > cap_tiles || ps.passes > kMaxPasses || ps.bits < 8 || ps.bits > kMaxDigitBits)
     return set_error(IGC_ERR_INTERNAL, "igc_grid_build: radix sort workspace too small");
   uint64_t* src = a;
   uint64_t* dst = b;
   for (int p = 0; p < ps.passes; ++p) {
     const int shift = ps.lo_bit + ps.bits * p;
     const uint32_t* hp = hist + ((size_t)p << ps.bits);
-    BitRuns r{};
-    if (runs && p == ps.passes - 1) r = *runs;
-    if (ps.bits == 8) radix_pass<8>(src, dst, n, shift, hp, cnt, off, tiles, guard, r, s);
-    else radix_pass<9>(src, dst, n, shift, hp, cnt, off, tiles, guard, r, s);
+    if (ps.bits == 8) radix_pass<8>(src, dst, n, shift, hp, cnt, off, tiles, guard, s);
+    else radix_pass<9>(src, dst, n, shift, hp, cnt, off, tiles, guard, s);
     IGC_HIP(hipGetLastError(), "igc_grid_build: radix pass launch");
     std::swap(src, dst);
   }
@@ -727,10 +725,18 @@ PassSpec pass_spec(uint64_t varying, int min_bit = 0) {
 // Block b counts, among keys [b*4096, (b+1)*4096), those that start a new leaf, lower node
 // and upper node. Counts are packed in 16-bit fields 1..3 of one 64-bit word (field 0, the
 // voxels, is counted from the leaf masks after registration).
-__device__ __forceinline__ uint64_t start_flags(uint64_t key, uint64_t prev, bool first) {
+// The shifts that leave a key's leaf / lower / upper part: 9 / 21 / 36 for whole keys, the
+// compacted positions of those boundaries for compacted ones.
+struct KeyForm {
+  int cs_lower, cs_upper;
+  BitRuns runs;  // runs.n > 0: keys are compacted
+};
+
+__device__ __forceinline__ uint64_t start_flags(uint64_t key, uint64_t prev, bool first, int cs_lower, int cs_upper) {
   if (first) return 0x0001000100010000ull;
   return ((uint64_t)((key >> 9) != (prev >> 9)) << 16) |
-         ((uint64_t)((key >> 21) != (prev >> 21)) << 32) | ((uint64_t)((key >> 36) != (prev >> 36)) << 48);
+         ((uint64_t)((key >> cs_lower) != (prev >> cs_lower)) << 32) |
+         ((uint64_t)((key >> cs_upper) != (prev >> cs_upper)) << 48);
 }
 
 // A block's keys sit in LDS with one pad entry after every 16: each thread then reads its 16
@@ -754,7 +760,7 @@ __device__ __forceinline__ void stage_block(const uint64_t* __restrict__ keys, i
 }
 
 __global__ __launch_bounds__(256) void k_count(const uint64_t* __restrict__ keys, int64_t n,
-                                               uint64_t* __restrict__ block_counts) {
+                                               uint64_t* __restrict__ block_counts, int cs_lower, int cs_upper) {
   __shared__ uint64_t s_keys[kPaddedKeys];
   __shared__ uint64_t s_prev;
   __shared__ uint64_t s_tmp[4];
@@ -764,7 +770,7 @@ __global__ __launch_bounds__(256) void k_count(const uint64_t* __restrict__ keys
   for (int q = 0; q < kKeysPerThread; ++q) {
     const int p = threadIdx.x * kKeysPerThread + q;
     const int64_t e = base + p;
-    if (e < n) c += start_flags(s_keys[kpad(p)], p ? s_keys[kpad(p - 1)] : s_prev, e == 0);
+    if (e < n) c += start_flags(s_keys[kpad(p)], p ? s_keys[kpad(p - 1)] : s_prev, e == 0, cs_lower, cs_upper);
   }
   uint64_t total;
   block_excl_scan64<kThreads>(c, s_tmp, &total);
@@ -824,7 +830,7 @@ __device__ __forceinline__ int4 key_origin(uint64_t key, uint64_t tile, uint32_t
 constexpr int kLeafCache = 64;  // leaves of a block whose masks are merged in LDS
 
 __global__ __launch_bounds__(256) void k_register(const uint64_t* __restrict__ keys, int64_t n,
-                                                  const uint64_t* __restrict__ prefix, Topo t) {
+                                                  const uint64_t* __restrict__ prefix, Topo t, const KeyForm kf) {
   __shared__ uint64_t s_keys[kPaddedKeys];
   __shared__ uint64_t s_prev;
   __shared__ uint64_t s_tmp[4];
@@ -836,7 +842,9 @@ __global__ __launch_bounds__(256) void k_register(const uint64_t* __restrict__ k
   uint64_t c = 0;
   for (int q = 0; q < kKeysPerThread; ++q) {
     const int64_t e = base + p0 + q;
-    if (e < n) c += start_flags(s_keys[kpad(p0 + q)], (p0 + q) ? s_keys[kpad(p0 + q - 1)] : s_prev, e == 0);
+    if (e < n)
+      c += start_flags(s_keys[kpad(p0 + q)], (p0 + q) ? s_keys[kpad(p0 + q - 1)] : s_prev, e == 0, kf.cs_lower,
+                       kf.cs_upper);
   }
   uint64_t total;
   const uint64_t excl = block_excl_scan64<kThreads>(c, s_tmp, &total);
@@ -856,31 +864,39 @@ __global__ __launch_bounds__(256) void k_register(const uint64_t* __restrict__ k
     const int64_t e = base + p0 + q;
     if (e >= n) break;
     const uint64_t key = s_keys[kpad(p0 + q)];
-    const uint64_t f = start_flags(key, (p0 + q) ? s_keys[kpad(p0 + q - 1)] : s_prev, e == 0);
+    const uint64_t f =
+        start_flags(key, (p0 + q) ? s_keys[kpad(p0 + q - 1)] : s_prev, e == 0, kf.cs_lower, kf.cs_upper);
     nf += (int64_t)((f >> 16) & 1);
     nl += (int64_t)((f >> 32) & 1);
     nu += (int64_t)((f >> 48) & 1);
     const int64_t lf = nf - 1, lw = nl - 1, u = nu - 1;
-    if (lf < lf0 || lf >= t.n_leaf || lw >= t.n_lower || u >= t.n_upper || (int64_t)(key >> 36) >= t.n_upper) {
+    if (lf < lf0 || lf >= t.n_leaf || lw >= t.n_lower || u >= t.n_upper) {
       atomicOr(t.guard, 1u);
       break;
     }
-    const uint64_t tile = t.tiles[key >> 36];
-    if ((f >> 48) & 1) {
-      t.root_list[u] = tile;
-      t.upper_origin[u] = key_origin(key, tile, 12);
-      t.upper_first[u] = (uint32_t)lw;
-    }
-    if ((f >> 32) & 1) {
-      const uint32_t cu = (uint32_t)(key >> 21) & 0x7FFFu;
-      atomicOr((unsigned long long*)&t.upper_mask[u * 512 + (cu >> 6)], 1ull << (cu & 63u));
-      t.lower_origin[lw] = key_origin(key, tile, 7);
-      t.lower_first[lw] = (uint32_t)lf;
-    }
-    if ((f >> 16) & 1) {
-      const uint32_t cl = (uint32_t)(key >> 9) & 0xFFFu;
-      atomicOr((unsigned long long*)&t.lower_mask[lw * 64 + (cl >> 6)], 1ull << (cl & 63u));
-      t.leaf_origin[lf] = key_origin(key, tile, 3);
+    if (f) {  // a key that starts a leaf (and maybe its lower / upper node): expanded, and the tile read, only here
+      const uint64_t key = kf.runs.n ? runs_expand(s_keys[kpad(p0 + q)], kf.runs) : s_keys[kpad(p0 + q)];
+      if ((int64_t)(key >> 36) >= t.n_upper) {
+        atomicOr(t.guard, 1u);
+        break;
+      }
+      const uint64_t tile = t.tiles[key >> 36];
+      if ((f >> 48) & 1) {
+        t.root_list[u] = tile;
+        t.upper_origin[u] = key_origin(key, tile, 12);
+        t.upper_first[u] = (uint32_t)lw;
+      }
+      if ((f >> 32) & 1) {
+        const uint32_t cu = (uint32_t)(key >> 21) & 0x7FFFu;
+        atomicOr((unsigned long long*)&t.upper_mask[u * 512 + (cu >> 6)], 1ull << (cu & 63u));
+        t.lower_origin[lw] = key_origin(key, tile, 7);
+        t.lower_first[lw] = (uint32_t)lf;
+      }
+      if ((f >> 16) & 1) {
+        const uint32_t cl = (uint32_t)(key >> 9) & 0xFFFu;
+        atomicOr((unsigned long long*)&t.lower_mask[lw * 64 + (cl >> 6)], 1ull << (cl & 63u));
+        t.leaf_origin[lf] = key_origin(key, tile, 3);
+      }
     }
     const uint32_t vox = (uint32_t)key & 511u;
     if (lf - lf0 < kLeafCache) {
@@ -1201,11 +1217,19 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
     IGC_HIP(hipGetLastError(), "igc_grid_build: histogram reduce launch");
   }
   uint64_t* sorted = ka;
-  if ((rc = radix_sort(ka, kb, n_in, ps, hist, rcnt, roff, sort_tiles, &st->guard, s, &sorted, &runs))) return rc;
+  if ((rc = radix_sort(ka, kb, n_in, ps, hist, rcnt, roff, sort_tiles, &st->guard, s, &sorted))) return rc;
+  // The sorted keys stay compacted: leaf, lower and upper boundaries are compared at the
+  // compacted positions of leaf-part bits 0, 12 and 27, and the register pass expands a key
+  // only where it starts a leaf.
+  KeyForm kf{21, 36, runs};
+  if (runs.n) {
+    kf.cs_lower = 9 + __builtin_popcountll(leaf_var & 0xFFFull);
+    kf.cs_upper = 9 + __builtin_popcountll(leaf_var & ((1ull << 27) - 1ull));
+  }
 
   // Counts, then the read-back that sizes the topology.
   const int64_t nb = tiles;
-  k_count<<<(unsigned)nb, kThreads, 0, s>>>(sorted, n_in, bcounts);
+  k_count<<<(unsigned)nb, kThreads, 0, s>>>(sorted, n_in, bcounts, kf.cs_lower, kf.cs_upper);
   IGC_HIP(hipGetLastError(), "igc_grid_build: count launch");
   k_scan_blocks<<<1, 1024, 0, s>>>(bcounts, nb, bprefix, st);
   IGC_HIP(hipGetLastError(), "igc_grid_build: block scan launch");
@@ -1259,7 +1283,7 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   Topo t{F,           Lw,           U,          &st->guard,     tiles_sorted,
          g->root_list, g->upper_origin, g->upper_mask, g->upper_first, g->lower_origin, g->lower_mask,
          g->lower_first, g->leaf,     g->leaf_origin};
-  k_register<<<(unsigned)nb, kThreads, 0, s>>>(sorted, n_in, bprefix, t);
+  k_register<<<(unsigned)nb, kThreads, 0, s>>>(sorted, n_in, bprefix, t, kf);
   IGC_HIP(hipGetLastError(), "igc_grid_build: register launch");
   const int64_t groups = (F + kLeafGroup - 1) / kLeafGroup;
   uint64_t* gsum = bprefix;  // the block prefixes are consumed by the register pass
