@@ -11,6 +11,9 @@
 // consecutive rows, so every store of map[o, r] is one contiguous 256-byte run.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+#include <cstring>
+
 #include <algorithm>
 
 #include "igc_host.h"
@@ -22,7 +25,12 @@ namespace {
 
 constexpr int kMaxOffsets = 256;
 constexpr int64_t kMapGroups = 1280;  // workgroups of the persistent kernel-map form (5 per CU)
+constexpr int64_t kMapGroupsPc = 512;   // workgroups of the producer / consumer form (2 per CU)
+constexpr int64_t kMapPcLeaves = 16384; // grids with at least this many leaves take the producer / consumer form
 constexpr uint32_t kVoxelMajor = 128;  // leaves with at most this many voxels take the voxel-major stores
+// The quad stores place each row's head and tail elements at voxels c and count - 6 + c: a
+// leaf needs at least 3 voxels there, or that index wraps below zero.
+static_assert(kVoxelMajor >= 2, "the quad-store path needs leaves of at least 3 voxels");
 
 struct OffsetList {
   int8_t d[kMaxOffsets][3];
@@ -332,6 +340,174 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) voi
 }
 #undef IGC_LOAD_REC
 
+// Producer / consumer form of the standard-stencil kernel map. Stores and loads share one
+// completion counter on this GPU, in issue order, so a wave that loads the next leaf's records
+// after storing this leaf's map rows waits for those stores too: the store latency is exposed
+// once per leaf. Here the four consumer waves of a workgroup issue no global loads at all; a
+// fifth wave loads the 27 records of the next leaf of every consumer into a second LDS buffer
+// while they answer the current ones, and one workgroup barrier (ordering LDS only, so it waits
+// for no store) separates the steps. The consumers' work per leaf is that of the form above:
+// window of row indices, then voxel-major or quad stores.
+constexpr int kPcConsumers = 4;
+constexpr int kPcThreads = 64 * (kPcConsumers + 1);
+
+__device__ __forceinline__ void lds_step_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__global__ __launch_bounds__(kPcThreads) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_kernel_map_pc(
+    GridView g, int32_t* __restrict__ map,
+                                                               uint32_t* __restrict__ nbmask) {
+  __shared__ __align__(16) uint32_t s_rec[2][kPcConsumers][27][kRecWords];
+  __shared__ int32_t s_idx[kPcConsumers][1000];
+  __shared__ uint16_t s_cell[kPcConsumers][512];
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int64_t F = g.n_leaf, N = g.n_voxels;
+  // Workgroup b goes to XCD b mod 8; each XCD takes one contiguous range of leaves [lo, hi),
+  // and at step k the consumers of local workgroup j answer leaves lo + (k * mine + j) * 4 + c.
+  const int64_t G = gridDim.x, x = blockIdx.x & 7, q = G >> 3, rem = G & 7;
+  const int64_t before = x * q + (x < rem ? x : rem), mine = q + (x < rem ? 1 : 0);
+  const int64_t lo = F * before / G, hi = F * (before + mine) / G;
+  const int64_t j = blockIdx.x >> 3;
+  const int64_t span = hi - lo - kPcConsumers * j;
+  const int64_t steps = span > 0 ? (span + kPcConsumers * mine - 1) / (kPcConsumers * mine) : 0;
+  auto leaf_of = [&](int64_t k, int c) -> int64_t {
+    const int64_t f = lo + (k * mine + j) * kPcConsumers + c;
+    return f < hi ? f : -1;
+  };
+
+  if (wave == kPcConsumers) {
+    // Producer. Lane l serves (consumer, slot) pairs l and l + 64 of the 4 * 27 = 108.
+    const int p0 = lane, p1 = lane + 64;
+    const bool has1 = p1 < kPcConsumers * 27;
+    const int c0 = p0 / 27, t0 = p0 % 27, c1 = has1 ? p1 / 27 : 0, t1 = has1 ? p1 % 27 : 0;
+    auto nbr_of = [&](int64_t k, int c, int t) -> int32_t {
+      const int64_t f = k < steps ? leaf_of(k, c) : -1;
+      return f >= 0 ? g.leaf_nbr[f * 27 + t] : -1;
+    };
+    auto fill = [&](int buf, int c, int t, int32_t nl) {
+      const u32x4 z = {0, 0, 0, 0};
+      u32x4 r[5] = {z, z, z, z, z};
+      if (nl >= 0) {
+        const u32x4* src = (const u32x4*)(g.leaf + nl);
+#pragma unroll
+        for (int i = 0; i < 5; ++i) r[i] = src[i];
+      }
+      u32x4* d = (u32x4*)s_rec[buf][c][t];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) d[i] = r[i];
+    };
+    int32_t n0 = nbr_of(0, c0, t0), n1 = has1 ? nbr_of(0, c1, t1) : -1;
+    fill(0, c0, t0, n0);
+    if (has1) fill(0, c1, t1, n1);
+    n0 = nbr_of(1, c0, t0);
+    n1 = has1 ? nbr_of(1, c1, t1) : -1;
+    lds_step_barrier();
+    for (int64_t k = 0; k < steps; ++k) {
+      // Records of step k + 1 into the other buffer; neighbour entries of step k + 2.
+      const int buf = (int)((k + 1) & 1);
+      const int32_t m0 = nbr_of(k + 2, c0, t0), m1 = has1 ? nbr_of(k + 2, c1, t1) : -1;
+      fill(buf, c0, t0, n0);
+      if (has1) fill(buf, c1, t1, n1);
+      n0 = m0;
+      n1 = m1;
+      lds_step_barrier();
+    }
+    return;
+  }
+
+  // Consumer `wave`.
+  const int c = wave;
+  lds_step_barrier();
+  for (int64_t k = 0; k < steps; ++k) {
+    const int64_t f = leaf_of(k, c);
+    if (f >= 0) {
+      const uint32_t(*rec)[kRecWords] = s_rec[k & 1][c];
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      // Window cells of the active voxels in row order (mbcnt: set bits of the word below the lane).
+      const uint32_t* own = rec[13];
+      uint32_t mw[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mw[i] = own[i];
+      const uint32_t base = own[16];
+      uint32_t count = 0;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const uint32_t lo32 = mw[2 * w], hi32 = mw[2 * w + 1];
+        const uint32_t rank = __builtin_amdgcn_mbcnt_hi(hi32, __builtin_amdgcn_mbcnt_lo(lo32, count));
+        if ((((uint64_t)hi32 << 32 | lo32) >> ln) & 1ull)
+          s_cell[c][rank] = (uint16_t)(w * 100 + (ln >> 3) * 10 + (ln & 7) + 111);
+        count += (uint32_t)__popc(lo32) + (uint32_t)__popc(hi32);
+      }
+#pragma unroll 1
+      for (int p = ln; p < 100; p += 64) window_column(rec, p, &s_idx[c][p]);
+      wave_sync();
+
+      if ((uint64_t)base + count > (uint64_t)N) count = (uint64_t)base < (uint64_t)N ? (uint32_t)(N - base) : 0u;
+      if (count <= kVoxelMajor) {
+        for (uint32_t t = ln; t < count; t += 64) {
+          const int32_t* nbh = &s_idx[c][s_cell[c][t] - 111];
+          int32_t v[27];
+#pragma unroll
+          for (int o = 0; o < 27; ++o) v[o] = nbh[win_off(o)];
+#pragma unroll
+          for (int o = 0; o < 27; ++o) (map + (size_t)o * (size_t)N + base)[t] = v[o];
+          if (nbmask) {
+            uint32_t bits = 0;
+#pragma unroll
+            for (int o = 0; o < 27; ++o) bits |= (v[o] >= 0 ? 1u : 0u) << o;
+            nbmask[base + t] = bits;
+          }
+        }
+      } else {
+        const uint32_t n4 = (uint32_t)N & 3u, s0 = base & 3u;
+#pragma unroll 1
+        for (int ox = 0; ox < 3; ++ox) {
+#pragma unroll
+          for (int r = 0; r < 9; ++r) {
+            const int o = 9 * ox + r;
+            const uint32_t s = (s0 + (uint32_t)o * n4) & 3u;
+            const uint32_t hd = (4u - s) & 3u;
+            const uint32_t fq = ((s + count) >> 2) - (s ? 1u : 0u);
+            int32_t* rowp = map + (size_t)o * (size_t)N + base + hd;  // 16-byte aligned
+            for (uint32_t kq = ln; kq < fq; kq += 64) {
+              const uint32_t tq = hd + 4u * kq;
+              int32_t v[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = s_idx[c][(int)s_cell[c][tq + e] - 111 + 100 * ox + win_off(r)];
+              *(i32x4*)(rowp + 4u * kq) = i32x4{v[0], v[1], v[2], v[3]};
+            }
+          }
+        }
+        for (uint32_t p = ln; p < 162u; p += 64) {
+          const uint32_t o = p / 6u, e = p - 6u * o;
+          const uint32_t s = (s0 + o * n4) & 3u;
+          const uint32_t hd = (4u - s) & 3u;
+          const uint32_t fq = ((s + count) >> 2) - (s ? 1u : 0u);
+          const uint32_t t = e < 3u ? e : count - 6u + e;
+          if (e < 3u ? t < hd : t >= hd + 4u * fq)
+            (map + (size_t)o * (size_t)N + base)[t] = s_idx[c][(int)s_cell[c][t] - 111 + win_off((int)o)];
+        }
+        if (nbmask) {
+          for (uint32_t t = ln; t < count; t += 64) {
+            const int32_t* nbh = &s_idx[c][s_cell[c][t] - 111];
+            uint32_t bits = 0;
+#pragma unroll
+            for (int o = 0; o < 27; ++o) bits |= (nbh[win_off(o)] >= 0 ? 1u : 0u) << o;
+            nbmask[base + t] = bits;
+          }
+        }
+      }
+      wave_sync();
+    }
+    lds_step_barrier();
+  }
+}
+
 }  // namespace
 
 int launch_active_ijk(const igc_grid* g, int32_t* d_out, hipStream_t s) {
@@ -365,11 +541,25 @@ int launch_kernel_map(const igc_grid* g, const int32_t* h_offsets, int32_t K, in
   for (int o = 0; o < K && standard; ++o)
     standard = h_offsets[3 * o] == o / 9 - 1 && h_offsets[3 * o + 1] == (o / 3) % 3 - 1 && h_offsets[3 * o + 2] == o % 3 - 1;
   // The window form stores 16-byte quads: it needs a 16-byte aligned map.
-  if (standard && ((uintptr_t)d_map & 15u) == 0)
-    k_kernel_map_window<<<(unsigned)std::min<int64_t>((g->n_leaf + 3) / 4, kMapGroups), 256, 0, s>>>(g->view(), d_map,
-                                                                                                   d_nbmask);
-  else
+  if (standard && ((uintptr_t)d_map & 15u) == 0) {
+    // Large grids are bound by the map's stores: the producer / consumer form keeps them from
+    // being waited on. Small grids are bound by per-leaf latency, where the persistent form with
+    // four independent waves and no workgroup barrier is faster. IGC_TEST_KMAP_FORM = "pc" or
+    // "window" forces one form (tests).
+    bool pc = g->n_leaf >= kMapPcLeaves;
+    if (const char* e = std::getenv("IGC_TEST_KMAP_FORM")) {
+      if (std::strcmp(e, "pc") == 0) pc = true;
+      if (std::strcmp(e, "window") == 0) pc = false;
+    }
+    if (pc)
+      k_kernel_map_pc<<<(unsigned)std::min<int64_t>((g->n_leaf + 3) / 4, kMapGroupsPc), kPcThreads, 0, s>>>(
+          g->view(), d_map, d_nbmask);
+    else
+      k_kernel_map_window<<<(unsigned)std::min<int64_t>((g->n_leaf + 3) / 4, kMapGroups), 256, 0, s>>>(
+          g->view(), d_map, d_nbmask);
+  } else {
     k_kernel_map<<<(unsigned)((g->n_leaf + 3) / 4), 256, 0, s>>>(g->view(), off, d_map, d_nbmask);
+  }
   IGC_HIP(hipGetLastError(), "igc_kernel_map: launch");
   return IGC_OK;
 }

@@ -188,3 +188,22 @@ def test_errors():
     off = np.array([[9, 0, 0]], np.int32)
     with pytest.raises(igc.IgcError):
         igc.kernel_map(g, off)
+
+
+@pytest.mark.parametrize("form", ["pc", "window"])
+def test_kernel_map_forms(monkeypatch, form):
+    """Both standard-stencil kernel-map forms (producer / consumer, taken by grids of many leaves,
+    and the persistent window form) agree with the oracle on every grid shape, whichever the
+    grid size would select: a single voxel, sparse and full leaves, a leaf count that leaves
+    workgroups without a full step, and a grid large enough for many steps per workgroup."""
+    monkeypatch.setenv("IGC_TEST_KMAP_FORM", form)
+    rng = np.random.default_rng(31)
+    check_grid(np.array([[5, -3, 7]], np.int32), f"{form}: one voxel")
+    origins = np.unique(rng.integers(-200, 200, size=(4001, 3)) * 8, axis=0)
+    one = (origins + rng.integers(0, 8, size=origins.shape)).astype(np.int32)
+    check_grid(one[:4001], f"{form}: one voxel per leaf")
+    g3 = np.stack(np.meshgrid(np.arange(8), np.arange(8), np.arange(8), indexing="ij"), -1).reshape(-1, 3)
+    full = (origins[:37, None, :] + g3[None]).reshape(-1, 3).astype(np.int32)
+    check_grid(full, f"{form}: 37 full leaves")
+    check_grid(workloads.make_coords("lidar"), f"{form}: lidar")
+    check_grid(workloads.make_coords("leaf"), f"{form}: leaf")
