@@ -167,7 +167,7 @@ int igc_kernel_map(const igc_grid* grid, const int32_t* h_offsets, int32_t K, in
  *     LEAF: dtype F32, (cin, cout) in {(4,8), (4,16), (4,32), (8,8), (8,16), (8,32),
  *           (16,16), (8,4), (16,4), (16,8)};
  *           dtype BF16 (the leaf window of the pages' brick backend: a dense bf16 10^3 halo
- *           per leaf), cin in {16, 32}, cout in {16, 32, 64}
+ *           per leaf), cin in {16, 32, 64}, cout in {16, 32, 64}
  *     GGS : dtype BF16, cin a multiple of 32 up to 1024, cout a multiple of 64 up to 1024
  * Anything else returns IGC_ERR_UNSUPPORTED. d_out must not alias d_feats. */
 int igc_sparse_conv(const igc_grid* grid, const int32_t* d_map, const void* d_feats, int32_t dtype,
@@ -229,10 +229,12 @@ int igc_sparse_conv_between(const igc_grid* out, const int32_t* d_map, int64_t n
                             int32_t dtype, int32_t cin, const void* d_w, int32_t cout, void* d_out,
                             igc_stream stream);
 
-/* The path IGC_PATH_AUTO takes for this grid and layer shape (host only). Leaf when the
- * dtype is F32 and the shape is supported by LEAF, GGS otherwise; IGC_ERR_UNSUPPORTED when
- * neither path supports the shape. The IGC_PATH environment variable ("leaf" / "ggs")
- * overrides the automatic choice. */
+/* The path IGC_PATH_AUTO takes for this grid and layer shape (host only). LEAF when LEAF
+ * supports (dtype, cin, cout) and either GGS does not or the grid's leaf occupancy (active
+ * voxels / (512 x leaves)) is at least 0.2 for cin <= 32 or 0.5 for cin >= 64 (the fVDB notes
+ * put the leaf backend's break-even near 20%; the higher bar at 64 channels is measured);
+ * GGS otherwise; IGC_ERR_UNSUPPORTED when neither path supports the shape. The IGC_PATH
+ * environment variable ("leaf" / "ggs") overrides the automatic choice. */
 int igc_select_path(const igc_grid* grid, int32_t dtype, int32_t cin, int32_t cout, int32_t* path);
 
 /* Message of the last failed call on this host thread ("" if none). */

@@ -148,10 +148,13 @@ static void free_grid(igc_grid* g) {
   delete g;
 }
 
-static bool leaf_occupancy_ok(const igc_grid* g) {
+static bool leaf_occupancy_ok(const igc_grid* g, int32_t cin) {
   // Leaf path pays for 512 positions per leaf; the fVDB notes put its break-even against a
-  // general backend at a leaf occupancy of about 20%.
-  return g->n_leaf > 0 && (double)g->n_voxels >= 0.2 * 512.0 * (double)g->n_leaf;
+  // general backend at a leaf occupancy of about 20%. With 64 input channels the window holds
+  // one leaf per CU and the gather-GEMM-scatter path wins up to a higher occupancy (measured,
+  // bf16 64 -> 64: 9.1 against 12.6 ms at 0.23, 1.33 against 1.25 ms at 0.60).
+  const double min_occ = cin >= 64 ? 0.5 : 0.2;
+  return g->n_leaf > 0 && (double)g->n_voxels >= min_occ * 512.0 * (double)g->n_leaf;
 }
 
 static int choose_path(const igc_grid* g, int32_t dtype, int32_t cin, int32_t cout, int32_t* path) {
@@ -161,7 +164,7 @@ static int choose_path(const igc_grid* g, int32_t dtype, int32_t cin, int32_t co
     if (!std::strcmp(e, "leaf") && leaf_ok) return *path = IGC_PATH_LEAF, IGC_OK;
     if (!std::strcmp(e, "ggs") && ggs_ok) return *path = IGC_PATH_GGS, IGC_OK;
   }
-  if (leaf_ok && (leaf_occupancy_ok(g) || !ggs_ok)) return *path = IGC_PATH_LEAF, IGC_OK;
+  if (leaf_ok && (leaf_occupancy_ok(g, cin) || !ggs_ok)) return *path = IGC_PATH_LEAF, IGC_OK;
   if (ggs_ok) return *path = IGC_PATH_GGS, IGC_OK;
   return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: no path supports dtype " + std::to_string(dtype) +
                                             " with cin " + std::to_string(cin) + " and cout " + std::to_string(cout));

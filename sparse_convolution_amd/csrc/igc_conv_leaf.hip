@@ -580,7 +580,7 @@ int launch_leaf(const igc_grid* g, const void* d_feats, const void* d_w, void* d
 // fVDB notes, "accelerated operators for sparse convolution": the brick backend densifies small
 // output windows with their halo and runs a dense convolution on the tensor cores, for feature
 // depths of 32 to 64 at high neighbour occupancy. gfx950 form: the window is a whole leaf's
-// 10^3 halo in LDS as bf16 (2 KB per channel: 32 KB for 16 channels, 64 KB for 32), zeros where
+// 10^3 halo in LDS as bf16 (2 KB per channel: 32 KB for 16 channels, 128 KB for 64), zeros where
 // inactive; the M dimension of v_mfma_f32_16x16x32_bf16 is the leaf's active voxels 16 at a
 // time (inactive outputs of the window are not computed), K = 27 offsets x CIN, N = COUT in
 // 16-column blocks, fp32 accumulation, bf16 output (round to nearest even).
@@ -613,12 +613,13 @@ __device__ __forceinline__ int bf16_swz(int c) {
 // One workgroup per leaf. Wave w takes column block w % NS and the row blocks w / NS, w / NS +
 // 4 / NS, ...; its B fragments (W^T, one per k-step) stay in registers, and each k-step is one
 // 16-byte window read and one MFMA. K runs in steps of 32: lane group kg = lane / 16 holds k =
-// 32 q + 8 kg .. + 7, i.e. one offset's 8 channels; k past 27 CIN (CIN 16: the second half of
-// the last step) reads offset 0's cell against zero W.
+// 32 q + 8 kg .. + 7, i.e. 8 channels of one offset (CIN 64: offset q / 2, channels 32 (q % 2)
+// + 8 kg ..; CIN 32: offset q; CIN 16: offset 2 q + kg / 2); k past 27 CIN (CIN 16: the second
+// half of the last step) reads offset 0's cell against zero W.
 template <int CIN, int COUT>
 __global__ __launch_bounds__(256) void k_conv_leaf_bf16(GridView g, const uint16_t* __restrict__ feats,
                                                         const uint16_t* __restrict__ wt, uint16_t* __restrict__ out) {
-  static_assert(CIN == 16 || CIN == 32, "window cells of two or four 16-byte granules");
+  static_assert(CIN == 16 || CIN == 32 || CIN == 64, "window cells of two, four or eight 16-byte granules");
   static_assert(COUT == 16 || COUT == 32 || COUT == 64, "column blocks per wave");
   constexpr int NS = COUT / 16;
   constexpr int KP = (27 * CIN + 31) / 32 * 32;
@@ -645,10 +646,10 @@ __global__ __launch_bounds__(256) void k_conv_leaf_bf16(GridView g, const uint16
   const uint16_t* wrow = wt + (size_t)(ns * 16 + rl) * KP + kg * 8;
 #pragma unroll
   for (int q = 0; q < NCH; ++q) wb[q] = *(const bf16x8*)(wrow + q * 32);
-  // k-step q, lane group kg: offset q and granule kg (CIN 32), or offset 2 q + kg / 2 and
-  // granule kg % 2 (CIN 16).
-  const int gran = CIN == 32 ? kg : (kg & 1);
-  const int ohalf = CIN == 32 ? 0 : (kg >> 1);
+  // k-step q, lane group kg: offset q and granule kg (CIN 32), offset 2 q + kg / 2 and granule
+  // kg % 2 (CIN 16), or offset q / 2 and granule 4 (q % 2) + kg (CIN 64).
+  const int gran = CIN == 16 ? (kg & 1) : kg;
+  const int ohalf = CIN == 16 ? (kg >> 1) : 0;
   load_leaf_block(g, f, tid, s_mask, s_off, s_pre);
   __syncthreads();
 
@@ -692,19 +693,35 @@ __global__ __launch_bounds__(256) void k_conv_leaf_bf16(GridView g, const uint16
     const uint32_t t = rb * 16 + rl;
     const uint32_t p = s_pos[t < count ? t : 0];
     const int cell0 = (int)((p >> 6) * 100 + ((p >> 3) & 7u) * 10 + (p & 7u));  // cell of offset (-1,-1,-1)
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q = 0; q < NCH; ++q) {
-      int dc;
-      if constexpr (CIN == 32) {
+    // A fragment of k-step q: a window read at a constant cell distance from cell0.
+    auto frag = [&](int q) -> bf16x8 {
+      int dc, gq = gran;
+      if constexpr (CIN == 64) {
+        dc = cell_delta(q >> 1);
+        gq = ((q & 1) << 2) | gran;
+      } else if constexpr (CIN == 32) {
         dc = cell_delta(q);
       } else {
         const int o0 = 2 * q, o1 = 2 * q + 1 < 27 ? 2 * q + 1 : 0;
         dc = ohalf ? cell_delta(o1) : cell_delta(o0);
       }
       const int c = cell0 + dc;
-      const bf16x8 a = __builtin_bit_cast(bf16x8, s_win[c * GPC + (gran ^ bf16_swz<GPC>(c))]);
+      return __builtin_bit_cast(bf16x8, s_win[c * GPC + (gq ^ bf16_swz<GPC>(c))]);
+    };
+    // The reads run PF k-steps ahead of their MFMA, held there by scheduling barriers (the
+    // compiler's own schedule keeps two in flight, and each MFMA then waits for most of an LDS
+    // round trip).
+    constexpr int PF = CIN == 64 ? 6 : 8;
+    bf16x8 ring[PF];
+#pragma unroll
+    for (int d = 0; d < PF; ++d) ring[d] = frag(d);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      const bf16x8 a = ring[q % PF];
+      if (q + PF < NCH) ring[q % PF] = frag(q + PF);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wb[q], acc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);  // keep each read PF steps ahead of its MFMA
     }
     // D: lane holds column lane%16 of rows 4*(lane/16) + j.
 #pragma unroll
@@ -749,7 +766,7 @@ int launch_wgrad_leaf_t(const igc_grid* g, const void* d_feats, const void* d_do
 bool leaf_conv_supported(int32_t dtype, int32_t cin, int32_t cout) {
   if (dtype == IGC_BF16) {
     switch (cin * 1000 + cout) {
-      case 16016: case 16032: case 16064: case 32016: case 32032: case 32064:
+      case 16016: case 16032: case 16064: case 32016: case 32032: case 32064: case 64016: case 64032: case 64064:
         return true;
       default:
         return false;
@@ -775,6 +792,9 @@ int launch_conv_leaf(const igc_grid* g, const void* d_feats, int32_t dtype, int3
       case 32016: return launch_leaf_bf16<32, 16>(g, d_feats, d_w, d_out, s);
       case 32032: return launch_leaf_bf16<32, 32>(g, d_feats, d_w, d_out, s);
       case 32064: return launch_leaf_bf16<32, 64>(g, d_feats, d_w, d_out, s);
+      case 64016: return launch_leaf_bf16<64, 16>(g, d_feats, d_w, d_out, s);
+      case 64032: return launch_leaf_bf16<64, 32>(g, d_feats, d_w, d_out, s);
+      case 64064: return launch_leaf_bf16<64, 64>(g, d_feats, d_w, d_out, s);
       default: return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: bf16 leaf path shape");
     }
   }

@@ -99,7 +99,7 @@ def test_fp32_leaf_shapes(cin, cout):
     run_backward(c, cin, cout, torch.float32, "leaf", "clusters", seed=cin * 5 + cout)
 
 
-@pytest.mark.parametrize("cin,cout", [(16, 16), (16, 32), (32, 16), (32, 32)])
+@pytest.mark.parametrize("cin,cout", [(16, 16), (16, 32), (32, 16), (32, 32), (16, 64), (32, 64), (64, 64)])
 def test_bf16_leaf_input_gradient_shapes(cin, cout):
     # dgrad runs cout -> cin on the bf16 leaf window; the bf16 weight gradient needs cout >= 64.
     c = _cluster_coords(4, 20, 200, seed=cin * 41 + cout)

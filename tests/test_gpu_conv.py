@@ -84,7 +84,8 @@ def test_ggs_path_shapes(cin, cout):
     run_conv(c, cin, cout, torch.bfloat16, "ggs", "clusters", seed=cin * 3 + cout, std=1.0 / np.sqrt(27 * cin))
 
 
-@pytest.mark.parametrize("cin,cout", [(16, 16), (16, 32), (16, 64), (32, 16), (32, 32), (32, 64)])
+@pytest.mark.parametrize("cin,cout", [(16, 16), (16, 32), (16, 64), (32, 16), (32, 32), (32, 64), (64, 16),
+                                      (64, 32), (64, 64)])
 def test_leaf_path_bf16_shapes(cin, cout):
     # The bf16 leaf window (brick) path: dense clusters and a sparse shell in one grid.
     c = np.concatenate([_cluster_coords(4, 20, 200, seed=cin * 11 + cout, fill=0.6),
@@ -122,6 +123,12 @@ def test_band_workload_ggs_sampled():
              std=w.weight_std, sample_rows=1 << 16)
 
 
+def test_band_workload_leaf_sampled():
+    w = workloads.WORKLOADS["band"]
+    run_conv(workloads.make_coords("band"), w.cin, w.cout, torch.bfloat16, "leaf", "band leaf window", seed=w.index,
+             std=w.weight_std, sample_rows=1 << 16)
+
+
 def test_identity_kernel_both_paths():
     igc = _igc()
     c = _cluster_coords(3, 16, 100, seed=3)
@@ -140,6 +147,7 @@ def test_identity_kernel_both_paths():
     wb = torch.zeros(27, 32, 32, device="cuda", dtype=torch.bfloat16)
     wb[13] = torch.eye(32, device="cuda", dtype=torch.bfloat16)
     assert torch.equal(igc.sparse_conv(g, fb, wb, path="leaf"), fb)
+    assert torch.equal(igc.sparse_conv(g, f16, w16, path="leaf"), f16)  # 64 channels on the leaf window
 
 
 def test_path_selection_and_errors():
@@ -148,6 +156,11 @@ def test_path_selection_and_errors():
     assert g.select_path(torch.float32, 8, 8) == "leaf"
     assert g.select_path(torch.bfloat16, 64, 64) == "ggs"
     assert g.select_path(torch.bfloat16, 32, 32) == "leaf"  # the only bf16 path below 64 outputs
+    assert g.select_path(torch.bfloat16, 64, 32) == "leaf"
+    cube = np.stack(np.meshgrid(*[np.arange(32)] * 3, indexing="ij"), -1).reshape(-1, 3).astype(np.int32)
+    dense = igc.grid_build(to_dev(cube))  # 64 full leaves
+    assert dense.leaf_occupancy == 1.0
+    assert dense.select_path(torch.bfloat16, 64, 64) == "leaf"  # 64 input channels: leaf window above 0.5
     f = torch.randn(g.n_voxels, 8, device="cuda")
     w = torch.randn(27, 8, 8, device="cuda")
     with pytest.raises(igc.IgcError):
