@@ -524,13 +524,24 @@ __global__ __launch_bounds__(256) void k_hist(const uint64_t* __restrict__ keys,
 // [w*64*kSortKPT, (w+1)*64*kSortKPT), 64 consecutive keys per round): the lanes holding the
 // same digit are found with BITS ballots, and the first of them adds their number to the
 // wave's count of that digit, so no two lanes update one counter in the same round.
-template <int BITS>
+// STABLE = false (the first pass of a sort): ranks come from one LDS atomic add per key, in
+// whatever order the adds land. An LSD sort needs only its later passes to keep the order of
+// equal digits; the first pass has no earlier order to keep.
+template <int BITS, bool STABLE>
 __device__ __forceinline__ void rank_keys(const uint64_t* __restrict__ src, int64_t n, int64_t wbase, int shift,
                                           uint64_t* key, uint32_t* rank, uint32_t* cnt) {
   const int lane = lane_id();
   const uint64_t lt_mask = (1ull << lane) - 1ull;
 #pragma unroll
   for (int r = 0; r < kSortKPT; ++r) key[r] = wbase + r * 64 < n ? src[wbase + r * 64] : 0ull;
+  if constexpr (!STABLE) {
+#pragma unroll
+    for (int r = 0; r < kSortKPT; ++r) {
+      const uint32_t d = (uint32_t)(key[r] >> shift) & ((1u << BITS) - 1u);
+      rank[r] = wbase + r * 64 < n ? atomicAdd(&cnt[d], 1u) : 0u;
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < kSortKPT; ++r) {
     const bool valid = wbase + r * 64 < n;
@@ -594,7 +605,7 @@ __global__ __launch_bounds__(kThreads) void k_radix_scan(const uint32_t* __restr
 
 // Step 3: stable scatter of one tile to its digits' runs. Thread tid owns the J consecutive
 // digits [tid J, tid J + J).
-template <int BITS>
+template <int BITS, bool STABLE>
 __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint64_t* __restrict__ src,
                                                             uint64_t* __restrict__ dst, int64_t n, int shift,
                                                             const uint32_t* __restrict__ off, int64_t T,
@@ -618,7 +629,7 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint64_t* __re
   uint64_t key[kSortKPT];
   uint32_t rank[kSortKPT];
   const int64_t wbase = tile_base + wave * (64 * kSortKPT) + lane_id();
-  rank_keys<BITS>(src, n, wbase, shift, key, rank, s_cnt[wave]);
+  rank_keys<BITS, STABLE>(src, n, wbase, shift, key, rank, s_cnt[wave]);
   __syncthreads();
 
   // Tile counts of the owned digits, per-wave exclusive offsets and the tile scan.
@@ -668,10 +679,13 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint64_t* __re
 
 template <int BITS>
 void radix_pass(const uint64_t* src, uint64_t* dst, int64_t n, int shift, const uint32_t* hist, uint32_t* cnt,
-                uint32_t* off, int64_t tiles, uint32_t* guard, hipStream_t s) {
+                uint32_t* off, int64_t tiles, uint32_t* guard, bool first, hipStream_t s) {
   k_radix_hist<BITS><<<(unsigned)tiles, kThreads, 0, s>>>(src, n, shift, cnt, tiles);
   k_radix_scan<<<1u << BITS, kThreads, 0, s>>>(cnt, tiles, hist, off);
-  k_radix_scatter<BITS><<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, shift, off, tiles, guard);
+  if (first)
+    k_radix_scatter<BITS, false><<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, shift, off, tiles, guard);
+  else
+    k_radix_scatter<BITS, true><<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, shift, off, tiles, guard);
 }
 
 // Sorts keys[0..n) (in a, scratch b) over the digits of ps; returns the buffer holding the
@@ -689,8 +703,8 @@ int radix_sort(uint64_t* a, uint64_t* b, int64_t n, PassSpec ps, const uint32_t*
   for (int p = 0; p < ps.passes; ++p) {
     const int shift = ps.lo_bit + ps.bits * p;
     const uint32_t* hp = hist + ((size_t)p << ps.bits);
-    if (ps.bits == 8) radix_pass<8>(src, dst, n, shift, hp, cnt, off, tiles, guard, s);
-    else radix_pass<9>(src, dst, n, shift, hp, cnt, off, tiles, guard, s);
+    if (ps.bits == 8) radix_pass<8>(src, dst, n, shift, hp, cnt, off, tiles, guard, p == 0, s);
+    else radix_pass<9>(src, dst, n, shift, hp, cnt, off, tiles, guard, p == 0, s);
     IGC_HIP(hipGetLastError(), "igc_grid_build: radix pass launch");
     std::swap(src, dst);
   }
