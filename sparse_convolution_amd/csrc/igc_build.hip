@@ -122,7 +122,10 @@ int fill_u64(uint64_t* p, int64_t n, uint64_t v, hipStream_t s) {
 
 // ------------------------------------------------------------------------------ root tiles
 
-__device__ void insert_tile(uint64_t* keys, uint32_t mask, uint32_t limit, uint64_t key, BuildState* st) {
+// A key that is new to the table also goes to list[its insertion number] while that number is
+// below list_cap, so that up to list_cap distinct tiles need no compaction pass.
+__device__ void insert_tile(uint64_t* keys, uint32_t mask, uint32_t limit, uint64_t key, BuildState* st,
+                            uint64_t* list, uint32_t list_cap) {
   uint32_t s = hash_tile(key) & mask;
   for (uint32_t p = 0; p < limit; ++p) {
     uint64_t cur = keys[s];  // cached read first; a stale empty slot is settled by the CAS
@@ -132,7 +135,8 @@ __device__ void insert_tile(uint64_t* keys, uint32_t mask, uint32_t limit, uint6
       const unsigned long long prev = atomicCAS((unsigned long long*)&keys[s], (unsigned long long)kEmptyKey,
                                                 (unsigned long long)key);
       if (prev == kEmptyKey) {
-        atomicAdd(&st->n_tiles, 1u);
+        const uint32_t idx = atomicAdd(&st->n_tiles, 1u);
+        if (idx < list_cap) list[idx] = key;
         return;
       }
       if (prev == key) return;
@@ -149,7 +153,8 @@ __device__ void insert_tile(uint64_t* keys, uint32_t mask, uint32_t limit, uint6
 // fit the LDS set go to the table directly. Also records OR / AND of keys and in-tile offsets.
 __global__ __launch_bounds__(256) void k_tile_insert(const int32_t* __restrict__ ijk, int64_t n,
                                                      uint64_t* __restrict__ keys, uint32_t mask, uint32_t limit,
-                                                     uint64_t* __restrict__ partial, BuildState* st) {
+                                                     uint64_t* __restrict__ partial, BuildState* st,
+                                                     uint64_t* __restrict__ list, uint32_t list_cap) {
   __shared__ uint64_t s_red[4][4];
   __shared__ uint64_t s_set[kTileCache];
   const int lane = lane_id();
@@ -211,14 +216,15 @@ __global__ __launch_bounds__(256) void k_tile_insert(const int32_t* __restrict__
               break;
             }
           }
-          if (!placed) insert_tile(keys, mask, limit, lk, st);
+          if (!placed) insert_tile(keys, mask, limit, lk, st, list, list_cap);
         }
         pending &= ~same;
       }
     }
   }
   __syncthreads();
-  if (threadIdx.x < kTileCache && s_set[threadIdx.x] != kEmptyKey) insert_tile(keys, mask, limit, s_set[threadIdx.x], st);
+  if (threadIdx.x < kTileCache && s_set[threadIdx.x] != kEmptyKey)
+    insert_tile(keys, mask, limit, s_set[threadIdx.x], st, list, list_cap);
   off_or = wave_or64(off_or);
   off_and = wave_and64(off_and);
   key_or = wave_or64(key_or);
@@ -303,10 +309,9 @@ __global__ void k_tile_compact(const uint64_t* __restrict__ keys, uint32_t cap, 
   }
 }
 
-// Bitonic sort of up to kSmallSort keys in one workgroup of 1024 threads.
-__global__ __launch_bounds__(1024) void k_sort_small(const uint64_t* __restrict__ in, uint64_t* __restrict__ out,
-                                                     int n) {
-  __shared__ uint64_t s[kSmallSort];
+// Bitonic sort of up to kSmallSort keys in LDS by one workgroup of 1024 threads (s holds the
+// keys ascending afterwards, padded with kEmptyKey to a power of two).
+__device__ __forceinline__ void bitonic_sort_lds(const uint64_t* __restrict__ in, uint64_t* s, int n) {
   int p2 = 2;
   while (p2 < n) p2 <<= 1;
   for (int t = threadIdx.x; t < p2; t += blockDim.x) s[t] = t < n ? in[t] : kEmptyKey;
@@ -326,7 +331,6 @@ __global__ __launch_bounds__(1024) void k_sort_small(const uint64_t* __restrict_
       __syncthreads();
     }
   }
-  for (int t = threadIdx.x; t < n; t += blockDim.x) out[t] = s[t];
 }
 
 // Slot of tile key k (present by construction); flags the guard if it is missing.
@@ -346,6 +350,21 @@ __global__ void k_tile_rank(const uint64_t* __restrict__ sorted, int64_t U, cons
   for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < U; r += (int64_t)gridDim.x * blockDim.x) {
     const int64_t s = probe_slot(keys, mask, sorted[r], st);
     if (s >= 0) vals[s] = (int32_t)r;
+  }
+}
+
+// Up to kSmallSort tile keys: bitonic sort in one workgroup, then each key's rank into the
+// table (the sort and the rank pass of larger tile sets in one launch).
+__global__ __launch_bounds__(1024) void k_sort_rank_small(const uint64_t* __restrict__ in, uint64_t* __restrict__ out,
+                                                          int n, const uint64_t* __restrict__ keys,
+                                                          int32_t* __restrict__ vals, uint32_t mask, BuildState* st) {
+  __shared__ uint64_t s[kSmallSort];
+  bitonic_sort_lds(in, s, n);
+  for (int t = threadIdx.x; t < n; t += blockDim.x) {
+    const uint64_t k = s[t];
+    out[t] = k;
+    const int64_t slot = probe_slot(keys, mask, k, st);
+    if (slot >= 0) vals[slot] = t;
   }
 }
 
@@ -1143,7 +1162,8 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
     IGC_HIP(hipGetLastError(), "igc_grid_build: init launch");
     const uint32_t limit = (uint32_t)std::min<uint64_t>(cap, 4096);
     const int nbt = grid_for((n_in + 3) / 4, 256, kTileBlocks);
-    k_tile_insert<<<nbt, 256, 0, s>>>(d_ijk, n_in, root_keys, (uint32_t)(cap - 1), limit, partial, st);
+    k_tile_insert<<<nbt, 256, 0, s>>>(d_ijk, n_in, root_keys, (uint32_t)(cap - 1), limit, partial, st, tile_list,
+                                      (uint32_t)kSmallSort);
     IGC_HIP(hipGetLastError(), "igc_grid_build: tile insert launch");
     k_reduce_bits<<<1, 256, 0, s>>>(partial, nbt, st);
     IGC_HIP(hipGetLastError(), "igc_grid_build: tile bits launch");
@@ -1162,16 +1182,17 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   if (U < 1 || (uint64_t)U > (1ull << 27))
     return set_error(U < 1 ? IGC_ERR_INTERNAL : IGC_ERR_RANGE, "igc_grid_build: root tile count out of range");
 
+  // Up to kSmallSort tiles the tile pass has listed them already; more are compacted from the table.
   if (U > kSmallSort) {
     if ((rc = ar.get_extra(&tile_list, U * sizeof(uint64_t), "igc_grid_build: tile list"))) return rc;
     if ((rc = ar.get_extra(&tile_tmp, U * sizeof(uint64_t), "igc_grid_build: tile list"))) return rc;
+    k_tile_compact<<<grid_for((int64_t)cap, 256, 1024), 256, 0, s>>>(root_keys, (uint32_t)cap, tile_list, (uint32_t)U,
+                                                                     st);
+    IGC_HIP(hipGetLastError(), "igc_grid_build: tile compaction launch");
   }
-  k_tile_compact<<<grid_for((int64_t)cap, 256, 1024), 256, 0, s>>>(root_keys, (uint32_t)cap, tile_list, (uint32_t)U,
-                                                                   st);
-  IGC_HIP(hipGetLastError(), "igc_grid_build: tile compaction launch");
   uint64_t* tiles_sorted = tile_tmp;
   if (U <= kSmallSort) {
-    k_sort_small<<<1, 1024, 0, s>>>(tile_list, tile_tmp, (int)U);
+    k_sort_rank_small<<<1, 1024, 0, s>>>(tile_list, tile_tmp, (int)U, root_keys, root_vals, (uint32_t)(cap - 1), st);
     IGC_HIP(hipGetLastError(), "igc_grid_build: tile sort launch");
   } else {
     const PassSpec tps = pass_spec(key_var);
@@ -1187,9 +1208,9 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
     if ((rc = radix_sort(tile_list, tile_tmp, U, tps, hist + kMaxPasses * kMaxBins, tcnt, tcnt + ttiles * kMaxBins, ttiles,
                          &st->guard, s, &tiles_sorted)))
       return rc;
+    k_tile_rank<<<grid_for(U, 256, 1024), 256, 0, s>>>(tiles_sorted, U, root_keys, root_vals, (uint32_t)(cap - 1), st);
+    IGC_HIP(hipGetLastError(), "igc_grid_build: tile rank launch");
   }
-  k_tile_rank<<<grid_for(U, 256, 1024), 256, 0, s>>>(tiles_sorted, U, root_keys, root_vals, (uint32_t)(cap - 1), st);
-  IGC_HIP(hipGetLastError(), "igc_grid_build: tile rank launch");
 
   // key2, its histograms and its sort over the varying bit span.
   int rank_bits = 0;
