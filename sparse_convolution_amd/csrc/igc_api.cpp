@@ -19,6 +19,7 @@ thread_local std::string g_last_error;
 std::mutex g_pool_mutex;
 std::vector<int> g_pool_ready;
 thread_local void* g_staging = nullptr;
+thread_local void* g_staging_dev = nullptr;  // the same pinned buffer as the device addresses it
 thread_local size_t g_staging_bytes = 0;
 
 // The per-device cached workspace block (see Workspace).
@@ -131,14 +132,24 @@ void ws_release(Workspace* w, hipStream_t s) {
   *w = Workspace{};
 }
 
-void* host_staging(size_t bytes) {
+void* host_staging(size_t bytes, void** device_view) {
   if (g_staging_bytes < bytes) {
     if (g_staging) (void)hipHostFree(g_staging);
     g_staging = nullptr;
+    g_staging_dev = nullptr;
     g_staging_bytes = 0;
-    if (hipHostMalloc(&g_staging, bytes, hipHostMallocDefault) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    void* d = nullptr;
+    if (hipHostMalloc(&p, bytes, hipHostMallocDefault) != hipSuccess) return nullptr;
+    if (hipHostGetDevicePointer(&d, p, 0) != hipSuccess) {
+      (void)hipHostFree(p);
+      return nullptr;
+    }
+    g_staging = p;
+    g_staging_dev = d;
     g_staging_bytes = bytes;
   }
+  if (device_view) *device_view = g_staging_dev;
   return g_staging;
 }
 

@@ -72,6 +72,17 @@ struct BuildState {
   uint64_t counts[4];         // N, F, Lw, U from the sorted keys
 };
 
+// The build state as the host reads it at a synchronisation: one thread of the last kernel
+// before it copies the state into pinned host memory and makes the copy visible system-wide,
+// which saves a device -> host copy (and its dispatch) per read-back.
+__device__ __forceinline__ void publish_state(const BuildState* st, BuildState* host) {
+  const uint64_t* src = reinterpret_cast<const uint64_t*>(st);
+  uint64_t* dst = reinterpret_cast<uint64_t*>(host);
+#pragma unroll
+  for (int w = 0; w < (int)(sizeof(BuildState) / 8); ++w) dst[w] = src[w];
+  __threadfence_system();
+}
+
 // ------------------------------------------------------------------------------ utilities
 
 // Zeroes fill[0 .. nfill) and copies src[0 .. ncopy) to dst (one launch for both).
@@ -252,7 +263,8 @@ __global__ __launch_bounds__(256) void k_tile_insert(const int32_t* __restrict__
 }
 
 // OR / AND of the tile pass's per-workgroup partials into the state. One workgroup.
-__global__ __launch_bounds__(256) void k_reduce_bits(const uint64_t* __restrict__ partial, int nb, BuildState* st) {
+__global__ __launch_bounds__(256) void k_reduce_bits(const uint64_t* __restrict__ partial, int nb, BuildState* st,
+                                                     BuildState* host) {
   __shared__ uint64_t s_red[4][4];
   uint64_t off_or = 0, off_and = ~0ull, key_or = 0, key_and = ~0ull;
   constexpr int R = 8;  // partials per thread and round, loaded before any is combined
@@ -295,6 +307,7 @@ __global__ __launch_bounds__(256) void k_reduce_bits(const uint64_t* __restrict_
     st->off_and = off_and;
     st->key_or = key_or;
     st->key_and = key_and;
+    publish_state(st, host);
   }
 }
 
@@ -813,7 +826,8 @@ __global__ __launch_bounds__(256) void k_count(const uint64_t* __restrict__ keys
 // Exclusive scan of the per-block packed counts into 64-bit prefixes per block (fields 1..3
 // of four), and the totals F, Lw, U. One workgroup.
 __global__ __launch_bounds__(1024) void k_scan_blocks(const uint64_t* __restrict__ block_counts, int64_t nb,
-                                                      uint64_t* __restrict__ prefix, BuildState* st) {
+                                                      uint64_t* __restrict__ prefix, BuildState* st,
+                                                      BuildState* host) {
   __shared__ uint64_t s_tmp[16];
   const int64_t per = (nb + 1023) / 1024;
   const int64_t b0 = threadIdx.x * per;
@@ -827,8 +841,10 @@ __global__ __launch_bounds__(1024) void k_scan_blocks(const uint64_t* __restrict
       prefix[b * 4 + c] = excl[c];
       excl[c] += (block_counts[b] >> (16 * c)) & 0xFFFFull;
     }
-  if (threadIdx.x == 0)
+  if (threadIdx.x == 0) {
     for (int c = 1; c < 4; ++c) st->counts[c] = tot[c];
+    publish_state(st, host);
+  }
 }
 
 // ------------------------------------------------------------------------------ registration
@@ -1004,7 +1020,8 @@ __global__ __launch_bounds__(256) void k_leaf_count(LeafRec* __restrict__ leaf, 
 }
 
 // In-place exclusive scan of v[0..nb); the total is the voxel count N. One workgroup.
-__global__ __launch_bounds__(1024) void k_scan_groups(uint64_t* __restrict__ v, int64_t nb, BuildState* st) {
+__global__ __launch_bounds__(1024) void k_scan_groups(uint64_t* __restrict__ v, int64_t nb, BuildState* st,
+                                                      BuildState* host) {
   __shared__ uint64_t s_tmp[16];
   uint64_t carry = 0;
   for (int64_t b0 = 0; b0 < nb; b0 += 1024) {
@@ -1015,7 +1032,10 @@ __global__ __launch_bounds__(1024) void k_scan_groups(uint64_t* __restrict__ v, 
     if (b < nb) v[b] = carry + ex;
     carry += tot;
   }
-  if (threadIdx.x == 0) st->counts[0] = carry;
+  if (threadIdx.x == 0) {
+    st->counts[0] = carry;
+    publish_state(st, host);
+  }
 }
 
 __global__ __launch_bounds__(256) void k_leaf_offset(LeafRec* __restrict__ leaf, int64_t F,
@@ -1154,8 +1174,9 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   uint64_t* tile_tmp = ar.take<uint64_t>((size_t)kSmallSort * 8);
   uint64_t* root_keys = ar.take<uint64_t>((size_t)cap * 12);
   if (!root_keys) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: workspace layout");
-  BuildState* h = (BuildState*)host_staging(sizeof(BuildState));
-  if (!h) return set_error(IGC_ERR_OOM, "igc_grid_build: pinned staging buffer");
+  BuildState* hd = nullptr;  // the staging buffer as kernels write it
+  BuildState* h = (BuildState*)host_staging(sizeof(BuildState), (void**)&hd);
+  if (!h || !hd) return set_error(IGC_ERR_OOM, "igc_grid_build: pinned staging buffer");
 
   for (int attempt = 0;; ++attempt) {
     k_init_root<<<grid_for((int64_t)cap, 256, 4096), 256, 0, s>>>(st, root_keys, (int64_t)cap);
@@ -1165,9 +1186,8 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
     k_tile_insert<<<nbt, 256, 0, s>>>(d_ijk, n_in, root_keys, (uint32_t)(cap - 1), limit, partial, st, tile_list,
                                       (uint32_t)kSmallSort);
     IGC_HIP(hipGetLastError(), "igc_grid_build: tile insert launch");
-    k_reduce_bits<<<1, 256, 0, s>>>(partial, nbt, st);
+    k_reduce_bits<<<1, 256, 0, s>>>(partial, nbt, st, hd);  // also publishes the state to h
     IGC_HIP(hipGetLastError(), "igc_grid_build: tile bits launch");
-    IGC_HIP(hipMemcpyAsync(h, st, sizeof(BuildState), hipMemcpyDeviceToHost, s), "igc_grid_build: read tile count");
     IGC_HIP(hipStreamSynchronize(s), "igc_grid_build: tile pass");
     if (!h->overflow) break;
     if (cap >= full_cap || attempt >= 2)
@@ -1266,9 +1286,8 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   const int64_t nb = tiles;
   k_count<<<(unsigned)nb, kThreads, 0, s>>>(sorted, n_in, bcounts, kf.cs_lower, kf.cs_upper);
   IGC_HIP(hipGetLastError(), "igc_grid_build: count launch");
-  k_scan_blocks<<<1, 1024, 0, s>>>(bcounts, nb, bprefix, st);
+  k_scan_blocks<<<1, 1024, 0, s>>>(bcounts, nb, bprefix, st, hd);  // also publishes the state to h
   IGC_HIP(hipGetLastError(), "igc_grid_build: block scan launch");
-  IGC_HIP(hipMemcpyAsync(h, st, sizeof(BuildState), hipMemcpyDeviceToHost, s), "igc_grid_build: read counts");
   IGC_HIP(hipStreamSynchronize(s), "igc_grid_build: sort and count");
   if (h->guard) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: device bounds check failed before registration");
   const int64_t F = (int64_t)h->counts[1], Lw = (int64_t)h->counts[2];
@@ -1323,22 +1342,24 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   const int64_t groups = (F + kLeafGroup - 1) / kLeafGroup;
   uint64_t* gsum = bprefix;  // the block prefixes are consumed by the register pass
   if ((size_t)groups * 8 > (size_t)tiles * 32) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: leaf scan workspace");
-  k_leaf_count<<<(unsigned)groups, 256, 0, s>>>(g->leaf, F, gsum);
-  IGC_HIP(hipGetLastError(), "igc_grid_build: leaf count launch");
-  k_scan_groups<<<1, 1024, 0, s>>>(gsum, groups, st);
-  IGC_HIP(hipGetLastError(), "igc_grid_build: leaf scan launch");
-  if (groups > 1) {
-    k_leaf_offset<<<(unsigned)groups, 256, 0, s>>>(g->leaf, F, gsum);
-    IGC_HIP(hipGetLastError(), "igc_grid_build: leaf offset launch");
-  }
+  // Node prefixes and the leaf neighbour table (neither reads the leaves' rows) go before the
+  // leaf scan, so that the group scan, which publishes N, follows every kernel that can set
+  // the guard.
   const int64_t nbl = (Lw + 3) / 4;
   k_node_prefix<<<(unsigned)(nbl + (U + 3) / 4), 256, 0, s>>>(g->lower_mask, g->lower_pre, Lw, nbl, g->upper_mask,
                                                              g->upper_pre, U);
   IGC_HIP(hipGetLastError(), "igc_grid_build: node prefix launch");
   k_leaf_neighbors<<<grid_for(F * 27, 256, 8192), 256, 0, s>>>(g->view(), g->leaf_nbr);
   IGC_HIP(hipGetLastError(), "igc_grid_build: leaf neighbour launch");
+  k_leaf_count<<<(unsigned)groups, 256, 0, s>>>(g->leaf, F, gsum);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: leaf count launch");
+  k_scan_groups<<<1, 1024, 0, s>>>(gsum, groups, st, hd);  // also publishes the state (N) to h
+  IGC_HIP(hipGetLastError(), "igc_grid_build: leaf scan launch");
+  if (groups > 1) {
+    k_leaf_offset<<<(unsigned)groups, 256, 0, s>>>(g->leaf, F, gsum);
+    IGC_HIP(hipGetLastError(), "igc_grid_build: leaf offset launch");
+  }
   // Last read-back: the voxel count.
-  IGC_HIP(hipMemcpyAsync(h, st, sizeof(BuildState), hipMemcpyDeviceToHost, s), "igc_grid_build: read voxel count");
   IGC_HIP(hipStreamSynchronize(s), "igc_grid_build: registration");
   if (h->guard) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: device bounds check failed in registration");
   const int64_t N = (int64_t)h->counts[0];

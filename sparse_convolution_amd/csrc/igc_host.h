@@ -72,8 +72,9 @@ int hip_status(hipError_t e, const char* what);
 int dev_alloc(void** p, size_t bytes, hipStream_t s, const char* what);
 void dev_free(void* p, hipStream_t s);
 
-// Pinned host staging buffer of at least `bytes` for small device -> host reads.
-void* host_staging(size_t bytes);
+// Pinned host staging buffer (per host thread) of at least `bytes` for small device -> host
+// reads; *device_view (if given) receives the address kernels write it through.
+void* host_staging(size_t bytes, void** device_view = nullptr);
 
 // Temporary device workspace of one call. Each device keeps one block that is handed to one
 // call at a time and grows to the largest request (a call that finds it taken allocates its
