@@ -19,21 +19,25 @@
 //     (the OR and AND of all keys, taken in the tile pass, give that span).
 //  3. Keys are sorted by their leaf part (key2 >> 9) only: the voxel bits inside a leaf are
 //     OR-ed into the leaf's mask, so their order never matters, and the sort needs
-//     ceil(varying leaf-key bits / 8) passes instead of ceil(varying key bits / 8). The sort
-//     is an LSD radix sort with 8-bit digits over tiles of 4096 keys. Each pass is
+//     ceil(varying leaf-key bits / 9) passes instead of ceil(varying key bits / 9). The sort
+//     is an LSD radix sort with 8- or 9-bit digits over tiles of 4096 keys. Each pass is
 //     reduce-then-scan: per-tile digit counts, a scan of every digit's counts over the tiles,
-//     and a scatter that ranks the tile's keys with 64-lane ballots (stable multisplit), sorts
-//     them in LDS and writes them out as runs per digit. A single-pass form with decoupled
+//     and a scatter that ranks the tile's keys (LDS atomics in the first pass, which needs no
+//     stability; 64-lane ballots, a stable multisplit, in later ones), sorts them in LDS and
+//     writes them out as runs per digit. A single-pass form with decoupled
 //     look-back was measured slower here: with all tiles resident at once, late tiles walk
 //     back over hundreds of predecessors that have published only their own counts.
 //  4. Leaves, lower and upper nodes are counted in one pass over the sorted keys (a key
-//     starts a leaf / lower / upper when key>>9, key>>21, key>>36 differ from its
-//     predecessor); after the read-back of the counts, a second pass gives every key its
+//     starts a leaf / lower / upper when its leaf / lower / upper part differs from its
+//     predecessor's; the keys stay compacted, and those parts are compared at their compacted
+//     bit positions); after the read-back of the counts, a second pass gives every key its
 //     leaf / node rows from the scanned block counts and registers the nodes top-down. Leaf
 //     mask bits are OR-ed in (duplicates set the same bit), first in LDS per block of keys:
 //     leaves that lie inside the block are stored whole, the block's first and last leaf
 //     are OR-ed into memory. Unique voxels are then the masks' popcounts: a scan over the
-//     leaves gives every leaf its first row and the voxel count N (read back last).
+//     leaves gives every leaf its first row and the voxel count N (read back last). At each of
+//     the three read-backs the last kernel before it writes the build state into pinned host
+//     memory itself.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
