@@ -207,3 +207,40 @@ def test_kernel_map_forms(monkeypatch, form):
     check_grid(full, f"{form}: 37 full leaves")
     check_grid(workloads.make_coords("lidar"), f"{form}: lidar")
     check_grid(workloads.make_coords("leaf"), f"{form}: leaf")
+
+
+def test_concurrent_builds_two_threads():
+    """Two host threads building on their own streams at once (the shared workspace is busy for
+    one of them, and each thread has its own pinned staging buffer for the read-backs) give
+    the same grids as builds one at a time."""
+    import threading
+    igc = _igc()
+    inputs = [workloads.make_coords("lidar"), workloads.make_coords("tiny"),
+              np.random.default_rng(41).integers(-3000, 3000, size=(200000, 3)).astype(np.int32)]
+    ref = [igc.grid_build(to_dev(c)).export() for c in inputs]
+    torch.cuda.synchronize()
+    say("concurrent builds")
+    results, errors = {}, []
+
+    def worker(tid):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                for rep in range(3):
+                    for i, c in enumerate(inputs):
+                        g = igc.grid_build(to_dev(c))
+                        stream.synchronize()
+                        results[(tid, rep, i)] = g.export()
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    assert len(results) == 2 * 3 * len(inputs)
+    for (tid, rep, i), topo in results.items():
+        for k in ref[i]:
+            assert np.array_equal(topo[k], ref[i][k]), (tid, rep, i, k)
