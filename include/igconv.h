@@ -65,7 +65,8 @@ typedef enum { IGC_F32 = 0, IGC_BF16 = 1 } igc_dtype;
 typedef enum {
   IGC_PATH_AUTO = 0, /* choose from measured leaf occupancy, neighbour count and channels */
   IGC_PATH_LEAF = 1, /* leaf-local dense convolution over an LDS window of 10^3 voxels */
-  IGC_PATH_GGS = 2   /* gather-GEMM-scatter over tiles of consecutive output rows */
+  IGC_PATH_GGS = 2,  /* gather-GEMM-scatter over tiles of consecutive output rows */
+  IGC_PATH_MIXED = 3 /* per-leaf dispatch: dense leaves on LEAF, the other rows on GGS */
 } igc_path;
 
 typedef struct {
@@ -169,6 +170,13 @@ int igc_kernel_map(const igc_grid* grid, const int32_t* h_offsets, int32_t K, in
  *           dtype BF16 (the leaf window of the pages' brick backend: a dense bf16 10^3 halo
  *           per leaf), cin in {16, 32, 64}, cout in {16, 32, 64}
  *     GGS : dtype BF16, cin a multiple of 32 up to 1024, cout a multiple of 64 up to 1024
+ *     MIXED (per-leaf dispatch, fVDB notes, "accelerated operators for sparse convolution",
+ *           which name picking a kernel per leaf by its local sparsity as future work): dtype
+ *           BF16 with a shape both LEAF and GGS support; leaves with at least 256 (cin >= 64)
+ *           or 103 active voxels run on the leaf window, all other rows on GGS (d_map
+ *           required). Never chosen by IGC_PATH_AUTO: measured slower than both single paths on
+ *           the workloads tried (the GGS pass costs nearly as much with the dense leaves' rows
+ *           removed).
  * Anything else returns IGC_ERR_UNSUPPORTED. d_out must not alias d_feats. */
 int igc_sparse_conv(const igc_grid* grid, const int32_t* d_map, const void* d_feats, int32_t dtype,
                     int32_t cin, const void* d_w, int32_t cout, void* d_out, int32_t path,

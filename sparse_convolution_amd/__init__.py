@@ -21,8 +21,8 @@ __all__ = [
 ]
 
 F32, BF16 = 0, 1
-PATH_AUTO, PATH_LEAF, PATH_GGS = 0, 1, 2
-_PATHS = {"auto": PATH_AUTO, "leaf": PATH_LEAF, "ggs": PATH_GGS}
+PATH_AUTO, PATH_LEAF, PATH_GGS, PATH_MIXED = 0, 1, 2, 3
+_PATHS = {"auto": PATH_AUTO, "leaf": PATH_LEAF, "ggs": PATH_GGS, "mixed": PATH_MIXED}
 
 
 def _stream(device: torch.device) -> ctypes.c_void_p:

@@ -168,6 +168,16 @@ static bool leaf_occupancy_ok(const igc_grid* g, int32_t cin) {
   return g->n_leaf > 0 && (double)g->n_voxels >= min_occ * 512.0 * (double)g->n_leaf;
 }
 
+// Active voxels from which a leaf takes the leaf window under per-leaf dispatch (the same
+// occupancy bars as the whole-grid choice below; IGC_MIXED_MIN overrides it).
+static uint32_t mixed_dense_min(int32_t cin) {
+  if (const char* e = std::getenv("IGC_MIXED_MIN")) {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v >= 1 && v <= 512) return (uint32_t)v;
+  }
+  return cin >= 64 ? 256u : 103u;
+}
+
 static int choose_path(const igc_grid* g, int32_t dtype, int32_t cin, int32_t cout, int32_t* path) {
   const bool leaf_ok = leaf_conv_supported(dtype, cin, cout);
   const bool ggs_ok = ggs_conv_supported(dtype, cin, cout);
@@ -320,7 +330,7 @@ int igc_sparse_conv(const igc_grid* g, const int32_t* d_map, const void* d_feats
   if (!g) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: grid is null");
   if (dtype != IGC_F32 && dtype != IGC_BF16) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: bad dtype");
   if (cin < 1 || cout < 1) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: cin and cout must be positive");
-  if (path != IGC_PATH_AUTO && path != IGC_PATH_LEAF && path != IGC_PATH_GGS)
+  if (path != IGC_PATH_AUTO && path != IGC_PATH_LEAF && path != IGC_PATH_GGS && path != IGC_PATH_MIXED)
     return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: bad path");
   if (!d_w) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: d_w is null");
   if (g->n_voxels > 0 && (!d_feats || !d_out))
@@ -335,10 +345,21 @@ int igc_sparse_conv(const igc_grid* g, const int32_t* d_map, const void* d_feats
     return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: leaf path does not support this dtype / cin / cout");
   if (p == IGC_PATH_GGS && !ggs_conv_supported(dtype, cin, cout))
     return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: gather-GEMM-scatter path does not support this dtype / cin / cout");
-  if (p == IGC_PATH_GGS && !d_map && g->n_voxels > 0)
+  if (p == IGC_PATH_MIXED && !(dtype == IGC_BF16 && leaf_conv_supported(dtype, cin, cout) &&
+                                ggs_conv_supported(dtype, cin, cout)))
+    return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: per-leaf dispatch needs a shape both paths support");
+  if ((p == IGC_PATH_GGS || p == IGC_PATH_MIXED) && !d_map && g->n_voxels > 0)
     return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: the gather-GEMM-scatter path needs d_map");
   if (g->n_voxels == 0) return IGC_OK;
   if (p == IGC_PATH_LEAF) return launch_conv_leaf(g, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream);
+  if (p == IGC_PATH_MIXED) {
+    // Per-leaf dispatch: leaves with at least dense_min active voxels on the leaf window, the
+    // rest on gather-GEMM-scatter (which writes zeros into the dense leaves' rows first).
+    const uint32_t dense_min = mixed_dense_min(cin);
+    int rc = launch_conv_ggs(g, d_map, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream, dense_min);
+    if (rc) return rc;
+    return launch_conv_leaf(g, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream, dense_min);
+  }
   return launch_conv_ggs(g, d_map, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream);
 }
 

@@ -75,15 +75,17 @@ __global__ void k_transpose_w(const uint16_t* __restrict__ w, uint16_t* __restri
 
 // Per tile: perm[tile*256 + p] = output row at sorted position p (-1 past N), and
 // blk[tile*27 + o] bit b = some row at sorted positions [16b, 16b+16) has a neighbour at o.
+// Rows with skip[row] != 0 (per-leaf dispatch: another path writes them) count as having none.
 __global__ __launch_bounds__(kBM) void k_ggs_plan(const int32_t* __restrict__ map, int64_t N,
-                                                  int32_t* __restrict__ perm, uint16_t* __restrict__ blk) {
+                                                  int32_t* __restrict__ perm, uint16_t* __restrict__ blk,
+                                                  const uint8_t* __restrict__ skip) {
   __shared__ uint64_t s_key[kBM];
   __shared__ uint32_t s_part[kBM / 64][kNOff];
   const int t = threadIdx.x;
   const int64_t r0 = (int64_t)blockIdx.x * kBM;
   const int64_t row = r0 + t;
   uint32_t mask = 0;
-  if (row < N) {
+  if (row < N && !(skip && skip[row])) {
 #pragma unroll
     for (int o = 0; o < kNOff; ++o) mask |= (map[(size_t)o * (size_t)N + row] >= 0 ? 1u : 0u) << o;
   }
@@ -376,10 +378,27 @@ void launch_main(int64_t n_tiles, int64_t col_tiles, const int32_t* map, int64_t
 
 }  // namespace
 
-int launch_ggs_plan(const int32_t* d_map, int64_t N, int32_t* perm, uint16_t* blk, hipStream_t s) {
+// Per-leaf dispatch: skip[r] = 1 for every row r of a leaf with at least min_count active
+// voxels, 0 for the others. One wave per leaf (rows offset .. offset + count of the leaf).
+__global__ __launch_bounds__(256) void k_dense_rows(const LeafRec* __restrict__ leaf, int64_t F, int64_t N,
+                                                    uint32_t min_count, uint8_t* __restrict__ skip) {
+  const int64_t f = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (f >= F) return;
+  const int lane = lane_id();
+  uint32_t c = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) c += (uint32_t)__popcll(leaf[f].mask[w]);
+  const uint64_t off = leaf[f].offset;
+  const uint8_t v = c >= min_count ? 1 : 0;
+  for (uint32_t t = (uint32_t)lane; t < c; t += 64)
+    if (off + t < (uint64_t)N) skip[off + t] = v;
+}
+
+int launch_ggs_plan(const int32_t* d_map, int64_t N, int32_t* perm, uint16_t* blk, hipStream_t s,
+                    const uint8_t* skip) {
   const int64_t n_tiles = (N + kBM - 1) / kBM;
   if (n_tiles == 0) return IGC_OK;
-  k_ggs_plan<<<(unsigned)n_tiles, kBM, 0, s>>>(d_map, N, perm, blk);
+  k_ggs_plan<<<(unsigned)n_tiles, kBM, 0, s>>>(d_map, N, perm, blk, skip);
   IGC_HIP(hipGetLastError(), "igc_sparse_conv: plan launch");
   return IGC_OK;
 }
@@ -390,24 +409,31 @@ bool ggs_conv_supported(int32_t dtype, int32_t cin, int32_t cout) {
 }
 
 int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype, int32_t cin,
-                    const void* d_w, int32_t cout, void* d_out, hipStream_t s) {
+                    const void* d_w, int32_t cout, void* d_out, hipStream_t s, uint32_t dense_min) {
   (void)dtype;
   const int64_t N = g->n_voxels;
   const int64_t n_tiles = (N + kBM - 1) / kBM;
   const size_t wt_bytes = align_up((size_t)27 * cin * cout * 2, 256);
   const size_t perm_bytes = align_up((size_t)n_tiles * kBM * 4, 256);
   const size_t blk_bytes = align_up((size_t)n_tiles * kNOff * 2, 256);
+  const size_t skip_bytes = dense_min ? align_up((size_t)N, 256) : 0;
   Workspace wsb;
-  int rc = ws_acquire(&wsb, wt_bytes + perm_bytes + blk_bytes, s, "igc_sparse_conv: gather-GEMM-scatter workspace");
+  int rc = ws_acquire(&wsb, wt_bytes + perm_bytes + blk_bytes + skip_bytes, s,
+                      "igc_sparse_conv: gather-GEMM-scatter workspace");
   if (rc) return rc;
   char* ws = (char*)wsb.p;
   uint16_t* wt = (uint16_t*)ws;
   int32_t* perm = (int32_t*)(ws + wt_bytes);
   uint16_t* blk = (uint16_t*)(ws + wt_bytes + perm_bytes);
+  uint8_t* skip = dense_min ? (uint8_t*)(ws + wt_bytes + perm_bytes + blk_bytes) : nullptr;
   k_transpose_w<<<256, 256, 0, s>>>((const uint16_t*)d_w, wt, cin, cout);
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess && skip) {
+    k_dense_rows<<<(unsigned)((g->n_leaf + 3) / 4), 256, 0, s>>>(g->leaf, g->n_leaf, N, dense_min, skip);
+    e = hipGetLastError();
+  }
   if (e == hipSuccess) {
-    k_ggs_plan<<<(unsigned)n_tiles, kBM, 0, s>>>(d_map, N, perm, blk);
+    k_ggs_plan<<<(unsigned)n_tiles, kBM, 0, s>>>(d_map, N, perm, blk, skip);
     e = hipGetLastError();
   }
   if (e == hipSuccess) {

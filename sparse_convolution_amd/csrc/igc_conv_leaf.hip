@@ -618,7 +618,8 @@ __device__ __forceinline__ int bf16_swz(int c) {
 // half of the last step) reads offset 0's cell against zero W.
 template <int CIN, int COUT>
 __global__ __launch_bounds__(256) void k_conv_leaf_bf16(GridView g, const uint16_t* __restrict__ feats,
-                                                        const uint16_t* __restrict__ wt, uint16_t* __restrict__ out) {
+                                                        const uint16_t* __restrict__ wt, uint16_t* __restrict__ out,
+                                                        uint32_t min_count) {
   static_assert(CIN == 16 || CIN == 32 || CIN == 64, "window cells of two, four or eight 16-byte granules");
   static_assert(COUT == 16 || COUT == 32 || COUT == 64, "column blocks per wave");
   constexpr int NS = COUT / 16;
@@ -640,6 +641,12 @@ __global__ __launch_bounds__(256) void k_conv_leaf_bf16(GridView g, const uint16
   const int kg = lane >> 4;  // k group of A and B, row group of D
   const int ns = wave % NS;
   const int64_t f = xcd_block(blockIdx.x, gridDim.x);
+  if (min_count) {  // per-leaf dispatch: sparser leaves belong to the other path (uniform exit)
+    uint32_t c = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) c += (uint32_t)__popcll(g.leaf[f].mask[w]);
+    if (c < min_count) return;
+  }
 
   // B fragments of this wave's column block (in flight while the leaf records arrive).
   bf16x8 wb[NCH];
@@ -733,7 +740,8 @@ __global__ __launch_bounds__(256) void k_conv_leaf_bf16(GridView g, const uint16
 }
 
 template <int CIN, int COUT>
-int launch_leaf_bf16(const igc_grid* g, const void* d_feats, const void* d_w, void* d_out, hipStream_t s) {
+int launch_leaf_bf16(const igc_grid* g, const void* d_feats, const void* d_w, void* d_out, hipStream_t s,
+                     uint32_t min_count) {
   constexpr int KP = (27 * CIN + 31) / 32 * 32;
   Workspace wsb;
   int rc = ws_acquire(&wsb, (size_t)COUT * KP * 2, s, "igc_sparse_conv: leaf W transpose");
@@ -743,7 +751,7 @@ int launch_leaf_bf16(const igc_grid* g, const void* d_feats, const void* d_w, vo
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) {
     k_conv_leaf_bf16<CIN, COUT><<<(unsigned)g->n_leaf, 256, 0, s>>>(g->view(), (const uint16_t*)d_feats, wt,
-                                                                   (uint16_t*)d_out);
+                                                                   (uint16_t*)d_out, min_count);
     e = hipGetLastError();
   }
   ws_release(&wsb, s);
@@ -783,18 +791,19 @@ bool leaf_conv_supported(int32_t dtype, int32_t cin, int32_t cout) {
 }
 
 int launch_conv_leaf(const igc_grid* g, const void* d_feats, int32_t dtype, int32_t cin, const void* d_w,
-                     int32_t cout, void* d_out, hipStream_t s) {
+                     int32_t cout, void* d_out, hipStream_t s, uint32_t min_count) {
+  if (min_count && dtype != IGC_BF16) return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: per-leaf dispatch dtype");
   if (dtype == IGC_BF16) {
     switch (cin * 1000 + cout) {
-      case 16016: return launch_leaf_bf16<16, 16>(g, d_feats, d_w, d_out, s);
-      case 16032: return launch_leaf_bf16<16, 32>(g, d_feats, d_w, d_out, s);
-      case 16064: return launch_leaf_bf16<16, 64>(g, d_feats, d_w, d_out, s);
-      case 32016: return launch_leaf_bf16<32, 16>(g, d_feats, d_w, d_out, s);
-      case 32032: return launch_leaf_bf16<32, 32>(g, d_feats, d_w, d_out, s);
-      case 32064: return launch_leaf_bf16<32, 64>(g, d_feats, d_w, d_out, s);
-      case 64016: return launch_leaf_bf16<64, 16>(g, d_feats, d_w, d_out, s);
-      case 64032: return launch_leaf_bf16<64, 32>(g, d_feats, d_w, d_out, s);
-      case 64064: return launch_leaf_bf16<64, 64>(g, d_feats, d_w, d_out, s);
+      case 16016: return launch_leaf_bf16<16, 16>(g, d_feats, d_w, d_out, s, min_count);
+      case 16032: return launch_leaf_bf16<16, 32>(g, d_feats, d_w, d_out, s, min_count);
+      case 16064: return launch_leaf_bf16<16, 64>(g, d_feats, d_w, d_out, s, min_count);
+      case 32016: return launch_leaf_bf16<32, 16>(g, d_feats, d_w, d_out, s, min_count);
+      case 32032: return launch_leaf_bf16<32, 32>(g, d_feats, d_w, d_out, s, min_count);
+      case 32064: return launch_leaf_bf16<32, 64>(g, d_feats, d_w, d_out, s, min_count);
+      case 64016: return launch_leaf_bf16<64, 16>(g, d_feats, d_w, d_out, s, min_count);
+      case 64032: return launch_leaf_bf16<64, 32>(g, d_feats, d_w, d_out, s, min_count);
+      case 64064: return launch_leaf_bf16<64, 64>(g, d_feats, d_w, d_out, s, min_count);
       default: return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: bf16 leaf path shape");
     }
   }

@@ -101,12 +101,16 @@ int launch_kernel_map(const igc_grid* g, const int32_t* h_offsets, int32_t K, in
                       hipStream_t s);
 bool leaf_conv_supported(int32_t dtype, int32_t cin, int32_t cout);
 bool ggs_conv_supported(int32_t dtype, int32_t cin, int32_t cout);
+// min_count > 0 (bf16 only): leaves with fewer active voxels are skipped (their rows untouched).
 int launch_conv_leaf(const igc_grid* g, const void* d_feats, int32_t dtype, int32_t cin, const void* d_w, int32_t cout,
-                     void* d_out, hipStream_t s);
+                     void* d_out, hipStream_t s, uint32_t min_count = 0);
+// dense_min > 0: rows of leaves with at least dense_min active voxels get no pairs (zero output).
 int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype, int32_t cin,
-                    const void* d_w, int32_t cout, void* d_out, hipStream_t s);
-// Mask-sorted tiles of 256 output rows (row order perm, 16-row blocks with pairs per offset blk).
-int launch_ggs_plan(const int32_t* d_map, int64_t N, int32_t* perm, uint16_t* blk, hipStream_t s);
+                    const void* d_w, int32_t cout, void* d_out, hipStream_t s, uint32_t dense_min = 0);
+// Mask-sorted tiles of 256 output rows (row order perm, 16-row blocks with pairs per offset blk);
+// rows with skip[row] != 0 (if skip is given) count as having no neighbours.
+int launch_ggs_plan(const int32_t* d_map, int64_t N, int32_t* perm, uint16_t* blk, hipStream_t s,
+                    const uint8_t* skip = nullptr);
 // Leaf-local fp32 weight gradient: `groups` partial dW blocks [groups][27][cin][cout] in `part`.
 bool wgrad_leaf_supported(int32_t cin, int32_t cout);
 int64_t wgrad_leaf_groups(const igc_grid* g);

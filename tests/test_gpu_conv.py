@@ -117,6 +117,21 @@ def test_lidar_workload_ggs():
              std=w.weight_std)
 
 
+@pytest.mark.parametrize("cin,cout", [(32, 64), (64, 64)])
+@pytest.mark.parametrize("dense_min", [None, "1", "512"])
+def test_mixed_path_per_leaf_dispatch(monkeypatch, cin, cout, dense_min):
+    # Per-leaf dispatch: dense leaves (full cubes) on the bf16 leaf window, the rest (a sparse
+    # shell and partly filled clusters) on gather-GEMM-scatter; thresholds that send every leaf
+    # to one side or leave only full leaves on the window must give the same result.
+    if dense_min is not None:
+        monkeypatch.setenv("IGC_MIXED_MIN", dense_min)
+    g3 = np.stack(np.meshgrid(*[np.arange(16)] * 3, indexing="ij"), -1).reshape(-1, 3)
+    c = np.concatenate([_cluster_coords(3, 20, 150, seed=cin + cout, fill=0.5), g3 + 600,
+                        workloads.make_coords("tiny") + 900]).astype(np.int32)
+    run_conv(c, cin, cout, torch.bfloat16, "mixed", f"mixed dense_min={dense_min}", seed=cin * 7 + cout,
+             std=1.0 / np.sqrt(27 * cin))
+
+
 def test_band_workload_ggs_sampled():
     w = workloads.WORKLOADS["band"]
     run_conv(workloads.make_coords("band"), w.cin, w.cout, torch.bfloat16, "ggs", "band", seed=w.index,
