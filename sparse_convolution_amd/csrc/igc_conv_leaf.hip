@@ -361,12 +361,11 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
     f32x4 acc[NS];
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) acc[ns] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q = 0; q < NCH; ++q) {
-      bf16x8 a[3];
+    // The three split fragments of chunk q (k past 27 CIN reads the cell of offset 0, a real
+    // neighbour, against zero W splits).
+    auto frag3 = [&](int q, bf16x8* a) {
 #pragma unroll
       for (int sp = 0; sp < 3; ++sp) {
-        // k past 27 CIN reads the cell of offset 0, a real neighbour, against zero W splits.
         if constexpr (CIN == 8) {
           a[sp] = *(const bf16x8*)&s_win[(cell0 + dcell[q][0]) * CS + sp * CIN];
         } else {
@@ -375,6 +374,18 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
           a[sp] = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
         }
       }
+    };
+    // Fragments are read RING - 1 chunks ahead of their MFMAs, held there by scheduling
+    // barriers (the compiler's own schedule reuses one register quad and waits on each read).
+    constexpr int RING = 3;
+    bf16x8 ring[RING][3];
+#pragma unroll
+    for (int d = 0; d < RING - 1; ++d)
+      if (d < NCH) frag3(d, ring[d]);
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      if (q + RING - 1 < NCH) frag3(q + RING - 1, ring[(q + RING - 1) % RING]);
+      const bf16x8* a = ring[q % RING];
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
         f32x4 c = acc[ns];
@@ -386,6 +397,7 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], wb[q][0][ns], c, 0, 0, 0);
         acc[ns] = c;
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // D: lane holds column lane%16 of rows 4*(lane/16) + j.
 #pragma unroll
