@@ -158,19 +158,53 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32_wide(GridView g, const fl
     f32x4 acc[NS];
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) acc[ns] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int o = 0; o < 27; ++o) {
+    // A value of step i = o KS + ks. With one column block the reads run PF steps ahead of
+    // their MFMAs, held there by scheduling barriers (the compiler's own schedule keeps two in
+    // flight); with two, each read already feeds two MFMAs and the prefetch measured slower.
+    auto aval = [&](int i) -> float {
+      const int o = i / KS, ks = i % KS;
       const int cell = cell0 + (o / 9) * 100 + ((o / 3) % 3) * 10 + o % 3;
       const int rot = win_rot<CIN>(cell);
+      return s_win[cell * CIN + (((ks + rot) & (KS - 1)) << 2) + kq];
+    };
+    constexpr int STEPS = 27 * KS;
+    auto step = [&](int i, float a) {
+      const int o = i / KS, ks = i % KS;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const float a = s_win[cell * CIN + (((ks + rot) & (KS - 1)) << 2) + kq];
+      for (int ns = 0; ns < NS; ++ns) {
+        float b;
+        if constexpr (kWRegs) b = wreg[(o * KS + ks) * NS + ns];
+        else b = s_w[(o * CIN + ks * 4 + kq) * COUTP + ns * 16 + rl];
+        acc[ns] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[ns], 0, 0, 0);
+      }
+    };
+    if constexpr (NS == 1) {
+      constexpr int PF = 8;
+      float ring[PF];
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns) {
-          float b;
-          if constexpr (kWRegs) b = wreg[(o * KS + ks) * NS + ns];
-          else b = s_w[(o * CIN + ks * 4 + kq) * COUTP + ns * 16 + rl];
-          acc[ns] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[ns], 0, 0, 0);
+      for (int d = 0; d < PF; ++d) ring[d] = aval(d);
+#pragma unroll
+      for (int i = 0; i < STEPS; ++i) {
+        const float a = ring[i % PF];
+        if (i + PF < STEPS) ring[i % PF] = aval(i + PF);
+        step(i, a);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int o = 0; o < 27; ++o) {
+        const int cell = cell0 + (o / 9) * 100 + ((o / 3) % 3) * 10 + o % 3;
+        const int rot = win_rot<CIN>(cell);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const float a = s_win[cell * CIN + (((ks + rot) & (KS - 1)) << 2) + kq];
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns) {
+            float b;
+            if constexpr (kWRegs) b = wreg[(o * KS + ks) * NS + ns];
+            else b = s_w[(o * CIN + ks * 4 + kq) * COUTP + ns * 16 + rl];
+            acc[ns] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[ns], 0, 0, 0);
+          }
         }
       }
     }
