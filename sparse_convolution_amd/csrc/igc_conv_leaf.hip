@@ -557,21 +557,30 @@ __global__ __launch_bounds__(256) void k_wgrad_leaf_f32(GridView g, int64_t n_le
       if (e < cnt4 * (COUT / 4)) ((float4*)s_dy)[e] = d[i];
     }
     __syncthreads();
-    for (uint32_t t0 = (uint32_t)wave * 4; t0 < count; t0 += 16) {
-      const uint32_t t = t0 + (uint32_t)kq;
-      const int cell0 = s_cell[t < count ? t : 0u];
-      float b[NS];
+    // Two K steps per round (t0 and t0 + 16), every read of both issued before their MFMAs:
+    // a step is a chain of LDS reads (cell, then window), which one step alone leaves exposed.
+    // Voxels past cnt4 (the second step of the last round) read dY as zero.
+    for (uint32_t t0 = (uint32_t)wave * 4; t0 < count; t0 += 32) {
+      float a[2][MB], b[2][NS];
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns) {
-        const int col = ns * 16 + rl;
-        b[ns] = col < COUT ? s_dy[t * COUT + col] : 0.f;
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t t = t0 + 16u * h + (uint32_t)kq;
+        const int cell0 = s_cell[t < count ? t : 0u];
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+          const int col = ns * 16 + rl;
+          b[h][ns] = col < COUT && t < cnt4 ? s_dy[t * COUT + col] : 0.f;
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) a[h][mb] = aoff[mb] >= 0 ? s_win[cell0 * CIN + aoff[mb]] : 0.f;
       }
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const float a = aoff[mb] >= 0 ? s_win[cell0 * CIN + aoff[mb]] : 0.f;
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns) acc[mb][ns] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b[ns], acc[mb][ns], 0, 0, 0);
-      }
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns)
+            acc[mb][ns] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[h][mb], b[h][ns], acc[mb][ns], 0, 0, 0);
     }
   }
   // Cross-wave sum in the window's space, fragment-major: wave 0 stores, waves 1..3 add in turn.
