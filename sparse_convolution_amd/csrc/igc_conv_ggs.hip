@@ -438,14 +438,16 @@ int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats
   }
   if (e == hipSuccess) {
     const bool k64 = cin % 64 == 0;
-    // Tile shapes measured on MI355X: 256 x 256 with eight waves (two per SIMD), 256 x 128
-    // with sixteen, 256 x 64 with eight (each wave 32 rows by all 64 channels: 2% faster on
-    // 64 -> 64 than 64 rows by 32); 32-channel chunks when cin is not a multiple of 64.
+    // Tile shapes measured on MI355X: 256 x 256 with eight waves (two per SIMD, each 128 rows
+    // by 64 channels: 64 rows by 128 is 0.5% slower on 128 -> 256), 256 x 128 with sixteen
+    // (each 32 rows by 64 channels: 1.6% faster on 128 -> 128 than 64 by 32), 256 x 64 with
+    // eight (each 32 rows by all 64 channels: 2% faster on 64 -> 64 than 64 by 32); 32-channel
+    // chunks when cin is not a multiple of 64.
     const int64_t n256 = cout / 256, n128 = cout / 128, n64 = cout / 64;
     if (cout % 256 == 0 && k64) {
       launch_main<256, 64, 2, 2, 8>(n_tiles, n256, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
     } else if (cout % 128 == 0 && k64) {
-      launch_main<128, 64, 4, 2, 16>(n_tiles, n128, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      launch_main<128, 64, 8, 2, 16>(n_tiles, n128, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
     } else if (cout % 128 == 0) {
       launch_main<128, 32, 2, 2, 8>(n_tiles, n128, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
     } else if (k64) {
