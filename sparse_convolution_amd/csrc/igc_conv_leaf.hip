@@ -773,7 +773,7 @@ __global__ __launch_bounds__(256) void k_conv_leaf_bf16(GridView g, const uint16
     // The reads run PF k-steps ahead of their MFMA, held there by scheduling barriers (the
     // compiler's own schedule keeps two in flight, and each MFMA then waits for most of an LDS
     // round trip).
-    constexpr int PF = CIN == 64 ? 6 : 8;
+    constexpr int PF = CIN == 16 ? 8 : 6;  // measured: 6 is 0.6% faster than 8 at 32 -> 32
     bf16x8 ring[PF];
 #pragma unroll
     for (int d = 0; d < PF; ++d) ring[d] = frag(d);
