@@ -69,6 +69,22 @@ typedef enum {
   IGC_PATH_MIXED = 3 /* per-leaf dispatch: dense leaves on LEAF, the other rows on GGS */
 } igc_path;
 
+/* Device memory provider. When a grid is created with an allocator (igc_grid_build,
+ * igc_conv_grid), every device allocation the library makes for that grid goes through it: the
+ * grid's own topology block (returned by igc_grid_destroy) and the temporaries of every later
+ * call on the grid (returned at the end of that call). Both are stream-ordered, like
+ * hipMallocAsync / hipFreeAsync and a PyTorch caching allocator: `alloc` returns memory usable
+ * by work enqueued on `stream` from now on (NULL on failure, which the calling function reports
+ * as IGC_ERR_OOM naming itself), and `release` hands back a block whose last use has been
+ * enqueued on `stream` (the provider may reuse it for work enqueued later on that stream).
+ * Blocks must be at least 256-byte aligned. The struct is copied; `ctx` must stay valid until
+ * the grid is destroyed. A NULL allocator selects the library's own per-device memory pool. */
+typedef struct igc_allocator {
+  void* (*alloc)(void* ctx, size_t bytes, igc_stream stream);
+  void (*release)(void* ctx, void* ptr, size_t bytes, igc_stream stream);
+  void* ctx;
+} igc_allocator;
+
 typedef struct {
   int64_t n_input;        /* coordinates passed to igc_grid_build (duplicates included) */
   int64_t n_voxels;       /* N: distinct active voxels = rows of every feature array */
@@ -78,9 +94,9 @@ typedef struct {
   int64_t topology_bytes; /* device bytes held by the grid */
   int32_t sort_passes;    /* 8-bit digit passes the build's radix sort ran */
   int32_t root_capacity;  /* slots of the root hash table */
-} igc_grid_info;
+} igc_grid_info_t;
 
-/* Host buffers for igc_grid_export, sized from igc_grid_info (U, Lw, F). A null pointer
+/* Host buffers for igc_grid_export, sized from igc_grid_info_t (U, Lw, F). A null pointer
  * skips that array. Layouts:
  *   root_key     uint64[U]      packed tile key of each upper node, ascending
  *   upper_origin int32[U,3]     coordinate of the node's first voxel (low 12 bits clear)
@@ -114,16 +130,21 @@ typedef struct {
  * n_in == 0 gives an empty grid) - fVDB notes, "GPU-accelerated IndexGrid build": root
  * tile keys, radix sort of per-tile 64-bit keys, run-length encoding, upper / lower / leaf
  * counts, allocation, top-down registration of nodes and leaf bit masks.
- * Host synchronisations: three - the root tile count and varying key bits (to plan the
- * sort), the node counts (to size the topology), and the voxel count N (reported by
- * igc_grid_info). If the root hash table overflows its first capacity the first step
- * repeats with a larger one (DriveRT, dynamic sizes). Errors: IGC_ERR_INVALID_ARG (out
- * null, d_ijk null with n_in > 0, n_in < 0), IGC_ERR_RANGE (n_in > 2^31-1), IGC_ERR_OOM, IGC_ERR_HIP,
- * IGC_ERR_CAPACITY, IGC_ERR_INTERNAL. On success *out owns one device allocation until
- * igc_grid_destroy. Temporaries come from a workspace block that the library keeps per device
- * and reuses across calls (grown to the largest request; a call that finds it in use allocates
- * its own). d_ijk may be freed once the stream reaches the end of the call. */
-int igc_grid_build(const int32_t* d_ijk, int64_t n_in, igc_stream stream, igc_grid** out);
+ * Memory: `alloc` (may be NULL, see igc_allocator) provides the grid's block and the build's
+ * temporaries. Host synchronisations: three - the root tile count and varying key bits (to plan
+ * the sort), the node counts (to size the topology), and the voxel count N (reported by
+ * igc_grid_info); none for n_in == 0 (no device work is done then). If the root hash table
+ * overflows its first capacity the first step repeats with a larger one (DriveRT, dynamic
+ * sizes). Errors: IGC_ERR_INVALID_ARG (out null, d_ijk null with n_in > 0, n_in < 0, an
+ * allocator without both functions), IGC_ERR_RANGE (n_in > 2^31-1), IGC_ERR_OOM (including an
+ * allocator returning NULL), IGC_ERR_HIP, IGC_ERR_CAPACITY, IGC_ERR_INTERNAL; every block taken
+ * so far is returned on error. On success *out owns one device allocation until
+ * igc_grid_destroy. Without an allocator the temporaries come from a workspace block that the
+ * library keeps per device and reuses across calls (grown to the largest request, returned by
+ * igc_release_memory; a call that finds it in use allocates its own). d_ijk may be freed once
+ * the stream reaches the end of the call. */
+int igc_grid_build(const int32_t* d_ijk, int64_t n_in, const igc_allocator* alloc, igc_stream stream,
+                   igc_grid** out);
 
 /* Frees the grid's device memory in order on the stream the grid was built on (no host
  * synchronisation): work already queued on that stream finishes reading the grid first. Work
@@ -132,7 +153,13 @@ int igc_grid_build(const int32_t* d_ijk, int64_t n_in, igc_stream stream, igc_gr
 int igc_grid_destroy(igc_grid* grid);
 
 /* Counts and sizes of the grid (host only, no device work). */
-int igc_grid_get_info(const igc_grid* grid, igc_grid_info* out);
+int igc_grid_info(const igc_grid* grid, igc_grid_info_t* out);
+
+/* Returns the library's cached device memory (the per-device workspace blocks and the free
+ * blocks of its memory pools) to the driver. Synchronises every device it holds memory on; no
+ * other library call may be in flight. Memory of grids built with an allocator is not held by
+ * the library and is not affected. */
+int igc_release_memory(void);
 
 /* d_out int32[N,3] (device): the active voxels in linear-index order. This is the row order
  * every feature array over the grid uses. */
@@ -202,17 +229,19 @@ int igc_sparse_conv_backward(const igc_grid* grid, const int32_t* d_map, const v
                              float* d_dw, int32_t path, igc_stream stream);
 
 /* Output grid of a 3x3x3 convolution with per-axis stride h_stride[0..2] (host, each 1, 2 or 3)
- * over `in` (fVDB notes, grid-to-grid ops ConvGrid and ConvTransposeGrid; the pages name the
- * ops without a formula, so the plain reading is taken), offsets d in {-1, 0, 1}^3:
+ * over `in` (the grid-to-grid ops ConvGrid and ConvTransposeGrid in the op table of the "ONNX
+ * Runtime support for fVDB operations" proposal; the pages name the ops without a formula, so
+ * the plain reading is taken), offsets d in {-1, 0, 1}^3:
  *     transposed == 0: y is active iff some active x of `in` has x = stride * y + d
  *                      (stride 1 gives the dilation of `in` by one voxel);
  *     transposed != 0: y is active iff y = stride * x + d for some active x of `in`.
  * The result is a new immutable grid (*out, library-owned, freed with igc_grid_destroy) in the
- * canonical order of igc_grid_build. Errors: IGC_ERR_UNSUPPORTED for strides outside 1..3,
+ * canonical order of igc_grid_build, whose memory comes from `alloc` (may be NULL) as for
+ * igc_grid_build. Errors: IGC_ERR_UNSUPPORTED for strides outside 1..3,
  * IGC_ERR_RANGE when an output coordinate leaves the int32 range; *out is then NULL. One host
  * synchronization more than igc_grid_build. */
-int igc_conv_grid(const igc_grid* in, const int32_t* h_stride, int32_t transposed, igc_stream stream,
-                  igc_grid** out);
+int igc_conv_grid(const igc_grid* in, const int32_t* h_stride, int32_t transposed, const igc_allocator* alloc,
+                  igc_stream stream, igc_grid** out);
 
 /* Neighbour map between two grids for that convolution (DriveRT, "Shared neighbour maps", for
  * two coordinate domains): d_map int32[27, N_out] (device, caller-owned, N_out = voxels of

@@ -16,7 +16,7 @@ from ._lib import IgcError
 
 __all__ = [
     "Grid", "grid_build", "kernel_map", "sparse_conv", "sparse_conv_backward", "conv_grid", "conv_map",
-    "sparse_conv_between", "standard_offsets", "IgcError",
+    "sparse_conv_between", "standard_offsets", "release_memory", "IgcError",
     "PATH_AUTO", "PATH_LEAF", "PATH_GGS",
 ]
 
@@ -52,6 +52,40 @@ def standard_offsets() -> np.ndarray:
     return np.ascontiguousarray(np.stack([di.ravel(), dj.ravel(), dk.ravel()], axis=1))
 
 
+# PyTorch's caching allocator as the library's memory provider (igc_allocator): the grid's
+# block and every call's temporaries are torch allocations on the call's stream.
+def _torch_alloc(ctx, nbytes, stream):
+    try:
+        return torch.cuda.caching_allocator_alloc(int(nbytes), torch.cuda.current_device(), int(stream or 0))
+    except Exception:  # reported by the library as IGC_ERR_OOM
+        return None
+
+
+def _torch_release(ctx, ptr, nbytes, stream):
+    try:
+        torch.cuda.caching_allocator_delete(ptr)
+    except Exception:
+        pass
+
+
+_TORCH_ALLOC_CB = _lib.ALLOC_FN(_torch_alloc)
+_TORCH_RELEASE_CB = _lib.RELEASE_FN(_torch_release)
+TORCH_ALLOCATOR = _lib.Allocator(_TORCH_ALLOC_CB, _TORCH_RELEASE_CB, None)
+
+
+def _allocator(memory: str):
+    if memory == "torch":
+        return ctypes.byref(TORCH_ALLOCATOR)
+    if memory == "library":
+        return None
+    raise ValueError("memory must be 'torch' (PyTorch's caching allocator) or 'library' (the library's pool)")
+
+
+def release_memory() -> None:
+    """Returns the library's own cached device memory (igc_release_memory)."""
+    _lib.check(_lib.load().igc_release_memory())
+
+
 class Grid:
     """An immutable IndexGrid on one GPU (igc_grid_build)."""
 
@@ -59,7 +93,7 @@ class Grid:
         self._h = handle
         self.device = device
         info = _lib.GridInfo()
-        _lib.check(_lib.load().igc_grid_get_info(self._h, ctypes.byref(info)))
+        _lib.check(_lib.load().igc_grid_info(self._h, ctypes.byref(info)))
         self.n_input = info.n_input
         self.n_voxels = info.n_voxels
         self.n_leaf = info.n_leaf
@@ -127,11 +161,14 @@ def _dtype_code(dtype: torch.dtype) -> int:
     raise TypeError(f"unsupported dtype {dtype}")
 
 
-def grid_build(ijk: torch.Tensor) -> Grid:
-    """IndexGrid from int32[n, 3] device coordinates (any order, duplicates allowed)."""
+def grid_build(ijk: torch.Tensor, memory: str = "torch") -> Grid:
+    """IndexGrid from int32[n, 3] device coordinates (any order, duplicates allowed). Its device
+    memory, and that of every later call on it, comes from PyTorch's caching allocator
+    (memory="torch") or from the library's own pool (memory="library")."""
     ijk = _device_tensor(ijk, "ijk", torch.int32, 3)
     h = ctypes.c_void_p()
-    _lib.check(_lib.load().igc_grid_build(_ptr(ijk), ijk.shape[0], _stream(ijk.device), ctypes.byref(h)))
+    _lib.check(_lib.load().igc_grid_build(_ptr(ijk), ijk.shape[0], _allocator(memory), _stream(ijk.device),
+                                          ctypes.byref(h)))
     return Grid(h, ijk.device)
 
 
@@ -208,13 +245,13 @@ def _stride_array(stride) -> np.ndarray:
     return np.ascontiguousarray(s)
 
 
-def conv_grid(grid: Grid, stride=2, transposed: bool = False) -> Grid:
+def conv_grid(grid: Grid, stride=2, transposed: bool = False, memory: str = "torch") -> Grid:
     """Output grid of a 3x3x3 convolution with the given stride (int or 3 ints, each 1..3) over
-    `grid`, or of the transposed convolution (igc_conv_grid)."""
+    `grid`, or of the transposed convolution (igc_conv_grid); memory as for grid_build."""
     s = _stride_array(stride)
     h = ctypes.c_void_p()
     _lib.check(_lib.load().igc_conv_grid(grid.handle, s.ctypes.data_as(ctypes.c_void_p), int(bool(transposed)),
-                                         _stream(grid.device), ctypes.byref(h)))
+                                         _allocator(memory), _stream(grid.device), ctypes.byref(h)))
     return Grid(h, grid.device)
 
 

@@ -8,7 +8,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libigconv.so")
 
 EXPORTS = (
-    "igc_grid_build", "igc_grid_destroy", "igc_grid_get_info", "igc_grid_active_ijk",
+    "igc_grid_build", "igc_grid_destroy", "igc_grid_info", "igc_release_memory", "igc_grid_active_ijk",
     "igc_grid_ijk_to_index", "igc_grid_export", "igc_kernel_map", "igc_sparse_conv",
     "igc_sparse_conv_backward", "igc_conv_grid", "igc_conv_map", "igc_sparse_conv_between", "igc_select_path",
     "igc_last_error",
@@ -26,6 +26,15 @@ class GridInfo(ctypes.Structure):
         ("n_lower", ctypes.c_int64), ("n_upper", ctypes.c_int64), ("topology_bytes", ctypes.c_int64),
         ("sort_passes", ctypes.c_int32), ("root_capacity", ctypes.c_int32),
     ]
+
+
+# igc_allocator: stream-ordered device memory provider (include/igconv.h).
+ALLOC_FN = ctypes.CFUNCTYPE(ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p)
+RELEASE_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p)
+
+
+class Allocator(ctypes.Structure):
+    _fields_ = [("alloc", ALLOC_FN), ("release", RELEASE_FN), ("ctx", ctypes.c_void_p)]
 
 
 class TopologyHost(ctypes.Structure):
@@ -54,16 +63,17 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     sig = {
-        "igc_grid_build": [P, i64, P, ctypes.POINTER(P)],
+        "igc_grid_build": [P, i64, ctypes.POINTER(Allocator), P, ctypes.POINTER(P)],
         "igc_grid_destroy": [P],
-        "igc_grid_get_info": [P, ctypes.POINTER(GridInfo)],
+        "igc_grid_info": [P, ctypes.POINTER(GridInfo)],
+        "igc_release_memory": [],
         "igc_grid_active_ijk": [P, P, P],
         "igc_grid_ijk_to_index": [P, P, i64, P, P],
         "igc_grid_export": [P, ctypes.POINTER(TopologyHost)],
         "igc_kernel_map": [P, P, i32, P, P, P],
         "igc_sparse_conv": [P, P, P, i32, i32, P, i32, P, i32, P],
         "igc_sparse_conv_backward": [P, P, P, i32, i32, P, i32, P, P, P, i32, P],
-        "igc_conv_grid": [P, P, i32, P, ctypes.POINTER(P)],
+        "igc_conv_grid": [P, P, i32, ctypes.POINTER(Allocator), P, ctypes.POINTER(P)],
         "igc_conv_map": [P, P, P, i32, P, P],
         "igc_sparse_conv_between": [P, P, i64, P, i32, i32, P, i32, P, P],
         "igc_select_path": [P, i32, i32, i32, ctypes.POINTER(i32)],

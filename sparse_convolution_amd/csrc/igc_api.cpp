@@ -16,21 +16,61 @@ namespace igc {
 
 namespace {
 thread_local std::string g_last_error;
-std::mutex g_pool_mutex;
-std::vector<int> g_pool_ready;
 thread_local void* g_staging = nullptr;
 thread_local void* g_staging_dev = nullptr;  // the same pinned buffer as the device addresses it
 thread_local size_t g_staging_bytes = 0;
 
-// The per-device cached workspace block (see Workspace).
-struct WsSlot {
-  void* p = nullptr;
-  size_t bytes = 0;
-  bool busy = false;
-  hipEvent_t released = nullptr;  // recorded on the last user's stream at release
+// Per device: the library's private stream-ordered memory pool (free blocks kept across calls:
+// repeated builds do not return memory to the driver between calls; the device's default pool
+// and other users of it are left as they are) and the cached workspace block (see Workspace).
+struct DevMem {
+  hipMemPool_t pool = nullptr;
+  bool pool_tried = false;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  bool ws_busy = false;
+  hipEvent_t ws_released = nullptr;  // recorded on the last user's stream at release
 };
-std::mutex g_ws_mutex;
-std::vector<WsSlot> g_ws;
+std::mutex g_mem_mutex;
+std::vector<DevMem> g_mem;
+
+DevMem& dev_mem(int dev) {  // g_mem_mutex held
+  if ((int)g_mem.size() <= dev) g_mem.resize(dev + 1);
+  return g_mem[dev];
+}
+
+// The device's private pool, created on first use (nullptr if the runtime refuses one: the
+// device's default pool then serves, unchanged).
+hipMemPool_t private_pool(int dev) {  // g_mem_mutex held
+  DevMem& m = dev_mem(dev);
+  if (!m.pool_tried) {
+    m.pool_tried = true;
+    hipMemPoolProps props{};
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    if (hipMemPoolCreate(&pool, &props) == hipSuccess) {
+      uint64_t threshold = ~0ull;
+      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+      m.pool = pool;
+    } else {
+      (void)hipGetLastError();
+    }
+  }
+  return m.pool;
+}
+
+int pool_alloc(void** p, size_t bytes, int dev, hipStream_t s) {  // g_mem_mutex held
+  hipMemPool_t pool = private_pool(dev);
+  const hipError_t e = pool ? hipMallocFromPoolAsync(p, bytes, pool, s) : hipMallocAsync(p, bytes, s);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    (void)hipGetLastError();
+  }
+  return e;
+}
 }  // namespace
 
 int set_error(int status, const std::string& msg) {
@@ -45,68 +85,62 @@ int hip_status(hipError_t e, const char* what) {
   return set_error(e == hipErrorOutOfMemory ? IGC_ERR_OOM : IGC_ERR_HIP, m);
 }
 
-// Keeps freed blocks in the device's default pool so repeated builds do not return memory
-// to the driver between calls.
-static void prepare_pool(int dev) {
-  std::lock_guard<std::mutex> lock(g_pool_mutex);
-  if ((int)g_pool_ready.size() <= dev) g_pool_ready.resize(dev + 1, 0);
-  if (g_pool_ready[dev]) return;
-  hipMemPool_t pool;
-  if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
-    uint64_t threshold = ~0ull;
-    (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
-  }
-  g_pool_ready[dev] = 1;
-}
-
-int dev_alloc(void** p, size_t bytes, hipStream_t s, const char* what) {
+int dev_alloc(void** p, size_t bytes, hipStream_t s, const char* what, const igc_allocator* a) {
   *p = nullptr;
+  if (bytes == 0) bytes = 256;
+  if (a) {
+    *p = a->alloc(a->ctx, bytes, (igc_stream)s);
+    if (!*p)
+      return set_error(IGC_ERR_OOM, std::string(what) + ": the caller's allocator returned NULL for " +
+                                        std::to_string(bytes) + " bytes");
+    return IGC_OK;
+  }
   int dev = 0;
   IGC_HIP(hipGetDevice(&dev), what);
-  prepare_pool(dev);
-  if (bytes == 0) bytes = 256;
-  hipError_t e = hipMallocAsync(p, bytes, s);
-  if (e != hipSuccess) {
-    *p = nullptr;
+  hipError_t e;
+  {
+    std::lock_guard<std::mutex> lock(g_mem_mutex);
+    e = (hipError_t)pool_alloc(p, bytes, dev, s);
+  }
+  if (e != hipSuccess)
     return set_error(e == hipErrorOutOfMemory ? IGC_ERR_OOM : IGC_ERR_HIP,
                      std::string(what) + ": device allocation of " + std::to_string(bytes) +
                          " bytes failed: " + hipGetErrorString(e));
-  }
   return IGC_OK;
 }
 
-void dev_free(void* p, hipStream_t s) {
-  if (p) (void)hipFreeAsync(p, s);
+void dev_free(void* p, size_t bytes, hipStream_t s, const igc_allocator* a) {
+  if (!p) return;
+  if (a) a->release(a->ctx, p, bytes ? bytes : 256, (igc_stream)s);
+  else (void)hipFreeAsync(p, s);
 }
 
-int ws_acquire(Workspace* w, size_t bytes, hipStream_t s, const char* what) {
+int ws_acquire(Workspace* w, size_t bytes, hipStream_t s, const char* what, const igc_allocator* a) {
   *w = Workspace{};
+  if (bytes == 0) bytes = 256;
+  if (a) {
+    w->a = a;
+    w->bytes = bytes;
+    return dev_alloc(&w->p, bytes, s, what, a);
+  }
   int dev = 0;
   IGC_HIP(hipGetDevice(&dev), what);
-  prepare_pool(dev);
-  if (bytes == 0) bytes = 256;
   {
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
-    WsSlot& sl = g_ws[dev];
-    if (!sl.busy) {
-      if (sl.released) IGC_HIP(hipStreamWaitEvent(s, sl.released, 0), what);
-      if (sl.bytes < bytes) {
-        if (sl.p) (void)hipFreeAsync(sl.p, s);
-        sl.p = nullptr;
-        sl.bytes = 0;
+    std::lock_guard<std::mutex> lock(g_mem_mutex);
+    DevMem& m = dev_mem(dev);
+    if (!m.ws_busy) {
+      if (m.ws_released) IGC_HIP(hipStreamWaitEvent(s, m.ws_released, 0), what);
+      if (m.ws_bytes < bytes) {
+        if (m.ws) (void)hipFreeAsync(m.ws, s);
+        m.ws = nullptr;
+        m.ws_bytes = 0;
         const size_t want = std::max(bytes, align_up(bytes + bytes / 4, 1 << 20));
-        if (hipMallocAsync(&sl.p, want, s) == hipSuccess) {
-          sl.bytes = want;
-        } else {
-          sl.p = nullptr;
-          (void)hipGetLastError();
-        }
+        if (pool_alloc(&m.ws, want, dev, s) == hipSuccess) m.ws_bytes = want;
       }
-      if (sl.p) {
-        sl.busy = true;
-        w->p = sl.p;
-        w->bytes = sl.bytes;
+      if (m.ws) {
+        m.ws_busy = true;
+        w->p = m.ws;
+        w->bytes = m.ws_bytes;
         w->dev = dev;
         w->cached = true;
         return IGC_OK;
@@ -121,13 +155,13 @@ int ws_acquire(Workspace* w, size_t bytes, hipStream_t s, const char* what) {
 void ws_release(Workspace* w, hipStream_t s) {
   if (!w->p) return;
   if (!w->cached) {
-    dev_free(w->p, s);
+    dev_free(w->p, w->bytes, s, w->a);
   } else {
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    WsSlot& sl = g_ws[w->dev];
-    if (!sl.released) (void)hipEventCreateWithFlags(&sl.released, hipEventDisableTiming);
-    if (sl.released) (void)hipEventRecord(sl.released, s);
-    sl.busy = false;
+    std::lock_guard<std::mutex> lock(g_mem_mutex);
+    DevMem& m = dev_mem(w->dev);
+    if (!m.ws_released) (void)hipEventCreateWithFlags(&m.ws_released, hipEventDisableTiming);
+    if (m.ws_released) (void)hipEventRecord(m.ws_released, s);
+    m.ws_busy = false;
   }
   *w = Workspace{};
 }
@@ -155,9 +189,11 @@ void* host_staging(size_t bytes, void** device_view) {
 
 static void free_grid(igc_grid* g) {
   if (!g) return;
-  dev_free(g->block, g->stream);  // the root table lives in the same allocation
+  dev_free(g->block, g->bytes, g->stream, grid_alloc(g));  // the root table lives in the same allocation
   delete g;
 }
+
+static bool allocator_ok(const igc_allocator* a) { return !a || (a->alloc && a->release); }
 
 static bool leaf_occupancy_ok(const igc_grid* g, int32_t cin) {
   // Leaf path pays for 512 positions per leaf; the fVDB notes put its break-even against a
@@ -191,29 +227,67 @@ static int choose_path(const igc_grid* g, int32_t dtype, int32_t cin, int32_t co
                                             " with cin " + std::to_string(cin) + " and cout " + std::to_string(cout));
 }
 
+uint32_t mixed_dense_rows(int32_t cin) { return mixed_dense_min(cin); }
+
+int check_conv_args(const char* fn, const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype,
+                    int32_t cin, const void* d_w, int32_t cout, void* d_out, int32_t* path) {
+  const std::string f(fn);
+  if (!g) return set_error(IGC_ERR_INVALID_ARG, f + ": grid is null");
+  if (dtype != IGC_F32 && dtype != IGC_BF16) return set_error(IGC_ERR_INVALID_ARG, f + ": bad dtype");
+  if (cin < 1 || cout < 1) return set_error(IGC_ERR_INVALID_ARG, f + ": cin and cout must be positive");
+  const int32_t p0 = *path;
+  if (p0 != IGC_PATH_AUTO && p0 != IGC_PATH_LEAF && p0 != IGC_PATH_GGS && p0 != IGC_PATH_MIXED)
+    return set_error(IGC_ERR_INVALID_ARG, f + ": bad path");
+  if (!d_w) return set_error(IGC_ERR_INVALID_ARG, f + ": d_w is null");
+  if (g->n_voxels > 0 && (!d_feats || !d_out)) return set_error(IGC_ERR_INVALID_ARG, f + ": d_feats or d_out is null");
+  if (d_feats && d_feats == d_out) return set_error(IGC_ERR_INVALID_ARG, f + ": d_out aliases d_feats");
+  int32_t p = p0;
+  if (p == IGC_PATH_AUTO) {
+    const int rc = choose_path(g, dtype, cin, cout, &p);
+    if (rc) return rc;
+  }
+  if (p == IGC_PATH_LEAF && !leaf_conv_supported(dtype, cin, cout))
+    return set_error(IGC_ERR_UNSUPPORTED, f + ": leaf path does not support this dtype / cin / cout");
+  if (p == IGC_PATH_GGS && !ggs_conv_supported(dtype, cin, cout))
+    return set_error(IGC_ERR_UNSUPPORTED, f + ": gather-GEMM-scatter path does not support this dtype / cin / cout");
+  if (p == IGC_PATH_MIXED &&
+      !(dtype == IGC_BF16 && leaf_conv_supported(dtype, cin, cout) && ggs_conv_supported(dtype, cin, cout)))
+    return set_error(IGC_ERR_UNSUPPORTED, f + ": per-leaf dispatch needs a shape both paths support");
+  if ((p == IGC_PATH_GGS || p == IGC_PATH_MIXED) && !d_map && g->n_voxels > 0)
+    return set_error(IGC_ERR_INVALID_ARG, f + ": the gather-GEMM-scatter path needs d_map");
+  *path = p;
+  return IGC_OK;
+}
+
 }  // namespace igc
 
 using namespace igc;
 
 extern "C" {
 
-int igc_grid_build(const int32_t* d_ijk, int64_t n_in, igc_stream stream, igc_grid** out) {
+int igc_grid_build(const int32_t* d_ijk, int64_t n_in, const igc_allocator* alloc, igc_stream stream,
+                   igc_grid** out) {
   clear_error();
   if (!out) return set_error(IGC_ERR_INVALID_ARG, "igc_grid_build: out is null");
   *out = nullptr;
   if (n_in < 0) return set_error(IGC_ERR_INVALID_ARG, "igc_grid_build: n_in is negative");
   if (n_in > 0 && !d_ijk) return set_error(IGC_ERR_INVALID_ARG, "igc_grid_build: d_ijk is null");
   if (n_in > INT32_MAX) return set_error(IGC_ERR_RANGE, "igc_grid_build: n_in exceeds 2^31-1");
+  if (!allocator_ok(alloc))
+    return set_error(IGC_ERR_INVALID_ARG, "igc_grid_build: the allocator needs both alloc and release");
   igc_grid* g = new (std::nothrow) igc_grid();
   if (!g) return set_error(IGC_ERR_OOM, "igc_grid_build: host allocation");
   g->stream = (hipStream_t)stream;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) {
-    delete g;
-    return hip_status(e, "igc_grid_build: hipGetDevice");
+  if (alloc) g->alloc = *alloc;
+  if (n_in > 0) {  // an empty grid does no device work
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+      delete g;
+      return hip_status(e, "igc_grid_build: hipGetDevice");
+    }
+    g->device = dev;
   }
-  g->device = dev;
   const int rc = build_grid(d_ijk, n_in, (hipStream_t)stream, g);
   if (rc != IGC_OK) {
     free_grid(g);
@@ -230,9 +304,9 @@ int igc_grid_destroy(igc_grid* grid) {
   return IGC_OK;
 }
 
-int igc_grid_get_info(const igc_grid* g, igc_grid_info* out) {
+int igc_grid_info(const igc_grid* g, igc_grid_info_t* out) {
   clear_error();
-  if (!g || !out) return set_error(IGC_ERR_INVALID_ARG, "igc_grid_get_info: null argument");
+  if (!g || !out) return set_error(IGC_ERR_INVALID_ARG, "igc_grid_info: null argument");
   out->n_input = g->n_input;
   out->n_voxels = g->n_voxels;
   out->n_leaf = g->n_leaf;
@@ -242,6 +316,36 @@ int igc_grid_get_info(const igc_grid* g, igc_grid_info* out) {
   out->sort_passes = g->sort_passes;
   out->root_capacity = (int32_t)g->root_cap;
   return IGC_OK;
+}
+
+int igc_release_memory(void) {
+  clear_error();
+  std::lock_guard<std::mutex> lock(g_mem_mutex);
+  int cur = 0;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  int rc = IGC_OK;
+  for (int dev = 0; dev < (int)g_mem.size(); ++dev) {
+    DevMem& m = g_mem[dev];
+    if (!m.ws && !m.pool) continue;
+    if (m.ws_busy) {
+      rc = set_error(IGC_ERR_INVALID_ARG, "igc_release_memory: a library call is in flight on device " +
+                                              std::to_string(dev));
+      continue;
+    }
+    if (hipSetDevice(dev) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+      rc = hip_status(hipGetLastError(), "igc_release_memory: device synchronize");
+      continue;
+    }
+    if (m.ws) {
+      (void)hipFreeAsync(m.ws, nullptr);
+      (void)hipStreamSynchronize(nullptr);
+      m.ws = nullptr;
+      m.ws_bytes = 0;
+    }
+    if (m.pool) (void)hipMemPoolTrimTo(m.pool, 0);
+  }
+  if (have_cur) (void)hipSetDevice(cur);
+  return rc;
 }
 
 int igc_grid_active_ijk(const igc_grid* g, int32_t* d_out, igc_stream stream) {
@@ -327,36 +431,15 @@ int igc_select_path(const igc_grid* g, int32_t dtype, int32_t cin, int32_t cout,
 int igc_sparse_conv(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype, int32_t cin,
                     const void* d_w, int32_t cout, void* d_out, int32_t path, igc_stream stream) {
   clear_error();
-  if (!g) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: grid is null");
-  if (dtype != IGC_F32 && dtype != IGC_BF16) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: bad dtype");
-  if (cin < 1 || cout < 1) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: cin and cout must be positive");
-  if (path != IGC_PATH_AUTO && path != IGC_PATH_LEAF && path != IGC_PATH_GGS && path != IGC_PATH_MIXED)
-    return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: bad path");
-  if (!d_w) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: d_w is null");
-  if (g->n_voxels > 0 && (!d_feats || !d_out))
-    return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: d_feats or d_out is null");
-  if (d_feats && d_feats == d_out) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: d_out aliases d_feats");
   int32_t p = path;
-  if (p == IGC_PATH_AUTO) {
-    const int rc = choose_path(g, dtype, cin, cout, &p);
-    if (rc) return rc;
-  }
-  if (p == IGC_PATH_LEAF && !leaf_conv_supported(dtype, cin, cout))
-    return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: leaf path does not support this dtype / cin / cout");
-  if (p == IGC_PATH_GGS && !ggs_conv_supported(dtype, cin, cout))
-    return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: gather-GEMM-scatter path does not support this dtype / cin / cout");
-  if (p == IGC_PATH_MIXED && !(dtype == IGC_BF16 && leaf_conv_supported(dtype, cin, cout) &&
-                                ggs_conv_supported(dtype, cin, cout)))
-    return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: per-leaf dispatch needs a shape both paths support");
-  if ((p == IGC_PATH_GGS || p == IGC_PATH_MIXED) && !d_map && g->n_voxels > 0)
-    return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv: the gather-GEMM-scatter path needs d_map");
-  if (g->n_voxels == 0) return IGC_OK;
+  int rc = check_conv_args("igc_sparse_conv", g, d_map, d_feats, dtype, cin, d_w, cout, d_out, &p);
+  if (rc || g->n_voxels == 0) return rc;
   if (p == IGC_PATH_LEAF) return launch_conv_leaf(g, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream);
   if (p == IGC_PATH_MIXED) {
     // Per-leaf dispatch: leaves with at least dense_min active voxels on the leaf window, the
     // rest on gather-GEMM-scatter (which writes zeros into the dense leaves' rows first).
     const uint32_t dense_min = mixed_dense_min(cin);
-    int rc = launch_conv_ggs(g, d_map, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream, dense_min);
+    rc = launch_conv_ggs(g, d_map, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream, dense_min);
     if (rc) return rc;
     return launch_conv_leaf(g, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream, dense_min);
   }
@@ -400,12 +483,14 @@ int igc_sparse_conv_backward(const igc_grid* g, const int32_t* d_map, const void
   return launch_conv_backward(g, d_map, d_feats, dtype, cin, d_w, cout, d_dout, d_dfeats, d_dw, p, (hipStream_t)stream);
 }
 
-int igc_conv_grid(const igc_grid* in, const int32_t* h_stride, int32_t transposed, igc_stream stream,
-                  igc_grid** out) {
+int igc_conv_grid(const igc_grid* in, const int32_t* h_stride, int32_t transposed, const igc_allocator* alloc,
+                  igc_stream stream, igc_grid** out) {
   clear_error();
   if (!out) return set_error(IGC_ERR_INVALID_ARG, "igc_conv_grid: out is null");
   *out = nullptr;
   if (!in || !h_stride) return set_error(IGC_ERR_INVALID_ARG, "igc_conv_grid: in or h_stride is null");
+  if (!allocator_ok(alloc))
+    return set_error(IGC_ERR_INVALID_ARG, "igc_conv_grid: the allocator needs both alloc and release");
   int n[3];
   if (!conv_grid_slots(h_stride, transposed, n))
     return set_error(IGC_ERR_UNSUPPORTED, "igc_conv_grid: strides must be 1, 2 or 3");
@@ -413,6 +498,7 @@ int igc_conv_grid(const igc_grid* in, const int32_t* h_stride, int32_t transpose
   if (!g) return set_error(IGC_ERR_OOM, "igc_conv_grid: host allocation");
   g->stream = (hipStream_t)stream;
   g->device = in->device;
+  if (alloc) g->alloc = *alloc;
   const int rc = build_conv_grid(in, h_stride, transposed, (hipStream_t)stream, g);
   if (rc != IGC_OK) {
     free_grid(g);
@@ -448,7 +534,7 @@ int igc_sparse_conv_between(const igc_grid* out, const int32_t* d_map, int64_t n
     return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_between: d_map, d_feats or d_out is null");
   if (d_feats && d_feats == d_out) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_between: d_out aliases d_feats");
   if (out->n_voxels == 0) return IGC_OK;
-  return launch_conv_ggs(out, d_map, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream);
+  return launch_conv_ggs(out, d_map, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream, 0, n_in);
 }
 
 const char* igc_last_error(void) { return g_last_error.c_str(); }

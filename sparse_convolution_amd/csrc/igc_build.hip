@@ -1102,17 +1102,18 @@ __global__ __launch_bounds__(256) void k_leaf_neighbors(GridView g, int32_t* __r
 // released on every exit path.
 struct Arena {
   hipStream_t s;
+  const igc_allocator* a;
   Workspace ws;
   char* base = nullptr;
   size_t used = 0, cap = 0;
-  std::vector<void*> extra;  // rare oversized pieces
-  explicit Arena(hipStream_t st) : s(st) {}
+  std::vector<std::pair<void*, size_t>> extra;  // rare oversized pieces
+  Arena(hipStream_t st, const igc_allocator* al) : s(st), a(al) {}
   ~Arena() {
-    for (void* p : extra) dev_free(p, s);
+    for (const auto& e : extra) dev_free(e.first, e.second, s, a);
     ws_release(&ws, s);
   }
   int reserve(size_t bytes) {
-    const int rc = ws_acquire(&ws, bytes, s, "igc_grid_build: workspace");
+    const int rc = ws_acquire(&ws, bytes, s, "igc_grid_build: workspace", a);
     base = (char*)ws.p;
     cap = bytes;
     return rc;
@@ -1125,8 +1126,8 @@ struct Arena {
   }
   template <class T>
   int get_extra(T** out, size_t bytes, const char* what) {
-    const int rc = dev_alloc((void**)out, bytes, s, what);
-    if (rc == IGC_OK) extra.push_back(*out);
+    const int rc = dev_alloc((void**)out, bytes, s, what, a);
+    if (rc == IGC_OK) extra.push_back({(void*)*out, bytes});
     return rc;
   }
 };
@@ -1138,7 +1139,15 @@ constexpr int kTileBlocks = 2048;  // workgroups of the tile pass
 
 int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   g->n_input = n_in;
-  if (n_in == 0) return IGC_OK;
+  if (n_in == 0) {
+    // No device work. A grid built with an allocator still owns one (minimal) block from it.
+    if (grid_alloc(g)) {
+      const int rc = dev_alloc(&g->block, 256, s, "igc_grid_build: topology", grid_alloc(g));
+      if (rc) return rc;
+      g->bytes = 256;
+    }
+    return IGC_OK;
+  }
 
   // Root table (keys, then upper-node rows): first capacity from an estimate, then the size
   // that always suffices (U <= n_in) - the capacity retry. It is built in the workspace and
@@ -1161,7 +1170,7 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
                     2 * align_up((size_t)n_in * 8, 256) + 2 * align_up((size_t)sort_tiles * kMaxBins * 4, 256) +
                     align_up((size_t)tiles * 8, 256) + align_up((size_t)tiles * 32, 256) +
                     2 * align_up((size_t)kSmallSort * 8, 256) + align_up((size_t)cap * 12, 256);
-  Arena ar(s);
+  Arena ar(s, grid_alloc(g));
   int rc = ar.reserve(ws);
   if (rc) return rc;
   BuildState* st = ar.take<BuildState>(sizeof(BuildState));
@@ -1310,7 +1319,7 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
                o_upf = carve(U * 4), o_loo = carve(Lw * 16), o_lop = carve(Lw * 64 * 2), o_lof = carve(Lw * 4),
                o_lfo = carve(F * 16), o_nbr = carve(F * 27 * 4), o_root = carve(cap * 12);
   char* blk = nullptr;
-  if ((rc = dev_alloc((void**)&blk, off, s, "igc_grid_build: topology"))) return rc;
+  if ((rc = dev_alloc((void**)&blk, off, s, "igc_grid_build: topology", grid_alloc(g)))) return rc;
   g->block = blk;
   g->bytes = off;
   g->root_keys = (uint64_t*)(blk + o_root);

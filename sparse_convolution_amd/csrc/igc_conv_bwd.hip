@@ -334,7 +334,8 @@ int launch_wgrad_bf16(const igc_grid* g, const int32_t* d_map, const void* d_fea
   const size_t blk_bytes = align_up((size_t)n_tiles * kNOff * 2, 256);
   const size_t part_bytes = align_up((size_t)chunks * E * 4, 256);
   Workspace wsb;
-  int rc = ws_acquire(&wsb, perm_bytes + blk_bytes + part_bytes, s, "igc_sparse_conv_backward: wgrad workspace");
+  int rc = ws_acquire(&wsb, perm_bytes + blk_bytes + part_bytes, s, "igc_sparse_conv_backward: wgrad workspace",
+                      grid_alloc(g));
   if (rc) return rc;
   char* ws = (char*)wsb.p;
   int32_t* perm = (int32_t*)ws;
@@ -359,7 +360,7 @@ int launch_wgrad_f32(const igc_grid* g, const int32_t* d_map, const void* d_feat
   if (wgrad_leaf_supported(cin, cout)) {
     const int64_t groups = wgrad_leaf_groups(g);
     Workspace wsb;
-    int rc = ws_acquire(&wsb, (size_t)groups * E * 4, s, "igc_sparse_conv_backward: wgrad partials");
+    int rc = ws_acquire(&wsb, (size_t)groups * E * 4, s, "igc_sparse_conv_backward: wgrad partials", grid_alloc(g));
     if (rc) return rc;
     float* part = (float*)wsb.p;
     rc = launch_wgrad_leaf(g, d_feats, cin, d_dout, cout, part, groups, s);
@@ -373,7 +374,7 @@ int launch_wgrad_f32(const igc_grid* g, const int32_t* d_map, const void* d_feat
   rpc = (rpc + kStage - 1) / kStage * kStage;
   chunks = (N + rpc - 1) / rpc;
   Workspace wsb;
-  int rc = ws_acquire(&wsb, (size_t)chunks * E * 4, s, "igc_sparse_conv_backward: wgrad partials");
+  int rc = ws_acquire(&wsb, (size_t)chunks * E * 4, s, "igc_sparse_conv_backward: wgrad partials", grid_alloc(g));
   if (rc) return rc;
   float* part = (float*)wsb.p;
   k_wgrad_f32<<<(unsigned)(kNOff * chunks), 256, 0, s>>>(d_map, N, (const float*)d_feats, (const float*)d_dout, cin,
@@ -409,7 +410,8 @@ int launch_conv_backward(const igc_grid* g, const int32_t* d_map, const void* d_
   const size_t esize = dtype == IGC_BF16 ? 2 : 4;
   if (d_dfeats) {
     void* wf = nullptr;
-    int rc = dev_alloc(&wf, (size_t)kNOff * cin * cout * esize, s, "igc_sparse_conv_backward: flipped weights");
+    const size_t wf_bytes = (size_t)kNOff * cin * cout * esize;
+    int rc = dev_alloc(&wf, wf_bytes, s, "igc_sparse_conv_backward: flipped weights", grid_alloc(g));
     if (rc) return rc;
     if (dtype == IGC_BF16)
       k_flip_w<uint16_t><<<256, 256, 0, s>>>((const uint16_t*)d_w, (uint16_t*)wf, cin, cout);
@@ -417,13 +419,13 @@ int launch_conv_backward(const igc_grid* g, const int32_t* d_map, const void* d_
       k_flip_w<float><<<256, 256, 0, s>>>((const float*)d_w, (float*)wf, cin, cout);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
-      dev_free(wf, s);
+      dev_free(wf, wf_bytes, s, grid_alloc(g));
       return hip_status(e, "igc_sparse_conv_backward: weight flip launch");
     }
     // dX = forward conv of dY (cout channels) with W~ (cout -> cin).
     rc = dgrad_path == IGC_PATH_LEAF ? launch_conv_leaf(g, d_dout, dtype, cout, wf, cin, d_dfeats, s)
                                      : launch_conv_ggs(g, d_map, d_dout, dtype, cout, wf, cin, d_dfeats, s);
-    dev_free(wf, s);
+    dev_free(wf, wf_bytes, s, grid_alloc(g));
     if (rc) return rc;
   }
   if (d_dw) {

@@ -23,7 +23,7 @@
 // (used offset, KC input channels): the tile's input rows of that offset are gathered by the
 // kernel map (absent neighbours read a zero row) into LDS next to the matching BN x KC slice
 // of W[o]^T, and each wave multiplies its (256/WM) x (BN/WN) sub-tile with 16x16x32 MFMAs,
-// skipping the 16-row blocks that have no pair at that offset. Both operands go from global
+// skipping the chunks in which none of its 16-row blocks has a pair at that offset. Both operands go from global
 // memory straight into LDS (global_load_lds_dwordx4: no staging registers, which the 256 x 256
 // accumulators leave none of); the next chunk's loads are in flight while the current chunk is
 // multiplied (two LDS stages, one barrier per chunk). The tile's map entries of every used
@@ -73,12 +73,13 @@ __global__ void k_transpose_w(const uint16_t* __restrict__ w, uint16_t* __restri
   }
 }
 
-// Per tile: perm[tile*256 + p] = output row at sorted position p (-1 past N), and
+// Per tile of 256 rows: perm[tile*256 + p] = output row at sorted position p (-1 past N), and
 // blk[tile*27 + o] bit b = some row at sorted positions [16b, 16b+16) has a neighbour at o.
-// Rows with skip[row] != 0 (per-leaf dispatch: another path writes them) count as having none.
-__global__ __launch_bounds__(kBM) void k_ggs_plan(const int32_t* __restrict__ map, int64_t N,
-                                                  int32_t* __restrict__ perm, uint16_t* __restrict__ blk,
-                                                  const uint8_t* __restrict__ skip) {
+// A map entry counts as a neighbour when it lies in [0, n_in). Rows with skip[row] != 0
+// (per-leaf dispatch: another path writes them) count as having none.
+__global__ __launch_bounds__(kBM) void k_ggs_plan(const int32_t* __restrict__ map, int64_t N, int64_t n_in,
+                                                 int32_t* __restrict__ perm, uint16_t* __restrict__ blk,
+                                                 const uint8_t* __restrict__ skip) {
   __shared__ uint64_t s_key[kBM];
   __shared__ uint32_t s_part[kBM / 64][kNOff];
   const int t = threadIdx.x;
@@ -86,8 +87,11 @@ __global__ __launch_bounds__(kBM) void k_ggs_plan(const int32_t* __restrict__ ma
   const int64_t row = r0 + t;
   uint32_t mask = 0;
   if (row < N && !(skip && skip[row])) {
+    int32_t v[kNOff];
 #pragma unroll
-    for (int o = 0; o < kNOff; ++o) mask |= (map[(size_t)o * (size_t)N + row] >= 0 ? 1u : 0u) << o;
+    for (int o = 0; o < kNOff; ++o) v[o] = map[(size_t)o * (size_t)N + row];
+#pragma unroll
+    for (int o = 0; o < kNOff; ++o) mask |= ((uint64_t)(int64_t)v[o] < (uint64_t)n_in ? 1u : 0u) << o;
   }
   // Ascending on the complemented mask: equal masks adjacent, padding rows (mask 0) last.
   s_key[t] = ((uint64_t)(~mask & 0x7FFFFFFu) << 8) | (uint64_t)t;
@@ -153,7 +157,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // BN output channels per workgroup, KC input channels per chunk, WM waves along the rows
 // (NWV / WM along the channels), NST LDS stages (NST - 1 chunks of loads in flight), NWV waves.
 template <int BN, int KC, int WM, int NST, int NWV>
-__global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __restrict__ map, int64_t N,
+__global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __restrict__ map, int64_t N, int64_t n_in,
                                                        const int32_t* __restrict__ perm,
                                                        const uint16_t* __restrict__ blk,
                                                        const uint16_t* __restrict__ feats,
@@ -218,6 +222,7 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
 
   // The tile's kernel-map entries of every used offset, in sorted-row order, go to LDS once:
   // all loads are issued before the first wait, so the map's latency is paid once per tile.
+  // An entry outside [0, n_in) is stored as -1 (absent): the gather never leaves the input.
   {
     // kBM rows x 27 offsets over NT threads: thread t takes row t % kBM and every
     // (NT / kBM)-th offset starting at t / kBM.
@@ -236,7 +241,7 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
 #pragma unroll
     for (int i = 0; i < OPT; ++i) {
       const int o = o0 + OSTEP * i;
-      if (o < kNOff) s_map[o][row] = (used >> o) & 1u ? v[i] : -1;
+      if (o < kNOff) s_map[o][row] = ((used >> o) & 1u) && (uint64_t)(int64_t)v[i] < (uint64_t)n_in ? v[i] : -1;
     }
   }
   __syncthreads();
@@ -288,16 +293,37 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) a[d][mi] = *(const bf16x8*)(A + (wm * MW + mi * 16 + frow) * ROWB + slot);
     };
-    frags(0, 0);
+    if (vm) {
+      // Schedule (one basic block): the reads of k-step 0, then its MFMAs with the reads of
+      // k-step 1 issued between them (after the first two), then the MFMAs of k-step 1; each
+      // wait for reads then overlaps MFMAs already issued. Blocks without a pair at this offset
+      // gathered the zero row (their products add nothing), so no block is skipped.
+      frags(0, 0);
 #pragma unroll
-    for (int t = 0; t < KST; ++t) {
-      if (t + 1 < KST) frags(t + 1, (t + 1) & 1);
+      for (int t = 0; t < KST; ++t) {
+        if (t + 1 < KST) frags(t + 1, (t + 1) & 1);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        if ((vm >> mi) & 1u) {
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t & 1][mi], b[t & 1][ni], acc[mi][ni], 0, 0, 0);
+      }
+      constexpr int NR = MI + NI;         // reads of one k-step
+      constexpr int NM = MI * NI;         // MFMAs of one k-step
+      constexpr int PER = (NM - 2) / NR;  // MFMAs between consecutive reads
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+      for (int t = 0; t < KST; ++t) {
+        if (t + 1 < KST) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, NM - 2 - NR * PER, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
         }
       }
     }
@@ -369,11 +395,11 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
 }
 
 template <int BN, int KC, int WM, int NST, int NWV>
-void launch_main(int64_t n_tiles, int64_t col_tiles, const int32_t* map, int64_t N, const int32_t* perm,
+void launch_main(int64_t n_tiles, int64_t col_tiles, const int32_t* map, int64_t N, int64_t n_in, const int32_t* perm,
                  const uint16_t* blk, const void* feats, const uint16_t* wt, int cin, int cout, void* out,
                  hipStream_t s) {
   k_conv_ggs_bf16<BN, KC, WM, NST, NWV><<<(unsigned)(n_tiles * col_tiles), 64 * NWV, 0, s>>>(
-      map, N, perm, blk, (const uint16_t*)feats, wt, cin, cout, (uint16_t*)out, col_tiles);
+      map, N, n_in, perm, blk, (const uint16_t*)feats, wt, cin, cout, (uint16_t*)out, col_tiles);
 }
 
 }  // namespace
@@ -398,7 +424,7 @@ int launch_ggs_plan(const int32_t* d_map, int64_t N, int32_t* perm, uint16_t* bl
                     const uint8_t* skip) {
   const int64_t n_tiles = (N + kBM - 1) / kBM;
   if (n_tiles == 0) return IGC_OK;
-  k_ggs_plan<<<(unsigned)n_tiles, kBM, 0, s>>>(d_map, N, perm, blk, skip);
+  k_ggs_plan<<<(unsigned)n_tiles, kBM, 0, s>>>(d_map, N, N, perm, blk, skip);
   IGC_HIP(hipGetLastError(), "igc_sparse_conv: plan launch");
   return IGC_OK;
 }
@@ -408,35 +434,57 @@ bool ggs_conv_supported(int32_t dtype, int32_t cin, int32_t cout) {
          cout % 64 == 0;
 }
 
+namespace {
+struct GgsLayout {
+  int64_t n_tiles = 0;
+  size_t wt_bytes = 0, perm_bytes = 0, blk_bytes = 0, skip_bytes = 0;
+  size_t total() const { return wt_bytes + perm_bytes + blk_bytes + skip_bytes; }
+};
+
+GgsLayout ggs_layout(int64_t N, int32_t cin, int32_t cout, bool with_skip) {
+  GgsLayout L;
+  L.n_tiles = (N + kBM - 1) / kBM;
+  L.wt_bytes = align_up((size_t)27 * cin * cout * 2, 256);
+  L.perm_bytes = align_up((size_t)L.n_tiles * kBM * 4, 256);
+  L.blk_bytes = align_up((size_t)L.n_tiles * kNOff * 2, 256);
+  L.skip_bytes = with_skip ? align_up((size_t)N, 256) : 0;
+  return L;
+}
+}  // namespace
+
+size_t ggs_scratch_bytes(int64_t N, int32_t cin, int32_t cout, bool with_skip) {
+  return ggs_layout(N, cin, cout, with_skip).total();
+}
+
 int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype, int32_t cin,
-                    const void* d_w, int32_t cout, void* d_out, hipStream_t s, uint32_t dense_min) {
+                    const void* d_w, int32_t cout, void* d_out, hipStream_t s, uint32_t dense_min, int64_t n_in,
+                    void* scratch) {
   (void)dtype;
   const int64_t N = g->n_voxels;
-  const int64_t n_tiles = (N + kBM - 1) / kBM;
-  const size_t wt_bytes = align_up((size_t)27 * cin * cout * 2, 256);
-  const size_t perm_bytes = align_up((size_t)n_tiles * kBM * 4, 256);
-  const size_t blk_bytes = align_up((size_t)n_tiles * kNOff * 2, 256);
-  const size_t skip_bytes = dense_min ? align_up((size_t)N, 256) : 0;
+  if (n_in < 0) n_in = N;
+  const GgsLayout L = ggs_layout(N, cin, cout, dense_min != 0);
+  const int64_t n_tiles = L.n_tiles;
   Workspace wsb;
-  int rc = ws_acquire(&wsb, wt_bytes + perm_bytes + blk_bytes + skip_bytes, s,
-                      "igc_sparse_conv: gather-GEMM-scatter workspace");
-  if (rc) return rc;
-  char* ws = (char*)wsb.p;
+  if (!scratch) {
+    int rc = ws_acquire(&wsb, L.total(), s, "igc_sparse_conv: gather-GEMM-scatter workspace", grid_alloc(g));
+    if (rc) return rc;
+  }
+  char* ws = scratch ? (char*)scratch : (char*)wsb.p;
   uint16_t* wt = (uint16_t*)ws;
-  int32_t* perm = (int32_t*)(ws + wt_bytes);
-  uint16_t* blk = (uint16_t*)(ws + wt_bytes + perm_bytes);
-  uint8_t* skip = dense_min ? (uint8_t*)(ws + wt_bytes + perm_bytes + blk_bytes) : nullptr;
+  int32_t* perm = (int32_t*)(ws + L.wt_bytes);
+  uint16_t* blk = (uint16_t*)(ws + L.wt_bytes + L.perm_bytes);
+  uint8_t* skip = dense_min ? (uint8_t*)(ws + L.wt_bytes + L.perm_bytes + L.blk_bytes) : nullptr;
   k_transpose_w<<<256, 256, 0, s>>>((const uint16_t*)d_w, wt, cin, cout);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && skip) {
     k_dense_rows<<<(unsigned)((g->n_leaf + 3) / 4), 256, 0, s>>>(g->leaf, g->n_leaf, N, dense_min, skip);
     e = hipGetLastError();
   }
-  if (e == hipSuccess) {
-    k_ggs_plan<<<(unsigned)n_tiles, kBM, 0, s>>>(d_map, N, perm, blk, skip);
+  if (e == hipSuccess && n_tiles > 0) {
+    k_ggs_plan<<<(unsigned)n_tiles, kBM, 0, s>>>(d_map, N, n_in, perm, blk, skip);
     e = hipGetLastError();
   }
-  if (e == hipSuccess) {
+  if (e == hipSuccess && n_tiles > 0) {
     const bool k64 = cin % 64 == 0;
     // Tile shapes measured on MI355X: 256 x 256 with eight waves (two per SIMD, each 128 rows
     // by 64 channels: 64 rows by 128 is 0.5% slower on 128 -> 256), 256 x 128 with sixteen
@@ -445,15 +493,15 @@ int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats
     // chunks when cin is not a multiple of 64.
     const int64_t n256 = cout / 256, n128 = cout / 128, n64 = cout / 64;
     if (cout % 256 == 0 && k64) {
-      launch_main<256, 64, 2, 2, 8>(n_tiles, n256, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      launch_main<256, 64, 2, 2, 8>(n_tiles, n256, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
     } else if (cout % 128 == 0 && k64) {
-      launch_main<128, 64, 8, 2, 16>(n_tiles, n128, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      launch_main<128, 64, 8, 2, 16>(n_tiles, n128, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
     } else if (cout % 128 == 0) {
-      launch_main<128, 32, 2, 2, 8>(n_tiles, n128, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      launch_main<128, 32, 2, 2, 8>(n_tiles, n128, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
     } else if (k64) {
-      launch_main<64, 64, 8, 2, 8>(n_tiles, n64, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      launch_main<64, 64, 8, 2, 8>(n_tiles, n64, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
     } else {
-      launch_main<64, 32, 4, 2, 4>(n_tiles, n64, d_map, N, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      launch_main<64, 32, 4, 2, 4>(n_tiles, n64, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
     }
     e = hipGetLastError();
   }

@@ -1,6 +1,7 @@
 // Output grids of strided and transposed 3x3x3 convolutions, and the neighbour map between two
-// grids (fVDB notes, grid-to-grid ops ConvGrid / ConvTransposeGrid; DriveRT, "Shared neighbour
-// maps" for two coordinate domains). Offsets d run over {-1, 0, 1}^3, o = (dx+1)*9 + (dy+1)*3 +
+// grids (the grid-to-grid ops ConvGrid / ConvTransposeGrid in the op table of the "ONNX Runtime
+// support for fVDB operations" proposal; DriveRT, "Shared neighbour maps" for two coordinate
+// domains). Offsets d run over {-1, 0, 1}^3, o = (dx+1)*9 + (dy+1)*3 +
 // (dz+1), and the stride s is per axis:
 //   strided:    y is an output iff some input x = s*y + d; map[o, y] = in.index(s*y + d_o);
 //   transposed: y is an output iff y = s*x + d for an input x; map[o, y] = in.index((y - d_o)/s)
@@ -195,7 +196,8 @@ int build_conv_grid(const igc_grid* in, const int32_t* stride, int32_t transpose
   const size_t ijk_bytes = transposed ? align_up((size_t)N * 12, 256) : 0;
   const size_t cand_bytes = align_up((size_t)n_cand * 12, 256);
   char* ws = nullptr;
-  int rc = dev_alloc((void**)&ws, ijk_bytes + cand_bytes + 256, s, "igc_conv_grid: workspace");
+  const size_t ws_bytes = ijk_bytes + cand_bytes + 256;
+  int rc = dev_alloc((void**)&ws, ws_bytes, s, "igc_conv_grid: workspace", grid_alloc(out));
   if (rc) return rc;
   int32_t* ijk = (int32_t*)ws;
   int32_t* cand = (int32_t*)(ws + ijk_bytes);
@@ -203,7 +205,7 @@ int build_conv_grid(const igc_grid* in, const int32_t* stride, int32_t transpose
   rc = fill_u32(flag, 1, 0u, s);
   hipError_t e = hipSuccess;
   if (rc) {
-    dev_free(ws, s);
+    dev_free(ws, ws_bytes, s, grid_alloc(out));
     return rc;
   }
   Stride3 st{{stride[0], stride[1], stride[2]}};
@@ -225,7 +227,7 @@ int build_conv_grid(const igc_grid* in, const int32_t* stride, int32_t transpose
   if (e == hipSuccess && rc == IGC_OK && h_flag)
     rc = set_error(IGC_ERR_RANGE, "igc_conv_grid: an output coordinate leaves the int32 range");
   if (e == hipSuccess && rc == IGC_OK) rc = build_grid(cand, n_cand, s, out);
-  dev_free(ws, s);
+  dev_free(ws, ws_bytes, s, grid_alloc(out));
   if (e != hipSuccess) return hip_status(e, "igc_conv_grid: candidates");
   return rc;
 }
@@ -235,7 +237,7 @@ int launch_conv_map(const igc_grid* in, const igc_grid* out, const int32_t* stri
   const int64_t n_out = out->n_voxels;
   if (n_out == 0) return IGC_OK;
   Workspace wsb;
-  int rc = ws_acquire(&wsb, (size_t)n_out * 12, s, "igc_conv_map: output coordinates");
+  int rc = ws_acquire(&wsb, (size_t)n_out * 12, s, "igc_conv_map: output coordinates", grid_alloc(out));
   if (rc) return rc;
   int32_t* ijk = (int32_t*)wsb.p;
   rc = launch_active_ijk(out, ijk, s);

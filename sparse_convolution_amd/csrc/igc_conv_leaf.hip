@@ -77,7 +77,8 @@ __device__ __forceinline__ int win_rot(int c) {
 // leaf is absent.
 template <int CIN>
 __device__ __forceinline__ void fill_window_f32(float* s_win, const uint64_t (*s_mask)[8], const uint64_t* s_off,
-                                                const uint64_t* s_pre, const float* __restrict__ feats, int tid) {
+                                                const uint64_t* s_pre, const float* __restrict__ feats, uint64_t n_rows,
+                                                int tid) {
   for (int c = tid; c < 1000; c += 256) {
     const int x = c / 100 - 1, y = (c / 10) % 10 - 1, z = c % 10 - 1;  // leaf-local, in [-1, 8]
     const int slot = ((x >> 3) + 1) * 9 + ((y >> 3) + 1) * 3 + ((z >> 3) + 1);
@@ -87,7 +88,8 @@ __device__ __forceinline__ void fill_window_f32(float* s_win, const uint64_t (*s
     float4* dst = (float4*)&s_win[c * CIN];
     if (word & bit) {
       const uint32_t pre = q ? (uint32_t)(s_pre[slot] >> (9u * (q - 1u))) & 511u : 0u;
-      const uint64_t row = s_off[slot] + pre + (uint32_t)__popcll(word & (bit - 1ull));
+      const uint64_t r0 = s_off[slot] + pre + (uint32_t)__popcll(word & (bit - 1ull));
+      const uint64_t row = r0 < n_rows ? r0 : 0;  // never past the feature array
       const float4* src = (const float4*)(feats + row * CIN);
       const int rot = win_rot<CIN>(c);
 #pragma unroll
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32_wide(GridView g, const fl
 
   // Compacted active positions of this leaf (wave 0), and the window (all threads).
   if (wave == 0) compact_leaf(lane, s_mask, s_pos, &s_count);
-  fill_window_f32<CIN>(s_win, s_mask, s_off, s_pre, feats, tid);
+  fill_window_f32<CIN>(s_win, s_mask, s_off, s_pre, feats, (uint64_t)g.n_voxels, tid);
   __syncthreads();
 
   const uint32_t count = s_count;
@@ -354,7 +356,8 @@ __global__ __launch_bounds__(256) void k_conv_leaf_f32(GridView g, const float* 
     const uint64_t word = c < 1000 ? s_mask[slot][q] : 0ull;
     if (word & bit) {
       const uint32_t pre = q ? (uint32_t)(s_pre[slot] >> (9u * (q - 1u))) & 511u : 0u;
-      const uint64_t row = s_off[slot] + pre + (uint32_t)__popcll(word & (bit - 1ull));
+      const uint64_t r0 = s_off[slot] + pre + (uint32_t)__popcll(word & (bit - 1ull));
+      const uint64_t row = r0 < (uint64_t)g.n_voxels ? r0 : 0;  // never past the feature array
       const float4* src = (const float4*)(feats + row * CIN);
 #pragma unroll
       for (int j = 0; j < CIN / 4; ++j) {
@@ -515,7 +518,8 @@ __global__ __launch_bounds__(256) void k_wgrad_leaf_f32(GridView g, int64_t n_le
       const uint64_t word = c < 1000 ? s_mask[slot][q] : 0ull;
       if (word & bit) {
         const uint32_t pre = q ? (uint32_t)(s_pre[slot] >> (9u * (q - 1u))) & 511u : 0u;
-        const uint64_t row = s_off[slot] + pre + (uint32_t)__popcll(word & (bit - 1ull));
+        const uint64_t r0 = s_off[slot] + pre + (uint32_t)__popcll(word & (bit - 1ull));
+        const uint64_t row = r0 < (uint64_t)g.n_voxels ? r0 : 0;  // never past the feature array
         const float4* src = (const float4*)(feats + row * CIN);
 #pragma unroll
         for (int j = 0; j < CIN / 4; ++j) v[i][j] = src[j];
@@ -730,7 +734,8 @@ __global__ __launch_bounds__(256) void k_conv_leaf_bf16(GridView g, const uint16
     const uint64_t word = c < 1000 ? s_mask[slot][q] : 0ull;
     if (word & bit) {
       const uint32_t pre = q ? (uint32_t)(s_pre[slot] >> (9u * (q - 1u))) & 511u : 0u;
-      const uint64_t row = s_off[slot] + pre + (uint32_t)__popcll(word & (bit - 1ull));
+      const uint64_t r0 = s_off[slot] + pre + (uint32_t)__popcll(word & (bit - 1ull));
+      const uint64_t row = r0 < (uint64_t)g.n_voxels ? r0 : 0;  // never past the feature array
       const uint4* src = (const uint4*)(feats + row * CIN);
 #pragma unroll
       for (int j = 0; j < GPC; ++j) v[i][j] = src[j];
@@ -796,12 +801,14 @@ __global__ __launch_bounds__(256) void k_conv_leaf_bf16(GridView g, const uint16
 
 template <int CIN, int COUT>
 int launch_leaf_bf16(const igc_grid* g, const void* d_feats, const void* d_w, void* d_out, hipStream_t s,
-                     uint32_t min_count) {
+                     uint32_t min_count, void* scratch) {
   constexpr int KP = (27 * CIN + 31) / 32 * 32;
   Workspace wsb;
-  int rc = ws_acquire(&wsb, (size_t)COUT * KP * 2, s, "igc_sparse_conv: leaf W transpose");
-  if (rc) return rc;
-  uint16_t* wt = (uint16_t*)wsb.p;
+  if (!scratch) {
+    int rc = ws_acquire(&wsb, (size_t)COUT * KP * 2, s, "igc_sparse_conv: leaf W transpose", grid_alloc(g));
+    if (rc) return rc;
+  }
+  uint16_t* wt = (uint16_t*)(scratch ? scratch : wsb.p);
   k_leaf_wt_bf16<CIN, COUT><<<(COUT * KP + 255) / 256, 256, 0, s>>>((const uint16_t*)d_w, wt);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) {
@@ -845,20 +852,25 @@ bool leaf_conv_supported(int32_t dtype, int32_t cin, int32_t cout) {
   }
 }
 
+size_t leaf_scratch_bytes(int32_t dtype, int32_t cin, int32_t cout) {
+  if (dtype != IGC_BF16) return 0;  // the fp32 kernels split W per workgroup, in LDS
+  return align_up((size_t)cout * (size_t)((27 * cin + 31) / 32 * 32) * 2, 256);
+}
+
 int launch_conv_leaf(const igc_grid* g, const void* d_feats, int32_t dtype, int32_t cin, const void* d_w,
-                     int32_t cout, void* d_out, hipStream_t s, uint32_t min_count) {
+                     int32_t cout, void* d_out, hipStream_t s, uint32_t min_count, void* scratch) {
   if (min_count && dtype != IGC_BF16) return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: per-leaf dispatch dtype");
   if (dtype == IGC_BF16) {
     switch (cin * 1000 + cout) {
-      case 16016: return launch_leaf_bf16<16, 16>(g, d_feats, d_w, d_out, s, min_count);
-      case 16032: return launch_leaf_bf16<16, 32>(g, d_feats, d_w, d_out, s, min_count);
-      case 16064: return launch_leaf_bf16<16, 64>(g, d_feats, d_w, d_out, s, min_count);
-      case 32016: return launch_leaf_bf16<32, 16>(g, d_feats, d_w, d_out, s, min_count);
-      case 32032: return launch_leaf_bf16<32, 32>(g, d_feats, d_w, d_out, s, min_count);
-      case 32064: return launch_leaf_bf16<32, 64>(g, d_feats, d_w, d_out, s, min_count);
-      case 64016: return launch_leaf_bf16<64, 16>(g, d_feats, d_w, d_out, s, min_count);
-      case 64032: return launch_leaf_bf16<64, 32>(g, d_feats, d_w, d_out, s, min_count);
-      case 64064: return launch_leaf_bf16<64, 64>(g, d_feats, d_w, d_out, s, min_count);
+      case 16016: return launch_leaf_bf16<16, 16>(g, d_feats, d_w, d_out, s, min_count, scratch);
+      case 16032: return launch_leaf_bf16<16, 32>(g, d_feats, d_w, d_out, s, min_count, scratch);
+      case 16064: return launch_leaf_bf16<16, 64>(g, d_feats, d_w, d_out, s, min_count, scratch);
+      case 32016: return launch_leaf_bf16<32, 16>(g, d_feats, d_w, d_out, s, min_count, scratch);
+      case 32032: return launch_leaf_bf16<32, 32>(g, d_feats, d_w, d_out, s, min_count, scratch);
+      case 32064: return launch_leaf_bf16<32, 64>(g, d_feats, d_w, d_out, s, min_count, scratch);
+      case 64016: return launch_leaf_bf16<64, 16>(g, d_feats, d_w, d_out, s, min_count, scratch);
+      case 64032: return launch_leaf_bf16<64, 32>(g, d_feats, d_w, d_out, s, min_count, scratch);
+      case 64064: return launch_leaf_bf16<64, 64>(g, d_feats, d_w, d_out, s, min_count, scratch);
       default: return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: bf16 leaf path shape");
     }
   }

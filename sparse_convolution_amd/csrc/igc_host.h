@@ -17,6 +17,7 @@ struct igc_grid {
   uint32_t root_cap = 0;
   size_t bytes = 0;
   void* block = nullptr;  // one device allocation holding every array below
+  igc_allocator alloc{};  // the caller's memory provider (alloc.alloc == nullptr: the library's pool)
 
   uint64_t* root_keys = nullptr;   // [root_cap]
   int32_t* root_vals = nullptr;    // [root_cap]
@@ -68,30 +69,43 @@ int hip_status(hipError_t e, const char* what);
     if (e_ != hipSuccess) return ::igc::hip_status(e_, what); \
   } while (0)
 
-// Stream-ordered device allocation from the device's memory pool (kept across calls).
-int dev_alloc(void** p, size_t bytes, hipStream_t s, const char* what);
-void dev_free(void* p, hipStream_t s);
+// The memory provider of a grid, or nullptr for the library's own pool.
+inline const igc_allocator* grid_alloc(const igc_grid* g) { return g && g->alloc.alloc ? &g->alloc : nullptr; }
+
+// Stream-ordered device allocation: through `a` when given, else from the library's private
+// per-device memory pool (free blocks kept across calls until igc_release_memory).
+int dev_alloc(void** p, size_t bytes, hipStream_t s, const char* what, const igc_allocator* a = nullptr);
+void dev_free(void* p, size_t bytes, hipStream_t s, const igc_allocator* a = nullptr);
 
 // Pinned host staging buffer (per host thread) of at least `bytes` for small device -> host
 // reads; *device_view (if given) receives the address kernels write it through.
 void* host_staging(size_t bytes, void** device_view = nullptr);
 
-// Temporary device workspace of one call. Each device keeps one block that is handed to one
-// call at a time and grows to the largest request (a call that finds it taken allocates its
-// own). A stream-ordered allocation and free cost tens of microseconds of host time per
-// call; the block makes the common case free of both. On release an event is recorded on the
-// caller's stream, and the next user's stream waits for it, so work still reading the block
-// finishes first.
+// Temporary device workspace of one call. With a caller's allocator it is allocated through it
+// and returned at release. Otherwise each device keeps one block that is handed to one call at
+// a time and grows to the largest request (a call that finds it taken allocates its own): a
+// stream-ordered allocation and free cost tens of microseconds of host time per call, and the
+// block makes the common case free of both. On release an event is recorded on the caller's
+// stream, and the next user's stream waits for it, so work still reading the block finishes
+// first.
 struct Workspace {
   void* p = nullptr;
   size_t bytes = 0;
   int dev = -1;
   bool cached = false;
+  const igc_allocator* a = nullptr;
 };
-int ws_acquire(Workspace* w, size_t bytes, hipStream_t s, const char* what);
+int ws_acquire(Workspace* w, size_t bytes, hipStream_t s, const char* what, const igc_allocator* a = nullptr);
 void ws_release(Workspace* w, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Host-side checks shared by igc_sparse_conv and igc_sparse_conv_noalloc (fn names the call in
+// messages); *path is the requested path on entry and the one to run on success.
+int check_conv_args(const char* fn, const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype,
+                    int32_t cin, const void* d_w, int32_t cout, void* d_out, int32_t* path);
+// Active voxels from which a leaf takes the leaf window under per-leaf dispatch.
+uint32_t mixed_dense_rows(int32_t cin);
 
 // Launchers (defined in the .hip files).
 int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g);
@@ -102,11 +116,19 @@ int launch_kernel_map(const igc_grid* g, const int32_t* h_offsets, int32_t K, in
 bool leaf_conv_supported(int32_t dtype, int32_t cin, int32_t cout);
 bool ggs_conv_supported(int32_t dtype, int32_t cin, int32_t cout);
 // min_count > 0 (bf16 only): leaves with fewer active voxels are skipped (their rows untouched).
+// scratch (may be null): caller-provided device memory of at least leaf_scratch_bytes() used
+// instead of a workspace (nothing is allocated then).
 int launch_conv_leaf(const igc_grid* g, const void* d_feats, int32_t dtype, int32_t cin, const void* d_w, int32_t cout,
-                     void* d_out, hipStream_t s, uint32_t min_count = 0);
+                     void* d_out, hipStream_t s, uint32_t min_count = 0, void* scratch = nullptr);
+size_t leaf_scratch_bytes(int32_t dtype, int32_t cin, int32_t cout);
 // dense_min > 0: rows of leaves with at least dense_min active voxels get no pairs (zero output).
+// n_in: rows of d_feats (map entries outside [0, n_in) read as absent); -1 = the grid's N.
+// scratch (may be null): caller-provided device memory of at least ggs_scratch_bytes() used
+// instead of a workspace (nothing is allocated then).
 int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype, int32_t cin,
-                    const void* d_w, int32_t cout, void* d_out, hipStream_t s, uint32_t dense_min = 0);
+                    const void* d_w, int32_t cout, void* d_out, hipStream_t s, uint32_t dense_min = 0,
+                    int64_t n_in = -1, void* scratch = nullptr);
+size_t ggs_scratch_bytes(int64_t N, int32_t cin, int32_t cout, bool with_skip);
 // Mask-sorted tiles of 256 output rows (row order perm, 16-row blocks with pairs per offset blk);
 // rows with skip[row] != 0 (if skip is given) count as having no neighbours.
 int launch_ggs_plan(const int32_t* d_map, int64_t N, int32_t* perm, uint16_t* blk, hipStream_t s,
