@@ -20,7 +20,7 @@ _SRC = os.path.join(_HERE, "igc_oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 __all__ = ["build_library", "OracleGrid", "kernel_map", "conv", "conv_rows", "conv_dgrad", "conv_wgrad",
-           "conv_grid_coords", "conv_map_between", "standard_offsets", "num_threads"]
+           "conv_grid_candidates", "conv_grid_coords", "conv_map_between", "standard_offsets", "num_threads"]
 
 
 def build_library(force: bool = True) -> str:
@@ -183,35 +183,49 @@ def conv_rows(nbrs: np.ndarray, feats_of: dict, w: np.ndarray) -> np.ndarray:
     return out
 
 
-def conv_dgrad(kmap: np.ndarray, dout: np.ndarray, w: np.ndarray) -> np.ndarray:
+def conv_dgrad(kmap: np.ndarray, dout: np.ndarray, w: np.ndarray, rows: np.ndarray | None = None) -> np.ndarray:
     """Gradient of the submanifold convolution with respect to its input features, in float64:
     dX[s, ci] = sum over the pairs (o, r) with map[o, r] = s of sum_co dY[r, co] W[o, ci, co]
     (the convolution of the fVDB notes' sparse-conv operators differentiated term by term).
 
     kmap int32[K, N], dout float32[N, cout] (exact bf16 values for bf16 data),
-    w float32[K, cin, cout]; returns float64[N, cin]."""
+    w float32[K, cin, cout]; returns float64[N, cin], or float64[len(rows), cin] for the input
+    rows `rows` only (sorted, unique): then only the pairs whose input is one of them are summed."""
     kmap = np.asarray(kmap)
-    dy = np.asarray(dout, dtype=np.float64)
+    dy = np.asarray(dout)
     ww = np.asarray(w, dtype=np.float64)
-    dx = np.zeros((kmap.shape[1], ww.shape[1]), np.float64)
+    if rows is None:
+        dx = np.zeros((kmap.shape[1], ww.shape[1]), np.float64)
+    else:
+        rows = np.asarray(rows, dtype=np.int64)
+        dx = np.zeros((rows.shape[0], ww.shape[1]), np.float64)
+        wanted = np.zeros(kmap.shape[1], bool)
+        wanted[rows] = True
     for o in range(kmap.shape[0]):
         valid = kmap[o] >= 0
-        np.add.at(dx, kmap[o][valid], dy[valid] @ ww[o].T)
+        if rows is not None:
+            valid[valid] = wanted[kmap[o][valid]]
+        s = kmap[o][valid]
+        np.add.at(dx, s if rows is None else np.searchsorted(rows, s), dy[valid].astype(np.float64) @ ww[o].T)
     return dx
 
 
-def conv_wgrad(kmap: np.ndarray, feats: np.ndarray, dout: np.ndarray) -> np.ndarray:
+def conv_wgrad(kmap: np.ndarray, feats: np.ndarray, dout: np.ndarray, rows: np.ndarray | None = None) -> np.ndarray:
     """Gradient of the submanifold convolution with respect to its weights, in float64:
     dW[o, ci, co] = sum over r with map[o, r] >= 0 of feats[map[o, r], ci] dY[r, co].
 
-    kmap int32[K, N], feats float32[N, cin], dout float32[N, cout]; returns float64[K, cin, cout]."""
+    kmap int32[K, N], feats float32[N, cin], dout float32[N, cout]; returns float64[K, cin, cout].
+    With `rows` the sum runs over those output rows only (the gradient for a dY that is zero at
+    every other row)."""
     kmap = np.asarray(kmap)
-    f = np.asarray(feats, dtype=np.float64)
-    dy = np.asarray(dout, dtype=np.float64)
+    f = np.asarray(feats)
+    dy = np.asarray(dout)
     dw = np.zeros((kmap.shape[0], f.shape[1], dy.shape[1]), np.float64)
+    r = np.arange(kmap.shape[1]) if rows is None else np.asarray(rows, dtype=np.int64)
     for o in range(kmap.shape[0]):
-        valid = kmap[o] >= 0
-        dw[o] = f[kmap[o][valid]].T @ dy[valid]
+        src = kmap[o][r]
+        valid = src >= 0
+        dw[o] = f[src[valid]].astype(np.float64).T @ dy[r[valid]].astype(np.float64)
     return dw
 
 
@@ -221,27 +235,38 @@ def _stride3(stride) -> np.ndarray:
     return s
 
 
-def conv_grid_coords(coords: np.ndarray, stride, transposed: bool = False) -> np.ndarray:
-    """Output coordinates of a 3x3x3 sparse convolution with the given stride (fVDB notes'
-    grid-to-grid ops ConvGrid / ConvTransposeGrid; the pages name them without a formula, so
-    the plain reading is used). Offsets d run over {-1, 0, 1}^3.
-
-    strided:    y is an output iff some input x has x = s * y + d (its receptive field holds
-                an input voxel);
-    transposed: y is an output iff y = s * x + d for some input x.
-    Returns the unique coordinates, int32[M, 3], in lexicographic order."""
+def conv_grid_candidates(coords: np.ndarray, stride, transposed: bool = False) -> np.ndarray:
+    """Every output coordinate of a 3x3x3 sparse convolution with the given stride, once per
+    (input voxel, offset) that produces it, duplicates included (see conv_grid_coords for the
+    definition). Offsets d run over {-1, 0, 1}^3. Returns int32[M, 3], input-major per offset;
+    passing it to OracleGrid gives the output grid without a separate dedupe."""
     c = np.asarray(coords, dtype=np.int64).reshape(-1, 3)
     s = _stride3(stride)
     parts = []
     for d in standard_offsets().astype(np.int64):
         if transposed:
-            parts.append(s * c + d)
+            parts.append((s * c + d).astype(np.int32))
         else:
             z = c - d
             ok = np.all(z % s == 0, axis=1)
-            parts.append(z[ok] // s)
-    out = np.unique(np.concatenate(parts, axis=0), axis=0) if parts else np.zeros((0, 3), np.int64)
-    return out.astype(np.int32)
+            parts.append((z[ok] // s).astype(np.int32))
+    return np.concatenate(parts, axis=0) if parts else np.zeros((0, 3), np.int32)
+
+
+def conv_grid_coords(coords: np.ndarray, stride, transposed: bool = False) -> np.ndarray:
+    """Output coordinates of a 3x3x3 sparse convolution with the given stride (the grid-to-grid
+    ops ConvGrid / ConvTransposeGrid in the op table of the "ONNX Runtime support for fVDB
+    operations" proposal; the pages name them without a formula, so the plain reading is used).
+    Offsets d run over {-1, 0, 1}^3.
+
+    strided:    y is an output iff some input x has x = s * y + d (its receptive field holds
+                an input voxel);
+    transposed: y is an output iff y = s * x + d for some input x.
+    Returns the unique coordinates, int32[M, 3], in lexicographic order."""
+    cand = conv_grid_candidates(coords, stride, transposed)
+    if cand.shape[0] == 0:
+        return cand
+    return np.unique(cand.astype(np.int64), axis=0).astype(np.int32)
 
 
 def conv_map_between(out_grid: OracleGrid, in_grid: OracleGrid, stride, transposed: bool = False) -> np.ndarray:

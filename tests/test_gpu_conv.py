@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import workloads
-from tests._gpu import normwise_error, require_gpu, say, to_dev
+from tests._gpu import elementwise_error, normwise_error, require_gpu, say, segment_sample_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -48,14 +48,16 @@ def run_conv(coords, cin, cout, dtype, path, name, seed=0, std=None, sample_rows
     mr = ref_grid.kernel_map()
     rows = None
     if sample_rows is not None and sample_rows < g.n_voxels:
-        rows = np.sort(np.random.default_rng(seed + 77).choice(g.n_voxels, sample_rows, replace=False))
-        rows = np.concatenate([rows, [0, g.n_voxels - 1]])
+        # Half in whole 256-row runs spread over the grid (first and last included), half uniform.
+        rows = segment_sample_rows(g.n_voxels, sample_rows // 512, seg=256, n_random=sample_rows // 2,
+                                   seed=seed + 77)
     r = oracle.conv(mr, ft.float().numpy(), wt.float().numpy(), rows=rows)
     yy = y.float().cpu().numpy()
     if rows is not None:
         yy = yy[rows]
     err = normwise_error(yy, r)
-    say(f"  normwise error {err:.3e}")
+    say(f"  normwise error {err:.3e}, elementwise {elementwise_error(yy, r):.3e}"
+        + (f" ({rows.shape[0]} sampled rows)" if rows is not None else ""))
     assert np.all(np.isfinite(yy))
     assert err <= TOL[dtype], f"normwise error {err} > {TOL[dtype]}"
     return g, y
@@ -78,7 +80,8 @@ def test_leaf_path_shapes(cin, cout):
     run_conv(c, cin, cout, torch.float32, "leaf", "clusters", seed=cin + cout)
 
 
-@pytest.mark.parametrize("cin,cout", [(32, 64), (64, 64), (64, 128), (128, 128), (128, 256), (96, 192)])
+@pytest.mark.parametrize("cin,cout", [(32, 64), (64, 64), (64, 128), (128, 128), (128, 256), (96, 192), (32, 128),
+                                      (96, 256), (64, 256), (256, 64)])
 def test_ggs_path_shapes(cin, cout):
     c = _cluster_coords(5, 24, 300, seed=cin + cout, fill=0.2)
     run_conv(c, cin, cout, torch.bfloat16, "ggs", "clusters", seed=cin * 3 + cout, std=1.0 / np.sqrt(27 * cin))
@@ -97,7 +100,7 @@ def test_leaf_path_bf16_shapes(cin, cout):
 def test_leaf_workload_bf16_sampled():
     w = workloads.WORKLOADS["leaf"]
     run_conv(workloads.make_coords("leaf"), 32, 32, torch.bfloat16, "leaf", "leaf bf16 32->32", seed=w.index,
-             std=1.0 / np.sqrt(27 * 32), sample_rows=1 << 16)
+             std=1.0 / np.sqrt(27 * 32), sample_rows=1 << 18)
 
 
 def test_tiny_workload_leaf():
@@ -135,13 +138,13 @@ def test_mixed_path_per_leaf_dispatch(monkeypatch, cin, cout, dense_min):
 def test_band_workload_ggs_sampled():
     w = workloads.WORKLOADS["band"]
     run_conv(workloads.make_coords("band"), w.cin, w.cout, torch.bfloat16, "ggs", "band", seed=w.index,
-             std=w.weight_std, sample_rows=1 << 16)
+             std=w.weight_std, sample_rows=1 << 20)
 
 
 def test_band_workload_leaf_sampled():
     w = workloads.WORKLOADS["band"]
     run_conv(workloads.make_coords("band"), w.cin, w.cout, torch.bfloat16, "leaf", "band leaf window", seed=w.index,
-             std=w.weight_std, sample_rows=1 << 16)
+             std=w.weight_std, sample_rows=1 << 20)
 
 
 def test_identity_kernel_both_paths():

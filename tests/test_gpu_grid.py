@@ -1,5 +1,6 @@
 """GPU parity of the IndexGrid build, the index query and the kernel map against the CPU
 oracle: bit-exact topology, row order, indices and maps."""
+import ctypes
 import os
 
 import numpy as np
@@ -181,9 +182,9 @@ def test_errors():
     lib = _lib.load()
     import ctypes
     h = ctypes.c_void_p()
-    assert lib.igc_grid_build(None, 5, None, ctypes.byref(h)) == 1
+    assert lib.igc_grid_build(None, 5, None, None, ctypes.byref(h)) == 1
     assert b"d_ijk" in lib.igc_last_error()
-    assert lib.igc_grid_build(None, -1, None, ctypes.byref(h)) == 1
+    assert lib.igc_grid_build(None, -1, None, None, ctypes.byref(h)) == 1
     g = igc.grid_build(to_dev(np.array([[1, 2, 3]], np.int32)))
     off = np.array([[9, 0, 0]], np.int32)
     with pytest.raises(igc.IgcError):
@@ -244,3 +245,68 @@ def test_concurrent_builds_two_threads():
     for (tid, rep, i), topo in results.items():
         for k in ref[i]:
             assert np.array_equal(topo[k], ref[i][k]), (tid, rep, i, k)
+
+
+class _TorchCountingAllocator:
+    """PyTorch's caching allocator behind the C allocator interface, counting live blocks and
+    failing the `fail_at`-th request (1-based) on purpose."""
+
+    def __init__(self, fail_at=None):
+        from sparse_convolution_amd import _lib as L
+        self.fail_at = fail_at
+        self.n_req = 0
+        self.live = {}
+        self._a = L.ALLOC_FN(self._alloc)
+        self._r = L.RELEASE_FN(self._release)
+        self.struct = L.Allocator(self._a, self._r, None)
+
+    def _alloc(self, ctx, nbytes, stream):
+        self.n_req += 1
+        if self.fail_at is not None and self.n_req == self.fail_at:
+            return None
+        p = torch.cuda.caching_allocator_alloc(int(nbytes), torch.cuda.current_device(), int(stream or 0))
+        self.live[p] = nbytes
+        return p
+
+    def _release(self, ctx, ptr, nbytes, stream):
+        assert self.live.pop(ptr) == nbytes
+        torch.cuda.caching_allocator_delete(ptr)
+
+
+def test_caller_allocator_and_failure_injection():
+    # Every device block of a build, a kernel map and a conv comes from the caller's allocator and
+    # goes back to it; an allocation failing at any point of the build is reported as
+    # IGC_ERR_OOM and every block taken before it is returned.
+    from sparse_convolution_amd import _lib as L
+    igc = _igc()
+    lib = L.load()
+    c = to_dev(workloads.make_coords("lidar"))
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    say("allocator: counting build, map and conv")
+    a = _TorchCountingAllocator()
+    h = ctypes.c_void_p()
+    assert lib.igc_grid_build(ctypes.c_void_p(c.data_ptr()), c.shape[0], ctypes.byref(a.struct), stream,
+                              ctypes.byref(h)) == 0
+    n_build = a.n_req
+    assert n_build >= 2 and len(a.live) == 1  # the grid's block stays, the temporaries came back
+    g = igc.Grid(h, c.device)
+    ref = igc.grid_build(c, memory="library")
+    for k, v in g.export().items():
+        assert np.array_equal(v, ref.export()[k]), k
+    m = igc.kernel_map(g)
+    f = torch.randn(g.n_voxels, 128, device="cuda").bfloat16()
+    w = (torch.randn(27, 128, 128, device="cuda") * 0.02).bfloat16()
+    y = igc.sparse_conv(g, f, w, kmap=m, path="ggs")
+    assert torch.equal(y, igc.sparse_conv(ref, f, w, kmap=m, path="ggs"))
+    assert a.n_req > n_build and len(a.live) == 1  # the conv's workspace came back too
+    torch.cuda.synchronize()
+    del g
+    assert len(a.live) == 0
+    for k in range(1, n_build + 1):
+        say(f"allocator: request {k} of {n_build} fails")
+        b = _TorchCountingAllocator(fail_at=k)
+        h = ctypes.c_void_p()
+        assert lib.igc_grid_build(ctypes.c_void_p(c.data_ptr()), c.shape[0], ctypes.byref(b.struct), stream,
+                                  ctypes.byref(h)) == 3
+        assert b"igc_grid_build" in lib.igc_last_error()
+        assert not h.value and len(b.live) == 0

@@ -2,14 +2,24 @@
 the oracle's build of oracle.conv_grid_coords), the neighbour map between two grids (bit-exact
 against oracle.conv_map_between) and the convolution between two grids (bf16 inputs, fp32
 accumulation; normwise error <= 2e-2 against the float64 oracle reading the same bf16 values).
+
+At full size (band: 17.3M voxels, large: 48.2M voxels, stride 2) the oracle's output grid and
+map were computed once by tests/golden/make_strided_golden.py; the HIP results must match their
+SHA-256 digests bit for bit, and the convolution between the grids is then checked at sampled
+output rows against oracle.conv over the (oracle-identical) map's columns.
 """
+import hashlib
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads
-from tests._gpu import assert_topology_equal, normwise_error, require_gpu, say, to_dev
+from tests._gpu import (TOPO_KEYS, assert_topology_equal, elementwise_error, normwise_error, require_gpu, say,
+                        segment_sample_rows, sub_map, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -83,7 +93,8 @@ def _conv_case(coords, stride, transposed, cin, cout, name, seed, sample_rows=No
 
 
 @pytest.mark.parametrize("stride,transposed,cin,cout", [(2, False, 64, 64), (2, False, 128, 256), (1, False, 32, 64),
-                                                        (2, True, 128, 64), ((2, 1, 2), False, 64, 128)])
+                                                        (2, True, 128, 64), ((2, 1, 2), False, 64, 128),
+                                                        (2, False, 32, 128), (2, True, 96, 256)])
 def test_conv_between_clusters(stride, transposed, cin, cout):
     _conv_case(_clusters(70 + cin + cout), stride, transposed, cin, cout, "clusters", seed=cin + cout)
 
@@ -115,3 +126,47 @@ def test_edge_cases():
     w = torch.randn(27, 16, 16, device="cuda")
     with pytest.raises(igc.IgcError):  # fp32 is not a gather-GEMM-scatter dtype
         igc.sparse_conv_between(down, f, w, igc.conv_map(one, down, 2))
+
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _digest(a: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+@pytest.mark.parametrize("name", ["band", "large"])
+def test_strided_workload_full_size(name):
+    igc = _igc()
+    with open(os.path.join(GOLDEN, f"strided_{name}.json")) as fh:
+        gold = json.load(fh)
+    wl = workloads.WORKLOADS[name]
+    say(f"strided {name}: build input grid")
+    gi = igc.grid_build(to_dev(workloads.make_coords(name)))
+    assert gi.n_voxels == gold["n_in"]
+    S = gold["stride"]
+    say(f"strided {name}: stride-{S} output grid and map")
+    go = igc.conv_grid(gi, S)
+    m = igc.conv_map(gi, go, S)
+    counts = {"n_voxels": go.n_voxels, "n_leaf": go.n_leaf, "n_lower": go.n_lower, "n_upper": go.n_upper}
+    assert counts == gold["counts"]
+    topo = go.export()
+    for k in TOPO_KEYS:
+        assert _digest(topo[k]) == gold["topology_sha256"][k], f"output grid topology array {k} differs"
+    assert _digest(go.active_ijk().cpu().numpy()) == gold["active_ijk_sha256"]
+    mh = m.cpu().numpy()
+    assert _digest(mh) == gold["map_sha256"]
+    say(f"strided {name}: conv between grids bf16 {wl.cin}->{wl.cout}")
+    f = workloads.make_features_device(gi.n_voxels, wl.cin, 8000 + wl.index, "cuda", torch.bfloat16)
+    w = torch.from_numpy(workloads.make_weights(wl.cin, wl.cout, 9000 + wl.index, wl.weight_std)).bfloat16()
+    y = igc.sparse_conv_between(go, f, w.cuda(), m)
+    torch.cuda.synchronize()
+    rows = segment_sample_rows(go.n_voxels, 1024, seg=256, n_random=1 << 18, seed=wl.index)
+    sub, need = sub_map(mh, rows)
+    del mh
+    say(f"strided {name}: oracle conv on {rows.shape[0]} rows")
+    ref = oracle.conv(sub, f[torch.from_numpy(need).cuda()].float().cpu().numpy(), w.float().numpy())
+    got = y[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    err = normwise_error(got, ref)
+    say(f"  normwise error {err:.3e}, elementwise {elementwise_error(got, ref):.3e}")
+    assert np.all(np.isfinite(got)) and err <= BF16_TOL

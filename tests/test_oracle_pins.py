@@ -385,6 +385,45 @@ def test_conv_gradients_match_autograd_of_masked_dense_conv3d():
     assert np.max(np.abs(dw - wt.grad.numpy())) <= 1e-12 * np.max(np.abs(dw))
 
 
+def test_conv_gradients_on_row_subsets_match_autograd():
+    """The row-restricted gradients: conv_dgrad(rows=R) equals the autograd input gradient at the
+    rows R, and conv_wgrad(rows=R) equals the autograd weight gradient of a dY that is zero
+    outside R (torch conv3d on the zero-filled dense volume, float64)."""
+    c = workloads.random_coords(700, -4, 6, seed=53)
+    g = OracleGrid(c)
+    act = g.active_ijk().astype(np.int64)
+    rng = np.random.default_rng(54)
+    cin, cout = 3, 5
+    f = rng.standard_normal((g.n, cin)).astype(np.float32)
+    w = rng.standard_normal((27, cin, cout)).astype(np.float32)
+    dy = rng.standard_normal((g.n, cout)).astype(np.float32)
+    sel = np.sort(rng.choice(g.n, g.n // 3, replace=False))
+    dy_sel = np.zeros_like(dy)
+    dy_sel[sel] = dy[sel]
+    lo = act.min(axis=0) - 1
+    ext = act.max(axis=0) - lo + 2
+    loc = torch.from_numpy(act - lo)
+
+    def autograd(dy_used):
+        x = torch.from_numpy(f.astype(np.float64)).requires_grad_(True)
+        wt = torch.from_numpy(w.astype(np.float64)).requires_grad_(True)
+        vol = torch.zeros((cin, *ext.tolist()), dtype=torch.float64)
+        vol = vol.index_put((torch.arange(cin)[:, None], loc[:, 0][None], loc[:, 1][None], loc[:, 2][None]), x.T)
+        k = wt.reshape(3, 3, 3, cin, cout).permute(4, 3, 0, 1, 2)
+        out = torch.nn.functional.conv3d(vol[None], k, padding=1)[0]
+        (out[:, loc[:, 0], loc[:, 1], loc[:, 2]].T * torch.from_numpy(dy_used.astype(np.float64))).sum().backward()
+        return x.grad.numpy(), wt.grad.numpy()
+
+    m = g.kernel_map()
+    gx, _ = autograd(dy)
+    _, gw_sel = autograd(dy_sel)
+    dx = oracle.conv_dgrad(m, dy, w, rows=sel)
+    dw = oracle.conv_wgrad(m, f, dy, rows=sel)
+    assert dx.shape == (sel.shape[0], cin)
+    assert np.max(np.abs(dx - gx[sel])) <= 1e-12 * np.max(np.abs(dx))
+    assert np.max(np.abs(dw - gw_sel)) <= 1e-12 * np.max(np.abs(dw))
+
+
 def test_conv_gradients_are_adjoints_of_the_forward():
     """<conv(x, W), dY> = <x, dgrad(dY, W)> = <W, wgrad(x, dY)>."""
     c = workloads.random_coords(4000, -15, 15, seed=61)
