@@ -6,7 +6,10 @@ IndexGrid from the shuffled coordinates (tile hash, radix sort, node registratio
 27-offset kernel map, and the 3x3x3 submanifold convolution on the automatically chosen
 path. Prints one JSON line.
 
-    python bench.py [--workload leaf] [--steps K] [--warmup W] [--gpus 1] [--backward | --strided S]
+    python bench.py [--workload large] [--steps K] [--warmup W] [--gpus 1] [--backward | --strided S]
+
+The default workload is the largest one (50M signed coordinates -> 48.2M voxels, bf16 128 -> 256):
+the headline line. The others (tiny, leaf, band, lidar, band32) are selected with --workload.
 
 value = effective conv FLOPs (2 * pairs * cin * cout, empty MACs excluded, as the fVDB notes
 define effective TFLOPS in their micro-benchmarks) per second of the whole step. The line also
@@ -44,7 +47,7 @@ CONV_SRC = {"leaf": "sparse_convolution_amd/csrc/igc_conv_leaf.hip",
             "ggs": "sparse_convolution_amd/csrc/igc_conv_ggs.hip"}
 CONV_KERNEL = {("leaf", "f32"): "k_conv_leaf_f32", ("leaf", "bf16"): "k_conv_leaf_bf16",
                ("ggs", "bf16"): "k_conv_ggs_bf16"}
-DEFAULT_STEPS = {"tiny": (50, 5), "leaf": (20, 3), "band": (10, 2), "lidar": (20, 3), "large": (3, 1),
+DEFAULT_STEPS = {"tiny": (50, 5), "leaf": (20, 3), "band": (10, 2), "lidar": (20, 3), "large": (10, 2),
                  "band32": (10, 2)}
 
 
@@ -64,6 +67,23 @@ def _traffic(path_name: str, dtype: str, workload: str):
     if d.get("source_sha") != _sha(CONV_SRC[path_name]):
         return None
     return d.get("bytes_per_launch")
+
+
+def _progress(msg: str) -> None:
+    """Progress on stderr (stdout carries only the JSON line)."""
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _pct(a, q):
@@ -119,7 +139,7 @@ def cpu_baseline(coords, wl, cin, cout, dtype_name, min_seconds=10.0):
         desc += " (conv time scaled to all rows)"
     desc += f"; build {t_build:.2f} s, kernel map {t_kmap:.2f} s, conv {t_conv_all:.2f} s"
     return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": desc, "build_mvox_s": sample.shape[0] / t_build / 1e6}
+            "sample": desc, "build_mvox_s": sample.shape[0] / t_build / 1e6, "cpu_model": _cpu_model()}
 
 
 def main() -> int:
@@ -127,7 +147,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="leaf", choices=["tiny", "leaf", "band", "lidar", "large", "band32"])
+    ap.add_argument("--workload", default="large", choices=["tiny", "leaf", "band", "lidar", "large", "band32"])
     ap.add_argument("--path", default="auto", choices=["auto", "leaf", "ggs"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -156,6 +176,7 @@ def main() -> int:
     warmup = args.warmup if args.warmup is not None else warmup
     tdtype = torch.float32 if wl.dtype == "f32" else torch.bfloat16
 
+    _progress(f"workload {args.workload}: coordinates")
     coords = workloads.make_coords(args.workload)
     dev = torch.device("cuda", 0)
     coords_d = torch.from_numpy(coords).to(dev)
@@ -192,6 +213,7 @@ def main() -> int:
             return g, m, dx, dw
         return g, m
 
+    _progress(f"{warmup} warm-up steps, then {steps} timed steps")
     for _ in range(warmup):
         step([torch.cuda.Event(enable_timing=True) for _ in range(n_ev)])
     torch.cuda.synchronize()
@@ -272,6 +294,7 @@ def main() -> int:
     if args.backward:
         line["backward"] = backward
     if not args.no_cpu_baseline:
+        _progress("cpu baseline (the oracle on a bounded sample)")
         line["cpu_baseline"] = cpu_baseline(coords, wl, wl.cin, wl.cout, wl.dtype)
     print(json.dumps(line), flush=True)
     return 0
