@@ -209,6 +209,19 @@ int igc_sparse_conv(const igc_grid* grid, const int32_t* d_map, const void* d_fe
                     int32_t cin, const void* d_w, int32_t cout, void* d_out, int32_t path,
                     igc_stream stream);
 
+/* igc_sparse_conv for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation. Same arguments, paths, results and errors
+ * as igc_sparse_conv, on the same kernels, but it calls no allocator (not hipMalloc, not the
+ * grid's igc_allocator): the temporaries (transposed weights, the gather-GEMM-scatter tile plan,
+ * per-leaf dispatch flags) live in a static device array of 64 MiB that the library holds on each
+ * GPU it runs on until the process ends. A layer that needs more (about 27*cin*cout*2 bytes plus
+ * 4.5 bytes per output row on the gather-GEMM-scatter path; the fp32 leaf path needs none)
+ * returns IGC_ERR_CAPACITY before any launch. Every call on a GPU shares that GPU's array: calls
+ * that overlap on one GPU (different streams or host threads without ordering between them)
+ * race and give undefined results. */
+int igc_sparse_conv_noalloc(const igc_grid* grid, const int32_t* d_map, const void* d_feats, int32_t dtype,
+                            int32_t cin, const void* d_w, int32_t cout, void* d_out, int32_t path, igc_stream stream);
+
 /* Backward pass of igc_sparse_conv (the same operator differentiated; fVDB notes, "accelerated
  * operators for sparse convolution", which list training support for these backends as future
  * work). Given d_dout = dL/dY [N, cout] (type `dtype`):
