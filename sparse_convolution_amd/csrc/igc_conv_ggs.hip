@@ -180,7 +180,7 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
   constexpr int OG = BN / 8;                  // 16-byte granules per output row
   static_assert(MI >= 1 && NI >= 1 && AI >= 1 && BI >= 1, "tile shape");
   static_assert(OUT_ROWS * BN * 2 <= STAGE_BYTES && OG >= 8, "output pass fits one stage");
-  static_assert(NST == 2 || NST == 4, "stages");
+  static_assert(NST >= 2 && NST <= 6, "stages");
   constexpr int LPC = AI + BI;  // loads per wave and chunk
   static_assert((NST - 2) * LPC < 64, "vmcnt range");
   // Stages as separate objects: the compiler then sees that the loads into one stage never
@@ -188,7 +188,9 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
   __shared__ uint4 s_st0[STAGE_BYTES / 16];
   __shared__ uint4 s_st1[STAGE_BYTES / 16];
   __shared__ uint4 s_st2[NST > 2 ? STAGE_BYTES / 16 : 1];
-  __shared__ uint4 s_st3[NST > 2 ? STAGE_BYTES / 16 : 1];
+  __shared__ uint4 s_st3[NST > 3 ? STAGE_BYTES / 16 : 1];
+  __shared__ uint4 s_st4[NST > 4 ? STAGE_BYTES / 16 : 1];
+  __shared__ uint4 s_st5[NST > 5 ? STAGE_BYTES / 16 : 1];
   __shared__ int32_t s_perm[kBM];
   __shared__ int32_t s_map[kNOff][kBM];
   __shared__ uint16_t s_blk[kNOff];
@@ -331,9 +333,15 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
   // Waits until chunk c+1 has landed while the chunks after it, up to `last`, stay in flight
   // (every chunk issues exactly LPC loads per wave, and vmcnt retires them in order).
   auto wait_next = [&](int ahead) {
-    if (NST > 2 && ahead >= 2) wait_vmcnt<(NST > 2 ? 2 * LPC : 0)>();
-    else if (NST > 2 && ahead == 1) wait_vmcnt<(NST > 2 ? LPC : 0)>();
+    if (NST > 5 && ahead >= 4) wait_vmcnt<(NST > 5 ? 4 * LPC : 0)>();
+    else if (NST > 4 && ahead >= 3) wait_vmcnt<(NST > 4 ? 3 * LPC : 0)>();
+    else if (NST > 3 && ahead >= 2) wait_vmcnt<(NST > 3 ? 2 * LPC : 0)>();
+    else if (NST > 2 && ahead >= 1) wait_vmcnt<(NST > 2 ? LPC : 0)>();
     else wait_vmcnt<0>();
+  };
+  // Stage i (i < NST); with the pipeline loops unrolled every use names one object.
+  auto stage = [&](int i) -> uint4* {
+    return i == 0 ? s_st0 : i == 1 ? s_st1 : i == 2 ? s_st2 : i == 3 ? s_st3 : i == 4 ? s_st4 : s_st5;
   };
   // One chunk: start filling the stage freed by the previous chunk with chunk c+NST-1,
   // multiply chunk c, wait for chunk c+1 and meet the other waves.
@@ -345,23 +353,17 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
     __syncthreads();
   };
 
-  if (nchunks > 0) issue(0, s_st0);
-  if (NST > 2) {
-    if (nchunks > 1) issue(1, s_st1);
-    if (nchunks > 2) issue(2, s_st2);
-  }
-  wait_next((NST > 2 ? (nchunks < NST - 1 ? nchunks : NST - 1) : 1) - 1);
+  // Prologue: chunks 0 .. NST-2 in flight, wait for chunk 0.
+#pragma unroll
+  for (int q = 0; q < NST - 1; ++q)
+    if (q < nchunks) issue(q, stage(q));
+  wait_next((nchunks < NST - 1 ? nchunks : NST - 1) - 1);
   __syncthreads();
+  // Chunk c is in stage c % NST; the stage it fills is the one chunk c-1 used.
   for (int c = 0; c < nchunks; c += NST) {
-    if (NST == 2) {
-      step(c, s_st0, s_st1);
-      if (c + 1 < nchunks) step(c + 1, s_st1, s_st0);
-    } else {
-      step(c, s_st0, s_st3);
-      if (c + 1 < nchunks) step(c + 1, s_st1, s_st0);
-      if (c + 2 < nchunks) step(c + 2, s_st2, s_st1);
-      if (c + 3 < nchunks) step(c + 3, s_st3, s_st2);
-    }
+#pragma unroll
+    for (int q = 0; q < NST; ++q)
+      if (q == 0 || c + q < nchunks) step(c + q, stage(q), stage((q + NST - 1) % NST));
   }
 
   // Output: rows in passes of OUT_ROWS through stage 0, granules swizzled by row; D layout of
