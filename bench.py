@@ -6,7 +6,7 @@ IndexGrid from the shuffled coordinates (tile hash, radix sort, node registratio
 27-offset kernel map, and the 3x3x3 submanifold convolution on the automatically chosen
 path. Prints one JSON line.
 
-    python bench.py [--workload large] [--steps K] [--warmup W] [--gpus 1] [--backward | --strided S]
+    python bench.py [--workload large] [--steps K] [--warmup W] [--gpus 1] [--backward | --strided S | --chain S,..]
 
 The default workload is the largest one (50M signed coordinates -> 48.2M voxels, bf16 128 -> 256):
 the headline line. The others (tiny, leaf, band, lidar, band32) are selected with --workload.
@@ -23,8 +23,10 @@ value is then 3 * 2 * pairs * cin * cout per second of the whole step, and the l
 both gradients' phase times and rooflines. With --strided S a step is one strided layer on
 the gather-GEMM-scatter path (bf16 workloads): build the input grid, its stride-S output grid
 (igc_conv_grid), the map between them (igc_conv_map) and the convolution (igc_sparse_conv_between);
-value is 2 * pairs * cin * cout of that convolution per second of the step. The default line is
-unchanged.
+value is 2 * pairs * cin * cout of that convolution per second of the step. With --chain
+S1,S2,... a step builds a chain of strided output grids with the counts kept on the device
+(igc_conv_grid_chain, one synchronisation) and, for comparison, the same grids one call at a
+time; value is the chain's wall-clock milliseconds. The default line is unchanged.
 """
 from __future__ import annotations
 
@@ -153,6 +155,7 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--backward", action="store_true", help="add the input and weight gradients to the step")
     ap.add_argument("--strided", type=int, default=0, help="time one strided layer with this stride instead")
+    ap.add_argument("--chain", default="", help="time a chain of strided output grids, e.g. 2,2,2,2, instead")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -169,6 +172,8 @@ def main() -> int:
 
     if args.strided:
         return strided_main(args, torch, igc, workloads)
+    if args.chain:
+        return chain_main(args, torch, igc, workloads)
 
     wl = workloads.WORKLOADS[args.workload]
     steps, warmup = DEFAULT_STEPS[args.workload]
@@ -369,6 +374,51 @@ def strided_main(args, torch, igc, workloads) -> int:
                      "frac": round(conv_tflops / peak, 4), "traffic": None, "kernel": "k_conv_ggs_bf16",
                      "flops_per_launch": flops, "avg_launch_ms": round(conv_ms, 4)},
     }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def chain_main(args, torch, igc, workloads) -> int:
+    """A chain of strided output grids (stage k over stage k-1's output) built with the counts on
+    the device and one synchronisation (igc_conv_grid_chain), against the same grids built one
+    call at a time (igc_conv_grid, one read-back each). Wall-clock per chain: the host waits
+    are the point."""
+    strides = [int(x) for x in args.chain.split(",")]
+    steps, warmup = DEFAULT_STEPS[args.workload]
+    steps = args.steps if args.steps is not None else max(steps, 5)
+    warmup = args.warmup if args.warmup is not None else max(warmup, 1)
+    dev = torch.device("cuda", 0)
+    g = igc.grid_build(torch.from_numpy(workloads.make_coords(args.workload)).to(dev))
+
+    def chained():
+        return igc.conv_grid_chain(g, strides)
+
+    def one_by_one():
+        out, cur = [], g
+        for s in strides:
+            cur = igc.conv_grid(cur, s)
+            out.append(cur)
+        return out
+
+    res = {}
+    for name, fn in (("chain", chained), ("one_by_one", one_by_one)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(steps):
+            t0 = time.perf_counter()
+            grids = fn()
+            torch.cuda.synchronize()
+            t.append((time.perf_counter() - t0) * 1e3)
+        res[name] = {"mean_ms": round(float(np.mean(t)), 4), "p50": _pct(t, 50), "p95": _pct(t, 95),
+                     "n_voxels": [x.n_voxels for x in grids], "n_leaf": [x.n_leaf for x in grids]}
+    line = {"metric": "strided output-grid chain, ms per chain (wall clock)", "value": res["chain"]["mean_ms"],
+            "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": res["chain"]["mean_ms"],
+            "higher_is_better": False, "dtype": "int32", "data": "synthetic",
+            "config": {"workload": args.workload, "strides": strides, "n_input_voxels": g.n_voxels},
+            "chain": res["chain"], "one_by_one": res["one_by_one"],
+            "host_syncs": {"chain": 1, "one_by_one": len(strides)}}
     print(json.dumps(line), flush=True)
     return 0
 

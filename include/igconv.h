@@ -251,10 +251,28 @@ int igc_sparse_conv_backward(const igc_grid* grid, const int32_t* d_map, const v
  * The result is a new immutable grid (*out, library-owned, freed with igc_grid_destroy) in the
  * canonical order of igc_grid_build, whose memory comes from `alloc` (may be NULL) as for
  * igc_grid_build. Errors: IGC_ERR_UNSUPPORTED for strides outside 1..3,
- * IGC_ERR_RANGE when an output coordinate leaves the int32 range; *out is then NULL. One host
- * synchronization more than igc_grid_build. */
+ * IGC_ERR_RANGE when an output coordinate leaves the int32 range; *out is then NULL. Built
+ * from the input's leaves with one host synchronisation (as igc_conv_grid_chain with one stage)
+ * when the output spans at most 4096 root tiles, else as igc_grid_build of the candidate outputs
+ * (one synchronisation more than igc_grid_build). */
 int igc_conv_grid(const igc_grid* in, const int32_t* h_stride, int32_t transposed, const igc_allocator* alloc,
                   igc_stream stream, igc_grid** out);
+
+/* Output grids of a chain of those convolutions, stage k's input being stage k-1's output
+ * (stage 0's: `in`), with the voxel counts kept on the device through the chain (DriveRT,
+ * "Counts kept on the GPU"): one host synchronisation for the whole chain instead of one per
+ * grid. h_strides int32[n_stages][3] (host, each 1, 2 or 3), h_transposed int32[n_stages]
+ * (host; NULL means none transposed), 1 <= n_stages <= 16. out[0 .. n_stages) receives new
+ * immutable grids (library-owned, each freed with igc_grid_destroy), identical to those of
+ * n_stages igc_conv_grid calls in turn, with memory from `alloc` as for igc_grid_build. Node
+ * arrays are sized from estimates; when a stage outgrows one the chain runs again from that
+ * stage with the exact counts it reported (DriveRT, "Compilation and deployment": results are
+ * never truncated), which adds one synchronisation per repetition. Errors as for
+ * igc_conv_grid, plus IGC_ERR_UNSUPPORTED when a stage's output spans more than 4096 root tiles
+ * (build such stages with igc_conv_grid); on any error every out[k] is NULL. */
+#define IGC_MAX_CHAIN 16
+int igc_conv_grid_chain(const igc_grid* in, int32_t n_stages, const int32_t* h_strides, const int32_t* h_transposed,
+                        const igc_allocator* alloc, igc_stream stream, igc_grid** out);
 
 /* Neighbour map between two grids for that convolution (DriveRT, "Shared neighbour maps", for
  * two coordinate domains): d_map int32[27, N_out] (device, caller-owned, N_out = voxels of

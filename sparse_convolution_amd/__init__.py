@@ -15,7 +15,7 @@ from . import _lib
 from ._lib import IgcError
 
 __all__ = [
-    "Grid", "grid_build", "kernel_map", "sparse_conv", "sparse_conv_backward", "conv_grid", "conv_map",
+    "Grid", "grid_build", "kernel_map", "sparse_conv", "sparse_conv_backward", "conv_grid", "conv_grid_chain", "conv_map",
     "sparse_conv_between", "standard_offsets", "release_memory", "IgcError",
     "PATH_AUTO", "PATH_LEAF", "PATH_GGS",
 ]
@@ -253,6 +253,23 @@ def conv_grid(grid: Grid, stride=2, transposed: bool = False, memory: str = "tor
     _lib.check(_lib.load().igc_conv_grid(grid.handle, s.ctypes.data_as(ctypes.c_void_p), int(bool(transposed)),
                                          _allocator(memory), _stream(grid.device), ctypes.byref(h)))
     return Grid(h, grid.device)
+
+
+def conv_grid_chain(grid: Grid, strides, transposed=None, memory: str = "torch") -> list:
+    """Output grids of a chain of 3x3x3 convolutions (stage k over stage k-1's output), strides a
+    list of ints or 3-int triples, transposed a list of bools (None: none), built with the
+    counts on the device and one synchronisation (igc_conv_grid_chain)."""
+    st = np.ascontiguousarray(np.stack([_stride_array(x) for x in strides]), dtype=np.int32)
+    n = st.shape[0]
+    tr = np.zeros(n, dtype=np.int32) if transposed is None else np.asarray([int(bool(t)) for t in transposed],
+                                                                           dtype=np.int32)
+    if tr.shape[0] != n:
+        raise ValueError("transposed must have one entry per stage")
+    hs = (ctypes.c_void_p * n)()
+    _lib.check(_lib.load().igc_conv_grid_chain(grid.handle, n, st.ctypes.data_as(ctypes.c_void_p),
+                                               tr.ctypes.data_as(ctypes.c_void_p), _allocator(memory),
+                                               _stream(grid.device), hs))
+    return [Grid(ctypes.c_void_p(hs[k]), grid.device) for k in range(n)]
 
 
 def conv_map(in_grid: Grid, out_grid: Grid, stride=2, transposed: bool = False) -> torch.Tensor:

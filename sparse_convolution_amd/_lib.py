@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libigconv.s
 EXPORTS = (
     "igc_grid_build", "igc_grid_destroy", "igc_grid_info", "igc_release_memory", "igc_grid_active_ijk",
     "igc_grid_ijk_to_index", "igc_grid_export", "igc_kernel_map", "igc_sparse_conv", "igc_sparse_conv_noalloc",
-    "igc_sparse_conv_backward", "igc_conv_grid", "igc_conv_map", "igc_sparse_conv_between", "igc_select_path",
+    "igc_sparse_conv_backward", "igc_conv_grid", "igc_conv_grid_chain", "igc_conv_map", "igc_sparse_conv_between", "igc_select_path",
     "igc_last_error",
 )
 
@@ -75,6 +75,7 @@ def load() -> ctypes.CDLL:
         "igc_sparse_conv_noalloc": [P, P, P, i32, i32, P, i32, P, i32, P],
         "igc_sparse_conv_backward": [P, P, P, i32, i32, P, i32, P, P, P, i32, P],
         "igc_conv_grid": [P, P, i32, ctypes.POINTER(Allocator), P, ctypes.POINTER(P)],
+        "igc_conv_grid_chain": [P, i32, P, P, ctypes.POINTER(Allocator), P, ctypes.POINTER(P)],
         "igc_conv_map": [P, P, P, i32, P, P],
         "igc_sparse_conv_between": [P, P, i64, P, i32, i32, P, i32, P, P],
         "igc_select_path": [P, i32, i32, i32, ctypes.POINTER(i32)],

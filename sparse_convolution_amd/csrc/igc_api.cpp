@@ -499,12 +499,54 @@ int igc_conv_grid(const igc_grid* in, const int32_t* h_stride, int32_t transpose
   g->stream = (hipStream_t)stream;
   g->device = in->device;
   if (alloc) g->alloc = *alloc;
-  const int rc = build_conv_grid(in, h_stride, transposed, (hipStream_t)stream, g);
+  const int32_t tr = transposed ? 1 : 0;
+  // Built from the input's leaves with the counts on the device (one read-back) where the
+  // derived build covers the input; otherwise as the coordinate build of candidate outputs.
+  const int rc = in->n_voxels > 0 && derive_supported(in, h_stride, tr)
+                     ? derive_chain(in, 1, h_stride, &tr, (hipStream_t)stream, &g)
+                     : build_conv_grid(in, h_stride, transposed, (hipStream_t)stream, g);
   if (rc != IGC_OK) {
     free_grid(g);
     return rc;
   }
   *out = g;
+  return IGC_OK;
+}
+
+int igc_conv_grid_chain(const igc_grid* in, int32_t n_stages, const int32_t* h_strides, const int32_t* h_transposed,
+                        const igc_allocator* alloc, igc_stream stream, igc_grid** out) {
+  clear_error();
+  if (!out) return set_error(IGC_ERR_INVALID_ARG, "igc_conv_grid_chain: out is null");
+  if (n_stages < 1 || n_stages > IGC_MAX_CHAIN)
+    return set_error(IGC_ERR_INVALID_ARG, "igc_conv_grid_chain: n_stages must be 1 .. 16");
+  for (int k = 0; k < n_stages; ++k) out[k] = nullptr;
+  if (!in || !h_strides) return set_error(IGC_ERR_INVALID_ARG, "igc_conv_grid_chain: in or h_strides is null");
+  if (!allocator_ok(alloc))
+    return set_error(IGC_ERR_INVALID_ARG, "igc_conv_grid_chain: the allocator needs both alloc and release");
+  int32_t tr[IGC_MAX_CHAIN];
+  for (int k = 0; k < n_stages; ++k) {
+    int n[3];
+    tr[k] = h_transposed && h_transposed[k] ? 1 : 0;
+    if (!conv_grid_slots(h_strides + 3 * k, tr[k], n))
+      return set_error(IGC_ERR_UNSUPPORTED, "igc_conv_grid_chain: strides must be 1, 2 or 3");
+  }
+  igc_grid* g[IGC_MAX_CHAIN] = {};
+  for (int k = 0; k < n_stages; ++k) {
+    g[k] = new (std::nothrow) igc_grid();
+    if (!g[k]) {
+      for (int q = 0; q < k; ++q) free_grid(g[q]);
+      return set_error(IGC_ERR_OOM, "igc_conv_grid_chain: host allocation");
+    }
+    g[k]->stream = (hipStream_t)stream;
+    g[k]->device = in->device;
+    if (alloc) g[k]->alloc = *alloc;
+  }
+  const int rc = derive_chain(in, n_stages, h_strides, tr, (hipStream_t)stream, g);
+  if (rc != IGC_OK) {
+    for (int k = 0; k < n_stages; ++k) free_grid(g[k]);
+    return rc;
+  }
+  for (int k = 0; k < n_stages; ++k) out[k] = g[k];
   return IGC_OK;
 }
 

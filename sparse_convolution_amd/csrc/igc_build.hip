@@ -70,7 +70,8 @@ struct BuildState {
   uint32_t n_tiles;           // distinct root tiles inserted
   uint32_t tile_list_count;   // compaction cursor
   uint32_t guard;             // a device-side bounds check failed (the build is rejected)
-  uint32_t pad;
+  uint32_t range;             // a derived grid's coordinate left the int32 range
+  uint32_t cap_over;          // a derived grid outgrew a node capacity (the chain is repeated)
   uint64_t off_or, off_and;   // OR / AND over all in-tile offsets
   uint64_t key_or, key_and;   // OR / AND over all tile keys
   uint64_t counts[4];         // N, F, Lw, U from the sorted keys
@@ -113,6 +114,8 @@ __global__ void k_init_root(BuildState* st, uint64_t* __restrict__ keys, int64_t
     st->n_tiles = 0;
     st->tile_list_count = 0;
     st->guard = 0;
+    st->range = 0;
+    st->cap_over = 0;
     st->off_or = 0;
     st->off_and = ~0ull;
     st->key_or = 0;
@@ -372,10 +375,23 @@ __global__ void k_tile_rank(const uint64_t* __restrict__ sorted, int64_t U, cons
 
 // Up to kSmallSort tile keys: bitonic sort in one workgroup, then each key's rank into the
 // table (the sort and the rank pass of larger tile sets in one launch).
+// n < 0: the count is the state's tile count. When that exceeds ucap (or kSmallSort), or the
+// table overflowed, the table is emptied (every later lookup then misses instead of returning
+// a rank beyond the node arrays) and cap_over is set.
 __global__ __launch_bounds__(1024) void k_sort_rank_small(const uint64_t* __restrict__ in, uint64_t* __restrict__ out,
-                                                          int n, const uint64_t* __restrict__ keys,
-                                                          int32_t* __restrict__ vals, uint32_t mask, BuildState* st) {
+                                                          int n, uint64_t* __restrict__ keys,
+                                                          int32_t* __restrict__ vals, uint32_t mask, BuildState* st,
+                                                          int64_t ucap) {
   __shared__ uint64_t s[kSmallSort];
+  if (n < 0) {
+    const uint32_t nt = st->n_tiles;
+    if ((int64_t)nt > (ucap < kSmallSort ? ucap : kSmallSort) || st->overflow) {
+      for (uint32_t t = threadIdx.x; t <= mask; t += blockDim.x) keys[t] = kEmptyKey;
+      if (threadIdx.x == 0) atomicOr(&st->cap_over, 1u);
+      return;
+    }
+    n = (int)nt;
+  }
   bitonic_sort_lds(in, s, n);
   for (int t = threadIdx.x; t < n; t += blockDim.x) {
     const uint64_t k = s[t];
@@ -992,8 +1008,9 @@ __global__ __launch_bounds__(256) void k_register(const uint64_t* __restrict__ k
 constexpr int kLeafPer = 4;                       // leaves per thread
 constexpr int kLeafGroup = 256 * kLeafPer;        // leaves per workgroup
 __global__ __launch_bounds__(256) void k_leaf_count(LeafRec* __restrict__ leaf, int64_t F,
-                                                    uint64_t* __restrict__ group_sum) {
+                                                    uint64_t* __restrict__ group_sum, const uint64_t* dcnt) {
   __shared__ uint64_t s_tmp[4];
+  if (dcnt && (int64_t)dcnt[1] < F) F = (int64_t)dcnt[1];
   const int64_t f0 = (int64_t)blockIdx.x * kLeafGroup + (int64_t)threadIdx.x * kLeafPer;
   uint32_t cnt[kLeafPer];
   uint64_t tsum = 0;
@@ -1043,7 +1060,8 @@ __global__ __launch_bounds__(1024) void k_scan_groups(uint64_t* __restrict__ v, 
 }
 
 __global__ __launch_bounds__(256) void k_leaf_offset(LeafRec* __restrict__ leaf, int64_t F,
-                                                     const uint64_t* __restrict__ group_pre) {
+                                                     const uint64_t* __restrict__ group_pre, const uint64_t* dcnt) {
+  if (dcnt && (int64_t)dcnt[1] < F) F = (int64_t)dcnt[1];
   const uint64_t add = group_pre[blockIdx.x];
   const int64_t f0 = (int64_t)blockIdx.x * kLeafGroup + (int64_t)threadIdx.x * kLeafPer;
 #pragma unroll
@@ -1055,8 +1073,12 @@ __global__ __launch_bounds__(256) void k_leaf_offset(LeafRec* __restrict__ leaf,
 // words) in the first nbl workgroups and upper nodes (512 words) after them.
 __global__ __launch_bounds__(256) void k_node_prefix(const uint64_t* __restrict__ lmask, uint16_t* __restrict__ lpre,
                                                      int64_t nl, int64_t nbl, const uint64_t* __restrict__ umask,
-                                                     uint16_t* __restrict__ upre, int64_t nu) {
+                                                     uint16_t* __restrict__ upre, int64_t nu, const uint64_t* dcnt) {
   const int lane = lane_id();
+  if (dcnt) {
+    if ((int64_t)dcnt[2] < nl) nl = (int64_t)dcnt[2];
+    if ((int64_t)dcnt[3] < nu) nu = (int64_t)dcnt[3];
+  }
   const bool lower = (int64_t)blockIdx.x < nbl;
   const int64_t node = (lower ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - nbl) * 4 + (threadIdx.x >> 6);
   const int words = lower ? 64 : 512;
@@ -1074,8 +1096,8 @@ __global__ __launch_bounds__(256) void k_node_prefix(const uint64_t* __restrict_
 
 // The 3x3x3 block of leaves around every leaf, resolved once through the tree (root hash and
 // fixed-fanout descent) for the kernel map and the leaf-local convolution.
-__global__ __launch_bounds__(256) void k_leaf_neighbors(GridView g, int32_t* __restrict__ nbr) {
-  const int64_t total = g.n_leaf * 27;
+__global__ __launch_bounds__(256) void k_leaf_neighbors(GridView g, int32_t* __restrict__ nbr, const uint64_t* dcnt) {
+  const int64_t total = (dcnt && (int64_t)dcnt[1] < g.n_leaf ? (int64_t)dcnt[1] : g.n_leaf) * 27;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t f = e / 27;
     const int slot = (int)(e - f * 27);
@@ -1225,7 +1247,8 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   }
   uint64_t* tiles_sorted = tile_tmp;
   if (U <= kSmallSort) {
-    k_sort_rank_small<<<1, 1024, 0, s>>>(tile_list, tile_tmp, (int)U, root_keys, root_vals, (uint32_t)(cap - 1), st);
+    k_sort_rank_small<<<1, 1024, 0, s>>>(tile_list, tile_tmp, (int)U, root_keys, root_vals, (uint32_t)(cap - 1), st,
+                                         (int64_t)U);
     IGC_HIP(hipGetLastError(), "igc_grid_build: tile sort launch");
   } else {
     const PassSpec tps = pass_spec(key_var);
@@ -1360,16 +1383,16 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   // the guard.
   const int64_t nbl = (Lw + 3) / 4;
   k_node_prefix<<<(unsigned)(nbl + (U + 3) / 4), 256, 0, s>>>(g->lower_mask, g->lower_pre, Lw, nbl, g->upper_mask,
-                                                             g->upper_pre, U);
+                                                             g->upper_pre, U, nullptr);
   IGC_HIP(hipGetLastError(), "igc_grid_build: node prefix launch");
-  k_leaf_neighbors<<<grid_for(F * 27, 256, 8192), 256, 0, s>>>(g->view(), g->leaf_nbr);
+  k_leaf_neighbors<<<grid_for(F * 27, 256, 8192), 256, 0, s>>>(g->view(), g->leaf_nbr, nullptr);
   IGC_HIP(hipGetLastError(), "igc_grid_build: leaf neighbour launch");
-  k_leaf_count<<<(unsigned)groups, 256, 0, s>>>(g->leaf, F, gsum);
+  k_leaf_count<<<(unsigned)groups, 256, 0, s>>>(g->leaf, F, gsum, nullptr);
   IGC_HIP(hipGetLastError(), "igc_grid_build: leaf count launch");
   k_scan_groups<<<1, 1024, 0, s>>>(gsum, groups, st, hd);  // also publishes the state (N) to h
   IGC_HIP(hipGetLastError(), "igc_grid_build: leaf scan launch");
   if (groups > 1) {
-    k_leaf_offset<<<(unsigned)groups, 256, 0, s>>>(g->leaf, F, gsum);
+    k_leaf_offset<<<(unsigned)groups, 256, 0, s>>>(g->leaf, F, gsum, nullptr);
     IGC_HIP(hipGetLastError(), "igc_grid_build: leaf offset launch");
   }
   // Last read-back: the voxel count.
@@ -1379,6 +1402,637 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   if (N < F || N > n_in) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: inconsistent voxel count");
   g->n_voxels = N;
   return IGC_OK;
+}
+
+
+// ------------------------------------------------------------------------------ derived grids
+//
+// Output grids of strided / transposed 3x3x3 convolutions built from the input grid's leaves,
+// with every count kept on the device (DriveRT, "Counts kept on the GPU": a chain of strided
+// layers needs one host synchronisation, not one per layer).
+//
+// Per axis an output coordinate y and an input coordinate x are related when |x - s y| <= 1
+// (strided) or |y - s x| <= 1 (transposed); y is active iff some active x is related to it on
+// all three axes (offsets d in {-1, 0, 1}^3). The relation is separable, so one input leaf's
+// contribution to one output leaf comes from 8-bit row operations on its mask: output row
+// (yi, yj) ORs the input rows (xi, xj) related to it, and the k bits of that row map through
+// the k relation.
+//  1. Records: one wave per (input leaf, output-leaf slot) writes the slot's 512-bit mask and
+//     origin (or marks it empty); a non-empty record inserts its root tile into the new
+//     grid's root table.
+//  2. The root tiles are sorted and ranked in one workgroup (up to 4096 tiles).
+//  3. Record r gets key ((tile rank << 27 | upper child << 12 | lower child) << IB) | r, an
+//     empty one ~0; a radix sort over the rank and child bits puts the records in canonical
+//     leaf order, records of one output leaf next to each other.
+//  4. Leaf / lower / upper starts are counted over the sorted keys and scanned (F, Lw, U); the
+//     register pass writes the nodes top-down and ORs every record's mask into its leaf.
+//  5. Node prefixes, the leaf neighbour table, leaf rows and N follow as in the coordinate
+//     build, each bounded by the counts on the device.
+// Node arrays are sized from estimates made on the host. A stage that outgrows one sets a
+// flag; after the one read-back the chain runs again from that stage with the exact counts it
+// reported (DriveRT, "Compilation and deployment": buffers start from an estimated capacity
+// and the invocation is repeated with larger ones; results are never truncated).
+
+namespace {
+
+struct Derive {
+  int32_t s[3];
+  int32_t tr;    // transposed
+  int32_t L[3];  // output-leaf slots per axis and input leaf
+};
+
+__device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+// Output span [lo, hi] on one axis of the input span [x0, x0 + 7].
+__device__ __forceinline__ void derive_span(int64_t x0, int32_t s, int32_t tr, int64_t* lo, int64_t* hi) {
+  if (tr) {
+    *lo = (int64_t)s * x0 - 1;
+    *hi = (int64_t)s * (x0 + 7) + 1;
+  } else {
+    *lo = -floor_div(1 - x0, s);  // ceil((x0 - 1) / s)
+    *hi = floor_div(x0 + 8, s);
+  }
+}
+
+// Bits t in [0, 8) of the input positions x0 + t related to the output Y + l on one axis,
+// with c = s Y - x0 (strided) or c = Y - s x0 (transposed), so that only small integers occur.
+__device__ __forceinline__ uint32_t related_bits(int32_t c, int32_t l, int32_t s, int32_t tr) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int d = -1; d <= 1; ++d) {
+    int32_t t;
+    if (tr) {
+      const int32_t z = c + l - d;  // s (x - x0) when s divides it
+      if (z % s != 0) continue;
+      t = z / s;
+    } else {
+      t = c + s * l + d;
+    }
+    if (t >= 0 && t < 8) m |= 1u << t;
+  }
+  return m;
+}
+
+// Step 1. Record w = f * S + slot for input leaf f (f below the input's leaf count, read from
+// in_counts[1] when the input is itself a derived grid) and output-leaf slot `slot`.
+__global__ __launch_bounds__(256) void k_derive_records(const LeafRec* __restrict__ leaf,
+                                                        const int4* __restrict__ origin, int64_t F_cap,
+                                                        const uint64_t* in_counts, Derive dv,
+                                                        int4* __restrict__ rec_origin, uint64_t* __restrict__ rec_mask,
+                                                        uint64_t* __restrict__ root_keys, uint32_t root_mask,
+                                                        uint64_t* __restrict__ tile_list, BuildState* st) {
+  const int S = dv.L[0] * dv.L[1] * dv.L[2];
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= F_cap * S) return;
+  const int lane = lane_id();
+  int64_t F = F_cap;
+  if (in_counts && (int64_t)in_counts[1] < F) F = (int64_t)in_counts[1];
+  const int64_t f = w / S;
+  const int slot = (int)(w - f * S);
+  int4 out_o = make_int4(0, 0, 0, 0);  // .w = 1: the record is not empty
+  if (f < F) {
+    const int4 o = origin[f];
+    const int64_t x0[3] = {o.x, o.y, o.z};
+    const int q[3] = {slot / (dv.L[1] * dv.L[2]), (slot / dv.L[2]) % dv.L[1], slot % dv.L[2]};
+    int64_t Y[3];
+    bool inside = true, in_range = true;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      int64_t lo, hi;
+      derive_span(x0[a], dv.s[a], dv.tr, &lo, &hi);
+      Y[a] = floor_div(lo, 8) * 8 + 8 * q[a];
+      if (Y[a] > hi) inside = false;
+      if (Y[a] < (int64_t)INT32_MIN || Y[a] > (int64_t)INT32_MAX - 7) in_range = false;
+    }
+    if (inside) {
+      const int l = lane & 7;
+      int32_t c[3];
+#pragma unroll
+      for (int a = 0; a < 3; ++a)
+        c[a] = (int32_t)(dv.tr ? Y[a] - (int64_t)dv.s[a] * x0[a] : (int64_t)dv.s[a] * Y[a] - x0[a]);
+      // Lanes 0..7 hold the relation masks of positions l = 0..7 (every lane computes its l's).
+      const uint32_t ri = related_bits(c[0], l, dv.s[0], dv.tr);
+      const uint32_t rj = related_bits(c[1], l, dv.s[1], dv.tr);
+      const uint32_t rk = related_bits(c[2], l, dv.s[2], dv.tr);
+      const int yi = lane >> 3, yj = lane & 7;
+      const uint32_t mi = (uint32_t)__shfl((int)ri, yi, 64), mj = (uint32_t)__shfl((int)rj, yj, 64);
+      uint64_t sel = 0;  // the bytes (input rows xj) related to yj
+#pragma unroll
+      for (int xj = 0; xj < 8; ++xj) sel |= ((mj >> xj) & 1u) ? (0xFFull << (8 * xj)) : 0ull;
+      uint64_t acc = 0;
+#pragma unroll
+      for (int xi = 0; xi < 8; ++xi) {
+        const uint64_t word = leaf[f].mask[xi];
+        acc |= ((mi >> xi) & 1u) ? (word & sel) : 0ull;
+      }
+      acc |= acc >> 32;
+      acc |= acc >> 16;
+      acc |= acc >> 8;
+      const uint32_t b = (uint32_t)acc & 0xFFu;  // input k bits reaching this output row
+      uint32_t r = 0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) r |= (b & (uint32_t)__shfl((int)rk, t, 64)) ? (1u << t) : 0u;
+      // Mask word yi of the output leaf: bits yj * 8 + k from the 8 lanes of row yi.
+      uint64_t v = (uint64_t)r << (8 * yj);
+      v |= shfl_xor64(v, 1);
+      v |= shfl_xor64(v, 2);
+      v |= shfl_xor64(v, 4);
+      if (__ballot(r != 0u) != 0ull) {
+        if (in_range) {
+          if (yj == 0) rec_mask[w * 8 + yi] = v;
+          if (lane == 0) {
+            out_o = make_int4((int32_t)Y[0], (int32_t)Y[1], (int32_t)Y[2], 1);
+            insert_tile(root_keys, root_mask, root_mask + 1u, tile_key(out_o.x, out_o.y, out_o.z), st, tile_list,
+                        (uint32_t)kSmallSort);
+          }
+        } else if (lane == 0) {
+          atomicOr(&st->range, 1u);
+        }
+      }
+    }
+  }
+  if (lane == 0) rec_origin[w] = out_o;
+}
+
+// Step 3. Sort keys of the records and the digit histograms of their sort.
+__global__ __launch_bounds__(256) void k_derive_keys(const int4* __restrict__ rec_origin, int64_t R,
+                                                     const uint64_t* __restrict__ root_keys,
+                                                     const int32_t* __restrict__ root_vals, uint32_t root_mask, int ib,
+                                                     int32_t rank_cap, PassSpec ps, uint64_t* __restrict__ keys,
+                                                     uint32_t* __restrict__ hist, BuildState* st) {
+  __shared__ uint32_t s_hist[kHistWidth];
+  for (int x = threadIdx.x; x < (ps.passes << ps.bits); x += blockDim.x) s_hist[x] = 0;
+  // A stage already over capacity (its table emptied) only writes empty keys: the rest of its
+  // kernels then do no work, and the chain is repeated.
+  const bool dead = st->cap_over != 0u;
+  __syncthreads();
+  for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < R; r += (int64_t)gridDim.x * blockDim.x) {
+    const int4 o = rec_origin[r];
+    uint64_t k = ~0ull;
+    if (o.w && !dead) {
+      const int64_t slot = probe_slot(root_keys, root_mask, tile_key(o.x, o.y, o.z), st);
+      if (slot >= 0 && root_vals[slot] >= rank_cap) {
+        atomicOr(&st->cap_over, 1u);  // more tiles than the key has rank bits for (the host widens it)
+      } else if (slot >= 0) {
+        const uint32_t ui = (uint32_t)o.x, uj = (uint32_t)o.y, uk = (uint32_t)o.z;
+        const uint64_t up = (((ui >> 7) & 31u) << 10) | (((uj >> 7) & 31u) << 5) | ((uk >> 7) & 31u);
+        const uint64_t lo = (((ui >> 3) & 15u) << 8) | (((uj >> 3) & 15u) << 4) | ((uk >> 3) & 15u);
+        k = ((((uint64_t)root_vals[slot] << 27) | (up << 12) | lo) << ib) | (uint64_t)r;
+      }
+    }
+    keys[r] = k;
+    hist_add(s_hist, k, ps);
+  }
+  hist_flush(s_hist, hist, ps);
+}
+
+// Leaf / lower / upper starts of a sorted record key (packed as in start_flags); the empty
+// records (~0) sort last and start nothing.
+__device__ __forceinline__ uint64_t derive_flags(uint64_t key, uint64_t prev, bool first, int ib) {
+  if (key == ~0ull) return 0;
+  if (first) return 0x0001000100010000ull;
+  return ((uint64_t)((key >> ib) != (prev >> ib)) << 16) |
+         ((uint64_t)((key >> (ib + 12)) != (prev >> (ib + 12))) << 32) |
+         ((uint64_t)((key >> (ib + 27)) != (prev >> (ib + 27))) << 48);
+}
+
+// Step 4a. Per block of 4096 sorted keys, the leaf / lower / upper starts.
+__global__ __launch_bounds__(256) void k_derive_count(const uint64_t* __restrict__ keys, int64_t n, int ib,
+                                                      uint64_t* __restrict__ block_counts) {
+  __shared__ uint64_t s_keys[kPaddedKeys];
+  __shared__ uint64_t s_prev;
+  __shared__ uint64_t s_tmp[4];
+  const int64_t base = (int64_t)blockIdx.x * kTileKeys;
+  stage_block(keys, n, base, s_keys, &s_prev);
+  uint64_t c = 0;
+  for (int q = 0; q < kKeysPerThread; ++q) {
+    const int p = threadIdx.x * kKeysPerThread + q;
+    const int64_t e = base + p;
+    if (e < n) c += derive_flags(s_keys[kpad(p)], p ? s_keys[kpad(p - 1)] : s_prev, e == 0, ib);
+  }
+  uint64_t total;
+  block_excl_scan64<kThreads>(c, s_tmp, &total);
+  if (threadIdx.x == 0) block_counts[blockIdx.x] = total;
+}
+
+// Step 4b. Registration: node rows from the scanned block counts, nodes written top-down, the
+// records' masks OR-ed into their leaves. Rows past a capacity set cap_over and stop.
+__global__ __launch_bounds__(256) void k_derive_register(const uint64_t* __restrict__ keys, int64_t n,
+                                                         const uint64_t* __restrict__ prefix, int ib,
+                                                         const int4* __restrict__ rec_origin,
+                                                         const uint64_t* __restrict__ rec_mask, Topo t,
+                                                         BuildState* st) {
+  __shared__ uint64_t s_keys[kPaddedKeys];
+  __shared__ uint64_t s_prev;
+  __shared__ uint64_t s_tmp[4];
+  const int64_t base = (int64_t)blockIdx.x * kTileKeys;
+  stage_block(keys, n, base, s_keys, &s_prev);
+  const int p0 = threadIdx.x * kKeysPerThread;
+  uint64_t c = 0;
+  for (int q = 0; q < kKeysPerThread; ++q) {
+    const int64_t e = base + p0 + q;
+    if (e < n) c += derive_flags(s_keys[kpad(p0 + q)], (p0 + q) ? s_keys[kpad(p0 + q - 1)] : s_prev, e == 0, ib);
+  }
+  const uint64_t excl = block_excl_scan64<kThreads>(c, s_tmp, nullptr);
+  int64_t nf = (int64_t)prefix[blockIdx.x * 4 + 1] + (int64_t)((excl >> 16) & 0xFFFF);
+  int64_t nl = (int64_t)prefix[blockIdx.x * 4 + 2] + (int64_t)((excl >> 32) & 0xFFFF);
+  int64_t nu = (int64_t)prefix[blockIdx.x * 4 + 3] + (int64_t)((excl >> 48) & 0xFFFF);
+  for (int q = 0; q < kKeysPerThread; ++q) {
+    const int64_t e = base + p0 + q;
+    if (e >= n) break;
+    const uint64_t key = s_keys[kpad(p0 + q)];
+    if (key == ~0ull) break;
+    const uint64_t f = derive_flags(key, (p0 + q) ? s_keys[kpad(p0 + q - 1)] : s_prev, e == 0, ib);
+    nf += (int64_t)((f >> 16) & 1);
+    nl += (int64_t)((f >> 32) & 1);
+    nu += (int64_t)((f >> 48) & 1);
+    const int64_t lf = nf - 1, lw = nl - 1, u = nu - 1;
+    if (lf >= t.n_leaf || lw >= t.n_lower || u >= t.n_upper) {
+      atomicOr(&st->cap_over, 1u);
+      break;
+    }
+    const uint64_t r = key & ((1ull << ib) - 1ull);
+    const int4 o = rec_origin[r];
+    const uint32_t ui = (uint32_t)o.x, uj = (uint32_t)o.y, uk = (uint32_t)o.z;
+    if ((f >> 48) & 1) {
+      t.root_list[u] = tile_key(o.x, o.y, o.z);
+      t.upper_origin[u] = make_int4(o.x & ~4095, o.y & ~4095, o.z & ~4095, 0);
+      t.upper_first[u] = (uint32_t)lw;
+    }
+    if ((f >> 32) & 1) {
+      const uint32_t cu = (((ui >> 7) & 31u) << 10) | (((uj >> 7) & 31u) << 5) | ((uk >> 7) & 31u);
+      atomicOr((unsigned long long*)&t.upper_mask[u * 512 + (cu >> 6)], 1ull << (cu & 63u));
+      t.lower_origin[lw] = make_int4(o.x & ~127, o.y & ~127, o.z & ~127, 0);
+      t.lower_first[lw] = (uint32_t)lf;
+    }
+    if ((f >> 16) & 1) {
+      const uint32_t cl = (((ui >> 3) & 15u) << 8) | (((uj >> 3) & 15u) << 4) | ((uk >> 3) & 15u);
+      atomicOr((unsigned long long*)&t.lower_mask[lw * 64 + (cl >> 6)], 1ull << (cl & 63u));
+      t.leaf_origin[lf] = make_int4(o.x, o.y, o.z, 0);
+    }
+#pragma unroll
+    for (int wd = 0; wd < 8; ++wd) {
+      const uint64_t m = rec_mask[r * 8 + wd];
+      if (m) atomicOr((unsigned long long*)&t.leaf[lf].mask[wd], m);
+    }
+  }
+}
+
+}  // namespace
+
+namespace {
+
+// Output values on one axis reached from `n` consecutive input values (the input span of a
+// leaf, n = 8, or of a root tile, n = 4096), and how many aligned blocks of n they can touch.
+int64_t span_len(int64_t n, int32_t s, int32_t tr) { return tr ? (int64_t)s * (n - 1) + 3 : (n + 1) / s + 1; }
+int span_blocks(int64_t n, int32_t s, int32_t tr) { return (int)((span_len(n, s, tr) - 1 + n - 1) / n + 1); }
+
+// Node count estimate of a derived grid from its input's: per axis the output span of one
+// node over the node size; strided grids at least half the input's (sparse inputs shrink
+// less than dense ones); 1.5x room for strided, none for transposed (the volume growth
+// already bounds a band's).
+int64_t derive_estimate(int64_t n_in, int64_t unit, const int32_t* s, int32_t tr, int64_t cap) {
+  double g = 1.0;
+  for (int a = 0; a < 3; ++a) g *= (double)span_len(unit, s[a], tr) / (double)unit;
+  if (!tr) g = std::max(g, 0.5) * 1.5;
+  const double e = std::ceil(g * (double)n_in) + 16.0;
+  return std::max<int64_t>(1, std::min<int64_t>(cap, e > 9e18 ? cap : (int64_t)e));
+}
+
+struct DeriveStage {
+  Derive dv{};
+  int64_t F_in = 0, Lw_in = 0, U_in = 0;  // input capacities (exact for the chain's input)
+  int64_t R = 0;                           // records
+  int64_t F = 0, Lw = 0, U = 0;            // output capacities
+  uint32_t root = 0;                       // root table capacity (power of two)
+  int ib = 0, rb = 0;                      // record-index bits and tile-rank bits of a key
+  bool exact = false;                      // capacities are the counts a previous run reported
+};
+
+size_t derive_topology_bytes(const DeriveStage& d, size_t* zero_end) {
+  size_t off = 0;
+  auto carve = [&](size_t bytes) { off = align_up(off + bytes, 256); };
+  carve(d.U * 512 * 8);
+  carve(d.Lw * 64 * 8);
+  carve(d.F * sizeof(LeafRec));
+  *zero_end = off;
+  carve(d.U * 8);
+  carve(d.U * 16);
+  carve(d.U * 512 * 2);
+  carve(d.U * 4);
+  carve(d.Lw * 16);
+  carve(d.Lw * 64 * 2);
+  carve(d.Lw * 4);
+  carve(d.F * 16);
+  carve(d.F * 27 * 4);
+  carve((size_t)d.root * 12);
+  return off;
+}
+
+// Carves the topology arrays of g from its block (same layout as the coordinate build).
+void derive_carve(const DeriveStage& d, igc_grid* g) {
+  char* blk = (char*)g->block;
+  size_t off = 0;
+  auto carve = [&](size_t bytes) {
+    char* p = blk + off;
+    off = align_up(off + bytes, 256);
+    return p;
+  };
+  g->upper_mask = (uint64_t*)carve(d.U * 512 * 8);
+  g->lower_mask = (uint64_t*)carve(d.Lw * 64 * 8);
+  g->leaf = (LeafRec*)carve(d.F * sizeof(LeafRec));
+  g->root_list = (uint64_t*)carve(d.U * 8);
+  g->upper_origin = (int4*)carve(d.U * 16);
+  g->upper_pre = (uint16_t*)carve(d.U * 512 * 2);
+  g->upper_first = (uint32_t*)carve(d.U * 4);
+  g->lower_origin = (int4*)carve(d.Lw * 16);
+  g->lower_pre = (uint16_t*)carve(d.Lw * 64 * 2);
+  g->lower_first = (uint32_t*)carve(d.Lw * 4);
+  g->leaf_origin = (int4*)carve(d.F * 16);
+  g->leaf_nbr = (int32_t*)carve(d.F * 27 * 4);
+  g->root_keys = (uint64_t*)carve((size_t)d.root * 12);
+  g->root_vals = (int32_t*)(g->root_keys + d.root);
+  g->root_cap = d.root;
+  g->n_leaf = d.F;  // capacities until the read-back
+  g->n_lower = d.Lw;
+  g->n_upper = d.U;
+}
+
+// Temporaries of one stage, carved from the chain's workspace.
+struct DeriveWs {
+  int4* rec_origin;
+  uint64_t* rec_mask;
+  uint64_t *ka, *kb;
+  uint32_t *hpart, *hist, *cnt, *off;
+  uint64_t *bcounts, *bprefix, *gsum;
+  uint64_t *tile_list, *tile_tmp;
+  int64_t sort_tiles, nbh, nb, groups;
+};
+
+size_t derive_ws_bytes(const DeriveStage& d, DeriveWs* w, char* base) {
+  size_t off = 0;
+  auto carve = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off = align_up(off + bytes, 256);
+    return p;
+  };
+  const int64_t R = std::max<int64_t>(d.R, 1);
+  w->sort_tiles = (R + kSortTile - 1) / kSortTile;
+  w->nbh = grid_for(R, 256, kHistBlocks);
+  w->nb = (R + kTileKeys - 1) / kTileKeys;
+  w->groups = (d.F + kLeafGroup - 1) / kLeafGroup;
+  w->rec_origin = (int4*)carve(R * 16);
+  w->rec_mask = (uint64_t*)carve(R * 64);
+  w->ka = (uint64_t*)carve(R * 8);
+  w->kb = (uint64_t*)carve(R * 8);
+  w->hpart = (uint32_t*)carve((size_t)w->nbh * kHistWidth * 4);
+  w->hist = (uint32_t*)carve((size_t)kMaxPasses * kMaxBins * 4);
+  w->cnt = (uint32_t*)carve((size_t)w->sort_tiles * kMaxBins * 4);
+  w->off = (uint32_t*)carve((size_t)w->sort_tiles * kMaxBins * 4);
+  w->bcounts = (uint64_t*)carve((size_t)w->nb * 8);
+  w->bprefix = (uint64_t*)carve((size_t)w->nb * 32);
+  w->gsum = (uint64_t*)carve((size_t)std::max<int64_t>(w->groups, 1) * 8);
+  w->tile_list = (uint64_t*)carve((size_t)kSmallSort * 8);
+  w->tile_tmp = (uint64_t*)carve((size_t)kSmallSort * 8);
+  return off;
+}
+
+// Enqueues one stage: `in` (its counts on the device in in_counts when it is itself derived)
+// to `out`, whose block is allocated and carved. st: this stage's device state, hd its
+// pinned host copy.
+int derive_enqueue(const igc_grid* in, const uint64_t* in_counts, const DeriveStage& d, const DeriveWs& w,
+                   igc_grid* out, BuildState* st, BuildState* hd, hipStream_t s) {
+  k_init_root<<<grid_for((int64_t)d.root, 256, 4096), 256, 0, s>>>(st, out->root_keys, (int64_t)d.root);
+  IGC_HIP(hipGetLastError(), "igc_conv_grid: init launch");
+  size_t zero_end = 0;
+  derive_topology_bytes(d, &zero_end);
+  int rc = fill_u64((uint64_t*)out->block, (int64_t)(zero_end / 8), 0ull, s);
+  if (rc) return rc;
+  if (d.R > 0) {
+    k_derive_records<<<(unsigned)((d.R + 3) / 4), 256, 0, s>>>(in->leaf, in->leaf_origin, d.F_in, in_counts, d.dv,
+                                                               w.rec_origin, w.rec_mask, out->root_keys,
+                                                               d.root - 1u, w.tile_list, st);
+    IGC_HIP(hipGetLastError(), "igc_conv_grid: record launch");
+  }
+  k_sort_rank_small<<<1, 1024, 0, s>>>(w.tile_list, w.tile_tmp, -1, out->root_keys, out->root_vals, d.root - 1u, st,
+                                       d.U);
+  IGC_HIP(hipGetLastError(), "igc_conv_grid: tile sort launch");
+  const int key_bits = d.rb + 27;
+  const PassSpec ps = pass_spec(((1ull << key_bits) - 1ull) << d.ib);
+  uint64_t* sorted = w.ka;
+  if (d.R > 0) {
+    k_derive_keys<<<(unsigned)w.nbh, 256, 0, s>>>(w.rec_origin, d.R, out->root_keys, out->root_vals, d.root - 1u, d.ib,
+                                                  (int32_t)(1 << (d.rb - 1)), ps, w.ka, w.hpart, st);
+    IGC_HIP(hipGetLastError(), "igc_conv_grid: key launch");
+    const int width = ps.passes << ps.bits;
+    k_hist_reduce<<<(width + 15) / 16, 256, 0, s>>>(w.hpart, (int)w.nbh, width, w.hist);
+    IGC_HIP(hipGetLastError(), "igc_conv_grid: histogram reduce launch");
+    if ((rc = radix_sort(w.ka, w.kb, d.R, ps, w.hist, w.cnt, w.off, w.sort_tiles, &st->guard, s, &sorted))) return rc;
+    k_derive_count<<<(unsigned)w.nb, kThreads, 0, s>>>(sorted, d.R, d.ib, w.bcounts);
+    IGC_HIP(hipGetLastError(), "igc_conv_grid: count launch");
+  }
+  k_scan_blocks<<<1, 1024, 0, s>>>(w.bcounts, d.R > 0 ? w.nb : 0, w.bprefix, st, hd);
+  IGC_HIP(hipGetLastError(), "igc_conv_grid: block scan launch");
+  if (d.R > 0) {
+    Topo t{d.F,           d.Lw,          d.U,           &st->guard,      nullptr,
+           out->root_list, out->upper_origin, out->upper_mask, out->upper_first, out->lower_origin, out->lower_mask,
+           out->lower_first, out->leaf,   out->leaf_origin};
+    k_derive_register<<<(unsigned)w.nb, kThreads, 0, s>>>(sorted, d.R, w.bprefix, d.ib, w.rec_origin, w.rec_mask, t,
+                                                          st);
+    IGC_HIP(hipGetLastError(), "igc_conv_grid: register launch");
+  }
+  const uint64_t* dc = st->counts;
+  const int64_t nbl = (d.Lw + 3) / 4;
+  k_node_prefix<<<(unsigned)(nbl + (d.U + 3) / 4), 256, 0, s>>>(out->lower_mask, out->lower_pre, d.Lw, nbl,
+                                                                out->upper_mask, out->upper_pre, d.U, dc);
+  IGC_HIP(hipGetLastError(), "igc_conv_grid: node prefix launch");
+  k_leaf_neighbors<<<grid_for(d.F * 27, 256, 8192), 256, 0, s>>>(out->view(), out->leaf_nbr, dc);
+  IGC_HIP(hipGetLastError(), "igc_conv_grid: leaf neighbour launch");
+  k_leaf_count<<<(unsigned)std::max<int64_t>(w.groups, 1), 256, 0, s>>>(out->leaf, d.F, w.gsum, dc);
+  IGC_HIP(hipGetLastError(), "igc_conv_grid: leaf count launch");
+  k_scan_groups<<<1, 1024, 0, s>>>(w.gsum, std::max<int64_t>(w.groups, 1), st, hd);  // publishes the state
+  IGC_HIP(hipGetLastError(), "igc_conv_grid: leaf scan launch");
+  if (w.groups > 1) {
+    k_leaf_offset<<<(unsigned)w.groups, 256, 0, s>>>(out->leaf, d.F, w.gsum, dc);
+    IGC_HIP(hipGetLastError(), "igc_conv_grid: leaf offset launch");
+  }
+  return IGC_OK;
+}
+
+int bits_for(int64_t n) {  // bits that hold 0 .. n-1 (at least 1)
+  int b = 1;
+  while (b < 63 && (1ll << b) < n) ++b;
+  return b;
+}
+
+}  // namespace
+
+bool derive_supported(const igc_grid* in, const int32_t* stride, int32_t transposed) {
+  const int32_t tr = transposed ? 1 : 0;
+  int64_t tiles = std::max<int64_t>(in->n_upper, 1), S = 1;
+  for (int a = 0; a < 3; ++a) {
+    tiles *= span_blocks(4096, stride[a], tr);
+    S *= span_blocks(8, stride[a], tr);
+  }
+  if (tiles > kSmallSort) return false;
+  const int ib = 64 - 27 - (bits_for(std::max<int64_t>(tiles, 2)) + 1);
+  return in->n_leaf * S < (1ll << ib);
+}
+
+int derive_chain(const igc_grid* in, int n, const int32_t* strides, const int32_t* transposed, hipStream_t s,
+                 igc_grid** outs) {
+  std::vector<DeriveStage> d((size_t)n);
+  auto plan = [&](int k) {  // capacities of stage k from stage k-1's (or the input's)
+    DeriveStage& c = d[(size_t)k];
+    const int32_t* st = strides + 3 * k;
+    c.dv.tr = transposed[k] ? 1 : 0;
+    int S = 1;
+    int64_t tiles = 1;
+    for (int a = 0; a < 3; ++a) {
+      c.dv.s[a] = st[a];
+      c.dv.L[a] = span_blocks(8, st[a], c.dv.tr);
+      S *= c.dv.L[a];
+      tiles *= span_blocks(4096, st[a], c.dv.tr);
+    }
+    if (k == 0) {
+      c.F_in = in->n_leaf;
+      c.Lw_in = in->n_lower;
+      c.U_in = in->n_upper;
+    } else {
+      c.F_in = d[(size_t)k - 1].F;
+      c.Lw_in = d[(size_t)k - 1].Lw;
+      c.U_in = d[(size_t)k - 1].U;
+    }
+    c.R = c.F_in * S;
+    if (!c.exact) {
+      c.F = derive_estimate(c.F_in, 8, st, c.dv.tr, std::max<int64_t>(c.R, 1));
+      c.Lw = std::min(c.F, derive_estimate(c.Lw_in, 128, st, c.dv.tr, std::max<int64_t>(c.R, 1)));
+      c.U = std::min<int64_t>({(int64_t)kSmallSort, std::max<int64_t>(c.U_in, 1) * tiles, c.F});
+      uint32_t root = 64;
+      while ((int64_t)root < 2 * c.U) root <<= 1;
+      c.root = std::max(c.root, root);
+    }
+    c.rb = bits_for(std::max<int64_t>(c.U, 2)) + 1;  // rank < U, one spare bit keeps real keys below ~0
+    c.ib = 64 - 27 - c.rb;
+  };
+  for (int k = 0; k < n; ++k) {
+    plan(k);
+    if (d[(size_t)k].R >= (1ll << d[(size_t)k].ib))
+      return set_error(IGC_ERR_UNSUPPORTED, "igc_conv_grid: too many output-leaf records for one derived grid");
+  }
+  // Device states of every stage (a later stage reads its input's counts from them) and their
+  // pinned read-back copies.
+  struct States {
+    BuildState* p = nullptr;
+    size_t bytes;
+    hipStream_t s;
+    const igc_allocator* a;
+    ~States() {
+      if (p) dev_free(p, bytes, s, a);
+    }
+  } states{nullptr, align_up(sizeof(BuildState) * (size_t)n, 256), s, grid_alloc(outs[0])};
+  {
+    const int rc = dev_alloc((void**)&states.p, states.bytes, s, "igc_conv_grid: chain state", states.a);
+    if (rc) return rc;
+  }
+  BuildState* hd = nullptr;
+  BuildState* h = (BuildState*)host_staging(sizeof(BuildState) * (size_t)n, (void**)&hd);
+  if (!h || !hd) return set_error(IGC_ERR_OOM, "igc_conv_grid: pinned staging buffer");
+
+  int first = 0;
+  for (int attempt = 0; attempt <= 2 * n + 2; ++attempt) {
+    // Output blocks of stages first .. n-1.
+    for (int k = first; k < n; ++k) {
+      igc_grid* g = outs[k];
+      if (g->block) {
+        dev_free(g->block, g->bytes, s, grid_alloc(g));
+        g->block = nullptr;
+        g->bytes = 0;
+      }
+      size_t zero_end = 0;
+      const size_t bytes = derive_topology_bytes(d[(size_t)k], &zero_end);
+      int rc = dev_alloc(&g->block, bytes, s, "igc_conv_grid: topology", grid_alloc(g));
+      if (rc) return rc;
+      g->bytes = bytes;
+      derive_carve(d[(size_t)k], g);
+    }
+    // One workspace for the largest stage (stages run in stream order).
+    size_t ws_bytes = 0;
+    DeriveWs w{};
+    for (int k = first; k < n; ++k) ws_bytes = std::max(ws_bytes, derive_ws_bytes(d[(size_t)k], &w, nullptr));
+    Workspace wsb;
+    int rc = ws_acquire(&wsb, ws_bytes, s, "igc_conv_grid: workspace", grid_alloc(outs[0]));
+    if (rc) return rc;
+    char* base = (char*)wsb.p;
+    for (int k = first; k < n && rc == IGC_OK; ++k) {
+      derive_ws_bytes(d[(size_t)k], &w, base);
+      const igc_grid* src = k == 0 ? in : outs[k - 1];
+      const uint64_t* in_counts = k == 0 ? nullptr : states.p[k - 1].counts;
+      rc = derive_enqueue(src, in_counts, d[(size_t)k], w, outs[k], &states.p[k], hd + k, s);
+    }
+    if (rc == IGC_OK) {
+      const hipError_t e = hipStreamSynchronize(s);  // the chain's one read-back
+      if (e != hipSuccess) rc = hip_status(e, "igc_conv_grid: synchronize");
+    }
+    ws_release(&wsb, s);
+    if (rc) return rc;
+    int bad = -1;
+    for (int k = first; k < n; ++k) {
+      const BuildState& r = h[k];
+      if (r.range) return set_error(IGC_ERR_RANGE, "igc_conv_grid: an output coordinate leaves the int32 range");
+      if (r.n_tiles > (uint32_t)kSmallSort)
+        return set_error(IGC_ERR_UNSUPPORTED, "igc_conv_grid: more than 4096 root tiles in a derived grid");
+      DeriveStage& c = d[(size_t)k];
+      if (!r.overflow && (int64_t)r.n_tiles > c.U) {  // more root tiles than planned: exact count next time
+        c.U = (int64_t)r.n_tiles;
+        c.F = std::max(c.F, c.U);
+        c.Lw = std::max(c.Lw, c.U);
+        while ((int64_t)c.root < 2 * c.U) c.root <<= 1;
+        c.exact = true;
+        bad = k;
+        break;
+      }
+      if (r.overflow) {  // root table too small: the tiles were not all inserted
+        c.root <<= 2;
+        c.U = std::min<int64_t>(kSmallSort, std::max<int64_t>(c.U, (int64_t)r.n_tiles) * 2);
+        bad = k;
+        break;
+      }
+      if (r.cap_over) {
+        c.F = std::max<int64_t>(1, (int64_t)r.counts[1]);
+        c.Lw = std::max<int64_t>(1, (int64_t)r.counts[2]);
+        c.U = std::max<int64_t>(1, (int64_t)r.counts[3]);
+        c.exact = true;
+        bad = k;
+        break;
+      }
+      if (r.guard) return set_error(IGC_ERR_INTERNAL, "igc_conv_grid: device bounds check failed");
+      const int64_t N = (int64_t)r.counts[0], F = (int64_t)r.counts[1], Lw = (int64_t)r.counts[2],
+                    U = (int64_t)r.counts[3];
+      if (F > c.F || Lw > c.Lw || U > c.U || (int64_t)r.n_tiles != U || (F > 0) != (N > 0) || N > 512 * F)
+        return set_error(IGC_ERR_INTERNAL, "igc_conv_grid: inconsistent derived counts");
+    }
+    if (bad < 0) {
+      for (int k = 0; k < n; ++k) {
+        const BuildState& r = h[k];
+        igc_grid* g = outs[k];
+        g->n_voxels = (int64_t)r.counts[0];
+        g->n_leaf = (int64_t)r.counts[1];
+        g->n_lower = (int64_t)r.counts[2];
+        g->n_upper = (int64_t)r.counts[3];
+        g->n_input = k == 0 ? in->n_voxels : outs[k - 1]->n_voxels;
+        g->sort_passes = 0;
+      }
+      return IGC_OK;
+    }
+    // Later stages are planned again from the corrected capacities.
+    for (int k = bad; k < n; ++k) plan(k);
+    for (int k = bad; k < n; ++k)
+      if (d[(size_t)k].R >= (1ll << d[(size_t)k].ib))
+        return set_error(IGC_ERR_UNSUPPORTED, "igc_conv_grid: too many output-leaf records for one derived grid");
+    first = bad;
+  }
+  return set_error(IGC_ERR_CAPACITY, "igc_conv_grid: derived grid capacities still too small after retries");
 }
 
 }  // namespace igc

@@ -109,6 +109,14 @@ uint32_t mixed_dense_rows(int32_t cin);
 
 // Launchers (defined in the .hip files).
 int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g);
+// Output grids of a chain of strided / transposed 3x3x3 convolutions (stage k reads stage
+// k-1's output), built from leaves with the counts on the device and one host synchronisation.
+// strides [n][3]; outs[k] are allocated igc_grid objects (device, stream, allocator set) whose
+// topology this fills. derive_supported: whether one stage over `in` fits the derived build
+// (at most 4096 root tiles, record indices within the sort key).
+bool derive_supported(const igc_grid* in, const int32_t* stride, int32_t transposed);
+int derive_chain(const igc_grid* in, int n, const int32_t* strides, const int32_t* transposed, hipStream_t s,
+                 igc_grid** outs);
 int launch_active_ijk(const igc_grid* g, int32_t* d_out, hipStream_t s);
 int launch_ijk_to_index(const igc_grid* g, const int32_t* d_q, int64_t m, int32_t* d_idx, hipStream_t s);
 int launch_kernel_map(const igc_grid* g, const int32_t* h_offsets, int32_t K, int32_t* d_map, uint32_t* d_nbmask,
