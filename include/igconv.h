@@ -209,6 +209,25 @@ int igc_sparse_conv(const igc_grid* grid, const int32_t* d_map, const void* d_fe
                     int32_t cin, const void* d_w, int32_t cout, void* d_out, int32_t path,
                     igc_stream stream);
 
+/* Loads the per-layer configuration of the gather-GEMM-scatter row order from a text file
+ * (DriveRT, "Kernels selected per GPU": tile sizes, bit orders and offset groups are
+ * configuration values measured per layer on the target GPU; "Measurement and
+ * reproducibility": the selection is stored in a documented file). The plan sorts the output
+ * rows by their 27-bit neighbour mask within spans of consecutive rows and cuts them into tiles
+ * of 256; each tile computes only its group of offsets (those some of its rows have), so wider
+ * spans give smaller offset groups and gather from a wider stretch of rows. One rule per line
+ * ('#' starts a comment, first match wins):
+ *     ggs <cin|*> <cout|*> <occupancy_lo> <occupancy_hi> <span> <natural|class>
+ * matches a layer by channels and the grid's leaf occupancy N / (512 F) in [lo, hi); span is
+ * 256, 1024 or 4096 rows; the key's bit order is natural (offset o at bit o) or class (corner,
+ * then edge, face and centre offsets most significant). A layer no rule matches sorts within
+ * its 256-row tiles in natural order. The table is process-wide, replaced whole by each load
+ * (path NULL clears it), and read by later igc_sparse_conv / _noalloc / _between calls on the
+ * gather-GEMM-scatter path. It changes which offsets a tile visits, not the value of any
+ * output (rows only gain exact zero products). Errors: IGC_ERR_INVALID_ARG for an unreadable
+ * file or a malformed line (the table is then unchanged). */
+int igc_tuning_load(const char* path);
+
 /* igc_sparse_conv for callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation. Same arguments, paths, results and errors
  * as igc_sparse_conv, on the same kernels, but it calls no allocator (not hipMalloc, not the

@@ -16,7 +16,7 @@ from ._lib import IgcError
 
 __all__ = [
     "Grid", "grid_build", "kernel_map", "sparse_conv", "sparse_conv_backward", "conv_grid", "conv_grid_chain", "conv_map",
-    "sparse_conv_between", "standard_offsets", "release_memory", "IgcError",
+    "sparse_conv_between", "standard_offsets", "release_memory", "tuning_load", "IgcError",
     "PATH_AUTO", "PATH_LEAF", "PATH_GGS",
 ]
 
@@ -270,6 +270,12 @@ def conv_grid_chain(grid: Grid, strides, transposed=None, memory: str = "torch")
                                                tr.ctypes.data_as(ctypes.c_void_p), _allocator(memory),
                                                _stream(grid.device), hs))
     return [Grid(ctypes.c_void_p(hs[k]), grid.device) for k in range(n)]
+
+
+def tuning_load(path) -> None:
+    """Replaces the per-layer row-order table of the gather-GEMM-scatter path (igc_tuning_load);
+    None clears it. The package's measured table (igconv_tuning.txt) is loaded with the library."""
+    _lib.check(_lib.load().igc_tuning_load(None if path is None else str(path).encode()))
 
 
 def conv_map(in_grid: Grid, out_grid: Grid, stride=2, transposed: bool = False) -> torch.Tensor:

@@ -6,10 +6,11 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libigconv.so")
+TUNING_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "igconv_tuning.txt")
 
 EXPORTS = (
     "igc_grid_build", "igc_grid_destroy", "igc_grid_info", "igc_release_memory", "igc_grid_active_ijk",
-    "igc_grid_ijk_to_index", "igc_grid_export", "igc_kernel_map", "igc_sparse_conv", "igc_sparse_conv_noalloc",
+    "igc_grid_ijk_to_index", "igc_grid_export", "igc_kernel_map", "igc_sparse_conv", "igc_sparse_conv_noalloc", "igc_tuning_load",
     "igc_sparse_conv_backward", "igc_conv_grid", "igc_conv_grid_chain", "igc_conv_map", "igc_sparse_conv_between", "igc_select_path",
     "igc_last_error",
 )
@@ -73,6 +74,7 @@ def load() -> ctypes.CDLL:
         "igc_kernel_map": [P, P, i32, P, P, P],
         "igc_sparse_conv": [P, P, P, i32, i32, P, i32, P, i32, P],
         "igc_sparse_conv_noalloc": [P, P, P, i32, i32, P, i32, P, i32, P],
+        "igc_tuning_load": [ctypes.c_char_p],
         "igc_sparse_conv_backward": [P, P, P, i32, i32, P, i32, P, P, P, i32, P],
         "igc_conv_grid": [P, P, i32, ctypes.POINTER(Allocator), P, ctypes.POINTER(P)],
         "igc_conv_grid_chain": [P, i32, P, P, ctypes.POINTER(Allocator), P, ctypes.POINTER(P)],
@@ -86,6 +88,9 @@ def load() -> ctypes.CDLL:
         fn.argtypes = args
         fn.restype = ctypes.c_char_p if name == "igc_last_error" else ctypes.c_int
     _lib = lib
+    # The measured per-layer row-order selection shipped with the package (igc_tuning_load).
+    if os.path.exists(TUNING_PATH) and lib.igc_tuning_load(TUNING_PATH.encode()) != 0:
+        raise IgcError(1, lib.igc_last_error().decode(errors="replace"))
     return lib
 
 

@@ -8,13 +8,15 @@
 //
 // gfx950 form, in two kernels:
 //
-// k_ggs_plan, one workgroup per tile of 256 consecutive output rows: each row's 27-bit
-// neighbour mask (bit o set when the kernel map has a neighbour at offset o) is read from the
-// map, the tile's rows are sorted by that mask, and for every offset a 16-bit mask records
-// which 16-row blocks of the sorted tile hold at least one pair. Sorting groups rows with the
-// same neighbour set (DriveRT, "Kernels selected per GPU": rows sorted by their 27-bit
-// neighbour mask give threads uniform work), so the pages' per-offset pair lists padded to 16
-// become "the blocks whose bit is set".
+// k_ggs_plan, one workgroup per span of 256, 1024 or 4096 consecutive output rows: each row's
+// 27-bit neighbour mask (bit o set when the kernel map has a neighbour at offset o) is read
+// from the map, the span's rows are sorted by that mask (in a configurable bit order) and cut
+// into tiles of 256, and for every offset a 16-bit mask records which 16-row blocks of a tile
+// hold at least one pair. Sorting groups rows with the same neighbour set (DriveRT, "Kernels
+// selected per GPU": rows sorted by their 27-bit neighbour mask give threads uniform work), so
+// the pages' per-offset pair lists padded to 16 become "the blocks whose bit is set", and each
+// tile computes only its own group of offsets; span and bit order are chosen per layer
+// (igc_tuning_load).
 //
 // k_conv_ggs_bf16, one workgroup per tile x BN output channels, output-stationary:
 // the fp32 accumulators of the 256 x BN tile stay in registers for the whole reduction, so
@@ -73,63 +75,161 @@ __global__ void k_transpose_w(const uint16_t* __restrict__ w, uint16_t* __restri
   }
 }
 
-// Per tile of 256 rows: perm[tile*256 + p] = output row at sorted position p (-1 past N), and
-// blk[tile*27 + o] bit b = some row at sorted positions [16b, 16b+16) has a neighbour at o.
-// A map entry counts as a neighbour when it lies in [0, n_in). Rows with skip[row] != 0
-// (per-leaf dispatch: another path writes them) count as having none.
-__global__ __launch_bounds__(kBM) void k_ggs_plan(const int32_t* __restrict__ map, int64_t N, int64_t n_in,
-                                                 int32_t* __restrict__ perm, uint16_t* __restrict__ blk,
-                                                 const uint8_t* __restrict__ skip) {
-  __shared__ uint64_t s_key[kBM];
-  __shared__ uint32_t s_part[kBM / 64][kNOff];
+// Row order of the tiles (the plan). Rows are sorted by their 27-bit neighbour mask within
+// spans of SPAN consecutive rows (DriveRT, "Kernels selected per GPU": rows sorted by the mask
+// execute the same work), and the sorted rows are cut into tiles of 256:
+//   perm[q] = output row at sorted position q (-1 past N; positions below n_pos only), and
+//   blk[tile*27 + o] bit b = some row at sorted positions [16b, 16b+16) of the tile has a
+//   neighbour at o.
+// A tile then computes only its own group of offsets (those with a bit in blk), and a wider span
+// makes the groups smaller at the cost of gathering from a wider stretch of rows; the span and
+// the bit order of the key (which offsets are the most significant) are configuration values
+// measured per layer. The key of local row r is (the complemented mask with offset order[i] at
+// bit 26 - i) << log2(SPAN) | r: equal masks stay in row order, rows without neighbours (and
+// the padding past N) sort last. A map entry counts as a neighbour when it lies in [0, n_in).
+// Rows with skip[row] != 0 (per-leaf dispatch: another path writes them) count as having none.
+//
+// One workgroup per span, min(SPAN, 1024) threads, SPAN / threads keys per thread in
+// registers (position q * threads + t): a bitonic network whose compare-exchanges at a stride
+// of at least the thread count stay in registers, below 64 go through wave shuffles, and the
+// rest through LDS.
+struct BitOrder {
+  uint8_t o[kNOff];  // o[i]: offset at key bit 26 - i
+};
+
+template <int SPAN>
+__global__ __launch_bounds__(SPAN < 1024 ? SPAN : 1024) void k_ggs_plan(const int32_t* __restrict__ map, int64_t N,
+                                                                       int64_t n_in, int32_t* __restrict__ perm,
+                                                                       int64_t n_pos, uint16_t* __restrict__ blk,
+                                                                       const uint8_t* __restrict__ skip, BitOrder bo) {
+  constexpr int T = SPAN < 1024 ? SPAN : 1024;
+  constexpr int K = SPAN / T;
+  constexpr int LB = SPAN == 256 ? 8 : SPAN == 1024 ? 10 : 12;
+  constexpr int NT = SPAN / kBM;  // tiles per span
+  static_assert(SPAN == 256 || SPAN == 1024 || SPAN == 4096, "span");
+  __shared__ uint64_t s_x[SPAN];
+  __shared__ uint32_t s_mask[SPAN];
+  __shared__ uint32_t s_blk[NT][kNOff];
   const int t = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * kBM;
-  const int64_t row = r0 + t;
-  uint32_t mask = 0;
-  if (row < N && !(skip && skip[row])) {
-    int32_t v[kNOff];
+  const int lane = lane_id();
+  const int64_t base = (int64_t)blockIdx.x * SPAN;
+  for (int x = t; x < NT * kNOff; x += T) (&s_blk[0][0])[x] = 0u;
+
+  uint64_t key[K];
 #pragma unroll
-    for (int o = 0; o < kNOff; ++o) v[o] = map[(size_t)o * (size_t)N + row];
+  for (int q = 0; q < K; ++q) {
+    const int local = q * T + t;
+    const int64_t row = base + local;
+    uint32_t mask = 0;
+    if (row < N && !(skip && skip[row])) {
+      int32_t v[kNOff];
 #pragma unroll
-    for (int o = 0; o < kNOff; ++o) mask |= ((uint64_t)(int64_t)v[o] < (uint64_t)n_in ? 1u : 0u) << o;
+      for (int o = 0; o < kNOff; ++o) v[o] = map[(size_t)o * (size_t)N + row];
+#pragma unroll
+      for (int o = 0; o < kNOff; ++o) mask |= ((uint64_t)(int64_t)v[o] < (uint64_t)n_in ? 1u : 0u) << o;
+    }
+    s_mask[local] = mask;
+    uint64_t pk = 0;
+#pragma unroll
+    for (int b = 0; b < kNOff; ++b) pk |= (uint64_t)((~mask >> bo.o[b]) & 1u) << (kNOff - 1 - b);
+    key[q] = (pk << LB) | (uint64_t)local;
   }
-  // Ascending on the complemented mask: equal masks adjacent, padding rows (mask 0) last.
-  s_key[t] = ((uint64_t)(~mask & 0x7FFFFFFu) << 8) | (uint64_t)t;
-  __syncthreads();
-  for (int k = 2; k <= kBM; k <<= 1) {
+
+  for (int k = 2; k <= SPAN; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      const int p = t ^ j;
-      if (p > t) {
-        const uint64_t a = s_key[t], b = s_key[p];
-        if ((a > b) == ((t & k) == 0)) {
-          s_key[t] = b;
-          s_key[p] = a;
+      if (j >= T) {  // partner in this thread's registers
+        const int qj = j / T;
+#pragma unroll
+        for (int q = 0; q < K; ++q) {
+          if (q & qj) continue;
+          const bool asc = ((q * T + t) & k) == 0;
+          const uint64_t a = key[q], b = key[q | qj];
+          const bool sw = (a > b) == asc;
+          key[q] = sw ? b : a;
+          key[q | qj] = sw ? a : b;
+        }
+      } else {
+        uint64_t other[K];
+        if (j < 64) {
+#pragma unroll
+          for (int q = 0; q < K; ++q) other[q] = shfl_xor64(key[q], j);
+        } else {
+          __syncthreads();
+#pragma unroll
+          for (int q = 0; q < K; ++q) s_x[q * T + t] = key[q];
+          __syncthreads();
+#pragma unroll
+          for (int q = 0; q < K; ++q) other[q] = s_x[(q * T + t) ^ j];
+        }
+#pragma unroll
+        for (int q = 0; q < K; ++q) {
+          const int p = q * T + t;
+          const bool asc = (p & k) == 0, lower = (p & j) == 0;
+          const uint64_t a = key[q], b = other[q];
+          key[q] = (lower == asc) ? (a < b ? a : b) : (a < b ? b : a);
         }
       }
-      __syncthreads();
     }
   }
-  const uint64_t key = s_key[t];
-  const int64_t src = r0 + (int64_t)(key & 255u);
-  const uint32_t m = ~(uint32_t)(key >> 8) & 0x7FFFFFFu;
-  perm[row] = src < N ? (int32_t)src : -1;
-  const int lane = lane_id(), wave = t >> 6;
-  for (int o = 0; o < kNOff; ++o) {
-    const uint64_t b = __ballot((m >> o) & 1u);
-    if (lane == 0) {
-      uint32_t bits = 0;
+
+  // Sorted position p = q * T + t: its row, and its tile's block bits (a wave holds 64
+  // consecutive positions, four 16-row blocks of one tile).
+  __syncthreads();
 #pragma unroll
-      for (int q = 0; q < 4; ++q) bits |= ((b >> (16 * q)) & 0xFFFFull) ? (1u << q) : 0u;
-      s_part[wave][o] = bits;
+  for (int q = 0; q < K; ++q) {
+    const int p = q * T + t;
+    const int local = (int)(key[q] & (uint64_t)(SPAN - 1));
+    const int64_t row = base + local;
+    if (base + p < n_pos) perm[base + p] = row < N ? (int32_t)row : -1;
+    const uint32_t m = s_mask[local];
+    const int tl = p / kBM, quarter = (p % kBM) / 64;
+    for (int o = 0; o < kNOff; ++o) {
+      const uint64_t bb = __ballot((m >> o) & 1u);
+      if (lane == 0 && bb) {
+        uint32_t bits = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) bits |= ((bb >> (16 * b)) & 0xFFFFull) ? (1u << b) : 0u;
+        atomicOr(&s_blk[tl][o], bits << (4 * quarter));
+      }
     }
   }
   __syncthreads();
-  if (t < kNOff) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int w = 0; w < kBM / 64; ++w) v |= s_part[w][t] << (4 * w);
-    blk[(size_t)blockIdx.x * kNOff + t] = (uint16_t)v;
+  for (int x = t; x < NT * kNOff; x += T) {
+    const int tl = x / kNOff, o = x % kNOff;
+    const int64_t tile = base / kBM + tl;
+    if (tile * kBM < n_pos) blk[(size_t)tile * kNOff + o] = (uint16_t)s_blk[tl][o];
   }
+}
+
+// Natural order (offset o at key bit o) and the class order (corners, then edges, faces and
+// the centre, the rarest neighbours most significant).
+BitOrder bit_order(int which) {
+  BitOrder b{};
+  if (which == 0) {
+    for (int i = 0; i < kNOff; ++i) b.o[i] = (uint8_t)(kNOff - 1 - i);
+    return b;
+  }
+  int n = 0;
+  for (int cls = 3; cls >= 0; --cls)
+    for (int o = 0; o < kNOff; ++o) {
+      const int nz = (o / 9 != 1) + ((o / 3) % 3 != 1) + (o % 3 != 1);
+      if (nz == cls) b.o[n++] = (uint8_t)o;
+    }
+  return b;
+}
+
+hipError_t launch_plan(int span, int order, const int32_t* map, int64_t N, int64_t n_in, int32_t* perm,
+                       uint16_t* blk, const uint8_t* skip, hipStream_t s) {
+  const int64_t n_pos = (N + kBM - 1) / kBM * kBM;
+  if (n_pos == 0) return hipSuccess;
+  const BitOrder bo = bit_order(order);
+  if (span == 4096)
+    k_ggs_plan<4096><<<(unsigned)((N + 4095) / 4096), 1024, 0, s>>>(map, N, n_in, perm, n_pos, blk, skip, bo);
+  else if (span == 1024)
+    k_ggs_plan<1024><<<(unsigned)((N + 1023) / 1024), 1024, 0, s>>>(map, N, n_in, perm, n_pos, blk, skip, bo);
+  else
+    k_ggs_plan<256><<<(unsigned)((N + 255) / 256), 256, 0, s>>>(map, N, n_in, perm, n_pos, blk, skip, bo);
+  return hipGetLastError();
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -426,8 +526,7 @@ int launch_ggs_plan(const int32_t* d_map, int64_t N, int32_t* perm, uint16_t* bl
                     const uint8_t* skip) {
   const int64_t n_tiles = (N + kBM - 1) / kBM;
   if (n_tiles == 0) return IGC_OK;
-  k_ggs_plan<<<(unsigned)n_tiles, kBM, 0, s>>>(d_map, N, N, perm, blk, skip);
-  IGC_HIP(hipGetLastError(), "igc_sparse_conv: plan launch");
+  IGC_HIP(launch_plan(256, 0, d_map, N, N, perm, blk, skip, s), "igc_sparse_conv: plan launch");
   return IGC_OK;
 }
 
@@ -483,8 +582,8 @@ int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats
     e = hipGetLastError();
   }
   if (e == hipSuccess && n_tiles > 0) {
-    k_ggs_plan<<<(unsigned)n_tiles, kBM, 0, s>>>(d_map, N, n_in, perm, blk, skip);
-    e = hipGetLastError();
+    const GgsTuning tu = ggs_tuning(cin, cout, N, g->n_leaf);
+    e = launch_plan(tu.span, tu.order, d_map, N, n_in, perm, blk, skip, s);
   }
   if (e == hipSuccess && n_tiles > 0) {
     const bool k64 = cin % 64 == 0;

@@ -123,6 +123,15 @@ int launch_kernel_map(const igc_grid* g, const int32_t* h_offsets, int32_t K, in
                       hipStream_t s);
 bool leaf_conv_supported(int32_t dtype, int32_t cin, int32_t cout);
 bool ggs_conv_supported(int32_t dtype, int32_t cin, int32_t cout);
+
+// Row order of the gather-GEMM-scatter plan for one layer: rows sorted by neighbour mask within
+// spans of `span` rows (256, 1024 or 4096), key bit order 0 = natural, 1 = class (corners,
+// edges, faces, centre); from the rules igc_tuning_load read (default: 256, natural).
+struct GgsTuning {
+  int span = 256;
+  int order = 0;
+};
+GgsTuning ggs_tuning(int32_t cin, int32_t cout, int64_t n_voxels, int64_t n_leaf);
 // min_count > 0 (bf16 only): leaves with fewer active voxels are skipped (their rows untouched).
 // scratch (may be null): caller-provided device memory of at least leaf_scratch_bytes() used
 // instead of a workspace (nothing is allocated then).

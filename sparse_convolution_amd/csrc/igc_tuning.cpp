@@ -1,0 +1,90 @@
+// Per-layer configuration of the gather-GEMM-scatter row order (DriveRT, "Kernels selected per
+// GPU": tile sizes, bit orders and offset groups are configuration values measured per layer
+// on the target GPU; "Measurement and reproducibility": the selection is stored in a
+// documented file). A rule maps a layer (input / output channels and the grid's leaf
+// occupancy N / (512 F)) to the span over which rows are sorted by their neighbour mask and
+// the bit order of that sort; without a matching rule the span is one tile (256 rows) in
+// natural order.
+//
+// File format (text, one rule per line, '#' starts a comment, first matching rule wins):
+//   ggs <cin|*> <cout|*> <occupancy_lo> <occupancy_hi> <span> <natural|class>
+// with span 256, 1024 or 4096 and lo <= occupancy < hi.
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "igc_host.h"
+
+namespace igc {
+namespace {
+
+struct Rule {
+  int32_t cin = -1, cout = -1;  // -1: any
+  double occ_lo = 0.0, occ_hi = 1e30;
+  GgsTuning tu;
+};
+
+std::mutex g_mu;
+std::vector<Rule> g_rules;
+
+}  // namespace
+
+GgsTuning ggs_tuning(int32_t cin, int32_t cout, int64_t n_voxels, int64_t n_leaf) {
+  const double occ = n_leaf > 0 ? (double)n_voxels / (512.0 * (double)n_leaf) : 0.0;
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (const Rule& r : g_rules)
+    if ((r.cin < 0 || r.cin == cin) && (r.cout < 0 || r.cout == cout) && occ >= r.occ_lo && occ < r.occ_hi) return r.tu;
+  return GgsTuning{};
+}
+
+}  // namespace igc
+
+using namespace igc;
+
+extern "C" int igc_tuning_load(const char* path) {
+  clear_error();
+  if (!path) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_rules.clear();
+    return IGC_OK;
+  }
+  FILE* f = std::fopen(path, "r");
+  if (!f) return set_error(IGC_ERR_INVALID_ARG, std::string("igc_tuning_load: cannot open ") + path);
+  std::vector<Rule> rules;
+  char line[512];
+  int lineno = 0;
+  int rc = IGC_OK;
+  while (std::fgets(line, sizeof line, f)) {
+    ++lineno;
+    if (char* h = std::strchr(line, '#')) *h = '\0';
+    char kind[16], cin[16], cout[16], order[16];
+    double lo = 0, hi = 0;
+    int span = 0;
+    const int n = std::sscanf(line, "%15s %15s %15s %lf %lf %d %15s", kind, cin, cout, &lo, &hi, &span, order);
+    if (n <= 0) continue;  // blank or comment
+    Rule r;
+    const bool order_ok = !std::strcmp(order, "natural") || !std::strcmp(order, "class");
+    if (n != 7 || std::strcmp(kind, "ggs") || !(span == 256 || span == 1024 || span == 4096) || !order_ok ||
+        !(lo <= hi)) {
+      rc = set_error(IGC_ERR_INVALID_ARG, "igc_tuning_load: " + std::string(path) + ":" + std::to_string(lineno) +
+                                              ": expected 'ggs <cin|*> <cout|*> <occ_lo> <occ_hi> <256|1024|4096> "
+                                              "<natural|class>'");
+      break;
+    }
+    r.cin = std::strcmp(cin, "*") ? std::atoi(cin) : -1;
+    r.cout = std::strcmp(cout, "*") ? std::atoi(cout) : -1;
+    r.occ_lo = lo;
+    r.occ_hi = hi;
+    r.tu.span = span;
+    r.tu.order = std::strcmp(order, "class") ? 0 : 1;
+    rules.push_back(r);
+  }
+  std::fclose(f);
+  if (rc != IGC_OK) return rc;
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_rules.swap(rules);
+  return IGC_OK;
+}

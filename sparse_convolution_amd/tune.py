@@ -1,0 +1,99 @@
+"""Selects the gather-GEMM-scatter row order per layer on this GPU and writes the tuning file
+that the library loads (igc_tuning_load; the package loads igconv_tuning.txt beside it).
+
+    python -m sparse_convolution_amd.tune [--workloads lidar band large] [--out PATH]
+
+For every workload (synthetic scenes of the bench, see workloads/) each candidate row order
+(span 256 / 1024 / 4096 rows sorted by neighbour mask, natural or class bit order) is timed on
+the same path that runs in deployment (igc_sparse_conv, gather-GEMM-scatter), after checking
+that its output equals the default order's; the fastest is written as one rule for the layer's
+channels, with the measured times as comments (DriveRT, "Measurement and reproducibility":
+algorithms are selected offline on the target GPU with the deployment path, and the selection
+is stored in a documented file).
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import sys
+import tempfile
+import time
+
+import torch
+
+from . import _lib
+import sparse_convolution_amd as igc
+
+CANDIDATES = [(256, "natural"), (256, "class"), (1024, "natural"), (1024, "class"), (4096, "natural"),
+              (4096, "class")]
+
+
+def _time(fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def tune_workload(name: str, log) -> tuple[str, list]:
+    import workloads
+    wl = workloads.WORKLOADS[name]
+    c = torch.from_numpy(workloads.make_coords(name)).cuda()
+    g = igc.grid_build(c)
+    m = igc.kernel_map(g)
+    f = workloads.make_features_device(g.n_voxels, wl.cin, 3000 + wl.index, "cuda", torch.bfloat16)
+    w = torch.from_numpy(workloads.make_weights(wl.cin, wl.cout, 4000 + wl.index, wl.weight_std)).bfloat16().cuda()
+    occ = g.n_voxels / (512.0 * g.n_leaf)
+    reps = 3 if g.n_voxels > 20_000_000 else 10
+    results = []
+    ref = None
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "rule.txt")
+        for span, order in CANDIDATES:
+            with open(path, "w") as fh:
+                fh.write(f"ggs {wl.cin} {wl.cout} 0 1e30 {span} {order}\n")
+            igc.tuning_load(path)
+            out = torch.empty((g.n_voxels, wl.cout), dtype=torch.bfloat16, device="cuda")
+            ms = _time(lambda: igc.sparse_conv(g, f, w, kmap=m, path="ggs", out=out), reps)
+            if ref is None:
+                ref = out.clone()
+            elif not torch.equal(out.float().abs(), ref.float().abs()):  # signs of exact zeros may differ
+                raise RuntimeError(f"{name}: row order {span} {order} changed the output")
+            results.append((ms, span, order))
+            log(f"[tune] {name} span {span} {order}: {ms:.4f} ms")
+    igc.tuning_load(None)
+    best = min(results)
+    lines = [f"# {name}: {g.n_voxels} voxels, leaf occupancy {occ:.3f}, bf16 {wl.cin} -> {wl.cout}; ms per conv: "
+             + ", ".join(f"{s}/{o} {ms:.3f}" for ms, s, o in results),
+             f"ggs {wl.cin} {wl.cout} 0 1e30 {best[1]} {best[2]}"]
+    return "\n".join(lines), results
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--workloads", nargs="+", default=["lidar", "band", "large"])
+    ap.add_argument("--out", default=_lib.TUNING_PATH)
+    args = ap.parse_args()
+    log = lambda s: (sys.stderr.write(s + "\n"), sys.stderr.flush())
+    _lib.load()
+    igc.tuning_load(None)
+    blocks = [f"# gather-GEMM-scatter row order per layer, selected by python -m sparse_convolution_amd.tune on "
+              f"{torch.cuda.get_device_name(0)} {getattr(torch.cuda.get_device_properties(0), 'gcnArchName', '')} "
+              f"({time.strftime('%Y-%m-%d')})",
+              "# ggs <cin|*> <cout|*> <occupancy_lo> <occupancy_hi> <span 256|1024|4096> <natural|class>"]
+    for name in args.workloads:
+        text, _ = tune_workload(name, log)
+        blocks.append(text)
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(blocks) + "\n")
+    log(f"[tune] wrote {args.out}")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

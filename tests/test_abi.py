@@ -114,3 +114,21 @@ def test_allocator_without_both_functions_is_rejected():
     h = ctypes.c_void_p()
     assert lib.igc_grid_build(None, 0, ctypes.byref(half), None, ctypes.byref(h)) == 1
     assert b"allocator" in lib.igc_last_error()
+
+
+def test_tuning_file_is_parsed_on_the_host(tmp_path):
+    lib = _lib()
+    good = tmp_path / "good.txt"
+    good.write_text("# comment\n\nggs 128 * 0 0.1 4096 class  # lidar-like\nggs * * 0 1e30 256 natural\n")
+    assert lib.igc_tuning_load(str(good).encode()) == 0
+    for bad_line in ("ggs 128 128 0 1 512 class\n", "ggs 128 128 0 1 256 sideways\n", "conv 1 1 0 1 256 natural\n",
+                     "ggs 128 128 0.5 0.1 256 natural\n", "ggs 128 128 0 1\n"):
+        bad = tmp_path / "bad.txt"
+        bad.write_text(bad_line)
+        assert lib.igc_tuning_load(str(bad).encode()) == 1, bad_line
+        assert b"igc_tuning_load" in lib.igc_last_error()
+    assert lib.igc_tuning_load(str(tmp_path / "missing.txt").encode()) == 1
+    assert lib.igc_tuning_load(None) == 0
+    from sparse_convolution_amd import _lib as L
+    if os.path.exists(L.TUNING_PATH):  # the shipped table parses
+        assert lib.igc_tuning_load(L.TUNING_PATH.encode()) == 0

@@ -201,3 +201,46 @@ def test_conv_deterministic():
     a = igc.sparse_conv(g, ft.cuda(), wt.cuda(), kmap=m, path="ggs")
     b = igc.sparse_conv(g, ft.cuda(), wt.cuda(), kmap=m, path="ggs")
     assert torch.equal(a, b)
+
+
+@pytest.fixture
+def _restore_tuning():
+    yield
+    from sparse_convolution_amd import _lib as L
+    import os
+    _igc().tuning_load(L.TUNING_PATH if os.path.exists(L.TUNING_PATH) else None)
+
+
+@pytest.mark.parametrize("span,order", [(256, "class"), (1024, "natural"), (4096, "natural"), (4096, "class")])
+@pytest.mark.parametrize("case", ["lidar", "clusters", "mixed"])
+def test_row_order_rules_keep_outputs(tmp_path, _restore_tuning, span, order, case):
+    # A row-order rule (igc_tuning_load) changes which offsets each tile visits, never an output:
+    # every rule gives the default order's output (up to the sign of exact zeros), and that
+    # output matches the oracle on sampled rows. Spans wider than the grid and ragged last spans
+    # are included (clusters: a few thousand rows).
+    igc = _igc()
+    if case == "lidar":
+        coords, cin, cout, path = workloads.make_coords("lidar"), 128, 128, "ggs"
+    elif case == "clusters":
+        coords, cin, cout, path = _cluster_coords(4, 14, 200, seed=5), 64, 64, "ggs"
+    else:
+        g3 = np.stack(np.meshgrid(*[np.arange(16)] * 3, indexing="ij"), -1).reshape(-1, 3)
+        coords = np.concatenate([_cluster_coords(3, 20, 150, seed=9, fill=0.5), g3 + 600]).astype(np.int32)
+        cin, cout, path = 64, 64, "mixed"
+    say(f"row order {case} span={span} order={order} n_in={coords.shape[0]}")
+    g = igc.grid_build(to_dev(coords))
+    m = igc.kernel_map(g)
+    ft, wt = _inputs(g.n_voxels, cin, cout, torch.bfloat16, 31, 1.0 / np.sqrt(27 * cin))
+    f, w = ft.cuda(), wt.cuda()
+    igc.tuning_load(None)
+    y0 = igc.sparse_conv(g, f, w, kmap=m, path=path)
+    rule = tmp_path / "rule.txt"
+    rule.write_text(f"ggs * * 0 1e30 {span} {order}\n")
+    igc.tuning_load(str(rule))
+    y1 = igc.sparse_conv(g, f, w, kmap=m, path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.float().abs(), y0.float().abs())
+    rows = np.random.default_rng(span).choice(g.n_voxels, size=min(g.n_voxels, 2000), replace=False)
+    mr = oracle.OracleGrid(coords).kernel_map()
+    r = oracle.conv(mr, ft.float().numpy(), wt.float().numpy(), rows=rows)
+    assert normwise_error(y1.float().cpu().numpy()[rows], r) <= TOL[torch.bfloat16]
