@@ -75,6 +75,7 @@ struct BuildState {
   uint64_t off_or, off_and;   // OR / AND over all in-tile offsets
   uint64_t key_or, key_and;   // OR / AND over all tile keys
   uint64_t counts[4];         // N, F, Lw, U from the sorted keys
+  uint64_t n_rec;             // a derived grid's records (input leaves x slots); later kernels stop there
 };
 
 // The build state as the host reads it at a synchronisation: one thread of the last kernel
@@ -121,6 +122,7 @@ __global__ void k_init_root(BuildState* st, uint64_t* __restrict__ keys, int64_t
     st->key_or = 0;
     st->key_and = ~0ull;
     for (int c = 0; c < 4; ++c) st->counts[c] = 0;
+    st->n_rec = 0;
   }
 }
 
@@ -617,7 +619,8 @@ __device__ __forceinline__ void rank_keys(const uint64_t* __restrict__ src, int6
 // one histogram per wave (only the counts are needed here, not the ranks).
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void k_radix_hist(const uint64_t* __restrict__ src, int64_t n, int shift,
-                                                         uint32_t* __restrict__ cnt, int64_t T) {
+                                                         uint32_t* __restrict__ cnt, int64_t T, const uint64_t* dn) {
+  if (dn && (int64_t)*dn < n) n = (int64_t)*dn;
   constexpr int D = 1 << BITS;
   __shared__ uint32_t s_cnt[4][D];
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -661,7 +664,8 @@ template <int BITS, bool STABLE>
 __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint64_t* __restrict__ src,
                                                             uint64_t* __restrict__ dst, int64_t n, int shift,
                                                             const uint32_t* __restrict__ off, int64_t T,
-                                                            uint32_t* guard) {
+                                                            uint32_t* guard, const uint64_t* dn) {
+  if (dn && (int64_t)*dn < n) n = (int64_t)*dn;
   constexpr int D = 1 << BITS, J = D / kThreads;
   __shared__ uint64_t s_keys[kSortTile];
   __shared__ uint32_t s_cnt[4][D];
@@ -731,20 +735,21 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint64_t* __re
 
 template <int BITS>
 void radix_pass(const uint64_t* src, uint64_t* dst, int64_t n, int shift, const uint32_t* hist, uint32_t* cnt,
-                uint32_t* off, int64_t tiles, uint32_t* guard, bool first, hipStream_t s) {
-  k_radix_hist<BITS><<<(unsigned)tiles, kThreads, 0, s>>>(src, n, shift, cnt, tiles);
+                uint32_t* off, int64_t tiles, uint32_t* guard, bool first, hipStream_t s, const uint64_t* dn) {
+  k_radix_hist<BITS><<<(unsigned)tiles, kThreads, 0, s>>>(src, n, shift, cnt, tiles, dn);
   k_radix_scan<<<1u << BITS, kThreads, 0, s>>>(cnt, tiles, hist, off);
   if (first)
-    k_radix_scatter<BITS, false><<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, shift, off, tiles, guard);
+    k_radix_scatter<BITS, false><<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, shift, off, tiles, guard, dn);
   else
-    k_radix_scatter<BITS, true><<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, shift, off, tiles, guard);
+    k_radix_scatter<BITS, true><<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, shift, off, tiles, guard, dn);
 }
 
 // Sorts keys[0..n) (in a, scratch b) over the digits of ps; returns the buffer holding the
 // result. hist holds the digit counts of every pass ([passes][bins]); cnt and off hold
-// kMaxBins * cap_tiles words each. Compacted keys stay compacted.
+// kMaxBins * cap_tiles words each. Compacted keys stay compacted. dn (device, may be null):
+// only keys below *dn are sorted (hist must count exactly those).
 int radix_sort(uint64_t* a, uint64_t* b, int64_t n, PassSpec ps, const uint32_t* hist, uint32_t* cnt, uint32_t* off,
-               int64_t cap_tiles, uint32_t* guard, hipStream_t s, uint64_t** result) {
+               int64_t cap_tiles, uint32_t* guard, hipStream_t s, uint64_t** result, const uint64_t* dn = nullptr) {
   *result = a;
   if (n <= 0 || ps.passes == 0) return IGC_OK;
   const int64_t tiles = (n + kSortTile - 1) / kSortTile;
@@ -755,8 +760,8 @@ int radix_sort(uint64_t* a, uint64_t* b, int64_t n, PassSpec ps, const uint32_t*
   for (int p = 0; p < ps.passes; ++p) {
     const int shift = ps.lo_bit + ps.bits * p;
     const uint32_t* hp = hist + ((size_t)p << ps.bits);
-    if (ps.bits == 8) radix_pass<8>(src, dst, n, shift, hp, cnt, off, tiles, guard, p == 0, s);
-    else radix_pass<9>(src, dst, n, shift, hp, cnt, off, tiles, guard, p == 0, s);
+    if (ps.bits == 8) radix_pass<8>(src, dst, n, shift, hp, cnt, off, tiles, guard, p == 0, s, dn);
+    else radix_pass<9>(src, dst, n, shift, hp, cnt, off, tiles, guard, p == 0, s, dn);
     IGC_HIP(hipGetLastError(), "igc_grid_build: radix pass launch");
     std::swap(src, dst);
   }
@@ -1441,7 +1446,14 @@ struct Derive {
   int32_t L[3];  // output-leaf slots per axis and input leaf
 };
 
-__device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+// floor(a / b) for b in {1, 2, 3, 8}: each case divides by a constant (a multiply, not a
+// 64-bit division routine).
+__device__ __forceinline__ int64_t floor_div(int64_t a, int32_t b) {
+  if (b == 1) return a;
+  if (b == 2) return a >> 1;
+  if (b == 8) return a >> 3;
+  return a >= 0 ? a / 3 : -((-a + 2) / 3);
+}
 
 // Output span [lo, hi] on one axis of the input span [x0, x0 + 7].
 __device__ __forceinline__ void derive_span(int64_t x0, int32_t s, int32_t tr, int64_t* lo, int64_t* hi) {
@@ -1462,9 +1474,10 @@ __device__ __forceinline__ uint32_t related_bits(int32_t c, int32_t l, int32_t s
   for (int d = -1; d <= 1; ++d) {
     int32_t t;
     if (tr) {
-      const int32_t z = c + l - d;  // s (x - x0) when s divides it
-      if (z % s != 0) continue;
-      t = z / s;
+      const int32_t z = c + l - d;  // s (x - x0) when s divides it; |z| < 64
+      const int32_t zq = s == 1 ? z : s == 2 ? (z >> 1) : (int32_t)floor_div(z, 3);
+      if (zq * s != z) continue;
+      t = zq;
     } else {
       t = c + s * l + d;
     }
@@ -1483,10 +1496,11 @@ __global__ __launch_bounds__(256) void k_derive_records(const LeafRec* __restric
                                                         uint64_t* __restrict__ tile_list, BuildState* st) {
   const int S = dv.L[0] * dv.L[1] * dv.L[2];
   const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (w >= F_cap * S) return;
-  const int lane = lane_id();
   int64_t F = F_cap;
   if (in_counts && (int64_t)in_counts[1] < F) F = (int64_t)in_counts[1];
+  if (blockIdx.x == 0 && threadIdx.x == 0) st->n_rec = (uint64_t)(F * S);
+  if (w >= F * S) return;  // records past the input's leaves: later kernels stop at n_rec
+  const int lane = lane_id();
   const int64_t f = w / S;
   const int slot = (int)(w - f * S);
   int4 out_o = make_int4(0, 0, 0, 0);  // .w = 1: the record is not empty
@@ -1565,6 +1579,7 @@ __global__ __launch_bounds__(256) void k_derive_keys(const int4* __restrict__ re
   // A stage already over capacity (its table emptied) only writes empty keys: the rest of its
   // kernels then do no work, and the chain is repeated.
   const bool dead = st->cap_over != 0u;
+  if ((int64_t)st->n_rec < R) R = (int64_t)st->n_rec;
   __syncthreads();
   for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < R; r += (int64_t)gridDim.x * blockDim.x) {
     const int4 o = rec_origin[r];
@@ -1596,85 +1611,82 @@ __device__ __forceinline__ uint64_t derive_flags(uint64_t key, uint64_t prev, bo
          ((uint64_t)((key >> (ib + 27)) != (prev >> (ib + 27))) << 48);
 }
 
-// Step 4a. Per block of 4096 sorted keys, the leaf / lower / upper starts.
+// Step 4a. Per block of 256 sorted keys (one per thread), the leaf / lower / upper starts.
 __global__ __launch_bounds__(256) void k_derive_count(const uint64_t* __restrict__ keys, int64_t n, int ib,
-                                                      uint64_t* __restrict__ block_counts) {
-  __shared__ uint64_t s_keys[kPaddedKeys];
-  __shared__ uint64_t s_prev;
+                                                      uint64_t* __restrict__ block_counts, const BuildState* st) {
   __shared__ uint64_t s_tmp[4];
-  const int64_t base = (int64_t)blockIdx.x * kTileKeys;
-  stage_block(keys, n, base, s_keys, &s_prev);
-  uint64_t c = 0;
-  for (int q = 0; q < kKeysPerThread; ++q) {
-    const int p = threadIdx.x * kKeysPerThread + q;
-    const int64_t e = base + p;
-    if (e < n) c += derive_flags(s_keys[kpad(p)], p ? s_keys[kpad(p - 1)] : s_prev, e == 0, ib);
-  }
+  if ((int64_t)st->n_rec < n) n = (int64_t)st->n_rec;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const uint64_t c = e < n ? derive_flags(keys[e], e > 0 ? keys[e - 1] : 0ull, e == 0, ib) : 0ull;
   uint64_t total;
-  block_excl_scan64<kThreads>(c, s_tmp, &total);
+  block_excl_scan64<256>(c, s_tmp, &total);
   if (threadIdx.x == 0) block_counts[blockIdx.x] = total;
 }
 
-// Step 4b. Registration: node rows from the scanned block counts, nodes written top-down, the
-// records' masks OR-ed into their leaves. Rows past a capacity set cap_over and stop.
+// Step 4b. Registration, one sorted key per thread: node rows from the scanned block counts,
+// nodes written top-down. The records of one output leaf are consecutive; a wave ORs the masks
+// of each run of equal leaves with shuffles, and the first lane of a run ORs them into the leaf.
+// Rows past a capacity set cap_over and write nothing.
 __global__ __launch_bounds__(256) void k_derive_register(const uint64_t* __restrict__ keys, int64_t n,
                                                          const uint64_t* __restrict__ prefix, int ib,
                                                          const int4* __restrict__ rec_origin,
                                                          const uint64_t* __restrict__ rec_mask, Topo t,
                                                          BuildState* st) {
-  __shared__ uint64_t s_keys[kPaddedKeys];
-  __shared__ uint64_t s_prev;
   __shared__ uint64_t s_tmp[4];
-  const int64_t base = (int64_t)blockIdx.x * kTileKeys;
-  stage_block(keys, n, base, s_keys, &s_prev);
-  const int p0 = threadIdx.x * kKeysPerThread;
-  uint64_t c = 0;
-  for (int q = 0; q < kKeysPerThread; ++q) {
-    const int64_t e = base + p0 + q;
-    if (e < n) c += derive_flags(s_keys[kpad(p0 + q)], (p0 + q) ? s_keys[kpad(p0 + q - 1)] : s_prev, e == 0, ib);
-  }
-  const uint64_t excl = block_excl_scan64<kThreads>(c, s_tmp, nullptr);
-  int64_t nf = (int64_t)prefix[blockIdx.x * 4 + 1] + (int64_t)((excl >> 16) & 0xFFFF);
-  int64_t nl = (int64_t)prefix[blockIdx.x * 4 + 2] + (int64_t)((excl >> 32) & 0xFFFF);
-  int64_t nu = (int64_t)prefix[blockIdx.x * 4 + 3] + (int64_t)((excl >> 48) & 0xFFFF);
-  for (int q = 0; q < kKeysPerThread; ++q) {
-    const int64_t e = base + p0 + q;
-    if (e >= n) break;
-    const uint64_t key = s_keys[kpad(p0 + q)];
-    if (key == ~0ull) break;
-    const uint64_t f = derive_flags(key, (p0 + q) ? s_keys[kpad(p0 + q - 1)] : s_prev, e == 0, ib);
-    nf += (int64_t)((f >> 16) & 1);
-    nl += (int64_t)((f >> 32) & 1);
-    nu += (int64_t)((f >> 48) & 1);
-    const int64_t lf = nf - 1, lw = nl - 1, u = nu - 1;
-    if (lf >= t.n_leaf || lw >= t.n_lower || u >= t.n_upper) {
-      atomicOr(&st->cap_over, 1u);
-      break;
-    }
-    const uint64_t r = key & ((1ull << ib) - 1ull);
-    const int4 o = rec_origin[r];
-    const uint32_t ui = (uint32_t)o.x, uj = (uint32_t)o.y, uk = (uint32_t)o.z;
-    if ((f >> 48) & 1) {
-      t.root_list[u] = tile_key(o.x, o.y, o.z);
-      t.upper_origin[u] = make_int4(o.x & ~4095, o.y & ~4095, o.z & ~4095, 0);
-      t.upper_first[u] = (uint32_t)lw;
-    }
-    if ((f >> 32) & 1) {
-      const uint32_t cu = (((ui >> 7) & 31u) << 10) | (((uj >> 7) & 31u) << 5) | ((uk >> 7) & 31u);
-      atomicOr((unsigned long long*)&t.upper_mask[u * 512 + (cu >> 6)], 1ull << (cu & 63u));
-      t.lower_origin[lw] = make_int4(o.x & ~127, o.y & ~127, o.z & ~127, 0);
-      t.lower_first[lw] = (uint32_t)lf;
-    }
-    if ((f >> 16) & 1) {
-      const uint32_t cl = (((ui >> 3) & 15u) << 8) | (((uj >> 3) & 15u) << 4) | ((uk >> 3) & 15u);
-      atomicOr((unsigned long long*)&t.lower_mask[lw * 64 + (cl >> 6)], 1ull << (cl & 63u));
-      t.leaf_origin[lf] = make_int4(o.x, o.y, o.z, 0);
-    }
+  const int lane = lane_id();
+  if ((int64_t)st->n_rec < n) n = (int64_t)st->n_rec;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const uint64_t key = e < n ? keys[e] : ~0ull;
+  const uint64_t prev = e > 0 && e - 1 < n ? keys[e - 1] : 0ull;
+  const uint64_t f = e < n ? derive_flags(key, prev, e == 0, ib) : 0ull;
+  const uint64_t incl = block_excl_scan64<256>(f, s_tmp, nullptr) + f;
+  const int64_t lf = (int64_t)prefix[blockIdx.x * 4 + 1] + (int64_t)((incl >> 16) & 0xFFFF) - 1;
+  const int64_t lw = (int64_t)prefix[blockIdx.x * 4 + 2] + (int64_t)((incl >> 32) & 0xFFFF) - 1;
+  const int64_t u = (int64_t)prefix[blockIdx.x * 4 + 3] + (int64_t)((incl >> 48) & 0xFFFF) - 1;
+  const bool valid = key != ~0ull;
+  const bool fits = valid && lf < t.n_leaf && lw < t.n_lower && u < t.n_upper;
+  if (valid && !fits) atomicOr(&st->cap_over, 1u);
+  const uint64_t r = key & ((1ull << ib) - 1ull);
+  const uint64_t leafkey = key >> ib;
+  // Lanes d ahead hold the same leaf iff their leaf key is equal (runs are contiguous).
+  uint64_t m[8];
+#pragma unroll
+  for (int wd = 0; wd < 8; ++wd) m[wd] = fits ? rec_mask[r * 8 + wd] : 0ull;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t ok = shfl64(leafkey, lane + d < 64 ? lane + d : lane);
+    const bool same = lane + d < 64 && ok == leafkey;
 #pragma unroll
     for (int wd = 0; wd < 8; ++wd) {
-      const uint64_t m = rec_mask[r * 8 + wd];
-      if (m) atomicOr((unsigned long long*)&t.leaf[lf].mask[wd], m);
+      const uint64_t o = shfl64(m[wd], lane + d < 64 ? lane + d : lane);
+      m[wd] |= same ? o : 0ull;
     }
+  }
+  const uint64_t lk_prev = shfl64(leafkey, lane > 0 ? lane - 1 : 0);
+  if (!fits) return;
+  if ((f >> 16) & 1 || lane == 0 || lk_prev != leafkey) {
+#pragma unroll
+    for (int wd = 0; wd < 8; ++wd)
+      if (m[wd]) atomicOr((unsigned long long*)&t.leaf[lf].mask[wd], m[wd]);
+  }
+  if (!(f & 0x0001000100010000ull)) return;
+  const int4 o = rec_origin[r];
+  const uint32_t ui = (uint32_t)o.x, uj = (uint32_t)o.y, uk = (uint32_t)o.z;
+  if ((f >> 48) & 1) {
+    t.root_list[u] = tile_key(o.x, o.y, o.z);
+    t.upper_origin[u] = make_int4(o.x & ~4095, o.y & ~4095, o.z & ~4095, 0);
+    t.upper_first[u] = (uint32_t)lw;
+  }
+  if ((f >> 32) & 1) {
+    const uint32_t cu = (((ui >> 7) & 31u) << 10) | (((uj >> 7) & 31u) << 5) | ((uk >> 7) & 31u);
+    atomicOr((unsigned long long*)&t.upper_mask[u * 512 + (cu >> 6)], 1ull << (cu & 63u));
+    t.lower_origin[lw] = make_int4(o.x & ~127, o.y & ~127, o.z & ~127, 0);
+    t.lower_first[lw] = (uint32_t)lf;
+  }
+  if ((f >> 16) & 1) {
+    const uint32_t cl = (((ui >> 3) & 15u) << 8) | (((uj >> 3) & 15u) << 4) | ((uk >> 3) & 15u);
+    atomicOr((unsigned long long*)&t.lower_mask[lw * 64 + (cl >> 6)], 1ull << (cl & 63u));
+    t.leaf_origin[lf] = make_int4(o.x, o.y, o.z, 0);
   }
 }
 
@@ -1779,7 +1791,7 @@ size_t derive_ws_bytes(const DeriveStage& d, DeriveWs* w, char* base) {
   const int64_t R = std::max<int64_t>(d.R, 1);
   w->sort_tiles = (R + kSortTile - 1) / kSortTile;
   w->nbh = grid_for(R, 256, kHistBlocks);
-  w->nb = (R + kTileKeys - 1) / kTileKeys;
+  w->nb = (R + 255) / 256;
   w->groups = (d.F + kLeafGroup - 1) / kLeafGroup;
   w->rec_origin = (int4*)carve(R * 16);
   w->rec_mask = (uint64_t*)carve(R * 64);
@@ -1827,8 +1839,9 @@ int derive_enqueue(const igc_grid* in, const uint64_t* in_counts, const DeriveSt
     const int width = ps.passes << ps.bits;
     k_hist_reduce<<<(width + 15) / 16, 256, 0, s>>>(w.hpart, (int)w.nbh, width, w.hist);
     IGC_HIP(hipGetLastError(), "igc_conv_grid: histogram reduce launch");
-    if ((rc = radix_sort(w.ka, w.kb, d.R, ps, w.hist, w.cnt, w.off, w.sort_tiles, &st->guard, s, &sorted))) return rc;
-    k_derive_count<<<(unsigned)w.nb, kThreads, 0, s>>>(sorted, d.R, d.ib, w.bcounts);
+    if ((rc = radix_sort(w.ka, w.kb, d.R, ps, w.hist, w.cnt, w.off, w.sort_tiles, &st->guard, s, &sorted, &st->n_rec)))
+      return rc;
+    k_derive_count<<<(unsigned)w.nb, 256, 0, s>>>(sorted, d.R, d.ib, w.bcounts, st);
     IGC_HIP(hipGetLastError(), "igc_conv_grid: count launch");
   }
   k_scan_blocks<<<1, 1024, 0, s>>>(w.bcounts, d.R > 0 ? w.nb : 0, w.bprefix, st, hd);
@@ -1837,7 +1850,7 @@ int derive_enqueue(const igc_grid* in, const uint64_t* in_counts, const DeriveSt
     Topo t{d.F,           d.Lw,          d.U,           &st->guard,      nullptr,
            out->root_list, out->upper_origin, out->upper_mask, out->upper_first, out->lower_origin, out->lower_mask,
            out->lower_first, out->leaf,   out->leaf_origin};
-    k_derive_register<<<(unsigned)w.nb, kThreads, 0, s>>>(sorted, d.R, w.bprefix, d.ib, w.rec_origin, w.rec_mask, t,
+    k_derive_register<<<(unsigned)w.nb, 256, 0, s>>>(sorted, d.R, w.bprefix, d.ib, w.rec_origin, w.rec_mask, t,
                                                           st);
     IGC_HIP(hipGetLastError(), "igc_conv_grid: register launch");
   }
