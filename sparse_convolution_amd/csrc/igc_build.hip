@@ -1486,8 +1486,11 @@ __device__ __forceinline__ uint32_t related_bits(int32_t c, int32_t l, int32_t s
   return m;
 }
 
-// Step 1. Record w = f * S + slot for input leaf f (f below the input's leaf count, read from
-// in_counts[1] when the input is itself a derived grid) and output-leaf slot `slot`.
+// Step 1. One wave per input leaf f (f below the input's leaf count, read from in_counts[1]
+// when the input is itself a derived grid): its mask words are read once (lanes 0..7, then
+// shuffled), and for each of its output-leaf slots that the leaf's output span reaches, the
+// wave computes the slot's 512-bit mask (lane = output row (yi, yj)) into record f * S + slot.
+// Slots out of reach, or whose mask is empty, are records with origin.w = 0.
 __global__ __launch_bounds__(256) void k_derive_records(const LeafRec* __restrict__ leaf,
                                                         const int4* __restrict__ origin, int64_t F_cap,
                                                         const uint64_t* in_counts, Derive dv,
@@ -1495,77 +1498,89 @@ __global__ __launch_bounds__(256) void k_derive_records(const LeafRec* __restric
                                                         uint64_t* __restrict__ root_keys, uint32_t root_mask,
                                                         uint64_t* __restrict__ tile_list, BuildState* st) {
   const int S = dv.L[0] * dv.L[1] * dv.L[2];
-  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t f = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   int64_t F = F_cap;
   if (in_counts && (int64_t)in_counts[1] < F) F = (int64_t)in_counts[1];
   if (blockIdx.x == 0 && threadIdx.x == 0) st->n_rec = (uint64_t)(F * S);
-  if (w >= F * S) return;  // records past the input's leaves: later kernels stop at n_rec
+  if (f >= F) return;  // records past the input's leaves: later kernels stop at n_rec
   const int lane = lane_id();
-  const int64_t f = w / S;
-  const int slot = (int)(w - f * S);
-  int4 out_o = make_int4(0, 0, 0, 0);  // .w = 1: the record is not empty
-  if (f < F) {
-    const int4 o = origin[f];
-    const int64_t x0[3] = {o.x, o.y, o.z};
-    const int q[3] = {slot / (dv.L[1] * dv.L[2]), (slot / dv.L[2]) % dv.L[1], slot % dv.L[2]};
-    int64_t Y[3];
-    bool inside = true, in_range = true;
+  const int4 o = origin[f];
+  const int64_t x0[3] = {o.x, o.y, o.z};
+  const uint64_t my_word = lane < 8 ? leaf[f].mask[lane] : 0ull;
+  uint64_t m8[8];
 #pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      int64_t lo, hi;
-      derive_span(x0[a], dv.s[a], dv.tr, &lo, &hi);
-      Y[a] = floor_div(lo, 8) * 8 + 8 * q[a];
-      if (Y[a] > hi) inside = false;
-      if (Y[a] < (int64_t)INT32_MIN || Y[a] > (int64_t)INT32_MAX - 7) in_range = false;
+  for (int xi = 0; xi < 8; ++xi) m8[xi] = shfl64(my_word, xi);
+  int64_t Y0[3];
+  int n[3];
+  bool in_range[3][4];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    int64_t lo, hi;
+    derive_span(x0[a], dv.s[a], dv.tr, &lo, &hi);
+    Y0[a] = floor_div(lo, 8) * 8;
+    n[a] = (int)((hi - Y0[a]) / 8) + 1;  // output leaves the span reaches (at most L[a])
+    if (n[a] > dv.L[a]) n[a] = dv.L[a];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t y = Y0[a] + 8 * q;
+      in_range[a][q] = y >= (int64_t)INT32_MIN && y <= (int64_t)INT32_MAX - 7;
     }
-    if (inside) {
-      const int l = lane & 7;
-      int32_t c[3];
-#pragma unroll
-      for (int a = 0; a < 3; ++a)
-        c[a] = (int32_t)(dv.tr ? Y[a] - (int64_t)dv.s[a] * x0[a] : (int64_t)dv.s[a] * Y[a] - x0[a]);
-      // Lanes 0..7 hold the relation masks of positions l = 0..7 (every lane computes its l's).
-      const uint32_t ri = related_bits(c[0], l, dv.s[0], dv.tr);
-      const uint32_t rj = related_bits(c[1], l, dv.s[1], dv.tr);
-      const uint32_t rk = related_bits(c[2], l, dv.s[2], dv.tr);
-      const int yi = lane >> 3, yj = lane & 7;
-      const uint32_t mi = (uint32_t)__shfl((int)ri, yi, 64), mj = (uint32_t)__shfl((int)rj, yj, 64);
+  }
+  const int l = lane & 7, yi = lane >> 3, yj = lane & 7;
+  // Slots out of reach stay empty records (lanes 0 .. S-1 write their origins).
+  if (lane < S) {
+    const int qi = lane / (dv.L[1] * dv.L[2]), qj = (lane / dv.L[2]) % dv.L[1], qk = lane % dv.L[2];
+    if (qi >= n[0] || qj >= n[1] || qk >= n[2]) rec_origin[f * S + lane] = make_int4(0, 0, 0, 0);
+  }
+  for (int qi = 0; qi < n[0]; ++qi) {
+    const int32_t ci = (int32_t)(dv.tr ? Y0[0] + 8 * qi - (int64_t)dv.s[0] * x0[0]
+                                       : (int64_t)dv.s[0] * (Y0[0] + 8 * qi) - x0[0]);
+    const uint32_t mi = (uint32_t)__shfl((int)related_bits(ci, l, dv.s[0], dv.tr), yi, 64);
+    for (int qj = 0; qj < n[1]; ++qj) {
+      const int32_t cj = (int32_t)(dv.tr ? Y0[1] + 8 * qj - (int64_t)dv.s[1] * x0[1]
+                                         : (int64_t)dv.s[1] * (Y0[1] + 8 * qj) - x0[1]);
+      const uint32_t mj = (uint32_t)__shfl((int)related_bits(cj, l, dv.s[1], dv.tr), yj, 64);
       uint64_t sel = 0;  // the bytes (input rows xj) related to yj
 #pragma unroll
       for (int xj = 0; xj < 8; ++xj) sel |= ((mj >> xj) & 1u) ? (0xFFull << (8 * xj)) : 0ull;
       uint64_t acc = 0;
 #pragma unroll
-      for (int xi = 0; xi < 8; ++xi) {
-        const uint64_t word = leaf[f].mask[xi];
-        acc |= ((mi >> xi) & 1u) ? (word & sel) : 0ull;
-      }
+      for (int xi = 0; xi < 8; ++xi) acc |= ((mi >> xi) & 1u) ? (m8[xi] & sel) : 0ull;
       acc |= acc >> 32;
       acc |= acc >> 16;
       acc |= acc >> 8;
       const uint32_t b = (uint32_t)acc & 0xFFu;  // input k bits reaching this output row
-      uint32_t r = 0;
+      for (int qk = 0; qk < n[2]; ++qk) {
+        const int32_t ck = (int32_t)(dv.tr ? Y0[2] + 8 * qk - (int64_t)dv.s[2] * x0[2]
+                                           : (int64_t)dv.s[2] * (Y0[2] + 8 * qk) - x0[2]);
+        const uint32_t rk = related_bits(ck, l, dv.s[2], dv.tr);
+        uint32_t r = 0;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) r |= (b & (uint32_t)__shfl((int)rk, t, 64)) ? (1u << t) : 0u;
-      // Mask word yi of the output leaf: bits yj * 8 + k from the 8 lanes of row yi.
-      uint64_t v = (uint64_t)r << (8 * yj);
-      v |= shfl_xor64(v, 1);
-      v |= shfl_xor64(v, 2);
-      v |= shfl_xor64(v, 4);
-      if (__ballot(r != 0u) != 0ull) {
-        if (in_range) {
-          if (yj == 0) rec_mask[w * 8 + yi] = v;
-          if (lane == 0) {
-            out_o = make_int4((int32_t)Y[0], (int32_t)Y[1], (int32_t)Y[2], 1);
-            insert_tile(root_keys, root_mask, root_mask + 1u, tile_key(out_o.x, out_o.y, out_o.z), st, tile_list,
+        for (int t = 0; t < 8; ++t) r |= (b & (uint32_t)__shfl((int)rk, t, 64)) ? (1u << t) : 0u;
+        // Mask word yi of the output leaf: bits yj * 8 + k from the 8 lanes of row yi.
+        uint64_t v = (uint64_t)r << (8 * yj);
+        v |= shfl_xor64(v, 1);
+        v |= shfl_xor64(v, 2);
+        v |= shfl_xor64(v, 4);
+        const int slot = (qi * dv.L[1] + qj) * dv.L[2] + qk;
+        const int64_t w = f * S + slot;
+        const bool any = __ballot(r != 0u) != 0ull;
+        const bool ok = any && in_range[0][qi] && in_range[1][qj] && in_range[2][qk];
+        if (ok && yj == 0) rec_mask[w * 8 + yi] = v;
+        if (lane == 0) {
+          const int4 yo = make_int4((int32_t)(Y0[0] + 8 * qi), (int32_t)(Y0[1] + 8 * qj), (int32_t)(Y0[2] + 8 * qk),
+                                    ok ? 1 : 0);
+          rec_origin[w] = ok ? yo : make_int4(0, 0, 0, 0);
+          if (ok) {
+            insert_tile(root_keys, root_mask, root_mask + 1u, tile_key(yo.x, yo.y, yo.z), st, tile_list,
                         (uint32_t)kSmallSort);
+          } else if (any) {
+            atomicOr(&st->range, 1u);
           }
-        } else if (lane == 0) {
-          atomicOr(&st->range, 1u);
         }
       }
     }
   }
-  if (lane == 0) rec_origin[w] = out_o;
 }
 
 // Step 3. Sort keys of the records and the digit histograms of their sort.
@@ -1821,7 +1836,7 @@ int derive_enqueue(const igc_grid* in, const uint64_t* in_counts, const DeriveSt
   int rc = fill_u64((uint64_t*)out->block, (int64_t)(zero_end / 8), 0ull, s);
   if (rc) return rc;
   if (d.R > 0) {
-    k_derive_records<<<(unsigned)((d.R + 3) / 4), 256, 0, s>>>(in->leaf, in->leaf_origin, d.F_in, in_counts, d.dv,
+    k_derive_records<<<(unsigned)((d.F_in + 3) / 4), 256, 0, s>>>(in->leaf, in->leaf_origin, d.F_in, in_counts, d.dv,
                                                                w.rec_origin, w.rec_mask, out->root_keys,
                                                                d.root - 1u, w.tile_list, st);
     IGC_HIP(hipGetLastError(), "igc_conv_grid: record launch");
