@@ -92,8 +92,10 @@ typedef struct {
   int64_t n_lower;        /* Lw: 128^3 lower internal nodes */
   int64_t n_upper;        /* U: 4096^3 upper internal nodes = root tiles */
   int64_t topology_bytes; /* device bytes held by the grid */
-  int32_t sort_passes;    /* 8-bit digit passes the build's radix sort ran */
+  int32_t sort_passes;    /* digit passes the build's radix sort ran */
   int32_t root_capacity;  /* slots of the root hash table */
+  int32_t host_syncs;     /* host synchronisations the build took (1 unless a capacity was repeated) */
+  int32_t reserved;
 } igc_grid_info_t;
 
 /* Host buffers for igc_grid_export, sized from igc_grid_info_t (U, Lw, F). A null pointer
@@ -131,11 +133,14 @@ typedef struct {
  * tile keys, radix sort of per-tile 64-bit keys, run-length encoding, upper / lower / leaf
  * counts, allocation, top-down registration of nodes and leaf bit masks.
  * Memory: `alloc` (may be NULL, see igc_allocator) provides the grid's block and the build's
- * temporaries. Host synchronisations: three - the root tile count and varying key bits (to plan
- * the sort), the node counts (to size the topology), and the voxel count N (reported by
- * igc_grid_info); none for n_in == 0 (no device work is done then). If the root hash table
- * overflows its first capacity the first step repeats with a larger one (DriveRT, dynamic
- * sizes). Errors: IGC_ERR_INVALID_ARG (out null, d_ijk null with n_in > 0, n_in < 0, an
+ * temporaries. Host synchronisations (DriveRT, "Counts kept on the GPU"): one, at the end
+ * (the counts N, F, Lw, U come back together) for scenes of at most 4096 root tiles. The sort
+ * is planned on the device and the node arrays are sized from the previous build's rows per
+ * coordinate. If an estimate was too small, the build runs once more with the exact counts (two).
+ * A scene with more root tiles falls back to read-backs after the tile pass and after the counts
+ * (four), and grows its root hash table if it overflows (DriveRT, "Compilation and deployment":
+ * dynamic sizes, never truncated). None for n_in == 0 (no device work is done then);
+ * igc_grid_info reports the count. Errors: IGC_ERR_INVALID_ARG (out null, d_ijk null with n_in > 0, n_in < 0, an
  * allocator without both functions), IGC_ERR_RANGE (n_in > 2^31-1), IGC_ERR_OOM (including an
  * allocator returning NULL), IGC_ERR_HIP, IGC_ERR_CAPACITY, IGC_ERR_INTERNAL; every block taken
  * so far is returned on error. On success *out owns one device allocation until

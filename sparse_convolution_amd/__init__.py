@@ -101,6 +101,7 @@ class Grid:
         self.n_upper = info.n_upper
         self.topology_bytes = info.topology_bytes
         self.sort_passes = info.sort_passes
+        self.host_syncs = info.host_syncs
         self.root_capacity = info.root_capacity
 
     def __del__(self):

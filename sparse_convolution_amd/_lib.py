@@ -25,7 +25,8 @@ class GridInfo(ctypes.Structure):
     _fields_ = [
         ("n_input", ctypes.c_int64), ("n_voxels", ctypes.c_int64), ("n_leaf", ctypes.c_int64),
         ("n_lower", ctypes.c_int64), ("n_upper", ctypes.c_int64), ("topology_bytes", ctypes.c_int64),
-        ("sort_passes", ctypes.c_int32), ("root_capacity", ctypes.c_int32),
+        ("sort_passes", ctypes.c_int32), ("root_capacity", ctypes.c_int32), ("host_syncs", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

@@ -315,6 +315,8 @@ int igc_grid_info(const igc_grid* g, igc_grid_info_t* out) {
   out->topology_bytes = (int64_t)g->bytes;
   out->sort_passes = g->sort_passes;
   out->root_capacity = (int32_t)g->root_cap;
+  out->host_syncs = g->host_syncs;
+  out->reserved = 0;
   return IGC_OK;
 }
 

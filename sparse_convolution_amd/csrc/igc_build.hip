@@ -42,7 +42,9 @@
 
 #include <algorithm>
 #include <cstdlib>
+#include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "igc_host.h"
@@ -71,7 +73,9 @@ struct BuildState {
   uint32_t tile_list_count;   // compaction cursor
   uint32_t guard;             // a device-side bounds check failed (the build is rejected)
   uint32_t range;             // a derived grid's coordinate left the int32 range
-  uint32_t cap_over;          // a derived grid outgrew a node capacity (the chain is repeated)
+  uint32_t cap_over;          // node arrays sized from an estimate were too small (the build is repeated)
+  uint32_t sort_passes;       // radix passes the counted build's plan chose
+  uint32_t sort_span;         // bits those passes cover
   uint64_t off_or, off_and;   // OR / AND over all in-tile offsets
   uint64_t key_or, key_and;   // OR / AND over all tile keys
   uint64_t counts[4];         // N, F, Lw, U from the sorted keys
@@ -117,6 +121,7 @@ __global__ void k_init_root(BuildState* st, uint64_t* __restrict__ keys, int64_t
     st->guard = 0;
     st->range = 0;
     st->cap_over = 0;
+    st->sort_passes = 0;
     st->off_or = 0;
     st->off_and = ~0ull;
     st->key_or = 0;
@@ -456,6 +461,114 @@ __device__ __forceinline__ uint64_t runs_expand(uint64_t sk, const BitRuns& r) {
   return (x << 9) | (sk & 511u);
 }
 
+// Digits over the varying bits at or above min_bit: as few passes as digits of up to
+// kMaxDigitBits allow, each digit as narrow as that pass count allows (at least 8 bits).
+__host__ __device__ PassSpec pass_spec(uint64_t varying, int min_bit = 0) {
+  PassSpec ps{0, 0, 8};
+  if (min_bit > 0) varying &= ~((1ull << min_bit) - 1ull);
+  if (!varying) return ps;
+  const int lo = __builtin_ctzll(varying);
+  const int hi = 63 - __builtin_clzll(varying);
+  const int span = hi - lo + 1;
+  ps.lo_bit = lo;
+  ps.passes = (span + kMaxDigitBits - 1) / kMaxDigitBits;
+  ps.bits = (span + ps.passes - 1) / ps.passes;
+  if (ps.bits < 8) ps.bits = 8;
+  // The key pass keeps passes * bins counters in LDS (at most kHistWidth).
+  while ((ps.passes << ps.bits) > kHistWidth) {
+    ++ps.passes;
+    ps.bits = (span + ps.passes - 1) / ps.passes;
+    if (ps.bits < 8) ps.bits = 8;
+  }
+  return ps;
+}
+
+// The shifts that leave a key's leaf / lower / upper part: 9 / 21 / 36 for whole keys, the
+// compacted positions of those boundaries for compacted ones.
+struct KeyForm {
+  int cs_lower, cs_upper;
+  BitRuns runs;  // runs.n > 0: keys are compacted
+};
+
+// How the keys of one build are sorted, from the OR / AND of the in-tile offsets and the tile
+// count U: the leaf part of key2 (rank << 27 | upper child << 12 | lower child) is compacted to
+// its varying bits when they form at most 16 runs, and only the digits over those bits are
+// sorted. digit_bits > 0: digits of exactly that width (the counted build, whose passes are
+// launched before the plan is known and skip themselves past `passes`).
+struct SortPlan {
+  KeyForm kf;
+  PassSpec ps;
+  int32_t span;  // sorted key bits (0: nothing to sort)
+  int32_t shift[kMaxPasses];  // bit of pass p's digit, -1 past the last pass
+};
+
+__host__ __device__ inline SortPlan make_sort_plan(uint64_t off_or, uint64_t off_and, uint64_t U, int digit_bits) {
+  SortPlan pl{};
+  int rank_bits = 0;
+  while (rank_bits < 27 && (1ull << rank_bits) < U) ++rank_bits;
+  const uint64_t varying = (off_or ^ off_and) | (rank_bits ? (((1ull << rank_bits) - 1ull) << 36) : 0ull);
+  BitRuns runs{};
+  const uint64_t leaf_var = varying >> 9;
+  if (leaf_var) {
+    int pos = 0;
+    for (int b = 0; b < 55 && runs.n <= 16;) {
+      if (!((leaf_var >> b) & 1ull)) {
+        ++b;
+        continue;
+      }
+      int e = b;
+      while (e < 55 && ((leaf_var >> e) & 1ull)) ++e;
+      if (runs.n == 16) {
+        runs.n = 17;
+        break;
+      }
+      runs.lo[runs.n] = (uint8_t)b;
+      runs.len[runs.n] = (uint8_t)(e - b);
+      runs.pos[runs.n] = (uint8_t)pos;
+      ++runs.n;
+      pos += e - b;
+      b = e;
+    }
+    if (runs.n > 16 || (runs.n == 1 && runs.lo[0] == 0)) runs.n = 0;  // too fragmented, or already compact
+    else runs.cbits = (off_and >> 9) & ~leaf_var;
+  }
+  const uint64_t sort_var = runs.n ? (((1ull << __builtin_popcountll(leaf_var)) - 1ull) << 9) : varying;
+  PassSpec ps = pass_spec(sort_var, 9);
+  if (ps.passes > 0) {
+    const int lo = ps.lo_bit, hi = 63 - __builtin_clzll(sort_var & ~((1ull << 9) - 1ull));
+    pl.span = hi - lo + 1;
+    if (digit_bits > 0) {
+      ps.bits = digit_bits;
+      ps.passes = (pl.span + digit_bits - 1) / digit_bits;
+    }
+  }
+  if (ps.passes == 0) runs.n = 0;
+  pl.kf.cs_lower = 21;
+  pl.kf.cs_upper = 36;
+  pl.kf.runs = runs;
+  if (runs.n) {
+    pl.kf.cs_lower = 9 + __builtin_popcountll(leaf_var & 0xFFFull);
+    pl.kf.cs_upper = 9 + __builtin_popcountll(leaf_var & ((1ull << 27) - 1ull));
+  }
+  pl.ps = ps;
+  for (int p = 0; p < kMaxPasses; ++p) pl.shift[p] = p < ps.passes ? ps.lo_bit + ps.bits * p : -1;
+  return pl;
+}
+
+// The counted build sorts with digits of 8 or 9 bits, chosen on the host before the key span is
+// known (5 passes cover the <= 12 rank and 27 leaf-part bits of up to 4096 tiles either way).
+constexpr int kCountedPasses = 5;
+
+// The counted build's plan, from the tile pass's state (one thread).
+__global__ void k_make_plan(BuildState* st, SortPlan* plan, int digit_bits) {
+  if (threadIdx.x != 0) return;
+  const uint64_t U = st->n_tiles <= (uint32_t)kSmallSort ? st->n_tiles : 1u;
+  const SortPlan pl = make_sort_plan(st->off_or, st->off_and, U, digit_bits);
+  *plan = pl;
+  st->sort_passes = (uint32_t)pl.ps.passes;
+  st->sort_span = (uint32_t)pl.span;
+}
+
 // LDS histograms of every pass digit (one copy per workgroup), merged into the global ones.
 __device__ __forceinline__ void hist_add(uint32_t* s_hist, uint64_t key, PassSpec ps) {
   const uint32_t bins = 1u << ps.bits;
@@ -466,9 +579,9 @@ __device__ __forceinline__ void hist_add(uint32_t* s_hist, uint64_t key, PassSpe
 }
 
 // Writes this workgroup's histograms to its row of `part` ([blocks][passes * bins]).
-__device__ __forceinline__ void hist_flush(const uint32_t* s_hist, uint32_t* part, PassSpec ps) {
+__device__ __forceinline__ void hist_flush(const uint32_t* s_hist, uint32_t* part, PassSpec ps, int width = 0) {
   __syncthreads();
-  const int width = ps.passes << ps.bits;
+  if (width <= 0) width = ps.passes << ps.bits;
   uint32_t* row = part + (size_t)blockIdx.x * width;
   for (int x = threadIdx.x; x < width; x += blockDim.x) row[x] = s_hist[x];
 }
@@ -511,10 +624,24 @@ __global__ __launch_bounds__(256) void k_key2(const int32_t* __restrict__ ijk, i
                                               const int32_t* __restrict__ root_vals, uint32_t mask,
                                               const uint64_t* __restrict__ tiles, int64_t U,
                                               uint64_t* __restrict__ out, PassSpec ps, BitRuns runs,
-                                              uint32_t* __restrict__ hist, BuildState* st) {
+                                              uint32_t* __restrict__ hist, BuildState* st,
+                                              const SortPlan* plan = nullptr, int hist_width = 0,
+                                              uint64_t* __restrict__ out_odd = nullptr) {
   __shared__ uint32_t s_hist[kHistWidth];
   __shared__ uint64_t s_tiles[kRootInLds];
-  for (int x = threadIdx.x; x < (ps.passes << ps.bits); x += blockDim.x) s_hist[x] = 0;
+  // Counted build: the plan, the tile count and the output buffer come from the device (keys go
+  // where the first radix pass reads them); a build whose tile step failed writes zero keys.
+  bool dead = false;
+  if (plan) {
+    ps = plan->ps;
+    runs = plan->kf.runs;
+    U = (int64_t)st->n_tiles;
+    dead = st->cap_over != 0u || st->overflow != 0u || U > kSmallSort;
+    if (dead) U = 0;
+    if (ps.passes & 1) out = out_odd;
+  }
+  const int width = hist_width > 0 ? hist_width : (ps.passes << ps.bits);
+  for (int x = threadIdx.x; x < width; x += blockDim.x) s_hist[x] = 0;
   const bool local = U <= kRootInLds;
   if (local)
     for (int x = threadIdx.x; x < U; x += blockDim.x) s_tiles[x] = tiles[x];
@@ -538,6 +665,11 @@ __global__ __launch_bounds__(256) void k_key2(const int32_t* __restrict__ ijk, i
     const int32_t i = ci[u], j = cj[u], k = ck[u];
     const uint64_t tk = tile_key(i, j, k);
     uint64_t rank = 0;
+    if (dead) {
+      out[e] = 0ull;
+      hist_add(s_hist, 0ull, ps);
+      continue;
+    }
     if (local) {
       int lo = 0, hi = (int)U - 1;  // s_tiles is ascending and holds tk
       while (lo < hi) {
@@ -555,7 +687,7 @@ __global__ __launch_bounds__(256) void k_key2(const int32_t* __restrict__ ijk, i
     hist_add(s_hist, key, ps);
    }
   }
-  hist_flush(s_hist, hist, ps);
+  hist_flush(s_hist, hist, ps, width);
 }
 
 // Digit histograms of an existing key array (used for the tile-key sort when U is large).
@@ -619,8 +751,14 @@ __device__ __forceinline__ void rank_keys(const uint64_t* __restrict__ src, int6
 // one histogram per wave (only the counts are needed here, not the ranks).
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void k_radix_hist(const uint64_t* __restrict__ src, int64_t n, int shift,
-                                                         uint32_t* __restrict__ cnt, int64_t T, const uint64_t* dn) {
+                                                         uint32_t* __restrict__ cnt, int64_t T, const uint64_t* dn,
+                                                         const SortPlan* plan, int pass, const uint64_t* alt) {
   if (dn && (int64_t)*dn < n) n = (int64_t)*dn;
+  if (plan) {  // counted build: pass `pass` of plan->ps.passes reads buffer (passes - pass) & 1
+    if (pass >= plan->ps.passes) return;
+    shift = plan->shift[pass];
+    if ((plan->ps.passes - pass) & 1) src = alt;
+  }
   constexpr int D = 1 << BITS;
   __shared__ uint32_t s_cnt[4][D];
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -641,7 +779,9 @@ __global__ __launch_bounds__(kThreads) void k_radix_hist(const uint64_t* __restr
 // Step 2, one workgroup per digit d: off[d * T + t] = (keys whose digit is below d) +
 // (keys with digit d in tiles before t). hist holds the pass's digit counts over all keys.
 __global__ __launch_bounds__(kThreads) void k_radix_scan(const uint32_t* __restrict__ cnt, int64_t T,
-                                                         const uint32_t* __restrict__ hist, uint32_t* __restrict__ off) {
+                                                         const uint32_t* __restrict__ hist, uint32_t* __restrict__ off,
+                                                         const SortPlan* plan, int pass) {
+  if (plan && pass >= plan->ps.passes) return;
   __shared__ uint64_t s_tmp[kThreads / 64];
   const int d = blockIdx.x, tid = threadIdx.x;
   uint64_t below = 0;
@@ -664,8 +804,18 @@ template <int BITS, bool STABLE>
 __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint64_t* __restrict__ src,
                                                             uint64_t* __restrict__ dst, int64_t n, int shift,
                                                             const uint32_t* __restrict__ off, int64_t T,
-                                                            uint32_t* guard, const uint64_t* dn) {
+                                                            uint32_t* guard, const uint64_t* dn,
+                                                            const SortPlan* plan, int pass) {
   if (dn && (int64_t)*dn < n) n = (int64_t)*dn;
+  if (plan) {
+    if (pass >= plan->ps.passes) return;
+    shift = plan->shift[pass];
+    if ((plan->ps.passes - pass) & 1) {
+      uint64_t* t = (uint64_t*)src;
+      src = dst;
+      dst = t;
+    }
+  }
   constexpr int D = 1 << BITS, J = D / kThreads;
   __shared__ uint64_t s_keys[kSortTile];
   __shared__ uint32_t s_cnt[4][D];
@@ -735,13 +885,16 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint64_t* __re
 
 template <int BITS>
 void radix_pass(const uint64_t* src, uint64_t* dst, int64_t n, int shift, const uint32_t* hist, uint32_t* cnt,
-                uint32_t* off, int64_t tiles, uint32_t* guard, bool first, hipStream_t s, const uint64_t* dn) {
-  k_radix_hist<BITS><<<(unsigned)tiles, kThreads, 0, s>>>(src, n, shift, cnt, tiles, dn);
-  k_radix_scan<<<1u << BITS, kThreads, 0, s>>>(cnt, tiles, hist, off);
+                uint32_t* off, int64_t tiles, uint32_t* guard, bool first, hipStream_t s, const uint64_t* dn,
+                const SortPlan* plan = nullptr, int pass = 0) {
+  k_radix_hist<BITS><<<(unsigned)tiles, kThreads, 0, s>>>(src, n, shift, cnt, tiles, dn, plan, pass, dst);
+  k_radix_scan<<<1u << BITS, kThreads, 0, s>>>(cnt, tiles, hist, off, plan, pass);
   if (first)
-    k_radix_scatter<BITS, false><<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, shift, off, tiles, guard, dn);
+    k_radix_scatter<BITS, false><<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, shift, off, tiles, guard, dn, plan,
+                                                                      pass);
   else
-    k_radix_scatter<BITS, true><<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, shift, off, tiles, guard, dn);
+    k_radix_scatter<BITS, true><<<(unsigned)tiles, kThreads, 0, s>>>(src, dst, n, shift, off, tiles, guard, dn, plan,
+                                                                     pass);
 }
 
 // Sorts keys[0..n) (in a, scratch b) over the digits of ps; returns the buffer holding the
@@ -769,43 +922,14 @@ int radix_sort(uint64_t* a, uint64_t* b, int64_t n, PassSpec ps, const uint32_t*
   return IGC_OK;
 }
 
-// Digits over the varying bits at or above min_bit: as few passes as digits of up to
-// kMaxDigitBits allow, each digit as narrow as that pass count allows (at least 8 bits).
-PassSpec pass_spec(uint64_t varying, int min_bit = 0) {
-  PassSpec ps{0, 0, 8};
-  if (min_bit > 0) varying &= ~((1ull << min_bit) - 1ull);
-  if (!varying) return ps;
-  const int lo = __builtin_ctzll(varying);
-  const int hi = 63 - __builtin_clzll(varying);
-  const int span = hi - lo + 1;
-  ps.lo_bit = lo;
-  ps.passes = (span + kMaxDigitBits - 1) / kMaxDigitBits;
-  ps.bits = (span + ps.passes - 1) / ps.passes;
-  if (ps.bits < 8) ps.bits = 8;
-  // The key pass keeps passes * bins counters in LDS (at most kHistWidth).
-  while ((ps.passes << ps.bits) > kHistWidth) {
-    ++ps.passes;
-    ps.bits = (span + ps.passes - 1) / ps.passes;
-    if (ps.bits < 8) ps.bits = 8;
-  }
-  return ps;
-}
-
 // ------------------------------------------------------------------------------ counting
 
-// Block b counts, among keys [b*4096, (b+1)*4096), those that start a new leaf, lower node
-// and upper node. Counts are packed in 16-bit fields 1..3 of one 64-bit word (field 0, the
-// voxels, is counted from the leaf masks after registration).
-// The shifts that leave a key's leaf / lower / upper part: 9 / 21 / 36 for whole keys, the
-// compacted positions of those boundaries for compacted ones.
-struct KeyForm {
-  int cs_lower, cs_upper;
-  BitRuns runs;  // runs.n > 0: keys are compacted
-};
-
+// Block b counts, among keys [b*4096, (b+1)*4096), those that start a new voxel, leaf, lower
+// node and upper node, packed in the 16-bit fields 0..3 of one 64-bit word (duplicate
+// coordinates have equal keys, so voxel starts count the unique voxels).
 __device__ __forceinline__ uint64_t start_flags(uint64_t key, uint64_t prev, bool first, int cs_lower, int cs_upper) {
-  if (first) return 0x0001000100010000ull;
-  return ((uint64_t)((key >> 9) != (prev >> 9)) << 16) |
+  if (first) return 0x0001000100010001ull;
+  return (uint64_t)(key != prev) | ((uint64_t)((key >> 9) != (prev >> 9)) << 16) |
          ((uint64_t)((key >> cs_lower) != (prev >> cs_lower)) << 32) |
          ((uint64_t)((key >> cs_upper) != (prev >> cs_upper)) << 48);
 }
@@ -831,9 +955,14 @@ __device__ __forceinline__ void stage_block(const uint64_t* __restrict__ keys, i
 }
 
 __global__ __launch_bounds__(256) void k_count(const uint64_t* __restrict__ keys, int64_t n,
-                                               uint64_t* __restrict__ block_counts, int cs_lower, int cs_upper) {
+                                               uint64_t* __restrict__ block_counts, int cs_lower, int cs_upper,
+                                               const SortPlan* plan = nullptr) {
   __shared__ uint64_t s_keys[kPaddedKeys];
   __shared__ uint64_t s_prev;
+  if (plan) {
+    cs_lower = plan->kf.cs_lower;
+    cs_upper = plan->kf.cs_upper;
+  }
   __shared__ uint64_t s_tmp[4];
   const int64_t base = (int64_t)blockIdx.x * kTileKeys;
   stage_block(keys, n, base, s_keys, &s_prev);
@@ -848,8 +977,8 @@ __global__ __launch_bounds__(256) void k_count(const uint64_t* __restrict__ keys
   if (threadIdx.x == 0) block_counts[blockIdx.x] = total;
 }
 
-// Exclusive scan of the per-block packed counts into 64-bit prefixes per block (fields 1..3
-// of four), and the totals F, Lw, U. One workgroup.
+// Exclusive scan of the per-block packed counts into 64-bit prefixes per block, and the totals
+// N, F, Lw, U. One workgroup.
 __global__ __launch_bounds__(1024) void k_scan_blocks(const uint64_t* __restrict__ block_counts, int64_t nb,
                                                       uint64_t* __restrict__ prefix, BuildState* st,
                                                       BuildState* host) {
@@ -858,16 +987,16 @@ __global__ __launch_bounds__(1024) void k_scan_blocks(const uint64_t* __restrict
   const int64_t b0 = threadIdx.x * per;
   uint64_t run[4] = {0, 0, 0, 0};
   for (int64_t b = b0; b < b0 + per && b < nb; ++b)
-    for (int c = 1; c < 4; ++c) run[c] += (block_counts[b] >> (16 * c)) & 0xFFFFull;
+    for (int c = 0; c < 4; ++c) run[c] += (block_counts[b] >> (16 * c)) & 0xFFFFull;
   uint64_t excl[4] = {0, 0, 0, 0}, tot[4] = {0, 0, 0, 0};
-  for (int c = 1; c < 4; ++c) excl[c] = block_excl_scan64<1024>(run[c], s_tmp, &tot[c]);
+  for (int c = 0; c < 4; ++c) excl[c] = block_excl_scan64<1024>(run[c], s_tmp, &tot[c]);
   for (int64_t b = b0; b < b0 + per && b < nb; ++b)
     for (int c = 0; c < 4; ++c) {
       prefix[b * 4 + c] = excl[c];
       excl[c] += (block_counts[b] >> (16 * c)) & 0xFFFFull;
     }
   if (threadIdx.x == 0) {
-    for (int c = 1; c < 4; ++c) st->counts[c] = tot[c];
+    for (int c = 0; c < 4; ++c) st->counts[c] = tot[c];
     publish_state(st, host);
   }
 }
@@ -877,6 +1006,7 @@ __global__ __launch_bounds__(1024) void k_scan_blocks(const uint64_t* __restrict
 struct Topo {
   int64_t n_leaf, n_lower, n_upper;  // allocation sizes (bounds checks)
   uint32_t* guard;
+  uint32_t* cap_over;  // a row past an allocation size (sizes from an estimate: the build is repeated)
   const uint64_t* tiles;  // [U] tile keys in rank order
   uint64_t* root_list;
   int4* upper_origin;
@@ -904,7 +1034,9 @@ __device__ __forceinline__ int4 key_origin(uint64_t key, uint64_t tile, uint32_t
 constexpr int kLeafCache = 64;  // leaves of a block whose masks are merged in LDS
 
 __global__ __launch_bounds__(256) void k_register(const uint64_t* __restrict__ keys, int64_t n,
-                                                  const uint64_t* __restrict__ prefix, Topo t, const KeyForm kf) {
+                                                  const uint64_t* __restrict__ prefix, Topo t, KeyForm kf,
+                                                  const SortPlan* plan = nullptr) {
+  if (plan) kf = plan->kf;
   __shared__ uint64_t s_keys[kPaddedKeys];
   __shared__ uint64_t s_prev;
   __shared__ uint64_t s_tmp[4];
@@ -944,14 +1076,18 @@ __global__ __launch_bounds__(256) void k_register(const uint64_t* __restrict__ k
     nl += (int64_t)((f >> 32) & 1);
     nu += (int64_t)((f >> 48) & 1);
     const int64_t lf = nf - 1, lw = nl - 1, u = nu - 1;
-    if (lf < lf0 || lf >= t.n_leaf || lw >= t.n_lower || u >= t.n_upper) {
+    if (lf < lf0) {
       atomicOr(t.guard, 1u);
       break;
     }
-    if (f) {  // a key that starts a leaf (and maybe its lower / upper node): expanded, and the tile read, only here
+    if (lf >= t.n_leaf || lw >= t.n_lower || u >= t.n_upper) {
+      atomicOr(t.cap_over, 1u);
+      break;
+    }
+    if (f & 0x0001000100010000ull) {  // starts a leaf (and maybe its lower / upper node): expanded, tile read, only here
       const uint64_t key = kf.runs.n ? runs_expand(s_keys[kpad(p0 + q)], kf.runs) : s_keys[kpad(p0 + q)];
       if ((int64_t)(key >> 36) >= t.n_upper) {
-        atomicOr(t.guard, 1u);
+        atomicOr(t.cap_over, 1u);
         break;
       }
       const uint64_t tile = t.tiles[key >> 36];
@@ -993,8 +1129,12 @@ __global__ __launch_bounds__(256) void k_register(const uint64_t* __restrict__ k
   for (int x = threadIdx.x; x < nloc * 8; x += kThreads) {
     const int slot = x >> 3, w = x & 7;
     const int64_t lf = lf0 + slot;
-    if (lf < 0 || lf >= t.n_leaf) {
+    if (lf < 0) {
       atomicOr(t.guard, 1u);
+      continue;
+    }
+    if (lf >= t.n_leaf) {
+      atomicOr(t.cap_over, 1u);
       continue;
     }
     const uint64_t v = s_lmask[slot][w];
@@ -1164,17 +1304,9 @@ struct Arena {
 constexpr int kHistBlocks = 1024;  // workgroups of the key / histogram passes
 constexpr int kTileBlocks = 2048;  // workgroups of the tile pass
 
-int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
-  g->n_input = n_in;
-  if (n_in == 0) {
-    // No device work. A grid built with an allocator still owns one (minimal) block from it.
-    if (grid_alloc(g)) {
-      const int rc = dev_alloc(&g->block, 256, s, "igc_grid_build: topology", grid_alloc(g));
-      if (rc) return rc;
-      g->bytes = 256;
-    }
-    return IGC_OK;
-  }
+// The build with a host read-back after the tile pass (the tile count and key bits choose the
+// sort) and after the counts (they size the topology): any number of root tiles.
+int build_grid_synced(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
 
   // Root table (keys, then upper-node rows): first capacity from an estimate, then the size
   // that always suffices (U <= n_in) - the capacity retry. It is built in the workspace and
@@ -1274,36 +1406,10 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   }
 
   // key2, its histograms and its sort over the varying bit span.
-  int rank_bits = 0;
-  while ((1ll << rank_bits) < U) ++rank_bits;
-  const uint64_t varying = off_var | (rank_bits ? (((1ull << rank_bits) - 1ull) << 36) : 0ull);
-  // Sort on the leaf part of key2 only, compacted to its varying bits.
-  BitRuns runs{};
-  const uint64_t leaf_var = varying >> 9;
-  if (leaf_var) {
-    int pos = 0;
-    for (int b = 0; b < 55 && runs.n <= 16;) {
-      if (!((leaf_var >> b) & 1ull)) { ++b; continue; }
-      int e = b;
-      while (e < 55 && ((leaf_var >> e) & 1ull)) ++e;
-      if (runs.n == 16) { runs.n = 17; break; }
-      runs.lo[runs.n] = (uint8_t)b;
-      runs.len[runs.n] = (uint8_t)(e - b);
-      runs.pos[runs.n] = (uint8_t)pos;
-      ++runs.n;
-      pos += e - b;
-      b = e;
-    }
-    if (runs.n > 16 || (runs.n == 1 && runs.lo[0] == 0)) {
-      runs.n = 0;  // too fragmented, or already compact
-    } else {
-      runs.cbits = (h->off_and >> 9) & ~leaf_var;
-    }
-  }
-  const uint64_t sort_var = runs.n ? (((1ull << __builtin_popcountll(leaf_var)) - 1ull) << 9) : varying;
-  const PassSpec ps = pass_spec(sort_var, 9);
+  const SortPlan plan = make_sort_plan(h->off_or, h->off_and, (uint64_t)U, 0);
+  const BitRuns runs = plan.kf.runs;
+  const PassSpec ps = plan.ps;
   const int nbk = grid_for((n_in + 3) / 4, 256, kHistBlocks);
-  if (ps.passes == 0) runs.n = 0;
   k_key2<<<nbk, 256, 0, s>>>(d_ijk, n_in, root_keys, root_vals, (uint32_t)(cap - 1), tiles_sorted, U, ka, ps, runs,
                              hpart, st);
   IGC_HIP(hipGetLastError(), "igc_grid_build: key pass launch");
@@ -1317,11 +1423,7 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   // The sorted keys stay compacted: leaf, lower and upper boundaries are compared at the
   // compacted positions of leaf-part bits 0, 12 and 27, and the register pass expands a key
   // only where it starts a leaf.
-  KeyForm kf{21, 36, runs};
-  if (runs.n) {
-    kf.cs_lower = 9 + __builtin_popcountll(leaf_var & 0xFFFull);
-    kf.cs_upper = 9 + __builtin_popcountll(leaf_var & ((1ull << 27) - 1ull));
-  }
+  const KeyForm kf = plan.kf;
 
   // Counts, then the read-back that sizes the topology.
   const int64_t nb = tiles;
@@ -1375,7 +1477,7 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
       (uint64_t*)blk, (int64_t)(zero_end / 8), g->root_keys, root_keys, root_words);
   IGC_HIP(hipGetLastError(), "igc_grid_build: topology initialisation launch");
 
-  Topo t{F,           Lw,           U,          &st->guard,     tiles_sorted,
+  Topo t{F,           Lw,           U,          &st->guard,     &st->cap_over, tiles_sorted,
          g->root_list, g->upper_origin, g->upper_mask, g->upper_first, g->lower_origin, g->lower_mask,
          g->lower_first, g->leaf,     g->leaf_origin};
   k_register<<<(unsigned)nb, kThreads, 0, s>>>(sorted, n_in, bprefix, t, kf);
@@ -1402,11 +1504,267 @@ int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
   }
   // Last read-back: the voxel count.
   IGC_HIP(hipStreamSynchronize(s), "igc_grid_build: registration");
-  if (h->guard) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: device bounds check failed in registration");
+  if (h->guard || h->cap_over)
+    return set_error(IGC_ERR_INTERNAL, "igc_grid_build: device bounds check failed in registration");
   const int64_t N = (int64_t)h->counts[0];
   if (N < F || N > n_in) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: inconsistent voxel count");
   g->n_voxels = N;
   return IGC_OK;
+}
+
+// ------------------------------------------------------------------------------ counted build
+//
+// The build with one host read-back (DriveRT, "Counts kept on the GPU"), for scenes of at most
+// kSmallSort root tiles. The tile pass's state stays on the device: the tiles are ranked from
+// the device count, a one-thread kernel derives the sort plan (key compaction and passes of
+// 8- or 9-bit digits) from the OR / AND of the keys, the radix passes are launched up to the largest
+// count and skip themselves past the plan's (the key pass writes into the buffer that makes the
+// last pass end in the first), and the counts N, F, Lw, U come out of the count pass on the
+// device. The topology is sized from estimates (rows per coordinate of the last build in this
+// process); a row past one sets cap_over and the build runs again with the exact counts it
+// reported (DriveRT, "Compilation and deployment": results are never truncated). A scene with
+// more tiles falls back to the synced build.
+namespace {
+
+constexpr uint32_t kCountedRoot = 2 * kSmallSort;  // root table slots of the counted build
+
+struct BuildHint {
+  double leaf = 0.25, lower = 1.0 / 64.0;  // leaves, lower nodes per input coordinate
+  int64_t upper = 32;
+  int digit_bits = 8;  // 9 when the last key span took fewer 9-bit passes than 8-bit ones
+};
+std::mutex g_hint_mu;
+BuildHint g_hint;
+
+enum CountedStatus { kBuilt = 0, kFallBack = 1, kRepeat = 2 };
+
+template <int BITS>
+int build_grid_counted(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g, int64_t capF, int64_t capLw,
+                       int64_t capU, int* status, int64_t exact[3]) {
+  constexpr int kCountedHist = kCountedPasses << BITS;
+  *status = kFallBack;
+  uint64_t cap = kCountedRoot;
+  if (const char* e = std::getenv("IGC_TEST_INITIAL_CAPACITY")) {  // forces the synced build's retries
+    const uint64_t want = std::strtoull(e, nullptr, 10);
+    cap = 1;
+    while (cap < want) cap <<= 1;
+  }
+  const int64_t tiles = (n_in + kTileKeys - 1) / kTileKeys;
+  const int64_t sort_tiles = (n_in + kSortTile - 1) / kSortTile;
+  const int64_t groups = (capF + kLeafGroup - 1) / kLeafGroup;
+  const size_t ws = align_up(sizeof(BuildState), 256) + align_up(sizeof(SortPlan), 256) +
+                    align_up((size_t)kTileBlocks * 32, 256) + align_up((size_t)kMaxPasses * kMaxBins * 4, 256) +
+                    align_up((size_t)kHistBlocks * kCountedHist * 4, 256) + 2 * align_up((size_t)n_in * 8, 256) +
+                    2 * align_up((size_t)sort_tiles * kMaxBins * 4, 256) + align_up((size_t)tiles * 8, 256) +
+                    align_up((size_t)tiles * 32, 256) + align_up((size_t)groups * 8, 256) +
+                    2 * align_up((size_t)kSmallSort * 8, 256) + align_up((size_t)cap * 12, 256);
+  Arena ar(s, grid_alloc(g));
+  int rc = ar.reserve(ws);
+  if (rc) return rc;
+  BuildState* st = ar.take<BuildState>(sizeof(BuildState));
+  SortPlan* plan = ar.take<SortPlan>(sizeof(SortPlan));
+  uint64_t* partial = ar.take<uint64_t>((size_t)kTileBlocks * 32);
+  uint32_t* hist = ar.take<uint32_t>((size_t)kMaxPasses * kMaxBins * 4);
+  uint32_t* hpart = ar.take<uint32_t>((size_t)kHistBlocks * kCountedHist * 4);
+  uint64_t* ka = ar.take<uint64_t>((size_t)n_in * 8);
+  uint64_t* kb = ar.take<uint64_t>((size_t)n_in * 8);
+  uint32_t* rcnt = ar.take<uint32_t>((size_t)sort_tiles * kMaxBins * 4);
+  uint32_t* roff = ar.take<uint32_t>((size_t)sort_tiles * kMaxBins * 4);
+  uint64_t* bcounts = ar.take<uint64_t>((size_t)tiles * 8);
+  uint64_t* bprefix = ar.take<uint64_t>((size_t)tiles * 32);
+  uint64_t* gsum = ar.take<uint64_t>((size_t)groups * 8);
+  uint64_t* tile_list = ar.take<uint64_t>((size_t)kSmallSort * 8);
+  uint64_t* tile_tmp = ar.take<uint64_t>((size_t)kSmallSort * 8);
+  uint64_t* root_keys = ar.take<uint64_t>((size_t)cap * 12);
+  if (!root_keys) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: workspace layout");
+  int32_t* root_vals = (int32_t*)(root_keys + cap);
+  BuildState* hd = nullptr;
+  BuildState* h = (BuildState*)host_staging(sizeof(BuildState), (void**)&hd);
+  if (!h || !hd) return set_error(IGC_ERR_OOM, "igc_grid_build: pinned staging buffer");
+
+  // Tiles, their ranks and the sort plan, all on the device.
+  k_init_root<<<grid_for((int64_t)cap, 256, 4096), 256, 0, s>>>(st, root_keys, (int64_t)cap);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: init launch");
+  const int nbt = grid_for((n_in + 3) / 4, 256, kTileBlocks);
+  k_tile_insert<<<nbt, 256, 0, s>>>(d_ijk, n_in, root_keys, (uint32_t)(cap - 1), (uint32_t)cap, partial, st, tile_list,
+                                    (uint32_t)kSmallSort);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: tile insert launch");
+  k_reduce_bits<<<1, 256, 0, s>>>(partial, nbt, st, hd);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: tile bits launch");
+  // More tiles than upper-node rows: the table is emptied (no lookup can return a row past the
+  // upper arrays), the rest of the build does no work, and it is repeated with the exact count.
+  k_sort_rank_small<<<1, 1024, 0, s>>>(tile_list, tile_tmp, -1, root_keys, root_vals, (uint32_t)(cap - 1), st, capU);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: tile sort launch");
+  k_make_plan<<<1, 64, 0, s>>>(st, plan, BITS);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: sort plan launch");
+
+  // Keys, their sort and the counts.
+  const int nbk = grid_for((n_in + 3) / 4, 256, kHistBlocks);
+  k_key2<<<nbk, 256, 0, s>>>(d_ijk, n_in, root_keys, root_vals, (uint32_t)(cap - 1), tile_tmp, kSmallSort, ka,
+                             PassSpec{0, 0, BITS}, BitRuns{}, hpart, st, plan, kCountedHist, kb);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: key pass launch");
+  k_hist_reduce<<<(kCountedHist + 15) / 16, 256, 0, s>>>(hpart, nbk, kCountedHist, hist);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: histogram reduce launch");
+  for (int p = 0; p < kCountedPasses; ++p) {
+    radix_pass<BITS>(ka, kb, n_in, 0, hist + ((size_t)p << BITS), rcnt, roff, sort_tiles, &st->guard, p == 0, s,
+                     nullptr, plan, p);
+    IGC_HIP(hipGetLastError(), "igc_grid_build: radix pass launch");
+  }
+  k_count<<<(unsigned)tiles, kThreads, 0, s>>>(ka, n_in, bcounts, 0, 0, plan);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: count launch");
+  k_scan_blocks<<<1, 1024, 0, s>>>(bcounts, tiles, bprefix, st, hd);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: block scan launch");
+
+  // Topology sized from the estimates (zeroed masks, the root table copied in).
+  size_t off = 0;
+  auto carve = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const int64_t F = capF, Lw = capLw, U = capU;
+  const size_t o_upm = carve(U * 512 * 8), o_lom = carve(Lw * 64 * 8), o_leaf = carve(F * sizeof(LeafRec)),
+               zero_end = off, o_root_list = carve(U * 8), o_upo = carve(U * 16), o_upp = carve(U * 512 * 2),
+               o_upf = carve(U * 4), o_loo = carve(Lw * 16), o_lop = carve(Lw * 64 * 2), o_lof = carve(Lw * 4),
+               o_lfo = carve(F * 16), o_nbr = carve(F * 27 * 4), o_root = carve(cap * 12);
+  char* blk = nullptr;
+  if ((rc = dev_alloc((void**)&blk, off, s, "igc_grid_build: topology", grid_alloc(g)))) return rc;
+  g->block = blk;
+  g->bytes = off;
+  g->root_keys = (uint64_t*)(blk + o_root);
+  g->root_vals = (int32_t*)(g->root_keys + cap);
+  g->root_cap = (uint32_t)cap;
+  g->root_list = (uint64_t*)(blk + o_root_list);
+  g->upper_origin = (int4*)(blk + o_upo);
+  g->upper_mask = (uint64_t*)(blk + o_upm);
+  g->upper_pre = (uint16_t*)(blk + o_upp);
+  g->upper_first = (uint32_t*)(blk + o_upf);
+  g->lower_origin = (int4*)(blk + o_loo);
+  g->lower_mask = (uint64_t*)(blk + o_lom);
+  g->lower_pre = (uint16_t*)(blk + o_lop);
+  g->lower_first = (uint32_t*)(blk + o_lof);
+  g->leaf = (LeafRec*)(blk + o_leaf);
+  g->leaf_origin = (int4*)(blk + o_lfo);
+  g->leaf_nbr = (int32_t*)(blk + o_nbr);
+  g->n_leaf = F;  // capacities until the read-back
+  g->n_lower = Lw;
+  g->n_upper = U;
+  const int64_t root_words = (int64_t)((cap * 12 + 7) / 8);
+  k_fill_copy_u64<<<grid_for((int64_t)(zero_end / 8) + root_words, 256, 4096), 256, 0, s>>>(
+      (uint64_t*)blk, (int64_t)(zero_end / 8), g->root_keys, root_keys, root_words);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: topology initialisation launch");
+
+  Topo t{F,           Lw,           U,          &st->guard,     &st->cap_over, tile_tmp,
+         g->root_list, g->upper_origin, g->upper_mask, g->upper_first, g->lower_origin, g->lower_mask,
+         g->lower_first, g->leaf,     g->leaf_origin};
+  k_register<<<(unsigned)tiles, kThreads, 0, s>>>(ka, n_in, bprefix, t, KeyForm{21, 36, BitRuns{}}, plan);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: register launch");
+  const uint64_t* dc = st->counts;
+  const int64_t nbl = (Lw + 3) / 4;
+  k_node_prefix<<<(unsigned)(nbl + (U + 3) / 4), 256, 0, s>>>(g->lower_mask, g->lower_pre, Lw, nbl, g->upper_mask,
+                                                             g->upper_pre, U, dc);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: node prefix launch");
+  k_leaf_neighbors<<<grid_for(F * 27, 256, 8192), 256, 0, s>>>(g->view(), g->leaf_nbr, dc);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: leaf neighbour launch");
+  k_leaf_count<<<(unsigned)std::max<int64_t>(groups, 1), 256, 0, s>>>(g->leaf, F, gsum, dc);
+  IGC_HIP(hipGetLastError(), "igc_grid_build: leaf count launch");
+  k_scan_groups<<<1, 1024, 0, s>>>(gsum, std::max<int64_t>(groups, 1), st, hd);  // publishes the state
+  IGC_HIP(hipGetLastError(), "igc_grid_build: leaf scan launch");
+  if (groups > 1) {
+    k_leaf_offset<<<(unsigned)groups, 256, 0, s>>>(g->leaf, F, gsum, dc);
+    IGC_HIP(hipGetLastError(), "igc_grid_build: leaf offset launch");
+  }
+
+  IGC_HIP(hipStreamSynchronize(s), "igc_grid_build: the read-back");  // the one synchronisation
+  auto drop_block = [&]() {
+    dev_free(g->block, g->bytes, s, grid_alloc(g));
+    g->block = nullptr;
+    g->bytes = 0;
+  };
+  g->host_syncs += 1;
+  if (h->overflow || h->n_tiles == 0 || h->n_tiles > (uint32_t)kSmallSort) {
+    drop_block();
+    *status = kFallBack;
+    return IGC_OK;
+  }
+  if ((int64_t)h->n_tiles > U) {  // the tile count is exact; leaves and lower nodes were not counted
+    drop_block();
+    exact[0] = std::max<int64_t>(F, (int64_t)h->n_tiles);
+    exact[1] = std::max<int64_t>(Lw, (int64_t)h->n_tiles);
+    exact[2] = (int64_t)h->n_tiles;
+    *status = kRepeat;
+    return IGC_OK;
+  }
+  // F, Lw, U come from the count pass; N from the leaves' popcounts (partial when registration
+  // stopped at an estimate, so it is checked only after that case).
+  const int64_t N = (int64_t)h->counts[0], Fx = (int64_t)h->counts[1], Lwx = (int64_t)h->counts[2],
+                Ux = (int64_t)h->counts[3];
+  if (h->guard) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: device bounds check failed");
+  if ((int64_t)h->n_tiles != Ux || Fx < 1 || Fx > n_in || Lwx > Fx || Ux > Lwx)
+    return set_error(IGC_ERR_INTERNAL, "igc_grid_build: inconsistent node counts");
+  if (h->cap_over || Fx > F || Lwx > Lw || Ux > U) {
+    drop_block();
+    exact[0] = Fx;
+    exact[1] = Lwx;
+    exact[2] = Ux;
+    *status = kRepeat;
+    return IGC_OK;
+  }
+  if (N < Fx || N > n_in) return set_error(IGC_ERR_INTERNAL, "igc_grid_build: inconsistent voxel count");
+  g->n_voxels = N;
+  g->n_leaf = Fx;
+  g->n_lower = Lwx;
+  g->n_upper = Ux;
+  g->sort_passes = (int32_t)h->sort_passes;
+  {
+    std::lock_guard<std::mutex> lk(g_hint_mu);
+    g_hint.leaf = (double)Fx / (double)n_in;
+    g_hint.lower = (double)Lwx / (double)n_in;
+    g_hint.upper = Ux;
+    const int span = (int)h->sort_span;
+    g_hint.digit_bits = (span + 8) / 9 < (span + 7) / 8 ? 9 : 8;
+  }
+  *status = kBuilt;
+  return IGC_OK;
+}
+
+}  // namespace
+
+int build_grid(const int32_t* d_ijk, int64_t n_in, hipStream_t s, igc_grid* g) {
+  g->n_input = n_in;
+  if (n_in == 0) {
+    // No device work. A grid built with an allocator still owns one (minimal) block from it.
+    if (grid_alloc(g)) {
+      const int rc = dev_alloc(&g->block, 256, s, "igc_grid_build: topology", grid_alloc(g));
+      if (rc) return rc;
+      g->bytes = 256;
+    }
+    return IGC_OK;
+  }
+  BuildHint hint;
+  {
+    std::lock_guard<std::mutex> lk(g_hint_mu);
+    hint = g_hint;
+  }
+  const double n = (double)n_in;
+  int64_t capF = std::min<int64_t>(n_in, (int64_t)std::ceil(hint.leaf * n * 1.25) + 256);
+  int64_t capLw = std::min<int64_t>(capF, (int64_t)std::ceil(hint.lower * n * 1.25) + 64);
+  int64_t capU = std::min<int64_t>({(int64_t)kSmallSort, capLw, 2 * hint.upper + 8});
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    int status = kFallBack;
+    int64_t exact[3] = {0, 0, 0};
+    const int rc = hint.digit_bits == 9 ? build_grid_counted<9>(d_ijk, n_in, s, g, capF, capLw, capU, &status, exact)
+                                        : build_grid_counted<8>(d_ijk, n_in, s, g, capF, capLw, capU, &status, exact);
+    if (rc != IGC_OK) return rc;
+    if (status == kBuilt) return IGC_OK;
+    if (status == kFallBack) break;
+    capF = exact[0];
+    capLw = exact[1];
+    capU = exact[2];
+  }
+  const int rc = build_grid_synced(d_ijk, n_in, s, g);
+  g->host_syncs += 3;
+  return rc;
 }
 
 
@@ -1862,7 +2220,7 @@ int derive_enqueue(const igc_grid* in, const uint64_t* in_counts, const DeriveSt
   k_scan_blocks<<<1, 1024, 0, s>>>(w.bcounts, d.R > 0 ? w.nb : 0, w.bprefix, st, hd);
   IGC_HIP(hipGetLastError(), "igc_conv_grid: block scan launch");
   if (d.R > 0) {
-    Topo t{d.F,           d.Lw,          d.U,           &st->guard,      nullptr,
+    Topo t{d.F,           d.Lw,          d.U,           &st->guard,      &st->cap_over, nullptr,
            out->root_list, out->upper_origin, out->upper_mask, out->upper_first, out->lower_origin, out->lower_mask,
            out->lower_first, out->leaf,   out->leaf_origin};
     k_derive_register<<<(unsigned)w.nb, 256, 0, s>>>(sorted, d.R, w.bprefix, d.ib, w.rec_origin, w.rec_mask, t,
@@ -1967,7 +2325,7 @@ int derive_chain(const igc_grid* in, int n, const int32_t* strides, const int32_
   BuildState* h = (BuildState*)host_staging(sizeof(BuildState) * (size_t)n, (void**)&hd);
   if (!h || !hd) return set_error(IGC_ERR_OOM, "igc_conv_grid: pinned staging buffer");
 
-  int first = 0;
+  int first = 0, syncs = 0;
   for (int attempt = 0; attempt <= 2 * n + 2; ++attempt) {
     // Output blocks of stages first .. n-1.
     for (int k = first; k < n; ++k) {
@@ -2000,6 +2358,7 @@ int derive_chain(const igc_grid* in, int n, const int32_t* strides, const int32_
     }
     if (rc == IGC_OK) {
       const hipError_t e = hipStreamSynchronize(s);  // the chain's one read-back
+      ++syncs;
       if (e != hipSuccess) rc = hip_status(e, "igc_conv_grid: synchronize");
     }
     ws_release(&wsb, s);
@@ -2050,6 +2409,7 @@ int derive_chain(const igc_grid* in, int n, const int32_t* strides, const int32_
         g->n_upper = (int64_t)r.counts[3];
         g->n_input = k == 0 ? in->n_voxels : outs[k - 1]->n_voxels;
         g->sort_passes = 0;
+        g->host_syncs = syncs;
       }
       return IGC_OK;
     }

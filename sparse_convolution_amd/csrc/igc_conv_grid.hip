@@ -226,7 +226,10 @@ int build_conv_grid(const igc_grid* in, const int32_t* stride, int32_t transpose
   }
   if (e == hipSuccess && rc == IGC_OK && h_flag)
     rc = set_error(IGC_ERR_RANGE, "igc_conv_grid: an output coordinate leaves the int32 range");
-  if (e == hipSuccess && rc == IGC_OK) rc = build_grid(cand, n_cand, s, out);
+  if (e == hipSuccess && rc == IGC_OK) {
+    rc = build_grid(cand, n_cand, s, out);
+    out->host_syncs += 1;  // the range flag's read-back
+  }
   dev_free(ws, ws_bytes, s, grid_alloc(out));
   if (e != hipSuccess) return hip_status(e, "igc_conv_grid: candidates");
   return rc;

@@ -14,6 +14,7 @@ struct igc_grid {
   hipStream_t stream = nullptr;  // stream the grid was built on (destroy waits for it)
   int64_t n_input = 0, n_voxels = 0, n_leaf = 0, n_lower = 0, n_upper = 0;
   int32_t sort_passes = 0;
+  int32_t host_syncs = 0;  // host synchronisations the build took
   uint32_t root_cap = 0;
   size_t bytes = 0;
   void* block = nullptr;  // one device allocation holding every array below

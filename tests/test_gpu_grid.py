@@ -148,10 +148,32 @@ def test_capacity_retry(monkeypatch):
 
 
 def test_many_tiles_radix_tile_sort():
-    # more than 4096 distinct root tiles: the tile keys go through the radix sort too
+    # more than 4096 distinct root tiles: the one-read-back build falls back to the build with
+    # read-backs after the tile pass and the counts, whose tile keys go through the radix sort
     rng = np.random.default_rng(17)
     c = rng.integers(-2**30, 2**30, size=(60000, 3)).astype(np.int32)
-    check_grid(c, "many tiles")
+    g, _ = check_grid(c, "many tiles")
+    assert g.host_syncs == 4
+
+
+def test_counted_build_repeats_with_exact_counts():
+    # The build sizes its node arrays from the previous build's rows per coordinate and reads the
+    # device state back once. A dense block (216 leaves for 110,592 coordinates) followed by 343
+    # isolated voxels, each its own leaf, lower node and root tile, outgrows every estimate: the
+    # build is repeated with the exact counts (a second read-back) and matches the oracle.
+    igc = _igc()
+    dense = np.stack(np.meshgrid(*[np.arange(48)] * 3, indexing="ij"), -1).reshape(-1, 3).astype(np.int32)
+    igc.grid_build(to_dev(dense))
+    g1, _ = check_grid(dense, "dense block")
+    assert g1.host_syncs == 1  # the same scene again: its estimate fits
+    t = np.arange(-3, 4)
+    pts = np.stack(np.meshgrid(4096 * t + 7, 4096 * t + 100, 4096 * t + 1000, indexing="ij"), -1)
+    pts = pts.reshape(-1, 3).astype(np.int32)
+    g2, ref = check_grid(pts, "isolated voxels in 343 tiles")
+    assert (g2.n_leaf, g2.n_lower, g2.n_upper) == (343, 343, 343)
+    assert g2.host_syncs == 2
+    g3, _ = check_grid(workloads.make_coords("lidar"), "lidar after isolated voxels")
+    assert g3.host_syncs in (1, 2)
 
 
 def test_empty_grid():
