@@ -581,8 +581,8 @@ int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats
     k_dense_rows<<<(unsigned)((g->n_leaf + 3) / 4), 256, 0, s>>>(g->leaf, g->n_leaf, N, dense_min, skip);
     e = hipGetLastError();
   }
+  const GgsTuning tu = ggs_tuning(cin, cout, N, g->n_leaf);
   if (e == hipSuccess && n_tiles > 0) {
-    const GgsTuning tu = ggs_tuning(cin, cout, N, g->n_leaf);
     e = launch_plan(tu.span, tu.order, d_map, N, n_in, perm, blk, skip, s);
   }
   if (e == hipSuccess && n_tiles > 0) {
@@ -593,11 +593,15 @@ int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats
     // eight (each 32 rows by all 64 channels: 2% faster on 64 -> 64 than 64 by 32); 32-channel
     // chunks when cin is not a multiple of 64.
     const int64_t n256 = cout / 256, n128 = cout / 128, n64 = cout / 64;
-    if (cout % 256 == 0 && k64) {
+    // A layer's rule may ask for narrower output tiles (more workgroups, each gathering the
+    // same input rows for fewer channels).
+    int bn = cout % 256 == 0 && k64 ? 256 : cout % 128 == 0 ? 128 : 64;
+    if (tu.bn > 0 && tu.bn < bn && cout % tu.bn == 0) bn = tu.bn;
+    if (bn == 256) {
       launch_main<256, 64, 2, 2, 8>(n_tiles, n256, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
-    } else if (cout % 128 == 0 && k64) {
+    } else if (bn == 128 && k64) {
       launch_main<128, 64, 8, 2, 16>(n_tiles, n128, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
-    } else if (cout % 128 == 0) {
+    } else if (bn == 128) {
       launch_main<128, 32, 2, 2, 8>(n_tiles, n128, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
     } else if (k64) {
       launch_main<64, 64, 8, 2, 8>(n_tiles, n64, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);

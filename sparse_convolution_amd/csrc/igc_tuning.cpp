@@ -7,8 +7,9 @@
 // natural order.
 //
 // File format (text, one rule per line, '#' starts a comment, first matching rule wins):
-//   ggs <cin|*> <cout|*> <occupancy_lo> <occupancy_hi> <span> <natural|class>
-// with span 256, 1024 or 4096 and lo <= occupancy < hi.
+//   ggs <cin|*> <cout|*> <occupancy_lo> <occupancy_hi> <span> <natural|class> [tile]
+// with span 256, 1024 or 4096, lo <= occupancy < hi, and tile (output channels per workgroup)
+// auto, 256, 128 or 64.
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -60,20 +61,24 @@ extern "C" int igc_tuning_load(const char* path) {
   while (std::fgets(line, sizeof line, f)) {
     ++lineno;
     if (char* h = std::strchr(line, '#')) *h = '\0';
-    char kind[16], cin[16], cout[16], order[16];
+    char kind[16], cin[16], cout[16], order[16], tile[16] = "auto";
     double lo = 0, hi = 0;
     int span = 0;
-    const int n = std::sscanf(line, "%15s %15s %15s %lf %lf %d %15s", kind, cin, cout, &lo, &hi, &span, order);
+    const int n =
+        std::sscanf(line, "%15s %15s %15s %lf %lf %d %15s %15s", kind, cin, cout, &lo, &hi, &span, order, tile);
     if (n <= 0) continue;  // blank or comment
     Rule r;
     const bool order_ok = !std::strcmp(order, "natural") || !std::strcmp(order, "class");
-    if (n != 7 || std::strcmp(kind, "ggs") || !(span == 256 || span == 1024 || span == 4096) || !order_ok ||
-        !(lo <= hi)) {
+    const int bn = !std::strcmp(tile, "auto") ? 0 : std::atoi(tile);
+    const bool tile_ok = !std::strcmp(tile, "auto") || bn == 256 || bn == 128 || bn == 64;
+    if ((n != 7 && n != 8) || std::strcmp(kind, "ggs") || !(span == 256 || span == 1024 || span == 4096) ||
+        !order_ok || !tile_ok || !(lo <= hi)) {
       rc = set_error(IGC_ERR_INVALID_ARG, "igc_tuning_load: " + std::string(path) + ":" + std::to_string(lineno) +
                                               ": expected 'ggs <cin|*> <cout|*> <occ_lo> <occ_hi> <256|1024|4096> "
-                                              "<natural|class>'");
+                                              "<natural|class> [auto|256|128|64]'");
       break;
     }
+    r.tu.bn = bn;
     r.cin = std::strcmp(cin, "*") ? std::atoi(cin) : -1;
     r.cout = std::strcmp(cout, "*") ? std::atoi(cout) : -1;
     r.occ_lo = lo;

@@ -3,9 +3,9 @@ that the library loads (igc_tuning_load; the package loads igconv_tuning.txt bes
 
     python -m sparse_convolution_amd.tune [--workloads lidar band large] [--out PATH]
 
-For every workload (synthetic scenes of the bench, see workloads/) each candidate row order
-(span 256 / 1024 / 4096 rows sorted by neighbour mask, natural or class bit order) is timed on
-the same path that runs in deployment (igc_sparse_conv, gather-GEMM-scatter), after checking
+For every workload (synthetic scenes of the bench, see workloads/) each candidate (span 256 /
+1024 / 4096 rows sorted by neighbour mask, natural or class bit order, output-tile width) is timed
+on the same path that runs in deployment (igc_sparse_conv, gather-GEMM-scatter), after checking
 that its output equals the default order's; the fastest is written as one rule for the layer's
 channels, with the measured times as comments (DriveRT, "Measurement and reproducibility":
 algorithms are selected offline on the target GPU with the deployment path, and the selection
@@ -24,8 +24,13 @@ import torch
 from . import _lib
 import sparse_convolution_amd as igc
 
-CANDIDATES = [(256, "natural"), (256, "class"), (1024, "natural"), (1024, "class"), (4096, "natural"),
-              (4096, "class")]
+SPANS = [(256, "natural"), (256, "class"), (1024, "natural"), (1024, "class"), (4096, "natural"), (4096, "class")]
+
+
+def _tiles(cin: int, cout: int) -> list:
+    """Output-tile widths the layer can use (auto = the widest)."""
+    widest = 256 if cout % 256 == 0 and cin % 64 == 0 else 128 if cout % 128 == 0 else 64
+    return ["auto"] + [str(b) for b in (128, 64) if b < widest and cout % b == 0]
 
 
 def _time(fn, reps):
@@ -54,23 +59,23 @@ def tune_workload(name: str, log) -> tuple[str, list]:
     ref = None
     with tempfile.TemporaryDirectory() as d:
         path = os.path.join(d, "rule.txt")
-        for span, order in CANDIDATES:
+        for (span, order), tile in [(so, t) for so in SPANS for t in _tiles(wl.cin, wl.cout)]:
             with open(path, "w") as fh:
-                fh.write(f"ggs {wl.cin} {wl.cout} 0 1e30 {span} {order}\n")
+                fh.write(f"ggs {wl.cin} {wl.cout} 0 1e30 {span} {order} {tile}\n")
             igc.tuning_load(path)
             out = torch.empty((g.n_voxels, wl.cout), dtype=torch.bfloat16, device="cuda")
             ms = _time(lambda: igc.sparse_conv(g, f, w, kmap=m, path="ggs", out=out), reps)
             if ref is None:
                 ref = out.clone()
             elif not torch.equal(out.float().abs(), ref.float().abs()):  # signs of exact zeros may differ
-                raise RuntimeError(f"{name}: row order {span} {order} changed the output")
-            results.append((ms, span, order))
-            log(f"[tune] {name} span {span} {order}: {ms:.4f} ms")
+                raise RuntimeError(f"{name}: row order {span} {order} tile {tile} changed the output")
+            results.append((ms, span, order, tile))
+            log(f"[tune] {name} span {span} {order} tile {tile}: {ms:.4f} ms")
     igc.tuning_load(None)
     best = min(results)
     lines = [f"# {name}: {g.n_voxels} voxels, leaf occupancy {occ:.3f}, bf16 {wl.cin} -> {wl.cout}; ms per conv: "
-             + ", ".join(f"{s}/{o} {ms:.3f}" for ms, s, o in results),
-             f"ggs {wl.cin} {wl.cout} 0 1e30 {best[1]} {best[2]}"]
+             + ", ".join(f"{s}/{o}/{t} {ms:.3f}" for ms, s, o, t in results),
+             f"ggs {wl.cin} {wl.cout} 0 1e30 {best[1]} {best[2]} {best[3]}"]
     return "\n".join(lines), results
 
 
@@ -82,10 +87,10 @@ def main() -> int:
     log = lambda s: (sys.stderr.write(s + "\n"), sys.stderr.flush())
     _lib.load()
     igc.tuning_load(None)
-    blocks = [f"# gather-GEMM-scatter row order per layer, selected by python -m sparse_convolution_amd.tune on "
+    blocks = [f"# gather-GEMM-scatter row order and tile width per layer, selected by python -m sparse_convolution_amd.tune on "
               f"{torch.cuda.get_device_name(0)} {getattr(torch.cuda.get_device_properties(0), 'gcnArchName', '')} "
               f"({time.strftime('%Y-%m-%d')})",
-              "# ggs <cin|*> <cout|*> <occupancy_lo> <occupancy_hi> <span 256|1024|4096> <natural|class>"]
+              "# ggs <cin|*> <cout|*> <occupancy_lo> <occupancy_hi> <span 256|1024|4096> <natural|class> <tile>"]
     for name in args.workloads:
         text, _ = tune_workload(name, log)
         blocks.append(text)

@@ -211,11 +211,13 @@ def _restore_tuning():
     _igc().tuning_load(L.TUNING_PATH if os.path.exists(L.TUNING_PATH) else None)
 
 
-@pytest.mark.parametrize("span,order", [(256, "class"), (1024, "natural"), (4096, "natural"), (4096, "class")])
+@pytest.mark.parametrize("span,order,tile", [(256, "class", "auto"), (1024, "natural", "64"), (4096, "natural", "auto"),
+                                             (4096, "class", "64")])
 @pytest.mark.parametrize("case", ["lidar", "clusters", "mixed"])
-def test_row_order_rules_keep_outputs(tmp_path, _restore_tuning, span, order, case):
-    # A row-order rule (igc_tuning_load) changes which offsets each tile visits, never an output:
-    # every rule gives the default order's output (up to the sign of exact zeros), and that
+def test_row_order_rules_keep_outputs(tmp_path, _restore_tuning, span, order, tile, case):
+    # A row-order / tile rule (igc_tuning_load) changes which offsets each tile visits and how
+    # many channels a workgroup computes, never an output: every rule gives the default's output
+    # (up to the sign of exact zeros), and that
     # output matches the oracle on sampled rows. Spans wider than the grid and ragged last spans
     # are included (clusters: a few thousand rows).
     igc = _igc()
@@ -235,7 +237,7 @@ def test_row_order_rules_keep_outputs(tmp_path, _restore_tuning, span, order, ca
     igc.tuning_load(None)
     y0 = igc.sparse_conv(g, f, w, kmap=m, path=path)
     rule = tmp_path / "rule.txt"
-    rule.write_text(f"ggs * * 0 1e30 {span} {order}\n")
+    rule.write_text(f"ggs * * 0 1e30 {span} {order} {tile}\n")
     igc.tuning_load(str(rule))
     y1 = igc.sparse_conv(g, f, w, kmap=m, path=path)
     torch.cuda.synchronize()
