@@ -26,11 +26,15 @@ the gather-GEMM-scatter path (bf16 workloads): build the input grid, its stride-
 value is 2 * pairs * cin * cout of that convolution per second of the step. With --chain
 S1,S2,... a step builds a chain of strided output grids with the counts kept on the device
 (igc_conv_grid_chain, one synchronisation) and, for comparison, the same grids one call at a
-time; value is the chain's wall-clock milliseconds. The default line is unchanged.
+time; value is the chain's wall-clock milliseconds. With --layer DTYPE:CIN:COUT the step runs the
+workload's scene with that layer shape instead (for example --layer bf16:4:32, which no tuned
+path takes and runs on the general-shape path, whose roof is the fp32 vector peak). The default
+line is unchanged.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -48,7 +52,7 @@ PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}  # dense MFMA peaks of MI355X
 CONV_SRC = {"leaf": "sparse_convolution_amd/csrc/igc_conv_leaf.hip",
             "ggs": "sparse_convolution_amd/csrc/igc_conv_ggs.hip"}
 CONV_KERNEL = {("leaf", "f32"): "k_conv_leaf_f32", ("leaf", "bf16"): "k_conv_leaf_bf16",
-               ("ggs", "bf16"): "k_conv_ggs_bf16"}
+               ("ggs", "bf16"): "k_conv_ggs_bf16", ("gather", "f32"): "k_conv_gather", ("gather", "bf16"): "k_conv_gather"}
 DEFAULT_STEPS = {"tiny": (50, 5), "leaf": (20, 3), "band": (10, 2), "lidar": (20, 3), "large": (10, 2),
                  "band32": (10, 2)}
 
@@ -150,7 +154,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="large", choices=["tiny", "leaf", "band", "lidar", "large", "band32"])
-    ap.add_argument("--path", default="auto", choices=["auto", "leaf", "ggs"])
+    ap.add_argument("--path", default="auto", choices=["auto", "leaf", "ggs", "gather"])
+    ap.add_argument("--layer", default="", help="DTYPE:CIN:COUT (f32 or bf16) in place of the workload's layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--backward", action="store_true", help="add the input and weight gradients to the step")
@@ -176,6 +181,11 @@ def main() -> int:
         return chain_main(args, torch, igc, workloads)
 
     wl = workloads.WORKLOADS[args.workload]
+    if args.layer:
+        dt, ci, co = args.layer.split(":")
+        if dt not in ("f32", "bf16"):
+            raise SystemExit("--layer: dtype must be f32 or bf16")
+        wl = dataclasses.replace(wl, dtype=dt, cin=int(ci), cout=int(co), weight_std=1.0 / np.sqrt(27 * int(ci)))
     steps, warmup = DEFAULT_STEPS[args.workload]
     steps = args.steps if args.steps is not None else steps
     warmup = args.warmup if args.warmup is not None else warmup
@@ -244,8 +254,10 @@ def main() -> int:
 
     conv_ms = float(np.mean(t_conv))
     conv_tflops = flops / (conv_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[wl.dtype]
-    roofline = {"bound": "mfma", "achieved": round(conv_tflops, 3), "peak": peak, "unit": "TFLOP/s",
+    # The general-shape path runs fp32 FMAs on the vector ALUs: its roof is the fp32 vector peak.
+    peak = PEAK_TFLOPS["f32"] if path == "gather" else PEAK_TFLOPS[wl.dtype]
+    roofline = {"bound": "alu" if path == "gather" else "mfma", "achieved": round(conv_tflops, 3), "peak": peak,
+                "unit": "TFLOP/s",
                 "frac": round(conv_tflops / peak, 4), "traffic": _traffic(path, wl.dtype, args.workload),
                 "kernel": CONV_KERNEL[(path, wl.dtype)], "flops_per_launch": flops,
                 "avg_launch_ms": round(conv_ms, 4)}
@@ -282,7 +294,11 @@ def main() -> int:
             # The weight gradient's operands are the layer's dtype; its fp32 form runs on fp32 MFMA.
             backward[name] = {"tflops": round(tf, 3), "peak": peak, "frac": round(tf / peak, 4),
                               "avg_call_ms": round(float(np.mean(t)), 4)}
-        backward["wgrad"]["kernel"] = "k_wgrad_bf16" if wl.dtype == "bf16" else "k_wgrad_leaf_f32"
+        bf16_mfma = wl.dtype == "bf16" and wl.cin % 32 == 0 and wl.cout % 64 == 0
+        f32_leaf = wl.dtype == "f32" and (wl.cin, wl.cout) in {(4, 4), (4, 8), (4, 16), (4, 32), (8, 4), (8, 8), (8, 16),
+                                                               (8, 32), (16, 4), (16, 8), (16, 16)}
+        backward["wgrad"]["kernel"] = ("k_wgrad_bf16" if bf16_mfma else "k_wgrad_leaf_f32" if f32_leaf
+                                       else "k_wgrad_gather")
 
     line = {
         "metric": (METRIC if not args.backward else
@@ -291,7 +307,8 @@ def main() -> int:
         "value": round(value, 4), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
-        "config": {"workload": args.workload, "description": wl.description, "cin": wl.cin, "cout": wl.cout,
+        "config": {"workload": args.workload + (f" layer {args.layer}" if args.layer else ""),
+                   "description": wl.description, "cin": wl.cin, "cout": wl.cout,
                    "path": path, "pairs": pairs, "pairs_per_voxel": round(pairs / N, 3), **info},
         "build_mvox_s": round(info["n_input"] / (np.mean(t_build) * 1e-3) / 1e6, 1),
         "conv_tflops": round(conv_tflops, 3),

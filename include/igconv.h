@@ -66,7 +66,8 @@ typedef enum {
   IGC_PATH_AUTO = 0, /* choose from measured leaf occupancy, neighbour count and channels */
   IGC_PATH_LEAF = 1, /* leaf-local dense convolution over an LDS window of 10^3 voxels */
   IGC_PATH_GGS = 2,  /* gather-GEMM-scatter over tiles of consecutive output rows */
-  IGC_PATH_MIXED = 3 /* per-leaf dispatch: dense leaves on LEAF, the other rows on GGS */
+  IGC_PATH_MIXED = 3, /* per-leaf dispatch: dense leaves on LEAF, the other rows on GGS */
+  IGC_PATH_GATHER = 4 /* general shapes: one wave per output row, fp32 accumulation */
 } igc_path;
 
 /* Device memory provider. When a grid is created with an allocator (igc_grid_build,
@@ -209,6 +210,11 @@ int igc_kernel_map(const igc_grid* grid, const int32_t* h_offsets, int32_t K, in
  *           required). Never chosen by IGC_PATH_AUTO: measured slower than both single paths on
  *           the workloads tried (the GGS pass costs nearly as much with the dense leaves' rows
  *           removed).
+ *     GATHER (general shapes): dtype F32 or BF16, any cin and cout from 1 to 4096 (d_map
+ *           required; map entries outside [0, N) read as absent). One wave per output row with
+ *           fp32 accumulation in offset-then-channel order, no matrix cores: IGC_PATH_AUTO takes it
+ *           only for shapes neither LEAF nor GGS supports (for example a bf16 first layer with 3 or
+ *           4 input channels, bf16 128 -> 32, or fp32 32 -> 32).
  * Anything else returns IGC_ERR_UNSUPPORTED. d_out must not alias d_feats. */
 int igc_sparse_conv(const igc_grid* grid, const int32_t* d_map, const void* d_feats, int32_t dtype,
                     int32_t cin, const void* d_w, int32_t cout, void* d_out, int32_t path,
@@ -261,8 +267,12 @@ int igc_sparse_conv_noalloc(const igc_grid* grid, const int32_t* d_map, const vo
  * convolution of d_dout with W~[o] = W[26 - o]^T (the map is symmetric under offset negation),
  * so it runs on the path igc_select_path picks for (dtype, cout, cin) unless `path` forces one;
  * that shape must be supported (see igc_sparse_conv; the fp32 leaf path also takes 8 -> 4,
- * 16 -> 4, 16 -> 8). The weight gradient supports BF16 with cin a multiple of 32 and cout a multiple of
- * 64 (up to 1024), and F32 with cin, cout <= 64 and cin * cout <= 1024. Anything else returns
+ * 16 -> 4, 16 -> 8; IGC_PATH_GATHER takes any shape up to 4096 channels). The weight gradient
+ * runs on matrix-core kernels for BF16 with cin a multiple of 32 and cout a multiple of 64 (up
+ * to 1024), on the leaf window for the small F32 shapes the leaf path covers, and on a
+ * general-shape kernel (tiles of up to 64 x 64 channels, rows staged in LDS, 4 x 4 register
+ * blocks) for every other F32 or BF16 shape up to 4096 channels; all of them sum in fp32 within
+ * row chunks and in fp64 across chunks in a fixed order. Anything else returns
  * IGC_ERR_UNSUPPORTED. Outputs must not alias inputs. */
 int igc_sparse_conv_backward(const igc_grid* grid, const int32_t* d_map, const void* d_feats, int32_t dtype,
                              int32_t cin, const void* d_w, int32_t cout, const void* d_dout, void* d_dfeats,
@@ -317,9 +327,10 @@ int igc_conv_map(const igc_grid* in, const igc_grid* out, const int32_t* h_strid
  *     d_out[r, co] = sum_{o, ci : map[o, r] >= 0} d_feats[map[o, r], ci] * d_w[o, ci, co]
  * with d_map from igc_conv_map (int32[27, N_out], values < n_in), d_feats [n_in, cin] the input
  * grid's features, d_w [27, cin, cout] and d_out [N_out, cout]. Runs on the gather-GEMM-scatter
- * path: dtype BF16 with the shapes igc_sparse_conv supports there (fp32 accumulation, outputs
- * rounded to nearest even); anything else returns IGC_ERR_UNSUPPORTED. d_out must not alias
- * d_feats. */
+ * path for the BF16 shapes igc_sparse_conv supports there and on the general-shape path for
+ * every other F32 or BF16 shape up to 4096 channels (fp32 accumulation, bf16 outputs rounded to
+ * nearest even; map entries outside [0, n_in) read as absent); anything else returns
+ * IGC_ERR_UNSUPPORTED. d_out must not alias d_feats. */
 int igc_sparse_conv_between(const igc_grid* out, const int32_t* d_map, int64_t n_in, const void* d_feats,
                             int32_t dtype, int32_t cin, const void* d_w, int32_t cout, void* d_out,
                             igc_stream stream);
@@ -328,8 +339,9 @@ int igc_sparse_conv_between(const igc_grid* out, const int32_t* d_map, int64_t n
  * supports (dtype, cin, cout) and either GGS does not or the grid's leaf occupancy (active
  * voxels / (512 x leaves)) is at least 0.2 for cin <= 32 or 0.5 for cin >= 64 (the fVDB notes
  * put the leaf backend's break-even near 20%; the higher bar at 64 channels is measured);
- * GGS otherwise; IGC_ERR_UNSUPPORTED when neither path supports the shape. The IGC_PATH
- * environment variable ("leaf" / "ggs") overrides the automatic choice. */
+ * GGS when GGS supports the shape; GATHER for the other shapes up to 4096 channels;
+ * IGC_ERR_UNSUPPORTED beyond. The IGC_PATH environment variable ("leaf" / "ggs") overrides the
+ * automatic choice where that path supports the shape. */
 int igc_select_path(const igc_grid* grid, int32_t dtype, int32_t cin, int32_t cout, int32_t* path);
 
 /* Message of the last failed call on this host thread ("" if none). */

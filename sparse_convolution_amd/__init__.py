@@ -17,12 +17,12 @@ from ._lib import IgcError
 __all__ = [
     "Grid", "grid_build", "kernel_map", "sparse_conv", "sparse_conv_backward", "conv_grid", "conv_grid_chain", "conv_map",
     "sparse_conv_between", "standard_offsets", "release_memory", "tuning_load", "IgcError",
-    "PATH_AUTO", "PATH_LEAF", "PATH_GGS",
+    "PATH_AUTO", "PATH_LEAF", "PATH_GGS", "PATH_GATHER",
 ]
 
 F32, BF16 = 0, 1
-PATH_AUTO, PATH_LEAF, PATH_GGS, PATH_MIXED = 0, 1, 2, 3
-_PATHS = {"auto": PATH_AUTO, "leaf": PATH_LEAF, "ggs": PATH_GGS, "mixed": PATH_MIXED}
+PATH_AUTO, PATH_LEAF, PATH_GGS, PATH_MIXED, PATH_GATHER = 0, 1, 2, 3, 4
+_PATHS = {"auto": PATH_AUTO, "leaf": PATH_LEAF, "ggs": PATH_GGS, "mixed": PATH_MIXED, "gather": PATH_GATHER}
 
 
 def _stream(device: torch.device) -> ctypes.c_void_p:
@@ -151,7 +151,7 @@ class Grid:
     def select_path(self, dtype: torch.dtype, cin: int, cout: int) -> str:
         p = ctypes.c_int32(0)
         _lib.check(_lib.load().igc_select_path(self._h, _dtype_code(dtype), cin, cout, ctypes.byref(p)))
-        return {PATH_LEAF: "leaf", PATH_GGS: "ggs"}[p.value]
+        return {PATH_LEAF: "leaf", PATH_GGS: "ggs", PATH_GATHER: "gather"}[p.value]
 
 
 def _dtype_code(dtype: torch.dtype) -> int:

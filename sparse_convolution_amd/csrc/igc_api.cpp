@@ -223,6 +223,7 @@ static int choose_path(const igc_grid* g, int32_t dtype, int32_t cin, int32_t co
   }
   if (leaf_ok && (leaf_occupancy_ok(g, cin) || !ggs_ok)) return *path = IGC_PATH_LEAF, IGC_OK;
   if (ggs_ok) return *path = IGC_PATH_GGS, IGC_OK;
+  if (gather_conv_supported(dtype, cin, cout)) return *path = IGC_PATH_GATHER, IGC_OK;
   return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv: no path supports dtype " + std::to_string(dtype) +
                                             " with cin " + std::to_string(cin) + " and cout " + std::to_string(cout));
 }
@@ -236,7 +237,8 @@ int check_conv_args(const char* fn, const igc_grid* g, const int32_t* d_map, con
   if (dtype != IGC_F32 && dtype != IGC_BF16) return set_error(IGC_ERR_INVALID_ARG, f + ": bad dtype");
   if (cin < 1 || cout < 1) return set_error(IGC_ERR_INVALID_ARG, f + ": cin and cout must be positive");
   const int32_t p0 = *path;
-  if (p0 != IGC_PATH_AUTO && p0 != IGC_PATH_LEAF && p0 != IGC_PATH_GGS && p0 != IGC_PATH_MIXED)
+  if (p0 != IGC_PATH_AUTO && p0 != IGC_PATH_LEAF && p0 != IGC_PATH_GGS && p0 != IGC_PATH_MIXED &&
+      p0 != IGC_PATH_GATHER)
     return set_error(IGC_ERR_INVALID_ARG, f + ": bad path");
   if (!d_w) return set_error(IGC_ERR_INVALID_ARG, f + ": d_w is null");
   if (g->n_voxels > 0 && (!d_feats || !d_out)) return set_error(IGC_ERR_INVALID_ARG, f + ": d_feats or d_out is null");
@@ -253,8 +255,11 @@ int check_conv_args(const char* fn, const igc_grid* g, const int32_t* d_map, con
   if (p == IGC_PATH_MIXED &&
       !(dtype == IGC_BF16 && leaf_conv_supported(dtype, cin, cout) && ggs_conv_supported(dtype, cin, cout)))
     return set_error(IGC_ERR_UNSUPPORTED, f + ": per-leaf dispatch needs a shape both paths support");
-  if ((p == IGC_PATH_GGS || p == IGC_PATH_MIXED) && !d_map && g->n_voxels > 0)
-    return set_error(IGC_ERR_INVALID_ARG, f + ": the gather-GEMM-scatter path needs d_map");
+  if (p == IGC_PATH_GATHER && !gather_conv_supported(dtype, cin, cout))
+    return set_error(IGC_ERR_UNSUPPORTED, f + ": general-shape path takes at most " +
+                                              std::to_string(kGatherMaxChannels) + " channels");
+  if ((p == IGC_PATH_GGS || p == IGC_PATH_MIXED || p == IGC_PATH_GATHER) && !d_map && g->n_voxels > 0)
+    return set_error(IGC_ERR_INVALID_ARG, f + ": the gather-GEMM-scatter and general-shape paths need d_map");
   *path = p;
   return IGC_OK;
 }
@@ -437,6 +442,9 @@ int igc_sparse_conv(const igc_grid* g, const int32_t* d_map, const void* d_feats
   int rc = check_conv_args("igc_sparse_conv", g, d_map, d_feats, dtype, cin, d_w, cout, d_out, &p);
   if (rc || g->n_voxels == 0) return rc;
   if (p == IGC_PATH_LEAF) return launch_conv_leaf(g, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream);
+  if (p == IGC_PATH_GATHER)
+    return launch_conv_gather(g, d_map, g->n_voxels, g->n_voxels, d_feats, dtype, cin, d_w, cout, d_out,
+                              (hipStream_t)stream);
   if (p == IGC_PATH_MIXED) {
     // Per-leaf dispatch: leaves with at least dense_min active voxels on the leaf window, the
     // rest on gather-GEMM-scatter (which writes zeros into the dense leaves' rows first).
@@ -457,7 +465,7 @@ int igc_sparse_conv_backward(const igc_grid* g, const int32_t* d_map, const void
     return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_backward: bad dtype");
   if (cin < 1 || cout < 1)
     return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_backward: cin and cout must be positive");
-  if (path != IGC_PATH_AUTO && path != IGC_PATH_LEAF && path != IGC_PATH_GGS)
+  if (path != IGC_PATH_AUTO && path != IGC_PATH_LEAF && path != IGC_PATH_GGS && path != IGC_PATH_GATHER)
     return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_backward: bad path");
   if (!d_w) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_backward: d_w is null");
   if (g->n_voxels > 0 && (!d_map || !d_dout || (d_dw && !d_feats)))
@@ -475,6 +483,9 @@ int igc_sparse_conv_backward(const igc_grid* g, const int32_t* d_map, const void
     if (p == IGC_PATH_GGS && !ggs_conv_supported(dtype, cout, cin))
       return set_error(IGC_ERR_UNSUPPORTED,
                        "igc_sparse_conv_backward: gather-GEMM-scatter path does not support the input-gradient shape");
+    if (p == IGC_PATH_GATHER && !gather_conv_supported(dtype, cout, cin))
+      return set_error(IGC_ERR_UNSUPPORTED,
+                       "igc_sparse_conv_backward: general-shape path does not support the input-gradient shape");
   }
   if (d_dw && !wgrad_supported(dtype, cin, cout))
     return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv_backward: weight gradient does not support this dtype / cin / cout");
@@ -572,12 +583,15 @@ int igc_sparse_conv_between(const igc_grid* out, const int32_t* d_map, int64_t n
   if (cin < 1 || cout < 1 || n_in < 0)
     return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_between: cin, cout must be positive and n_in >= 0");
   if (!d_w) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_between: d_w is null");
-  if (!ggs_conv_supported(dtype, cin, cout))
-    return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv_between: gather-GEMM-scatter path does not support this dtype / cin / cout");
+  const bool ggs = ggs_conv_supported(dtype, cin, cout);
+  if (!ggs && !gather_conv_supported(dtype, cin, cout))
+    return set_error(IGC_ERR_UNSUPPORTED, "igc_sparse_conv_between: no path supports this dtype / cin / cout");
   if (out->n_voxels > 0 && (!d_map || !d_out || (n_in > 0 && !d_feats)))
     return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_between: d_map, d_feats or d_out is null");
   if (d_feats && d_feats == d_out) return set_error(IGC_ERR_INVALID_ARG, "igc_sparse_conv_between: d_out aliases d_feats");
   if (out->n_voxels == 0) return IGC_OK;
+  if (!ggs)
+    return launch_conv_gather(out, d_map, out->n_voxels, n_in, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream);
   return launch_conv_ggs(out, d_map, d_feats, dtype, cin, d_w, cout, d_out, (hipStream_t)stream, 0, n_in);
 }
 

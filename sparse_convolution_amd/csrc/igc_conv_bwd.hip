@@ -22,6 +22,9 @@
 //    leaf path's shapes, otherwise plain fp32 FMAs over 64-row stages in LDS.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+#include <cstring>
+
 #include "igc_host.h"
 #include "igc_internal.h"
 #include "igc_wave.h"
@@ -233,52 +236,6 @@ __global__ __launch_bounds__(64 * NWV) void k_wgrad_bf16(const int32_t* __restri
       }
 }
 
-// Partial dW per (offset, chunk of rows), fp32 data with cin, cout <= 64 and cin * cout <= 1024.
-__global__ __launch_bounds__(256) void k_wgrad_f32(const int32_t* __restrict__ map, int64_t N,
-                                                   const float* __restrict__ feats, const float* __restrict__ dout,
-                                                   int cin, int cout, int64_t rows_per_chunk,
-                                                   float* __restrict__ part) {
-  __shared__ float s_x[kStage * 64];
-  __shared__ float s_d[kStage * 64];
-  const int tid = threadIdx.x;
-  const int o = (int)(blockIdx.x % kNOff);
-  const int64_t chunk = blockIdx.x / kNOff;
-  const int64_t r0 = chunk * rows_per_chunk;
-  const int64_t r1 = r0 + rows_per_chunk < N ? r0 + rows_per_chunk : N;
-  const int E = cin * cout;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t base = r0; base < r1; base += kStage) {
-    __syncthreads();
-    for (int i = tid; i < kStage * cin; i += 256) {
-      const int k = i / cin, c = i - k * cin;
-      const int64_t r = base + k;
-      const int32_t src = r < r1 ? map[(size_t)o * (size_t)N + r] : -1;
-      s_x[i] = src >= 0 ? feats[(size_t)src * cin + c] : 0.f;
-    }
-    for (int i = tid; i < kStage * cout; i += 256) {
-      const int k = i / cout, c = i - k * cout;
-      const int64_t r = base + k;
-      s_d[i] = r < r1 ? dout[(size_t)r * cout + c] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = tid + 256 * j;
-      if (e < E) {
-        const int ci = e / cout, co = e - ci * cout;
-        float sum = 0.f;
-        for (int k = 0; k < kStage; ++k) sum = fmaf(s_x[k * cin + ci], s_d[k * cout + co], sum);
-        acc[j] += sum;
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = tid + 256 * j;
-    if (e < E) part[((size_t)chunk * kNOff + o) * E + e] = acc[j];
-  }
-}
-
 // dw[e] = sum over chunks c of part[c * E + e], in fp64 and in a fixed order: thread group q
 // of NG adds the chunks c = q, q + NG, ... in increasing order, then the NG group sums are added
 // in order of q. A workgroup covers 256 / NG consecutive elements.
@@ -304,6 +261,8 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ 
   }
 }
 
+}  // namespace
+
 int launch_wgrad_reduce(const float* part, int64_t chunks, int64_t E, float* dw, hipStream_t s) {
   // Few elements and many chunks: more threads per element.
   if (E >= 65536 || chunks <= 64)
@@ -313,6 +272,8 @@ int launch_wgrad_reduce(const float* part, int64_t chunks, int64_t E, float* dw,
   IGC_HIP(hipGetLastError(), "igc_sparse_conv_backward: weight-gradient reduction launch");
   return IGC_OK;
 }
+
+namespace {
 
 template <int MB, int NB, int NWV>
 int launch_wgrad_bf16(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t cin,
@@ -368,21 +329,9 @@ int launch_wgrad_f32(const igc_grid* g, const int32_t* d_map, const void* d_feat
     ws_release(&wsb, s);
     return rc;
   }
-  const int64_t N = g->n_voxels;
-  int64_t chunks = 2048 / kNOff;
-  int64_t rpc = (N + chunks - 1) / chunks;
-  rpc = (rpc + kStage - 1) / kStage * kStage;
-  chunks = (N + rpc - 1) / rpc;
-  Workspace wsb;
-  int rc = ws_acquire(&wsb, (size_t)chunks * E * 4, s, "igc_sparse_conv_backward: wgrad partials", grid_alloc(g));
-  if (rc) return rc;
-  float* part = (float*)wsb.p;
-  k_wgrad_f32<<<(unsigned)(kNOff * chunks), 256, 0, s>>>(d_map, N, (const float*)d_feats, (const float*)d_dout, cin,
-                                                        cout, rpc, part);
-  hipError_t e = hipGetLastError();
-  rc = e != hipSuccess ? hip_status(e, "igc_sparse_conv_backward: wgrad launch") : launch_wgrad_reduce(part, chunks, E, d_dw, s);
-  ws_release(&wsb, s);
-  return rc;
+  // Row chunks on the general-shape kernel (4 x 4 register blocks): 55.7 ms against 387 ms for
+  // one workgroup per (offset, chunk) with a thread per weight, fp32 32 -> 32 on the band scene.
+  return launch_wgrad_gather(g, d_map, d_feats, IGC_F32, cin, d_dout, cout, d_dw, s);
 }
 
 __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
@@ -400,6 +349,10 @@ int fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
 }
 
 bool wgrad_supported(int32_t dtype, int32_t cin, int32_t cout) {
+  return wgrad_tuned_supported(dtype, cin, cout) || gather_conv_supported(dtype, cin, cout);
+}
+
+bool wgrad_tuned_supported(int32_t dtype, int32_t cin, int32_t cout) {
   if (dtype == IGC_BF16) return cin >= 32 && cin % 32 == 0 && cin <= 1024 && cout >= 64 && cout % 64 == 0 && cout <= 1024;
   return dtype == IGC_F32 && cin >= 1 && cout >= 1 && cin <= 64 && cout <= 64 && cin * cout <= 1024;
 }
@@ -423,12 +376,19 @@ int launch_conv_backward(const igc_grid* g, const int32_t* d_map, const void* d_
       return hip_status(e, "igc_sparse_conv_backward: weight flip launch");
     }
     // dX = forward conv of dY (cout channels) with W~ (cout -> cin).
-    rc = dgrad_path == IGC_PATH_LEAF ? launch_conv_leaf(g, d_dout, dtype, cout, wf, cin, d_dfeats, s)
-                                     : launch_conv_ggs(g, d_map, d_dout, dtype, cout, wf, cin, d_dfeats, s);
+    rc = dgrad_path == IGC_PATH_LEAF     ? launch_conv_leaf(g, d_dout, dtype, cout, wf, cin, d_dfeats, s)
+         : dgrad_path == IGC_PATH_GATHER ? launch_conv_gather(g, d_map, g->n_voxels, g->n_voxels, d_dout, dtype, cout,
+                                                              wf, cin, d_dfeats, s)
+                                         : launch_conv_ggs(g, d_map, d_dout, dtype, cout, wf, cin, d_dfeats, s);
     dev_free(wf, wf_bytes, s, grid_alloc(g));
     if (rc) return rc;
   }
   if (d_dw) {
+    // Shapes the tuned kernels do not take run on the general-shape kernel (IGC_TEST_WGRAD_FORM =
+    // "general" sends every shape there: tests and measurements).
+    const char* form = std::getenv("IGC_TEST_WGRAD_FORM");
+    if (!wgrad_tuned_supported(dtype, cin, cout) || (form && !std::strcmp(form, "general")))
+      return launch_wgrad_gather(g, d_map, d_feats, dtype, cin, d_dout, cout, d_dw, s);
     if (dtype == IGC_BF16) {
       // 128 x 256 blocks on 8 waves (85 FLOP per staged byte instead of 64) measured slower on
       // the large workload (222 ms against 214): staging is not bound by the L2 feed.

@@ -124,6 +124,19 @@ int launch_kernel_map(const igc_grid* g, const int32_t* h_offsets, int32_t K, in
                       hipStream_t s);
 bool leaf_conv_supported(int32_t dtype, int32_t cin, int32_t cout);
 bool ggs_conv_supported(int32_t dtype, int32_t cin, int32_t cout);
+// General-shape path (any channel counts up to kGatherMaxChannels, fp32 or bf16).
+constexpr int32_t kGatherMaxChannels = 4096;
+bool gather_conv_supported(int32_t dtype, int32_t cin, int32_t cout);
+// d_map int32[27, N]; entries outside [0, n_in) read as absent. scratch (may be null): at least
+// gather_scratch_bytes() of device memory used instead of a workspace from g's allocator.
+int launch_conv_gather(const igc_grid* g, const int32_t* d_map, int64_t N, int64_t n_in, const void* d_feats,
+                       int32_t dtype, int32_t cin, const void* d_w, int32_t cout, void* d_out, hipStream_t s,
+                       void* scratch = nullptr);
+size_t gather_scratch_bytes(int32_t cin, int32_t cout);
+int launch_wgrad_gather(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype, int32_t cin,
+                        const void* d_dout, int32_t cout, float* d_dw, hipStream_t s);
+// dw[e] = sum over c < chunks of part[c * E + e] in fp64, in a fixed order (weight gradients).
+int launch_wgrad_reduce(const float* part, int64_t chunks, int64_t E, float* dw, hipStream_t s);
 
 // Row order of the gather-GEMM-scatter plan for one layer: rows sorted by neighbour mask within
 // spans of `span` rows (256, 1024 or 4096), key bit order 0 = natural, 1 = class (corners,
@@ -165,6 +178,7 @@ int launch_conv_map(const igc_grid* in, const igc_grid* out, const int32_t* stri
 // Fills n 32-bit words with v on stream s (a kernel, so it can sit in captured work).
 int fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 bool wgrad_supported(int32_t dtype, int32_t cin, int32_t cout);
+bool wgrad_tuned_supported(int32_t dtype, int32_t cin, int32_t cout);
 int launch_conv_backward(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype, int32_t cin,
                          const void* d_w, int32_t cout, const void* d_dout, void* d_dfeats, float* d_dw,
                          int32_t dgrad_path, hipStream_t s);

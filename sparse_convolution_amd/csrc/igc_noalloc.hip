@@ -1,7 +1,7 @@
 // igc_sparse_conv_noalloc: igc_sparse_conv for callers that cannot allocate device memory
 // (code under HIP graph capture, tight serving loops, harnesses that forbid it). The kernels'
-// temporaries (transposed weights, the mask-sorted tile plan of the gather-GEMM-scatter path,
-// per-leaf dispatch flags) live in one file-scope device array of fixed size instead of a
+// temporaries (transposed or packed weights, the mask-sorted tile plan of the gather-GEMM-scatter
+// path, per-leaf dispatch flags) live in one file-scope device array of fixed size instead of a
 // workspace; every other step is the one igc_sparse_conv runs, on the same kernels.
 #include <hip/hip_runtime.h>
 
@@ -56,6 +56,7 @@ extern "C" int igc_sparse_conv_noalloc(const igc_grid* g, const int32_t* d_map, 
   if (rc || g->n_voxels == 0) return rc;
   const uint32_t dense_min = p == IGC_PATH_MIXED ? mixed_dense_rows(cin) : 0u;
   size_t need = 0;
+  if (p == IGC_PATH_GATHER) need = gather_scratch_bytes(cin, cout);
   if (p == IGC_PATH_LEAF || p == IGC_PATH_MIXED) need = leaf_scratch_bytes(dtype, cin, cout);
   if (p == IGC_PATH_GGS || p == IGC_PATH_MIXED)
     need = std::max(need, ggs_scratch_bytes(g->n_voxels, cin, cout, dense_min != 0));
@@ -66,6 +67,8 @@ extern "C" int igc_sparse_conv_noalloc(const igc_grid* g, const int32_t* d_map, 
   void* sp = nullptr;
   if (need > 0 && (rc = scratch_address(&sp, fn))) return rc;
   hipStream_t s = (hipStream_t)stream;
+  if (p == IGC_PATH_GATHER)
+    return launch_conv_gather(g, d_map, g->n_voxels, g->n_voxels, d_feats, dtype, cin, d_w, cout, d_out, s, sp);
   if (p == IGC_PATH_LEAF) return launch_conv_leaf(g, d_feats, dtype, cin, d_w, cout, d_out, s, 0, sp);
   if (p == IGC_PATH_MIXED) {
     // The two launches run in stream order, so the leaf pass may reuse the scratch after the

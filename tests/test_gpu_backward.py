@@ -203,10 +203,17 @@ def test_unsupported_shapes_raise():
     dyb = torch.randn(n, 64, device="cuda").bfloat16()
     with pytest.raises(igc.IgcError):  # dgrad 64 -> 32 is not a gather-GEMM-scatter shape
         igc.sparse_conv_backward(g, fb, wb, dyb, m, path="ggs")
+    # The fp32 weight gradient beyond 64 x 64 channels runs on the general-shape kernel.
     f = torch.randn(n, 96, device="cuda")
     w = torch.randn(27, 96, 96, device="cuda")
-    with pytest.raises(igc.IgcError):  # fp32 weight gradient beyond 64 x 64 channels
-        igc.sparse_conv_backward(g, f, w, torch.randn(n, 96, device="cuda"), m, need_dfeats=False)
+    dy = torch.randn(n, 96, device="cuda")
+    _, dw = igc.sparse_conv_backward(g, f, w, dy, m, need_dfeats=False)
+    torch.cuda.synchronize()
+    r = oracle.conv_wgrad(m.cpu().numpy(), f.cpu().numpy(), dy.cpu().numpy())
+    assert normwise_error(dw.cpu().numpy(), r) <= WGRAD_TOL
+    with pytest.raises(igc.IgcError):  # beyond the general-shape path's 4096 channels
+        igc.sparse_conv_backward(g, torch.zeros((n, 4100), device="cuda"), torch.zeros((27, 4100, 4), device="cuda"),
+                                 torch.zeros((n, 4), device="cuda"), m, need_dfeats=False)
 
 
 def test_centre_identity_gradient():

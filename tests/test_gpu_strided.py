@@ -122,10 +122,17 @@ def test_edge_cases():
     big = igc.grid_build(to_dev(np.array([[2 ** 30, 0, 0]], np.int32)))
     with pytest.raises(igc.IgcError):
         igc.conv_grid(big, 3, True)  # 3 * 2^30 leaves the int32 range
+    # fp32 is not a gather-GEMM-scatter dtype: it runs on the general-shape path.
     f = torch.randn(one.n_voxels, 16, device="cuda")
     w = torch.randn(27, 16, 16, device="cuda")
-    with pytest.raises(igc.IgcError):  # fp32 is not a gather-GEMM-scatter dtype
-        igc.sparse_conv_between(down, f, w, igc.conv_map(one, down, 2))
+    mo = igc.conv_map(one, down, 2)
+    y = igc.sparse_conv_between(down, f, w, mo)
+    torch.cuda.synchronize()
+    r = oracle.conv(mo.cpu().numpy(), f.cpu().numpy(), w.cpu().numpy())
+    assert normwise_error(y.cpu().numpy(), r) <= 1e-5
+    with pytest.raises(igc.IgcError):  # beyond 4096 channels
+        igc.sparse_conv_between(down, torch.zeros((one.n_voxels, 4100), device="cuda"),
+                                torch.zeros((27, 4100, 4), device="cuda"), mo)
 
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
