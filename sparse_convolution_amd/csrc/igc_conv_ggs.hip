@@ -292,8 +292,9 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
   __shared__ uint4 s_st4[NST > 4 ? STAGE_BYTES / 16 : 1];
   __shared__ uint4 s_st5[NST > 5 ? STAGE_BYTES / 16 : 1];
   __shared__ int32_t s_perm[kBM];
-  __shared__ int32_t s_map[kNOff][kBM];
+  __shared__ __align__(16) int32_t s_map[kNOff][kBM];
   __shared__ uint16_t s_blk[kNOff];
+  __shared__ uint16_t s_blku[kNOff];  // s_blk of the u-th used offset
   __shared__ uint8_t s_olist[kNOff];
   __shared__ int s_nused;
   __shared__ uint32_t s_used;
@@ -314,6 +315,7 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
     uint32_t u = 0;
     for (int o = 0; o < kNOff; ++o)
       if (s_blk[o]) {
+        s_blku[n] = s_blk[o];
         s_olist[n++] = (uint8_t)o;
         u |= 1u << o;
       }
@@ -325,6 +327,13 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
   // The tile's kernel-map entries of every used offset, in sorted-row order, go to LDS once:
   // all loads are issued before the first wait, so the map's latency is paid once per tile.
   // An entry outside [0, n_in) is stored as -1 (absent): the gather never leaves the input.
+  // Layout: row u holds the u-th used offset, and the AI entries one lane gathers per chunk
+  // (rows (w*AI + q)*RPI + l, q < AI) are adjacent, so one vector read fetches them.
+  constexpr int RPI_ = 64 / (KC / 8), AI_ = kBM / RPI_ / NWV;
+  auto mslot = [&](int row) {
+    const int w = row / (AI_ * RPI_), rem = row % (AI_ * RPI_);
+    return (w * RPI_ + rem % RPI_) * AI_ + rem / RPI_;
+  };
   {
     // kBM rows x 27 offsets over NT threads: thread t takes row t % kBM and every
     // (NT / kBM)-th offset starting at t / kBM.
@@ -340,10 +349,14 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
       const int o = o0 + OSTEP * i;
       v[i] = (o < kNOff && ((used >> o) & 1u)) ? map[(size_t)o * (size_t)N + myrow] : map[0];
     }
+    const uint32_t listed = s_used;
+    const int slot = mslot(row);
 #pragma unroll
     for (int i = 0; i < OPT; ++i) {
       const int o = o0 + OSTEP * i;
-      if (o < kNOff) s_map[o][row] = ((used >> o) & 1u) && (uint64_t)(int64_t)v[i] < (uint64_t)n_in ? v[i] : -1;
+      if (o < kNOff && ((listed >> o) & 1u))
+        s_map[__popc(listed & ((1u << o) - 1u))][slot] =
+            ((used >> o) & 1u) && (uint64_t)(int64_t)v[i] < (uint64_t)n_in ? v[i] : -1;
     }
   }
   __syncthreads();
@@ -355,13 +368,42 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
   // holds the row's granule (lane%SEG) ^ swz (the swizzle is the same for every q).
   const int gran = (lane % SEG) ^ ((lane >> 3) & (SEG - 1));
   const uint16_t* bptr = wt + (size_t)(n0 + wave * BI * RPI + lane / SEG) * cin + gran * 8;
-  auto issue = [&](int c, uint4* st) {
-    const int o = s_olist[c / ksl];
-    const int kc = (c % ksl) * KC;
+  // What one chunk's loads need from LDS (its offset, channel slice and this lane's map entries),
+  // read one chunk ahead: the reads are in flight while the current chunk is multiplied, so the
+  // loads are issued without waiting on LDS.
+  struct Pend {
+    int o, kc;
+    int32_t src[AI];
+  };
+  const uint16_t* const zrow = g_zero_row + gran * 8;
+  static_assert(RPI_ == RPI && AI_ == AI && (AI == 2 || AI == 4), "map slots");
+  typedef int32_t i32xAI __attribute__((ext_vector_type(AI)));
+  // The chunks in order, as (u-th used offset, channel slice k): the fetch stream walks them one
+  // by one, keeping its offset as the lowest bit of the not yet passed used offsets (scalar
+  // registers, no LDS read and no division per chunk).
+  const int nused = s_nused;
+  uint32_t f_mask = __builtin_amdgcn_readfirstlane(s_used);
+  int f_u = 0, f_k = 0;
+  auto fetch_next = [&]() {
+    Pend p;
+    const int u = f_u < nused ? f_u : (nused > 0 ? nused - 1 : 0);  // past the end: never issued
+    p.o = f_mask ? __builtin_ctz(f_mask) : 0;
+    p.kc = f_k * KC;
+    const i32xAI src = *(const i32xAI*)&s_map[u][(wave * RPI + lane / SEG) * AI];
+#pragma unroll
+    for (int q = 0; q < AI; ++q) p.src[q] = src[q];
+    if (++f_k == ksl) {
+      f_k = 0;
+      ++f_u;
+      f_mask &= f_mask - 1u;
+    }
+    return p;
+  };
+  auto issue = [&](const Pend& p, uint4* st) {
+    const int o = p.o, kc = p.kc;
 #pragma unroll
     for (int q = 0; q < AI; ++q) {
-      const int32_t src = s_map[o][(wave * AI + q) * RPI + lane / SEG];
-      const uint16_t* ap = src >= 0 ? feats + (size_t)src * cin + kc + gran * 8 : g_zero_row + kc + gran * 8;
+      const uint16_t* ap = (p.src[q] >= 0 ? feats + (size_t)p.src[q] * cin + gran * 8 : zrow) + kc;
       __builtin_amdgcn_global_load_lds((const glb_void*)ap, (lds_void*)(st + (wave * AI + q) * 64), 16, 0, 0);
     }
     const uint16_t* bsrc = bptr + (size_t)o * cout * cin + kc;
@@ -379,9 +421,18 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
 
   const int frow = lane & 15;
   const int fsw = stage_swz<SEG>(frow);  // row bases are multiples of 16
-  auto compute = [&](int c, const uint4* st) {
-    const uint32_t vm = __builtin_amdgcn_readfirstlane(((uint32_t)s_blk[s_olist[c / ksl]] >> (wm * MI)) &
-                                                       ((1u << MI) - 1u));
+  // The compute stream's position (the chunk after the one being multiplied) and that chunk's
+  // 16-row block bits at its offset (all of the tile's; each wave uses its own).
+  int v_u = 0, v_k = 0;
+  auto blocks_next = [&]() -> uint32_t {
+    if (++v_k == ksl) {
+      v_k = 0;
+      ++v_u;
+    }
+    return v_u < nused ? (uint32_t)s_blku[v_u] : 0u;
+  };
+  // Multiplies chunk c (this wave's blocks vm) from stage st.
+  auto compute = [&](uint32_t vm, const uint4* st) {
     const char* A = (const char*)st;
     const char* B = A + A_BYTES;
     constexpr int KST = KC / 32;
@@ -445,9 +496,15 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
   };
   // One chunk: start filling the stage freed by the previous chunk with chunk c+NST-1,
   // multiply chunk c, wait for chunk c+1 and meet the other waves.
+  // pend: the LDS reads of chunk c+NST-1 (read during the previous chunk); vcur: chunk c's blocks.
+  Pend pend;
+  uint32_t vcur = 0;
   auto step = [&](int c, const uint4* cur, uint4* fill) {
-    if (c + NST - 1 < nchunks) issue(c + NST - 1, fill);
-    compute(c, cur);
+    const uint32_t vm = __builtin_amdgcn_readfirstlane((vcur >> (wm * MI)) & ((1u << MI) - 1u));
+    if (c + NST - 1 < nchunks) issue(pend, fill);
+    pend = fetch_next();  // chunk c + NST
+    vcur = blocks_next();  // chunk c + 1
+    compute(vm, cur);
     const int last = (c + NST - 1 < nchunks ? c + NST - 1 : nchunks - 1);
     wait_next(last - (c + 1));
     __syncthreads();
@@ -455,8 +512,12 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
 
   // Prologue: chunks 0 .. NST-2 in flight, wait for chunk 0.
 #pragma unroll
-  for (int q = 0; q < NST - 1; ++q)
-    if (q < nchunks) issue(q, stage(q));
+  for (int q = 0; q < NST - 1; ++q) {
+    const Pend p = fetch_next();  // chunk q
+    if (q < nchunks) issue(p, stage(q));
+  }
+  pend = fetch_next();  // chunk NST - 1
+  vcur = nused > 0 ? (uint32_t)s_blku[0] : 0u;
   wait_next((nchunks < NST - 1 ? nchunks : NST - 1) - 1);
   __syncthreads();
   // Chunk c is in stage c % NST; the stage it fills is the one chunk c-1 used.
