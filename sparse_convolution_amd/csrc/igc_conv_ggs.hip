@@ -38,6 +38,8 @@
 // output rows gather neighbouring input rows, and those stay in one L2.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "igc_host.h"
 #include "igc_internal.h"
 #include "igc_wave.h"
@@ -89,25 +91,30 @@ __global__ void k_transpose_w(const uint16_t* __restrict__ w, uint16_t* __restri
 // the padding past N) sort last. A map entry counts as a neighbour when it lies in [0, n_in).
 // Rows with skip[row] != 0 (per-leaf dispatch: another path writes them) count as having none.
 //
-// One workgroup per span, min(SPAN, 1024) threads, SPAN / threads keys per thread in
-// registers (position q * threads + t): a bitonic network whose compare-exchanges at a stride
-// of at least the thread count stay in registers, below 64 go through wave shuffles, and the
-// rest through LDS.
+// One workgroup of 256 threads per span, K = SPAN / 256 keys per thread in registers. Spans of
+// 1024 and 4096 rows sort with every compare-exchange between two registers of one thread: a
+// layout keeps RB = log2(K) consecutive bits [lo, lo + RB) of a key's position in the register
+// number and the other bits in the thread number, and moves to the group of bits the next
+// stages need by writing every key to LDS at its position and reading the new layout back
+// (22 such moves for 4096 rows, in place of 57 cross-lane and 18 LDS stages). Spans of 256
+// rows (one key per thread) exchange across lanes and through LDS. Then each 16-row block's
+// masks are OR-reduced across its lanes and lane o < 27 sets offset o's bits of four blocks.
 struct BitOrder {
   uint8_t o[kNOff];  // o[i]: offset at key bit 26 - i
 };
 
 template <int SPAN>
-__global__ __launch_bounds__(SPAN < 1024 ? SPAN : 1024) void k_ggs_plan(const int32_t* __restrict__ map, int64_t N,
-                                                                       int64_t n_in, int32_t* __restrict__ perm,
-                                                                       int64_t n_pos, uint16_t* __restrict__ blk,
-                                                                       const uint8_t* __restrict__ skip, BitOrder bo) {
-  constexpr int T = SPAN < 1024 ? SPAN : 1024;
+__global__ __launch_bounds__(256) void k_ggs_plan(const int32_t* __restrict__ map, int64_t N, int64_t n_in,
+                                                 int32_t* __restrict__ perm, int64_t n_pos,
+                                                 uint16_t* __restrict__ blk, const uint8_t* __restrict__ skip,
+                                                 BitOrder bo) {
+  constexpr int T = 256, TB = 8;
   constexpr int K = SPAN / T;
+  constexpr int RB = K == 16 ? 4 : K == 4 ? 2 : 0;
   constexpr int LB = SPAN == 256 ? 8 : SPAN == 1024 ? 10 : 12;
   constexpr int NT = SPAN / kBM;  // tiles per span
   static_assert(SPAN == 256 || SPAN == 1024 || SPAN == 4096, "span");
-  __shared__ uint64_t s_x[SPAN];
+  __shared__ uint64_t s_x[SPAN + SPAN / 32];
   __shared__ uint32_t s_mask[SPAN];
   __shared__ uint32_t s_blk[NT][kNOff];
   const int t = threadIdx.x;
@@ -115,8 +122,9 @@ __global__ __launch_bounds__(SPAN < 1024 ? SPAN : 1024) void k_ggs_plan(const in
   const int64_t base = (int64_t)blockIdx.x * SPAN;
   for (int x = t; x < NT * kNOff; x += T) (&s_blk[0][0])[x] = 0u;
 
-  uint64_t key[K];
-#pragma unroll
+  // Masks of local rows q * T + t (coalesced map reads; the loop is not unrolled so that only
+  // one row's 27 loads hold registers), then key q of thread t from its own masks.
+#pragma unroll 1
   for (int q = 0; q < K; ++q) {
     const int local = q * T + t;
     const int64_t row = base + local;
@@ -129,47 +137,77 @@ __global__ __launch_bounds__(SPAN < 1024 ? SPAN : 1024) void k_ggs_plan(const in
       for (int o = 0; o < kNOff; ++o) mask |= ((uint64_t)(int64_t)v[o] < (uint64_t)n_in ? 1u : 0u) << o;
     }
     s_mask[local] = mask;
+  }
+  uint64_t key[K];
+#pragma unroll
+  for (int q = 0; q < K; ++q) {
+    const int local = q * T + t;
+    const uint32_t mask = s_mask[local];
     uint64_t pk = 0;
 #pragma unroll
     for (int b = 0; b < kNOff; ++b) pk |= (uint64_t)((~mask >> bo.o[b]) & 1u) << (kNOff - 1 - b);
     key[q] = (pk << LB) | (uint64_t)local;
   }
 
-  for (int k = 2; k <= SPAN; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j >= T) {  // partner in this thread's registers
-        const int qj = j / T;
-#pragma unroll
-        for (int q = 0; q < K; ++q) {
-          if (q & qj) continue;
-          const bool asc = ((q * T + t) & k) == 0;
-          const uint64_t a = key[q], b = key[q | qj];
-          const bool sw = (a > b) == asc;
-          key[q] = sw ? b : a;
-          key[q | qj] = sw ? a : b;
-        }
-      } else {
-        uint64_t other[K];
+  if constexpr (K == 1) {
+    for (int k = 2; k <= SPAN; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        uint64_t other;
         if (j < 64) {
-#pragma unroll
-          for (int q = 0; q < K; ++q) other[q] = shfl_xor64(key[q], j);
+          other = shfl_xor64(key[0], j);
         } else {
           __syncthreads();
-#pragma unroll
-          for (int q = 0; q < K; ++q) s_x[q * T + t] = key[q];
+          s_x[t] = key[0];
           __syncthreads();
-#pragma unroll
-          for (int q = 0; q < K; ++q) other[q] = s_x[(q * T + t) ^ j];
+          other = s_x[t ^ j];
         }
+        const bool asc = (t & k) == 0, lower = (t & j) == 0;
+        const uint64_t a = key[0];
+        key[0] = (lower == asc) ? (a < other ? a : other) : (a < other ? other : a);
+      }
+    }
+  } else {
+    // Position of key q of thread t in layout lo: bits [lo, lo + RB) from q, the rest from t.
+    auto slot = [](int p) { return p + (p >> 5); };  // one spare word per 32 keys against bank conflicts
+    auto tpart = [&](int l) { return (t & ((1 << l) - 1)) | ((t >> l) << (l + RB)); };
+    int lo = TB;  // the load's layout: position q * T + t
+    auto remap = [&](int nlo) {
+      const int tp = tpart(lo);
+      __syncthreads();
 #pragma unroll
-        for (int q = 0; q < K; ++q) {
-          const int p = q * T + t;
-          const bool asc = (p & k) == 0, lower = (p & j) == 0;
-          const uint64_t a = key[q], b = other[q];
-          key[q] = (lower == asc) ? (a < b ? a : b) : (a < b ? b : a);
+      for (int q = 0; q < K; ++q) s_x[slot(tp | (q << lo))] = key[q];
+      __syncthreads();
+      const int tn = tpart(nlo);
+#pragma unroll
+      for (int q = 0; q < K; ++q) key[q] = s_x[slot(tn | (q << nlo))];
+      lo = nlo;
+    };
+    for (int k = 2; k <= SPAN; k <<= 1) {
+      for (int b = __builtin_ctz(k) - 1; b >= 0; --b) {
+        if (b < lo || b >= lo + RB) remap(b - RB + 1 > 0 ? b - RB + 1 : 0);
+        const int tp = tpart(lo);
+        // Partners differ in register bit d = b - lo (a compile-time stride per case).
+        auto cx = [&](auto dc) {
+          constexpr int qb = 1 << decltype(dc)::value;
+#pragma unroll
+          for (int q = 0; q < K; ++q) {
+            if (q & qb) continue;
+            const bool asc = ((tp | (q << lo)) & k) == 0;
+            const uint64_t x = key[q], y = key[q | qb];
+            const bool sw = (x > y) == asc;
+            key[q] = sw ? y : x;
+            key[q | qb] = sw ? x : y;
+          }
+        };
+        switch (b - lo) {
+          case 0: cx(std::integral_constant<int, 0>{}); break;
+          case 1: cx(std::integral_constant<int, 1>{}); break;
+          case 2: if constexpr (RB > 2) cx(std::integral_constant<int, (RB > 2 ? 2 : 0)>{}); break;
+          default: if constexpr (RB > 3) cx(std::integral_constant<int, (RB > 3 ? 3 : 0)>{}); break;
         }
       }
     }
+    if (lo != TB) remap(TB);
   }
 
   // Sorted position p = q * T + t: its row, and its tile's block bits (a wave holds 64
@@ -181,16 +219,18 @@ __global__ __launch_bounds__(SPAN < 1024 ? SPAN : 1024) void k_ggs_plan(const in
     const int local = (int)(key[q] & (uint64_t)(SPAN - 1));
     const int64_t row = base + local;
     if (base + p < n_pos) perm[base + p] = row < N ? (int32_t)row : -1;
-    const uint32_t m = s_mask[local];
+    uint32_t m = s_mask[local];
+    m |= (uint32_t)__shfl_xor((int)m, 1);
+    m |= (uint32_t)__shfl_xor((int)m, 2);
+    m |= (uint32_t)__shfl_xor((int)m, 4);
+    m |= (uint32_t)__shfl_xor((int)m, 8);
+    const uint32_t g0 = __builtin_amdgcn_readlane(m, 0), g1 = __builtin_amdgcn_readlane(m, 16);
+    const uint32_t g2 = __builtin_amdgcn_readlane(m, 32), g3 = __builtin_amdgcn_readlane(m, 48);
     const int tl = p / kBM, quarter = (p % kBM) / 64;
-    for (int o = 0; o < kNOff; ++o) {
-      const uint64_t bb = __ballot((m >> o) & 1u);
-      if (lane == 0 && bb) {
-        uint32_t bits = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) bits |= ((bb >> (16 * b)) & 0xFFFFull) ? (1u << b) : 0u;
-        atomicOr(&s_blk[tl][o], bits << (4 * quarter));
-      }
+    if (lane < kNOff) {
+      const uint32_t bits = ((g0 >> lane) & 1u) | (((g1 >> lane) & 1u) << 1) | (((g2 >> lane) & 1u) << 2) |
+                            (((g3 >> lane) & 1u) << 3);
+      if (bits) atomicOr(&s_blk[tl][lane], bits << (4 * quarter));
     }
   }
   __syncthreads();
@@ -224,9 +264,9 @@ hipError_t launch_plan(int span, int order, const int32_t* map, int64_t N, int64
   if (n_pos == 0) return hipSuccess;
   const BitOrder bo = bit_order(order);
   if (span == 4096)
-    k_ggs_plan<4096><<<(unsigned)((N + 4095) / 4096), 1024, 0, s>>>(map, N, n_in, perm, n_pos, blk, skip, bo);
+    k_ggs_plan<4096><<<(unsigned)((N + 4095) / 4096), 256, 0, s>>>(map, N, n_in, perm, n_pos, blk, skip, bo);
   else if (span == 1024)
-    k_ggs_plan<1024><<<(unsigned)((N + 1023) / 1024), 1024, 0, s>>>(map, N, n_in, perm, n_pos, blk, skip, bo);
+    k_ggs_plan<1024><<<(unsigned)((N + 1023) / 1024), 256, 0, s>>>(map, N, n_in, perm, n_pos, blk, skip, bo);
   else
     k_ggs_plan<256><<<(unsigned)((N + 255) / 256), 256, 0, s>>>(map, N, n_in, perm, n_pos, blk, skip, bo);
   return hipGetLastError();
