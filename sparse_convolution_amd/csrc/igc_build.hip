@@ -1885,6 +1885,7 @@ __global__ __launch_bounds__(256) void k_derive_records(const LeafRec* __restric
     }
   }
   const int l = lane & 7, yi = lane >> 3, yj = lane & 7;
+  uint64_t last_tile = kEmptyKey;  // lane 0: the root tile inserted last
   // Slots out of reach stay empty records (lanes 0 .. S-1 write their origins).
   if (lane < S) {
     const int qi = lane / (dv.L[1] * dv.L[2]), qj = (lane / dv.L[2]) % dv.L[1], qk = lane % dv.L[2];
@@ -1930,8 +1931,13 @@ __global__ __launch_bounds__(256) void k_derive_records(const LeafRec* __restric
                                     ok ? 1 : 0);
           rec_origin[w] = ok ? yo : make_int4(0, 0, 0, 0);
           if (ok) {
-            insert_tile(root_keys, root_mask, root_mask + 1u, tile_key(yo.x, yo.y, yo.z), st, tile_list,
-                        (uint32_t)kSmallSort);
+            // The slots of one input leaf nearly always share a root tile: insert a key once
+            // per run of equal keys (inserting a present key changes nothing).
+            const uint64_t tk = tile_key(yo.x, yo.y, yo.z);
+            if (tk != last_tile) {
+              insert_tile(root_keys, root_mask, root_mask + 1u, tk, st, tile_list, (uint32_t)kSmallSort);
+              last_tile = tk;
+            }
           } else if (any) {
             atomicOr(&st->range, 1u);
           }
