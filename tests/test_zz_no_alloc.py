@@ -2,7 +2,8 @@
 cannot allocate) against igc_sparse_conv on the same inputs: bit-identical outputs on every
 path (the same kernels run; only where their temporaries live differs), over two calls in a
 row on one device with the second one smaller, and a host-side capacity error for a layer
-whose temporaries exceed the static scratch array (nothing is launched then)."""
+whose temporaries exceed the static scratch array (nothing is launched then). The general-shape
+path keeps its packed fp32 weights there."""
 import ctypes
 
 import numpy as np
@@ -14,7 +15,7 @@ from tests._gpu import require_gpu, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
-PATH = {"leaf": 1, "ggs": 2, "mixed": 3}
+PATH = {"leaf": 1, "ggs": 2, "mixed": 3, "gather": 4}
 
 
 def _clusters(seed, n=4, size=20, spread=200, fill=0.35):
@@ -58,6 +59,8 @@ def _case(coords, cin, cout, dtype, path, seed):
     ("leaf", torch.bfloat16, 32, 32, "clusters", 3),
     ("leaf", torch.float32, 8, 16, "leaf", 4),
     ("mixed", torch.bfloat16, 64, 64, "clusters", 5),
+    ("gather", torch.bfloat16, 4, 32, "lidar", 6),
+    ("gather", torch.float32, 32, 300, "clusters", 7),
 ])
 def test_noalloc_matches_conv_twice_second_smaller(path, dtype, cin, cout, big, small):
     require_gpu()
@@ -78,6 +81,13 @@ def test_noalloc_rejects_layers_beyond_the_scratch():
     w = torch.zeros((27, 64, 64), dtype=torch.bfloat16, device="cuda")
     rc, y = _noalloc(g, m, f, w, "ggs")
     assert rc == 6  # IGC_ERR_CAPACITY, decided on the host before any launch
+    # The general-shape path's packed weights (27 * cin * cout * 4 bytes) beyond the scratch.
+    gs = igc.grid_build(to_dev(_clusters(91, n=1, size=8)))
+    ms = igc.kernel_map(gs)
+    f = torch.zeros((gs.n_voxels, 1024), dtype=torch.float32, device="cuda")
+    w = torch.zeros((27, 1024, 1024), dtype=torch.float32, device="cuda")
+    rc, y = _noalloc(gs, ms, f, w, "gather")
+    assert rc == 6
     assert b"igc_sparse_conv_noalloc" in igc._lib.load().igc_last_error()
     torch.cuda.synchronize()
     assert torch.isnan(y).all()  # nothing was written
