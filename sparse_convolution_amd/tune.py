@@ -1,7 +1,7 @@
 """Selects the gather-GEMM-scatter row order per layer on this GPU and writes the tuning file
 that the library loads (igc_tuning_load; the package loads igconv_tuning.txt beside it).
 
-    python -m sparse_convolution_amd.tune [--workloads lidar band large] [--out PATH]
+    python -m sparse_convolution_amd.tune [--workloads lidar band large large:grad] [--out PATH]
 
 For every workload (synthetic scenes of the bench, see workloads/) each candidate (span 256 /
 1024 / 4096 rows sorted by neighbour mask, natural or class bit order, output-tile width) is timed
@@ -9,7 +9,8 @@ on the same path that runs in deployment (igc_sparse_conv, gather-GEMM-scatter),
 that its output equals the default order's; the fastest is written as one rule for the layer's
 channels, with the measured times as comments (DriveRT, "Measurement and reproducibility":
 algorithms are selected offline on the target GPU with the deployment path, and the selection
-is stored in a documented file).
+is stored in a documented file). A workload named NAME:grad tunes the layer's input-gradient
+shape (cout -> cin, the gather-GEMM-scatter call the backward pass makes) on the same scene.
 """
 from __future__ import annotations
 
@@ -45,43 +46,46 @@ def _time(fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def tune_workload(name: str, log) -> tuple[str, list]:
+def tune_workload(spec: str, log) -> tuple[str, list]:
     import workloads
+    name, _, kind = spec.partition(":")
     wl = workloads.WORKLOADS[name]
+    cin, cout = (wl.cout, wl.cin) if kind == "grad" else (wl.cin, wl.cout)
     c = torch.from_numpy(workloads.make_coords(name)).cuda()
     g = igc.grid_build(c)
     m = igc.kernel_map(g)
-    f = workloads.make_features_device(g.n_voxels, wl.cin, 3000 + wl.index, "cuda", torch.bfloat16)
-    w = torch.from_numpy(workloads.make_weights(wl.cin, wl.cout, 4000 + wl.index, wl.weight_std)).bfloat16().cuda()
+    f = workloads.make_features_device(g.n_voxels, cin, 3000 + wl.index, "cuda", torch.bfloat16)
+    w = torch.from_numpy(workloads.make_weights(cin, cout, 4000 + wl.index, 1.0 / (27 * cin) ** 0.5)).bfloat16().cuda()
     occ = g.n_voxels / (512.0 * g.n_leaf)
     reps = 3 if g.n_voxels > 20_000_000 else 10
     results = []
     ref = None
     with tempfile.TemporaryDirectory() as d:
         path = os.path.join(d, "rule.txt")
-        for (span, order), tile in [(so, t) for so in SPANS for t in _tiles(wl.cin, wl.cout)]:
+        for (span, order), tile in [(so, t) for so in SPANS for t in _tiles(cin, cout)]:
             with open(path, "w") as fh:
-                fh.write(f"ggs {wl.cin} {wl.cout} 0 1e30 {span} {order} {tile}\n")
+                fh.write(f"ggs {cin} {cout} 0 1e30 {span} {order} {tile}\n")
             igc.tuning_load(path)
-            out = torch.empty((g.n_voxels, wl.cout), dtype=torch.bfloat16, device="cuda")
+            out = torch.empty((g.n_voxels, cout), dtype=torch.bfloat16, device="cuda")
             ms = _time(lambda: igc.sparse_conv(g, f, w, kmap=m, path="ggs", out=out), reps)
             if ref is None:
                 ref = out.clone()
             elif not torch.equal(out.float().abs(), ref.float().abs()):  # signs of exact zeros may differ
-                raise RuntimeError(f"{name}: row order {span} {order} tile {tile} changed the output")
+                raise RuntimeError(f"{spec}: row order {span} {order} tile {tile} changed the output")
             results.append((ms, span, order, tile))
-            log(f"[tune] {name} span {span} {order} tile {tile}: {ms:.4f} ms")
+            log(f"[tune] {spec} span {span} {order} tile {tile}: {ms:.4f} ms")
     igc.tuning_load(None)
     best = min(results)
-    lines = [f"# {name}: {g.n_voxels} voxels, leaf occupancy {occ:.3f}, bf16 {wl.cin} -> {wl.cout}; ms per conv: "
+    what = " (the input-gradient shape)" if kind == "grad" else ""
+    lines = [f"# {spec}: {g.n_voxels} voxels, leaf occupancy {occ:.3f}, bf16 {cin} -> {cout}{what}; ms per conv: "
              + ", ".join(f"{s}/{o}/{t} {ms:.3f}" for ms, s, o, t in results),
-             f"ggs {wl.cin} {wl.cout} 0 1e30 {best[1]} {best[2]} {best[3]}"]
+             f"ggs {cin} {cout} 0 1e30 {best[1]} {best[2]} {best[3]}"]
     return "\n".join(lines), results
 
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--workloads", nargs="+", default=["lidar", "band", "large"])
+    ap.add_argument("--workloads", nargs="+", default=["lidar", "band", "large", "large:grad"])
     ap.add_argument("--out", default=_lib.TUNING_PATH)
     args = ap.parse_args()
     log = lambda s: (sys.stderr.write(s + "\n"), sys.stderr.flush())
