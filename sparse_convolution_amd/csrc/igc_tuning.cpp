@@ -10,6 +10,7 @@
 //   ggs <cin|*> <cout|*> <occupancy_lo> <occupancy_hi> <span> <natural|class> [tile]
 // with span 256, 1024 or 4096, lo <= occupancy < hi, and tile (output channels per workgroup)
 // auto, 256, 128 or 64.
+#include <cctype>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -61,26 +62,40 @@ extern "C" int igc_tuning_load(const char* path) {
   while (std::fgets(line, sizeof line, f)) {
     ++lineno;
     if (char* h = std::strchr(line, '#')) *h = '\0';
-    char kind[16], cin[16], cout[16], order[16], tile[16] = "auto";
+    char kind[16] = "", cin[16] = "", cout[16] = "", order[16] = "", tile[16] = "auto";
     double lo = 0, hi = 0;
-    int span = 0;
-    const int n =
-        std::sscanf(line, "%15s %15s %15s %lf %lf %d %15s %15s", kind, cin, cout, &lo, &hi, &span, order, tile);
+    int span = 0, used = 0;
+    const int n = std::sscanf(line, "%15s %15s %15s %lf %lf %d %15s %15s%n", kind, cin, cout, &lo, &hi, &span, order,
+                              tile, &used);
     if (n <= 0) continue;  // blank or comment
+    // Nothing may follow the last field (%n is only set when all eight fields were read).
+    const char* rest = line + used;
+    if (n == 7) {  // no tile: everything after the order must be blank
+      const char* p = std::strstr(line, order);
+      rest = p ? p + std::strlen(order) : line;
+    }
+    bool extra = false;
+    for (const char* p = rest; *p; ++p) extra |= !std::isspace((unsigned char)*p);
+    // Channel counts: "*" or a positive integer.
+    auto channels = [](const char* t, int32_t* v) {
+      if (!std::strcmp(t, "*")) return *v = -1, true;
+      char* end = nullptr;
+      const long x = std::strtol(t, &end, 10);
+      return *v = (int32_t)x, end != t && *end == '\0' && x > 0 && x <= 1 << 20;
+    };
     Rule r;
+    const bool ch_ok = channels(cin, &r.cin) && channels(cout, &r.cout);
     const bool order_ok = !std::strcmp(order, "natural") || !std::strcmp(order, "class");
     const int bn = !std::strcmp(tile, "auto") ? 0 : std::atoi(tile);
     const bool tile_ok = !std::strcmp(tile, "auto") || bn == 256 || bn == 128 || bn == 64;
-    if ((n != 7 && n != 8) || std::strcmp(kind, "ggs") || !(span == 256 || span == 1024 || span == 4096) ||
-        !order_ok || !tile_ok || !(lo <= hi)) {
+    if ((n != 7 && n != 8) || extra || std::strcmp(kind, "ggs") || !ch_ok ||
+        !(span == 256 || span == 1024 || span == 4096) || !order_ok || !tile_ok || !(lo <= hi)) {
       rc = set_error(IGC_ERR_INVALID_ARG, "igc_tuning_load: " + std::string(path) + ":" + std::to_string(lineno) +
                                               ": expected 'ggs <cin|*> <cout|*> <occ_lo> <occ_hi> <256|1024|4096> "
                                               "<natural|class> [auto|256|128|64]'");
       break;
     }
     r.tu.bn = bn;
-    r.cin = std::strcmp(cin, "*") ? std::atoi(cin) : -1;
-    r.cout = std::strcmp(cout, "*") ? std::atoi(cout) : -1;
     r.occ_lo = lo;
     r.occ_hi = hi;
     r.tu.span = span;
