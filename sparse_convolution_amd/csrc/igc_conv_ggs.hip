@@ -687,12 +687,17 @@ int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats
     e = launch_plan(tu.span, tu.order, d_map, N, n_in, perm, blk, skip, s);
   }
   if (e == hipSuccess && n_tiles > 0) {
-    const bool k64 = cin % 64 == 0;
+    // 64-channel chunks where cin allows, unless the layer's rule asks for 32-channel chunks.
+    const bool k64 = cin % 64 == 0 && tu.kc != 32;
     // Tile shapes measured on MI355X: 256 x 256 with eight waves (two per SIMD, each 128 rows
     // by 64 channels: 64 rows by 128 is 0.5% slower on 128 -> 256), 256 x 128 with sixteen
     // (each 32 rows by 64 channels: 1.6% faster on 128 -> 128 than 64 by 32), 256 x 64 with
     // eight (each 32 rows by all 64 channels: 2% faster on 64 -> 64 than 64 by 32); 32-channel
-    // chunks when cin is not a multiple of 64.
+    // chunks when cin is not a multiple of 64 or the layer's rule asks for them. 256 x 64 with
+    // 32-channel chunks on four waves takes 70 KB of LDS, so two workgroups share a CU and one's
+    // gather latency overlaps the other's work: 64 -> 64 on 17M voxels 7.92 -> 7.07 ms and on
+    // 48M 22.3 -> 19.8 ms, 128 -> 64 on 17M 12.9 -> 11.8 ms, but 256 -> 64 on 17M 23.6 -> 25.3 ms
+    // and 128 -> 64 on 204k voxels 0.136 -> 0.147 ms; hence a per-layer choice.
     const int64_t n256 = cout / 256, n128 = cout / 128, n64 = cout / 64;
     // A layer's rule may ask for narrower output tiles (more workgroups, each gathering the
     // same input rows for fewer channels).

@@ -9,7 +9,8 @@
 // File format (text, one rule per line, '#' starts a comment, first matching rule wins):
 //   ggs <cin|*> <cout|*> <occupancy_lo> <occupancy_hi> <span> <natural|class> [tile]
 // with span 256, 1024 or 4096, lo <= occupancy < hi, and tile (output channels per workgroup)
-// auto, 256, 128 or 64.
+// auto, 256, 128 or 64; 128k32 and 64k32 take that width with 32-channel chunks (smaller LDS
+// stages: two workgroups fit on a CU at 64 channels).
 #include <cctype>
 #include <cstdio>
 #include <cstdlib>
@@ -56,12 +57,24 @@ extern "C" int igc_tuning_load(const char* path) {
   FILE* f = std::fopen(path, "r");
   if (!f) return set_error(IGC_ERR_INVALID_ARG, std::string("igc_tuning_load: cannot open ") + path);
   std::vector<Rule> rules;
-  char line[512];
+  // Whole lines of any length (the measured times are kept as long comment lines).
+  std::string text;
+  auto next_line = [&]() {
+    text.clear();
+    char chunk[512];
+    while (std::fgets(chunk, sizeof chunk, f)) {
+      text += chunk;
+      if (text.back() == '\n') return true;
+    }
+    return !text.empty();
+  };
   int lineno = 0;
   int rc = IGC_OK;
-  while (std::fgets(line, sizeof line, f)) {
+  while (next_line()) {
     ++lineno;
-    if (char* h = std::strchr(line, '#')) *h = '\0';
+    const size_t hash = text.find('#');
+    if (hash != std::string::npos) text.resize(hash);
+    const char* line = text.c_str();
     char kind[16] = "", cin[16] = "", cout[16] = "", order[16] = "", tile[16] = "auto";
     double lo = 0, hi = 0;
     int span = 0, used = 0;
@@ -86,16 +99,19 @@ extern "C" int igc_tuning_load(const char* path) {
     Rule r;
     const bool ch_ok = channels(cin, &r.cin) && channels(cout, &r.cout);
     const bool order_ok = !std::strcmp(order, "natural") || !std::strcmp(order, "class");
+    const bool k32 = !std::strcmp(tile, "128k32") || !std::strcmp(tile, "64k32");
     const int bn = !std::strcmp(tile, "auto") ? 0 : std::atoi(tile);
-    const bool tile_ok = !std::strcmp(tile, "auto") || bn == 256 || bn == 128 || bn == 64;
+    const bool tile_ok = !std::strcmp(tile, "auto") || k32 || !std::strcmp(tile, "256") ||
+                         !std::strcmp(tile, "128") || !std::strcmp(tile, "64");
     if ((n != 7 && n != 8) || extra || std::strcmp(kind, "ggs") || !ch_ok ||
         !(span == 256 || span == 1024 || span == 4096) || !order_ok || !tile_ok || !(lo <= hi)) {
       rc = set_error(IGC_ERR_INVALID_ARG, "igc_tuning_load: " + std::string(path) + ":" + std::to_string(lineno) +
                                               ": expected 'ggs <cin|*> <cout|*> <occ_lo> <occ_hi> <256|1024|4096> "
-                                              "<natural|class> [auto|256|128|64]'");
+                                              "<natural|class> [auto|256|128|64|128k32|64k32]'");
       break;
     }
     r.tu.bn = bn;
+    r.tu.kc = k32 ? 32 : 0;
     r.occ_lo = lo;
     r.occ_hi = hi;
     r.tu.span = span;

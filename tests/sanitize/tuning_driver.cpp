@@ -37,18 +37,22 @@ static int check(bool ok, const char* what) {
 
 int main() {
   int bad = 0;
-  const std::string good = write_file("good.txt",
-                                      "# comment line\n"
-                                      "\n"
-                                      "ggs 128 256 0 0.5 4096 class auto   # trailing comment\n"
-                                      "ggs 128 256 0.5 1e30 1024 natural 128\n"
-                                      "ggs * 64 0 1e30 256 class 64\n"
-                                      "ggs * * 0 1e30 1024 natural\n");
+  // A comment line longer than the parser's read buffer, then rules (one with a 32-channel-chunk tile).
+  const std::string text = "# comment line" + std::string(3000, 'x') + "\n"
+                           "\n"
+                           "ggs 128 256 0 0.5 4096 class auto   # trailing comment" + std::string(1000, 'y') + "\n"
+                           "ggs 128 256 0.5 1e30 1024 natural 128\n"
+                           "ggs 64 96 0 1e30 1024 class 64k32\n"
+                           "ggs * 64 0 1e30 256 class 64\n"
+                           "ggs * * 0 1e30 1024 natural\n";
+  const std::string good = write_file("good.txt", text.c_str());
   bad += check(igc_tuning_load(good.c_str()) == 0, "valid file rejected");
   igc::GgsTuning t = igc::ggs_tuning(128, 256, 1000, 100);  // occupancy 1000 / 51200 < 0.5
   bad += check(t.span == 4096 && t.order == 1 && t.bn == 0, "first rule not matched");
   t = igc::ggs_tuning(128, 256, 51200, 100);  // occupancy 1.0
   bad += check(t.span == 1024 && t.order == 0 && t.bn == 128, "second rule not matched");
+  t = igc::ggs_tuning(64, 96, 10, 10);
+  bad += check(t.span == 1024 && t.order == 1 && t.bn == 64 && t.kc == 32, "32-channel-chunk rule not matched");
   t = igc::ggs_tuning(32, 64, 10, 10);
   bad += check(t.span == 256 && t.order == 1 && t.bn == 64, "wildcard cin not matched");
   t = igc::ggs_tuning(96, 96, 10, 10);
@@ -56,8 +60,9 @@ int main() {
   const char* malformed[] = {"ggs 128 256 0 1 512 class\n",       "ggs 128 256 0 1 256 diagonal\n",
                              "ggs 128 256 0 1 256 natural 96\n",  "ggs 128 256 zero 1 256 natural\n",
                              "ggs 128\n",                         "conv 128 256 0 1 256 natural\n",
-                             "ggs -4 256 0 1 256 natural\n",      "ggs 128 256 0 1 256 natural auto extra\n"};
-  for (int i = 0; i < 8; ++i) {
+                             "ggs -4 256 0 1 256 natural\n",      "ggs 128 256 0 1 256 natural auto extra\n",
+                             "ggs 128 256 0 1 256 natural 256k32\n"};
+  for (size_t i = 0; i < sizeof malformed / sizeof malformed[0]; ++i) {
     const std::string p = write_file("bad.txt", malformed[i]);
     bad += check(igc_tuning_load(p.c_str()) != 0, "malformed line accepted");
     // A failed load leaves the previous table in place.
