@@ -232,13 +232,15 @@ int igc_sparse_conv(const igc_grid* grid, const int32_t* d_map, const void* d_fe
  * matches a layer by channels and the grid's leaf occupancy N / (512 F) in [lo, hi); span is
  * 256, 1024 or 4096 rows; the key's bit order is natural (offset o at bit o) or class (corner,
  * then edge, face and centre offsets most significant); tile is the output channels per
- * workgroup (auto = the widest the layer allows, or 256, 128, 64; a width the layer cannot use
- * is ignored). A layer no rule matches sorts within its 256-row tiles in natural order with
+ * workgroup (auto = the widest the layer allows, or 256, 128, 64; 128k32 and 64k32 take that
+ * width with 32-channel chunks, whose smaller LDS stages let two workgroups share a CU; a width
+ * the layer cannot use is ignored). A layer no rule matches sorts within its 256-row tiles in natural order with
  * automatic tiles. The table is process-wide, replaced whole by each load
  * (path NULL clears it), and read by later igc_sparse_conv / _noalloc / _between calls on the
  * gather-GEMM-scatter path. Neither changes an output value: the row order changes which
- * offsets a tile visits (rows only gain exact zero products), and the channel chunk, hence the
- * fp32 summation order, depends only on cin, not on the tile width. Errors: IGC_ERR_INVALID_ARG for an unreadable
+ * offsets a tile visits (rows only gain exact zero products), and every tile shape accumulates
+ * the same 32-channel MFMA steps in the same (offset, channel) order, so the fp32 summation
+ * order depends only on cin. Errors: IGC_ERR_INVALID_ARG for an unreadable
  * file or a malformed line (the table is then unchanged). */
 int igc_tuning_load(const char* path);
 
