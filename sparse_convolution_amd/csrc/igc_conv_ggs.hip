@@ -295,8 +295,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // BN output channels per workgroup, KC input channels per chunk, WM waves along the rows
-// (NWV / WM along the channels), NST LDS stages (NST - 1 chunks of loads in flight), NWV waves.
-template <int BN, int KC, int WM, int NST, int NWV>
+// (NWV / WM along the channels), NST LDS stages (NST - 1 chunks of loads in flight), NWV waves,
+// TBM output rows per workgroup: a whole plan tile (kBM) or a part of one (its rows and their
+// 16-row block bits).
+template <int BN, int KC, int WM, int NST, int NWV, int TBM>
 __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __restrict__ map, int64_t N, int64_t n_in,
                                                        const int32_t* __restrict__ perm,
                                                        const uint16_t* __restrict__ blk,
@@ -305,18 +307,18 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
                                                        uint16_t* __restrict__ out, int64_t col_tiles) {
   constexpr int NT = 64 * NWV;  // threads
   constexpr int WN = NWV / WM;
-  constexpr int MW = kBM / WM;  // rows per wave
+  constexpr int MW = TBM / WM;  // rows per wave
   constexpr int NW = BN / WN;   // channels per wave
   constexpr int MI = MW / 16, NI = NW / 16;
   constexpr int SEG = KC / 8;                 // 16-byte granules per staged row
   constexpr int ROWB = KC * 2;                // bytes per staged row
   constexpr int RPI = 64 / SEG;               // rows filled by one wave-wide LDS load
-  constexpr int AI = kBM / RPI / NWV;         // A loads per wave and chunk
+  constexpr int AI = TBM / RPI / NWV;         // A loads per wave and chunk
   constexpr int BI = BN / RPI / NWV;          // B loads per wave and chunk
-  constexpr int A_BYTES = kBM * ROWB, B_BYTES = BN * ROWB;
+  constexpr int A_BYTES = TBM * ROWB, B_BYTES = BN * ROWB;
   constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   constexpr int OUT_ROWS = 128 * BN * 2 <= STAGE_BYTES ? 128 : (64 * BN * 2 <= STAGE_BYTES ? 64 : 32);
-  constexpr int NPASS = kBM / OUT_ROWS;
+  constexpr int NPASS = TBM / OUT_ROWS;
   constexpr int OG = BN / 8;                  // 16-byte granules per output row
   static_assert(MI >= 1 && NI >= 1 && AI >= 1 && BI >= 1, "tile shape");
   static_assert(OUT_ROWS * BN * 2 <= STAGE_BYTES && OG >= 8, "output pass fits one stage");
@@ -331,8 +333,8 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
   __shared__ uint4 s_st3[NST > 3 ? STAGE_BYTES / 16 : 1];
   __shared__ uint4 s_st4[NST > 4 ? STAGE_BYTES / 16 : 1];
   __shared__ uint4 s_st5[NST > 5 ? STAGE_BYTES / 16 : 1];
-  __shared__ int32_t s_perm[kBM];
-  __shared__ __align__(16) int32_t s_map[kNOff][kBM];
+  __shared__ int32_t s_perm[TBM];
+  __shared__ __align__(16) int32_t s_map[kNOff][TBM];
   __shared__ uint16_t s_blk[kNOff];
   __shared__ uint16_t s_blku[kNOff];  // s_blk of the u-th used offset
   __shared__ uint8_t s_olist[kNOff];
@@ -344,11 +346,17 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
   const int wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int64_t t_lin = xcd_tile(blockIdx.x, gridDim.x);
-  const int64_t tile = t_lin / col_tiles;
+  // Rows [part * TBM, (part + 1) * TBM) of plan tile `tile` and their 16-row block bits.
+  constexpr int PARTS = kBM / TBM;
+  static_assert(PARTS * TBM == kBM && TBM % 16 == 0, "tile rows");
+  const int64_t wtile = t_lin / col_tiles;
+  const int64_t tile = wtile / PARTS;
+  const int part = (int)(wtile % PARTS);
   const int n0 = (int)(t_lin % col_tiles) * BN;
 
-  for (int r = tid; r < kBM; r += NT) s_perm[r] = perm[tile * kBM + r];
-  if (tid < kNOff) s_blk[tid] = blk[tile * kNOff + tid];
+  for (int r = tid; r < TBM; r += NT) s_perm[r] = perm[tile * kBM + part * TBM + r];
+  if (tid < kNOff)
+    s_blk[tid] = (uint16_t)((blk[tile * kNOff + tid] >> (part * (TBM / 16))) & ((1u << (TBM / 16)) - 1u));
   __syncthreads();
   if (tid == 0) {
     int n = 0;
@@ -369,17 +377,17 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
   // An entry outside [0, n_in) is stored as -1 (absent): the gather never leaves the input.
   // Layout: row u holds the u-th used offset, and the AI entries one lane gathers per chunk
   // (rows (w*AI + q)*RPI + l, q < AI) are adjacent, so one vector read fetches them.
-  constexpr int RPI_ = 64 / (KC / 8), AI_ = kBM / RPI_ / NWV;
+  constexpr int RPI_ = 64 / (KC / 8), AI_ = TBM / RPI_ / NWV;
   auto mslot = [&](int row) {
     const int w = row / (AI_ * RPI_), rem = row % (AI_ * RPI_);
     return (w * RPI_ + rem % RPI_) * AI_ + rem / RPI_;
   };
   {
-    // kBM rows x 27 offsets over NT threads: thread t takes row t % kBM and every
-    // (NT / kBM)-th offset starting at t / kBM.
-    constexpr int OSTEP = NT / kBM;
+    // TBM rows x 27 offsets over NT threads: thread t takes row t % TBM and every
+    // (NT / TBM)-th offset starting at t / TBM.
+    constexpr int OSTEP = NT / TBM;
     constexpr int OPT = (kNOff + OSTEP - 1) / OSTEP;
-    const int row = tid % kBM, o0 = tid / kBM;
+    const int row = tid % TBM, o0 = tid / TBM;
     const int32_t myrow = s_perm[row];
     const uint32_t used = myrow >= 0 ? s_used : 0u;
     int32_t v[OPT];
@@ -597,11 +605,11 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
   }
 }
 
-template <int BN, int KC, int WM, int NST, int NWV>
+template <int BN, int KC, int WM, int NST, int NWV, int TBM = kBM>
 void launch_main(int64_t n_tiles, int64_t col_tiles, const int32_t* map, int64_t N, int64_t n_in, const int32_t* perm,
                  const uint16_t* blk, const void* feats, const uint16_t* wt, int cin, int cout, void* out,
                  hipStream_t s) {
-  k_conv_ggs_bf16<BN, KC, WM, NST, NWV><<<(unsigned)(n_tiles * col_tiles), 64 * NWV, 0, s>>>(
+  k_conv_ggs_bf16<BN, KC, WM, NST, NWV, TBM><<<(unsigned)(n_tiles * (kBM / TBM) * col_tiles), 64 * NWV, 0, s>>>(
       map, N, n_in, perm, blk, (const uint16_t*)feats, wt, cin, cout, (uint16_t*)out, col_tiles);
 }
 
@@ -703,16 +711,34 @@ int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats
     // same input rows for fewer channels).
     int bn = cout % 256 == 0 && k64 ? 256 : cout % 128 == 0 ? 128 : 64;
     if (tu.bn > 0 && tu.bn < bn && cout % tu.bn == 0) bn = tu.bn;
+    // Half tiles (a rule's `h`): each workgroup takes 128 rows of a 256-row plan tile and only the
+    // offsets those rows have. At 128 and 64 channels the stages then fit two workgroups per CU
+    // (at 256 the tile stays whole). Measured with 64-channel chunks on 8 waves: 128 -> 128 on
+    // 204k voxels 0.157 -> 0.140 ms, 64 -> 128 0.106 -> 0.089 ms, 128 -> 128 on 17M 15.4 -> 15.3
+    // ms; with 32-channel chunks on 4 waves 64 -> 64 on 17M 7.08 -> 6.77 ms.
+    const bool half = tu.rows == 128 && bn <= 128;
     if (bn == 256) {
       launch_main<256, 64, 2, 2, 8>(n_tiles, n256, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
     } else if (bn == 128 && k64) {
-      launch_main<128, 64, 8, 2, 16>(n_tiles, n128, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      if (half)
+        launch_main<128, 64, 4, 2, 8, 128>(n_tiles, n128, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      else
+        launch_main<128, 64, 8, 2, 16>(n_tiles, n128, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
     } else if (bn == 128) {
-      launch_main<128, 32, 2, 2, 8>(n_tiles, n128, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      if (half)
+        launch_main<128, 32, 2, 2, 4, 128>(n_tiles, n128, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      else
+        launch_main<128, 32, 2, 2, 8>(n_tiles, n128, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
     } else if (k64) {
-      launch_main<64, 64, 8, 2, 8>(n_tiles, n64, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      if (half)
+        launch_main<64, 64, 4, 2, 4, 128>(n_tiles, n64, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      else
+        launch_main<64, 64, 8, 2, 8>(n_tiles, n64, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
     } else {
-      launch_main<64, 32, 4, 2, 4>(n_tiles, n64, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      if (half)
+        launch_main<64, 32, 2, 2, 4, 128>(n_tiles, n64, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
+      else
+        launch_main<64, 32, 4, 2, 4>(n_tiles, n64, d_map, N, n_in, perm, blk, d_feats, wt, cin, cout, d_out, s);
     }
     e = hipGetLastError();
   }

@@ -146,6 +146,7 @@ struct GgsTuning {
   int order = 0;
   int bn = 0;  // output channels per workgroup tile (0: the widest the shape allows)
   int kc = 0;  // input channels per chunk: 32 forces 32-channel chunks (0: 64 where cin allows)
+  int rows = 0;  // output rows per workgroup: 128 takes half of a 256-row plan tile (0: whole)
 };
 GgsTuning ggs_tuning(int32_t cin, int32_t cout, int64_t n_voxels, int64_t n_leaf);
 // min_count > 0 (bf16 only): leaves with fewer active voxels are skipped (their rows untouched).

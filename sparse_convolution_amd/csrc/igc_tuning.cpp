@@ -9,8 +9,9 @@
 // File format (text, one rule per line, '#' starts a comment, first matching rule wins):
 //   ggs <cin|*> <cout|*> <occupancy_lo> <occupancy_hi> <span> <natural|class> [tile]
 // with span 256, 1024 or 4096, lo <= occupancy < hi, and tile (output channels per workgroup)
-// auto, 256, 128 or 64; 128k32 and 64k32 take that width with 32-channel chunks (smaller LDS
-// stages: two workgroups fit on a CU at 64 channels).
+// auto, 256, 128 or 64. A width of 128 or 64 may carry the suffix k32 (32-channel chunks:
+// smaller LDS stages, two workgroups per CU at 64 channels) and then h (each workgroup takes
+// half of a 256-row plan tile), e.g. 128h or 64k32h.
 #include <cctype>
 #include <cstdio>
 #include <cstdlib>
@@ -99,19 +100,24 @@ extern "C" int igc_tuning_load(const char* path) {
     Rule r;
     const bool ch_ok = channels(cin, &r.cin) && channels(cout, &r.cout);
     const bool order_ok = !std::strcmp(order, "natural") || !std::strcmp(order, "class");
-    const bool k32 = !std::strcmp(tile, "128k32") || !std::strcmp(tile, "64k32");
-    const int bn = !std::strcmp(tile, "auto") ? 0 : std::atoi(tile);
-    const bool tile_ok = !std::strcmp(tile, "auto") || k32 || !std::strcmp(tile, "256") ||
-                         !std::strcmp(tile, "128") || !std::strcmp(tile, "64");
+    // Tile: <auto|256|128|64>, then for 128 and 64 optionally "k32", then optionally "h".
+    std::string tk(tile);
+    const bool half = tk.size() > 1 && tk.back() == 'h';
+    if (half) tk.pop_back();
+    const bool k32 = tk.size() > 3 && tk.compare(tk.size() - 3, 3, "k32") == 0;
+    if (k32) tk.resize(tk.size() - 3);
+    const int bn = tk == "256" ? 256 : tk == "128" ? 128 : tk == "64" ? 64 : 0;
+    const bool tile_ok = ((tk == "auto" || bn == 256) && !k32 && !half) || bn == 128 || bn == 64;
     if ((n != 7 && n != 8) || extra || std::strcmp(kind, "ggs") || !ch_ok ||
         !(span == 256 || span == 1024 || span == 4096) || !order_ok || !tile_ok || !(lo <= hi)) {
       rc = set_error(IGC_ERR_INVALID_ARG, "igc_tuning_load: " + std::string(path) + ":" + std::to_string(lineno) +
                                               ": expected 'ggs <cin|*> <cout|*> <occ_lo> <occ_hi> <256|1024|4096> "
-                                              "<natural|class> [auto|256|128|64|128k32|64k32]'");
+                                              "<natural|class> [auto|256|128|64, 128/64 with k32 and/or h]'");
       break;
     }
     r.tu.bn = bn;
     r.tu.kc = k32 ? 32 : 0;
+    r.tu.rows = half ? 128 : 0;
     r.occ_lo = lo;
     r.occ_hi = hi;
     r.tu.span = span;

@@ -4,8 +4,8 @@ that the library loads (igc_tuning_load; the package loads igconv_tuning.txt bes
     python -m sparse_convolution_amd.tune [--workloads lidar band large large:grad] [--out PATH]
 
 For every workload (synthetic scenes of the bench, see workloads/) each candidate (span 256 /
-1024 / 4096 rows sorted by neighbour mask, natural or class bit order, output-tile width and
-input channels per chunk) is timed
+1024 / 4096 rows sorted by neighbour mask, natural or class bit order, output-tile width,
+input channels per chunk and rows per workgroup) is timed
 on the same path that runs in deployment (igc_sparse_conv, gather-GEMM-scatter), after checking
 that its output equals the default order's; the fastest is written as one rule for the layer's
 channels, with the measured times as comments (DriveRT, "Measurement and reproducibility":
@@ -30,12 +30,14 @@ SPANS = [(256, "natural"), (256, "class"), (1024, "natural"), (1024, "class"), (
 
 
 def _tiles(cin: int, cout: int) -> list:
-    """Output-tile widths the layer can use (auto = the widest); with cin a multiple of 64 also
-    the 128- and 64-channel tiles on 32-channel chunks (NNNk32)."""
+    """Output-tile shapes the layer can use (auto = the widest): the narrower widths, with cin a
+    multiple of 64 also the 128- and 64-channel tiles on 32-channel chunks (NNNk32), and each
+    128- or 64-channel shape on half tiles (suffix h: 128 rows per workgroup)."""
     widest = 256 if cout % 256 == 0 and cin % 64 == 0 else 128 if cout % 128 == 0 else 64
     tiles = ["auto"] + [str(b) for b in (128, 64) if b < widest and cout % b == 0]
     if cin % 64 == 0:
         tiles += [f"{b}k32" for b in (128, 64) if cout % b == 0]
+    tiles += [t + "h" if t != "auto" else f"{widest}h" for t in tiles if t != "auto" or widest < 256]
     return tiles
 
 

@@ -43,6 +43,7 @@ int main() {
                            "ggs 128 256 0 0.5 4096 class auto   # trailing comment" + std::string(1000, 'y') + "\n"
                            "ggs 128 256 0.5 1e30 1024 natural 128\n"
                            "ggs 64 96 0 1e30 1024 class 64k32\n"
+                           "ggs 96 128 0 1e30 256 natural 128h\n"
                            "ggs * 64 0 1e30 256 class 64\n"
                            "ggs * * 0 1e30 1024 natural\n";
   const std::string good = write_file("good.txt", text.c_str());
@@ -53,6 +54,8 @@ int main() {
   bad += check(t.span == 1024 && t.order == 0 && t.bn == 128, "second rule not matched");
   t = igc::ggs_tuning(64, 96, 10, 10);
   bad += check(t.span == 1024 && t.order == 1 && t.bn == 64 && t.kc == 32, "32-channel-chunk rule not matched");
+  t = igc::ggs_tuning(96, 128, 10, 10);
+  bad += check(t.span == 256 && t.order == 0 && t.bn == 128 && t.kc == 0 && t.rows == 128, "half-tile rule not matched");
   t = igc::ggs_tuning(32, 64, 10, 10);
   bad += check(t.span == 256 && t.order == 1 && t.bn == 64, "wildcard cin not matched");
   t = igc::ggs_tuning(96, 96, 10, 10);
@@ -61,7 +64,7 @@ int main() {
                              "ggs 128 256 0 1 256 natural 96\n",  "ggs 128 256 zero 1 256 natural\n",
                              "ggs 128\n",                         "conv 128 256 0 1 256 natural\n",
                              "ggs -4 256 0 1 256 natural\n",      "ggs 128 256 0 1 256 natural auto extra\n",
-                             "ggs 128 256 0 1 256 natural 256k32\n"};
+                             "ggs 128 256 0 1 256 natural 256k32\n", "ggs 128 256 0 1 256 natural 256h\n"};
   for (size_t i = 0; i < sizeof malformed / sizeof malformed[0]; ++i) {
     const std::string p = write_file("bad.txt", malformed[i]);
     bad += check(igc_tuning_load(p.c_str()) != 0, "malformed line accepted");

@@ -121,12 +121,15 @@ def test_tuning_file_is_parsed_on_the_host(tmp_path):
     good = tmp_path / "good.txt"
     good.write_text("# comment " + "x" * 3000 + "\n\nggs 128 * 0 0.1 4096 class  # lidar-like\nggs 64 64 0 1 256 class 64\n"
                     "ggs 64 128 0 1 256 class 128k32\nggs 96 64 0 1 1024 natural 64k32\n"
+                    "ggs 128 128 0 1 256 class 128h\nggs 64 64 0 1 256 natural 64k32h\n"
                     "ggs * * 0 1e30 256 natural auto\n")
     assert lib.igc_tuning_load(str(good).encode()) == 0
     for bad_line in ("ggs 128 128 0 1 512 class\n", "ggs 128 128 0 1 256 sideways\n", "conv 1 1 0 1 256 natural\n",
                      "ggs 128 128 0.5 0.1 256 natural\n", "ggs 128 128 0 1\n", "ggs 128 128 0 1 256 class 32\n",
                      "ggs 128 128 0 1 256 class 256k32\n", "ggs 128 128 0 1 256 class 64k16\n",
-                     "ggs 128 128 0 1 256 class k32\n", "ggs 128 128 0 1 256 class 64k32x\n"):
+                     "ggs 128 128 0 1 256 class k32\n", "ggs 128 128 0 1 256 class 64k32x\n",
+                     "ggs 128 128 0 1 256 class 256h\n", "ggs 128 128 0 1 256 class autoh\n",
+                     "ggs 128 128 0 1 256 class 64hk32\n", "ggs 128 128 0 1 256 class h\n"):
         bad = tmp_path / "bad.txt"
         bad.write_text(bad_line)
         assert lib.igc_tuning_load(str(bad).encode()) == 1, bad_line

@@ -212,7 +212,9 @@ def _restore_tuning():
 
 
 @pytest.mark.parametrize("span,order,tile", [(256, "class", "auto"), (1024, "natural", "64"), (4096, "natural", "auto"),
-                                             (4096, "class", "64"), (256, "class", "64k32"), (1024, "class", "128k32")])
+                                             (4096, "class", "64"), (256, "class", "64k32"), (1024, "class", "128k32"),
+                                             (256, "class", "128h"), (4096, "natural", "64h"), (256, "natural", "64k32h"),
+                                             (1024, "class", "128k32h")])
 @pytest.mark.parametrize("case", ["lidar", "clusters", "mixed"])
 def test_row_order_rules_keep_outputs(tmp_path, _restore_tuning, span, order, tile, case):
     # A row-order / tile rule (igc_tuning_load) changes which offsets each tile visits and how
