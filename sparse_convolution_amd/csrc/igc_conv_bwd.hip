@@ -73,8 +73,13 @@ struct WgradSplit {
 // flight - the input and output-gradient rows of stage i+1, the source rows (kernel map) of
 // stage i+2 and the row order of stage i+3. Thread tid stages rows 2 (tid % 32) and
 // 2 (tid % 32) + 1 of a stage, for the 8-channel granules tid / 32 + (NT / 32) j.
+// At least three waves per SIMD: the 128 x 128 block then keeps its accumulators in 146 VGPRs
+// instead of spreading to 180 VGPR + AGPR, and three workgroups share a CU instead of two (each
+// stage waits on its gathers; more workgroups overlap those waits). Measured: 128 -> 256 on 48M
+// voxels 215 -> 195 ms, 128 -> 128 on 17M 36.2 -> 33.8 ms and on 204k 0.269 -> 0.239 ms; the
+// smaller blocks already run six or eight waves per SIMD. Four waves spill.
 template <int MB, int NB, int NWV>
-__global__ __launch_bounds__(64 * NWV) void k_wgrad_bf16(const int32_t* __restrict__ map, int64_t N,
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(3))) void k_wgrad_bf16(const int32_t* __restrict__ map, int64_t N,
                                                     const int32_t* __restrict__ perm,
                                                     const uint16_t* __restrict__ blk,
                                                     const uint16_t* __restrict__ feats,
