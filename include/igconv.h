@@ -233,8 +233,10 @@ int igc_sparse_conv(const igc_grid* grid, const int32_t* d_map, const void* d_fe
  * 256, 1024 or 4096 rows; the key's bit order is natural (offset o at bit o) or class (corner,
  * then edge, face and centre offsets most significant); tile is the output channels per
  * workgroup (auto = the widest the layer allows, or 256, 128, 64; 128k32 and 64k32 take that
- * width with 32-channel chunks, whose smaller LDS stages let two workgroups share a CU; a width
- * the layer cannot use is ignored). A layer no rule matches sorts within its 256-row tiles in natural order with
+ * width with 32-channel chunks, whose smaller LDS stages let two workgroups share a CU; a
+ * trailing h on a 128- or 64-channel tile, e.g. 128h or 64k32h, gives each workgroup half of a
+ * 256-row tile with only the offsets its own rows have; a width the layer cannot use is
+ * ignored). A layer no rule matches sorts within its 256-row tiles in natural order with
  * automatic tiles. The table is process-wide, replaced whole by each load
  * (path NULL clears it), and read by later igc_sparse_conv / _noalloc / _between calls on the
  * gather-GEMM-scatter path. Neither changes an output value: the row order changes which

@@ -18,8 +18,9 @@
 // tile computes only its own group of offsets; span and bit order are chosen per layer
 // (igc_tuning_load).
 //
-// k_conv_ggs_bf16, one workgroup per tile x BN output channels, output-stationary:
-// the fp32 accumulators of the 256 x BN tile stay in registers for the whole reduction, so
+// k_conv_ggs_bf16, one workgroup per tile x BN output channels (or per half tile: 128 rows of a
+// plan tile with their own offset group, chosen per layer, so that two workgroups share a CU),
+// output-stationary: the fp32 accumulators of the 256 x BN tile stay in registers for the whole reduction, so
 // every offset's product is "scattered" into registers and each output row is written once,
 // with no atomics and a fixed summation order (deterministic). The reduction runs over chunks
 // (used offset, KC input channels): the tile's input rows of that offset are gathered by the
