@@ -338,7 +338,6 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
   __shared__ __align__(16) int32_t s_map[kNOff][TBM];
   __shared__ uint16_t s_blk[kNOff];
   __shared__ uint16_t s_blku[kNOff];  // s_blk of the u-th used offset
-  __shared__ uint8_t s_olist[kNOff];
   __shared__ int s_nused;
   __shared__ uint32_t s_used;
 
@@ -359,17 +358,19 @@ __global__ __launch_bounds__(64 * NWV) void k_conv_ggs_bf16(const int32_t* __res
   if (tid < kNOff)
     s_blk[tid] = (uint16_t)((blk[tile * kNOff + tid] >> (part * (TBM / 16))) & ((1u << (TBM / 16)) - 1u));
   __syncthreads();
-  if (tid == 0) {
-    int n = 0;
-    uint32_t u = 0;
-    for (int o = 0; o < kNOff; ++o)
-      if (s_blk[o]) {
-        s_blku[n] = s_blk[o];
-        s_olist[n++] = (uint8_t)o;
-        u |= 1u << o;
-      }
-    s_nused = n;
-    s_used = u;
+  if (tid < 64) {
+    // The used offsets' block bits in ascending offset order: one ballot over lanes 0..26 of
+    // wave 0, each written at its rank.
+    const uint32_t b = tid < kNOff ? s_blk[tid] : 0u;
+    const uint64_t used = __ballot(b != 0u);
+    if (b) {
+      const int rank = __popcll(used & ((1ull << tid) - 1ull));
+      s_blku[rank] = (uint16_t)b;
+    }
+    if (tid == 0) {
+      s_nused = __popcll(used);
+      s_used = (uint32_t)used;
+    }
   }
   __syncthreads();
 
