@@ -68,9 +68,11 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t nblk) {
 }
 
 // Wt[o][n][k] = W[o][k][n] (bf16 as 16-bit words).
-__global__ void k_transpose_w(const uint16_t* __restrict__ w, uint16_t* __restrict__ wt, int cin, int cout) {
+// wt[o][n][k] = w[o][k][n], by workgroup b of nb (256 threads each).
+__device__ __forceinline__ void transpose_w(const uint16_t* __restrict__ w, uint16_t* __restrict__ wt, int cin,
+                                            int cout, int64_t b, int64_t nb) {
   const int64_t total = 27ll * cin * cout;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t e = b * 256 + threadIdx.x; e < total; e += nb * 256) {
     const int64_t o = e / ((int64_t)cin * cout);
     const int64_t rem = e - o * cin * cout;
     const int64_t n = rem / cin, k = rem - n * cin;
@@ -108,7 +110,14 @@ template <int SPAN>
 __global__ __launch_bounds__(256) void k_ggs_plan(const int32_t* __restrict__ map, int64_t N, int64_t n_in,
                                                  int32_t* __restrict__ perm, int64_t n_pos,
                                                  uint16_t* __restrict__ blk, const uint8_t* __restrict__ skip,
-                                                 BitOrder bo) {
+                                                 BitOrder bo, int64_t n_plan, const uint16_t* __restrict__ w,
+                                                 uint16_t* __restrict__ wt, int cin, int cout) {
+  // Workgroups past the plan's transpose the weights for the conv (independent work in the same
+  // launch, one dependent launch fewer per conv).
+  if ((int64_t)blockIdx.x >= n_plan) {
+    transpose_w(w, wt, cin, cout, (int64_t)blockIdx.x - n_plan, (int64_t)gridDim.x - n_plan);
+    return;
+  }
   constexpr int T = 256, TB = 8;
   constexpr int K = SPAN / T;
   constexpr int RB = K == 16 ? 4 : K == 4 ? 2 : 0;
@@ -259,17 +268,21 @@ BitOrder bit_order(int which) {
   return b;
 }
 
+// With w non-null, 256 more workgroups of the same launch write wt[o][n][k] = w[o][k][n].
 hipError_t launch_plan(int span, int order, const int32_t* map, int64_t N, int64_t n_in, int32_t* perm,
-                       uint16_t* blk, const uint8_t* skip, hipStream_t s) {
+                       uint16_t* blk, const uint8_t* skip, hipStream_t s, const uint16_t* w = nullptr,
+                       uint16_t* wt = nullptr, int cin = 0, int cout = 0) {
   const int64_t n_pos = (N + kBM - 1) / kBM * kBM;
   if (n_pos == 0) return hipSuccess;
   const BitOrder bo = bit_order(order);
+  const int64_t n_plan = (N + span - 1) / span;
+  const unsigned grid = (unsigned)(n_plan + (w ? 256 : 0));
   if (span == 4096)
-    k_ggs_plan<4096><<<(unsigned)((N + 4095) / 4096), 256, 0, s>>>(map, N, n_in, perm, n_pos, blk, skip, bo);
+    k_ggs_plan<4096><<<grid, 256, 0, s>>>(map, N, n_in, perm, n_pos, blk, skip, bo, n_plan, w, wt, cin, cout);
   else if (span == 1024)
-    k_ggs_plan<1024><<<(unsigned)((N + 1023) / 1024), 256, 0, s>>>(map, N, n_in, perm, n_pos, blk, skip, bo);
+    k_ggs_plan<1024><<<grid, 256, 0, s>>>(map, N, n_in, perm, n_pos, blk, skip, bo, n_plan, w, wt, cin, cout);
   else
-    k_ggs_plan<256><<<(unsigned)((N + 255) / 256), 256, 0, s>>>(map, N, n_in, perm, n_pos, blk, skip, bo);
+    k_ggs_plan<256><<<grid, 256, 0, s>>>(map, N, n_in, perm, n_pos, blk, skip, bo, n_plan, w, wt, cin, cout);
   return hipGetLastError();
 }
 
@@ -686,15 +699,14 @@ int launch_conv_ggs(const igc_grid* g, const int32_t* d_map, const void* d_feats
   int32_t* perm = (int32_t*)(ws + L.wt_bytes);
   uint16_t* blk = (uint16_t*)(ws + L.wt_bytes + L.perm_bytes);
   uint8_t* skip = dense_min ? (uint8_t*)(ws + L.wt_bytes + L.perm_bytes + L.blk_bytes) : nullptr;
-  k_transpose_w<<<256, 256, 0, s>>>((const uint16_t*)d_w, wt, cin, cout);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && skip) {
+  hipError_t e = hipSuccess;
+  if (skip) {
     k_dense_rows<<<(unsigned)((g->n_leaf + 3) / 4), 256, 0, s>>>(g->leaf, g->n_leaf, N, dense_min, skip);
     e = hipGetLastError();
   }
   const GgsTuning tu = ggs_tuning(cin, cout, N, g->n_leaf);
   if (e == hipSuccess && n_tiles > 0) {
-    e = launch_plan(tu.span, tu.order, d_map, N, n_in, perm, blk, skip, s);
+    e = launch_plan(tu.span, tu.order, d_map, N, n_in, perm, blk, skip, s, (const uint16_t*)d_w, wt, cin, cout);
   }
   if (e == hipSuccess && n_tiles > 0) {
     // 64-channel chunks where cin allows, unless the layer's rule asks for 32-channel chunks.
