@@ -14,7 +14,9 @@
 // k_wgrad_gather: partial dW per (chunk of rows, tile of up to 64 x 64 channels, offset), rows
 // staged 64 at a time in LDS (the gathered input rows of that offset and the output-gradient
 // rows) and multiplied in 4 x 4 register blocks, summed in fp32 in a fixed order; the chunks are
-// then summed in fp64 in a fixed order by the weight-gradient reduction.
+// then summed in fp64 in a fixed order by the weight-gradient reduction. Small layers (a first
+// layer's few input channels) take k_wgrad_gather_all instead: one workgroup covers all 27
+// offsets of its rows, so each output-gradient row is staged once instead of once per offset.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -237,6 +239,80 @@ hipError_t launch_gather_t(const int32_t* map, int64_t N, int64_t n_in, const vo
   return hipGetLastError();
 }
 
+// Small layers: 27 * ceil(cin / 4) * ceil(cout / 4) <= 256 and cin <= CM (4 or 8). One
+// workgroup per chunk of rows covers all 27 offsets, and thread (o, ti, tj) owns the 4 x 4 block
+// (4 ti.., 4 tj..) of offset o, summing the chunk's rows in order. Per 64-row step the gathered
+// input rows of every offset and the output-gradient rows (once) are staged in LDS. Same partial
+// layout as k_wgrad_gather.
+template <typename T, int CM>
+__global__ __launch_bounds__(256) void k_wgrad_gather_all(const int32_t* __restrict__ map, int64_t N, int64_t n_in,
+                                                          const T* __restrict__ feats, const T* __restrict__ dout,
+                                                          int cin, int cout, int64_t rows_per_chunk,
+                                                          float* __restrict__ part) {
+  __shared__ __align__(16) float s_x[kNOffG][kWgStage][CM];
+  __shared__ __align__(16) float s_d[kWgStage][kWgTile];
+  const int tid = threadIdx.x;
+  const int TI = (cin + 3) / 4, TJ = (cout + 3) / 4, TT = TI * TJ;
+  const int o = tid / TT, t = tid % TT, ti = t / TJ, tj = t % TJ;
+  const int64_t chunk = blockIdx.x;
+  const int64_t r0 = chunk * rows_per_chunk;
+  const int64_t r1 = r0 + rows_per_chunk < N ? r0 + rows_per_chunk : N;
+  float acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[a][c] = 0.f;
+  for (int64_t base = r0; base < r1; base += kWgStage) {
+    __syncthreads();
+    // Input rows of every (offset, row) of the step; absent neighbours and columns past cin
+    // stage zeros.
+    for (int i = tid; i < kNOffG * kWgStage; i += 256) {
+      const int o2 = i / kWgStage, k = i - o2 * kWgStage;
+      const int64_t r = base + k;
+      int32_t src = r < r1 ? map[(size_t)o2 * (size_t)N + r] : -1;
+      if (src < 0 || (int64_t)src >= n_in) src = -1;
+#pragma unroll
+      for (int c = 0; c < CM; ++c) s_x[o2][k][c] = src >= 0 && c < cin ? to_f32(feats[(size_t)src * cin + c]) : 0.f;
+    }
+    // Output-gradient rows, once for all offsets. Columns past cout are not written: they only
+    // reach accumulators that are never stored.
+    for (int i = tid; i < kWgStage * cout; i += 256) {
+      const int k = i / cout, c = i - k * cout;
+      const int64_t r = base + k;
+      s_d[k][c] = r < r1 ? to_f32(dout[(size_t)r * cout + c]) : 0.f;
+    }
+    __syncthreads();
+    if (o < kNOffG) {
+      for (int k = 0; k < kWgStage; ++k) {
+        const float4 x = *(const float4*)&s_x[o][k][4 * ti];
+        const float4 d = *(const float4*)&s_d[k][4 * tj];
+        const float xv[4] = {x.x, x.y, x.z, x.w}, dv[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(xv[a], dv[c], acc[a][c]);
+      }
+    }
+  }
+  if (o < kNOffG) {
+    float* dst = part + ((size_t)chunk * kNOffG + o) * (size_t)cin * cout;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int ci = 4 * ti + a;
+      if (ci < cin)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (4 * tj + c < cout) dst[(size_t)ci * cout + 4 * tj + c] = acc[a][c];
+    }
+  }
+}
+
+// The shapes k_wgrad_gather_all takes, and its input-channel bound.
+int wgrad_all_cm(int32_t cin, int32_t cout) {
+  if (cin < 1 || cout < 1 || cout > kWgTile || kNOffG * ((cin + 3) / 4) * ((cout + 3) / 4) > 256) return 0;
+  return cin <= 4 ? 4 : cin <= 8 ? 8 : 0;
+}
+
 }  // namespace
 
 bool gather_conv_supported(int32_t dtype, int32_t cin, int32_t cout) {
@@ -271,8 +347,43 @@ int launch_conv_gather(const igc_grid* g, const int32_t* d_map, int64_t N, int64
 int launch_wgrad_gather(const igc_grid* g, const int32_t* d_map, const void* d_feats, int32_t dtype, int32_t cin,
                         const void* d_dout, int32_t cout, float* d_dw, hipStream_t s) {
   const int64_t N = g->n_voxels;
-  const int ci_tiles = (cin + kWgTile - 1) / kWgTile, co_tiles = (cout + kWgTile - 1) / kWgTile;
   const int64_t E = (int64_t)kNOffG * cin * cout;
+  if (const int cm = wgrad_all_cm(cin, cout)) {
+    // All offsets per workgroup: about 8192 workgroups of 64 to 8192 rows, at most 256 MiB of
+    // partial sums.
+    int64_t chunks = 8192;
+    if (chunks < (N + 8191) / 8192) chunks = (N + 8191) / 8192;
+    const int64_t cap = ((int64_t)256 << 20) / (E * 4);
+    if (chunks > cap) chunks = cap;
+    if (chunks > (N + kWgStage - 1) / kWgStage) chunks = (N + kWgStage - 1) / kWgStage;
+    if (chunks < 1) chunks = 1;
+    const int64_t rpc = (N + chunks - 1) / chunks;
+    chunks = (N + rpc - 1) / rpc;
+    Workspace wsb;
+    int rc = ws_acquire(&wsb, (size_t)chunks * E * 4, s, "igc_sparse_conv_backward: general-shape wgrad partials",
+                        grid_alloc(g));
+    if (rc) return rc;
+    float* part = (float*)wsb.p;
+    const bool bf = dtype == IGC_BF16;
+    if (bf && cm == 4)
+      k_wgrad_gather_all<uint16_t, 4><<<(unsigned)chunks, 256, 0, s>>>(
+          d_map, N, N, (const uint16_t*)d_feats, (const uint16_t*)d_dout, cin, cout, rpc, part);
+    else if (bf)
+      k_wgrad_gather_all<uint16_t, 8><<<(unsigned)chunks, 256, 0, s>>>(
+          d_map, N, N, (const uint16_t*)d_feats, (const uint16_t*)d_dout, cin, cout, rpc, part);
+    else if (cm == 4)
+      k_wgrad_gather_all<float, 4><<<(unsigned)chunks, 256, 0, s>>>(d_map, N, N, (const float*)d_feats,
+                                                                    (const float*)d_dout, cin, cout, rpc, part);
+    else
+      k_wgrad_gather_all<float, 8><<<(unsigned)chunks, 256, 0, s>>>(d_map, N, N, (const float*)d_feats,
+                                                                    (const float*)d_dout, cin, cout, rpc, part);
+    const hipError_t e = hipGetLastError();
+    rc = e != hipSuccess ? hip_status(e, "igc_sparse_conv_backward: general-shape wgrad launch")
+                         : launch_wgrad_reduce(part, chunks, E, d_dw, s);
+    ws_release(&wsb, s);
+    return rc;
+  }
+  const int ci_tiles = (cin + kWgTile - 1) / kWgTile, co_tiles = (cout + kWgTile - 1) / kWgTile;
   // About 4096 workgroups, at most 8192 rows per chunk (the fp32 part of the sum), at least 64,
   // and at most 256 MiB of partial sums.
   int64_t chunks = 4096 / ((int64_t)kNOffG * ci_tiles * co_tiles);
