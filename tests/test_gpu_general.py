@@ -119,7 +119,7 @@ def test_between_grids(dtype, cin, cout, stride, transposed):
 
 @pytest.mark.parametrize("dtype,cin,cout", [(torch.float32, 32, 32), (torch.bfloat16, 4, 32), (torch.bfloat16, 128, 32),
                                             (torch.float32, 70, 130), (torch.float32, 3, 5), (torch.bfloat16, 1, 36),
-                                            (torch.bfloat16, 7, 16)])
+                                            (torch.bfloat16, 7, 16), (torch.float32, 64, 64), (torch.bfloat16, 20, 36)])
 def test_backward_matches_oracle(dtype, cin, cout):
     igc = _igc()
     coords = _clusters(700 + cin + cout, n=4)
